@@ -1,0 +1,188 @@
+"""CPU oracle for the uniform-grid index build -- TEST INFRASTRUCTURE ONLY.
+
+Plain, sequential C (``ugp_oracle.c``) behind ctypes. Only the tests, the
+smoke check and the benchmark's CPU-baseline leg may import this package;
+the GPU library never does, and this package imports nothing from it.
+
+Every function returns NumPy arrays computed on the host. See the C file's
+header for which page and section each step follows.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ugp_oracle.c")
+_LIB = os.path.join(_HERE, "libugp_oracle.so")
+
+CFLAGS = ["-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off", "-fPIC", "-shared"]
+
+_u32p = ctypes.POINTER(ctypes.c_uint32)
+_f32p = ctypes.POINTER(ctypes.c_float)
+
+
+def build(src: str = _SRC, out: str = _LIB, extra: list[str] | None = None) -> str:
+    """Compile the oracle with gcc; returns the path of the shared library."""
+    cmd = ["gcc", *CFLAGS, *(extra or []), src, "-o", out + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+class Oracle:
+    """ctypes view of one compiled oracle library."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        self.path = path
+        self._lib = lib
+        lib.ugp_oracle_check_grid.argtypes = [_f32p, ctypes.c_float, _u32p, ctypes.POINTER(ctypes.c_uint64)]
+        lib.ugp_oracle_cell_index.argtypes = [_f32p, ctypes.c_uint32, _f32p, ctypes.c_float, _u32p, _u32p]
+        lib.ugp_oracle_histogram.argtypes = [_u32p, ctypes.c_uint32, ctypes.c_uint32, _u32p]
+        lib.ugp_oracle_exclusive_scan.argtypes = [_u32p, ctypes.c_uint32, _u32p]
+        lib.ugp_oracle_scatter.argtypes = [_u32p, ctypes.c_uint32, _u32p, ctypes.c_uint32, _u32p, _u32p]
+        lib.ugp_oracle_reorder.argtypes = [_f32p, _u32p, ctypes.c_uint32, _f32p]
+        lib.ugp_oracle_grid_build.argtypes = [
+            _f32p, ctypes.c_uint32, _f32p, ctypes.c_float, _u32p,
+            _u32p, _u32p, _u32p, _u32p, _f32p, _u32p,
+        ]
+        lib.ugp_oracle_diag.argtypes = [
+            _u32p, ctypes.c_uint32, ctypes.c_uint32,
+            ctypes.POINTER(ctypes.c_uint32), ctypes.POINTER(ctypes.c_uint32),
+        ]
+        for fn in (
+            lib.ugp_oracle_check_grid, lib.ugp_oracle_cell_index, lib.ugp_oracle_histogram,
+            lib.ugp_oracle_exclusive_scan, lib.ugp_oracle_scatter, lib.ugp_oracle_reorder,
+            lib.ugp_oracle_grid_build, lib.ugp_oracle_diag,
+        ):
+            fn.restype = ctypes.c_int
+
+    # -- helpers -------------------------------------------------------
+    @staticmethod
+    def _p(a: np.ndarray, t):
+        return a.ctypes.data_as(t)
+
+    @staticmethod
+    def _grid(origin, cell_size, dims):
+        o = np.ascontiguousarray(np.asarray(origin, dtype=np.float32).reshape(3))
+        d = np.ascontiguousarray(np.asarray(dims, dtype=np.uint32).reshape(3))
+        return o, np.float32(cell_size), d
+
+    def _check(self, st: int, what: str):
+        if st != 0:
+            raise OracleError(f"{what}: oracle status {st}")
+
+    # -- steps ---------------------------------------------------------
+    def cells(self, origin, cell_size, dims) -> int:
+        o, h, d = self._grid(origin, cell_size, dims)
+        out = ctypes.c_uint64(0)
+        st = self._lib.ugp_oracle_check_grid(self._p(o, _f32p), h, self._p(d, _u32p), ctypes.byref(out))
+        self._check(st, "check_grid")
+        return int(out.value)
+
+    def check_grid(self, origin, cell_size, dims) -> int:
+        o, h, d = self._grid(origin, cell_size, dims)
+        out = ctypes.c_uint64(0)
+        return int(self._lib.ugp_oracle_check_grid(self._p(o, _f32p), h, self._p(d, _u32p), ctypes.byref(out)))
+
+    def cell_index(self, particles, origin, cell_size, dims) -> np.ndarray:
+        p = np.ascontiguousarray(particles, dtype=np.float32).reshape(-1, 8)
+        o, h, d = self._grid(origin, cell_size, dims)
+        n = p.shape[0]
+        out = np.empty(n, dtype=np.uint32)
+        st = self._lib.ugp_oracle_cell_index(self._p(p, _f32p), n, self._p(o, _f32p), h, self._p(d, _u32p), self._p(out, _u32p))
+        self._check(st, "cell_index")
+        return out
+
+    def histogram(self, celdaDe, cells: int) -> np.ndarray:
+        k = np.ascontiguousarray(celdaDe, dtype=np.uint32)
+        out = np.empty(cells, dtype=np.uint32)
+        st = self._lib.ugp_oracle_histogram(self._p(k, _u32p), k.size, cells, self._p(out, _u32p))
+        self._check(st, "histogram")
+        return out
+
+    def exclusive_scan(self, conteos) -> np.ndarray:
+        c = np.ascontiguousarray(conteos, dtype=np.uint32)
+        out = np.empty(c.size + 1, dtype=np.uint32)
+        st = self._lib.ugp_oracle_exclusive_scan(self._p(c, _u32p), c.size, self._p(out, _u32p))
+        self._check(st, "exclusive_scan")
+        return out
+
+    def scatter(self, celdaDe, inicios) -> np.ndarray:
+        k = np.ascontiguousarray(celdaDe, dtype=np.uint32)
+        s = np.ascontiguousarray(inicios, dtype=np.uint32)
+        cells = s.size - 1
+        cur = np.empty(max(cells, 1), dtype=np.uint32)
+        out = np.empty(k.size, dtype=np.uint32)
+        st = self._lib.ugp_oracle_scatter(self._p(k, _u32p), k.size, self._p(s, _u32p), cells, self._p(cur, _u32p), self._p(out, _u32p))
+        self._check(st, "scatter")
+        return out
+
+    def reorder(self, particles, ordenado) -> np.ndarray:
+        p = np.ascontiguousarray(particles, dtype=np.float32).reshape(-1, 8)
+        o = np.ascontiguousarray(ordenado, dtype=np.uint32)
+        out = np.empty_like(p)
+        st = self._lib.ugp_oracle_reorder(self._p(p, _f32p), self._p(o, _u32p), o.size, self._p(out, _f32p))
+        self._check(st, "reorder")
+        return out
+
+    def grid_build(self, particles, origin, cell_size, dims) -> "GridIndex":
+        p = np.ascontiguousarray(particles, dtype=np.float32).reshape(-1, 8)
+        o, h, d = self._grid(origin, cell_size, dims)
+        cells = self.cells(o, h, d)
+        n = p.shape[0]
+        celdaDe = np.empty(n, dtype=np.uint32)
+        conteos = np.empty(cells, dtype=np.uint32)
+        inicios = np.empty(cells + 1, dtype=np.uint32)
+        ordenado = np.empty(n, dtype=np.uint32)
+        reordered = np.empty_like(p)
+        cursor = np.empty(max(cells, 1), dtype=np.uint32)
+        st = self._lib.ugp_oracle_grid_build(
+            self._p(p, _f32p), n, self._p(o, _f32p), h, self._p(d, _u32p),
+            self._p(celdaDe, _u32p), self._p(conteos, _u32p), self._p(inicios, _u32p),
+            self._p(ordenado, _u32p), self._p(reordered, _f32p), self._p(cursor, _u32p),
+        )
+        self._check(st, "grid_build")
+        return GridIndex(celdaDe, conteos, inicios, ordenado, reordered)
+
+    def diag(self, conteos, capacity: int) -> tuple[int, int]:
+        c = np.ascontiguousarray(conteos, dtype=np.uint32)
+        mx = ctypes.c_uint32(0)
+        ov = ctypes.c_uint32(0)
+        st = self._lib.ugp_oracle_diag(self._p(c, _u32p), c.size, capacity, ctypes.byref(mx), ctypes.byref(ov))
+        self._check(st, "diag")
+        return int(mx.value), int(ov.value)
+
+
+@dataclass
+class GridIndex:
+    celdaDe: np.ndarray
+    conteos: np.ndarray
+    inicios: np.ndarray
+    ordenado: np.ndarray
+    reordered: np.ndarray
+
+
+_default: Oracle | None = None
+
+
+def load(rebuild: bool = False) -> Oracle:
+    """The default oracle library, compiled on first use if absent or stale."""
+    global _default
+    if _default is not None and not rebuild:
+        return _default
+    stale = (not os.path.exists(_LIB)) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC)
+    if rebuild or stale:
+        build()
+    _default = Oracle(_LIB)
+    return _default

@@ -1,0 +1,233 @@
+/*
+ * ugp_oracle.c -- plain, sequential CPU oracle for the uniform-grid index
+ * build (count -> scan -> scatter -> reorder).
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg load this library. The GPU library shares
+ * no code, header, table or constant with it, and the product path never
+ * calls it.
+ *
+ * Build: gcc -O2 -std=c11 -fno-fast-math -ffp-contract=off -fPIC -shared
+ * On x86-64 every float operation below is one IEEE-754 binary32 operation
+ * rounded to nearest-even (SSE arithmetic, no excess precision), and the
+ * division is the correctly rounded one.
+ *
+ * What it follows, page by page (titles and sections of the source pages):
+ *
+ *  - "Contar partículas por celda", section "El kernel": each particle's
+ *    cell index is computed once, stored per particle (celdaDe), and
+ *    counted into a per-cell histogram (conteos). The cell function does
+ *    one floor, a division per axis and two multiplications for the
+ *    linear index, and the range clamp lives inside the index function.
+ *    The page takes the function bodies from an earlier lesson it does
+ *    not reproduce, so the rule written out below is the plainest reading
+ *    the pages support: per axis floor((p - o) / h), clamped to
+ *    [0, dim - 1], then x + y*nx + z*nx*ny (that linear order is stated on
+ *    "Reordenar por celda y la coalescencia de memoria", section
+ *    "El orden de las celdas también importa").
+ *  - "Construir el índice de la rejilla con un prefix sum":
+ *      section "Del conteo al inicio" -- inicios is the exclusive prefix
+ *      sum of conteos, with one extra trailing slot that holds the total;
+ *      section "La dispersión" -- a per-cell cursor starting at zero hands
+ *      out slots inicios[c] + cursor[c] and each particle index is written
+ *      there (ordenado);
+ *      section "El orden dentro de la celda" -- the stable order within a
+ *      cell uses the particle index as the tie-break, which is what the
+ *      sequential loop below produces.
+ *  - "Reordenar por celda y la coalescencia de memoria", section
+ *    "El kernel de reordenación": a gather, destination slot k receives
+ *    the whole 32-byte record of particle ordenado[k].
+ *  - "Contar partículas por celda", section "Detectar el desbordamiento
+ *    sin salir de la GPU": the diagnostic pair (largest per-cell occupancy,
+ *    number of insertions that found the cell already at or above a fixed
+ *    capacity) -- computed here in closed form from the histogram.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <string.h>
+
+#define UGPO_OK 0
+#define UGPO_ERR_NULL (-1)
+#define UGPO_ERR_ARG (-2)
+#define UGPO_ERR_RANGE (-3)
+
+/* largest per-axis dimension: dim - 1 must be exact in float32 */
+#define UGPO_MAX_DIM (1u << 24)
+
+/* ------------------------------------------------------------------ */
+/* Argument checks (the oracle rejects what it cannot define).          */
+/* ------------------------------------------------------------------ */
+
+int ugp_oracle_check_grid(const float origin[3], float cell_size, const uint32_t dims[3],
+                          uint64_t *cells_out) {
+    if (!origin || !dims) return UGPO_ERR_NULL;
+    if (!isfinite(cell_size) || !(cell_size > 0.0f)) return UGPO_ERR_ARG;
+    for (int a = 0; a < 3; ++a) {
+        if (!isfinite(origin[a])) return UGPO_ERR_ARG;
+        if (dims[a] < 1u || dims[a] > UGPO_MAX_DIM) return UGPO_ERR_RANGE;
+    }
+    uint64_t cells = (uint64_t)dims[0] * (uint64_t)dims[1] * (uint64_t)dims[2];
+    if (cells > (uint64_t)UINT32_MAX - 1u) return UGPO_ERR_RANGE;
+    if (cells_out) *cells_out = cells;
+    return UGPO_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* Step 1a: the cell of one coordinate.                                 */
+/* ------------------------------------------------------------------ */
+
+/* One axis: subtract the origin (one rounding), divide by the cell size
+ * (one correctly rounded division), floor, then clamp into [0, dim-1].
+ * The clamp is done on the float value before any conversion: the lower
+ * test is written so that NaN fails it (NaN and -inf go to 0), the upper
+ * test sends +inf and everything past the last face to dim-1. */
+static uint32_t oracle_axis_cell(float p, float o, float h, uint32_t dim) {
+    float t = p - o;
+    float q = t / h;
+    float f = floorf(q);
+    if (!(f >= 0.0f)) f = 0.0f;
+    float top = (float)(dim - 1u);
+    if (f > top) f = top;
+    return (uint32_t)f;
+}
+
+/* Step 1b: per-particle linear cell index, x + y*nx + z*nx*ny.
+ * particles: n records of 8 floats, position in floats 0..2. */
+int ugp_oracle_cell_index(const float *particles, uint32_t n, const float origin[3],
+                          float cell_size, const uint32_t dims[3], uint32_t *celdaDe) {
+    uint64_t cells = 0;
+    int st = ugp_oracle_check_grid(origin, cell_size, dims, &cells);
+    if (st != UGPO_OK) return st;
+    if (n > 0 && (!particles || !celdaDe)) return UGPO_ERR_NULL;
+    const uint64_t nx = dims[0];
+    const uint64_t nxy = (uint64_t)dims[0] * (uint64_t)dims[1];
+    for (uint32_t i = 0; i < n; ++i) {
+        const float *rec = particles + (size_t)i * 8u;
+        uint64_t kx = oracle_axis_cell(rec[0], origin[0], cell_size, dims[0]);
+        uint64_t ky = oracle_axis_cell(rec[1], origin[1], cell_size, dims[1]);
+        uint64_t kz = oracle_axis_cell(rec[2], origin[2], cell_size, dims[2]);
+        uint64_t c = kx + ky * nx + kz * nxy;
+        if (c >= cells) return UGPO_ERR_RANGE; /* cannot happen after the clamp */
+        celdaDe[i] = (uint32_t)c;
+    }
+    return UGPO_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* Step 1c: histogram of cell indices.                                  */
+/* ------------------------------------------------------------------ */
+
+int ugp_oracle_histogram(const uint32_t *celdaDe, uint32_t n, uint32_t cells,
+                         uint32_t *conteos) {
+    if (cells > 0 && !conteos) return UGPO_ERR_NULL;
+    if (n > 0 && !celdaDe) return UGPO_ERR_NULL;
+    for (uint32_t c = 0; c < cells; ++c) conteos[c] = 0u;
+    for (uint32_t i = 0; i < n; ++i) {
+        uint32_t c = celdaDe[i];
+        if (c >= cells) return UGPO_ERR_RANGE;
+        conteos[c] += 1u;
+    }
+    return UGPO_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* Step 2: exclusive prefix sum with the total in slot `cells`.         */
+/* ------------------------------------------------------------------ */
+
+int ugp_oracle_exclusive_scan(const uint32_t *conteos, uint32_t cells, uint32_t *inicios) {
+    if (!inicios) return UGPO_ERR_NULL;
+    if (cells > 0 && !conteos) return UGPO_ERR_NULL;
+    uint64_t run = 0;
+    for (uint32_t c = 0; c < cells; ++c) {
+        inicios[c] = (uint32_t)run;
+        run += conteos[c];
+        if (run > UINT32_MAX) return UGPO_ERR_RANGE;
+    }
+    inicios[cells] = (uint32_t)run;
+    return UGPO_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* Step 3: scatter with a per-cell cursor, particles taken in ascending  */
+/* index order, so each cell lists its particles in ascending order.     */
+/* `cursor` is caller scratch of `cells` entries.                       */
+/* ------------------------------------------------------------------ */
+
+int ugp_oracle_scatter(const uint32_t *celdaDe, uint32_t n, const uint32_t *inicios,
+                       uint32_t cells, uint32_t *cursor, uint32_t *ordenado) {
+    if (n == 0) return UGPO_OK;
+    if (!celdaDe || !inicios || !cursor || !ordenado) return UGPO_ERR_NULL;
+    for (uint32_t c = 0; c < cells; ++c) cursor[c] = 0u;
+    for (uint32_t i = 0; i < n; ++i) {
+        uint32_t c = celdaDe[i];
+        if (c >= cells) return UGPO_ERR_RANGE;
+        uint64_t slot = (uint64_t)inicios[c] + cursor[c];
+        if (slot >= inicios[c + 1] || slot >= n) return UGPO_ERR_RANGE;
+        ordenado[slot] = i;
+        cursor[c] += 1u;
+    }
+    return UGPO_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* Step 4: gather reorder, 32 bytes copied verbatim per record.         */
+/* ------------------------------------------------------------------ */
+
+int ugp_oracle_reorder(const float *particles, const uint32_t *ordenado, uint32_t n,
+                       float *reordered) {
+    if (n == 0) return UGPO_OK;
+    if (!particles || !ordenado || !reordered) return UGPO_ERR_NULL;
+    for (uint32_t k = 0; k < n; ++k) {
+        uint32_t src = ordenado[k];
+        if (src >= n) return UGPO_ERR_RANGE;
+        memcpy(reordered + (size_t)k * 8u, particles + (size_t)src * 8u, 32u);
+    }
+    return UGPO_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* The whole chain.  cursor: caller scratch of `cells` entries.         */
+/* ------------------------------------------------------------------ */
+
+int ugp_oracle_grid_build(const float *particles, uint32_t n, const float origin[3],
+                          float cell_size, const uint32_t dims[3], uint32_t *celdaDe,
+                          uint32_t *conteos, uint32_t *inicios, uint32_t *ordenado,
+                          float *reordered, uint32_t *cursor) {
+    uint64_t cells64 = 0;
+    int st = ugp_oracle_check_grid(origin, cell_size, dims, &cells64);
+    if (st != UGPO_OK) return st;
+    uint32_t cells = (uint32_t)cells64;
+    st = ugp_oracle_cell_index(particles, n, origin, cell_size, dims, celdaDe);
+    if (st != UGPO_OK) return st;
+    st = ugp_oracle_histogram(celdaDe, n, cells, conteos);
+    if (st != UGPO_OK) return st;
+    st = ugp_oracle_exclusive_scan(conteos, cells, inicios);
+    if (st != UGPO_OK) return st;
+    st = ugp_oracle_scatter(celdaDe, n, inicios, cells, cursor, ordenado);
+    if (st != UGPO_OK) return st;
+    return ugp_oracle_reorder(particles, ordenado, n, reordered);
+}
+
+/* ------------------------------------------------------------------ */
+/* Overflow diagnostics, closed form from the histogram.                 */
+/* Insertion number j (1-based) into cell c overflows when j > capacity, */
+/* so cell c contributes max(0, conteos[c] - capacity) overflows and the */
+/* largest occupancy is the largest count.                               */
+/* ------------------------------------------------------------------ */
+
+int ugp_oracle_diag(const uint32_t *conteos, uint32_t cells, uint32_t capacity,
+                    uint32_t *max_per_cell, uint32_t *overflows) {
+    if (!max_per_cell || !overflows) return UGPO_ERR_NULL;
+    if (cells > 0 && !conteos) return UGPO_ERR_NULL;
+    uint32_t mx = 0;
+    uint64_t ov = 0;
+    for (uint32_t c = 0; c < cells; ++c) {
+        uint32_t v = conteos[c];
+        if (v > mx) mx = v;
+        if (v > capacity) ov += (uint64_t)(v - capacity);
+    }
+    *max_per_cell = mx;
+    *overflows = (uint32_t)ov;
+    return UGPO_OK;
+}

@@ -1,0 +1,324 @@
+"""Pins for the CPU oracle: checks against what the pages and mathematics fix.
+
+Each ``pin_*`` function takes an oracle object (the default build, or a
+deliberately broken copy in the mutation test) and raises AssertionError
+when the oracle disagrees with an independent source of truth:
+
+* the worked example printed on "Construir el índice de la rejilla con un
+  prefix sum", section "Del conteo al inicio" (golden fixture);
+* exact rational arithmetic with an explicit IEEE binary32
+  round-to-nearest-even written here from the definition of the format;
+* hand-placed particles whose cell is known by construction;
+* library routines the result must reduce to (``numpy.bincount``, a
+  stable ``numpy.argsort``, fancy indexing);
+* brute force over all cells on small inputs.
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def load_golden(name: str) -> dict:
+    with open(os.path.join(GOLDEN, name), encoding="utf-8") as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------------------
+# IEEE-754 binary32 rounding of an exact rational (round to nearest, ties to
+# even), written from the format's definition: 24-bit significand, smallest
+# normal exponent -126, subnormal spacing 2^-149, overflow to infinity.
+# ---------------------------------------------------------------------------
+
+def round_f32(x: Fraction):
+    if x == 0:
+        return Fraction(0)
+    neg = x < 0
+    a = -x if neg else x
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    # normalise so that 2^e <= a < 2^(e+1)
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    q = max(e, -126) - 23  # exponent of one unit in the last place
+    scaled = a / (Fraction(2) ** q)
+    m = scaled.numerator // scaled.denominator
+    r = scaled - m
+    if r > Fraction(1, 2) or (r == Fraction(1, 2) and m % 2 == 1):
+        m += 1
+    val = m * (Fraction(2) ** q)
+    if val >= Fraction(2) ** 128:
+        return -math.inf if neg else math.inf
+    return -val if neg else val
+
+
+def model_axis_cell(p: float, o: float, h: float, dim: int) -> int:
+    """Cell along one axis by exact rationals plus explicit binary32 rounding.
+
+    t = round(p - o); q = round(t / h); floor; clamp to [0, dim - 1].
+    NaN and -inf go to 0, +inf to dim - 1.
+    """
+    if math.isnan(p):
+        return 0
+    if math.isinf(p):
+        return 0 if p < 0 else dim - 1
+    t = round_f32(Fraction(p) - Fraction(o))
+    if isinstance(t, float):  # overflowed to +-inf
+        return 0 if t < 0 else dim - 1
+    q = round_f32(t / Fraction(h))
+    if isinstance(q, float):
+        return 0 if q < 0 else dim - 1
+    f = math.floor(q)
+    if f < 0:
+        return 0
+    if f > dim - 1:
+        return dim - 1
+    return int(f)
+
+
+def model_cell_index(particles, origin, h, dims) -> np.ndarray:
+    """Linear index x + y*nx + z*nx*ny of the binary32 model, one particle at a time."""
+    p = np.asarray(particles, dtype=np.float32).reshape(-1, 8)
+    o = [float(v) for v in np.asarray(origin, dtype=np.float32)]
+    hh = float(np.float32(h))
+    d = [int(v) for v in dims]
+    out = np.empty(p.shape[0], dtype=np.uint64)
+    for i in range(p.shape[0]):
+        k = [model_axis_cell(float(p[i, a]), o[a], hh, d[a]) for a in range(3)]
+        out[i] = k[0] + k[1] * d[0] + k[2] * d[0] * d[1]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Pins
+# ---------------------------------------------------------------------------
+
+def pin_round_f32_helper():
+    """The rounding helper itself against NumPy's double -> float32 cast."""
+    rng = np.random.Generator(np.random.PCG64(99))
+    xs = np.concatenate([
+        rng.standard_normal(2000) * 10.0 ** rng.integers(-40, 39, 2000),
+        np.array([1.0 + 2.0 ** -24, 1.0 + 3 * 2.0 ** -24, 2.0 ** -149 * 1.5, 2.0 ** -150, 3.4028235e38]),
+    ])
+    for x in xs:
+        x = float(x)
+        want = float(np.float32(x))
+        got = round_f32(Fraction(x))
+        got = float(got)
+        assert got == want or (math.isinf(want) and math.isinf(got)), (x, got, want)
+
+
+def pin_worked_example_scan(orc):
+    g = load_golden("worked_example_scan.json")
+    inicios = orc.exclusive_scan(np.asarray(g["conteos"], dtype=np.uint32))
+    assert inicios.tolist() == g["inicios_with_total_slot"], inicios.tolist()
+    assert inicios[:-1].tolist() == g["inicios_printed"]
+    # the end of cell c is the start of cell c+1 (trailing slot holds the total)
+    assert inicios[1:].tolist() == g["finales_printed"]
+    for c in g["empty_cells"]:
+        assert inicios[c] == inicios[c + 1]
+
+
+def pin_worked_example_pipeline(orc):
+    """The printed example realised as particles and run through every step."""
+    g = load_golden("worked_example_scan.json")
+    conteos = g["conteos"]
+    wl = W.make_worked_example(conteos, seed=7)
+    r = orc.grid_build(wl.particles, wl.origin, wl.cell_size, wl.dims)
+    assert r.conteos.tolist() == conteos
+    assert r.inicios.tolist() == g["inicios_with_total_slot"]
+    # vida holds each record's cell number by construction
+    cell_of = wl.particles[:, 3].astype(np.int64)
+    assert r.celdaDe.tolist() == cell_of.tolist()
+    starts = g["inicios_with_total_slot"]
+    for c in range(len(conteos)):
+        sl = r.ordenado[starts[c]:starts[c + 1]]
+        assert sorted(sl.tolist()) == sorted(np.nonzero(cell_of == c)[0].tolist())
+        assert sl.tolist() == sorted(sl.tolist())  # stable: ascending particle index
+        assert np.all(r.reordered[starts[c]:starts[c + 1], 3] == float(c))
+
+
+def pin_cell_centres_noncubic(orc):
+    """A particle at the centre of cell (kx, ky, kz) lands in kx + ky*nx + kz*nx*ny."""
+    for dims in ((7, 5, 3), (1, 1, 1), (3, 1, 4), (2, 9, 1), (16, 16, 16)):
+        ks = np.stack(np.meshgrid(*[np.arange(d) for d in dims], indexing="ij"), -1).reshape(-1, 3)
+        for origin, h in (((0.0, 0.0, 0.0), 1.0), ((-5.0, 2.5, -0.75), 0.625), ((3.0, -1.0, 7.0), 0.0390625)):
+            wl = W.make_cell_centres(dims, origin, h, ks)
+            got = orc.cell_index(wl.particles, wl.origin, wl.cell_size, wl.dims)
+            want = ks[:, 0] + ks[:, 1] * dims[0] + ks[:, 2] * dims[0] * dims[1]
+            assert np.array_equal(got.astype(np.int64), want.astype(np.int64)), (dims, origin, h)
+
+
+def pin_special_positions(orc):
+    """Faces, outside points, NaN and infinities, by the clamp reading."""
+    dims = np.array([7, 5, 3], dtype=np.uint32)
+    o = np.array([-1.0, 2.0, 0.5], dtype=np.float32)
+    h = np.float32(0.5)
+    cases = []  # (x, y, z, expected (kx, ky, kz))
+    cases.append((o[0] + 0.0, o[1] + 0.0, o[2] + 0.0, (0, 0, 0)))  # lower corner
+    cases.append((o[0] + 1 * h, o[1] + 2 * h, o[2] + 1 * h, (1, 2, 1)))  # interior faces -> upper cell
+    cases.append((o[0] + 7 * h, o[1] + 5 * h, o[2] + 3 * h, (6, 4, 2)))  # upper faces -> last cell
+    cases.append((o[0] - 0.25, o[1] - 100.0, o[2] - 1e30, (0, 0, 0)))  # below -> 0
+    cases.append((o[0] + 1e6, o[1] + 1e30, 3.0e38, (6, 4, 2)))  # above -> last
+    cases.append((np.nan, np.nan, np.nan, (0, 0, 0)))
+    cases.append((-np.inf, -np.inf, -np.inf, (0, 0, 0)))
+    cases.append((np.inf, np.inf, np.inf, (6, 4, 2)))
+    cases.append((np.inf, np.nan, -np.inf, (6, 0, 0)))
+    cases.append((-0.0 + o[0], o[1] + 4.75 * h, o[2] + 2.999 * h, (0, 4, 2)))
+    parts = np.zeros((len(cases), 8), dtype=np.float32)
+    for i, c in enumerate(cases):
+        parts[i, 0:3] = np.asarray(c[:3], dtype=np.float32)
+    want = [k[0] + k[1] * 7 + k[2] * 35 for (_, _, _, k) in cases]
+    got = orc.cell_index(parts, o, h, dims)
+    assert got.tolist() == want, (got.tolist(), want)
+
+
+def pin_binary32_model(orc, wl):
+    """Oracle cell index equals the exact-rational binary32 model, every particle."""
+    got = orc.cell_index(wl.particles, wl.origin, wl.cell_size, wl.dims)
+    want = model_cell_index(wl.particles, wl.origin, wl.cell_size, wl.dims)
+    bad = np.nonzero(got.astype(np.uint64) != want)[0]
+    assert bad.size == 0, f"{bad.size} mismatches, first at {bad[:5]}"
+
+
+def pin_exact_floor_far_from_faces(orc, wl):
+    """Away from cell faces the cell is the exact floor((p - o) / h), clamped."""
+    p = wl.particles
+    got = orc.cell_index(p, wl.origin, wl.cell_size, wl.dims)
+    d = [int(v) for v in wl.dims]
+    h = Fraction(float(wl.cell_size))
+    checked = 0
+    for i in range(p.shape[0]):
+        ks = []
+        far = True
+        for a in range(3):
+            q = (Fraction(float(p[i, a])) - Fraction(float(wl.origin[a]))) / h
+            fl = math.floor(q)
+            if min(q - fl, fl + 1 - q) < Fraction(1, 10_000):
+                far = False
+                break
+            ks.append(min(max(fl, 0), d[a] - 1))
+        if not far:
+            continue
+        checked += 1
+        want = ks[0] + ks[1] * d[0] + ks[2] * d[0] * d[1]
+        assert int(got[i]) == want, (i, p[i, :3], int(got[i]), want)
+    assert checked > 0.9 * p.shape[0] or p.shape[0] < 100
+
+
+def check_index_invariants(wl, r, stable: bool):
+    """Invariants every correct build satisfies (any size)."""
+    n = wl.n
+    cells = wl.cells
+    assert r.conteos.shape == (cells,)
+    assert r.inicios.shape == (cells + 1,)
+    assert int(r.inicios[0]) == 0
+    assert int(r.inicios[-1]) == n  # trailing slot holds the total
+    assert int(r.conteos.sum(dtype=np.uint64)) == n
+    assert np.all(np.diff(r.inicios.astype(np.int64)) == r.conteos.astype(np.int64))
+    # empty cell <=> start == end
+    assert np.array_equal(r.conteos == 0, r.inicios[:-1] == r.inicios[1:])
+    # ordenado is a permutation of 0..n-1
+    seen = np.zeros(n, dtype=bool)
+    seen[r.ordenado] = True
+    assert seen.all()
+    # slot k lies in the slice of its particle's cell
+    k = np.arange(n, dtype=np.int64)
+    c = r.celdaDe[r.ordenado].astype(np.int64)
+    assert np.all(r.inicios[c] <= k) and np.all(k < r.inicios[c + 1])
+    # reorder identity, bytewise
+    assert np.array_equal(
+        r.reordered.view(np.uint32), wl.particles.view(np.uint32)[r.ordenado]
+    )
+    if stable:
+        assert np.array_equal(r.ordenado, np.argsort(r.celdaDe, kind="stable").astype(np.uint32))
+
+
+def pin_library_reductions(orc, wl):
+    """Histogram == bincount; stable scatter == stable argsort; gather == fancy index."""
+    r = orc.grid_build(wl.particles, wl.origin, wl.cell_size, wl.dims)
+    assert np.array_equal(r.conteos, np.bincount(r.celdaDe, minlength=wl.cells).astype(np.uint32))
+    assert np.array_equal(r.inicios[:-1], (np.cumsum(r.conteos, dtype=np.uint64) - r.conteos).astype(np.uint32))
+    assert np.array_equal(r.ordenado, np.argsort(r.celdaDe, kind="stable").astype(np.uint32))
+    assert np.array_equal(r.reordered, wl.particles[r.ordenado])
+    check_index_invariants(wl, r, stable=True)
+    return r
+
+
+def pin_brute_force_slices(orc, wl):
+    """Every cell's slice equals {i : cell(i) = c}, found by visiting every cell."""
+    r = orc.grid_build(wl.particles, wl.origin, wl.cell_size, wl.dims)
+    key = model_cell_index(wl.particles, wl.origin, wl.cell_size, wl.dims) if wl.n <= 5000 else r.celdaDe
+    key = np.asarray(key, dtype=np.int64)
+    for c in range(wl.cells):
+        members = np.nonzero(key == c)[0].tolist()  # visits every particle for every cell
+        sl = r.ordenado[r.inicios[c]:r.inicios[c + 1]].tolist()
+        assert sl == members, c
+
+
+def pin_diag_closed_form(orc):
+    """Overflow diagnostics against a replay of the per-insertion rule.
+
+    The rule ("Contar partículas por celda", section "Detectar el
+    desbordamiento sin salir de la GPU"): the counter's old value plus one
+    is the occupancy after an insertion; the maximum of those is tracked
+    and every insertion whose occupancy exceeds the capacity is counted.
+    """
+    rng = np.random.Generator(np.random.PCG64(5))
+    for cells, n, cap in ((6, 15, 2), (50, 400, 8), (1, 30, 64), (300, 0, 4), (40, 500, 0)):
+        keys = rng.integers(0, cells, n) if n else np.zeros(0, dtype=np.int64)
+        occ = [0] * cells
+        mx = 0
+        ov = 0
+        for c in keys:
+            prev = occ[c]
+            occ[c] = prev + 1
+            mx = max(mx, prev + 1)
+            if prev + 1 > cap:
+                ov += 1
+        got = orc.diag(np.asarray(occ, dtype=np.uint32), cap)
+        assert got == (mx, ov), (cells, n, cap, got, (mx, ov))
+    g = load_golden("worked_example_scan.json")
+    assert orc.diag(np.asarray(g["conteos"], dtype=np.uint32), 2) == (5, 1 + 3 + 0 + 0 + 2)
+
+
+def pin_grid_validation(orc):
+    ok = (np.zeros(3, np.float32), np.float32(1.0), np.array([4, 4, 4], np.uint32))
+    assert orc.check_grid(*ok) == 0
+    assert orc.check_grid(ok[0], np.float32(0.0), ok[2]) != 0
+    assert orc.check_grid(ok[0], np.float32(-1.0), ok[2]) != 0
+    assert orc.check_grid(ok[0], np.float32(np.nan), ok[2]) != 0
+    assert orc.check_grid(ok[0], np.float32(np.inf), ok[2]) != 0
+    assert orc.check_grid(np.array([0, np.nan, 0], np.float32), ok[1], ok[2]) != 0
+    assert orc.check_grid(ok[0], ok[1], np.array([0, 4, 4], np.uint32)) != 0
+    assert orc.check_grid(ok[0], ok[1], np.array([1 << 24, 1, 1], np.uint32)) == 0
+    assert orc.check_grid(ok[0], ok[1], np.array([(1 << 24) + 1, 1, 1], np.uint32)) != 0
+    assert orc.check_grid(ok[0], ok[1], np.array([1 << 16, 1 << 16, 1], np.uint32)) != 0  # 2^32 cells
+    assert orc.check_grid(ok[0], ok[1], np.array([65535, 65537, 1], np.uint32)) != 0  # 2^32 - 1 cells
+    assert orc.check_grid(ok[0], ok[1], np.array([65535, 65536, 1], np.uint32)) == 0  # 2^32 - 2^16 cells
+
+
+def pin_empty_and_degenerate(orc):
+    # n = 0: histogram all zero, starts all zero
+    origin, h, dims = np.zeros(3, np.float32), np.float32(1.0), np.array([3, 2, 1], np.uint32)
+    r = orc.grid_build(np.zeros((0, 8), np.float32), origin, h, dims)
+    assert r.conteos.tolist() == [0] * 6 and r.inicios.tolist() == [0] * 7
+    assert r.ordenado.size == 0 and r.reordered.shape == (0, 8)
+    # one cell: everything lands there, in index order
+    parts = np.random.Generator(np.random.PCG64(3)).standard_normal((50, 8)).astype(np.float32)
+    r = orc.grid_build(parts, origin, h, np.array([1, 1, 1], np.uint32))
+    assert r.conteos.tolist() == [50] and r.inicios.tolist() == [0, 50]
+    assert r.ordenado.tolist() == list(range(50))
+    # one particle
+    r = orc.grid_build(parts[:1], origin, h, dims)
+    assert int(r.inicios[-1]) == 1 and r.ordenado.tolist() == [0]
