@@ -1,0 +1,183 @@
+/*
+ * ugp.h -- C ABI of the uniform-grid particle index build for MI355X (gfx950).
+ *
+ * The build is a counting sort of particles by cell key, in the steps the
+ * source pages describe:
+ *
+ *   1. count   -- every particle's cell index is stored per particle
+ *                 (celdaDe) and counted into a per-cell histogram (conteos).
+ *                 Page "Contar partículas por celda", section "El kernel".
+ *   2. scan    -- the exclusive prefix sum of the histogram gives the first
+ *                 slot of every cell (inicios), with one extra trailing slot
+ *                 holding the total, so cell c is [inicios[c], inicios[c+1]).
+ *                 Page "Construir el índice de la rejilla con un prefix sum",
+ *                 section "Del conteo al inicio".
+ *   3. scatter -- a per-cell atomic cursor hands out slots inside each cell's
+ *                 range and the particle index is written there (ordenado).
+ *                 Same page, section "La dispersión".
+ *   4. reorder -- the 32-byte records are copied into cell order in a second
+ *                 buffer (reordered[k] = particles[ordenado[k]]).
+ *                 Page "Reordenar por celda y la coalescencia de memoria",
+ *                 section "El kernel de reordenación".
+ *
+ * Cell key (the pages name it but leave its body to an earlier lesson; this
+ * is the reading the rest of the pages support): on each axis a,
+ *     t = p[a] - origin[a]            (binary32 subtraction)
+ *     q = t / cell_size               (correctly rounded binary32 division)
+ *     k[a] = floor(q) clamped to [0, dims[a]-1]   (NaN and -inf -> 0, +inf -> dims[a]-1)
+ * and celdaDe = k[0] + k[1]*dims[0] + k[2]*dims[0]*dims[1] (the linear order of
+ * "Reordenar por celda...", section "El orden de las celdas también importa").
+ * Points outside the domain, NaN and infinities are clamped, never errors.
+ *
+ * Conventions for every entry point below:
+ *  - Device pointers are HIP device memory on the current device; host
+ *    pointers are read before the call returns.
+ *  - The caller allocates and owns every buffer. The library never
+ *    allocates or frees memory, never synchronises the host with the
+ *    device, and keeps no state between calls.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    The call returns once the work is enqueued; outputs are valid when the
+ *    stream reaches that point, and inputs must not change before then.
+ *  - Arguments are validated on the host before anything is enqueued; on
+ *    any error nothing is enqueued and the status code says why. A launch
+ *    failure reported by the HIP runtime returns UGP_ERR_HIP.
+ *  - All u32 arrays and the particle arrays must be 16-byte aligned (any
+ *    torch/hipMalloc allocation is); the workspace must be 256-byte aligned.
+ *  - No two buffers passed to one call may overlap.
+ */
+#ifndef UGP_H
+#define UGP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* One particle: 32 bytes, fields at offsets 0 / 12 / 16 / 28.
+ * Page "El estado de las partículas en storage buffers", section
+ * "La estructura y su alineación". Records are copied bit for bit. */
+typedef struct ugp_particle {
+    float pos[3];
+    float vida;
+    float vel[3];
+    float masa;
+} ugp_particle;
+
+/* Status codes. */
+#define UGP_OK 0
+#define UGP_ERR_NULL (-1)      /* a required pointer is NULL */
+#define UGP_ERR_ARG (-2)       /* cell_size not finite or <= 0, origin not finite, unknown flag or stage */
+#define UGP_ERR_RANGE (-3)     /* a dim is 0 or > 2^24, or the cell count exceeds 2^32-2 */
+#define UGP_ERR_ALIAS (-4)     /* two buffers overlap */
+#define UGP_ERR_ALIGN (-5)     /* an array is not 16-byte aligned, or the workspace not 256-byte aligned */
+#define UGP_ERR_WORKSPACE (-6) /* workspace smaller than ugp_grid_workspace_bytes() */
+#define UGP_ERR_HIP (-7)       /* the HIP runtime reported an error while enqueueing */
+
+/* Flags. */
+/* Stable order: every cell lists its particle indices in ascending order,
+ * the unique order a sequential counting sort gives (tie-break by particle
+ * index, page "Construir el índice...", section "El orden dentro de la
+ * celda"). Without it the order inside a cell depends on atomic arrival
+ * order (same section): the grouping is exact, the order is not. */
+#define UGP_FLAG_STABLE 0x1u
+/* Reorder with a separate gather kernel (coalesced writes, scattered
+ * reads) instead of writing the record inside the scatter kernel. The
+ * result is identical; this only selects the kernel schedule. */
+#define UGP_FLAG_GATHER 0x2u
+
+/* Pipeline stages, for ugp_grid_build_stage(). */
+#define UGP_STAGE_CLEAR 0u      /* zero conteos and the per-tile partial sums */
+#define UGP_STAGE_COUNT 1u      /* cell keys -> celdaDe, histogram -> conteos */
+#define UGP_STAGE_SCAN 2u       /* conteos -> inicios[cells+1], cursor init */
+#define UGP_STAGE_SCATTER 3u    /* cursor -> ordenado (and reordered unless GATHER/STABLE) */
+#define UGP_STAGE_SORT_CELLS 4u /* STABLE only: sort each cell's slice of ordenado */
+#define UGP_STAGE_GATHER 5u     /* GATHER or STABLE only: reordered[k] = particles[ordenado[k]] */
+#define UGP_NUM_STAGES 6u
+
+/* Bytes of device workspace ugp_grid_build() needs for n particles on a
+ * dims[0] x dims[1] x dims[2] grid with the given flags.
+ * dims: host array of 3. Writes *bytes; returns UGP_OK or UGP_ERR_NULL /
+ * UGP_ERR_RANGE / UGP_ERR_ARG. Pure host function. */
+int ugp_grid_workspace_bytes(uint32_t n, const uint32_t dims[3], uint32_t flags, size_t *bytes);
+
+/* Build the uniform-grid index of n particles.
+ *
+ *   particles   device, in:  n records (ugp_particle), read only
+ *   n           number of particles (0 is valid: conteos and inicios are
+ *               zeroed and nothing else is written)
+ *   origin      host, in:    3 floats, lower corner of cell (0,0,0)
+ *   cell_size   edge length of a cubic cell, finite and > 0
+ *   dims        host, in:    cells per axis, each in [1, 2^24]; the cell
+ *               count C = dims[0]*dims[1]*dims[2] must be <= 2^32-2
+ *   celdaDe     device, out: n u32, cell index of each particle
+ *   conteos     device, out: C u32, particles per cell (the histogram;
+ *               it still holds the histogram when the call completes)
+ *   inicios     device, out: C+1 u32, exclusive prefix sum of conteos,
+ *               inicios[C] = n
+ *   ordenado    device, out: n u32, particle indices grouped by cell:
+ *               cell c occupies [inicios[c], inicios[c+1])
+ *   reordered   device, out: n records, reordered[k] = particles[ordenado[k]]
+ *               bit for bit; must not overlap particles (double buffer,
+ *               page "Reordenar por celda...", section "El kernel de
+ *               reordenación")
+ *   workspace   device scratch of at least ugp_grid_workspace_bytes(); its
+ *               content on entry is ignored and on exit unspecified
+ *   flags       UGP_FLAG_* bits
+ *   stream      hipStream_t or NULL
+ *
+ * Returns UGP_OK once all kernels are enqueued, or an error code with
+ * nothing enqueued. Calls that share a workspace must be ordered on one
+ * stream; calls on different streams need different workspaces. */
+int ugp_grid_build(const ugp_particle *particles, uint32_t n, const float origin[3],
+                   float cell_size, const uint32_t dims[3], uint32_t *celdaDe, uint32_t *conteos,
+                   uint32_t *inicios, uint32_t *ordenado, ugp_particle *reordered, void *workspace,
+                   size_t workspace_bytes, uint32_t flags, void *stream);
+
+/* Enqueue one stage (UGP_STAGE_*) of ugp_grid_build() with the same
+ * arguments. Running the stages 0..UGP_NUM_STAGES-1 in order on one stream
+ * is exactly ugp_grid_build(); a stage that does not apply to `flags`
+ * returns UGP_OK and enqueues nothing. Each stage reads what the previous
+ * ones left in the outputs and the workspace, so stages must run in order
+ * with identical arguments. Intended for per-stage timing and tests. */
+int ugp_grid_build_stage(uint32_t stage, const ugp_particle *particles, uint32_t n,
+                         const float origin[3], float cell_size, const uint32_t dims[3],
+                         uint32_t *celdaDe, uint32_t *conteos, uint32_t *inicios,
+                         uint32_t *ordenado, ugp_particle *reordered, void *workspace,
+                         size_t workspace_bytes, uint32_t flags, void *stream);
+
+/* Bytes of device workspace ugp_exclusive_scan_u32() needs for `count`
+ * elements. Pure host function. */
+int ugp_scan_workspace_bytes(uint32_t count, size_t *bytes);
+
+/* Exclusive prefix sum of `count` u32 values with the total appended:
+ * out[0] = 0, out[i+1] = out[i] + in[i], out[count] = sum (mod 2^32).
+ * Page "Construir el índice...", section "Del conteo al inicio".
+ *   in   device, in:  count u32 (count may be 0: out[0] = 0)
+ *   out  device, out: count+1 u32, must not overlap `in`
+ *   workspace  device scratch of ugp_scan_workspace_bytes(count) bytes */
+int ugp_exclusive_scan_u32(const uint32_t *in, uint32_t count, uint32_t *out, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+/* Gather reorder on its own: dst[k] = src[idx[k]] for k < n, 32 bytes each,
+ * bit for bit. Page "Reordenar por celda...", section "El kernel de
+ * reordenación". Every idx[k] must be < n_src; the kernel checks and skips
+ * (leaves dst[k] unwritten) any index that is not, and the call returns
+ * UGP_OK regardless -- validate indices beforehand when they are untrusted.
+ *   src  device, in: n_src records;  idx device, in: n u32;
+ *   dst  device, out: n records, must not overlap src or idx. */
+int ugp_reorder(const ugp_particle *src, uint32_t n_src, const uint32_t *idx, uint32_t n,
+                ugp_particle *dst, void *stream);
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char *ugp_status_string(int status);
+
+/* ABI version of this header: 1. */
+int ugp_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* UGP_H */

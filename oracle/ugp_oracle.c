@@ -42,6 +42,7 @@
  *    number of insertions that found the cell already at or above a fixed
  *    capacity) -- computed here in closed form from the histogram.
  */
+#include <float.h>
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -62,7 +63,8 @@
 int ugp_oracle_check_grid(const float origin[3], float cell_size, const uint32_t dims[3],
                           uint64_t *cells_out) {
     if (!origin || !dims) return UGPO_ERR_NULL;
-    if (!isfinite(cell_size) || !(cell_size > 0.0f)) return UGPO_ERR_ARG;
+    /* a usable cell size is a finite, normal, positive float */
+    if (!isfinite(cell_size) || !(cell_size >= FLT_MIN)) return UGPO_ERR_ARG;
     for (int a = 0; a < 3; ++a) {
         if (!isfinite(origin[a])) return UGPO_ERR_ARG;
         if (dims[a] < 1u || dims[a] > UGPO_MAX_DIM) return UGPO_ERR_RANGE;

@@ -1,0 +1,155 @@
+"""CPU tests of the C ABI: the library loads, exports every declared symbol,
+and rejects bad arguments on the host before touching a GPU."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ugp.h")
+
+ugp = pytest.importorskip("uniform_grid_particle_amd")
+
+
+def _declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ugp_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ugp.library_path()):
+        pytest.fail("libugp.so is not built (run __graft_entry__.build())")
+    return ugp.load_library()
+
+
+def test_header_declares_entry_points():
+    names = _declared_functions()
+    for want in ("ugp_grid_build", "ugp_grid_build_stage", "ugp_grid_workspace_bytes",
+                 "ugp_exclusive_scan_u32", "ugp_scan_workspace_bytes", "ugp_reorder",
+                 "ugp_status_string", "ugp_abi_version"):
+        assert want in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    raw = ctypes.CDLL(ugp.library_path())
+    for name in _declared_functions():
+        assert hasattr(raw, name), f"{name} declared in ugp.h but not exported"
+
+
+def test_status_strings(lib):
+    for st in range(0, -8, -1):
+        s = ugp.status_string(st)
+        assert s and s != "unknown status"
+    assert ugp.status_string(-99) == "unknown status"
+
+
+def test_workspace_sizes(lib):
+    a = ugp.workspace_bytes(1_000_000, (128, 128, 128))
+    assert a >= 4 * 128 ** 3 and a % 256 == 0
+    b = ugp.workspace_bytes(1_000_000, (128, 128, 128), ugp.FLAG_STABLE)
+    assert b > a
+    assert ugp.workspace_bytes(0, (1, 1, 1)) >= 4
+    with pytest.raises(ugp.UGPError) as e:
+        ugp.workspace_bytes(10, (0, 4, 4))
+    assert e.value.status == ugp.UGP_ERR_RANGE
+    with pytest.raises(ugp.UGPError) as e:
+        ugp.workspace_bytes(10, ((1 << 24) + 1, 1, 1))
+    assert e.value.status == ugp.UGP_ERR_RANGE
+    with pytest.raises(ugp.UGPError) as e:
+        ugp.workspace_bytes(10, (1 << 16, 1 << 16, 1))
+    assert e.value.status == ugp.UGP_ERR_RANGE
+    with pytest.raises(ugp.UGPError) as e:
+        ugp.workspace_bytes(10, (4, 4, 4), 0x80)
+    assert e.value.status == ugp.UGP_ERR_ARG
+
+
+def _call_build(lib, *, n=4, origin=(0.0, 0.0, 0.0), h=1.0, dims=(4, 4, 4), ptrs=None, ws_bytes=1 << 20,
+                flags=0, stage=None):
+    """Call ugp_grid_build with fake (never dereferenced) addresses.
+
+    Only argument combinations that fail host validation are used here, so
+    nothing is enqueued and no GPU is touched."""
+    base = 1 << 40
+    p = dict(particles=base, celdaDe=base + (1 << 30), conteos=base + (2 << 30), inicios=base + (3 << 30),
+             ordenado=base + (4 << 30), reordered=base + (5 << 30), workspace=base + (6 << 30))
+    if ptrs:
+        p.update(ptrs)
+    o = (ctypes.c_float * 3)(*origin)
+    d = (ctypes.c_uint32 * 3)(*dims)
+    args = [p["particles"], n, o, ctypes.c_float(h), d, p["celdaDe"], p["conteos"], p["inicios"], p["ordenado"],
+            p["reordered"], p["workspace"], ctypes.c_size_t(ws_bytes), flags, None]
+    if stage is None:
+        return lib.ugp_grid_build(*args)
+    return lib.ugp_grid_build_stage(stage, *args)
+
+
+def test_validation_errors_on_host(lib):
+    nan, inf = float("nan"), float("inf")
+    assert _call_build(lib, h=0.0) == ugp.UGP_ERR_ARG
+    assert _call_build(lib, h=-1.0) == ugp.UGP_ERR_ARG
+    assert _call_build(lib, h=nan) == ugp.UGP_ERR_ARG
+    assert _call_build(lib, h=inf) == ugp.UGP_ERR_ARG
+    assert _call_build(lib, h=1e-40) == ugp.UGP_ERR_ARG  # subnormal cell size
+    assert _call_build(lib, origin=(0.0, nan, 0.0)) == ugp.UGP_ERR_ARG
+    assert _call_build(lib, origin=(inf, 0.0, 0.0)) == ugp.UGP_ERR_ARG
+    assert _call_build(lib, dims=(0, 4, 4)) == ugp.UGP_ERR_RANGE
+    assert _call_build(lib, dims=(4, (1 << 24) + 1, 4)) == ugp.UGP_ERR_RANGE
+    assert _call_build(lib, dims=(1 << 16, 1 << 16, 1)) == ugp.UGP_ERR_RANGE
+    assert _call_build(lib, flags=0x100) == ugp.UGP_ERR_ARG
+    assert _call_build(lib, ptrs={"conteos": None}) == ugp.UGP_ERR_NULL
+    assert _call_build(lib, ptrs={"inicios": None}) == ugp.UGP_ERR_NULL
+    assert _call_build(lib, ptrs={"workspace": None}) == ugp.UGP_ERR_NULL
+    assert _call_build(lib, ptrs={"particles": None}) == ugp.UGP_ERR_NULL
+    assert _call_build(lib, ptrs={"reordered": None}) == ugp.UGP_ERR_NULL
+    assert _call_build(lib, ptrs={"conteos": (1 << 40) + (2 << 30) + 4}) == ugp.UGP_ERR_ALIGN
+    assert _call_build(lib, ptrs={"particles": (1 << 40) + 8}) == ugp.UGP_ERR_ALIGN
+    assert _call_build(lib, ptrs={"workspace": (1 << 40) + (6 << 30) + 16}) == ugp.UGP_ERR_ALIGN
+    assert _call_build(lib, ws_bytes=16) == ugp.UGP_ERR_WORKSPACE
+    # reordered overlapping particles (double buffer required)
+    assert _call_build(lib, ptrs={"reordered": (1 << 40) + 16 * 4}) == ugp.UGP_ERR_ALIAS
+    # inicios overlapping conteos
+    assert _call_build(lib, ptrs={"inicios": (1 << 40) + (2 << 30) + 64}) == ugp.UGP_ERR_ALIAS
+    # unknown stage
+    assert _call_build(lib, stage=99) == ugp.UGP_ERR_ARG
+    assert _call_build(lib, stage=0, h=0.0) == ugp.UGP_ERR_ARG
+
+
+def test_scan_and_reorder_validation_on_host(lib):
+    base = 1 << 40
+    need = ctypes.c_size_t(0)
+    assert lib.ugp_scan_workspace_bytes(1000, ctypes.byref(need)) == 0 and need.value >= 4
+    assert lib.ugp_exclusive_scan_u32(base, 1000, None, base + (1 << 30), need.value, None) == ugp.UGP_ERR_NULL
+    assert lib.ugp_exclusive_scan_u32(base, 1000, base + 4, base + (1 << 30), need.value, None) == ugp.UGP_ERR_ALIGN
+    assert lib.ugp_exclusive_scan_u32(base, 1000, base + 1024, base + (1 << 30), need.value, None) == ugp.UGP_ERR_ALIAS
+    assert lib.ugp_exclusive_scan_u32(base, 1000, base + (1 << 20), base + (1 << 30), 0, None) == ugp.UGP_ERR_WORKSPACE
+    assert lib.ugp_reorder(base, 10, base + (1 << 20), 10, base + 64, None) == ugp.UGP_ERR_ALIAS
+    assert lib.ugp_reorder(base, 10, None, 10, base + (1 << 21), None) == ugp.UGP_ERR_NULL
+    assert lib.ugp_reorder(base + 8, 10, base + (1 << 20), 10, base + (1 << 21), None) == ugp.UGP_ERR_ALIGN
+    assert lib.ugp_reorder(None, 0, None, 0, None, None) == ugp.UGP_OK  # n = 0: nothing to do
+
+
+def test_product_path_has_no_oracle_dependency():
+    """The package and the HIP source never reference the oracle."""
+    pkg = os.path.join(ROOT, "uniform_grid_particle_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                assert "oracle" not in text.lower(), f"{f} mentions the oracle"
+    assert "oracle" not in open(HEADER, encoding="utf-8").read().lower()
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    import importlib
+
+    mod = importlib.import_module("uniform_grid_particle_amd")
+    monkeypatch.setattr(mod, "_lib", None)
+    monkeypatch.setattr(mod, "LIB_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        mod.load_library()

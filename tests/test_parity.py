@@ -1,0 +1,288 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Rule per output:
+  celdaDe, conteos, inicios   bit-exact
+  ordenado                    atomic mode: every index lies in its own cell's
+                              slice and the array is a permutation (so each
+                              slice holds exactly the oracle's set);
+                              stable mode: element for element
+  reordered                   bit-exact identity with the GPU's own ordenado
+                              (reordered[k] == particles[ordenado[k]]), hence
+                              per-cell multiset equality with the oracle.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+import workloads as W  # noqa: E402
+from tests import pins  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+MODES = {"atomic": dict(stable=False, gather=False), "gather": dict(stable=False, gather=True),
+         "stable": dict(stable=True, gather=False)}
+
+
+@pytest.fixture(scope="module")
+def ugp():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    import uniform_grid_particle_amd as m
+
+    m.load_library()
+    return m
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.load()
+
+
+def _u32(t):
+    return t.detach().cpu().numpy().view(np.uint32)
+
+
+def run_gpu(ugp, wl, mode="atomic", **kw):
+    dev = torch.device("cuda:0")
+    parts = torch.from_numpy(np.ascontiguousarray(wl.particles)).to(dev)
+    r = ugp.grid_build(parts, [float(v) for v in wl.origin], float(wl.cell_size),
+                       [int(v) for v in wl.dims], **MODES[mode], **kw)
+    torch.cuda.synchronize()
+    return oracle.GridIndex(_u32(r.celdaDe)[: wl.n], _u32(r.conteos), _u32(r.inicios),
+                            _u32(r.ordenado)[: wl.n], r.reordered.cpu().numpy()[: wl.n])
+
+
+def assert_parity(wl, got, ref, mode):
+    assert np.array_equal(got.celdaDe, ref.celdaDe), f"celdaDe: {np.count_nonzero(got.celdaDe != ref.celdaDe)} differ"
+    assert np.array_equal(got.conteos, ref.conteos), "conteos differ"
+    assert np.array_equal(got.inicios, ref.inicios), "inicios differ"
+    pins.check_index_invariants(wl, got, stable=(mode == "stable"))
+    if mode == "stable":
+        assert np.array_equal(got.ordenado, ref.ordenado)
+        assert np.array_equal(got.reordered.view(np.uint32), ref.reordered.view(np.uint32))
+    else:
+        # per-cell multiset equality of the records, via a canonical order
+        c = got.celdaDe[got.ordenado].astype(np.int64)
+        key = np.lexsort((got.ordenado, c))
+        assert np.array_equal(got.ordenado[key], ref.ordenado)
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+@pytest.mark.parametrize("name", ["tiny", "sparse", "baseline", "contention"])
+def test_configs(ugp, orc, name, mode):
+    print(f"[parity] {name} {mode}", flush=True)
+    wl = W.make_config(name)
+    ref = orc.grid_build(wl.particles, wl.origin, wl.cell_size, wl.dims)
+    got = run_gpu(ugp, wl, mode)
+    assert_parity(wl, got, ref, mode)
+
+
+@pytest.mark.parametrize("mode", ["atomic", "stable"])
+def test_large_full_size(ugp, orc, mode):
+    """16,777,216 particles on 256^3 cells, the largest workload, in full."""
+    print(f"[parity] large {mode}", flush=True)
+    wl = W.make_config("large")
+    ref = orc.grid_build(wl.particles, wl.origin, wl.cell_size, wl.dims)
+    got = run_gpu(ugp, wl, mode)
+    assert_parity(wl, got, ref, mode)
+
+
+def test_contention_presorted_input(ugp, orc):
+    """Input already in cell order (the GPU's own reordered output)."""
+    wl = W.make_config("contention")
+    first = run_gpu(ugp, wl, "atomic")
+    wl2 = W.Workload("contention_sorted", np.ascontiguousarray(first.reordered), wl.origin, wl.cell_size, wl.dims)
+    ref = orc.grid_build(wl2.particles, wl2.origin, wl2.cell_size, wl2.dims)
+    for mode in ("atomic", "stable"):
+        assert_parity(wl2, run_gpu(ugp, wl2, mode), ref, mode)
+
+
+@pytest.mark.parametrize("h,o,d", [(0.625, -5.0, 16), (0.078125, -5.0, 128), (0.0390625, -5.0, 256),
+                                   (0.1, -3.0, 64), (0.013, -0.5, 200), (1.0 / 3.0, -2.0, 30)])
+def test_cell_faces(ugp, orc, h, o, d):
+    """Face-adjacent positions: an approximate division would differ here."""
+    print(f"[parity] faces h={h} d={d}", flush=True)
+    wl = W.make_boundary_probe((d, d, d), (o, o, o), np.float32(h), per_axis_random=4096)
+    ref = orc.grid_build(wl.particles, wl.origin, wl.cell_size, wl.dims)
+    assert_parity(wl, run_gpu(ugp, wl, "atomic"), ref, "atomic")
+
+
+def test_noncubic_ragged(ugp, orc):
+    """Non-cubic grid (x/y/z strides differ), cells and particles off every tile size."""
+    rng = np.random.Generator(np.random.PCG64(21))
+    for dims, n in (((7, 5, 3), 3001), ((33, 1, 17), 10007), ((1, 129, 2), 2049), ((257, 3, 5), 65537)):
+        parts = np.zeros((n, 8), np.float32)
+        lo = np.array([-1.0, 2.0, 0.5])
+        h = 0.37
+        ext = np.asarray(dims) * h
+        parts[:, :3] = (lo - 0.1 * ext + rng.random((n, 3)) * 1.2 * ext).astype(np.float32)
+        parts[:, 3:] = rng.standard_normal((n, 5)).astype(np.float32)
+        wl = W.Workload("ragged", parts, lo.astype(np.float32), np.float32(h), np.asarray(dims, np.uint32))
+        ref = orc.grid_build(wl.particles, wl.origin, wl.cell_size, wl.dims)
+        for mode in MODES:
+            assert_parity(wl, run_gpu(ugp, wl, mode), ref, mode)
+
+
+def test_special_values(ugp, orc):
+    rng = np.random.Generator(np.random.PCG64(8))
+    n = 5000
+    parts = rng.standard_normal((n, 8)).astype(np.float32) * 4
+    specials = np.array([np.nan, np.inf, -np.inf, -0.0, 0.0, 3.0e38, -3.0e38, 1e-40, -1e-40], np.float32)
+    mask = rng.random((n, 3)) < 0.2
+    parts[:, :3][mask] = rng.choice(specials, int(mask.sum()))
+    # NaN payloads in the passenger fields must be copied bit for bit
+    parts.view(np.uint32)[:, 5] = 0x7FC0_1234
+    wl = W.Workload("special", parts, np.array([-3, -2, -1], np.float32), np.float32(0.5),
+                    np.array([12, 9, 7], np.uint32))
+    ref = orc.grid_build(wl.particles, wl.origin, wl.cell_size, wl.dims)
+    for mode in MODES:
+        assert_parity(wl, run_gpu(ugp, wl, mode), ref, mode)
+
+
+def test_worked_example(ugp, orc):
+    g = pins.load_golden("worked_example_scan.json")
+    wl = W.make_worked_example(g["conteos"], seed=7)
+    got = run_gpu(ugp, wl, "stable")
+    assert got.conteos.tolist() == g["conteos"]
+    assert got.inicios.tolist() == g["inicios_with_total_slot"]
+    ref = orc.grid_build(wl.particles, wl.origin, wl.cell_size, wl.dims)
+    assert_parity(wl, got, ref, "stable")
+
+
+def test_empty_and_tiny_inputs(ugp, orc):
+    for n, dims in ((0, (3, 2, 1)), (1, (4, 4, 4)), (1, (1, 1, 1)), (2, (1, 1, 1)), (17, (2, 2, 2))):
+        rng = np.random.Generator(np.random.PCG64(n))
+        parts = (rng.random((n, 8)) * 2).astype(np.float32)
+        wl = W.Workload("small", parts, np.zeros(3, np.float32), np.float32(0.5), np.asarray(dims, np.uint32))
+        ref = orc.grid_build(wl.particles, wl.origin, wl.cell_size, wl.dims)
+        for mode in MODES:
+            got = run_gpu(ugp, wl, mode)
+            assert np.array_equal(got.conteos, ref.conteos) and np.array_equal(got.inicios, ref.inicios)
+            if n:
+                assert_parity(wl, got, ref, mode)
+
+
+@pytest.mark.parametrize("n", [16, 17, 5000, 16384, 16385, 40000])
+def test_one_cell_holds_everything(ugp, orc, n):
+    """C = 1: every particle in one cell; long-cell sort paths in stable mode
+    (registers, LDS bitonic, and the ordered compaction beyond 16384)."""
+    rng = np.random.Generator(np.random.PCG64(n))
+    parts = rng.standard_normal((n, 8)).astype(np.float32)
+    wl = W.Workload("one_cell", parts, np.zeros(3, np.float32), np.float32(1.0), np.array([1, 1, 1], np.uint32))
+    ref = orc.grid_build(wl.particles, wl.origin, wl.cell_size, wl.dims)
+    for mode in MODES:
+        assert_parity(wl, run_gpu(ugp, wl, mode), ref, mode)
+
+
+def test_run_to_run(ugp):
+    wl = W.make_config("contention")
+    a1, a2 = run_gpu(ugp, wl, "atomic"), run_gpu(ugp, wl, "atomic")
+    assert np.array_equal(a1.celdaDe, a2.celdaDe) and np.array_equal(a1.inicios, a2.inicios)
+    for ga in (a1, a2):
+        c = ga.celdaDe[ga.ordenado].astype(np.int64)
+        assert np.array_equal(np.sort(c), c)  # grouped identically; order inside cells may differ
+    s1, s2 = run_gpu(ugp, wl, "stable"), run_gpu(ugp, wl, "stable")
+    assert np.array_equal(s1.ordenado, s2.ordenado)
+    assert np.array_equal(s1.reordered.view(np.uint32), s2.reordered.view(np.uint32))
+
+
+def test_stages_equal_full_build(ugp, orc):
+    """Running the stages one by one is the full build."""
+    wl = W.make_config("sparse")
+    ref = orc.grid_build(wl.particles, wl.origin, wl.cell_size, wl.dims)
+    dev = torch.device("cuda:0")
+    parts = torch.from_numpy(wl.particles).to(dev)
+    for flags, mode in ((0, "atomic"), (ugp.FLAG_GATHER, "gather"), (ugp.FLAG_STABLE, "stable")):
+        out, ws = ugp.alloc_outputs(wl.n, wl.dims.tolist(), dev, flags)
+        for st in range(ugp.NUM_STAGES):
+            ugp.grid_build_stage(st, parts, wl.origin.tolist(), float(wl.cell_size), wl.dims.tolist(), out, ws,
+                                 flags=flags)
+        torch.cuda.synchronize()
+        got = oracle.GridIndex(_u32(out.celdaDe), _u32(out.conteos), _u32(out.inicios), _u32(out.ordenado),
+                               out.reordered.cpu().numpy())
+        assert_parity(wl, got, ref, mode)
+
+
+def test_reuse_buffers_and_workspace(ugp, orc):
+    """Outputs and workspace holding stale data from a previous, larger call."""
+    dev = torch.device("cuda:0")
+    big = W.make_config("baseline")
+    small = W.make_uniform(70_001, 128, seed=31)
+    out, ws = ugp.alloc_outputs(big.n, big.dims.tolist(), dev, ugp.FLAG_STABLE)
+    for wl in (big, small, big):
+        parts = torch.from_numpy(wl.particles).to(dev)
+        ugp.grid_build(parts, wl.origin.tolist(), float(wl.cell_size), wl.dims.tolist(), stable=True, out=out,
+                       workspace=ws)
+        torch.cuda.synchronize()
+        got = oracle.GridIndex(_u32(out.celdaDe)[: wl.n], _u32(out.conteos), _u32(out.inicios),
+                               _u32(out.ordenado)[: wl.n], out.reordered.cpu().numpy()[: wl.n])
+        ref = orc.grid_build(wl.particles, wl.origin, wl.cell_size, wl.dims)
+        assert_parity(wl, got, ref, "stable")
+
+
+# ---------------------------------------------------------------------------
+# Stand-alone scan and reorder entry points
+# ---------------------------------------------------------------------------
+
+def test_scan_worked_example(ugp, orc):
+    g = pins.load_golden("worked_example_scan.json")
+    x = torch.tensor(g["conteos"], dtype=torch.int32, device="cuda:0")
+    out = _u32(ugp.exclusive_scan_u32(x))
+    assert out.tolist() == g["inicios_with_total_slot"]
+
+
+@pytest.mark.parametrize("count", [0, 1, 2, 15, 16, 17, 4095, 4096, 4097, 1 << 21, (1 << 21) + 1, (1 << 24) + 3])
+def test_scan_sizes(ugp, orc, count):
+    rng = np.random.Generator(np.random.PCG64(count + 1))
+    hi = max(1, min(1000, (1 << 31) // max(count, 1)))
+    x = rng.integers(0, hi, count).astype(np.uint32)
+    got = _u32(ugp.exclusive_scan_u32(torch.from_numpy(x.view(np.int32)).to("cuda:0")))
+    assert np.array_equal(got, orc.exclusive_scan(x))
+
+
+def test_reorder_entry_point(ugp, orc):
+    rng = np.random.Generator(np.random.PCG64(77))
+    n = 123_457
+    src = rng.standard_normal((n, 8)).astype(np.float32)
+    idx = rng.permutation(n).astype(np.uint32)
+    got = ugp.reorder(torch.from_numpy(src).to("cuda:0"), torch.from_numpy(idx.view(np.int32)).to("cuda:0"))
+    assert np.array_equal(got.cpu().numpy().view(np.uint32), orc.reorder(src, idx).view(np.uint32))
+    # out-of-range indices are skipped, the rest still written
+    idx2 = idx.copy()
+    idx2[::7] = n + 5
+    dst = torch.zeros((n, 8), dtype=torch.float32, device="cuda:0")
+    ugp.reorder(torch.from_numpy(src).to("cuda:0"), torch.from_numpy(idx2.view(np.int32)).to("cuda:0"), out=dst)
+    d = dst.cpu().numpy()
+    ok = idx2 < n
+    assert np.array_equal(d[ok].view(np.uint32), src[idx2[ok]].view(np.uint32))
+    assert np.all(d[~ok] == 0)
+
+
+def test_gpu_validation_errors(ugp):
+    dev = torch.device("cuda:0")
+    wl = W.make_config("tiny")
+    parts = torch.from_numpy(wl.particles).to(dev)
+    out, ws = ugp.alloc_outputs(wl.n, wl.dims.tolist(), dev)
+    args = (wl.origin.tolist(), float(wl.cell_size), wl.dims.tolist())
+    with pytest.raises(ugp.UGPError) as e:
+        ugp.grid_build(parts, *args, out=out, workspace=ws[:64])
+    assert e.value.status == ugp.UGP_ERR_WORKSPACE
+    bad = ugp.GridIndex(out.celdaDe, out.conteos, out.inicios, out.ordenado, parts)  # reordered aliases particles
+    with pytest.raises(ugp.UGPError) as e:
+        ugp.grid_build(parts, *args, out=bad, workspace=ws)
+    assert e.value.status == ugp.UGP_ERR_ALIAS
+    flat = torch.empty(wl.cells + 2, dtype=torch.int32, device=dev)
+    mis = ugp.GridIndex(out.celdaDe, flat[1:], out.inicios, out.ordenado, out.reordered)  # 4-byte offset
+    with pytest.raises(ugp.UGPError) as e:
+        ugp.grid_build(parts, *args, out=mis, workspace=ws)
+    assert e.value.status == ugp.UGP_ERR_ALIGN
+    with pytest.raises(ugp.UGPError) as e:
+        ugp.grid_build(parts, wl.origin.tolist(), 0.0, wl.dims.tolist(), out=out, workspace=ws)
+    assert e.value.status == ugp.UGP_ERR_ARG
+    with pytest.raises(ValueError):
+        ugp.grid_build(torch.from_numpy(wl.particles), *args)  # CPU tensor: no CPU path

@@ -1,0 +1,269 @@
+"""Uniform-grid particle index build on MI355X: Python binding of libugp.so.
+
+Argument marshalling only. Every step of the build runs in the HIP
+kernels of ``csrc/ugp.hip`` behind the C ABI of ``include/ugp.h``; PyTorch
+supplies device memory and the current stream. There is no CPU fallback:
+if the library is not built, or the tensors are not on a GPU, the calls
+raise.
+
+The names follow the C ABI (``grid_build`` is ``ugp_grid_build``, etc.).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libugp.so")
+
+UGP_OK = 0
+UGP_ERR_NULL = -1
+UGP_ERR_ARG = -2
+UGP_ERR_RANGE = -3
+UGP_ERR_ALIAS = -4
+UGP_ERR_ALIGN = -5
+UGP_ERR_WORKSPACE = -6
+UGP_ERR_HIP = -7
+
+FLAG_STABLE = 0x1
+FLAG_GATHER = 0x2
+
+STAGE_CLEAR = 0
+STAGE_COUNT = 1
+STAGE_SCAN = 2
+STAGE_SCATTER = 3
+STAGE_SORT_CELLS = 4
+STAGE_GATHER = 5
+NUM_STAGES = 6
+STAGE_NAMES = ("clear", "count", "scan", "scatter", "sort_cells", "gather")
+
+_vp = ctypes.c_void_p
+_u32 = ctypes.c_uint32
+_u32_3 = _u32 * 3
+_f32_3 = ctypes.c_float * 3
+
+_lib = None
+
+
+class UGPError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def load_library():
+    """Load libugp.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"HIP library not built: {LIB_PATH} is missing "
+            "(run `python -c 'import __graft_entry__ as g; g.build()'` first)"
+        )
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.ugp_abi_version.restype = ctypes.c_int
+    lib.ugp_abi_version.argtypes = []
+    lib.ugp_status_string.restype = ctypes.c_char_p
+    lib.ugp_status_string.argtypes = [ctypes.c_int]
+    lib.ugp_grid_workspace_bytes.restype = ctypes.c_int
+    lib.ugp_grid_workspace_bytes.argtypes = [_u32, ctypes.POINTER(_u32), _u32, ctypes.POINTER(ctypes.c_size_t)]
+    build_args = [_vp, _u32, ctypes.POINTER(ctypes.c_float), ctypes.c_float, ctypes.POINTER(_u32),
+                  _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _u32, _vp]
+    lib.ugp_grid_build.restype = ctypes.c_int
+    lib.ugp_grid_build.argtypes = build_args
+    lib.ugp_grid_build_stage.restype = ctypes.c_int
+    lib.ugp_grid_build_stage.argtypes = [_u32, *build_args]
+    lib.ugp_scan_workspace_bytes.restype = ctypes.c_int
+    lib.ugp_scan_workspace_bytes.argtypes = [_u32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.ugp_exclusive_scan_u32.restype = ctypes.c_int
+    lib.ugp_exclusive_scan_u32.argtypes = [_vp, _u32, _vp, _vp, ctypes.c_size_t, _vp]
+    lib.ugp_reorder.restype = ctypes.c_int
+    lib.ugp_reorder.argtypes = [_vp, _u32, _vp, _u32, _vp, _vp]
+    if lib.ugp_abi_version() != 1:
+        raise RuntimeError("libugp.so ABI version mismatch")
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().ugp_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != UGP_OK:
+        raise UGPError(status, where)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(device: torch.device, stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _require_gpu(t: torch.Tensor, name: str, dtype: torch.dtype):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (no CPU path exists)")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _dims3(dims) -> tuple[int, int, int]:
+    d = tuple(int(v) for v in dims)
+    if len(d) != 3:
+        raise ValueError("dims must have 3 entries")
+    return d
+
+
+def workspace_bytes(n: int, dims: Sequence[int], flags: int = 0) -> int:
+    lib = load_library()
+    d = _u32_3(*_dims3(dims))
+    out = ctypes.c_size_t(0)
+    _check(lib.ugp_grid_workspace_bytes(int(n), d, int(flags), ctypes.byref(out)), "ugp_grid_workspace_bytes")
+    return int(out.value)
+
+
+@dataclass
+class GridIndex:
+    """Outputs of one build (all GPU tensors)."""
+
+    celdaDe: torch.Tensor  # (N,) int32 storage of u32 cell indices
+    conteos: torch.Tensor  # (C,) u32 histogram
+    inicios: torch.Tensor  # (C+1,) u32 starts, inicios[C] = N
+    ordenado: torch.Tensor  # (N,) u32 particle indices grouped by cell
+    reordered: torch.Tensor  # (N, 8) float32 records in cell order
+
+
+def alloc_outputs(n: int, dims: Sequence[int], device, flags: int = 0):
+    """Output tensors and the workspace for one build (torch allocations)."""
+    d = _dims3(dims)
+    cells = d[0] * d[1] * d[2]
+    dev = torch.device(device)
+    out = GridIndex(
+        celdaDe=torch.empty(n, dtype=torch.int32, device=dev),
+        conteos=torch.empty(cells, dtype=torch.int32, device=dev),
+        inicios=torch.empty(cells + 1, dtype=torch.int32, device=dev),
+        ordenado=torch.empty(n, dtype=torch.int32, device=dev),
+        reordered=torch.empty((n, 8), dtype=torch.float32, device=dev),
+    )
+    ws = torch.empty(max(workspace_bytes(n, d, flags), 256), dtype=torch.uint8, device=dev)
+    return out, ws
+
+
+def _build_args(particles, origin, cell_size, dims, out: GridIndex, workspace, flags, stream):
+    _require_gpu(particles, "particles", torch.float32)
+    if particles.dim() != 2 or particles.shape[1] != 8:
+        raise ValueError("particles must have shape (N, 8) (32-byte records)")
+    n = int(particles.shape[0])
+    d = _dims3(dims)
+    for name in ("celdaDe", "conteos", "inicios", "ordenado"):
+        _require_gpu(getattr(out, name), name, torch.int32)
+    _require_gpu(out.reordered, "reordered", torch.float32)
+    _require_gpu(workspace, "workspace", torch.uint8)
+    cells = d[0] * d[1] * d[2]
+    if out.celdaDe.numel() < n or out.ordenado.numel() < n or out.reordered.numel() < 8 * n:
+        raise ValueError("per-particle outputs are smaller than N")
+    if out.conteos.numel() < cells or out.inicios.numel() < cells + 1:
+        raise ValueError("per-cell outputs are smaller than the cell count")
+    o = _f32_3(*[float(v) for v in origin])
+    return [
+        _ptr(particles), n, o, ctypes.c_float(float(cell_size)), _u32_3(*d),
+        _ptr(out.celdaDe), _ptr(out.conteos), _ptr(out.inicios), _ptr(out.ordenado),
+        _ptr(out.reordered), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
+        int(flags), _stream_handle(particles.device, stream),
+    ]
+
+
+def grid_build(
+    particles: torch.Tensor,
+    origin: Sequence[float],
+    cell_size: float,
+    dims: Sequence[int],
+    *,
+    stable: bool = False,
+    gather: bool = False,
+    out: Optional[GridIndex] = None,
+    workspace: Optional[torch.Tensor] = None,
+    stream=None,
+) -> GridIndex:
+    """ugp_grid_build on torch tensors; enqueued on the current stream."""
+    lib = load_library()
+    flags = (FLAG_STABLE if stable else 0) | (FLAG_GATHER if gather else 0)
+    n = int(particles.shape[0])
+    if out is None or workspace is None:
+        o2, w2 = alloc_outputs(n, dims, particles.device, flags)
+        out = out or o2
+        workspace = workspace if workspace is not None else w2
+    args = _build_args(particles, origin, cell_size, dims, out, workspace, flags, stream)
+    _check(lib.ugp_grid_build(*args), "ugp_grid_build")
+    return out
+
+
+def grid_build_stage(stage: int, particles, origin, cell_size, dims, out: GridIndex, workspace,
+                     *, flags: int = 0, stream=None) -> None:
+    """ugp_grid_build_stage: enqueue one stage with the same arguments."""
+    lib = load_library()
+    args = _build_args(particles, origin, cell_size, dims, out, workspace, flags, stream)
+    _check(lib.ugp_grid_build_stage(int(stage), *args), f"ugp_grid_build_stage({stage})")
+
+
+def exclusive_scan_u32(x: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """ugp_exclusive_scan_u32: out[0..n] with out[n] = total (mod 2^32)."""
+    lib = load_library()
+    _require_gpu(x, "x", torch.int32)
+    n = int(x.numel())
+    if out is None:
+        out = torch.empty(n + 1, dtype=torch.int32, device=x.device)
+    _require_gpu(out, "out", torch.int32)
+    if out.numel() < n + 1:
+        raise ValueError("out needs n+1 entries")
+    need = ctypes.c_size_t(0)
+    _check(lib.ugp_scan_workspace_bytes(n, ctypes.byref(need)), "ugp_scan_workspace_bytes")
+    ws = torch.empty(max(int(need.value), 256), dtype=torch.uint8, device=x.device)
+    st = lib.ugp_exclusive_scan_u32(_ptr(x), n, _ptr(out), _ptr(ws), ctypes.c_size_t(ws.numel()),
+                                    _stream_handle(x.device, stream))
+    _check(st, "ugp_exclusive_scan_u32")
+    return out
+
+
+def reorder(src: torch.Tensor, idx: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """ugp_reorder: out[k] = src[idx[k]] (32-byte records, bit for bit)."""
+    lib = load_library()
+    _require_gpu(src, "src", torch.float32)
+    _require_gpu(idx, "idx", torch.int32)
+    if src.dim() != 2 or src.shape[1] != 8:
+        raise ValueError("src must have shape (N, 8)")
+    n = int(idx.numel())
+    if out is None:
+        out = torch.empty((n, 8), dtype=torch.float32, device=src.device)
+    _require_gpu(out, "out", torch.float32)
+    st = lib.ugp_reorder(_ptr(src), int(src.shape[0]), _ptr(idx), n, _ptr(out), _stream_handle(src.device, stream))
+    _check(st, "ugp_reorder")
+    return out
+
+
+def as_u32_numpy(t: torch.Tensor):
+    """Copy a u32-in-int32 GPU tensor to a NumPy uint32 array."""
+    return t.detach().cpu().numpy().view("uint32")
+
+
+__all__ = [
+    "GridIndex", "UGPError", "alloc_outputs", "as_u32_numpy", "exclusive_scan_u32", "grid_build",
+    "grid_build_stage", "library_path", "load_library", "reorder", "status_string", "workspace_bytes",
+    "FLAG_STABLE", "FLAG_GATHER", "STAGE_NAMES", "NUM_STAGES",
+]
