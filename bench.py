@@ -1,0 +1,313 @@
+"""Benchmark of the uniform-grid index build on one MI355X.
+
+One step = one full build (cell keys and histogram, prefix sums, scatter
+of particle indices, record reorder) over the Baseline workload: 1,000,000 uniform particles on 128^3 cells,
+32-byte records, resident in HBM before timing starts.
+
+Headline timing is cold: before every step a 1 GiB read-only pass evicts
+the L2s and the 256 MiB Infinity Cache with clean lines (a write-based
+flush would leave dirty lines whose write-back the next step would pay);
+the flush sits outside the HIP events that bracket each step, and ms_per_step is the mean of the K per-step event
+times. A warm figure (K back-to-back builds between one event pair) is
+reported separately; at this size the whole working set fits in the
+Infinity Cache, so warm numbers can exceed what HBM alone allows.
+
+Per-stage durations come from HIP events (torch events on the stream the
+kernels are launched on) that the library records around one stage slot
+inside a full cold build (one C call, so no host work separates stages),
+K builds per slot; the stage with the longest mean duration is the
+dominant kernel whose algorithmic bytes / duration is the roofline figure.
+
+Prints ONE JSON line on stdout.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth, GB/s
+METRIC = "grid-build particles/s (count+scan+scatter+reorder) and % of HBM peak, 1M@128^3"
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_baseline_1M_128.txt")
+KERNEL_DIR = os.path.join(ROOT, "uniform_grid_particle_amd", "csrc")
+
+WORKLOAD_NAMES = {
+    "tiny": "Tiny: 4,096 uniform particles on 16^3 cells",
+    "sparse": "Sparse: 100,000 uniform particles on 128^3 cells",
+    "baseline": "Baseline: 1,000,000 uniform particles on 128^3 cells",
+    "contention": "Contention/clamp: 1,000,000 particles on 128^3 cells, one 10,000-particle cell, 4 clusters, 5% outside",
+    "large": "Large SPH-like: 16,777,216 uniform particles on 256^3 cells",
+}
+
+
+def alg_bytes(n: int, c: int, mode: str) -> dict:
+    """Bytes each kernel must move by design, each logical array counted once
+    per kernel that touches it (32 B per record, 4 B per u32, 8 B per
+    (cell, index) pair). The small per-block tile matrix of the tiled path
+    is left out; tile_scan moves only that matrix and gets no figure.
+
+    The end-to-end figure uses the fixed model of the four page steps
+    instead: 116 N + 16 C + 4 (see hbm_frac_e2e)."""
+    move = mode == "atomic"
+    return {
+        # staged path (cells <= 2^22, n <= 2^21)
+        "chunk_sort": 72 * n,  # record read, celdaDe, chunk records + indices written
+        "tile_sort": (36 * n + 4 * c + 4 * (c + 1) + 4 * n + (32 * n if move else 0)),
+        # tiled path (cells <= 2^24)
+        "keys": 36 * n,  # record read + celdaDe write
+        "tile_scan": None,
+        "bucket": 12 * n,  # celdaDe read + pair write
+        "cells": (8 * n + 4 * c + 4 * (c + 1) + 4 * n + (64 * n if move else 0)),
+        # direct path (larger grids)
+        "clear": 4 * c,
+        "count": 36 * n,
+        "scan": 12 * c + 4,
+        "scatter": 80 * n if move else 12 * n,
+        # optional passes
+        "stable_sort": 4 * (c + 1) + 8 * n,
+        "gather": 68 * n,
+    }
+
+
+def source_digest() -> str:
+    """Digest of every kernel source file (traffic figures go stale with it)."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(KERNEL_DIR)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(KERNEL_DIR, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel: str):
+    """Measured HBM bytes per dispatch of `kernel`, from the committed counter
+    summary, or None when absent or taken on a different kernel source."""
+    if not os.path.exists(PROFILE_TRAFFIC):
+        return None
+    vals = {}
+    with open(PROFILE_TRAFFIC, encoding="utf-8") as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_sha256_16") != source_digest():
+        return None
+    key = f"{kernel}_bytes_per_dispatch"
+    return float(vals[key]) if key in vals else None
+
+
+def cpu_baseline(wl, budget_s: float):
+    """The oracle as it stands, single-threaded, on the same workload."""
+    import oracle
+
+    orc = oracle.load()
+    times = []
+    t_end = time.perf_counter() + budget_s
+    while True:
+        t0 = time.perf_counter()
+        orc.grid_build(wl.particles, wl.origin, wl.cell_size, wl.dims)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() >= t_end and len(times) >= 3:
+            break
+    med = statistics.median(times)
+    return {
+        "value": wl.n / med,
+        "unit": "particles/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"full {wl.name} build ({wl.n} particles, {wl.cells} cells) repeated {len(times)}x, "
+                  f"median {med * 1e3:.1f} ms; single-threaded C oracle",
+        "host_cpu": _cpu_model(),
+        "host_threads": os.cpu_count(),
+    }
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="baseline", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--mode", default="atomic", choices=["atomic", "gather", "stable"])
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle timing (0 = skip)")
+    ap.add_argument("--copy-reference", action="store_true",
+                    help="also run a 256 MiB device copy (counter calibration for rocprofv3 --pmc)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the index build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import uniform_grid_particle_amd as ugp
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    ugp.load_library()
+
+    wl = workloads.make_config(args.workload)
+    n, dims, cells = wl.n, [int(v) for v in wl.dims], wl.cells
+    origin, h = [float(v) for v in wl.origin], float(wl.cell_size)
+    flags = {"atomic": 0, "gather": ugp.FLAG_GATHER, "stable": ugp.FLAG_STABLE}[args.mode]
+    parts = torch.from_numpy(wl.particles).to(dev)
+    out, ws = ugp.alloc_outputs(n, dims, dev, flags)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB, read to evict caches
+
+    def evict():
+        torch.sum(flush)
+    stream = torch.cuda.current_stream(dev)
+
+    def build():
+        ugp.grid_build(parts, origin, h, dims, stable=args.mode == "stable", gather=args.mode == "gather",
+                       out=out, workspace=ws)
+
+    for _ in range(args.warmup):
+        build()
+    torch.cuda.synchronize()
+    # light self-check of the warm-up output (full parity lives in the tests)
+    ini = ugp.as_u32_numpy(out.inicios)
+    if int(ini[-1]) != n or int(ugp.as_u32_numpy(out.conteos).sum(dtype=np.uint64)) != n:
+        print("bench self-check failed: inicios[C] or sum(conteos) != N", file=sys.stderr)
+        return 1
+
+    if args.copy_reference:
+        a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    # ---- headline: K cold steps, each bracketed by events ----
+    K = args.steps
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for k in range(K):
+        evict()
+        starts[k].record(stream)
+        build()
+        ends[k].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = [starts[k].elapsed_time(ends[k]) for k in range(K)]
+    ms_per_step = sum(step_ms) / K
+
+    # ---- warm: K back-to-back builds between one event pair ----
+    w0 = torch.cuda.Event(enable_timing=True)
+    w1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0.record(stream)
+    for _ in range(K):
+        build()
+    w1.record(stream)
+    torch.cuda.synchronize()
+    warm_ms = w0.elapsed_time(w1) / K
+
+    # ---- per-stage: for every stage slot, K cold steps of the full build with
+    # two events recorded around that slot inside the same C call ----
+    names = ugp.stage_names(n, dims, flags)
+    bytes_k = alg_bytes(n, cells, args.mode)
+    stages = {}
+    for st, name in enumerate(names):
+        if name is None:
+            continue
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+        torch.cuda.synchronize()
+        for k in range(K):
+            evict()
+            ugp.grid_build_timed(st, evs[k][0], evs[k][1], parts, origin, h, dims, out, ws, flags=flags)
+        torch.cuda.synchronize()
+        us = 1e3 * sum(e0.elapsed_time(e1) for e0, e1 in evs) / K
+        b = bytes_k.get(name)
+        gbs = (b / (us * 1e3)) if (b and us > 0) else None
+        stages[name] = {"slot": st, "us": round(us, 3), "alg_bytes": b,
+                        "GBps": None if gbs is None else round(gbs, 1),
+                        "frac_hbm": None if gbs is None else round(gbs / HBM_PEAK_GBS, 4)}
+
+    b_total = 116 * n + 16 * cells + 4
+    dominant = max((s for s in stages if stages[s]["GBps"] is not None), key=lambda s: stages[s]["us"])
+    dom = stages[dominant]
+    achieved = dom["GBps"]
+    traffic = read_traffic(dominant)
+
+    t_s = ms_per_step * 1e-3
+    result = {
+        "metric": METRIC,
+        "value": n / t_s,
+        "unit": "particles/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": WORKLOAD_NAMES[args.workload],
+            "n_particles": n,
+            "dims": dims,
+            "cells": cells,
+            "cell_size": h,
+            "seed": wl.seed,
+            "mode": args.mode,
+            "timing": "cold: 1 GiB read-only cache eviction before each step, outside the per-step HIP events",
+        },
+        "hbm_frac_e2e": (b_total / t_s) / (HBM_PEAK_GBS * 1e9),
+        "alg_bytes_per_step": b_total,
+        "step_ms_median": statistics.median(step_ms),
+        "step_ms_p10_p90": [float(np.percentile(step_ms, 10)), float(np.percentile(step_ms, 90))],
+        "warm_ms_per_step": warm_ms,
+        "warm_note": "back-to-back builds; the working set can stay in the 256 MiB Infinity Cache",
+        "stages": stages,
+        "stage_sum_us": round(sum(s["us"] for s in stages.values()), 3),
+        "stage_note": "each stage timed alone inside a full cold build (events recorded around it in the same C call)",
+        "wall_s_timed_loop": wall,
+        "roofline": {
+            "kernel": dominant,
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": None if achieved is None else achieved / HBM_PEAK_GBS,
+            "traffic": traffic,
+        },
+    }
+    if args.cpu_budget > 0 and int(os.environ.get("RANK", "0")) == 0:
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

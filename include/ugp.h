@@ -68,7 +68,7 @@ typedef struct ugp_particle {
 /* Status codes. */
 #define UGP_OK 0
 #define UGP_ERR_NULL (-1)      /* a required pointer is NULL */
-#define UGP_ERR_ARG (-2)       /* cell_size not finite or <= 0, origin not finite, unknown flag or stage */
+#define UGP_ERR_ARG (-2)       /* cell_size not a finite normal positive float, origin not finite, unknown flag, stage or event */
 #define UGP_ERR_RANGE (-3)     /* a dim is 0 or > 2^24, or the cell count exceeds 2^32-2 */
 #define UGP_ERR_ALIAS (-4)     /* two buffers overlap */
 #define UGP_ERR_ALIGN (-5)     /* an array is not 16-byte aligned, or the workspace not 256-byte aligned */
@@ -87,13 +87,21 @@ typedef struct ugp_particle {
  * result is identical; this only selects the kernel schedule. */
 #define UGP_FLAG_GATHER 0x2u
 
-/* Pipeline stages, for ugp_grid_build_stage(). */
-#define UGP_STAGE_CLEAR 0u      /* zero conteos and the per-tile partial sums */
-#define UGP_STAGE_COUNT 1u      /* cell keys -> celdaDe, histogram -> conteos */
-#define UGP_STAGE_SCAN 2u       /* conteos -> inicios[cells+1], cursor init */
-#define UGP_STAGE_SCATTER 3u    /* cursor -> ordenado (and reordered unless GATHER/STABLE) */
-#define UGP_STAGE_SORT_CELLS 4u /* STABLE only: sort each cell's slice of ordenado */
-#define UGP_STAGE_GATHER 5u     /* GATHER or STABLE only: reordered[k] = particles[ordenado[k]] */
+/* Pipeline stage slots, for ugp_grid_build_stage() / ugp_grid_build_timed().
+ * The library picks one of three execution paths from n and the grid size;
+ * each path fills the six slots with its own kernels, named by
+ * ugp_grid_stage_name():
+ *   n == 0            slot 0 "clear" (zero conteos and inicios); others empty
+ *   cells <= 2^22 and n <= 2^21
+ *                     "chunk_sort", -, -, "tile_sort" -- two kernels, no
+ *                     global atomics, records moved through LDS
+ *   other cells <= 2^24
+ *                     "keys", "tile_scan", "bucket", "cells"  -- a two-level
+ *                     counting sort with LDS histograms and no global atomics
+ *   cells >  2^24     "clear", "count", "scan", "scatter"     -- one global
+ *                     atomic per particle in count and in scatter
+ *   slot 4 "stable_sort" (UGP_FLAG_STABLE only), slot 5 "gather"
+ *   (UGP_FLAG_GATHER or UGP_FLAG_STABLE only). */
 #define UGP_NUM_STAGES 6u
 
 /* Bytes of device workspace ugp_grid_build() needs for n particles on a
@@ -108,7 +116,8 @@ int ugp_grid_workspace_bytes(uint32_t n, const uint32_t dims[3], uint32_t flags,
  *   n           number of particles (0 is valid: conteos and inicios are
  *               zeroed and nothing else is written)
  *   origin      host, in:    3 floats, lower corner of cell (0,0,0)
- *   cell_size   edge length of a cubic cell, finite and > 0
+ *   cell_size   edge length of a cubic cell: finite, positive and normal
+ *               (>= FLT_MIN)
  *   dims        host, in:    cells per axis, each in [1, 2^24]; the cell
  *               count C = dims[0]*dims[1]*dims[2] must be <= 2^32-2
  *   celdaDe     device, out: n u32, cell index of each particle
@@ -135,8 +144,8 @@ int ugp_grid_build(const ugp_particle *particles, uint32_t n, const float origin
                    uint32_t *inicios, uint32_t *ordenado, ugp_particle *reordered, void *workspace,
                    size_t workspace_bytes, uint32_t flags, void *stream);
 
-/* Enqueue one stage (UGP_STAGE_*) of ugp_grid_build() with the same
- * arguments. Running the stages 0..UGP_NUM_STAGES-1 in order on one stream
+/* Enqueue one stage slot (0..UGP_NUM_STAGES-1) of ugp_grid_build() with the
+ * same arguments. Running the slots 0..UGP_NUM_STAGES-1 in order on one stream
  * is exactly ugp_grid_build(); a stage that does not apply to `flags`
  * returns UGP_OK and enqueues nothing. Each stage reads what the previous
  * ones left in the outputs and the workspace, so stages must run in order
@@ -146,6 +155,23 @@ int ugp_grid_build_stage(uint32_t stage, const ugp_particle *particles, uint32_t
                          uint32_t *celdaDe, uint32_t *conteos, uint32_t *inicios,
                          uint32_t *ordenado, ugp_particle *reordered, void *workspace,
                          size_t workspace_bytes, uint32_t flags, void *stream);
+
+/* ugp_grid_build() with two caller-owned HIP events (hipEvent_t passed as
+ * void*) recorded on `stream` immediately before and after stage slot
+ * `timed_stage`, in the same call, so no host work separates the stages.
+ * Returns UGP_ERR_ARG for a bad slot or a NULL event; otherwise as
+ * ugp_grid_build(). Intended for per-kernel timing. */
+int ugp_grid_build_timed(const ugp_particle *particles, uint32_t n, const float origin[3],
+                         float cell_size, const uint32_t dims[3], uint32_t *celdaDe,
+                         uint32_t *conteos, uint32_t *inicios, uint32_t *ordenado,
+                         ugp_particle *reordered, void *workspace, size_t workspace_bytes,
+                         uint32_t flags, void *stream, uint32_t timed_stage, void *event_before,
+                         void *event_after);
+
+/* Name of stage slot `stage` for this problem shape and flags ("keys",
+ * "count", ...), or NULL when the slot runs nothing or the shape is
+ * invalid. Static storage. Pure host function. */
+const char *ugp_grid_stage_name(uint32_t n, const uint32_t dims[3], uint32_t flags, uint32_t stage);
 
 /* Bytes of device workspace ugp_exclusive_scan_u32() needs for `count`
  * elements. Pure host function. */

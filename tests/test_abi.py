@@ -89,6 +89,16 @@ def _call_build(lib, *, n=4, origin=(0.0, 0.0, 0.0), h=1.0, dims=(4, 4, 4), ptrs
     return lib.ugp_grid_build_stage(stage, *args)
 
 
+def test_stage_names(lib):
+    assert ugp.stage_names(1000, (128, 128, 128)) == ["chunk_sort", None, None, "tile_sort", None, None]
+    assert ugp.stage_names(3_000_000, (128, 128, 128)) == ["keys", "tile_scan", "bucket", "cells", None, None]
+    assert ugp.stage_names(1000, (128, 128, 128), ugp.FLAG_STABLE)[4:] == ["stable_sort", "gather"]
+    assert ugp.stage_names(1000, (128, 128, 128), ugp.FLAG_GATHER)[4:] == [None, "gather"]
+    assert ugp.stage_names(0, (128, 128, 128)) == ["clear", None, None, None, None, None]
+    assert ugp.stage_names(1000, (4096, 4097, 1))[:4] == ["clear", "count", "scan", "scatter"]
+    assert ugp.stage_names(1000, (256, 256, 256))[:4] == ["keys", "tile_scan", "bucket", "cells"]
+
+
 def test_validation_errors_on_host(lib):
     nan, inf = float("nan"), float("inf")
     assert _call_build(lib, h=0.0) == ugp.UGP_ERR_ARG
@@ -115,8 +125,14 @@ def test_validation_errors_on_host(lib):
     assert _call_build(lib, ptrs={"reordered": (1 << 40) + 16 * 4}) == ugp.UGP_ERR_ALIAS
     # inicios overlapping conteos
     assert _call_build(lib, ptrs={"inicios": (1 << 40) + (2 << 30) + 64}) == ugp.UGP_ERR_ALIAS
-    # unknown stage
+    # unknown stage; timed build without events
     assert _call_build(lib, stage=99) == ugp.UGP_ERR_ARG
+    o = (ctypes.c_float * 3)(0, 0, 0)
+    d = (ctypes.c_uint32 * 3)(4, 4, 4)
+    b = 1 << 40
+    assert lib.ugp_grid_build_timed(b, 4, o, ctypes.c_float(1.0), d, b + (1 << 30), b + (2 << 30), b + (3 << 30),
+                                    b + (4 << 30), b + (5 << 30), b + (6 << 30), ctypes.c_size_t(1 << 20), 0, None,
+                                    0, None, None) == ugp.UGP_ERR_ARG
     assert _call_build(lib, stage=0, h=0.0) == ugp.UGP_ERR_ARG
 
 

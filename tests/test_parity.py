@@ -128,6 +128,55 @@ def test_noncubic_ragged(ugp, orc):
             assert_parity(wl, run_gpu(ugp, wl, mode), ref, mode)
 
 
+@pytest.mark.parametrize("dims", [(100, 100, 100), (129, 130, 131), (160, 160, 160), (200, 200, 200),
+                                  (256, 256, 255)])
+def test_tile_sizes(ugp, orc, dims):
+    """Grids that select every tile size of the tiled path (4096..32768 cells
+    per tile), each with a ragged last tile."""
+    print(f"[parity] tile sizes dims={dims}", flush=True)
+    rng = np.random.Generator(np.random.PCG64(sum(dims)))
+    n = 300_001
+    parts = rng.standard_normal((n, 8)).astype(np.float32)
+    ext = np.asarray(dims, np.float64) * 0.05
+    parts[:, :3] = (rng.random((n, 3)) * ext * 1.02 - 0.01 * ext).astype(np.float32)
+    wl = W.Workload("tiles", parts, np.zeros(3, np.float32), np.float32(0.05), np.asarray(dims, np.uint32))
+    ref = orc.grid_build(wl.particles, wl.origin, wl.cell_size, wl.dims)
+    for mode in MODES:
+        assert_parity(wl, run_gpu(ugp, wl, mode), ref, mode)
+
+
+def test_direct_path_beyond_tiled_limit(ugp, orc):
+    """More than 2^24 cells: the global-atomic path."""
+    dims = (4096, 4097, 1)
+    assert ugp.stage_names(n := 200_003, dims)[:4] == ["clear", "count", "scan", "scatter"]
+    rng = np.random.Generator(np.random.PCG64(99))
+    parts = rng.standard_normal((n, 8)).astype(np.float32)
+    parts[:, 0] = (rng.random(n) * 4096 * 1.01 - 10).astype(np.float32)
+    parts[:, 1] = (rng.random(n) * 4097 * 1.01 - 10).astype(np.float32)
+    parts[:, 2] = (rng.random(n) * 2 - 0.5).astype(np.float32)
+    parts[: n // 10, :3] = parts[0, :3]  # one dense cell
+    wl = W.Workload("direct", parts, np.zeros(3, np.float32), np.float32(1.0), np.asarray(dims, np.uint32))
+    ref = orc.grid_build(wl.particles, wl.origin, wl.cell_size, wl.dims)
+    for mode in MODES:
+        assert_parity(wl, run_gpu(ugp, wl, mode), ref, mode)
+
+
+def test_timed_build_matches(ugp, orc):
+    wl = W.make_config("sparse")
+    ref = orc.grid_build(wl.particles, wl.origin, wl.cell_size, wl.dims)
+    dev = torch.device("cuda:0")
+    parts = torch.from_numpy(wl.particles).to(dev)
+    out, ws = ugp.alloc_outputs(wl.n, wl.dims.tolist(), dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for st in range(ugp.NUM_STAGES):
+        ugp.grid_build_timed(st, e0, e1, parts, wl.origin.tolist(), float(wl.cell_size), wl.dims.tolist(), out, ws)
+        torch.cuda.synchronize()
+        assert e0.elapsed_time(e1) >= 0.0
+    got = oracle.GridIndex(_u32(out.celdaDe), _u32(out.conteos), _u32(out.inicios), _u32(out.ordenado),
+                           out.reordered.cpu().numpy())
+    assert_parity(wl, got, ref, "atomic")
+
+
 def test_special_values(ugp, orc):
     rng = np.random.Generator(np.random.PCG64(8))
     n = 5000

@@ -33,14 +33,7 @@ UGP_ERR_HIP = -7
 FLAG_STABLE = 0x1
 FLAG_GATHER = 0x2
 
-STAGE_CLEAR = 0
-STAGE_COUNT = 1
-STAGE_SCAN = 2
-STAGE_SCATTER = 3
-STAGE_SORT_CELLS = 4
-STAGE_GATHER = 5
-NUM_STAGES = 6
-STAGE_NAMES = ("clear", "count", "scan", "scatter", "sort_cells", "gather")
+NUM_STAGES = 6  # stage slots; names depend on the path, see stage_names()
 
 _vp = ctypes.c_void_p
 _u32 = ctypes.c_uint32
@@ -83,6 +76,10 @@ def load_library():
     lib.ugp_grid_build.argtypes = build_args
     lib.ugp_grid_build_stage.restype = ctypes.c_int
     lib.ugp_grid_build_stage.argtypes = [_u32, *build_args]
+    lib.ugp_grid_build_timed.restype = ctypes.c_int
+    lib.ugp_grid_build_timed.argtypes = [*build_args, _u32, _vp, _vp]
+    lib.ugp_grid_stage_name.restype = ctypes.c_char_p
+    lib.ugp_grid_stage_name.argtypes = [_u32, ctypes.POINTER(_u32), _u32, _u32]
     lib.ugp_scan_workspace_bytes.restype = ctypes.c_int
     lib.ugp_scan_workspace_bytes.argtypes = [_u32, ctypes.POINTER(ctypes.c_size_t)]
     lib.ugp_exclusive_scan_u32.restype = ctypes.c_int
@@ -136,6 +133,17 @@ def workspace_bytes(n: int, dims: Sequence[int], flags: int = 0) -> int:
     out = ctypes.c_size_t(0)
     _check(lib.ugp_grid_workspace_bytes(int(n), d, int(flags), ctypes.byref(out)), "ugp_grid_workspace_bytes")
     return int(out.value)
+
+
+def stage_names(n: int, dims: Sequence[int], flags: int = 0) -> list:
+    """Names of the stage slots for this shape and flags (None = slot unused)."""
+    lib = load_library()
+    d = _u32_3(*_dims3(dims))
+    out = []
+    for st in range(NUM_STAGES):
+        name = lib.ugp_grid_stage_name(int(n), d, int(flags), st)
+        out.append(None if name is None else name.decode())
+    return out
 
 
 @dataclass
@@ -222,6 +230,20 @@ def grid_build_stage(stage: int, particles, origin, cell_size, dims, out: GridIn
     _check(lib.ugp_grid_build_stage(int(stage), *args), f"ugp_grid_build_stage({stage})")
 
 
+def grid_build_timed(stage: int, event_before, event_after, particles, origin, cell_size, dims,
+                     out: GridIndex, workspace, *, flags: int = 0, stream=None) -> None:
+    """ugp_grid_build_timed: full build, two torch.cuda.Event objects recorded
+    around stage slot `stage` inside the same C call."""
+    lib = load_library()
+    for ev in (event_before, event_after):
+        if not getattr(ev, "cuda_event", 0):
+            ev.record()  # torch creates the underlying event lazily
+    args = _build_args(particles, origin, cell_size, dims, out, workspace, flags, stream)
+    st = lib.ugp_grid_build_timed(*args, int(stage), ctypes.c_void_p(event_before.cuda_event),
+                                  ctypes.c_void_p(event_after.cuda_event))
+    _check(st, "ugp_grid_build_timed")
+
+
 def exclusive_scan_u32(x: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """ugp_exclusive_scan_u32: out[0..n] with out[n] = total (mod 2^32)."""
     lib = load_library()
@@ -264,6 +286,6 @@ def as_u32_numpy(t: torch.Tensor):
 
 __all__ = [
     "GridIndex", "UGPError", "alloc_outputs", "as_u32_numpy", "exclusive_scan_u32", "grid_build",
-    "grid_build_stage", "library_path", "load_library", "reorder", "status_string", "workspace_bytes",
-    "FLAG_STABLE", "FLAG_GATHER", "STAGE_NAMES", "NUM_STAGES",
+    "grid_build_stage", "grid_build_timed", "library_path", "load_library", "reorder", "stage_names",
+    "status_string", "workspace_bytes", "FLAG_STABLE", "FLAG_GATHER", "NUM_STAGES",
 ]

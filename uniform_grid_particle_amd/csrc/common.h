@@ -1,0 +1,93 @@
+// common.h -- constants and device helpers shared by the index-build kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace ugp {
+
+constexpr int kBlock = 256;     // threads of the streaming kernels (4 waves of 64)
+constexpr int kBatch = 8;       // items per thread loaded together (memory-level parallelism)
+constexpr uint32_t kMaxDim = 1u << 24;
+
+struct GridParams {
+  float ox, oy, oz;  // origin
+  float h;           // cell size
+  float tx, ty, tz;  // dims - 1 as floats (exact: dims <= 2^24)
+  uint32_t nx;       // dims[0]
+  uint32_t nxy;      // dims[0] * dims[1] (fits: cells < 2^32)
+};
+
+// Cell along one axis: binary32 subtraction, correctly rounded binary32
+// division (the library is built without fast-math, so '/' is the IEEE
+// division), floor, then clamp in the float domain before converting.
+// The lower test is false for NaN, so NaN and -inf go to 0; +inf and
+// everything past the last face go to dim-1.
+__device__ __forceinline__ uint32_t axis_cell(float p, float o, float h, float top) {
+  const float q = (p - o) / h;
+  float f = floorf(q);
+  f = (f >= 0.0f) ? f : 0.0f;
+  f = (f > top) ? top : f;
+  return static_cast<uint32_t>(f);
+}
+
+// Linear cell index x + y*nx + z*nx*ny (< cells <= 2^32-2, no wrap).
+__device__ __forceinline__ uint32_t cell_of(float x, float y, float z, const GridParams& g) {
+  const uint32_t kx = axis_cell(x, g.ox, g.h, g.tx);
+  const uint32_t ky = axis_cell(y, g.oy, g.h, g.ty);
+  const uint32_t kz = axis_cell(z, g.oz, g.h, g.tz);
+  return kx + ky * g.nx + kz * g.nxy;
+}
+
+// Inclusive prefix sum across the 64 lanes of a wave, with DPP lane moves
+// (no LDS traffic): shifts of 1, 2, 4 and 8 lanes inside each row of 16
+// give row-inclusive sums, then row 0's total is broadcast into row 1 and
+// row 2's into row 3 (row_bcast:15), then the total of rows 0-1 into rows
+// 2-3 (row_bcast:31). Lanes without a source add 0.
+__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x) {
+  constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+  constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+  x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), kRowShr1, 0xf, 0xf, false));
+  x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), kRowShr2, 0xf, 0xf, false));
+  x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), kRowShr4, 0xf, 0xf, false));
+  x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), kRowShr8, 0xf, 0xf, false));
+  x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), kRowBcast15, 0xa, 0xf, false));
+  x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), kRowBcast31, 0xc, 0xf, false));
+  return x;
+}
+
+// Exclusive scan of one value per thread across a workgroup of NT threads.
+// Returns the exclusive prefix; *total receives the workgroup sum.
+// s_wave: NT/64 words of LDS. Contains two barriers; every thread of the
+// workgroup must call it.
+template <int NT>
+__device__ __forceinline__ uint32_t block_exclusive_sum(uint32_t x, uint32_t* s_wave,
+                                                        uint32_t* total) {
+  constexpr int kWaves = NT / 64;
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const uint32_t incl = wave_inclusive_sum(x);
+  if (lane == 63) s_wave[wid] = incl;
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const uint32_t v = s_wave[w];
+    before += (w < wid) ? v : 0u;
+    all += v;
+  }
+  __syncthreads();
+  *total = all;
+  return before + incl - x;
+}
+
+// Sum of one value per thread across a workgroup (all threads get it).
+template <int NT>
+__device__ __forceinline__ uint32_t block_sum(uint32_t x, uint32_t* s_wave) {
+  uint32_t total;
+  (void)block_exclusive_sum<NT>(x, s_wave, &total);
+  return total;
+}
+
+}  // namespace ugp

@@ -1,0 +1,139 @@
+// kernels_reorder.h -- the gather reorder and the stable-order pass.
+#pragma once
+
+#include "common.h"
+
+namespace ugp {
+
+constexpr int kGatherItems = 8;      // half-records per thread in the gather
+constexpr uint32_t kSmallSort = 16;  // cells up to this length are sorted in registers
+constexpr int kSortBlock = 1024;     // threads of the long-cell sort
+constexpr uint32_t kLdsSort = 16384; // longest cell sorted in LDS (64 KiB)
+constexpr int kSortGrid = 512;       // workgroups of the long-cell sort
+
+// Gather: two lanes per record, each moving one 16-byte half, so every
+// store instruction writes a contiguous span. Indices >= n_src are skipped.
+__global__ __launch_bounds__(kBlock) void gather_kernel(const uint32_t* __restrict__ idx, uint32_t n,
+                                                        uint32_t n_src,
+                                                        const uint4* __restrict__ src,
+                                                        uint4* __restrict__ dst) {
+  constexpr uint32_t kRecPerBlock = kBlock * kGatherItems / 2;
+  const uint32_t base = blockIdx.x * kRecPerBlock;
+  const uint32_t half = threadIdx.x & 1u;
+  uint4 v[kGatherItems];
+  uint32_t r[kGatherItems];
+  bool ok[kGatherItems];
+#pragma unroll
+  for (int j = 0; j < kGatherItems; ++j) {
+    r[j] = base + j * (kBlock / 2) + (threadIdx.x >> 1);
+    const uint32_t s = idx[r[j] < n ? r[j] : n - 1u];
+    ok[j] = (r[j] < n) && (s < n_src);
+    v[j] = src[static_cast<size_t>(s < n_src ? s : n_src - 1u) * 2u + half];
+  }
+#pragma unroll
+  for (int j = 0; j < kGatherItems; ++j)
+    if (ok[j]) dst[static_cast<size_t>(r[j]) * 2u + half] = v[j];
+}
+
+// Stable mode, short cells: one thread per cell. Cells of at most 16
+// entries are sorted in registers with a bitonic network (static indices,
+// padding with 0xFFFFFFFF which no particle index reaches); longer cells
+// are appended to a list for the LDS kernel.
+__global__ __launch_bounds__(kBlock) void sort_short_cells_kernel(
+    const uint32_t* __restrict__ inicios, uint32_t cells, uint32_t n,
+    uint32_t* __restrict__ ordenado, uint32_t* __restrict__ long_list, uint32_t long_cap,
+    uint32_t* __restrict__ long_count) {
+  const uint32_t c = blockIdx.x * kBlock + threadIdx.x;
+  if (c >= cells) return;
+  const uint32_t s = inicios[c];
+  const uint32_t e = inicios[c + 1];
+  if (e > n || e <= s || e - s < 2) return;
+  const uint32_t len = e - s;
+  if (len > kSmallSort) {
+    const uint32_t k = atomicAdd(long_count, 1u);
+    if (k < long_cap) long_list[k] = c;
+    return;
+  }
+  uint32_t v[kSmallSort];
+#pragma unroll
+  for (uint32_t k = 0; k < kSmallSort; ++k) v[k] = (k < len) ? ordenado[s + k] : 0xFFFFFFFFu;
+#pragma unroll
+  for (uint32_t kk = 2; kk <= kSmallSort; kk <<= 1) {
+#pragma unroll
+    for (uint32_t j = kk >> 1; j > 0; j >>= 1) {
+#pragma unroll
+      for (uint32_t i = 0; i < kSmallSort; ++i) {
+        const uint32_t l = i ^ j;
+        if (l > i) {
+          const bool up = (i & kk) == 0;
+          const uint32_t a = v[i], b = v[l];
+          if ((a > b) == up) {
+            v[i] = b;
+            v[l] = a;
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (uint32_t k = 0; k < kSmallSort; ++k)
+    if (k < len) ordenado[s + k] = v[k];
+}
+
+// Stable mode, long cells: one workgroup per listed cell (grid-stride over
+// the list). Up to 16384 entries: bitonic sort in LDS. Longer: ordered
+// compaction, i.e. walk all particles in index order and append those of
+// this cell (the cell's membership is exact already; only order changes).
+__global__ __launch_bounds__(kSortBlock) void sort_long_cells_kernel(
+    const uint32_t* __restrict__ inicios, const uint32_t* __restrict__ celdaDe, uint32_t n,
+    const uint32_t* __restrict__ long_list, uint32_t long_cap,
+    const uint32_t* __restrict__ long_count, uint32_t* __restrict__ ordenado) {
+  __shared__ uint32_t s_keys[kLdsSort];
+  __shared__ uint32_t s_wave[kSortBlock / 64];
+  uint32_t count = *long_count;
+  if (count > long_cap) count = long_cap;
+  for (uint32_t k = blockIdx.x; k < count; k += gridDim.x) {
+    const uint32_t c = long_list[k];
+    const uint32_t s = inicios[c];
+    const uint32_t e = inicios[c + 1];
+    if (e <= s || e > n) continue;  // uniform across the workgroup
+    const uint32_t len = e - s;
+    if (len <= kLdsSort) {
+      uint32_t L = 1;
+      while (L < len) L <<= 1;
+      for (uint32_t t = threadIdx.x; t < L; t += kSortBlock)
+        s_keys[t] = (t < len) ? ordenado[s + t] : 0xFFFFFFFFu;
+      __syncthreads();
+      for (uint32_t kk = 2; kk <= L; kk <<= 1) {
+        for (uint32_t j = kk >> 1; j > 0; j >>= 1) {
+          for (uint32_t t = threadIdx.x; t < (L >> 1); t += kSortBlock) {
+            const uint32_t i = (t / j) * (2 * j) + (t % j);
+            const uint32_t l = i + j;
+            const bool up = (i & kk) == 0;
+            const uint32_t a = s_keys[i], b = s_keys[l];
+            if ((a > b) == up) {
+              s_keys[i] = b;
+              s_keys[l] = a;
+            }
+          }
+          __syncthreads();
+        }
+      }
+      for (uint32_t t = threadIdx.x; t < len; t += kSortBlock) ordenado[s + t] = s_keys[t];
+      __syncthreads();
+    } else {
+      uint32_t run = 0;
+      for (uint64_t b0 = 0; b0 < n; b0 += kSortBlock) {
+        const uint64_t i = b0 + threadIdx.x;
+        const uint32_t flag = (i < n && celdaDe[i] == c) ? 1u : 0u;
+        uint32_t total;
+        const uint32_t excl = block_exclusive_sum<kSortBlock>(flag, s_wave, &total);
+        const uint32_t dst = s + run + excl;
+        if (flag && dst < e) ordenado[dst] = static_cast<uint32_t>(i);
+        run += total;
+      }
+    }
+  }
+}
+
+}  // namespace ugp

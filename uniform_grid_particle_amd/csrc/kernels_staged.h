@@ -1,0 +1,296 @@
+// kernels_staged.h -- the two-kernel index build (grids of up to 2^22 cells
+// and up to 2^21 particles; larger problems use kernels_tiled.h).
+//
+// Measured on MI355X: a dependent kernel boundary costs about 2.6 us, a
+// device-scope global atomic is a memory-side operation (about 23 G/s for
+// the whole chip, whatever the address range), and a random 32-byte record
+// access moves a whole 128-byte cache line. So this path has two kernels,
+// no global atomics, and moves every record with coalesced accesses,
+// reordering through LDS:
+//
+//   keys   one workgroup per chunk of 4096 particles: cell key per particle
+//          (celdaDe), a counting sort of the chunk by tile in LDS (a tile is
+//          2^shift consecutive cells, at most 256 tiles), the chunk written
+//          back contiguously in tile order (records and particle indices),
+//          and one row {count, exclusive prefix} per tile for the chunk.
+//   cells  one workgroup per tile: it reads the chunk rows of its tile
+//          (how many of its particles each chunk holds, and where), sums
+//          them into its start (the tile start is the number of particles
+//          in earlier tiles), expands the runs into a per-particle source
+//          map in LDS, loads its particles run by run, counts them
+//          into an LDS histogram of its cells (conteos), scans the
+//          histogram (inicios), takes every particle's slot with an LDS
+//          atomic, and writes ordenado and reordered through an LDS staging
+//          window so the stores are contiguous. A tile with more particles
+//          than the registers hold writes its slots directly instead.
+//
+// The result is the counting sort of the pages: exact histogram, exclusive
+// scan with the total in the extra slot, every particle inside its cell's
+// range; only the order inside a cell depends on LDS atomic arrival order,
+// as with the pages' atomic cursor (page "Construir el índice de la rejilla
+// con un prefix sum", section "El orden dentro de la celda").
+#pragma once
+
+#include "common.h"
+
+namespace ugp {
+
+constexpr int kChunkThreads = 512;                 // keys workgroup
+constexpr int kChunkItems = 8;                     // particles per thread
+constexpr uint32_t kChunk = kChunkThreads * kChunkItems;  // 4096 particles per chunk
+constexpr uint32_t kStagedMaxTiles = 256;          // one workgroup round of the cells kernel
+constexpr uint32_t kStagedMinShift = 12;
+constexpr uint32_t kStagedMaxShift = 14;           // up to 16384 cells per tile (64 KiB histogram)
+constexpr uint32_t kStagedMaxChunks = 512;         // up to 2^21 particles
+constexpr int kStagedCellsThreads = 1024;          // cells workgroup
+constexpr int kStagedRegs = 8;                     // particles per thread held in registers
+constexpr uint32_t kStagedCap = kStagedCellsThreads * kStagedRegs;  // staged tile capacity (8192)
+constexpr uint32_t kStagedWin = 2048;              // LDS staging window (records)
+
+static_assert(kStagedMaxTiles <= kChunkThreads, "one tile bin per keys thread in the scan");
+static_assert(kStagedMaxChunks <= kStagedCellsThreads, "one chunk row per cells thread");
+static_assert(2 * kStagedWin * 4 >= kStagedCap, "the source map fits in the staging buffer");
+
+// keys: chunk b holds particles [b*kChunk, (b+1)*kChunk).
+// rows[b*ntiles + t] = {particles of chunk b in tile t, those in tiles < t}.
+__global__ __launch_bounds__(kChunkThreads) void staged_keys_kernel(
+    const uint4* __restrict__ parts, uint32_t n, GridParams g, uint32_t* __restrict__ celdaDe,
+    uint2* __restrict__ rows, uint32_t tile_shift, uint32_t ntiles, uint4* __restrict__ chunk_rec,
+    uint32_t* __restrict__ chunk_idx) {
+  __shared__ uint4 s_rec[2 * kChunk];  // 128 KiB: the chunk in tile order
+  __shared__ uint32_t s_idx[kChunk];   // 16 KiB
+  __shared__ uint32_t s_hist[kStagedMaxTiles];
+  __shared__ uint32_t s_wave[kChunkThreads / 64];
+
+  if (threadIdx.x < kStagedMaxTiles) s_hist[threadIdx.x] = 0u;
+  const uint32_t base = blockIdx.x * kChunk;
+  // the records stay in registers (scalar arrays, static indices) until
+  // they are placed in LDS in tile order
+  uint32_t w[8][kChunkItems];
+#pragma unroll
+  for (int j = 0; j < kChunkItems; ++j) {
+    const uint32_t i = base + j * kChunkThreads + threadIdx.x;
+    const size_t ic = (i < n) ? i : n - 1u;  // unconditional loads, clamped index
+    const uint4 a = parts[ic * 2u];
+    const uint4 b = parts[ic * 2u + 1u];
+    w[0][j] = a.x; w[1][j] = a.y; w[2][j] = a.z; w[3][j] = a.w;
+    w[4][j] = b.x; w[5][j] = b.y; w[6][j] = b.z; w[7][j] = b.w;
+  }
+  __syncthreads();  // s_hist zeroed
+  uint32_t tile[kChunkItems], rank[kChunkItems];
+#pragma unroll
+  for (int j = 0; j < kChunkItems; ++j) {
+    const uint32_t i = base + j * kChunkThreads + threadIdx.x;
+    tile[j] = 0xFFFFFFFFu;
+    rank[j] = 0u;
+    if (i < n) {
+      const uint32_t c = cell_of(__uint_as_float(w[0][j]), __uint_as_float(w[1][j]),
+                                 __uint_as_float(w[2][j]), g);
+      celdaDe[i] = c;
+      tile[j] = c >> tile_shift;
+      rank[j] = atomicAdd(&s_hist[tile[j]], 1u);
+    }
+  }
+  __syncthreads();
+  // exclusive scan of the tile histogram: one bin per thread
+  const uint32_t cnt = (threadIdx.x < ntiles) ? s_hist[threadIdx.x] : 0u;
+  uint32_t total;
+  const uint32_t ex = block_exclusive_sum<kChunkThreads>(cnt, s_wave, &total);
+  if (threadIdx.x < ntiles) {
+    rows[static_cast<size_t>(blockIdx.x) * ntiles + threadIdx.x] = make_uint2(cnt, ex);
+    s_hist[threadIdx.x] = ex;  // now the first local slot of each tile
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kChunkItems; ++j) {
+    if (tile[j] != 0xFFFFFFFFu) {
+      const uint32_t local = s_hist[tile[j]] + rank[j];
+      s_rec[2 * local] = make_uint4(w[0][j], w[1][j], w[2][j], w[3][j]);
+      s_rec[2 * local + 1] = make_uint4(w[4][j], w[5][j], w[6][j], w[7][j]);
+      s_idx[local] = base + j * kChunkThreads + threadIdx.x;
+    }
+  }
+  __syncthreads();
+  // the chunk in tile order, written contiguously
+  const uint32_t in_chunk = total;  // valid particles of this chunk
+  uint4* dst = chunk_rec + static_cast<size_t>(base) * 2u;
+  for (uint32_t q = threadIdx.x; q < 2 * in_chunk; q += kChunkThreads) dst[q] = s_rec[q];
+  uint32_t* dsti = chunk_idx + base;
+  for (uint32_t q = threadIdx.x; q < in_chunk; q += kChunkThreads) dsti[q] = s_idx[q];
+}
+
+// cells: block t owns cells [t << SHIFT, (t+1) << SHIFT). MOVE: also write
+// the records (otherwise a separate gather follows).
+template <bool MOVE, uint32_t SHIFT>
+__global__ __launch_bounds__(kStagedCellsThreads) void staged_cells_kernel(
+    const uint2* __restrict__ rows, uint32_t nchunks, uint32_t ntiles, GridParams g,
+    uint32_t cells, uint32_t n, const uint4* __restrict__ chunk_rec,
+    const uint32_t* __restrict__ chunk_idx, uint32_t* __restrict__ conteos,
+    uint32_t* __restrict__ inicios, uint32_t* __restrict__ ordenado, uint4* __restrict__ dst) {
+  constexpr uint32_t kTileCells = 1u << SHIFT;
+  constexpr uint32_t kPer = kTileCells / kStagedCellsThreads;  // cells per thread in the scan
+  static_assert(kTileCells % kStagedCellsThreads == 0, "tile must cover the workgroup");
+  constexpr int NT = kStagedCellsThreads;
+  __shared__ uint32_t s_cnt[kTileCells];
+  __shared__ uint32_t s_dst[kStagedMaxChunks];  // tile-local start of each chunk's run
+  __shared__ uint32_t s_src[kStagedMaxChunks];  // where that run starts in the chunk array
+  __shared__ uint4 s_rec[2 * kStagedWin];
+  __shared__ uint32_t s_idx[kStagedWin];
+  __shared__ uint32_t s_wave[NT / 64];
+
+  const uint32_t t = blockIdx.x;
+  const uint32_t cell0 = t << SHIFT;
+  const uint32_t tc = (cells - cell0 < kTileCells) ? cells - cell0 : kTileCells;
+
+  // chunk runs of this tile; the tile start is the sum of the chunks' prefixes
+  uint2 r = make_uint2(0u, 0u);
+  if (threadIdx.x < nchunks) r = rows[static_cast<size_t>(threadIdx.x) * ntiles + t];
+  uint32_t count;
+  const uint32_t run_dst = block_exclusive_sum<NT>(r.x, s_wave, &count);
+  const uint32_t bs = block_sum<NT>(r.y, s_wave);
+  if (threadIdx.x < nchunks) {
+    s_dst[threadIdx.x] = run_dst;
+    s_src[threadIdx.x] = threadIdx.x * kChunk + r.y;
+  }
+  for (uint32_t j = threadIdx.x; j < kTileCells; j += NT) s_cnt[j] = 0u;
+  __syncthreads();
+
+  // position in the chunk array of tile-local particle p: the last chunk whose
+  // run starts at or before p (runs of empty chunks start at the same place,
+  // the last of them is the non-empty one). Used only for tiles too large to
+  // stage; staged tiles expand the runs into a source map instead.
+  auto source_of = [&](uint32_t p) -> uint32_t {
+    uint32_t lo = 0, hi = nchunks - 1;
+    while (lo < hi) {
+      const uint32_t mid = (lo + hi + 1) >> 1;
+      if (s_dst[mid] <= p) lo = mid; else hi = mid - 1;
+    }
+    return s_src[lo] + (p - s_dst[lo]);
+  };
+
+  const bool staged = count <= kStagedCap;
+  // records held in registers as scalar arrays (static indices)
+  uint32_t w[8][kStagedRegs], idx[kStagedRegs], loc[kStagedRegs];
+#pragma unroll
+  for (int k = 0; k < kStagedRegs; ++k) loc[k] = 0xFFFFFFFFu;  // no particle
+  if (staged) {
+    // source map: s_map[p] = chunk-array position of tile-local particle p
+    uint32_t* s_map = reinterpret_cast<uint32_t*>(s_rec);
+    if (threadIdx.x < nchunks)
+      for (uint32_t k = 0; k < r.x; ++k) s_map[run_dst + k] = threadIdx.x * kChunk + r.y + k;
+    __syncthreads();
+    if (count > 0) {  // count == 0: no valid source to clamp the idle lanes to
+      uint32_t src[kStagedRegs];
+#pragma unroll
+      for (int k = 0; k < kStagedRegs; ++k) {
+        const uint32_t p = threadIdx.x + k * NT;
+        src[k] = s_map[p < count ? p : 0u];  // clamped: loads below are unconditional
+      }
+#pragma unroll
+      for (int k = 0; k < kStagedRegs; ++k) {
+        const uint4 a = chunk_rec[static_cast<size_t>(src[k]) * 2u];
+        const uint4 b = MOVE ? chunk_rec[static_cast<size_t>(src[k]) * 2u + 1u] : make_uint4(0u, 0u, 0u, 0u);
+        idx[k] = chunk_idx[src[k]];
+        w[0][k] = a.x; w[1][k] = a.y; w[2][k] = a.z; w[3][k] = a.w;
+        w[4][k] = b.x; w[5][k] = b.y; w[6][k] = b.z; w[7][k] = b.w;
+      }
+#pragma unroll
+      for (int k = 0; k < kStagedRegs; ++k) {
+        const uint32_t p = threadIdx.x + k * NT;
+        if (p < count) {
+          const uint32_t c = cell_of(__uint_as_float(w[0][k]), __uint_as_float(w[1][k]),
+                                     __uint_as_float(w[2][k]), g);
+          loc[k] = c - cell0;
+          if (loc[k] < tc) atomicAdd(&s_cnt[loc[k]], 1u);
+        }
+      }
+    }
+  } else {
+    for (uint32_t p = threadIdx.x; p < count; p += NT) {
+      const uint32_t s = source_of(p);
+      const uint4 a = chunk_rec[static_cast<size_t>(s) * 2u];
+      const uint32_t c = cell_of(__uint_as_float(a.x), __uint_as_float(a.y), __uint_as_float(a.z), g);
+      if (c - cell0 < tc) atomicAdd(&s_cnt[c - cell0], 1u);
+    }
+  }
+  __syncthreads();
+
+  // histogram out: lane-contiguous 16-byte stores
+  uint4* s_cnt4 = reinterpret_cast<uint4*>(s_cnt);
+  const uint32_t tc4 = tc / 4;  // full vectors (tiles start at multiples of 4096 cells)
+  for (uint32_t q = threadIdx.x; q < tc4; q += NT)
+    reinterpret_cast<uint4*>(conteos + cell0)[q] = s_cnt4[q];
+  for (uint32_t j = 4 * tc4 + threadIdx.x; j < tc; j += NT) conteos[cell0 + j] = s_cnt[j];
+  // exclusive scan in LDS: kPer consecutive cells per thread, then the
+  // block scan of the per-thread sums; s_cnt becomes the slot cursors
+  const uint32_t j0 = threadIdx.x * kPer;
+  uint32_t sum = 0;
+#pragma unroll
+  for (uint32_t q = 0; q < kPer; ++q) sum += s_cnt[j0 + q];  // cells >= tc hold 0
+  uint32_t tot;
+  uint32_t run = block_exclusive_sum<NT>(sum, s_wave, &tot);
+#pragma unroll
+  for (uint32_t q = 0; q < kPer; ++q) {
+    const uint32_t v = s_cnt[j0 + q];
+    s_cnt[j0 + q] = run;
+    run += v;
+  }
+  __syncthreads();
+  // starts out: lane-contiguous 16-byte stores, offset by the tile start
+  for (uint32_t q = threadIdx.x; q < tc4; q += NT) {
+    const uint4 v = s_cnt4[q];
+    reinterpret_cast<uint4*>(inicios + cell0)[q] = make_uint4(bs + v.x, bs + v.y, bs + v.z, bs + v.w);
+  }
+  for (uint32_t j = 4 * tc4 + threadIdx.x; j < tc; j += NT) inicios[cell0 + j] = bs + s_cnt[j];
+  if (t == ntiles - 1 && threadIdx.x == 0) inicios[cells] = bs + count;
+  __syncthreads();  // every start read before the cursors advance
+
+  if (staged) {
+    uint32_t slot[kStagedRegs];
+#pragma unroll
+    for (int k = 0; k < kStagedRegs; ++k)
+      slot[k] = (loc[k] < tc) ? atomicAdd(&s_cnt[loc[k]], 1u) : 0xFFFFFFFFu;
+    for (uint32_t w0 = 0; w0 < count; w0 += kStagedWin) {
+      const uint32_t wn = (count - w0 < kStagedWin) ? count - w0 : kStagedWin;
+#pragma unroll
+      for (int k = 0; k < kStagedRegs; ++k) {
+        const uint32_t o = slot[k] - w0;
+        if (slot[k] != 0xFFFFFFFFu && o < wn) {
+          if (MOVE) {
+            s_rec[2 * o] = make_uint4(w[0][k], w[1][k], w[2][k], w[3][k]);
+            s_rec[2 * o + 1] = make_uint4(w[4][k], w[5][k], w[6][k], w[7][k]);
+          }
+          s_idx[o] = idx[k];
+        }
+      }
+      __syncthreads();
+      const size_t out0 = static_cast<size_t>(bs) + w0;
+      for (uint32_t q = threadIdx.x; q < wn; q += NT)
+        if (out0 + q < n) ordenado[out0 + q] = s_idx[q];
+      if (MOVE) {
+        for (uint32_t q = threadIdx.x; q < 2 * wn; q += NT)
+          if (out0 * 2u + q < 2ull * n) dst[out0 * 2u + q] = s_rec[q];
+      }
+      __syncthreads();
+    }
+  } else {
+    for (uint32_t p = threadIdx.x; p < count; p += NT) {
+      const uint32_t s = source_of(p);
+      const uint4 a = chunk_rec[static_cast<size_t>(s) * 2u];
+      const uint4 b = chunk_rec[static_cast<size_t>(s) * 2u + 1u];
+      const uint32_t c = cell_of(__uint_as_float(a.x), __uint_as_float(a.y), __uint_as_float(a.z), g);
+      if (c - cell0 < tc) {
+        const size_t out = static_cast<size_t>(bs) + atomicAdd(&s_cnt[c - cell0], 1u);
+        if (out < n) {
+          ordenado[out] = chunk_idx[s];
+          if (MOVE) {
+            dst[out * 2u] = a;
+            dst[out * 2u + 1u] = b;
+          }
+        }
+      }
+    }
+  }
+}
+
+}  // namespace ugp
