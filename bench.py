@@ -143,7 +143,92 @@ def _cpu_model() -> str:
     return "unknown"
 
 
+# ---------------------------------------------------------------------------
+# rocprofv3 summaries (run on CSV output: --output-format csv)
+# ---------------------------------------------------------------------------
+
+def _short_kernel(name: str) -> str:
+    name = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    for pre in ("ugp::",):
+        name = name.replace(pre, "")
+    cut = name.find("(")
+    return name[:cut] if cut > 0 else name
+
+
+def summarize_trace(stats_csv: str) -> str:
+    """Per-kernel durations from rocprofv3 --kernel-trace --stats (kernel_stats.csv)."""
+    import csv
+
+    rows = list(csv.DictReader(open(stats_csv, encoding="utf-8")))
+    out = [f"{'kernel':44s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'total%':>7s}"]
+    for r in rows:
+        out.append(f"{_short_kernel(r['Name'])[:44]:44s} {int(r['Calls']):6d} {float(r['AverageNs'])/1e3:9.2f} "
+                   f"{float(r['MinNs'])/1e3:9.2f} {float(r['MaxNs'])/1e3:9.2f} {float(r['Percentage']):7.2f}")
+    return "\n".join(out)
+
+
+def _counter_means(csv_path: str, counter: str) -> dict:
+    import csv
+
+    acc: dict = {}
+    for r in csv.DictReader(open(csv_path, encoding="utf-8")):
+        if r.get("Counter_Name") != counter:
+            continue
+        k = _short_kernel(r["Kernel_Name"])
+        acc.setdefault(k, []).append(float(r["Counter_Value"]))
+    return acc
+
+
+def summarize_counters(fetch_csv: str, write_csv: str, copy_bytes: int = 256 << 20) -> tuple[str, dict]:
+    """HBM bytes per dispatch from FETCH_SIZE / WRITE_SIZE (KiB), each scaled by
+    what the same counter reads for the largest device copy (copy_bytes read
+    and written) in the same run."""
+    fetch = _counter_means(fetch_csv, "FETCH_SIZE")
+    write = _counter_means(write_csv, "WRITE_SIZE")
+    copy_key = next((k for k in fetch if "copyBuffer" in k), None)
+    if copy_key is None:
+        raise SystemExit("no copy kernel in the counter run (use --copy-reference)")
+    f_scale = copy_bytes / (max(fetch[copy_key]) * 1024.0)
+    w_scale = copy_bytes / (max(write[copy_key]) * 1024.0)
+    lines = [f"copy reference: {copy_bytes} B read+written; FETCH_SIZE reads {max(fetch[copy_key]):.1f} KiB "
+             f"(scale {f_scale:.3f}), WRITE_SIZE reads {max(write[copy_key]):.1f} KiB (scale {w_scale:.3f})",
+             f"{'kernel':44s} {'dispatches':>10s} {'fetch_KiB':>11s} {'write_KiB':>11s} {'scaled_MB':>10s}"]
+    traffic = {}
+    for k in sorted(set(fetch) & set(write)):
+        if "copyBuffer" in k:
+            continue
+        fk = sum(fetch[k]) / len(fetch[k])
+        wk = sum(write[k]) / len(write[k])
+        b = fk * 1024.0 * f_scale + wk * 1024.0 * w_scale
+        traffic[k] = b
+        lines.append(f"{k[:44]:44s} {len(fetch[k]):10d} {fk:11.1f} {wk:11.1f} {b / 1e6:10.2f}")
+    return "\n".join(lines), traffic
+
+
+# kernel symbol -> stage name, for the traffic file
+KERNEL_STAGE = {
+    "staged_keys_kernel": "chunk_sort", "staged_cells_kernel": "tile_sort",
+    "tiled_keys_kernel": "keys", "tiled_colscan_kernel": "tile_scan", "tiled_bucket_kernel": "bucket",
+    "tiled_cells_kernel": "cells", "clear_kernel": "clear", "count_kernel": "count", "scan_kernel": "scan",
+    "scatter_kernel": "scatter", "gather_kernel": "gather",
+}
+
+
+def write_traffic_file(traffic: dict, path: str, command: str) -> None:
+    with open(path, "w", encoding="utf-8") as f:
+        f.write("# Measured HBM traffic per dispatch (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE),\n")
+        f.write("# each counter scaled by its reading for a 256 MiB device copy in the same run.\n")
+        f.write(f"# command: {command}\n")
+        f.write(f"source_sha256_16: {source_digest()}\n")
+        for k, b in traffic.items():
+            base = k.split("<")[0]
+            stage = KERNEL_STAGE.get(base, base)
+            f.write(f"{stage}_bytes_per_dispatch: {b:.0f}\n")
+
+
 def main(argv=None) -> int:
+    if argv is None and len(sys.argv) > 1 and sys.argv[1] == "summarize":
+        return summarize_main(sys.argv[2:])
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
@@ -306,6 +391,25 @@ def main(argv=None) -> int:
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
+    return 0
+
+
+def summarize_main(argv) -> int:
+    """python bench.py summarize trace STATS_CSV
+       python bench.py summarize counters FETCH_CSV WRITE_CSV [--write-traffic PATH --command CMD]"""
+    ap = argparse.ArgumentParser(prog="bench.py summarize")
+    ap.add_argument("kind", choices=["trace", "counters"])
+    ap.add_argument("files", nargs="+")
+    ap.add_argument("--write-traffic")
+    ap.add_argument("--command", default="")
+    a = ap.parse_args(argv)
+    if a.kind == "trace":
+        print(summarize_trace(a.files[0]))
+        return 0
+    text, traffic = summarize_counters(a.files[0], a.files[1])
+    print(text)
+    if a.write_traffic:
+        write_traffic_file(traffic, a.write_traffic, a.command)
     return 0
 
 

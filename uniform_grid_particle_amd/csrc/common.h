@@ -40,6 +40,20 @@ __device__ __forceinline__ uint32_t cell_of(float x, float y, float z, const Gri
   return kx + ky * g.nx + kz * g.nxy;
 }
 
+// Streaming accesses: data read or written once by this kernel. The
+// non-temporal hint keeps it from displacing reused lines in the caches.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_stream(uint4* p, uint4 v) {
+  const u32x4_t w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(p));
+}
+__device__ __forceinline__ uint32_t load_stream(const uint32_t* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ void store_stream(uint32_t* p, uint32_t v) { __builtin_nontemporal_store(v, p); }
+
 // Inclusive prefix sum across the 64 lanes of a wave, with DPP lane moves
 // (no LDS traffic): shifts of 1, 2, 4 and 8 lanes inside each row of 16
 // give row-inclusive sums, then row 0's total is broadcast into row 1 and

@@ -8,21 +8,26 @@
 // no global atomics, and moves every record with coalesced accesses,
 // reordering through LDS:
 //
-//   keys   one workgroup per chunk of 4096 particles: cell key per particle
-//          (celdaDe), a counting sort of the chunk by tile in LDS (a tile is
-//          2^shift consecutive cells, at most 256 tiles), the chunk written
-//          back contiguously in tile order (records and particle indices),
-//          and one row {count, exclusive prefix} per tile for the chunk.
-//   cells  one workgroup per tile: it reads the chunk rows of its tile
-//          (how many of its particles each chunk holds, and where), sums
-//          them into its start (the tile start is the number of particles
-//          in earlier tiles), expands the runs into a per-particle source
-//          map in LDS, loads its particles run by run, counts them
-//          into an LDS histogram of its cells (conteos), scans the
-//          histogram (inicios), takes every particle's slot with an LDS
-//          atomic, and writes ordenado and reordered through an LDS staging
-//          window so the stores are contiguous. A tile with more particles
-//          than the registers hold writes its slots directly instead.
+//   chunk_sort  one workgroup per chunk of particles: cell key per
+//               particle (celdaDe), a counting sort of the chunk by tile in
+//               LDS (a tile is 2^shift consecutive cells, at most 512 tiles),
+//               the chunk written back contiguously in tile order (records
+//               and particle indices), and one row {count, exclusive prefix}
+//               per tile for the chunk.
+//   tile_sort   one workgroup per tile: it reads the chunk rows of its tile
+//               (how many of its particles each chunk holds, and where), sums
+//               them into its start (the tile start is the number of
+//               particles in earlier tiles), expands the runs into a
+//               per-particle source map in LDS, loads its particles run by
+//               run, counts them into an LDS histogram of its cells
+//               (conteos), scans the histogram (inicios), takes every
+//               particle's slot with an LDS atomic, and writes ordenado and
+//               reordered through an LDS staging window so the stores are
+//               contiguous. A tile with more particles than the registers
+//               hold writes its slots directly instead.
+//
+// The workgroup sizes, the chunk size and the staging window are template
+// parameters; the host picks them per problem size.
 //
 // The result is the counting sort of the pages: exact histogram, exclusive
 // scan with the total in the extra slot, every particle inside its cell's
@@ -35,34 +40,48 @@
 
 namespace ugp {
 
-constexpr int kChunkThreads = 512;                 // keys workgroup
-constexpr int kChunkItems = 8;                     // particles per thread
-constexpr uint32_t kChunk = kChunkThreads * kChunkItems;  // 4096 particles per chunk
-constexpr uint32_t kStagedMaxTiles = 256;          // one workgroup round of the cells kernel
+constexpr int kChunkItems = 8;                      // particles per chunk_sort thread
+constexpr uint32_t kStagedMaxTiles = 512;
+constexpr uint32_t kStagedMaxChunks = 1024;
+constexpr int kStagedRegs = 8;                      // particles per tile_sort thread in registers
+
+// Geometry the host uses (chosen by measurement on MI355X, 1M particles on
+// 128^3 cells: runs of 8+ records per chunk and tile keep tile_sort's loads
+// efficient, 2048-particle chunks let two chunk_sort workgroups share a CU).
+constexpr int kChunkThreads = 256;                  // chunk_sort workgroup
+constexpr uint32_t kChunk = kChunkThreads * kChunkItems;  // 2048 particles per chunk
+constexpr uint32_t kStagedTiles = 256;              // tiles at most (one tile_sort round)
 constexpr uint32_t kStagedMinShift = 12;
-constexpr uint32_t kStagedMaxShift = 14;           // up to 16384 cells per tile (64 KiB histogram)
-constexpr uint32_t kStagedMaxChunks = 512;         // up to 2^21 particles
-constexpr int kStagedCellsThreads = 1024;          // cells workgroup
-constexpr int kStagedRegs = 8;                     // particles per thread held in registers
-constexpr uint32_t kStagedCap = kStagedCellsThreads * kStagedRegs;  // staged tile capacity (8192)
-constexpr uint32_t kStagedWin = 2048;              // LDS staging window (records)
+constexpr uint32_t kStagedMaxShift = 14;            // up to 16384 cells per tile
+constexpr int kCellsThreads = 1024;                 // tile_sort workgroup
+constexpr uint32_t kCellsWin = 2048;                // tile_sort LDS staging window
 
-static_assert(kStagedMaxTiles <= kChunkThreads, "one tile bin per keys thread in the scan");
-static_assert(kStagedMaxChunks <= kStagedCellsThreads, "one chunk row per cells thread");
-static_assert(2 * kStagedWin * 4 >= kStagedCap, "the source map fits in the staging buffer");
+// Tile t's workgroup index, spreading consecutive tiles over workgroups of
+// the same XCD (workgroups are dealt to the 8 XCDs round robin), so tiles
+// that read neighbouring runs of each chunk share that XCD's L2 lines.
+__device__ __forceinline__ uint32_t tile_of_block(uint32_t b, uint32_t ntiles) {
+  if (ntiles % 8 != 0) return b;
+  return (b % 8) * (ntiles / 8) + b / 8;
+}
 
-// keys: chunk b holds particles [b*kChunk, (b+1)*kChunk).
+// chunk_sort: CT threads, chunk b holds particles [b*chunk, (b+1)*chunk)
+// with chunk = CT * kChunkItems.
 // rows[b*ntiles + t] = {particles of chunk b in tile t, those in tiles < t}.
-__global__ __launch_bounds__(kChunkThreads) void staged_keys_kernel(
+template <int CT>
+__global__ __launch_bounds__(CT) void staged_keys_kernel(
     const uint4* __restrict__ parts, uint32_t n, GridParams g, uint32_t* __restrict__ celdaDe,
     uint2* __restrict__ rows, uint32_t tile_shift, uint32_t ntiles, uint4* __restrict__ chunk_rec,
     uint32_t* __restrict__ chunk_idx) {
-  __shared__ uint4 s_rec[2 * kChunk];  // 128 KiB: the chunk in tile order
-  __shared__ uint32_t s_idx[kChunk];   // 16 KiB
+  constexpr int kChunkThreads = CT;
+  constexpr uint32_t kChunk = CT * kChunkItems;
+  constexpr uint32_t kTilesPerThread = kStagedMaxTiles / CT;  // tile bins per thread
+  static_assert(kStagedMaxTiles % CT == 0, "whole tile bins per thread");
+  __shared__ uint4 s_rec[2 * kChunk];  // the chunk in tile order
+  __shared__ uint32_t s_idx[kChunk];
   __shared__ uint32_t s_hist[kStagedMaxTiles];
   __shared__ uint32_t s_wave[kChunkThreads / 64];
 
-  if (threadIdx.x < kStagedMaxTiles) s_hist[threadIdx.x] = 0u;
+  for (uint32_t t = threadIdx.x; t < kStagedMaxTiles; t += kChunkThreads) s_hist[t] = 0u;
   const uint32_t base = blockIdx.x * kChunk;
   // the records stay in registers (scalar arrays, static indices) until
   // they are placed in LDS in tile order
@@ -71,8 +90,8 @@ __global__ __launch_bounds__(kChunkThreads) void staged_keys_kernel(
   for (int j = 0; j < kChunkItems; ++j) {
     const uint32_t i = base + j * kChunkThreads + threadIdx.x;
     const size_t ic = (i < n) ? i : n - 1u;  // unconditional loads, clamped index
-    const uint4 a = parts[ic * 2u];
-    const uint4 b = parts[ic * 2u + 1u];
+    const uint4 a = load_stream(parts + ic * 2u);
+    const uint4 b = load_stream(parts + ic * 2u + 1u);
     w[0][j] = a.x; w[1][j] = a.y; w[2][j] = a.z; w[3][j] = a.w;
     w[4][j] = b.x; w[5][j] = b.y; w[6][j] = b.z; w[7][j] = b.w;
   }
@@ -92,13 +111,25 @@ __global__ __launch_bounds__(kChunkThreads) void staged_keys_kernel(
     }
   }
   __syncthreads();
-  // exclusive scan of the tile histogram: one bin per thread
-  const uint32_t cnt = (threadIdx.x < ntiles) ? s_hist[threadIdx.x] : 0u;
+  // exclusive scan of the tile histogram: kTilesPerThread consecutive bins per thread
+  uint32_t cnt[kTilesPerThread];
+  uint32_t sum = 0;
+#pragma unroll
+  for (uint32_t q = 0; q < kTilesPerThread; ++q) {
+    const uint32_t t = threadIdx.x * kTilesPerThread + q;
+    cnt[q] = (t < ntiles) ? s_hist[t] : 0u;
+    sum += cnt[q];
+  }
   uint32_t total;
-  const uint32_t ex = block_exclusive_sum<kChunkThreads>(cnt, s_wave, &total);
-  if (threadIdx.x < ntiles) {
-    rows[static_cast<size_t>(blockIdx.x) * ntiles + threadIdx.x] = make_uint2(cnt, ex);
-    s_hist[threadIdx.x] = ex;  // now the first local slot of each tile
+  uint32_t ex = block_exclusive_sum<kChunkThreads>(sum, s_wave, &total);
+#pragma unroll
+  for (uint32_t q = 0; q < kTilesPerThread; ++q) {
+    const uint32_t t = threadIdx.x * kTilesPerThread + q;
+    if (t < ntiles) {
+      rows[static_cast<size_t>(blockIdx.x) * ntiles + t] = make_uint2(cnt[q], ex);
+      s_hist[t] = ex;  // now the first local slot of each tile
+    }
+    ex += cnt[q];
   }
   __syncthreads();
 #pragma unroll
@@ -114,23 +145,28 @@ __global__ __launch_bounds__(kChunkThreads) void staged_keys_kernel(
   // the chunk in tile order, written contiguously
   const uint32_t in_chunk = total;  // valid particles of this chunk
   uint4* dst = chunk_rec + static_cast<size_t>(base) * 2u;
-  for (uint32_t q = threadIdx.x; q < 2 * in_chunk; q += kChunkThreads) dst[q] = s_rec[q];
+  for (uint32_t q = threadIdx.x; q < 2 * in_chunk; q += kChunkThreads) store_stream(dst + q, s_rec[q]);
   uint32_t* dsti = chunk_idx + base;
-  for (uint32_t q = threadIdx.x; q < in_chunk; q += kChunkThreads) dsti[q] = s_idx[q];
+  for (uint32_t q = threadIdx.x; q < in_chunk; q += kChunkThreads) store_stream(dsti + q, s_idx[q]);
 }
 
-// cells: block t owns cells [t << SHIFT, (t+1) << SHIFT). MOVE: also write
-// the records (otherwise a separate gather follows).
-template <bool MOVE, uint32_t SHIFT>
-__global__ __launch_bounds__(kStagedCellsThreads) void staged_cells_kernel(
-    const uint2* __restrict__ rows, uint32_t nchunks, uint32_t ntiles, GridParams g,
+// tile_sort: NT threads; the tile of block b (tile_of_block) owns cells
+// [t << SHIFT, (t+1) << SHIFT); WIN records are staged in LDS at a time.
+// MOVE: also write the records (otherwise a separate gather follows).
+template <bool MOVE, uint32_t SHIFT, int NT, uint32_t WIN>
+__global__ __launch_bounds__(NT) void staged_cells_kernel(
+    const uint2* __restrict__ rows, uint32_t nchunks, uint32_t chunk, uint32_t ntiles, GridParams g,
     uint32_t cells, uint32_t n, const uint4* __restrict__ chunk_rec,
     const uint32_t* __restrict__ chunk_idx, uint32_t* __restrict__ conteos,
     uint32_t* __restrict__ inicios, uint32_t* __restrict__ ordenado, uint4* __restrict__ dst) {
   constexpr uint32_t kTileCells = 1u << SHIFT;
-  constexpr uint32_t kPer = kTileCells / kStagedCellsThreads;  // cells per thread in the scan
-  static_assert(kTileCells % kStagedCellsThreads == 0, "tile must cover the workgroup");
-  constexpr int NT = kStagedCellsThreads;
+  constexpr uint32_t kPer = kTileCells / NT;  // cells per thread in the scan
+  constexpr uint32_t kChunksPerThread = kStagedMaxChunks / NT;
+  constexpr uint32_t kStagedCap = NT * kStagedRegs;  // staged tile capacity
+  constexpr uint32_t kStagedWin = WIN;
+  static_assert(kTileCells % NT == 0, "tile must cover the workgroup");
+  static_assert(kStagedMaxChunks % NT == 0, "whole chunk rows per thread");
+  static_assert(2 * WIN * 4 >= kStagedCap, "the source map fits in the staging buffer");
   __shared__ uint32_t s_cnt[kTileCells];
   __shared__ uint32_t s_dst[kStagedMaxChunks];  // tile-local start of each chunk's run
   __shared__ uint32_t s_src[kStagedMaxChunks];  // where that run starts in the chunk array
@@ -138,19 +174,32 @@ __global__ __launch_bounds__(kStagedCellsThreads) void staged_cells_kernel(
   __shared__ uint32_t s_idx[kStagedWin];
   __shared__ uint32_t s_wave[NT / 64];
 
-  const uint32_t t = blockIdx.x;
+  const uint32_t t = tile_of_block(blockIdx.x, ntiles);
   const uint32_t cell0 = t << SHIFT;
   const uint32_t tc = (cells - cell0 < kTileCells) ? cells - cell0 : kTileCells;
 
-  // chunk runs of this tile; the tile start is the sum of the chunks' prefixes
-  uint2 r = make_uint2(0u, 0u);
-  if (threadIdx.x < nchunks) r = rows[static_cast<size_t>(threadIdx.x) * ntiles + t];
+  // chunk runs of this tile (kChunksPerThread consecutive chunks per thread);
+  // the tile start is the sum of the chunks' prefixes
+  uint2 r[kChunksPerThread];
+  uint32_t len_sum = 0, pre_sum = 0;
+#pragma unroll
+  for (uint32_t q = 0; q < kChunksPerThread; ++q) {
+    const uint32_t c = threadIdx.x * kChunksPerThread + q;
+    r[q] = (c < nchunks) ? rows[static_cast<size_t>(c) * ntiles + t] : make_uint2(0u, 0u);
+    len_sum += r[q].x;
+    pre_sum += r[q].y;
+  }
   uint32_t count;
-  const uint32_t run_dst = block_exclusive_sum<NT>(r.x, s_wave, &count);
-  const uint32_t bs = block_sum<NT>(r.y, s_wave);
-  if (threadIdx.x < nchunks) {
-    s_dst[threadIdx.x] = run_dst;
-    s_src[threadIdx.x] = threadIdx.x * kChunk + r.y;
+  uint32_t run_dst = block_exclusive_sum<NT>(len_sum, s_wave, &count);
+  const uint32_t bs = block_sum<NT>(pre_sum, s_wave);
+#pragma unroll
+  for (uint32_t q = 0; q < kChunksPerThread; ++q) {
+    const uint32_t c = threadIdx.x * kChunksPerThread + q;
+    if (c < nchunks) {
+      s_dst[c] = run_dst;
+      s_src[c] = c * chunk + r[q].y;
+    }
+    run_dst += r[q].x;
   }
   for (uint32_t j = threadIdx.x; j < kTileCells; j += NT) s_cnt[j] = 0u;
   __syncthreads();
@@ -176,8 +225,12 @@ __global__ __launch_bounds__(kStagedCellsThreads) void staged_cells_kernel(
   if (staged) {
     // source map: s_map[p] = chunk-array position of tile-local particle p
     uint32_t* s_map = reinterpret_cast<uint32_t*>(s_rec);
-    if (threadIdx.x < nchunks)
-      for (uint32_t k = 0; k < r.x; ++k) s_map[run_dst + k] = threadIdx.x * kChunk + r.y + k;
+#pragma unroll
+    for (uint32_t q = 0; q < kChunksPerThread; ++q) {
+      const uint32_t c = threadIdx.x * kChunksPerThread + q;
+      if (c < nchunks)
+        for (uint32_t k = 0; k < r[q].x; ++k) s_map[s_dst[c] + k] = s_src[c] + k;
+    }
     __syncthreads();
     if (count > 0) {  // count == 0: no valid source to clamp the idle lanes to
       uint32_t src[kStagedRegs];
@@ -216,7 +269,7 @@ __global__ __launch_bounds__(kStagedCellsThreads) void staged_cells_kernel(
   __syncthreads();
 
   // histogram out: lane-contiguous 16-byte stores
-  uint4* s_cnt4 = reinterpret_cast<uint4*>(s_cnt);
+  const uint4* s_cnt4 = reinterpret_cast<const uint4*>(s_cnt);
   const uint32_t tc4 = tc / 4;  // full vectors (tiles start at multiples of 4096 cells)
   for (uint32_t q = threadIdx.x; q < tc4; q += NT)
     reinterpret_cast<uint4*>(conteos + cell0)[q] = s_cnt4[q];

@@ -95,7 +95,7 @@ int make_plan(uint32_t n, const uint32_t dims[3], uint32_t flags, Plan* p) {
     return UGP_OK;
   }
   const uint32_t tile_shift = (lg > kTileShiftMin + 9) ? lg - 9 : kTileShiftMin;
-  // staged path: at most 256 tiles (one workgroup round of its cells kernel)
+  // staged path: at most 256 tiles (one round of tile_sort workgroups)
   const uint32_t staged_shift = (lg > kStagedMinShift + 8) ? lg - 8 : kStagedMinShift;
   const uint64_t nchunks = (static_cast<uint64_t>(n) + kChunk - 1) / kChunk;
   if (staged_shift <= kStagedMaxShift && nchunks <= kStagedMaxChunks) {
@@ -275,16 +275,19 @@ void launch_staged_cells(uint32_t shift, dim3 grid, hipStream_t s, const uint2* 
                          uint32_t nchunks, uint32_t ntiles, GridParams g, uint32_t cells,
                          uint32_t n, const uint4* chunk_rec, const uint32_t* chunk_idx,
                          uint32_t* conteos, uint32_t* inicios, uint32_t* ordenado, uint4* dst) {
-  const dim3 block(kStagedCellsThreads);
+  const dim3 block(kCellsThreads);
   if (shift == 12)
-    hipLaunchKernelGGL((staged_cells_kernel<MOVE, 12>), grid, block, 0, s, rows, nchunks, ntiles, g,
-                       cells, n, chunk_rec, chunk_idx, conteos, inicios, ordenado, dst);
+    hipLaunchKernelGGL((staged_cells_kernel<MOVE, 12, kCellsThreads, kCellsWin>), grid, block, 0, s,
+                       rows, nchunks, kChunk, ntiles, g, cells, n, chunk_rec, chunk_idx, conteos,
+                       inicios, ordenado, dst);
   else if (shift == 13)
-    hipLaunchKernelGGL((staged_cells_kernel<MOVE, 13>), grid, block, 0, s, rows, nchunks, ntiles, g,
-                       cells, n, chunk_rec, chunk_idx, conteos, inicios, ordenado, dst);
+    hipLaunchKernelGGL((staged_cells_kernel<MOVE, 13, kCellsThreads, kCellsWin>), grid, block, 0, s,
+                       rows, nchunks, kChunk, ntiles, g, cells, n, chunk_rec, chunk_idx, conteos,
+                       inicios, ordenado, dst);
   else
-    hipLaunchKernelGGL((staged_cells_kernel<MOVE, 14>), grid, block, 0, s, rows, nchunks, ntiles, g,
-                       cells, n, chunk_rec, chunk_idx, conteos, inicios, ordenado, dst);
+    hipLaunchKernelGGL((staged_cells_kernel<MOVE, 14, kCellsThreads, kCellsWin>), grid, block, 0, s,
+                       rows, nchunks, kChunk, ntiles, g, cells, n, chunk_rec, chunk_idx, conteos,
+                       inicios, ordenado, dst);
 }
 
 // Stable-order and gather passes, shared by every path.
@@ -314,7 +317,7 @@ void enqueue_staged(uint32_t stage, const BuildArgs& a, const Plan& p) {
   hipStream_t s = a.stream;
   switch (stage) {
     case 0:
-      hipLaunchKernelGGL(staged_keys_kernel, dim3(p.nchunks), dim3(kChunkThreads), 0, s,
+      hipLaunchKernelGGL(staged_keys_kernel<kChunkThreads>, dim3(p.nchunks), dim3(kChunkThreads), 0, s,
                          reinterpret_cast<const uint4*>(a.particles), a.n, grid_params(a),
                          a.celdaDe, rows, p.tile_shift, p.ntiles, chunk_rec, chunk_idx);
       break;
