@@ -335,3 +335,32 @@ def test_gpu_validation_errors(ugp):
     assert e.value.status == ugp.UGP_ERR_ARG
     with pytest.raises(ValueError):
         ugp.grid_build(torch.from_numpy(wl.particles), *args)  # CPU tensor: no CPU path
+
+
+@pytest.mark.parametrize("mode", ["atomic", "stable"])
+def test_graph_capture_replays(ugp, orc, mode):
+    """A build captured in a HIP graph replays correctly, several times, with
+    eager work (new particle data, an eager build) between the replays."""
+    dev = torch.device("cuda:0")
+    flags = ugp.FLAG_STABLE if mode == "stable" else 0
+    wl0 = W.make_uniform(250_000, 128, seed=40)
+    parts = torch.from_numpy(wl0.particles).to(dev)
+    args = (wl0.origin.tolist(), float(wl0.cell_size), wl0.dims.tolist())
+    out, ws = ugp.alloc_outputs(wl0.n, wl0.dims.tolist(), dev, flags)
+    ugp.grid_build(parts, *args, stable=(mode == "stable"), out=out, workspace=ws)  # warm-up outside capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ugp.grid_build(parts, *args, stable=(mode == "stable"), out=out, workspace=ws)
+    for rep in range(3):
+        wl = W.make_uniform(250_000, 128, seed=41 + rep)
+        parts.copy_(torch.from_numpy(wl.particles).to(dev))  # eager work between replays
+        eager = ugp.grid_build(parts, *args, stable=(mode == "stable"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = oracle.GridIndex(_u32(out.celdaDe), _u32(out.conteos), _u32(out.inicios), _u32(out.ordenado),
+                               out.reordered.cpu().numpy())
+        ref = orc.grid_build(wl.particles, wl.origin, wl.cell_size, wl.dims)
+        assert_parity(wl, got, ref, mode)
+        assert np.array_equal(_u32(eager.inicios), got.inicios)

@@ -225,11 +225,23 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
   if (staged) {
     // source map: s_map[p] = chunk-array position of tile-local particle p
     uint32_t* s_map = reinterpret_cast<uint32_t*>(s_rec);
+    if (nchunks >= NT / 16) {
+      // many chunks, short runs: each thread expands the runs of its chunks
 #pragma unroll
-    for (uint32_t q = 0; q < kChunksPerThread; ++q) {
-      const uint32_t c = threadIdx.x * kChunksPerThread + q;
-      if (c < nchunks)
-        for (uint32_t k = 0; k < r[q].x; ++k) s_map[s_dst[c] + k] = s_src[c] + k;
+      for (uint32_t q = 0; q < kChunksPerThread; ++q) {
+        const uint32_t c = threadIdx.x * kChunksPerThread + q;
+        if (c < nchunks)
+          for (uint32_t k = 0; k < r[q].x; ++k) s_map[s_dst[c] + k] = s_src[c] + k;
+      }
+    } else {
+      // few chunks, long runs: one wave per run, its lanes striding the run
+      const uint32_t lane = threadIdx.x & 63u;
+      for (uint32_t c = threadIdx.x >> 6; c < nchunks; c += NT / 64) {
+        const uint32_t d0 = s_dst[c];
+        const uint32_t len = ((c + 1 < nchunks) ? s_dst[c + 1] : count) - d0;
+        const uint32_t s0 = s_src[c];
+        for (uint32_t k = lane; k < len; k += 64) s_map[d0 + k] = s0 + k;
+      }
     }
     __syncthreads();
     if (count > 0) {  // count == 0: no valid source to clamp the idle lanes to
