@@ -221,9 +221,9 @@ def write_traffic_file(traffic: dict, path: str, command: str) -> None:
         f.write(f"# command: {command}\n")
         f.write(f"source_sha256_16: {source_digest()}\n")
         for k, b in traffic.items():
-            base = k.split("<")[0]
-            stage = KERNEL_STAGE.get(base, base)
-            f.write(f"{stage}_bytes_per_dispatch: {b:.0f}\n")
+            stage = KERNEL_STAGE.get(k.split("<")[0])
+            if stage is not None:  # this library's kernels only
+                f.write(f"{stage}_bytes_per_dispatch: {b:.0f}\n")
 
 
 def main(argv=None) -> int:
