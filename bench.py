@@ -304,6 +304,30 @@ def main(argv=None) -> int:
     step_ms = [starts[k].elapsed_time(ends[k]) for k in range(K)]
     ms_per_step = sum(step_ms) / K
 
+    # ---- achievable bandwidth on this device: cold device-to-device copies,
+    # one of 1 GiB moved (512 MiB read + 512 MiB written) and one moving the
+    # same number of bytes as the byte model of one step ----
+    def copy_gbs(nbytes_moved: int) -> float:
+        half = max(1, nbytes_moved // 2)
+        src = torch.ones(half, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        t = []
+        for _ in range(5):
+            evict()
+            c0 = torch.cuda.Event(enable_timing=True)
+            c1 = torch.cuda.Event(enable_timing=True)
+            c0.record(stream)
+            dst.copy_(src)
+            c1.record(stream)
+            torch.cuda.synchronize()
+            t.append(c0.elapsed_time(c1))
+        del src, dst
+        return 2 * half / (statistics.median(t) * 1e-3) / 1e9
+
+    copy_big = copy_gbs(1 << 30)
+    copy_same = copy_gbs(116 * n + 16 * cells + 4)
+
     # ---- warm: K back-to-back builds between one event pair ----
     w0 = torch.cuda.Event(enable_timing=True)
     w1 = torch.cuda.Event(enable_timing=True)
@@ -392,6 +416,10 @@ def main(argv=None) -> int:
             "timing": "cold: 1 GiB read-only cache eviction before each step, outside the per-step HIP events",
         },
         "hbm_frac_e2e": (b_total / t_s) / (HBM_PEAK_GBS * 1e9),
+        "achievable_copy_GBps": {"1GiB": round(copy_big, 1), "same_bytes": round(copy_same, 1),
+                                 "note": "cold device-to-device copy, bytes read + written / time"},
+        "frac_of_copy_e2e": {"1GiB": (b_total / t_s) / (copy_big * 1e9),
+                             "same_bytes": (b_total / t_s) / (copy_same * 1e9)},
         "alg_bytes_per_step": b_total,
         "step_ms_median": statistics.median(step_ms),
         "step_ms_p10_p90": [float(np.percentile(step_ms, 10)), float(np.percentile(step_ms, 90))],

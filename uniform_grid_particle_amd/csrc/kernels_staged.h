@@ -96,23 +96,24 @@ __global__ __launch_bounds__(CT) void staged_keys_kernel(
     w[4][j] = b.x; w[5][j] = b.y; w[6][j] = b.z; w[7][j] = b.w;
   }
   __syncthreads();  // s_hist zeroed
-  uint32_t tile[kChunkItems], rank[kChunkItems];
+  // cell keys and tile ranks; every global store of this kernel is issued
+  // at its end: the wait for a record register loaded earlier would also
+  // wait for every store issued since (one counter tracks both)
+  uint32_t cellv[kChunkItems], rank[kChunkItems];
 #pragma unroll
   for (int j = 0; j < kChunkItems; ++j) {
     const uint32_t i = base + j * kChunkThreads + threadIdx.x;
-    tile[j] = 0xFFFFFFFFu;
+    cellv[j] = 0xFFFFFFFFu;
     rank[j] = 0u;
     if (i < n) {
-      const uint32_t c = cell_of(__uint_as_float(w[0][j]), __uint_as_float(w[1][j]),
-                                 __uint_as_float(w[2][j]), g);
-      celdaDe[i] = c;
-      tile[j] = c >> tile_shift;
-      rank[j] = atomicAdd(&s_hist[tile[j]], 1u);
+      cellv[j] = cell_of(__uint_as_float(w[0][j]), __uint_as_float(w[1][j]),
+                         __uint_as_float(w[2][j]), g);
+      rank[j] = atomicAdd(&s_hist[cellv[j] >> tile_shift], 1u);
     }
   }
   __syncthreads();
   // exclusive scan of the tile histogram: kTilesPerThread consecutive bins per thread
-  uint32_t cnt[kTilesPerThread];
+  uint32_t cnt[kTilesPerThread], exq[kTilesPerThread];
   uint32_t sum = 0;
 #pragma unroll
   for (uint32_t q = 0; q < kTilesPerThread; ++q) {
@@ -125,29 +126,36 @@ __global__ __launch_bounds__(CT) void staged_keys_kernel(
 #pragma unroll
   for (uint32_t q = 0; q < kTilesPerThread; ++q) {
     const uint32_t t = threadIdx.x * kTilesPerThread + q;
-    if (t < ntiles) {
-      rows[static_cast<size_t>(blockIdx.x) * ntiles + t] = make_uint2(cnt[q], ex);
-      s_hist[t] = ex;  // now the first local slot of each tile
-    }
+    exq[q] = ex;
+    if (t < ntiles) s_hist[t] = ex;  // now the first local slot of each tile
     ex += cnt[q];
   }
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < kChunkItems; ++j) {
-    if (tile[j] != 0xFFFFFFFFu) {
-      const uint32_t local = s_hist[tile[j]] + rank[j];
+    if (cellv[j] != 0xFFFFFFFFu) {
+      const uint32_t local = s_hist[cellv[j] >> tile_shift] + rank[j];
       s_rec[2 * local] = make_uint4(w[0][j], w[1][j], w[2][j], w[3][j]);
       s_rec[2 * local + 1] = make_uint4(w[4][j], w[5][j], w[6][j], w[7][j]);
       s_idx[local] = base + j * kChunkThreads + threadIdx.x;
     }
   }
   __syncthreads();
-  // the chunk in tile order, written contiguously
+  // the chunk in tile order, written contiguously (plain stores: the tile
+  // kernel reads these lines next), then the rows and the cell keys
   const uint32_t in_chunk = total;  // valid particles of this chunk
   uint4* dst = chunk_rec + static_cast<size_t>(base) * 2u;
-  for (uint32_t q = threadIdx.x; q < 2 * in_chunk; q += kChunkThreads) store_stream(dst + q, s_rec[q]);
+  for (uint32_t q = threadIdx.x; q < 2 * in_chunk; q += kChunkThreads) dst[q] = s_rec[q];
   uint32_t* dsti = chunk_idx + base;
-  for (uint32_t q = threadIdx.x; q < in_chunk; q += kChunkThreads) store_stream(dsti + q, s_idx[q]);
+  for (uint32_t q = threadIdx.x; q < in_chunk; q += kChunkThreads) dsti[q] = s_idx[q];
+#pragma unroll
+  for (uint32_t q = 0; q < kTilesPerThread; ++q) {
+    const uint32_t t = threadIdx.x * kTilesPerThread + q;
+    if (t < ntiles) rows[static_cast<size_t>(blockIdx.x) * ntiles + t] = make_uint2(cnt[q], exq[q]);
+  }
+#pragma unroll
+  for (int j = 0; j < kChunkItems; ++j)
+    if (cellv[j] != 0xFFFFFFFFu) celdaDe[base + j * kChunkThreads + threadIdx.x] = cellv[j];
 }
 
 // tile_sort: NT threads; the tile of block b (tile_of_block) owns cells
@@ -218,10 +226,12 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
   };
 
   const bool staged = count <= kStagedCap;
-  // records held in registers as scalar arrays (static indices)
-  uint32_t w[8][kStagedRegs], idx[kStagedRegs], loc[kStagedRegs];
+  // records held in registers as scalar arrays (static indices); lr packs a
+  // particle's tile-local cell (high half) and its rank in that cell (low
+  // half, < kStagedCap), all ones when the lane holds no particle
+  uint32_t w[8][kStagedRegs], idx[kStagedRegs], lr[kStagedRegs];
 #pragma unroll
-  for (int k = 0; k < kStagedRegs; ++k) loc[k] = 0xFFFFFFFFu;  // no particle
+  for (int k = 0; k < kStagedRegs; ++k) lr[k] = 0xFFFFFFFFu;
   if (staged) {
     // source map: s_map[p] = chunk-array position of tile-local particle p
     uint32_t* s_map = reinterpret_cast<uint32_t*>(s_rec);
@@ -259,14 +269,15 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
         w[0][k] = a.x; w[1][k] = a.y; w[2][k] = a.z; w[3][k] = a.w;
         w[4][k] = b.x; w[5][k] = b.y; w[6][k] = b.z; w[7][k] = b.w;
       }
+      // count each particle and keep its rank: its slot is later the
+      // cell's start plus that rank
 #pragma unroll
       for (int k = 0; k < kStagedRegs; ++k) {
         const uint32_t p = threadIdx.x + k * NT;
         if (p < count) {
-          const uint32_t c = cell_of(__uint_as_float(w[0][k]), __uint_as_float(w[1][k]),
-                                     __uint_as_float(w[2][k]), g);
-          loc[k] = c - cell0;
-          if (loc[k] < tc) atomicAdd(&s_cnt[loc[k]], 1u);
+          const uint32_t loc = cell_of(__uint_as_float(w[0][k]), __uint_as_float(w[1][k]),
+                                       __uint_as_float(w[2][k]), g) - cell0;
+          if (loc < tc) lr[k] = (loc << 16) | atomicAdd(&s_cnt[loc], 1u);
         }
       }
     }
@@ -280,18 +291,13 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
   }
   __syncthreads();
 
-  // histogram out: lane-contiguous 16-byte stores
-  const uint4* s_cnt4 = reinterpret_cast<const uint4*>(s_cnt);
-  const uint32_t tc4 = tc / 4;  // full vectors (tiles start at multiples of 4096 cells)
-  for (uint32_t q = threadIdx.x; q < tc4; q += NT)
-    reinterpret_cast<uint4*>(conteos + cell0)[q] = s_cnt4[q];
-  for (uint32_t j = 4 * tc4 + threadIdx.x; j < tc; j += NT) conteos[cell0 + j] = s_cnt[j];
   // exclusive scan in LDS: kPer consecutive cells per thread, then the
-  // block scan of the per-thread sums; s_cnt becomes the slot cursors
+  // block scan of the per-thread sums; s_cnt becomes the tile-local starts
+  // (cells past tc count 0, so their start is the tile total)
   const uint32_t j0 = threadIdx.x * kPer;
   uint32_t sum = 0;
 #pragma unroll
-  for (uint32_t q = 0; q < kPer; ++q) sum += s_cnt[j0 + q];  // cells >= tc hold 0
+  for (uint32_t q = 0; q < kPer; ++q) sum += s_cnt[j0 + q];
   uint32_t tot;
   uint32_t run = block_exclusive_sum<NT>(sum, s_wave, &tot);
 #pragma unroll
@@ -301,20 +307,32 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
     run += v;
   }
   __syncthreads();
-  // starts out: lane-contiguous 16-byte stores, offset by the tile start
-  for (uint32_t q = threadIdx.x; q < tc4; q += NT) {
-    const uint4 v = s_cnt4[q];
-    reinterpret_cast<uint4*>(inicios + cell0)[q] = make_uint4(bs + v.x, bs + v.y, bs + v.z, bs + v.w);
-  }
-  for (uint32_t j = 4 * tc4 + threadIdx.x; j < tc; j += NT) inicios[cell0 + j] = bs + s_cnt[j];
-  if (t == ntiles - 1 && threadIdx.x == 0) inicios[cells] = bs + count;
-  __syncthreads();  // every start read before the cursors advance
+
+  // conteos and inicios out, from the starts: a cell's count is the next
+  // start minus its own. Lane-contiguous 16-byte stores (tiles start at
+  // multiples of 4096 cells).
+  auto write_counts_starts = [&]() {
+    const uint4* s_cnt4 = reinterpret_cast<const uint4*>(s_cnt);
+    const uint32_t tc4 = tc / 4;
+    for (uint32_t q = threadIdx.x; q < tc4; q += NT) {
+      const uint4 v = s_cnt4[q];
+      const uint32_t next = (4 * q + 4 < kTileCells) ? s_cnt[4 * q + 4] : tot;
+      reinterpret_cast<uint4*>(conteos + cell0)[q] = make_uint4(v.y - v.x, v.z - v.y, v.w - v.z, next - v.w);
+      reinterpret_cast<uint4*>(inicios + cell0)[q] = make_uint4(bs + v.x, bs + v.y, bs + v.z, bs + v.w);
+    }
+    for (uint32_t j = 4 * tc4 + threadIdx.x; j < tc; j += NT) {
+      const uint32_t next = (j + 1 < kTileCells) ? s_cnt[j + 1] : tot;
+      conteos[cell0 + j] = next - s_cnt[j];
+      inicios[cell0 + j] = bs + s_cnt[j];
+    }
+    if (t == ntiles - 1 && threadIdx.x == 0) inicios[cells] = bs + count;
+  };
 
   if (staged) {
     uint32_t slot[kStagedRegs];
 #pragma unroll
     for (int k = 0; k < kStagedRegs; ++k)
-      slot[k] = (loc[k] < tc) ? atomicAdd(&s_cnt[loc[k]], 1u) : 0xFFFFFFFFu;
+      slot[k] = (lr[k] != 0xFFFFFFFFu) ? s_cnt[lr[k] >> 16] + (lr[k] & 0xFFFFu) : 0xFFFFFFFFu;
     for (uint32_t w0 = 0; w0 < count; w0 += kStagedWin) {
       const uint32_t wn = (count - w0 < kStagedWin) ? count - w0 : kStagedWin;
 #pragma unroll
@@ -338,7 +356,12 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
       }
       __syncthreads();
     }
+    // last: a later wait for a register loaded before a store would also
+    // wait for that store (one counter tracks loads and stores)
+    write_counts_starts();
   } else {
+    write_counts_starts();
+    __syncthreads();  // every start read before the cursors advance
     for (uint32_t p = threadIdx.x; p < count; p += NT) {
       const uint32_t s = source_of(p);
       const uint4 a = chunk_rec[static_cast<size_t>(s) * 2u];
