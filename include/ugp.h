@@ -156,6 +156,40 @@ int ugp_grid_build_stage(uint32_t stage, const ugp_particle *particles, uint32_t
                          uint32_t *ordenado, ugp_particle *reordered, void *workspace,
                          size_t workspace_bytes, uint32_t flags, void *stream);
 
+/* ugp_grid_build() plus the overflow diagnostics of page "Contar
+ * partículas por celda", section "Detectar el desbordamiento sin salir de
+ * la GPU", computed on the device in the same call:
+ *   capacity  particles a cell may hold (any value; 0 makes every insertion
+ *             an overflow)
+ *   diag      device, out: 2 u32, 4-byte aligned, must not overlap any other
+ *             buffer of the call.
+ *             diag[0] = largest occupancy of any cell = max_c conteos[c]
+ *                       (0 when n == 0);
+ *             diag[1] = insertions that found their cell already holding
+ *                       `capacity` or more particles
+ *                     = sum_c max(0, conteos[c] - capacity).
+ * Both are independent of the order of insertion. On grids of up to 2^22
+ * cells with n <= 2^21 the reduction runs inside the tile kernel over its
+ * LDS histogram (no extra memory traffic); otherwise a reduction over
+ * conteos follows the scatter. Other arguments and errors as
+ * ugp_grid_build(); UGP_ERR_NULL for a NULL diag. */
+int ugp_grid_build_diag(const ugp_particle *particles, uint32_t n, const float origin[3],
+                        float cell_size, const uint32_t dims[3], uint32_t *celdaDe,
+                        uint32_t *conteos, uint32_t *inicios, uint32_t *ordenado,
+                        ugp_particle *reordered, void *workspace, size_t workspace_bytes,
+                        uint32_t capacity, uint32_t *diag, uint32_t flags, void *stream);
+
+/* The same two diagnostics from an existing histogram (for example one
+ * read back every few frames, as the page suggests):
+ *   conteos   device, in: `cells` u32, 16-byte aligned (may be NULL when
+ *             cells == 0)
+ *   diag      device, out: 2 u32 as in ugp_grid_build_diag(), 4-byte
+ *             aligned, must not overlap conteos.
+ * Returns UGP_OK once enqueued, UGP_ERR_NULL / UGP_ERR_ALIGN /
+ * UGP_ERR_ALIAS with nothing enqueued, or UGP_ERR_HIP. */
+int ugp_cell_diag(const uint32_t *conteos, uint32_t cells, uint32_t capacity, uint32_t *diag,
+                  void *stream);
+
 /* ugp_grid_build() with two caller-owned HIP events (hipEvent_t passed as
  * void*) recorded on `stream` immediately before and after stage slot
  * `timed_stage`, in the same call, so no host work separates the stages.

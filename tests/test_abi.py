@@ -169,3 +169,25 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(mod, "LIB_PATH", str(tmp_path / "absent.so"))
     with pytest.raises(RuntimeError, match="not built"):
         mod.load_library()
+
+
+def test_diag_validation_on_host(lib):
+    """ugp_grid_build_diag / ugp_cell_diag reject bad arguments before any launch."""
+    b = 1 << 40
+    o = (ctypes.c_float * 3)(0, 0, 0)
+    d = (ctypes.c_uint32 * 3)(4, 4, 4)
+
+    def build_diag(diag, h=1.0):
+        return lib.ugp_grid_build_diag(b, 4, o, ctypes.c_float(h), d, b + (1 << 30), b + (2 << 30),
+                                       b + (3 << 30), b + (4 << 30), b + (5 << 30), b + (6 << 30),
+                                       ctypes.c_size_t(1 << 20), 64, diag, 0, None)
+
+    assert build_diag(None) == ugp.UGP_ERR_NULL
+    assert build_diag(b + (7 << 30) + 2) == ugp.UGP_ERR_ALIGN
+    assert build_diag(b + (2 << 30) + 16) == ugp.UGP_ERR_ALIAS  # inside conteos
+    assert build_diag(b + (7 << 30), h=0.0) == ugp.UGP_ERR_ARG
+    assert lib.ugp_cell_diag(b, 100, 8, None, None) == ugp.UGP_ERR_NULL
+    assert lib.ugp_cell_diag(None, 100, 8, b + (1 << 20), None) == ugp.UGP_ERR_NULL
+    assert lib.ugp_cell_diag(b + 4, 100, 8, b + (1 << 20), None) == ugp.UGP_ERR_ALIGN
+    assert lib.ugp_cell_diag(b, 100, 8, b + (1 << 20) + 1, None) == ugp.UGP_ERR_ALIGN
+    assert lib.ugp_cell_diag(b, 100, 8, b + 396, None) == ugp.UGP_ERR_ALIAS  # last word of conteos

@@ -78,6 +78,10 @@ def load_library():
     lib.ugp_grid_build_stage.argtypes = [_u32, *build_args]
     lib.ugp_grid_build_timed.restype = ctypes.c_int
     lib.ugp_grid_build_timed.argtypes = [*build_args, _u32, _vp, _vp]
+    lib.ugp_grid_build_diag.restype = ctypes.c_int
+    lib.ugp_grid_build_diag.argtypes = [*build_args[:-2], _u32, _vp, _u32, _vp]
+    lib.ugp_cell_diag.restype = ctypes.c_int
+    lib.ugp_cell_diag.argtypes = [_vp, _u32, _u32, _vp, _vp]
     lib.ugp_grid_stage_name.restype = ctypes.c_char_p
     lib.ugp_grid_stage_name.argtypes = [_u32, ctypes.POINTER(_u32), _u32, _u32]
     lib.ugp_scan_workspace_bytes.restype = ctypes.c_int
@@ -222,6 +226,55 @@ def grid_build(
     return out
 
 
+def grid_build_diag(
+    particles: torch.Tensor,
+    origin: Sequence[float],
+    cell_size: float,
+    dims: Sequence[int],
+    capacity: int,
+    *,
+    diag: Optional[torch.Tensor] = None,
+    stable: bool = False,
+    gather: bool = False,
+    out: Optional[GridIndex] = None,
+    workspace: Optional[torch.Tensor] = None,
+    stream=None,
+) -> tuple[GridIndex, torch.Tensor]:
+    """ugp_grid_build_diag: the build plus the overflow diagnostics in `diag`
+    (2 u32 on the GPU: largest cell occupancy, insertions past `capacity`)."""
+    lib = load_library()
+    flags = (FLAG_STABLE if stable else 0) | (FLAG_GATHER if gather else 0)
+    n = int(particles.shape[0])
+    if out is None or workspace is None:
+        o2, w2 = alloc_outputs(n, dims, particles.device, flags)
+        out = out or o2
+        workspace = workspace if workspace is not None else w2
+    if diag is None:
+        diag = torch.empty(2, dtype=torch.int32, device=particles.device)
+    _require_gpu(diag, "diag", torch.int32)
+    if diag.numel() < 2:
+        raise ValueError("diag needs 2 entries")
+    args = _build_args(particles, origin, cell_size, dims, out, workspace, flags, stream)
+    _check(lib.ugp_grid_build_diag(*args[:-2], int(capacity), _ptr(diag), *args[-2:]), "ugp_grid_build_diag")
+    return out, diag
+
+
+def cell_diag(conteos: torch.Tensor, capacity: int, out: Optional[torch.Tensor] = None,
+              stream=None) -> torch.Tensor:
+    """ugp_cell_diag: overflow diagnostics of an existing histogram."""
+    lib = load_library()
+    _require_gpu(conteos, "conteos", torch.int32)
+    if out is None:
+        out = torch.empty(2, dtype=torch.int32, device=conteos.device)
+    _require_gpu(out, "out", torch.int32)
+    if out.numel() < 2:
+        raise ValueError("out needs 2 entries")
+    st = lib.ugp_cell_diag(_ptr(conteos), int(conteos.numel()), int(capacity), _ptr(out),
+                           _stream_handle(conteos.device, stream))
+    _check(st, "ugp_cell_diag")
+    return out
+
+
 def grid_build_stage(stage: int, particles, origin, cell_size, dims, out: GridIndex, workspace,
                      *, flags: int = 0, stream=None) -> None:
     """ugp_grid_build_stage: enqueue one stage with the same arguments."""
@@ -285,7 +338,8 @@ def as_u32_numpy(t: torch.Tensor):
 
 
 __all__ = [
-    "GridIndex", "UGPError", "alloc_outputs", "as_u32_numpy", "exclusive_scan_u32", "grid_build",
+    "GridIndex", "UGPError", "alloc_outputs", "as_u32_numpy", "cell_diag", "exclusive_scan_u32", "grid_build",
+    "grid_build_diag",
     "grid_build_stage", "grid_build_timed", "library_path", "load_library", "reorder", "stage_names",
     "status_string", "workspace_bytes", "FLAG_STABLE", "FLAG_GATHER", "NUM_STAGES",
 ]

@@ -37,6 +37,7 @@
 #pragma once
 
 #include "common.h"
+#include "kernels_diag.h"
 
 namespace ugp {
 
@@ -71,7 +72,7 @@ template <int CT>
 __global__ __launch_bounds__(CT) void staged_keys_kernel(
     const uint4* __restrict__ parts, uint32_t n, GridParams g, uint32_t* __restrict__ celdaDe,
     uint2* __restrict__ rows, uint32_t tile_shift, uint32_t ntiles, uint4* __restrict__ chunk_rec,
-    uint32_t* __restrict__ chunk_idx) {
+    uint32_t* __restrict__ chunk_idx, uint32_t* __restrict__ diag) {
   constexpr int kChunkThreads = CT;
   constexpr uint32_t kChunk = CT * kChunkItems;
   constexpr uint32_t kTilesPerThread = kStagedMaxTiles / CT;  // tile bins per thread
@@ -82,6 +83,8 @@ __global__ __launch_bounds__(CT) void staged_keys_kernel(
   __shared__ uint32_t s_wave[kChunkThreads / 64];
 
   for (uint32_t t = threadIdx.x; t < kStagedMaxTiles; t += kChunkThreads) s_hist[t] = 0u;
+  // the overflow diagnostics (when asked for) accumulate in tile_sort
+  if (diag != nullptr && blockIdx.x == 0 && threadIdx.x < 2) diag[threadIdx.x] = 0u;
   const uint32_t base = blockIdx.x * kChunk;
   // the records stay in registers (scalar arrays, static indices) until
   // they are placed in LDS in tile order
@@ -161,12 +164,16 @@ __global__ __launch_bounds__(CT) void staged_keys_kernel(
 // tile_sort: NT threads; the tile of block b (tile_of_block) owns cells
 // [t << SHIFT, (t+1) << SHIFT); WIN records are staged in LDS at a time.
 // MOVE: also write the records (otherwise a separate gather follows).
-template <bool MOVE, uint32_t SHIFT, int NT, uint32_t WIN>
+// DIAG: also fold the tile's histogram into the overflow diagnostics
+// (diag[0] max occupancy, diag[1] overflowing insertions over capacity cap;
+// both zeroed by chunk_sort).
+template <bool MOVE, bool DIAG, uint32_t SHIFT, int NT, uint32_t WIN>
 __global__ __launch_bounds__(NT) void staged_cells_kernel(
     const uint2* __restrict__ rows, uint32_t nchunks, uint32_t chunk, uint32_t ntiles, GridParams g,
     uint32_t cells, uint32_t n, const uint4* __restrict__ chunk_rec,
     const uint32_t* __restrict__ chunk_idx, uint32_t* __restrict__ conteos,
-    uint32_t* __restrict__ inicios, uint32_t* __restrict__ ordenado, uint4* __restrict__ dst) {
+    uint32_t* __restrict__ inicios, uint32_t* __restrict__ ordenado, uint4* __restrict__ dst,
+    uint32_t cap, uint32_t* __restrict__ diag) {
   constexpr uint32_t kTileCells = 1u << SHIFT;
   constexpr uint32_t kPer = kTileCells / NT;  // cells per thread in the scan
   constexpr uint32_t kChunksPerThread = kStagedMaxChunks / NT;
@@ -181,6 +188,7 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
   __shared__ uint4 s_rec[2 * kStagedWin];
   __shared__ uint32_t s_idx[kStagedWin];
   __shared__ uint32_t s_wave[NT / 64];
+  __shared__ uint32_t s_dm[DIAG ? NT / 64 : 1], s_do[DIAG ? NT / 64 : 1];
 
   const uint32_t t = tile_of_block(blockIdx.x, ntiles);
   const uint32_t cell0 = t << SHIFT;
@@ -310,22 +318,47 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
 
   // conteos and inicios out, from the starts: a cell's count is the next
   // start minus its own. Lane-contiguous 16-byte stores (tiles start at
-  // multiples of 4096 cells).
+  // multiples of 4096 cells). DIAG: the same counts feed the overflow
+  // diagnostics (one more barrier, after which thread 0 publishes).
   auto write_counts_starts = [&]() {
     const uint4* s_cnt4 = reinterpret_cast<const uint4*>(s_cnt);
     const uint32_t tc4 = tc / 4;
+    uint32_t dmax = 0, dover = 0;
     for (uint32_t q = threadIdx.x; q < tc4; q += NT) {
       const uint4 v = s_cnt4[q];
       const uint32_t next = (4 * q + 4 < kTileCells) ? s_cnt[4 * q + 4] : tot;
-      reinterpret_cast<uint4*>(conteos + cell0)[q] = make_uint4(v.y - v.x, v.z - v.y, v.w - v.z, next - v.w);
+      const uint4 c = make_uint4(v.y - v.x, v.z - v.y, v.w - v.z, next - v.w);
+      reinterpret_cast<uint4*>(conteos + cell0)[q] = c;
       reinterpret_cast<uint4*>(inicios + cell0)[q] = make_uint4(bs + v.x, bs + v.y, bs + v.z, bs + v.w);
+      if (DIAG) {
+        const uint32_t a = (c.x > c.y) ? c.x : c.y;
+        const uint32_t b = (c.z > c.w) ? c.z : c.w;
+        dmax = (a > dmax) ? a : dmax;
+        dmax = (b > dmax) ? b : dmax;
+        dover += overflow_of(c.x, cap) + overflow_of(c.y, cap) + overflow_of(c.z, cap) + overflow_of(c.w, cap);
+      }
     }
     for (uint32_t j = 4 * tc4 + threadIdx.x; j < tc; j += NT) {
       const uint32_t next = (j + 1 < kTileCells) ? s_cnt[j + 1] : tot;
-      conteos[cell0 + j] = next - s_cnt[j];
+      const uint32_t c = next - s_cnt[j];
+      conteos[cell0 + j] = c;
       inicios[cell0 + j] = bs + s_cnt[j];
+      if (DIAG) {
+        dmax = (c > dmax) ? c : dmax;
+        dover += overflow_of(c, cap);
+      }
     }
     if (t == ntiles - 1 && threadIdx.x == 0) inicios[cells] = bs + count;
+    if (DIAG) {
+      dmax = wave_max_u32(dmax);
+      dover = wave_add_u32(dover);
+      if ((threadIdx.x & 63) == 0) {
+        s_dm[threadIdx.x >> 6] = dmax;
+        s_do[threadIdx.x >> 6] = dover;
+      }
+      __syncthreads();
+      publish_diag<NT>(s_dm, s_do, diag);
+    }
   };
 
   if (staged) {

@@ -19,7 +19,9 @@
 //   direct  larger grids: the global-atomic chain of kernels_direct.h
 //           (clear, count, scan, scatter).
 // Stable mode (ascending particle index inside every cell) and gather
-// mode add kernels_reorder.h passes after the scatter.
+// mode add kernels_reorder.h passes after the scatter. The overflow
+// diagnostics are folded into the staged tile kernel (a compile-time
+// variant); the other paths reduce conteos once it is final.
 
 #include <hip/hip_runtime.h>
 
@@ -29,6 +31,7 @@
 #include <cstdint>
 
 #include "common.h"
+#include "kernels_diag.h"
 #include "kernels_direct.h"
 #include "kernels_reorder.h"
 #include "kernels_staged.h"
@@ -191,6 +194,8 @@ struct BuildArgs {
   size_t workspace_bytes;
   uint32_t flags;
   hipStream_t stream;
+  uint32_t capacity;  // overflow diagnostics: capacity per cell
+  uint32_t* diag;     // overflow diagnostics out (2 words), or nullptr
 };
 
 int validate(const BuildArgs& a, Plan* plan) {
@@ -208,16 +213,17 @@ int validate(const BuildArgs& a, Plan* plan) {
   if (a.n > 0 && (!aligned(a.particles, 16) || !aligned(a.reordered, 16) ||
                   !aligned(a.celdaDe, 16) || !aligned(a.ordenado, 16)))
     return UGP_ERR_ALIGN;
+  if (a.diag && !aligned(a.diag, 4)) return UGP_ERR_ALIGN;
   if (a.workspace_bytes < plan->total) return UGP_ERR_WORKSPACE;
   const size_t n = a.n;
   const size_t c = plan->cells;
-  const Span spans[7] = {
+  const Span spans[8] = {
       span_of(a.particles, 32 * n),    span_of(a.celdaDe, 4 * n),   span_of(a.conteos, 4 * c),
       span_of(a.inicios, 4 * (c + 1)), span_of(a.ordenado, 4 * n), span_of(a.reordered, 32 * n),
-      span_of(a.workspace, plan->total),
+      span_of(a.workspace, plan->total), span_of(a.diag, a.diag ? 8 : 0),
   };
-  for (int i = 0; i < 7; ++i)
-    for (int j = i + 1; j < 7; ++j)
+  for (int i = 0; i < 8; ++i)
+    for (int j = i + 1; j < 8; ++j)
       if (overlap(spans[i], spans[j])) return UGP_ERR_ALIAS;
   return UGP_OK;
 }
@@ -270,24 +276,37 @@ void launch_tiled_cells(uint32_t shift, dim3 grid, hipStream_t s, const uint2* b
   }
 }
 
-template <bool MOVE>
+template <bool MOVE, bool DIAG>
 void launch_staged_cells(uint32_t shift, dim3 grid, hipStream_t s, const uint2* rows,
                          uint32_t nchunks, uint32_t ntiles, GridParams g, uint32_t cells,
                          uint32_t n, const uint4* chunk_rec, const uint32_t* chunk_idx,
-                         uint32_t* conteos, uint32_t* inicios, uint32_t* ordenado, uint4* dst) {
+                         uint32_t* conteos, uint32_t* inicios, uint32_t* ordenado, uint4* dst,
+                         uint32_t cap, uint32_t* diag) {
   const dim3 block(kCellsThreads);
   if (shift == 12)
-    hipLaunchKernelGGL((staged_cells_kernel<MOVE, 12, kCellsThreads, kCellsWin>), grid, block, 0, s,
-                       rows, nchunks, kChunk, ntiles, g, cells, n, chunk_rec, chunk_idx, conteos,
-                       inicios, ordenado, dst);
+    hipLaunchKernelGGL((staged_cells_kernel<MOVE, DIAG, 12, kCellsThreads, kCellsWin>), grid, block,
+                       0, s, rows, nchunks, kChunk, ntiles, g, cells, n, chunk_rec, chunk_idx,
+                       conteos, inicios, ordenado, dst, cap, diag);
   else if (shift == 13)
-    hipLaunchKernelGGL((staged_cells_kernel<MOVE, 13, kCellsThreads, kCellsWin>), grid, block, 0, s,
-                       rows, nchunks, kChunk, ntiles, g, cells, n, chunk_rec, chunk_idx, conteos,
-                       inicios, ordenado, dst);
+    hipLaunchKernelGGL((staged_cells_kernel<MOVE, DIAG, 13, kCellsThreads, kCellsWin>), grid, block,
+                       0, s, rows, nchunks, kChunk, ntiles, g, cells, n, chunk_rec, chunk_idx,
+                       conteos, inicios, ordenado, dst, cap, diag);
   else
-    hipLaunchKernelGGL((staged_cells_kernel<MOVE, 14, kCellsThreads, kCellsWin>), grid, block, 0, s,
-                       rows, nchunks, kChunk, ntiles, g, cells, n, chunk_rec, chunk_idx, conteos,
-                       inicios, ordenado, dst);
+    hipLaunchKernelGGL((staged_cells_kernel<MOVE, DIAG, 14, kCellsThreads, kCellsWin>), grid, block,
+                       0, s, rows, nchunks, kChunk, ntiles, g, cells, n, chunk_rec, chunk_idx,
+                       conteos, inicios, ordenado, dst, cap, diag);
+}
+
+// Overflow diagnostics of a final conteos array: zero the two words, then
+// reduce (paths other than staged, and the standalone entry point).
+void enqueue_cell_diag(const uint32_t* conteos, uint64_t cells, uint32_t cap, uint32_t* diag,
+                       hipStream_t s) {
+  launch_clear(diag, 2, nullptr, 0, s);
+  if (cells == 0) return;
+  uint32_t blocks = blocks_for((cells + 3) / 4, static_cast<uint64_t>(kDiagBlock) * kDiagItems);
+  if (blocks > kDiagMaxGrid) blocks = kDiagMaxGrid;
+  hipLaunchKernelGGL(diag_kernel, dim3(blocks), dim3(kDiagBlock), 0, s, conteos,
+                     static_cast<uint32_t>(cells), cap, diag);
 }
 
 // Stable-order and gather passes, shared by every path.
@@ -319,18 +338,29 @@ void enqueue_staged(uint32_t stage, const BuildArgs& a, const Plan& p) {
     case 0:
       hipLaunchKernelGGL(staged_keys_kernel<kChunkThreads>, dim3(p.nchunks), dim3(kChunkThreads), 0, s,
                          reinterpret_cast<const uint4*>(a.particles), a.n, grid_params(a),
-                         a.celdaDe, rows, p.tile_shift, p.ntiles, chunk_rec, chunk_idx);
+                         a.celdaDe, rows, p.tile_shift, p.ntiles, chunk_rec, chunk_idx, a.diag);
       break;
-    case 3:
-      if (p.gather)
-        launch_staged_cells<false>(p.tile_shift, dim3(p.ntiles), s, rows, p.nchunks, p.ntiles,
-                                   grid_params(a), cells, a.n, chunk_rec, chunk_idx, a.conteos,
-                                   a.inicios, a.ordenado, nullptr);
+    case 3: {
+      uint4* dst = p.gather ? nullptr : reinterpret_cast<uint4*>(a.reordered);
+      const dim3 grid(p.ntiles);
+      if (p.gather && a.diag)
+        launch_staged_cells<false, true>(p.tile_shift, grid, s, rows, p.nchunks, p.ntiles,
+                                         grid_params(a), cells, a.n, chunk_rec, chunk_idx,
+                                         a.conteos, a.inicios, a.ordenado, dst, a.capacity, a.diag);
+      else if (p.gather)
+        launch_staged_cells<false, false>(p.tile_shift, grid, s, rows, p.nchunks, p.ntiles,
+                                          grid_params(a), cells, a.n, chunk_rec, chunk_idx,
+                                          a.conteos, a.inicios, a.ordenado, dst, 0u, nullptr);
+      else if (a.diag)
+        launch_staged_cells<true, true>(p.tile_shift, grid, s, rows, p.nchunks, p.ntiles,
+                                        grid_params(a), cells, a.n, chunk_rec, chunk_idx,
+                                        a.conteos, a.inicios, a.ordenado, dst, a.capacity, a.diag);
       else
-        launch_staged_cells<true>(p.tile_shift, dim3(p.ntiles), s, rows, p.nchunks, p.ntiles,
-                                  grid_params(a), cells, a.n, chunk_rec, chunk_idx, a.conteos,
-                                  a.inicios, a.ordenado, reinterpret_cast<uint4*>(a.reordered));
+        launch_staged_cells<true, false>(p.tile_shift, grid, s, rows, p.nchunks, p.ntiles,
+                                         grid_params(a), cells, a.n, chunk_rec, chunk_idx,
+                                         a.conteos, a.inicios, a.ordenado, dst, 0u, nullptr);
       break;
+    }
     case 4:
       if (p.stable) enqueue_stable_sort(a, p, ws);
       break;
@@ -372,6 +402,7 @@ void enqueue_tiled(uint32_t stage, const BuildArgs& a, const Plan& p) {
                                  cells, a.n, a.conteos, a.inicios, a.ordenado,
                                  reinterpret_cast<const uint4*>(a.particles),
                                  reinterpret_cast<uint4*>(a.reordered));
+      if (a.diag) enqueue_cell_diag(a.conteos, p.cells, a.capacity, a.diag, s);
       break;
     case 4:
       if (p.stable) enqueue_stable_sort(a, p, ws);
@@ -412,6 +443,7 @@ void enqueue_direct(uint32_t stage, const BuildArgs& a, const Plan& p) {
         hipLaunchKernelGGL(scatter_kernel<true>, pgrid, dim3(kBlock), 0, s, a.celdaDe, a.n, cells,
                            cursor, a.ordenado, reinterpret_cast<const uint4*>(a.particles),
                            reinterpret_cast<uint4*>(a.reordered));
+      if (a.diag) enqueue_cell_diag(a.conteos, p.cells, a.capacity, a.diag, s);
       break;
     case 4:
       if (p.stable) enqueue_stable_sort(a, p, ws);
@@ -429,7 +461,7 @@ int enqueue_stage(uint32_t stage, const BuildArgs& a, const Plan& p) {
   switch (p.path) {
     case Path::kEmpty:
       if (stage == 0) {
-        launch_clear(a.conteos, p.cells, nullptr, 0, a.stream);
+        launch_clear(a.conteos, p.cells, a.diag, a.diag ? 2u : 0u, a.stream);
         launch_clear(a.inicios, p.cells + 1, nullptr, 0, a.stream);
       }
       break;
@@ -452,7 +484,8 @@ BuildArgs make_args(const ugp_particle* particles, uint32_t n, const float origi
                     size_t workspace_bytes, uint32_t flags, void* stream) {
   return BuildArgs{particles, n,        origin,          cell_size, dims,
                    celdaDe,   conteos,  inicios,         ordenado,  reordered,
-                   workspace, workspace_bytes, flags, static_cast<hipStream_t>(stream)};
+                   workspace, workspace_bytes, flags, static_cast<hipStream_t>(stream),
+                   0u,        nullptr};
 }
 
 }  // namespace
@@ -523,6 +556,35 @@ int ugp_grid_build(const ugp_particle* particles, uint32_t n, const float origin
     if (st != UGP_OK) return st;
   }
   return UGP_OK;
+}
+
+int ugp_grid_build_diag(const ugp_particle* particles, uint32_t n, const float origin[3],
+                        float cell_size, const uint32_t dims[3], uint32_t* celdaDe,
+                        uint32_t* conteos, uint32_t* inicios, uint32_t* ordenado,
+                        ugp_particle* reordered, void* workspace, size_t workspace_bytes,
+                        uint32_t capacity, uint32_t* diag, uint32_t flags, void* stream) {
+  if (!diag) return UGP_ERR_NULL;
+  BuildArgs a = make_args(particles, n, origin, cell_size, dims, celdaDe, conteos, inicios,
+                          ordenado, reordered, workspace, workspace_bytes, flags, stream);
+  a.capacity = capacity;
+  a.diag = diag;
+  Plan p;
+  int st = validate(a, &p);
+  if (st != UGP_OK) return st;
+  for (uint32_t stage = 0; stage < UGP_NUM_STAGES; ++stage) {
+    st = enqueue_stage(stage, a, p);
+    if (st != UGP_OK) return st;
+  }
+  return UGP_OK;
+}
+
+int ugp_cell_diag(const uint32_t* conteos, uint32_t cells, uint32_t capacity, uint32_t* diag,
+                  void* stream) {
+  if (!diag || (cells > 0 && !conteos)) return UGP_ERR_NULL;
+  if (!aligned(diag, 4) || (cells > 0 && !aligned(conteos, 16))) return UGP_ERR_ALIGN;
+  if (overlap(span_of(conteos, 4ull * cells), span_of(diag, 8))) return UGP_ERR_ALIAS;
+  enqueue_cell_diag(conteos, cells, capacity, diag, static_cast<hipStream_t>(stream));
+  return hipGetLastError() == hipSuccess ? UGP_OK : UGP_ERR_HIP;
 }
 
 int ugp_grid_build_timed(const ugp_particle* particles, uint32_t n, const float origin[3],
