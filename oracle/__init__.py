@@ -24,6 +24,9 @@ _LIB = os.path.join(_HERE, "libugp_oracle.so")
 CFLAGS = ["-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off", "-fPIC", "-shared"]
 
 _u32p = ctypes.POINTER(ctypes.c_uint32)
+
+ORDER_LINEAR = 0  # cell numbering x + y*nx + z*nx*ny
+ORDER_MORTON = 1  # Z-order bit interleave
 _f32p = ctypes.POINTER(ctypes.c_float)
 
 
@@ -56,6 +59,18 @@ class Oracle:
             _f32p, ctypes.c_uint32, _f32p, ctypes.c_float, _u32p,
             _u32p, _u32p, _u32p, _u32p, _f32p, _u32p,
         ]
+        lib.ugp_oracle_morton_bits.argtypes = [_u32p, ctypes.POINTER(ctypes.c_uint32), ctypes.POINTER(ctypes.c_uint64)]
+        lib.ugp_oracle_morton_key.argtypes = [ctypes.c_uint32] * 4
+        lib.ugp_oracle_morton_key.restype = ctypes.c_uint32
+        lib.ugp_oracle_morton_keys.argtypes = [_u32p, ctypes.c_uint32, ctypes.c_uint32, _u32p]
+        lib.ugp_oracle_key_count.argtypes = [_f32p, ctypes.c_float, _u32p, ctypes.c_uint32,
+                                             ctypes.POINTER(ctypes.c_uint64)]
+        lib.ugp_oracle_cell_key.argtypes = [_f32p, ctypes.c_uint32, _f32p, ctypes.c_float, _u32p,
+                                            ctypes.c_uint32, _u32p]
+        lib.ugp_oracle_grid_build_keyed.argtypes = [
+            _f32p, ctypes.c_uint32, _f32p, ctypes.c_float, _u32p, ctypes.c_uint32,
+            _u32p, _u32p, _u32p, _u32p, _f32p, _u32p,
+        ]
         lib.ugp_oracle_diag.argtypes = [
             _u32p, ctypes.c_uint32, ctypes.c_uint32,
             ctypes.POINTER(ctypes.c_uint32), ctypes.POINTER(ctypes.c_uint32),
@@ -63,7 +78,9 @@ class Oracle:
         for fn in (
             lib.ugp_oracle_check_grid, lib.ugp_oracle_cell_index, lib.ugp_oracle_histogram,
             lib.ugp_oracle_exclusive_scan, lib.ugp_oracle_scatter, lib.ugp_oracle_reorder,
-            lib.ugp_oracle_grid_build, lib.ugp_oracle_diag,
+            lib.ugp_oracle_grid_build, lib.ugp_oracle_diag, lib.ugp_oracle_morton_bits,
+            lib.ugp_oracle_morton_keys, lib.ugp_oracle_key_count, lib.ugp_oracle_cell_key,
+            lib.ugp_oracle_grid_build_keyed,
         ):
             fn.restype = ctypes.c_int
 
@@ -95,13 +112,41 @@ class Oracle:
         out = ctypes.c_uint64(0)
         return int(self._lib.ugp_oracle_check_grid(self._p(o, _f32p), h, self._p(d, _u32p), ctypes.byref(out)))
 
-    def cell_index(self, particles, origin, cell_size, dims) -> np.ndarray:
+    def cell_index(self, particles, origin, cell_size, dims, morton: bool = False) -> np.ndarray:
         p = np.ascontiguousarray(particles, dtype=np.float32).reshape(-1, 8)
         o, h, d = self._grid(origin, cell_size, dims)
         n = p.shape[0]
         out = np.empty(n, dtype=np.uint32)
-        st = self._lib.ugp_oracle_cell_index(self._p(p, _f32p), n, self._p(o, _f32p), h, self._p(d, _u32p), self._p(out, _u32p))
+        if morton:
+            st = self._lib.ugp_oracle_cell_key(self._p(p, _f32p), n, self._p(o, _f32p), h, self._p(d, _u32p),
+                                               ORDER_MORTON, self._p(out, _u32p))
+        else:
+            st = self._lib.ugp_oracle_cell_index(self._p(p, _f32p), n, self._p(o, _f32p), h, self._p(d, _u32p),
+                                                 self._p(out, _u32p))
         self._check(st, "cell_index")
+        return out
+
+    def key_count(self, origin, cell_size, dims, morton: bool = False) -> int:
+        o, h, d = self._grid(origin, cell_size, dims)
+        out = ctypes.c_uint64(0)
+        st = self._lib.ugp_oracle_key_count(self._p(o, _f32p), h, self._p(d, _u32p),
+                                            ORDER_MORTON if morton else ORDER_LINEAR, ctypes.byref(out))
+        self._check(st, "key_count")
+        return int(out.value)
+
+    def morton_bits(self, dims) -> int:
+        d = np.ascontiguousarray(np.asarray(dims, dtype=np.uint32).reshape(3))
+        b = ctypes.c_uint32(0)
+        k = ctypes.c_uint64(0)
+        self._check(self._lib.ugp_oracle_morton_bits(self._p(d, _u32p), ctypes.byref(b), ctypes.byref(k)),
+                    "morton_bits")
+        return int(b.value)
+
+    def morton_keys(self, k3, bits: int) -> np.ndarray:
+        k = np.ascontiguousarray(np.asarray(k3, dtype=np.uint32).reshape(-1, 3))
+        out = np.empty(k.shape[0], dtype=np.uint32)
+        self._check(self._lib.ugp_oracle_morton_keys(self._p(k, _u32p), k.shape[0], bits, self._p(out, _u32p)),
+                    "morton_keys")
         return out
 
     def histogram(self, celdaDe, cells: int) -> np.ndarray:
@@ -136,10 +181,10 @@ class Oracle:
         self._check(st, "reorder")
         return out
 
-    def grid_build(self, particles, origin, cell_size, dims) -> "GridIndex":
+    def grid_build(self, particles, origin, cell_size, dims, morton: bool = False) -> "GridIndex":
         p = np.ascontiguousarray(particles, dtype=np.float32).reshape(-1, 8)
         o, h, d = self._grid(origin, cell_size, dims)
-        cells = self.cells(o, h, d)
+        cells = self.key_count(o, h, d, morton)
         n = p.shape[0]
         celdaDe = np.empty(n, dtype=np.uint32)
         conteos = np.empty(cells, dtype=np.uint32)
@@ -147,9 +192,9 @@ class Oracle:
         ordenado = np.empty(n, dtype=np.uint32)
         reordered = np.empty_like(p)
         cursor = np.empty(max(cells, 1), dtype=np.uint32)
-        st = self._lib.ugp_oracle_grid_build(
+        st = self._lib.ugp_oracle_grid_build_keyed(
             self._p(p, _f32p), n, self._p(o, _f32p), h, self._p(d, _u32p),
-            self._p(celdaDe, _u32p), self._p(conteos, _u32p), self._p(inicios, _u32p),
+            ORDER_MORTON if morton else ORDER_LINEAR, self._p(celdaDe, _u32p), self._p(conteos, _u32p), self._p(inicios, _u32p),
             self._p(ordenado, _u32p), self._p(reordered, _f32p), self._p(cursor, _u32p),
         )
         self._check(st, "grid_build")

@@ -41,6 +41,14 @@
  *    sin salir de la GPU": the diagnostic pair (largest per-cell occupancy,
  *    number of insertions that found the cell already at or above a fixed
  *    capacity) -- computed here in closed form from the histogram.
+ *  - "Reordenar por celda y la coalescencia de memoria", section "El orden
+ *    de las celdas también importa": cells may instead be numbered along
+ *    the Z (Morton) curve. The page gives no formula; the reading taken is
+ *    the textbook 3-D bit interleave of the clamped cell coordinates --
+ *    bit b of x, y, z goes to key bits 3b, 3b+1, 3b+2 -- with every axis
+ *    padded to B bits, 2^B being the smallest power of two >= the largest
+ *    dimension, so there are 2^(3B) keys (exactly the cell count on a cubic
+ *    power-of-two grid; other grids leave keys no cell maps to).
  */
 #include <float.h>
 #include <math.h>
@@ -55,6 +63,12 @@
 
 /* largest per-axis dimension: dim - 1 must be exact in float32 */
 #define UGPO_MAX_DIM (1u << 24)
+
+/* cell numbering */
+#define UGPO_ORDER_LINEAR 0u
+#define UGPO_ORDER_MORTON 1u
+/* Morton keys: at most 10 bits per axis, 2^30 keys */
+#define UGPO_MORTON_MAX_BITS 10u
 
 /* ------------------------------------------------------------------ */
 /* Argument checks (the oracle rejects what it cannot define).          */
@@ -94,13 +108,68 @@ static uint32_t oracle_axis_cell(float p, float o, float h, uint32_t dim) {
     return (uint32_t)f;
 }
 
-/* Step 1b: per-particle linear cell index, x + y*nx + z*nx*ny.
- * particles: n records of 8 floats, position in floats 0..2. */
-int ugp_oracle_cell_index(const float *particles, uint32_t n, const float origin[3],
-                          float cell_size, const uint32_t dims[3], uint32_t *celdaDe) {
+/* Morton keys: bits per axis and key count for a grid. */
+int ugp_oracle_morton_bits(const uint32_t dims[3], uint32_t *bits, uint64_t *keys) {
+    if (!dims || !bits) return UGPO_ERR_NULL;
+    uint32_t largest = 0;
+    for (int a = 0; a < 3; ++a) {
+        if (dims[a] < 1u || dims[a] > UGPO_MAX_DIM) return UGPO_ERR_RANGE;
+        if (dims[a] > largest) largest = dims[a];
+    }
+    uint32_t b = 0;
+    while ((1u << b) < largest) ++b;
+    if (b > UGPO_MORTON_MAX_BITS) return UGPO_ERR_RANGE;
+    *bits = b;
+    if (keys) *keys = 1ull << (3u * b);
+    return UGPO_OK;
+}
+
+/* The Morton key of cell (kx, ky, kz), bit by bit. */
+uint32_t ugp_oracle_morton_key(uint32_t kx, uint32_t ky, uint32_t kz, uint32_t bits) {
+    uint64_t key = 0;
+    for (uint32_t b = 0; b < bits; ++b) {
+        key |= (uint64_t)((kx >> b) & 1u) << (3u * b);
+        key |= (uint64_t)((ky >> b) & 1u) << (3u * b + 1u);
+        key |= (uint64_t)((kz >> b) & 1u) << (3u * b + 2u);
+    }
+    return (uint32_t)key;
+}
+
+/* Array form: k3 holds n (kx, ky, kz) triples. */
+int ugp_oracle_morton_keys(const uint32_t *k3, uint32_t n, uint32_t bits, uint32_t *out) {
+    if (n > 0 && (!k3 || !out)) return UGPO_ERR_NULL;
+    if (bits > UGPO_MORTON_MAX_BITS) return UGPO_ERR_RANGE;
+    for (uint32_t i = 0; i < n; ++i)
+        out[i] = ugp_oracle_morton_key(k3[3u * i], k3[3u * i + 1u], k3[3u * i + 2u], bits);
+    return UGPO_OK;
+}
+
+/* Number of cell keys of a grid under a numbering (linear: the cell count). */
+int ugp_oracle_key_count(const float origin[3], float cell_size, const uint32_t dims[3],
+                         uint32_t order, uint64_t *keys) {
     uint64_t cells = 0;
     int st = ugp_oracle_check_grid(origin, cell_size, dims, &cells);
     if (st != UGPO_OK) return st;
+    if (order == UGPO_ORDER_LINEAR) {
+        if (keys) *keys = cells;
+        return UGPO_OK;
+    }
+    if (order != UGPO_ORDER_MORTON) return UGPO_ERR_ARG;
+    uint32_t bits = 0;
+    return ugp_oracle_morton_bits(dims, &bits, keys);
+}
+
+/* Step 1b: per-particle cell key. Linear order: x + y*nx + z*nx*ny;
+ * Morton order: the interleave above.
+ * particles: n records of 8 floats, position in floats 0..2. */
+int ugp_oracle_cell_key(const float *particles, uint32_t n, const float origin[3],
+                        float cell_size, const uint32_t dims[3], uint32_t order,
+                        uint32_t *celdaDe) {
+    uint64_t cells = 0;
+    int st = ugp_oracle_key_count(origin, cell_size, dims, order, &cells);
+    if (st != UGPO_OK) return st;
+    uint32_t bits = 0;
+    if (order == UGPO_ORDER_MORTON) ugp_oracle_morton_bits(dims, &bits, NULL);
     if (n > 0 && (!particles || !celdaDe)) return UGPO_ERR_NULL;
     const uint64_t nx = dims[0];
     const uint64_t nxy = (uint64_t)dims[0] * (uint64_t)dims[1];
@@ -109,11 +178,22 @@ int ugp_oracle_cell_index(const float *particles, uint32_t n, const float origin
         uint64_t kx = oracle_axis_cell(rec[0], origin[0], cell_size, dims[0]);
         uint64_t ky = oracle_axis_cell(rec[1], origin[1], cell_size, dims[1]);
         uint64_t kz = oracle_axis_cell(rec[2], origin[2], cell_size, dims[2]);
-        uint64_t c = kx + ky * nx + kz * nxy;
+        uint64_t c;
+        if (order == UGPO_ORDER_MORTON) {
+            c = ugp_oracle_morton_key((uint32_t)kx, (uint32_t)ky, (uint32_t)kz, bits);
+        } else {
+            c = kx + ky * nx + kz * nxy;
+        }
         if (c >= cells) return UGPO_ERR_RANGE; /* cannot happen after the clamp */
         celdaDe[i] = (uint32_t)c;
     }
     return UGPO_OK;
+}
+
+/* Linear cell index (the default numbering). */
+int ugp_oracle_cell_index(const float *particles, uint32_t n, const float origin[3],
+                          float cell_size, const uint32_t dims[3], uint32_t *celdaDe) {
+    return ugp_oracle_cell_key(particles, n, origin, cell_size, dims, UGPO_ORDER_LINEAR, celdaDe);
 }
 
 /* ------------------------------------------------------------------ */
@@ -189,18 +269,19 @@ int ugp_oracle_reorder(const float *particles, const uint32_t *ordenado, uint32_
 }
 
 /* ------------------------------------------------------------------ */
-/* The whole chain.  cursor: caller scratch of `cells` entries.         */
+/* The whole chain.  cursor: caller scratch of `keys` entries, where     */
+/* keys is the key count of the numbering (ugp_oracle_key_count).        */
 /* ------------------------------------------------------------------ */
 
-int ugp_oracle_grid_build(const float *particles, uint32_t n, const float origin[3],
-                          float cell_size, const uint32_t dims[3], uint32_t *celdaDe,
-                          uint32_t *conteos, uint32_t *inicios, uint32_t *ordenado,
-                          float *reordered, uint32_t *cursor) {
+int ugp_oracle_grid_build_keyed(const float *particles, uint32_t n, const float origin[3],
+                                float cell_size, const uint32_t dims[3], uint32_t order,
+                                uint32_t *celdaDe, uint32_t *conteos, uint32_t *inicios,
+                                uint32_t *ordenado, float *reordered, uint32_t *cursor) {
     uint64_t cells64 = 0;
-    int st = ugp_oracle_check_grid(origin, cell_size, dims, &cells64);
+    int st = ugp_oracle_key_count(origin, cell_size, dims, order, &cells64);
     if (st != UGPO_OK) return st;
     uint32_t cells = (uint32_t)cells64;
-    st = ugp_oracle_cell_index(particles, n, origin, cell_size, dims, celdaDe);
+    st = ugp_oracle_cell_key(particles, n, origin, cell_size, dims, order, celdaDe);
     if (st != UGPO_OK) return st;
     st = ugp_oracle_histogram(celdaDe, n, cells, conteos);
     if (st != UGPO_OK) return st;
@@ -209,6 +290,14 @@ int ugp_oracle_grid_build(const float *particles, uint32_t n, const float origin
     st = ugp_oracle_scatter(celdaDe, n, inicios, cells, cursor, ordenado);
     if (st != UGPO_OK) return st;
     return ugp_oracle_reorder(particles, ordenado, n, reordered);
+}
+
+int ugp_oracle_grid_build(const float *particles, uint32_t n, const float origin[3],
+                          float cell_size, const uint32_t dims[3], uint32_t *celdaDe,
+                          uint32_t *conteos, uint32_t *inicios, uint32_t *ordenado,
+                          float *reordered, uint32_t *cursor) {
+    return ugp_oracle_grid_build_keyed(particles, n, origin, cell_size, dims, UGPO_ORDER_LINEAR,
+                                       celdaDe, conteos, inicios, ordenado, reordered, cursor);
 }
 
 /* ------------------------------------------------------------------ */

@@ -23,6 +23,8 @@ from fractions import Fraction
 
 import numpy as np
 
+import oracle
+
 import workloads as W
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -216,10 +218,11 @@ def pin_exact_floor_far_from_faces(orc, wl):
     assert checked > 0.9 * p.shape[0] or p.shape[0] < 100
 
 
-def check_index_invariants(wl, r, stable: bool):
-    """Invariants every correct build satisfies (any size)."""
+def check_index_invariants(wl, r, stable: bool, keys: int | None = None):
+    """Invariants every correct build satisfies (any size). `keys`: the key
+    count when cells are numbered other than linearly (Morton)."""
     n = wl.n
-    cells = wl.cells
+    cells = wl.cells if keys is None else keys
     assert r.conteos.shape == (cells,)
     assert r.inicios.shape == (cells + 1,)
     assert int(r.inicios[0]) == 0
@@ -324,3 +327,90 @@ def pin_empty_and_degenerate(orc):
     # one particle
     r = orc.grid_build(parts[:1], origin, h, dims)
     assert int(r.inicios[-1]) == 1 and r.ordenado.tolist() == [0]
+
+
+# ---------------------------------------------------------------------------
+# Morton (Z-order) cell keys ("Reordenar por celda y la coalescencia de
+# memoria", section "El orden de las celdas también importa"). The key is the
+# 3-D bit interleave x0 y0 z0 x1 y1 z1 ... (x lowest). Pinned against
+# printed-by-hand values of the interleave, against the Z-curve's recursive
+# definition (a key is eight times its parent octant's key plus the child
+# number x + 2y + 4z), and against the linear numbering it relabels.
+# ---------------------------------------------------------------------------
+
+
+def morton_recursive(kx: int, ky: int, kz: int, bits: int) -> int:
+    """Z-curve key by octant recursion (independent of the bit loop)."""
+    if bits == 0:
+        return 0
+    return 8 * morton_recursive(kx >> 1, ky >> 1, kz >> 1, bits - 1) + (kx & 1) + 2 * (ky & 1) + 4 * (kz & 1)
+
+
+def pin_morton_textbook(orc):
+    cases = {
+        (0, 0, 0): 0, (1, 0, 0): 1, (0, 1, 0): 2, (0, 0, 1): 4, (1, 1, 1): 7,
+        (2, 0, 0): 8, (0, 2, 0): 16, (0, 0, 2): 32, (3, 3, 3): 63, (5, 0, 0): 0b1000001,
+        (1023, 0, 0): 0x09249249, (0, 1023, 0): 0x12492492, (0, 0, 1023): 0x24924924,
+        (1023, 1023, 1023): (1 << 30) - 1,
+    }
+    got = orc.morton_keys(list(cases), 10)
+    assert got.tolist() == list(cases.values()), got
+    assert orc.morton_bits((128, 128, 128)) == 7
+    assert orc.morton_bits((16, 16, 16)) == 4
+    assert orc.morton_bits((7, 5, 3)) == 3
+    assert orc.morton_bits((1, 1, 1)) == 0
+    assert orc.morton_bits((1024, 1, 1)) == 10
+    for bad in ((1025, 1, 1), (1 << 20, 2, 2)):
+        try:
+            orc.morton_bits(bad)
+        except oracle.OracleError:
+            continue
+        raise AssertionError(f"morton_bits{bad} should be out of range")
+
+
+def pin_morton_recursion_bijection(orc):
+    """Small grids exhaustively: keys follow the octant recursion and map
+    [0, 2^B)^3 one-to-one onto [0, 8^B); aligned runs of 8 keys are 2x2x2 cubes."""
+    for bits in range(1, 5):
+        side = 1 << bits
+        g = np.stack(np.meshgrid(np.arange(side), np.arange(side), np.arange(side), indexing="ij"), -1).reshape(-1, 3)
+        got = orc.morton_keys(g, bits).astype(np.int64)
+        want = np.array([morton_recursive(int(a), int(b), int(c), bits) for a, b, c in g], dtype=np.int64)
+        assert np.array_equal(got, want), bits
+        assert np.array_equal(np.sort(got), np.arange(side ** 3))
+        inv = np.empty_like(got)
+        inv[got] = np.arange(got.size)
+        blocks = g[inv].reshape(-1, 8, 3)
+        assert np.all(blocks.max(1) - blocks.min(1) == 1) and np.all(blocks.min(1) % 2 == 0)
+    rng = np.random.Generator(np.random.PCG64(12))
+    g = rng.integers(0, 1024, (500, 3))
+    got = orc.morton_keys(g, 10).astype(np.int64)
+    assert got.tolist() == [morton_recursive(int(a), int(b), int(c), 10) for a, b, c in g]
+
+
+def pin_morton_relabels_linear(orc, wl):
+    """A Morton build is the linear build with cells renamed: same clamped
+    cell per particle, key = interleave of its coordinates, the same counts
+    moved to the new keys, zero counts on keys no cell maps to (non-cubic
+    grids), and the same stable order within every cell."""
+    lin = orc.grid_build(wl.particles, wl.origin, wl.cell_size, wl.dims)
+    mor = orc.grid_build(wl.particles, wl.origin, wl.cell_size, wl.dims, morton=True)
+    d = [int(v) for v in wl.dims]
+    bits = orc.morton_bits(d)
+    keys = orc.key_count(wl.origin, wl.cell_size, wl.dims, morton=True)
+    assert keys == 1 << (3 * bits)
+    c = lin.celdaDe.astype(np.int64)
+    xyz = np.stack([c % d[0], (c // d[0]) % d[1], c // (d[0] * d[1])], -1)
+    want = np.array([morton_recursive(int(a), int(b), int(e), bits) for a, b, e in xyz], dtype=np.int64)
+    assert np.array_equal(mor.celdaDe.astype(np.int64), want)
+    cells = np.stack(np.meshgrid(np.arange(d[0]), np.arange(d[1]), np.arange(d[2]), indexing="ij"), -1).reshape(-1, 3)
+    lin_of = cells[:, 0] + cells[:, 1] * d[0] + cells[:, 2] * d[0] * d[1]
+    key_of = orc.morton_keys(cells, bits).astype(np.int64)
+    moved = np.zeros(keys, dtype=np.uint32)
+    moved[key_of] = lin.conteos[lin_of]
+    assert np.array_equal(mor.conteos, moved)
+    check_index_invariants(wl, mor, stable=True, keys=keys)
+    for k, lc in zip(key_of[:64], lin_of[:64]):
+        a = mor.ordenado[mor.inicios[k]:mor.inicios[k + 1]].tolist()
+        b = lin.ordenado[lin.inicios[lc]:lin.inicios[lc + 1]].tolist()
+        assert a == b, (k, lc)

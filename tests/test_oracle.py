@@ -125,8 +125,8 @@ def test_workloads_reproducible():
 # ---------------------------------------------------------------------------
 
 MUTATIONS = {
-    "axes_transposed": ("uint64_t c = kx + ky * nx + kz * nxy;", "uint64_t c = kz + ky * nx + kx * nxy;"),
-    "stride_uses_nxy_for_y": ("uint64_t c = kx + ky * nx + kz * nxy;", "uint64_t c = kx + ky * nxy + kz * nx;"),
+    "axes_transposed": ("c = kx + ky * nx + kz * nxy;", "c = kz + ky * nx + kx * nxy;"),
+    "stride_uses_nxy_for_y": ("c = kx + ky * nx + kz * nxy;", "c = kx + ky * nxy + kz * nx;"),
     "sign_flipped": ("float t = p - o;", "float t = o - p;"),
     "reciprocal_multiply": ("float q = t / h;", "float q = t * (1.0f / h);"),
     "divide_then_subtract": (
@@ -160,7 +160,42 @@ MUTATIONS = {
         "if (v > capacity) ov += 1u;",
     ),
     "diag_no_max": ("if (v > mx) mx = v;", "if (v > mx) mx = v - 1;"),
+    "morton_axes_swapped": (
+        "key |= (uint64_t)((kx >> b) & 1u) << (3u * b);\n        key |= (uint64_t)((ky >> b) & 1u) << (3u * b + 1u);",
+        "key |= (uint64_t)((ky >> b) & 1u) << (3u * b);\n        key |= (uint64_t)((kx >> b) & 1u) << (3u * b + 1u);",
+    ),
+    "morton_stride_off": ("<< (3u * b + 2u);", "<< (3u * b + 3u);"),
+    "morton_bits_floor": ("while ((1u << b) < largest) ++b;", "while ((2u << b) <= largest) ++b;"),
+    "morton_drops_top_level": ("for (uint32_t b = 0; b < bits; ++b) {\n        key",
+                               "for (uint32_t b = 0; b + 1 < bits; ++b) {\n        key"),
 }
+
+
+def _noncubic_workload():
+    """3000 particles on a 7x5x3 grid, some outside it (clamped)."""
+    rng = np.random.Generator(np.random.PCG64(33))
+    parts = rng.standard_normal((3000, 8)).astype(np.float32)
+    parts[:, :3] = (rng.random((3000, 3)) * np.array([8.0, 6.0, 4.0]) - 0.5).astype(np.float32)
+    return W.Workload("noncubic", parts, np.zeros(3, np.float32), np.float32(1.0), np.array([7, 5, 3], np.uint32))
+
+
+def test_morton_textbook(orc):
+    pins.pin_morton_textbook(orc)
+
+
+def test_morton_recursion_bijection(orc):
+    pins.pin_morton_recursion_bijection(orc)
+
+
+@pytest.mark.parametrize("which", ["tiny", "noncubic", "contention_small"])
+def test_morton_relabels_linear(orc, which):
+    if which == "tiny":
+        wl = W.make_config("tiny")
+    elif which == "noncubic":
+        wl = _noncubic_workload()
+    else:  # the contention recipe on a 32^3 grid (hot cell, clusters, clamped outsiders)
+        wl = W.make_contention(20_000, 32, seed=4, hot=1000, per_cluster=3000, outside=1000)
+    pins.pin_morton_relabels_linear(orc, wl)
 
 
 def _all_pins(orc_m):
@@ -168,6 +203,7 @@ def _all_pins(orc_m):
     face16 = W.make_boundary_probe((16, 16, 16), (-5.0, -5.0, -5.0), np.float32(0.625), per_axis_random=128)
     face128 = W.make_boundary_probe((128, 128, 128), (-5.0, -5.0, -5.0), np.float32(0.078125), per_axis_random=128)
     face_nd = W.make_boundary_probe((64, 64, 64), (-3.0, -3.0, -3.0), np.float32(0.1), per_axis_random=128)
+    noncubic = _noncubic_workload()
     checks = [
         lambda: pins.pin_worked_example_scan(orc_m),
         lambda: pins.pin_worked_example_pipeline(orc_m),
@@ -179,6 +215,10 @@ def _all_pins(orc_m):
         lambda: pins.pin_binary32_model(orc_m, face128),
         lambda: pins.pin_binary32_model(orc_m, face_nd),
         lambda: pins.pin_library_reductions(orc_m, tiny),
+        lambda: pins.pin_morton_textbook(orc_m),
+        lambda: pins.pin_morton_recursion_bijection(orc_m),
+        lambda: pins.pin_morton_relabels_linear(orc_m, tiny),
+        lambda: pins.pin_morton_relabels_linear(orc_m, noncubic),
     ]
     failed = 0
     for chk in checks:
