@@ -355,6 +355,21 @@ def main(argv=None) -> int:
         cd.append(c0.elapsed_time(c1))
     cell_diag_us = 1e3 * statistics.median(cd)
 
+    # ---- Morton-keyed variant: K cold builds numbering cells along the Z curve ----
+    mflags = flags | ugp.FLAG_MORTON
+    mout, mws = ugp.alloc_outputs(n, dims, dev, mflags)
+    mstarts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    mends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    for k in range(K):
+        evict()
+        mstarts[k].record(stream)
+        ugp.grid_build(parts, origin, h, dims, stable=args.mode == "stable", gather=args.mode == "gather",
+                       morton=True, out=mout, workspace=mws)
+        mends[k].record(stream)
+    torch.cuda.synchronize()
+    morton_ms = sum(mstarts[k].elapsed_time(mends[k]) for k in range(K)) / K
+    del mout, mws
+
     # ---- warm: K back-to-back builds between one event pair ----
     w0 = torch.cuda.Event(enable_timing=True)
     w1 = torch.cuda.Event(enable_timing=True)
@@ -451,6 +466,8 @@ def main(argv=None) -> int:
         "step_ms_median": statistics.median(step_ms),
         "step_ms_p10_p90": [float(np.percentile(step_ms, 10)), float(np.percentile(step_ms, 90))],
         "warm_ms_per_step": warm_ms,
+        "morton_variant": {"ms_per_step": morton_ms, "keys": ugp.key_count(dims, mflags),
+                           "note": "same cold protocol, cells numbered along the Z curve"},
         "diag_variant": {"capacity": 64, "ms_per_step": diag_ms, "max_per_cell_and_overflows": diag_val,
                          "note": "same cold protocol, overflow diagnostics folded into the build",
                          "cell_diag_us": round(cell_diag_us, 3),

@@ -86,23 +86,41 @@ typedef struct ugp_particle {
  * reads) instead of writing the record inside the scatter kernel. The
  * result is identical; this only selects the kernel schedule. */
 #define UGP_FLAG_GATHER 0x2u
+/* Number cells along the Z (Morton) curve instead of x + y*nx + z*nx*ny
+ * (page "Reordenar por celda y la coalescencia de memoria", section "El
+ * orden de las celdas también importa"). The key of cell (x, y, z) puts bit
+ * b of x, y, z at key bits 3b, 3b+1, 3b+2; every axis is padded to B bits,
+ * 2^B being the smallest power of two >= the largest dimension, so there are
+ * K = 2^(3B) keys (K = C on a cubic power-of-two grid; on other grids some
+ * keys hold no cell and always count 0). Requires B <= 10 (UGP_ERR_RANGE
+ * otherwise). celdaDe, conteos, inicios and the order of ordenado and
+ * reordered are then in keys: conteos has K entries and inicios K+1
+ * (ugp_grid_key_count()). */
+#define UGP_FLAG_MORTON 0x4u
 
 /* Pipeline stage slots, for ugp_grid_build_stage() / ugp_grid_build_timed().
- * The library picks one of three execution paths from n and the grid size;
+ * The library picks one of three execution paths from n and the key count K
+ * (ugp_grid_key_count(); the cell count C unless UGP_FLAG_MORTON);
  * each path fills the six slots with its own kernels, named by
  * ugp_grid_stage_name():
  *   n == 0            slot 0 "clear" (zero conteos and inicios); others empty
- *   cells <= 2^22 and n <= 2^21
+ *   K <= 2^22 and n <= 2^21
  *                     "chunk_sort", -, -, "tile_sort" -- two kernels, no
  *                     global atomics, records moved through LDS
- *   other cells <= 2^24
+ *   other K <= 2^24
  *                     "keys", "tile_scan", "bucket", "cells"  -- a two-level
  *                     counting sort with LDS histograms and no global atomics
- *   cells >  2^24     "clear", "count", "scan", "scatter"     -- one global
+ *   K >  2^24         "clear", "count", "scan", "scatter"     -- one global
  *                     atomic per particle in count and in scatter
  *   slot 4 "stable_sort" (UGP_FLAG_STABLE only), slot 5 "gather"
  *   (UGP_FLAG_GATHER or UGP_FLAG_STABLE only). */
 #define UGP_NUM_STAGES 6u
+
+/* Number of cell keys K for a grid and flags: C = dims[0]*dims[1]*dims[2]
+ * for the linear numbering, 2^(3B) with UGP_FLAG_MORTON. conteos holds K
+ * entries and inicios K+1. Writes *keys; returns UGP_OK, UGP_ERR_NULL,
+ * UGP_ERR_RANGE or UGP_ERR_ARG. Pure host function. */
+int ugp_grid_key_count(const uint32_t dims[3], uint32_t flags, uint64_t *keys);
 
 /* Bytes of device workspace ugp_grid_build() needs for n particles on a
  * dims[0] x dims[1] x dims[2] grid with the given flags.
@@ -120,11 +138,13 @@ int ugp_grid_workspace_bytes(uint32_t n, const uint32_t dims[3], uint32_t flags,
  *               (>= FLT_MIN)
  *   dims        host, in:    cells per axis, each in [1, 2^24]; the cell
  *               count C = dims[0]*dims[1]*dims[2] must be <= 2^32-2
- *   celdaDe     device, out: n u32, cell index of each particle
- *   conteos     device, out: C u32, particles per cell (the histogram;
- *               it still holds the histogram when the call completes)
- *   inicios     device, out: C+1 u32, exclusive prefix sum of conteos,
- *               inicios[C] = n
+ *   celdaDe     device, out: n u32, cell index of each particle (its key
+ *               with UGP_FLAG_MORTON)
+ *   conteos     device, out: K u32, particles per cell (the histogram;
+ *               it still holds the histogram when the call completes);
+ *               K = C unless UGP_FLAG_MORTON (ugp_grid_key_count())
+ *   inicios     device, out: K+1 u32, exclusive prefix sum of conteos,
+ *               inicios[K] = n
  *   ordenado    device, out: n u32, particle indices grouped by cell:
  *               cell c occupies [inicios[c], inicios[c+1])
  *   reordered   device, out: n records, reordered[k] = particles[ordenado[k]]

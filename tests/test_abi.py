@@ -191,3 +191,21 @@ def test_diag_validation_on_host(lib):
     assert lib.ugp_cell_diag(b + 4, 100, 8, b + (1 << 20), None) == ugp.UGP_ERR_ALIGN
     assert lib.ugp_cell_diag(b, 100, 8, b + (1 << 20) + 1, None) == ugp.UGP_ERR_ALIGN
     assert lib.ugp_cell_diag(b, 100, 8, b + 396, None) == ugp.UGP_ERR_ALIAS  # last word of conteos
+
+
+def test_key_count_on_host(lib):
+    assert ugp.key_count((128, 128, 128)) == 128 ** 3
+    assert ugp.key_count((7, 5, 3)) == 105
+    assert ugp.key_count((128, 128, 128), ugp.FLAG_MORTON) == 128 ** 3
+    assert ugp.key_count((7, 5, 3), ugp.FLAG_MORTON) == 512
+    assert ugp.key_count((1, 1, 1), ugp.FLAG_MORTON) == 1
+    assert ugp.key_count((256, 2, 2), ugp.FLAG_MORTON) == 1 << 24
+    assert ugp.key_count((257, 2, 2), ugp.FLAG_MORTON) == 1 << 27
+    with pytest.raises(ugp.UGPError) as e:
+        ugp.key_count((1025, 1, 1), ugp.FLAG_MORTON)
+    assert e.value.status == ugp.UGP_ERR_RANGE
+    # the path follows the key count: 7x5x3 Morton has 512 keys (staged),
+    # 257x2x2 has 2^27 (global-atomic path)
+    assert ugp.stage_names(100, (257, 2, 2), ugp.FLAG_MORTON)[0] == "clear"
+    assert ugp.stage_names(100, (257, 2, 2))[0] == "chunk_sort"
+    assert ugp.workspace_bytes(1000, (7, 5, 3), ugp.FLAG_MORTON) > 0

@@ -1,0 +1,132 @@
+"""GPU parity of Morton (Z-order) cell keys (UGP_FLAG_MORTON) against the
+oracle's keyed build (page "Reordenar por celda y la coalescencia de
+memoria", section "El orden de las celdas también importa").
+
+Same rule as the linear parity tests: celdaDe, conteos, inicios bit-exact;
+ordenado grouped by key (element for element in stable mode); reordered the
+bytewise gather of the GPU's own ordenado. Covers the staged, tiled and
+direct paths, non-cubic grids (keys no cell maps to), clamped and special
+positions, and the diagnostic variant.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+import workloads as W  # noqa: E402
+from tests import pins  # noqa: E402
+from tests.test_parity import MODES, _u32  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ugp():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    import uniform_grid_particle_amd as m
+
+    m.load_library()
+    return m
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.load()
+
+
+def run_morton(ugp, wl, mode="atomic"):
+    dev = torch.device("cuda:0")
+    parts = torch.from_numpy(np.ascontiguousarray(wl.particles)).to(dev)
+    r = ugp.grid_build(parts, [float(v) for v in wl.origin], float(wl.cell_size), [int(v) for v in wl.dims],
+                       morton=True, **MODES[mode])
+    torch.cuda.synchronize()
+    return oracle.GridIndex(_u32(r.celdaDe)[: wl.n], _u32(r.conteos), _u32(r.inicios),
+                            _u32(r.ordenado)[: wl.n], r.reordered.cpu().numpy()[: wl.n])
+
+
+def assert_morton_parity(orc, ugp, wl, mode):
+    ref = orc.grid_build(wl.particles, wl.origin, wl.cell_size, wl.dims, morton=True)
+    keys = ugp.key_count([int(v) for v in wl.dims], ugp.FLAG_MORTON)
+    assert keys == ref.conteos.size
+    got = run_morton(ugp, wl, mode)
+    assert np.array_equal(got.celdaDe, ref.celdaDe), f"{np.count_nonzero(got.celdaDe != ref.celdaDe)} keys differ"
+    assert np.array_equal(got.conteos, ref.conteos)
+    assert np.array_equal(got.inicios, ref.inicios)
+    pins.check_index_invariants(wl, got, stable=(mode == "stable"), keys=keys)
+    if mode == "stable":
+        assert np.array_equal(got.ordenado, ref.ordenado)
+    else:
+        c = got.celdaDe[got.ordenado].astype(np.int64)
+        assert np.array_equal(got.ordenado[np.lexsort((got.ordenado, c))], ref.ordenado)
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+@pytest.mark.parametrize("name", ["tiny", "sparse", "baseline", "contention"])
+def test_morton_configs(ugp, orc, name, mode):
+    print(f"[morton] {name} {mode}", flush=True)
+    assert_morton_parity(orc, ugp, W.make_config(name), mode)
+
+
+def test_morton_large_tiled_path(ugp, orc):
+    print("[morton] large", flush=True)
+    wl = W.make_config("large")
+    assert ugp.stage_names(wl.n, wl.dims.tolist(), ugp.FLAG_MORTON)[0] == "keys"
+    assert_morton_parity(orc, ugp, wl, "atomic")
+
+
+@pytest.mark.parametrize("dims,n", [((7, 5, 3), 3001), ((33, 1, 17), 10007), ((100, 3, 60), 65537),
+                                    ((400, 3, 2), 100_003)])
+def test_morton_noncubic(ugp, orc, dims, n):
+    """Non-cubic grids: padded keys (some always empty); (400, 3, 2) has
+    2^27 keys and takes the global-atomic path."""
+    print(f"[morton] noncubic {dims}", flush=True)
+    rng = np.random.Generator(np.random.PCG64(n))
+    parts = rng.standard_normal((n, 8)).astype(np.float32)
+    ext = np.asarray(dims, np.float64) * 0.25
+    parts[:, :3] = (rng.random((n, 3)) * ext * 1.04 - 0.02 * ext).astype(np.float32)
+    wl = W.Workload("noncubic", parts, np.zeros(3, np.float32), np.float32(0.25), np.asarray(dims, np.uint32))
+    for mode in ("atomic", "stable"):
+        assert_morton_parity(orc, ugp, wl, mode)
+
+
+def test_morton_faces_and_specials(ugp, orc):
+    """Face-adjacent positions and NaN/inf/huge coordinates map to the same
+    clamped cell as in the linear numbering, then to its key."""
+    wl = W.make_boundary_probe((128, 128, 128), (-5.0, -5.0, -5.0), np.float32(0.078125), per_axis_random=2048)
+    assert_morton_parity(orc, ugp, wl, "atomic")
+    rng = np.random.Generator(np.random.PCG64(8))
+    n = 5000
+    parts = rng.standard_normal((n, 8)).astype(np.float32) * 4
+    specials = np.array([np.nan, np.inf, -np.inf, -0.0, 0.0, 3.0e38, -3.0e38, 1e-40], np.float32)
+    mask = rng.random((n, 3)) < 0.2
+    parts[:, :3][mask] = rng.choice(specials, int(mask.sum()))
+    wl = W.Workload("special", parts, np.array([-3, -2, -1], np.float32), np.float32(0.5),
+                    np.array([12, 9, 7], np.uint32))
+    for mode in MODES:
+        assert_morton_parity(orc, ugp, wl, mode)
+
+
+def test_morton_diag(ugp, orc):
+    wl = W.make_config("contention")
+    ref = orc.grid_build(wl.particles, wl.origin, wl.cell_size, wl.dims, morton=True)
+    dev = torch.device("cuda:0")
+    parts = torch.from_numpy(wl.particles).to(dev)
+    r, d = ugp.grid_build_diag(parts, wl.origin.tolist(), float(wl.cell_size), wl.dims.tolist(), 64, morton=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(_u32(r.conteos), ref.conteos)
+    assert tuple(int(v) for v in _u32(d)) == orc.diag(ref.conteos, 64)
+
+
+def test_morton_key_count_and_errors(ugp):
+    assert ugp.key_count((128, 128, 128), ugp.FLAG_MORTON) == 128 ** 3
+    assert ugp.key_count((7, 5, 3), ugp.FLAG_MORTON) == 512
+    assert ugp.key_count((1, 1, 1), ugp.FLAG_MORTON) == 1
+    assert ugp.key_count((1024, 1, 1), ugp.FLAG_MORTON) == 1 << 30
+    with pytest.raises(ugp.UGPError) as e:
+        ugp.key_count((1025, 4, 4), ugp.FLAG_MORTON)
+    assert e.value.status == ugp.UGP_ERR_RANGE

@@ -32,6 +32,7 @@ UGP_ERR_HIP = -7
 
 FLAG_STABLE = 0x1
 FLAG_GATHER = 0x2
+FLAG_MORTON = 0x4
 
 NUM_STAGES = 6  # stage slots; names depend on the path, see stage_names()
 
@@ -68,6 +69,8 @@ def load_library():
     lib.ugp_abi_version.argtypes = []
     lib.ugp_status_string.restype = ctypes.c_char_p
     lib.ugp_status_string.argtypes = [ctypes.c_int]
+    lib.ugp_grid_key_count.restype = ctypes.c_int
+    lib.ugp_grid_key_count.argtypes = [ctypes.POINTER(_u32), _u32, ctypes.POINTER(ctypes.c_uint64)]
     lib.ugp_grid_workspace_bytes.restype = ctypes.c_int
     lib.ugp_grid_workspace_bytes.argtypes = [_u32, ctypes.POINTER(_u32), _u32, ctypes.POINTER(ctypes.c_size_t)]
     build_args = [_vp, _u32, ctypes.POINTER(ctypes.c_float), ctypes.c_float, ctypes.POINTER(_u32),
@@ -131,6 +134,19 @@ def _dims3(dims) -> tuple[int, int, int]:
     return d
 
 
+def key_count(dims: Sequence[int], flags: int = 0) -> int:
+    """Entries of conteos (inicios has one more) for this grid and flags."""
+    lib = load_library()
+    d = _u32_3(*_dims3(dims))
+    out = ctypes.c_uint64(0)
+    _check(lib.ugp_grid_key_count(d, int(flags), ctypes.byref(out)), "ugp_grid_key_count")
+    return int(out.value)
+
+
+def _flags(stable: bool, gather: bool, morton: bool) -> int:
+    return (FLAG_STABLE if stable else 0) | (FLAG_GATHER if gather else 0) | (FLAG_MORTON if morton else 0)
+
+
 def workspace_bytes(n: int, dims: Sequence[int], flags: int = 0) -> int:
     lib = load_library()
     d = _u32_3(*_dims3(dims))
@@ -164,7 +180,7 @@ class GridIndex:
 def alloc_outputs(n: int, dims: Sequence[int], device, flags: int = 0):
     """Output tensors and the workspace for one build (torch allocations)."""
     d = _dims3(dims)
-    cells = d[0] * d[1] * d[2]
+    cells = key_count(d, flags)
     dev = torch.device(device)
     out = GridIndex(
         celdaDe=torch.empty(n, dtype=torch.int32, device=dev),
@@ -187,7 +203,7 @@ def _build_args(particles, origin, cell_size, dims, out: GridIndex, workspace, f
         _require_gpu(getattr(out, name), name, torch.int32)
     _require_gpu(out.reordered, "reordered", torch.float32)
     _require_gpu(workspace, "workspace", torch.uint8)
-    cells = d[0] * d[1] * d[2]
+    cells = key_count(d, flags)
     if out.celdaDe.numel() < n or out.ordenado.numel() < n or out.reordered.numel() < 8 * n:
         raise ValueError("per-particle outputs are smaller than N")
     if out.conteos.numel() < cells or out.inicios.numel() < cells + 1:
@@ -209,13 +225,14 @@ def grid_build(
     *,
     stable: bool = False,
     gather: bool = False,
+    morton: bool = False,
     out: Optional[GridIndex] = None,
     workspace: Optional[torch.Tensor] = None,
     stream=None,
 ) -> GridIndex:
     """ugp_grid_build on torch tensors; enqueued on the current stream."""
     lib = load_library()
-    flags = (FLAG_STABLE if stable else 0) | (FLAG_GATHER if gather else 0)
+    flags = _flags(stable, gather, morton)
     n = int(particles.shape[0])
     if out is None or workspace is None:
         o2, w2 = alloc_outputs(n, dims, particles.device, flags)
@@ -236,6 +253,7 @@ def grid_build_diag(
     diag: Optional[torch.Tensor] = None,
     stable: bool = False,
     gather: bool = False,
+    morton: bool = False,
     out: Optional[GridIndex] = None,
     workspace: Optional[torch.Tensor] = None,
     stream=None,
@@ -243,7 +261,7 @@ def grid_build_diag(
     """ugp_grid_build_diag: the build plus the overflow diagnostics in `diag`
     (2 u32 on the GPU: largest cell occupancy, insertions past `capacity`)."""
     lib = load_library()
-    flags = (FLAG_STABLE if stable else 0) | (FLAG_GATHER if gather else 0)
+    flags = _flags(stable, gather, morton)
     n = int(particles.shape[0])
     if out is None or workspace is None:
         o2, w2 = alloc_outputs(n, dims, particles.device, flags)
@@ -341,5 +359,5 @@ __all__ = [
     "GridIndex", "UGPError", "alloc_outputs", "as_u32_numpy", "cell_diag", "exclusive_scan_u32", "grid_build",
     "grid_build_diag",
     "grid_build_stage", "grid_build_timed", "library_path", "load_library", "reorder", "stage_names",
-    "status_string", "workspace_bytes", "FLAG_STABLE", "FLAG_GATHER", "NUM_STAGES",
+    "status_string", "workspace_bytes", "key_count", "FLAG_STABLE", "FLAG_GATHER", "FLAG_MORTON", "NUM_STAGES",
 ]

@@ -17,6 +17,7 @@ struct GridParams {
   float tx, ty, tz;  // dims - 1 as floats (exact: dims <= 2^24)
   uint32_t nx;       // dims[0]
   uint32_t nxy;      // dims[0] * dims[1] (fits: cells < 2^32)
+  uint32_t morton;   // 1: cells numbered along the Z curve, 0: linearly
 };
 
 // Cell along one axis: binary32 subtraction, correctly rounded binary32
@@ -32,11 +33,27 @@ __device__ __forceinline__ uint32_t axis_cell(float p, float o, float h, float t
   return static_cast<uint32_t>(f);
 }
 
-// Linear cell index x + y*nx + z*nx*ny (< cells <= 2^32-2, no wrap).
+// Spreads the low 10 bits of v to bit positions 0, 3, 6, ..., 27 (each
+// step moves the upper half of every group to a slot three times wider).
+__device__ __forceinline__ uint32_t spread_bits3(uint32_t v) {
+  v &= 0x3FFu;
+  v = (v | (v << 16)) & 0x030000FFu;
+  v = (v | (v << 8)) & 0x0300F00Fu;
+  v = (v | (v << 4)) & 0x030C30C3u;
+  v = (v | (v << 2)) & 0x09249249u;
+  return v;
+}
+
+// Cell key of a position. Linear: x + y*nx + z*nx*ny (< cells <= 2^32-2,
+// no wrap). Morton (page "Reordenar por celda y la coalescencia de
+// memoria", section "El orden de las celdas también importa"): bit b of
+// x, y, z at key bits 3b, 3b+1, 3b+2 (coordinates < 2^10 on such grids).
+// g.morton is the same for every thread, so the branch is uniform.
 __device__ __forceinline__ uint32_t cell_of(float x, float y, float z, const GridParams& g) {
   const uint32_t kx = axis_cell(x, g.ox, g.h, g.tx);
   const uint32_t ky = axis_cell(y, g.oy, g.h, g.ty);
   const uint32_t kz = axis_cell(z, g.oz, g.h, g.tz);
+  if (g.morton) return spread_bits3(kx) | (spread_bits3(ky) << 1) | (spread_bits3(kz) << 2);
   return kx + ky * g.nx + kz * g.nxy;
 }
 

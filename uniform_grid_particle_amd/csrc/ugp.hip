@@ -44,6 +44,7 @@ using namespace ugp;
 
 constexpr uint32_t kMaxKeyBlocks = 1024;  // rows of the tiled block x tile matrix
 constexpr uint32_t kCounterWords = 64;    // small counter block (direct path)
+constexpr uint32_t kMortonMaxBits = 10;   // Morton keys: 10 bits per axis, 2^30 keys
 
 enum class Path { kEmpty, kStaged, kTiled, kDirect };
 
@@ -81,11 +82,19 @@ struct Plan {
 
 int make_plan(uint32_t n, const uint32_t dims[3], uint32_t flags, Plan* p) {
   if (!dims) return UGP_ERR_NULL;
-  if (flags & ~(UGP_FLAG_STABLE | UGP_FLAG_GATHER)) return UGP_ERR_ARG;
+  if (flags & ~(UGP_FLAG_STABLE | UGP_FLAG_GATHER | UGP_FLAG_MORTON)) return UGP_ERR_ARG;
   for (int a = 0; a < 3; ++a)
     if (dims[a] < 1u || dims[a] > kMaxDim) return UGP_ERR_RANGE;
-  const uint64_t cells = static_cast<uint64_t>(dims[0]) * dims[1] * dims[2];
+  uint64_t cells = static_cast<uint64_t>(dims[0]) * dims[1] * dims[2];
   if (cells > 0xFFFFFFFEull) return UGP_ERR_RANGE;
+  if (flags & UGP_FLAG_MORTON) {
+    // keys: 2^(3B), 2^B the smallest power of two >= the largest dimension
+    uint32_t largest = dims[0] > dims[1] ? dims[0] : dims[1];
+    largest = largest > dims[2] ? largest : dims[2];
+    const uint32_t bits = ceil_log2_u64(largest);
+    if (bits > kMortonMaxBits) return UGP_ERR_RANGE;
+    cells = 1ull << (3u * bits);
+  }
   *p = Plan{};
   p->cells = cells;
   p->stable = (flags & UGP_FLAG_STABLE) != 0;
@@ -239,6 +248,7 @@ GridParams grid_params(const BuildArgs& a) {
   g.tz = static_cast<float>(a.dims[2] - 1u);
   g.nx = a.dims[0];
   g.nxy = a.dims[0] * a.dims[1];
+  g.morton = (a.flags & UGP_FLAG_MORTON) ? 1u : 0u;
   return g;
 }
 
@@ -510,6 +520,15 @@ const char* ugp_status_string(int status) {
     case UGP_ERR_HIP: return "HIP runtime error while enqueueing";
     default: return "unknown status";
   }
+}
+
+int ugp_grid_key_count(const uint32_t dims[3], uint32_t flags, uint64_t* keys) {
+  if (!keys) return UGP_ERR_NULL;
+  Plan p;
+  const int st = make_plan(0, dims, flags, &p);
+  if (st != UGP_OK) return st;
+  *keys = p.cells;
+  return UGP_OK;
 }
 
 int ugp_grid_workspace_bytes(uint32_t n, const uint32_t dims[3], uint32_t flags, size_t* bytes) {
