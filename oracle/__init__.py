@@ -71,6 +71,10 @@ class Oracle:
             _f32p, ctypes.c_uint32, _f32p, ctypes.c_float, _u32p, ctypes.c_uint32,
             _u32p, _u32p, _u32p, _u32p, _f32p, _u32p,
         ]
+        lib.ugp_oracle_neighbor_count.argtypes = [
+            _f32p, ctypes.c_uint32, _f32p, ctypes.c_float, _u32p, ctypes.c_uint32,
+            _u32p, _u32p, ctypes.c_float, _u32p,
+        ]
         lib.ugp_oracle_diag.argtypes = [
             _u32p, ctypes.c_uint32, ctypes.c_uint32,
             ctypes.POINTER(ctypes.c_uint32), ctypes.POINTER(ctypes.c_uint32),
@@ -80,7 +84,7 @@ class Oracle:
             lib.ugp_oracle_exclusive_scan, lib.ugp_oracle_scatter, lib.ugp_oracle_reorder,
             lib.ugp_oracle_grid_build, lib.ugp_oracle_diag, lib.ugp_oracle_morton_bits,
             lib.ugp_oracle_morton_keys, lib.ugp_oracle_key_count, lib.ugp_oracle_cell_key,
-            lib.ugp_oracle_grid_build_keyed,
+            lib.ugp_oracle_grid_build_keyed, lib.ugp_oracle_neighbor_count,
         ):
             fn.restype = ctypes.c_int
 
@@ -199,6 +203,24 @@ class Oracle:
         )
         self._check(st, "grid_build")
         return GridIndex(celdaDe, conteos, inicios, ordenado, reordered)
+
+    def neighbor_count(self, particles, origin, cell_size, dims, radius: float, morton: bool = False,
+                       index: "GridIndex | None" = None) -> np.ndarray:
+        """Per particle (original order): other particles in the 27 cells around
+        its cell within `radius` (binary32 squared distance)."""
+        p = np.ascontiguousarray(particles, dtype=np.float32).reshape(-1, 8)
+        o, h, d = self._grid(origin, cell_size, dims)
+        if index is None:
+            index = self.grid_build(p, o, h, d, morton=morton)
+        ini = np.ascontiguousarray(index.inicios, dtype=np.uint32)
+        ordn = np.ascontiguousarray(index.ordenado, dtype=np.uint32)
+        out = np.empty(p.shape[0], dtype=np.uint32)
+        st = self._lib.ugp_oracle_neighbor_count(
+            self._p(p, _f32p), p.shape[0], self._p(o, _f32p), h, self._p(d, _u32p),
+            ORDER_MORTON if morton else ORDER_LINEAR, self._p(ini, _u32p), self._p(ordn, _u32p),
+            np.float32(radius), self._p(out, _u32p))
+        self._check(st, "neighbor_count")
+        return out
 
     def diag(self, conteos, capacity: int) -> tuple[int, int]:
         c = np.ascontiguousarray(conteos, dtype=np.uint32)

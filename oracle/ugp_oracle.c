@@ -49,6 +49,17 @@
  *    padded to B bits, 2^B being the smallest power of two >= the largest
  *    dimension, so there are 2^(3B) keys (exactly the cell count on a cubic
  *    power-of-two grid; other grids leave keys no cell maps to).
+ *  - "Construir el índice de la rejilla con un prefix sum", section "La
+ *    dispersión" (walking one cell's slice), and "Reordenar por celda y la
+ *    coalescencia de memoria", section "El orden de las celdas también
+ *    importa" (the neighbour loop visits the 27 cells around a particle's
+ *    cell): a neighbour query that consumes the index. The pages give no
+ *    kernel for it; the reading taken is a neighbour count -- for each
+ *    particle, the other particles in the 27 cells around its (clamped)
+ *    cell whose squared distance is <= radius^2, the squared distance being
+ *    (dx*dx + dy*dy) + dz*dz in binary32 with dx = xj - xi. With radius <=
+ *    cell size and every particle inside the grid this is every neighbour
+ *    within the radius.
  */
 #include <float.h>
 #include <math.h>
@@ -320,5 +331,60 @@ int ugp_oracle_diag(const uint32_t *conteos, uint32_t cells, uint32_t capacity,
     }
     *max_per_cell = mx;
     *overflows = (uint32_t)ov;
+    return UGPO_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* Neighbour count over the 27 cells around each particle's cell.       */
+/* index: the keyed build of the same particles (inicios, ordenado).    */
+/* counts[i] for particle i, in the original order.                     */
+/* ------------------------------------------------------------------ */
+
+int ugp_oracle_neighbor_count(const float *particles, uint32_t n, const float origin[3],
+                              float cell_size, const uint32_t dims[3], uint32_t order,
+                              const uint32_t *inicios, const uint32_t *ordenado, float radius,
+                              uint32_t *counts) {
+    uint64_t keys = 0;
+    int st = ugp_oracle_key_count(origin, cell_size, dims, order, &keys);
+    if (st != UGPO_OK) return st;
+    if (!isfinite(radius) || !(radius >= 0.0f)) return UGPO_ERR_ARG;
+    if (n == 0) return UGPO_OK;
+    if (!particles || !inicios || !ordenado || !counts) return UGPO_ERR_NULL;
+    uint32_t bits = 0;
+    if (order == UGPO_ORDER_MORTON) ugp_oracle_morton_bits(dims, &bits, NULL);
+    const float r2 = radius * radius;
+    for (uint32_t i = 0; i < n; ++i) {
+        const float *pi = particles + (size_t)i * 8u;
+        int64_t k[3];
+        for (int a = 0; a < 3; ++a) k[a] = oracle_axis_cell(pi[a], origin[a], cell_size, dims[a]);
+        uint32_t count = 0;
+        for (int64_t z = k[2] - 1; z <= k[2] + 1; ++z) {
+            if (z < 0 || z >= (int64_t)dims[2]) continue;
+            for (int64_t y = k[1] - 1; y <= k[1] + 1; ++y) {
+                if (y < 0 || y >= (int64_t)dims[1]) continue;
+                for (int64_t x = k[0] - 1; x <= k[0] + 1; ++x) {
+                    if (x < 0 || x >= (int64_t)dims[0]) continue;
+                    uint64_t c;
+                    if (order == UGPO_ORDER_MORTON)
+                        c = ugp_oracle_morton_key((uint32_t)x, (uint32_t)y, (uint32_t)z, bits);
+                    else
+                        c = (uint64_t)x + (uint64_t)y * dims[0] + (uint64_t)z * dims[0] * dims[1];
+                    if (c >= keys) return UGPO_ERR_RANGE;
+                    for (uint32_t t = inicios[c]; t < inicios[c + 1]; ++t) {
+                        const uint32_t j = ordenado[t];
+                        if (j >= n) return UGPO_ERR_RANGE;
+                        if (j == i) continue;
+                        const float *pj = particles + (size_t)j * 8u;
+                        const float dx = pj[0] - pi[0];
+                        const float dy = pj[1] - pi[1];
+                        const float dz = pj[2] - pi[2];
+                        const float d2 = dx * dx + dy * dy + dz * dz;
+                        if (d2 <= r2) count += 1u;
+                    }
+                }
+            }
+        }
+        counts[i] = count;
+    }
     return UGPO_OK;
 }

@@ -414,3 +414,57 @@ def pin_morton_relabels_linear(orc, wl):
         a = mor.ordenado[mor.inicios[k]:mor.inicios[k + 1]].tolist()
         b = lin.ordenado[lin.inicios[lc]:lin.inicios[lc + 1]].tolist()
         assert a == b, (k, lc)
+
+
+# ---------------------------------------------------------------------------
+# 27-cell neighbour count (a consumer of the index). Pinned against brute
+# force over all pairs (no grid involved), a lattice with a closed-form
+# answer (distance exactly equal to the radius counts), and pair symmetry.
+# ---------------------------------------------------------------------------
+
+
+def brute_force_neighbors(particles, radius) -> np.ndarray:
+    """#{j != i : (dx*dx + dy*dy) + dz*dz <= r*r}, binary32, all pairs."""
+    p = np.ascontiguousarray(particles[:, :3], dtype=np.float32)
+    r2 = np.float32(radius) * np.float32(radius)
+    out = np.zeros(p.shape[0], dtype=np.int64)
+    for s in range(0, p.shape[0], 512):
+        d = p[None, :, :] - p[s:s + 512, None, :]  # row i, column j: p[j] - p[i]
+        d2 = (d[..., 0] * d[..., 0] + d[..., 1] * d[..., 1]) + d[..., 2] * d[..., 2]
+        hit = d2 <= r2
+        hit[np.arange(hit.shape[0]), np.arange(s, s + hit.shape[0])] = False  # not itself
+        out[s:s + 512] = hit.sum(1)
+    return out
+
+
+def pin_neighbors_brute_force(orc, wl, radius, morton=False):
+    """With radius <= cell size and every particle inside the grid, the
+    27-cell count equals the all-pairs count."""
+    lo = np.asarray(wl.origin, np.float64)
+    hi = lo + np.asarray(wl.dims, np.float64) * float(wl.cell_size)
+    p = wl.particles[:, :3].astype(np.float64)
+    assert np.all((p >= lo) & (p < hi)), "pin needs every particle inside the grid"
+    assert radius <= float(wl.cell_size)
+    got = orc.neighbor_count(wl.particles, wl.origin, wl.cell_size, wl.dims, radius, morton=morton)
+    want = brute_force_neighbors(wl.particles, radius)
+    assert np.array_equal(got.astype(np.int64), want), np.nonzero(got != want)[0][:5]
+    assert int(got.sum()) % 2 == 0  # every pair counted from both ends
+
+
+def pin_neighbors_lattice(orc):
+    """Particles at the centres of a 6x5x4 grid of unit cells, radius 1: each
+    has exactly its axis neighbours (distance 1, equal to the radius; the
+    diagonals are at sqrt 2 and sqrt 3), i.e. the sum over axes of
+    [k > 0] + [k < dim - 1]. Radius 0.99: none."""
+    dims = (6, 5, 4)
+    g = np.stack(np.meshgrid(*[np.arange(d) for d in dims], indexing="ij"), -1).reshape(-1, 3)
+    rng = np.random.Generator(np.random.PCG64(6))
+    g = g[rng.permutation(g.shape[0])]
+    parts = np.zeros((g.shape[0], 8), np.float32)
+    parts[:, :3] = g + 0.5
+    want = sum((g[:, a] > 0).astype(int) + (g[:, a] < dims[a] - 1).astype(int) for a in range(3))
+    for morton in (False, True):
+        got = orc.neighbor_count(parts, np.zeros(3), 1.0, dims, 1.0, morton=morton)
+        assert np.array_equal(got.astype(np.int64), want)
+        got = orc.neighbor_count(parts, np.zeros(3), 1.0, dims, 0.99, morton=morton)
+        assert not got.any()

@@ -166,6 +166,12 @@ MUTATIONS = {
     ),
     "morton_stride_off": ("<< (3u * b + 2u);", "<< (3u * b + 3u);"),
     "morton_bits_floor": ("while ((1u << b) < largest) ++b;", "while ((2u << b) <= largest) ++b;"),
+    "neighbor_counts_self": ("if (j == i) continue;", "if (j == n) continue;"),
+    "neighbor_strict_radius": ("if (d2 <= r2) count += 1u;", "if (d2 < r2) count += 1u;"),
+    "neighbor_misses_lower_z": ("for (int64_t z = k[2] - 1; z <= k[2] + 1; ++z) {",
+                                "for (int64_t z = k[2]; z <= k[2] + 1; ++z) {"),
+    "neighbor_x_window_short": ("for (int64_t x = k[0] - 1; x <= k[0] + 1; ++x) {",
+                                "for (int64_t x = k[0] - 1; x <= k[0]; ++x) {"),
     "morton_drops_top_level": ("for (uint32_t b = 0; b < bits; ++b) {\n        key",
                                "for (uint32_t b = 0; b + 1 < bits; ++b) {\n        key"),
 }
@@ -198,6 +204,29 @@ def test_morton_relabels_linear(orc, which):
     pins.pin_morton_relabels_linear(orc, wl)
 
 
+def test_neighbors_lattice(orc):
+    pins.pin_neighbors_lattice(orc)
+
+
+@pytest.mark.parametrize("morton", [False, True])
+@pytest.mark.parametrize("frac", [1.0, 0.6])
+def test_neighbors_brute_force(orc, morton, frac):
+    wl = W.make_config("tiny")
+    pins.pin_neighbors_brute_force(orc, wl, frac * float(wl.cell_size), morton=morton)
+
+
+def test_neighbors_brute_force_dense_noncubic(orc):
+    """~40 particles per cell on a 9x6x4 grid (the pages' 20-60 per cell), duplicates included."""
+    rng = np.random.Generator(np.random.PCG64(17))
+    n = 9 * 6 * 4 * 40
+    parts = rng.standard_normal((n, 8)).astype(np.float32)
+    parts[:, :3] = (rng.random((n, 3)) * np.array([9.0, 6.0, 4.0]) * 0.5 - 1.0).astype(np.float32)
+    parts[100:120, :3] = parts[99, :3]  # coincident points: distance 0
+    wl = W.Workload("dense", parts, np.full(3, -1.0, np.float32), np.float32(0.5), np.array([9, 6, 4], np.uint32))
+    for morton in (False, True):
+        pins.pin_neighbors_brute_force(orc, wl, 0.5, morton=morton)
+
+
 def _all_pins(orc_m):
     tiny = W.make_config("tiny")
     face16 = W.make_boundary_probe((16, 16, 16), (-5.0, -5.0, -5.0), np.float32(0.625), per_axis_random=128)
@@ -219,6 +248,8 @@ def _all_pins(orc_m):
         lambda: pins.pin_morton_recursion_bijection(orc_m),
         lambda: pins.pin_morton_relabels_linear(orc_m, tiny),
         lambda: pins.pin_morton_relabels_linear(orc_m, noncubic),
+        lambda: pins.pin_neighbors_lattice(orc_m),
+        lambda: pins.pin_neighbors_brute_force(orc_m, tiny, float(tiny.cell_size)),
     ]
     failed = 0
     for chk in checks:
