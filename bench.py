@@ -226,6 +226,78 @@ def write_traffic_file(traffic: dict, path: str, command: str) -> None:
                 f.write(f"{stage}_bytes_per_dispatch: {b:.0f}\n")
 
 
+def candidate_pairs(conteos: np.ndarray, dims) -> int:
+    """Distance evaluations of one 27-cell neighbour pass, from the linear
+    histogram: every particle meets every particle of the (in-grid) 27 cells
+    around its cell except itself."""
+    nx, ny, nz = (int(v) for v in dims)
+    c = conteos.astype(np.int64).reshape(nz, ny, nx)
+    pad = np.pad(c, 1)
+    box = np.zeros_like(c)
+    for dz in range(3):
+        for dy in range(3):
+            for dx in range(3):
+                box += pad[dz:dz + nz, dy:dy + ny, dx:dx + nx]
+    return int((c * box).sum() - c.sum())
+
+
+def neighbor_bench(ugp, torch, dev, evict, stream, reps: int = 5) -> dict:
+    """27-cell neighbour count on the SPH-like workload: original order
+    through ordenado (the indirection) vs the build's reordered records, with
+    linear and Morton cell keys. Cold: caches evicted before each timing."""
+    import workloads
+
+    wl = workloads.make_sph_like()
+    n, dims = wl.n, [int(v) for v in wl.dims]
+    origin, h = [float(v) for v in wl.origin], float(wl.cell_size)
+    radius = workloads.SPH_RADIUS_FRACTION * h
+    parts = torch.from_numpy(wl.particles).to(dev)
+    out = torch.empty(n, dtype=torch.int32, device=dev)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        t = []
+        for _ in range(reps):
+            evict()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t.append(1e3 * e0.elapsed_time(e1))
+        return statistics.median(t)
+
+    res = {"workload": f"{n:,} uniform particles on {dims[0]}^3 cells (30.5 per cell), radius "
+                       f"{workloads.SPH_RADIUS_FRACTION} cell",
+           "radius": radius}
+    lin = ugp.grid_build(parts, origin, h, dims)
+    mor = ugp.grid_build(parts, origin, h, dims, morton=True)
+    torch.cuda.synchronize()
+    pairs = candidate_pairs(ugp.as_u32_numpy(lin.conteos), dims)
+    res["candidate_pairs"] = pairs
+    res["build_us"] = timed(lambda: ugp.grid_build(parts, origin, h, dims, out=lin))
+    runs = {
+        "indirect_linear": lambda: ugp.neighbor_count(parts, origin, h, dims, lin.inicios, lin.ordenado, radius, out=out),
+        "reordered_linear": lambda: ugp.neighbor_count(lin.reordered, origin, h, dims, lin.inicios, None, radius, out=out),
+        "indirect_morton": lambda: ugp.neighbor_count(parts, origin, h, dims, mor.inicios, mor.ordenado, radius,
+                                                      morton=True, out=out),
+        "reordered_morton": lambda: ugp.neighbor_count(mor.reordered, origin, h, dims, mor.inicios, None, radius,
+                                                       morton=True, out=out),
+    }
+    for name, fn in runs.items():
+        us = timed(fn)
+        res[name] = {"us": round(us, 2), "pairs_per_s": pairs / (us * 1e-6)}
+    res["mean_neighbors"] = float(ugp.as_u32_numpy(out).mean())
+    res["speedup_reordered_vs_indirect"] = res["indirect_linear"]["us"] / res["reordered_linear"]["us"]
+    res["speedup_morton_vs_linear_reordered"] = res["reordered_linear"]["us"] / res["reordered_morton"]["us"]
+    res["note"] = ("one thread per query; pairs = distance evaluations (27-cell candidates, self excluded); "
+                   "the reordered runs read the build's cell-ordered records, the indirect ones read the "
+                   "original array through ordenado")
+    return res
+
+
 def main(argv=None) -> int:
     if argv is None and len(sys.argv) > 1 and sys.argv[1] == "summarize":
         return summarize_main(sys.argv[2:])
@@ -236,6 +308,7 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default="baseline", choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--mode", default="atomic", choices=["atomic", "gather", "stable"])
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle timing (0 = skip)")
+    ap.add_argument("--no-neighbors", action="store_true", help="skip the neighbour-query section")
     ap.add_argument("--copy-reference", action="store_true",
                     help="also run a 256 MiB device copy (counter calibration for rocprofv3 --pmc)")
     args = ap.parse_args(argv)
@@ -492,6 +565,8 @@ def main(argv=None) -> int:
             "traffic": traffic,
         },
     }
+    if not args.no_neighbors:
+        result["neighbor_query"] = neighbor_bench(ugp, torch, dev, evict, stream)
     if args.cpu_budget > 0 and int(os.environ.get("RANK", "0")) == 0:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
     else:

@@ -210,6 +210,36 @@ int ugp_grid_build_diag(const ugp_particle *particles, uint32_t n, const float o
 int ugp_cell_diag(const uint32_t *conteos, uint32_t cells, uint32_t capacity, uint32_t *diag,
                   void *stream);
 
+/* A neighbour query that consumes a finished index: for each particle, the
+ * number of other particles among the 27 cells around its cell whose
+ * squared distance (dx*dx + dy*dy) + dz*dz (binary32, dx = xj - xi, no fused
+ * multiply-add) is <= radius*radius. Page "Construir el índice...", section
+ * "La dispersión" (walking a cell's slice), and page "Reordenar por
+ * celda...", sections "Qué cuesta la indirección" and "El orden de las
+ * celdas también importa" (the 27-cell loop; why the data order matters).
+ * With radius <= cell_size and every particle inside the grid this counts
+ * every neighbour within the radius; cells outside the grid are skipped.
+ *
+ *   particles  device, in: n records, 16-byte aligned. Either the build's
+ *              input (original order; pass its ordenado) or the build's
+ *              `reordered` output (cell order; pass ordenado = NULL).
+ *   origin, cell_size, dims   as given to the build
+ *   inicios    device, in: the build's K+1 starts (K = ugp_grid_key_count())
+ *   ordenado   device, in: the build's n particle indices, or NULL (above)
+ *   radius     finite, >= 0
+ *   counts     device, out: n u32, counts[k] for particle k of `particles`
+ *              (original index with ordenado; cell-order slot without);
+ *              must not overlap the inputs
+ *   flags      0 or UGP_FLAG_MORTON, as in the build
+ * Returns UGP_OK once enqueued; UGP_ERR_NULL / UGP_ERR_ARG / UGP_ERR_RANGE /
+ * UGP_ERR_ALIGN / UGP_ERR_ALIAS with nothing enqueued; UGP_ERR_HIP. The
+ * kernel reads inicios only at keys of in-grid cells and clips every slice
+ * to n, so an inconsistent index cannot make it read out of bounds. */
+int ugp_neighbor_count(const ugp_particle *particles, uint32_t n, const float origin[3],
+                       float cell_size, const uint32_t dims[3], const uint32_t *inicios,
+                       const uint32_t *ordenado, float radius, uint32_t *counts, uint32_t flags,
+                       void *stream);
+
 /* ugp_grid_build() with two caller-owned HIP events (hipEvent_t passed as
  * void*) recorded on `stream` immediately before and after stage slot
  * `timed_stage`, in the same call, so no host work separates the stages.

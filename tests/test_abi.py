@@ -209,3 +209,29 @@ def test_key_count_on_host(lib):
     assert ugp.stage_names(100, (257, 2, 2), ugp.FLAG_MORTON)[0] == "clear"
     assert ugp.stage_names(100, (257, 2, 2))[0] == "chunk_sort"
     assert ugp.workspace_bytes(1000, (7, 5, 3), ugp.FLAG_MORTON) > 0
+
+
+def test_neighbor_validation_on_host(lib):
+    b = 1 << 40
+    o = (ctypes.c_float * 3)(0, 0, 0)
+    d = (ctypes.c_uint32 * 3)(4, 4, 4)
+
+    def call(parts=b, ini=b + (1 << 30), ordn=b + (2 << 30), radius=1.0, counts=b + (3 << 30), flags=0, h=1.0, dims=d):
+        return lib.ugp_neighbor_count(parts, 100, o, ctypes.c_float(h), dims, ini, ordn, ctypes.c_float(radius),
+                                      counts, flags, None)
+
+    assert call(radius=float("nan")) == ugp.UGP_ERR_ARG
+    assert call(radius=-0.5) == ugp.UGP_ERR_ARG
+    assert call(h=0.0) == ugp.UGP_ERR_ARG
+    assert call(flags=ugp.FLAG_STABLE) == ugp.UGP_ERR_ARG
+    assert call(dims=(ctypes.c_uint32 * 3)(0, 4, 4)) == ugp.UGP_ERR_RANGE
+    assert call(dims=(ctypes.c_uint32 * 3)(2000, 4, 4), flags=ugp.FLAG_MORTON) == ugp.UGP_ERR_RANGE
+    assert call(parts=None) == ugp.UGP_ERR_NULL
+    assert call(ini=None) == ugp.UGP_ERR_NULL
+    assert call(counts=None) == ugp.UGP_ERR_NULL
+    assert call(parts=b + 8) == ugp.UGP_ERR_ALIGN
+    assert call(counts=b + (3 << 30) + 2) == ugp.UGP_ERR_ALIGN
+    assert call(counts=b + 64) == ugp.UGP_ERR_ALIAS  # inside the particles
+    assert call(counts=b + (2 << 30) + 8) == ugp.UGP_ERR_ALIAS  # inside ordenado
+    assert lib.ugp_neighbor_count(None, 0, o, ctypes.c_float(1.0), d, None, None, ctypes.c_float(1.0), None, 0,
+                                  None) == ugp.UGP_OK  # n = 0: nothing to do

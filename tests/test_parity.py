@@ -145,6 +145,18 @@ def test_tile_sizes(ugp, orc, dims):
         assert_parity(wl, run_gpu(ugp, wl, mode), ref, mode)
 
 
+@pytest.mark.parametrize("d", [16, 24, 32, 40, 64])
+def test_dense_grids(ugp, orc, d):
+    """1M particles on coarse grids (about 244, 72, 30, 16 and 4 per cell):
+    the tile size follows the particle density, down to 16 cells per tile."""
+    print(f"[parity] dense d={d}", flush=True)
+    wl = W.make_uniform(1_000_000, d, seed=50 + d)
+    assert ugp.stage_names(wl.n, wl.dims.tolist())[0] == "chunk_sort"
+    ref = orc.grid_build(wl.particles, wl.origin, wl.cell_size, wl.dims)
+    for mode in MODES:
+        assert_parity(wl, run_gpu(ugp, wl, mode), ref, mode)
+
+
 def test_direct_path_beyond_tiled_limit(ugp, orc):
     """More than 2^24 cells: the global-atomic path."""
     dims = (4096, 4097, 1)

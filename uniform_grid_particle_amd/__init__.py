@@ -83,6 +83,9 @@ def load_library():
     lib.ugp_grid_build_timed.argtypes = [*build_args, _u32, _vp, _vp]
     lib.ugp_grid_build_diag.restype = ctypes.c_int
     lib.ugp_grid_build_diag.argtypes = [*build_args[:-2], _u32, _vp, _u32, _vp]
+    lib.ugp_neighbor_count.restype = ctypes.c_int
+    lib.ugp_neighbor_count.argtypes = [_vp, _u32, ctypes.POINTER(ctypes.c_float), ctypes.c_float,
+                                       ctypes.POINTER(_u32), _vp, _vp, ctypes.c_float, _vp, _u32, _vp]
     lib.ugp_cell_diag.restype = ctypes.c_int
     lib.ugp_cell_diag.argtypes = [_vp, _u32, _u32, _vp, _vp]
     lib.ugp_grid_stage_name.restype = ctypes.c_char_p
@@ -293,6 +296,39 @@ def cell_diag(conteos: torch.Tensor, capacity: int, out: Optional[torch.Tensor] 
     return out
 
 
+def neighbor_count(particles: torch.Tensor, origin: Sequence[float], cell_size: float, dims: Sequence[int],
+                   inicios: torch.Tensor, ordenado: Optional[torch.Tensor], radius: float, *,
+                   morton: bool = False, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """ugp_neighbor_count: per-particle neighbour counts over the 27 cells.
+    Pass the build's input with its ordenado, or its `reordered` output with
+    ordenado=None (counts then follow the cell order)."""
+    lib = load_library()
+    _require_gpu(particles, "particles", torch.float32)
+    if particles.dim() != 2 or particles.shape[1] != 8:
+        raise ValueError("particles must have shape (N, 8)")
+    n = int(particles.shape[0])
+    d = _dims3(dims)
+    flags = FLAG_MORTON if morton else 0
+    _require_gpu(inicios, "inicios", torch.int32)
+    if inicios.numel() < key_count(d, flags) + 1:
+        raise ValueError("inicios is smaller than the key count + 1")
+    if ordenado is not None:
+        _require_gpu(ordenado, "ordenado", torch.int32)
+        if ordenado.numel() < n:
+            raise ValueError("ordenado is smaller than N")
+    if out is None:
+        out = torch.empty(n, dtype=torch.int32, device=particles.device)
+    _require_gpu(out, "out", torch.int32)
+    if out.numel() < n:
+        raise ValueError("out is smaller than N")
+    o = _f32_3(*[float(v) for v in origin])
+    st = lib.ugp_neighbor_count(_ptr(particles), n, o, ctypes.c_float(float(cell_size)), _u32_3(*d), _ptr(inicios),
+                                _ptr(ordenado), ctypes.c_float(float(radius)), _ptr(out), flags,
+                                _stream_handle(particles.device, stream))
+    _check(st, "ugp_neighbor_count")
+    return out
+
+
 def grid_build_stage(stage: int, particles, origin, cell_size, dims, out: GridIndex, workspace,
                      *, flags: int = 0, stream=None) -> None:
     """ugp_grid_build_stage: enqueue one stage with the same arguments."""
@@ -357,7 +393,7 @@ def as_u32_numpy(t: torch.Tensor):
 
 __all__ = [
     "GridIndex", "UGPError", "alloc_outputs", "as_u32_numpy", "cell_diag", "exclusive_scan_u32", "grid_build",
-    "grid_build_diag",
+    "grid_build_diag", "neighbor_count",
     "grid_build_stage", "grid_build_timed", "library_path", "load_library", "reorder", "stage_names",
     "status_string", "workspace_bytes", "key_count", "FLAG_STABLE", "FLAG_GATHER", "FLAG_MORTON", "NUM_STAGES",
 ]

@@ -1,0 +1,88 @@
+// kernels_neighbor.h -- a neighbour query that consumes the index: for each
+// particle, the number of other particles within a radius among the 27
+// cells around its cell (page "Construir el índice de la rejilla con un
+// prefix sum", section "La dispersión", for walking one cell's slice
+// [inicios[c], inicios[c+1]); page "Reordenar por celda y la coalescencia
+// de memoria", sections "Qué cuesta la indirección" and "El orden de las
+// celdas también importa", for the 27-cell loop and why the data order
+// matters).
+//
+// One thread per query particle, the loop the pages describe. Two data
+// orders:
+//   INDIRECT  particles in their original order; a cell's slice lists
+//             particle indices (ordenado) and every candidate position is
+//             a scattered read -- the indirection the reorder page prices.
+//   reordered particles already in cell order (the build's `reordered`);
+//             a slice is a contiguous run of records.
+// With the linear numbering the three cells x-1..x+1 of one row are
+// consecutive keys, so each of the 9 rows is one contiguous range; with
+// Morton keys each of the 27 cells is its own range.
+//
+// The squared distance is (dx*dx + dy*dy) + dz*dz in binary32, dx = xj - xi,
+// without contraction (the library is built with -ffp-contract=off), so the
+// comparison with r^2 is decided exactly as in a sequential reference.
+#pragma once
+
+#include "common.h"
+
+namespace ugp {
+
+constexpr int kNeighborBlock = 256;
+
+template <bool INDIRECT>
+__device__ __forceinline__ uint32_t count_range(const float4* __restrict__ parts,
+                                                const uint32_t* __restrict__ ordenado, uint32_t n,
+                                                uint32_t self, float4 pi, float r2, uint32_t s,
+                                                uint32_t e) {
+  e = (e < n) ? e : n;  // a slice never runs past the particle count
+  uint32_t cnt = 0;
+  for (uint32_t t = s; t < e; ++t) {
+    const uint32_t j = INDIRECT ? ordenado[t] : t;
+    if (j >= n || j == self) continue;
+    const float4 q = parts[2u * static_cast<size_t>(j)];
+    const float dx = q.x - pi.x;
+    const float dy = q.y - pi.y;
+    const float dz = q.z - pi.z;
+    const float d2 = dx * dx + dy * dy + dz * dz;
+    cnt += (d2 <= r2) ? 1u : 0u;
+  }
+  return cnt;
+}
+
+// counts[k] for query k: particle k of `parts` (original order when
+// INDIRECT, cell order otherwise). parts: n 32-byte records as float4 pairs.
+// dims: cells per axis; inicios: the build's starts (K+1 entries).
+template <bool INDIRECT, bool MORTON>
+__global__ __launch_bounds__(kNeighborBlock) void neighbor_count_kernel(
+    const float4* __restrict__ parts, uint32_t n, GridParams g, uint32_t ny, uint32_t nz,
+    const uint32_t* __restrict__ inicios, const uint32_t* __restrict__ ordenado, float r2,
+    uint32_t* __restrict__ counts) {
+  const uint32_t k = blockIdx.x * kNeighborBlock + threadIdx.x;
+  if (k >= n) return;
+  const float4 pi = parts[2u * static_cast<size_t>(k)];
+  const uint32_t kx = axis_cell(pi.x, g.ox, g.h, g.tx);
+  const uint32_t ky = axis_cell(pi.y, g.oy, g.h, g.ty);
+  const uint32_t kz = axis_cell(pi.z, g.oz, g.h, g.tz);
+  const uint32_t x0 = kx ? kx - 1u : 0u, x1 = (kx + 1u < g.nx) ? kx + 1u : kx;
+  const uint32_t y0 = ky ? ky - 1u : 0u, y1 = (ky + 1u < ny) ? ky + 1u : ky;
+  const uint32_t z0 = kz ? kz - 1u : 0u, z1 = (kz + 1u < nz) ? kz + 1u : kz;
+  uint32_t cnt = 0;
+  for (uint32_t z = z0; z <= z1; ++z) {
+    for (uint32_t y = y0; y <= y1; ++y) {
+      if (MORTON) {
+        const uint32_t yz = (spread_bits3(y) << 1) | (spread_bits3(z) << 2);
+        for (uint32_t x = x0; x <= x1; ++x) {
+          const uint32_t key = spread_bits3(x) | yz;
+          cnt += count_range<INDIRECT>(parts, ordenado, n, k, pi, r2, inicios[key], inicios[key + 1u]);
+        }
+      } else {
+        const uint32_t row = y * g.nx + z * g.nxy;
+        cnt += count_range<INDIRECT>(parts, ordenado, n, k, pi, r2, inicios[row + x0],
+                                     inicios[row + x1 + 1u]);
+      }
+    }
+  }
+  counts[k] = cnt;
+}
+
+}  // namespace ugp

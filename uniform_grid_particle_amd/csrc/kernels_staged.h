@@ -52,8 +52,9 @@ constexpr int kStagedRegs = 8;                      // particles per tile_sort t
 constexpr int kChunkThreads = 256;                  // chunk_sort workgroup
 constexpr uint32_t kChunk = kChunkThreads * kChunkItems;  // 2048 particles per chunk
 constexpr uint32_t kStagedTiles = 256;              // tiles at most (one tile_sort round)
-constexpr uint32_t kStagedMinShift = 12;
+constexpr uint32_t kStagedMinShift = 4;            // at least 16 cells per tile
 constexpr uint32_t kStagedMaxShift = 14;            // up to 16384 cells per tile
+constexpr uint64_t kStagedTarget = 4096;            // mean particles per tile sought (half the capacity)
 constexpr int kCellsThreads = 1024;                 // tile_sort workgroup
 constexpr uint32_t kCellsWin = 2048;                // tile_sort LDS staging window
 
@@ -175,11 +176,14 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
     uint32_t* __restrict__ inicios, uint32_t* __restrict__ ordenado, uint4* __restrict__ dst,
     uint32_t cap, uint32_t* __restrict__ diag) {
   constexpr uint32_t kTileCells = 1u << SHIFT;
-  constexpr uint32_t kPer = kTileCells / NT;  // cells per thread in the scan
+  // cells per thread in the scan (tiles smaller than the workgroup: one
+  // cell for each of the first kTileCells threads)
+  constexpr uint32_t kPer = (kTileCells >= NT) ? kTileCells / NT : 1u;
   constexpr uint32_t kChunksPerThread = kStagedMaxChunks / NT;
   constexpr uint32_t kStagedCap = NT * kStagedRegs;  // staged tile capacity
   constexpr uint32_t kStagedWin = WIN;
-  static_assert(kTileCells % NT == 0, "tile must cover the workgroup");
+  static_assert(kTileCells < NT || kTileCells % NT == 0, "whole cells per thread");
+  static_assert(SHIFT >= 2, "tiles start on 16-byte boundaries of conteos and inicios");
   static_assert(kStagedMaxChunks % NT == 0, "whole chunk rows per thread");
   static_assert(2 * WIN * 4 >= kStagedCap, "the source map fits in the staging buffer");
   __shared__ uint32_t s_cnt[kTileCells];
@@ -303,16 +307,21 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
   // block scan of the per-thread sums; s_cnt becomes the tile-local starts
   // (cells past tc count 0, so their start is the tile total)
   const uint32_t j0 = threadIdx.x * kPer;
+  const bool scans = j0 < kTileCells;
   uint32_t sum = 0;
+  if (scans) {
 #pragma unroll
-  for (uint32_t q = 0; q < kPer; ++q) sum += s_cnt[j0 + q];
+    for (uint32_t q = 0; q < kPer; ++q) sum += s_cnt[j0 + q];
+  }
   uint32_t tot;
   uint32_t run = block_exclusive_sum<NT>(sum, s_wave, &tot);
+  if (scans) {
 #pragma unroll
-  for (uint32_t q = 0; q < kPer; ++q) {
-    const uint32_t v = s_cnt[j0 + q];
-    s_cnt[j0 + q] = run;
-    run += v;
+    for (uint32_t q = 0; q < kPer; ++q) {
+      const uint32_t v = s_cnt[j0 + q];
+      s_cnt[j0 + q] = run;
+      run += v;
+    }
   }
   __syncthreads();
 

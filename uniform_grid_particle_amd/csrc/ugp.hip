@@ -32,6 +32,7 @@
 
 #include "common.h"
 #include "kernels_diag.h"
+#include "kernels_neighbor.h"
 #include "kernels_direct.h"
 #include "kernels_reorder.h"
 #include "kernels_staged.h"
@@ -107,8 +108,17 @@ int make_plan(uint32_t n, const uint32_t dims[3], uint32_t flags, Plan* p) {
     return UGP_OK;
   }
   const uint32_t tile_shift = (lg > kTileShiftMin + 9) ? lg - 9 : kTileShiftMin;
-  // staged path: at most 256 tiles (one round of tile_sort workgroups)
-  const uint32_t staged_shift = (lg > kStagedMinShift + 8) ? lg - 8 : kStagedMinShift;
+  // staged path: tiles of 2^shift consecutive keys. As large as 256 tiles
+  // allow (one round of tile_sort workgroups), but no larger than keeps the
+  // mean tile at kStagedTarget particles (dense grids: more, smaller tiles),
+  // and never more than kStagedMaxTiles tiles.
+  uint32_t staged_shift = (lg > kStagedMinShift + 8) ? lg - 8 : kStagedMinShift;
+  uint32_t dense_shift = 0;  // largest s with n * 2^s <= kStagedTarget * cells
+  while (dense_shift < 40 && (static_cast<uint64_t>(n) << (dense_shift + 1)) <= kStagedTarget * cells)
+    ++dense_shift;
+  if (dense_shift < staged_shift) staged_shift = dense_shift;
+  const uint32_t fewest_shift = (lg > kStagedMinShift + 9) ? lg - 9 : kStagedMinShift;  // 512 tiles
+  if (staged_shift < fewest_shift) staged_shift = fewest_shift;
   const uint64_t nchunks = (static_cast<uint64_t>(n) + kChunk - 1) / kChunk;
   if (staged_shift <= kStagedMaxShift && nchunks <= kStagedMaxChunks) {
     p->path = Path::kStaged;
@@ -286,25 +296,45 @@ void launch_tiled_cells(uint32_t shift, dim3 grid, hipStream_t s, const uint2* b
   }
 }
 
+template <bool MOVE, bool DIAG, uint32_t SHIFT>
+void launch_staged_cells_at(dim3 grid, hipStream_t s, const uint2* rows, uint32_t nchunks,
+                            uint32_t ntiles, GridParams g, uint32_t cells, uint32_t n,
+                            const uint4* chunk_rec, const uint32_t* chunk_idx, uint32_t* conteos,
+                            uint32_t* inicios, uint32_t* ordenado, uint4* dst, uint32_t cap,
+                            uint32_t* diag) {
+  hipLaunchKernelGGL((staged_cells_kernel<MOVE, DIAG, SHIFT, kCellsThreads, kCellsWin>), grid,
+                     dim3(kCellsThreads), 0, s, rows, nchunks, kChunk, ntiles, g, cells, n, chunk_rec,
+                     chunk_idx, conteos, inicios, ordenado, dst, cap, diag);
+}
+
 template <bool MOVE, bool DIAG>
 void launch_staged_cells(uint32_t shift, dim3 grid, hipStream_t s, const uint2* rows,
                          uint32_t nchunks, uint32_t ntiles, GridParams g, uint32_t cells,
                          uint32_t n, const uint4* chunk_rec, const uint32_t* chunk_idx,
                          uint32_t* conteos, uint32_t* inicios, uint32_t* ordenado, uint4* dst,
                          uint32_t cap, uint32_t* diag) {
-  const dim3 block(kCellsThreads);
-  if (shift == 12)
-    hipLaunchKernelGGL((staged_cells_kernel<MOVE, DIAG, 12, kCellsThreads, kCellsWin>), grid, block,
-                       0, s, rows, nchunks, kChunk, ntiles, g, cells, n, chunk_rec, chunk_idx,
-                       conteos, inicios, ordenado, dst, cap, diag);
-  else if (shift == 13)
-    hipLaunchKernelGGL((staged_cells_kernel<MOVE, DIAG, 13, kCellsThreads, kCellsWin>), grid, block,
-                       0, s, rows, nchunks, kChunk, ntiles, g, cells, n, chunk_rec, chunk_idx,
-                       conteos, inicios, ordenado, dst, cap, diag);
-  else
-    hipLaunchKernelGGL((staged_cells_kernel<MOVE, DIAG, 14, kCellsThreads, kCellsWin>), grid, block,
-                       0, s, rows, nchunks, kChunk, ntiles, g, cells, n, chunk_rec, chunk_idx,
-                       conteos, inicios, ordenado, dst, cap, diag);
+#define UGP_STAGED_CASE(S)                                                                    \
+  case S:                                                                                     \
+    launch_staged_cells_at<MOVE, DIAG, S>(grid, s, rows, nchunks, ntiles, g, cells, n, chunk_rec, \
+                                          chunk_idx, conteos, inicios, ordenado, dst, cap, diag); \
+    break;
+  switch (shift) {
+    UGP_STAGED_CASE(4)
+    UGP_STAGED_CASE(5)
+    UGP_STAGED_CASE(6)
+    UGP_STAGED_CASE(7)
+    UGP_STAGED_CASE(8)
+    UGP_STAGED_CASE(9)
+    UGP_STAGED_CASE(10)
+    UGP_STAGED_CASE(11)
+    UGP_STAGED_CASE(12)
+    UGP_STAGED_CASE(13)
+    default:
+      launch_staged_cells_at<MOVE, DIAG, 14>(grid, s, rows, nchunks, ntiles, g, cells, n, chunk_rec,
+                                             chunk_idx, conteos, inicios, ordenado, dst, cap, diag);
+      break;
+  }
+#undef UGP_STAGED_CASE
 }
 
 // Overflow diagnostics of a final conteos array: zero the two words, then
@@ -603,6 +633,51 @@ int ugp_cell_diag(const uint32_t* conteos, uint32_t cells, uint32_t capacity, ui
   if (!aligned(diag, 4) || (cells > 0 && !aligned(conteos, 16))) return UGP_ERR_ALIGN;
   if (overlap(span_of(conteos, 4ull * cells), span_of(diag, 8))) return UGP_ERR_ALIAS;
   enqueue_cell_diag(conteos, cells, capacity, diag, static_cast<hipStream_t>(stream));
+  return hipGetLastError() == hipSuccess ? UGP_OK : UGP_ERR_HIP;
+}
+
+int ugp_neighbor_count(const ugp_particle* particles, uint32_t n, const float origin[3],
+                       float cell_size, const uint32_t dims[3], const uint32_t* inicios,
+                       const uint32_t* ordenado, float radius, uint32_t* counts, uint32_t flags,
+                       void* stream) {
+  if (!origin || !dims) return UGP_ERR_NULL;
+  if (flags & ~UGP_FLAG_MORTON) return UGP_ERR_ARG;
+  Plan p;
+  int st = make_plan(n, dims, flags, &p);
+  if (st != UGP_OK) return st;
+  if (!std::isfinite(cell_size) || !(cell_size >= FLT_MIN)) return UGP_ERR_ARG;
+  for (int k = 0; k < 3; ++k)
+    if (!std::isfinite(origin[k])) return UGP_ERR_ARG;
+  if (!std::isfinite(radius) || !(radius >= 0.0f)) return UGP_ERR_ARG;
+  if (n == 0) return UGP_OK;
+  if (!particles || !inicios || !counts) return UGP_ERR_NULL;
+  if (!aligned(particles, 16) || !aligned(inicios, 4) || !aligned(counts, 4) ||
+      (ordenado && !aligned(ordenado, 4)))
+    return UGP_ERR_ALIGN;
+  const Span sc = span_of(counts, 4ull * n);
+  if (overlap(sc, span_of(particles, 32ull * n)) || overlap(sc, span_of(inicios, 4 * (p.cells + 1))) ||
+      overlap(sc, span_of(ordenado, ordenado ? 4ull * n : 0)))
+    return UGP_ERR_ALIAS;
+  BuildArgs a = make_args(particles, n, origin, cell_size, dims, nullptr, nullptr, nullptr, nullptr,
+                          nullptr, nullptr, 0, flags, stream);
+  const GridParams g = grid_params(a);
+  const float r2 = radius * radius;
+  const dim3 grid(blocks_for(n, kNeighborBlock)), block(kNeighborBlock);
+  const float4* pf = reinterpret_cast<const float4*>(particles);
+  hipStream_t s = a.stream;
+  const bool morton = (flags & UGP_FLAG_MORTON) != 0;
+  if (ordenado && morton)
+    hipLaunchKernelGGL((neighbor_count_kernel<true, true>), grid, block, 0, s, pf, n, g, dims[1], dims[2],
+                       inicios, ordenado, r2, counts);
+  else if (ordenado)
+    hipLaunchKernelGGL((neighbor_count_kernel<true, false>), grid, block, 0, s, pf, n, g, dims[1], dims[2],
+                       inicios, ordenado, r2, counts);
+  else if (morton)
+    hipLaunchKernelGGL((neighbor_count_kernel<false, true>), grid, block, 0, s, pf, n, g, dims[1], dims[2],
+                       inicios, nullptr, r2, counts);
+  else
+    hipLaunchKernelGGL((neighbor_count_kernel<false, false>), grid, block, 0, s, pf, n, g, dims[1], dims[2],
+                       inicios, nullptr, r2, counts);
   return hipGetLastError() == hipSuccess ? UGP_OK : UGP_ERR_HIP;
 }
 

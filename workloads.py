@@ -42,6 +42,8 @@ __all__ = [
     "make_boundary_probe",
     "make_cell_centres",
     "make_worked_example",
+    "make_sph_like",
+    "SPH_RADIUS_FRACTION",
 ]
 
 
@@ -167,6 +169,19 @@ def make_config(name: str, seed: int | None = None) -> Workload:
     if key == "contention":
         return make_contention(n=n, d=d, seed=s, name=key)
     return make_uniform(n, d, s, name=key)
+
+
+# Neighbour-query workload: 1,000,000 uniform particles on 32^3 cells gives
+# 30.5 particles per cell (inside the 20-60 per cell of a well-resolved fluid
+# on the counting page, section on dense-cell contention), and a radius of
+# 0.87 cell gives (4/3) pi 0.87^3 * 30.5 ~ 84 neighbours per particle, the
+# SPH figure on the reorder page (section "Qué cuesta la indirección").
+SPH_RADIUS_FRACTION = 0.87
+
+
+def make_sph_like(n: int = 1_000_000, d: int = 32, seed: int = 6) -> Workload:
+    """Uniform particles at SPH-like density for the 27-cell neighbour query."""
+    return make_uniform(n, d, seed, name="sph_like")
 
 
 def make_boundary_probe(
