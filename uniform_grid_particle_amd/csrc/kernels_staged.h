@@ -20,11 +20,13 @@
 //               particles in earlier tiles), expands the runs into a
 //               per-particle source map in LDS, loads its particles run by
 //               run, counts them into an LDS histogram of its cells
-//               (conteos), scans the histogram (inicios), takes every
-//               particle's slot with an LDS atomic, and writes ordenado and
-//               reordered through an LDS staging window so the stores are
-//               contiguous. A tile with more particles than the registers
-//               hold writes its slots directly instead.
+//               (conteos) keeping each particle's rank in its cell, scans
+//               the histogram (inicios), and writes ordenado and reordered
+//               at start + rank through an LDS staging window so the stores
+//               are contiguous. A tile with more particles than the
+//               registers hold (8192) goes in rounds of 8192: one counting
+//               pass, then a pass that takes slots from LDS cursors and
+//               writes them directly.
 //
 // The workgroup sizes, the chunk size and the staging window are template
 // parameters; the host picks them per problem size.
@@ -224,112 +226,64 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
   for (uint32_t j = threadIdx.x; j < kTileCells; j += NT) s_cnt[j] = 0u;
   __syncthreads();
 
-  // position in the chunk array of tile-local particle p: the last chunk whose
-  // run starts at or before p (runs of empty chunks start at the same place,
-  // the last of them is the non-empty one). Used only for tiles too large to
-  // stage; staged tiles expand the runs into a source map instead.
-  auto source_of = [&](uint32_t p) -> uint32_t {
-    uint32_t lo = 0, hi = nchunks - 1;
-    while (lo < hi) {
-      const uint32_t mid = (lo + hi + 1) >> 1;
-      if (s_dst[mid] <= p) lo = mid; else hi = mid - 1;
-    }
-    return s_src[lo] + (p - s_dst[lo]);
-  };
-
-  const bool staged = count <= kStagedCap;
-  // records held in registers as scalar arrays (static indices); lr packs a
-  // particle's tile-local cell (high half) and its rank in that cell (low
-  // half, < kStagedCap), all ones when the lane holds no particle
-  uint32_t w[8][kStagedRegs], idx[kStagedRegs], lr[kStagedRegs];
-#pragma unroll
-  for (int k = 0; k < kStagedRegs; ++k) lr[k] = 0xFFFFFFFFu;
-  if (staged) {
-    // source map: s_map[p] = chunk-array position of tile-local particle p
-    uint32_t* s_map = reinterpret_cast<uint32_t*>(s_rec);
+  // source map of a window of the tile: s_map[q] = chunk-array position of
+  // tile-local particle base + q, for q < len (s_map aliases the staging
+  // buffer, which holds kStagedCap words). Callers put barriers around it.
+  uint32_t* s_map = reinterpret_cast<uint32_t*>(s_rec);
+  auto build_map = [&](uint32_t base, uint32_t len) {
+    const uint32_t end = base + len;
     if (nchunks >= NT / 16) {
       // many chunks, short runs: each thread expands the runs of its chunks
 #pragma unroll
       for (uint32_t q = 0; q < kChunksPerThread; ++q) {
         const uint32_t c = threadIdx.x * kChunksPerThread + q;
-        if (c < nchunks)
-          for (uint32_t k = 0; k < r[q].x; ++k) s_map[s_dst[c] + k] = s_src[c] + k;
+        if (c < nchunks) {
+          const uint32_t d0 = s_dst[c], d1 = d0 + r[q].x;
+          const uint32_t lo = (d0 > base) ? d0 : base, hi = (d1 < end) ? d1 : end;
+          for (uint32_t k = lo; k < hi; ++k) s_map[k - base] = s_src[c] + (k - d0);
+        }
       }
     } else {
       // few chunks, long runs: one wave per run, its lanes striding the run
       const uint32_t lane = threadIdx.x & 63u;
       for (uint32_t c = threadIdx.x >> 6; c < nchunks; c += NT / 64) {
-        const uint32_t d0 = s_dst[c];
-        const uint32_t len = ((c + 1 < nchunks) ? s_dst[c + 1] : count) - d0;
-        const uint32_t s0 = s_src[c];
-        for (uint32_t k = lane; k < len; k += 64) s_map[d0 + k] = s0 + k;
+        const uint32_t d0 = s_dst[c], d1 = (c + 1 < nchunks) ? s_dst[c + 1] : count;
+        const uint32_t lo = (d0 > base) ? d0 : base, hi = (d1 < end) ? d1 : end;
+        for (uint32_t k = lo + lane; k < hi; k += 64) s_map[k - base] = s_src[c] + (k - d0);
       }
     }
-    __syncthreads();
-    if (count > 0) {  // count == 0: no valid source to clamp the idle lanes to
-      uint32_t src[kStagedRegs];
-#pragma unroll
-      for (int k = 0; k < kStagedRegs; ++k) {
-        const uint32_t p = threadIdx.x + k * NT;
-        src[k] = s_map[p < count ? p : 0u];  // clamped: loads below are unconditional
-      }
-#pragma unroll
-      for (int k = 0; k < kStagedRegs; ++k) {
-        const uint4 a = chunk_rec[static_cast<size_t>(src[k]) * 2u];
-        const uint4 b = MOVE ? chunk_rec[static_cast<size_t>(src[k]) * 2u + 1u] : make_uint4(0u, 0u, 0u, 0u);
-        idx[k] = chunk_idx[src[k]];
-        w[0][k] = a.x; w[1][k] = a.y; w[2][k] = a.z; w[3][k] = a.w;
-        w[4][k] = b.x; w[5][k] = b.y; w[6][k] = b.z; w[7][k] = b.w;
-      }
-      // count each particle and keep its rank: its slot is later the
-      // cell's start plus that rank
-#pragma unroll
-      for (int k = 0; k < kStagedRegs; ++k) {
-        const uint32_t p = threadIdx.x + k * NT;
-        if (p < count) {
-          const uint32_t loc = cell_of(__uint_as_float(w[0][k]), __uint_as_float(w[1][k]),
-                                       __uint_as_float(w[2][k]), g) - cell0;
-          if (loc < tc) lr[k] = (loc << 16) | atomicAdd(&s_cnt[loc], 1u);
-        }
-      }
-    }
-  } else {
-    for (uint32_t p = threadIdx.x; p < count; p += NT) {
-      const uint32_t s = source_of(p);
-      const uint4 a = chunk_rec[static_cast<size_t>(s) * 2u];
-      const uint32_t c = cell_of(__uint_as_float(a.x), __uint_as_float(a.y), __uint_as_float(a.z), g);
-      if (c - cell0 < tc) atomicAdd(&s_cnt[c - cell0], 1u);
-    }
-  }
-  __syncthreads();
+  };
 
   // exclusive scan in LDS: kPer consecutive cells per thread, then the
   // block scan of the per-thread sums; s_cnt becomes the tile-local starts
   // (cells past tc count 0, so their start is the tile total)
-  const uint32_t j0 = threadIdx.x * kPer;
-  const bool scans = j0 < kTileCells;
-  uint32_t sum = 0;
-  if (scans) {
+  auto scan_tile = [&]() -> uint32_t {
+    const uint32_t j0 = threadIdx.x * kPer;
+    const bool scans = j0 < kTileCells;
+    uint32_t sum = 0;
+    if (scans) {
 #pragma unroll
-    for (uint32_t q = 0; q < kPer; ++q) sum += s_cnt[j0 + q];
-  }
-  uint32_t tot;
-  uint32_t run = block_exclusive_sum<NT>(sum, s_wave, &tot);
-  if (scans) {
-#pragma unroll
-    for (uint32_t q = 0; q < kPer; ++q) {
-      const uint32_t v = s_cnt[j0 + q];
-      s_cnt[j0 + q] = run;
-      run += v;
+      for (uint32_t q = 0; q < kPer; ++q) sum += s_cnt[j0 + q];
     }
-  }
-  __syncthreads();
+    uint32_t tot;
+    uint32_t run = block_exclusive_sum<NT>(sum, s_wave, &tot);
+    if (scans) {
+#pragma unroll
+      for (uint32_t q = 0; q < kPer; ++q) {
+        const uint32_t v = s_cnt[j0 + q];
+        s_cnt[j0 + q] = run;
+        run += v;
+      }
+    }
+    __syncthreads();
+    return tot;
+  };
 
   // conteos and inicios out, from the starts: a cell's count is the next
   // start minus its own. Lane-contiguous 16-byte stores (tiles start at
-  // multiples of 4096 cells). DIAG: the same counts feed the overflow
+  // multiples of 16 cells). DIAG: the same counts feed the overflow
   // diagnostics (one more barrier, after which thread 0 publishes).
-  auto write_counts_starts = [&]() {
+  auto write_counts_starts = [&](uint32_t tot) {
     const uint4* s_cnt4 = reinterpret_cast<const uint4*>(s_cnt);
     const uint32_t tc4 = tc / 4;
     uint32_t dmax = 0, dover = 0;
@@ -370,7 +324,46 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
     }
   };
 
-  if (staged) {
+  if (count <= kStagedCap) {
+    // records held in registers as scalar arrays (static indices); lr packs
+    // a particle's tile-local cell (high half) and its rank in that cell
+    // (low half, < kStagedCap), all ones when the lane holds no particle.
+    // The two branches share nothing live, so these registers are not
+    // reserved while a tile past the capacity runs.
+    uint32_t w[8][kStagedRegs], idx[kStagedRegs], lr[kStagedRegs];
+#pragma unroll
+    for (int k = 0; k < kStagedRegs; ++k) lr[k] = 0xFFFFFFFFu;
+    build_map(0u, count);
+    __syncthreads();
+    if (count > 0) {  // count == 0: no valid source to clamp the idle lanes to
+      uint32_t src[kStagedRegs];
+#pragma unroll
+      for (int k = 0; k < kStagedRegs; ++k) {
+        const uint32_t p = threadIdx.x + k * NT;
+        src[k] = s_map[p < count ? p : 0u];  // clamped: loads below are unconditional
+      }
+#pragma unroll
+      for (int k = 0; k < kStagedRegs; ++k) {
+        const uint4 a = chunk_rec[static_cast<size_t>(src[k]) * 2u];
+        const uint4 b = MOVE ? chunk_rec[static_cast<size_t>(src[k]) * 2u + 1u] : make_uint4(0u, 0u, 0u, 0u);
+        idx[k] = chunk_idx[src[k]];
+        w[0][k] = a.x; w[1][k] = a.y; w[2][k] = a.z; w[3][k] = a.w;
+        w[4][k] = b.x; w[5][k] = b.y; w[6][k] = b.z; w[7][k] = b.w;
+      }
+      // count each particle and keep its rank: its slot is later the
+      // cell's start plus that rank
+#pragma unroll
+      for (int k = 0; k < kStagedRegs; ++k) {
+        const uint32_t p = threadIdx.x + k * NT;
+        if (p < count) {
+          const uint32_t loc = cell_of(__uint_as_float(w[0][k]), __uint_as_float(w[1][k]),
+                                       __uint_as_float(w[2][k]), g) - cell0;
+          if (loc < tc) lr[k] = (loc << 16) | atomicAdd(&s_cnt[loc], 1u);
+        }
+      }
+    }
+    __syncthreads();
+    const uint32_t tot = scan_tile();
     uint32_t slot[kStagedRegs];
 #pragma unroll
     for (int k = 0; k < kStagedRegs; ++k)
@@ -400,22 +393,82 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
     }
     // last: a later wait for a register loaded before a store would also
     // wait for that store (one counter tracks loads and stores)
-    write_counts_starts();
+    write_counts_starts(tot);
   } else {
-    write_counts_starts();
+    // a tile past the staged capacity (count > kStagedCap > 0): rounds of
+    // kStagedCap particles (kStagedRegs per thread), each with the source
+    // map of its window and its loads in flight together; the records are
+    // read again for the scatter below
+    for (uint32_t base = 0; base < count; base += kStagedCap) {
+      const uint32_t len = (count - base < kStagedCap) ? count - base : kStagedCap;
+      __syncthreads();  // the previous round's map reads are done
+      build_map(base, len);
+      __syncthreads();
+      uint32_t src[kStagedRegs];
+      float px[kStagedRegs], py[kStagedRegs], pz[kStagedRegs];
+#pragma unroll
+      for (int k = 0; k < kStagedRegs; ++k) {
+        const uint32_t q = threadIdx.x + k * NT;
+        src[k] = s_map[q < len ? q : 0u];  // clamped: loads below are unconditional
+      }
+#pragma unroll
+      for (int k = 0; k < kStagedRegs; ++k) {
+        const uint4 a = chunk_rec[static_cast<size_t>(src[k]) * 2u];
+        px[k] = __uint_as_float(a.x);
+        py[k] = __uint_as_float(a.y);
+        pz[k] = __uint_as_float(a.z);
+      }
+#pragma unroll
+      for (int k = 0; k < kStagedRegs; ++k) {
+        const uint32_t p = base + threadIdx.x + k * NT;
+        if (p < count) {
+          const uint32_t loc = cell_of(px[k], py[k], pz[k], g) - cell0;
+          if (loc < tc) atomicAdd(&s_cnt[loc], 1u);
+        }
+      }
+    }
+    __syncthreads();
+    const uint32_t tot = scan_tile();
+    write_counts_starts(tot);
     __syncthreads();  // every start read before the cursors advance
-    for (uint32_t p = threadIdx.x; p < count; p += NT) {
-      const uint32_t s = source_of(p);
-      const uint4 a = chunk_rec[static_cast<size_t>(s) * 2u];
-      const uint4 b = chunk_rec[static_cast<size_t>(s) * 2u + 1u];
-      const uint32_t c = cell_of(__uint_as_float(a.x), __uint_as_float(a.y), __uint_as_float(a.z), g);
-      if (c - cell0 < tc) {
-        const size_t out = static_cast<size_t>(bs) + atomicAdd(&s_cnt[c - cell0], 1u);
-        if (out < n) {
-          ordenado[out] = chunk_idx[s];
-          if (MOVE) {
-            dst[out * 2u] = a;
-            dst[out * 2u + 1u] = b;
+    // the same rounds: each particle takes its slot from its cell's cursor
+    // and is written there directly (the tile's output range is small
+    // enough that partial lines merge in L2)
+    constexpr int kOver = kStagedRegs;
+    for (uint32_t base = 0; base < count; base += NT * kOver) {
+      const uint32_t len = (count - base < NT * kOver) ? count - base : NT * kOver;
+      __syncthreads();  // the previous round's map reads are done
+      build_map(base, len);
+      __syncthreads();
+      uint32_t src[kOver], id[kOver], v[8][kOver];
+#pragma unroll
+      for (int k = 0; k < kOver; ++k) {
+        const uint32_t q = threadIdx.x + k * NT;
+        src[k] = s_map[q < len ? q : 0u];
+      }
+#pragma unroll
+      for (int k = 0; k < kOver; ++k) {
+        const uint4 a = chunk_rec[static_cast<size_t>(src[k]) * 2u];
+        const uint4 b = MOVE ? chunk_rec[static_cast<size_t>(src[k]) * 2u + 1u] : make_uint4(0u, 0u, 0u, 0u);
+        id[k] = chunk_idx[src[k]];
+        v[0][k] = a.x; v[1][k] = a.y; v[2][k] = a.z; v[3][k] = a.w;
+        v[4][k] = b.x; v[5][k] = b.y; v[6][k] = b.z; v[7][k] = b.w;
+      }
+#pragma unroll
+      for (int k = 0; k < kOver; ++k) {
+        const uint32_t p = base + threadIdx.x + k * NT;
+        if (p < count) {
+          const uint32_t loc = cell_of(__uint_as_float(v[0][k]), __uint_as_float(v[1][k]),
+                                       __uint_as_float(v[2][k]), g) - cell0;
+          if (loc < tc) {
+            const size_t out = static_cast<size_t>(bs) + atomicAdd(&s_cnt[loc], 1u);
+            if (out < n) {
+              ordenado[out] = id[k];
+              if (MOVE) {
+                dst[out * 2u] = make_uint4(v[0][k], v[1][k], v[2][k], v[3][k]);
+                dst[out * 2u + 1u] = make_uint4(v[4][k], v[5][k], v[6][k], v[7][k]);
+              }
+            }
           }
         }
       }
