@@ -75,6 +75,8 @@ class Oracle:
             _f32p, ctypes.c_uint32, _f32p, ctypes.c_float, _u32p, ctypes.c_uint32,
             _u32p, _u32p, ctypes.c_float, _u32p,
         ]
+        lib.ugp_oracle_gather_bytes.argtypes = [ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint32, _u32p,
+                                                 ctypes.c_uint32, ctypes.c_void_p]
         lib.ugp_oracle_diag.argtypes = [
             _u32p, ctypes.c_uint32, ctypes.c_uint32,
             ctypes.POINTER(ctypes.c_uint32), ctypes.POINTER(ctypes.c_uint32),
@@ -84,7 +86,7 @@ class Oracle:
             lib.ugp_oracle_exclusive_scan, lib.ugp_oracle_scatter, lib.ugp_oracle_reorder,
             lib.ugp_oracle_grid_build, lib.ugp_oracle_diag, lib.ugp_oracle_morton_bits,
             lib.ugp_oracle_morton_keys, lib.ugp_oracle_key_count, lib.ugp_oracle_cell_key,
-            lib.ugp_oracle_grid_build_keyed, lib.ugp_oracle_neighbor_count,
+            lib.ugp_oracle_grid_build_keyed, lib.ugp_oracle_neighbor_count, lib.ugp_oracle_gather_bytes,
         ):
             fn.restype = ctypes.c_int
 
@@ -220,6 +222,17 @@ class Oracle:
             ORDER_MORTON if morton else ORDER_LINEAR, self._p(ini, _u32p), self._p(ordn, _u32p),
             np.float32(radius), self._p(out, _u32p))
         self._check(st, "neighbor_count")
+        return out
+
+    def gather(self, src: np.ndarray, idx) -> np.ndarray:
+        """dst[k] = src[idx[k]] for arrays of fixed-size rows, byte for byte."""
+        a = np.ascontiguousarray(src)
+        i = np.ascontiguousarray(idx, dtype=np.uint32)
+        rows = a.shape[0]
+        eb = a.nbytes // rows if rows else a.itemsize * int(np.prod(a.shape[1:]))
+        out = np.empty((i.size,) + a.shape[1:], dtype=a.dtype)
+        st = self._lib.ugp_oracle_gather_bytes(a.ctypes.data, rows, eb, self._p(i, _u32p), i.size, out.ctypes.data)
+        self._check(st, "gather")
         return out
 
     def diag(self, conteos, capacity: int) -> tuple[int, int]:

@@ -60,6 +60,10 @@
  *    (dx*dx + dy*dy) + dz*dz in binary32 with dx = xj - xi. With radius <=
  *    cell size and every particle inside the grid this is every neighbour
  *    within the radius.
+ *  - "Reordenar por celda y la coalescencia de memoria", section "El kernel
+ *    de reordenación": when the state is split over several buffers, every
+ *    buffer is gathered with the same ordenado; the oracle gathers any
+ *    element size byte for byte.
  */
 #include <float.h>
 #include <math.h>
@@ -385,6 +389,25 @@ int ugp_oracle_neighbor_count(const float *particles, uint32_t n, const float or
             }
         }
         counts[i] = count;
+    }
+    return UGPO_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* Gather of one array of fixed-size elements: dst[k] = src[idx[k]],     */
+/* elem_bytes bytes each, for k < n (every idx[k] < n_src).              */
+/* ------------------------------------------------------------------ */
+
+int ugp_oracle_gather_bytes(const void *src, uint32_t n_src, uint32_t elem_bytes,
+                            const uint32_t *idx, uint32_t n, void *dst) {
+    if (n == 0) return UGPO_OK;
+    if (!src || !idx || !dst) return UGPO_ERR_NULL;
+    if (elem_bytes == 0) return UGPO_ERR_ARG;
+    const unsigned char *s = (const unsigned char *)src;
+    unsigned char *d = (unsigned char *)dst;
+    for (uint32_t k = 0; k < n; ++k) {
+        if (idx[k] >= n_src) return UGPO_ERR_RANGE;
+        memcpy(d + (size_t)k * elem_bytes, s + (size_t)idx[k] * elem_bytes, elem_bytes);
     }
     return UGPO_OK;
 }

@@ -468,3 +468,18 @@ def pin_neighbors_lattice(orc):
         assert np.array_equal(got.astype(np.int64), want)
         got = orc.neighbor_count(parts, np.zeros(3), 1.0, dims, 0.99, morton=morton)
         assert not got.any()
+
+
+def pin_gather_bytes(orc):
+    """Byte gather of split state: equals NumPy fancy indexing for every
+    element size, with repeated and reversed indices, bit for bit (NaN
+    payloads included)."""
+    rng = np.random.Generator(np.random.PCG64(44))
+    for eb in (4, 8, 12, 16, 20, 32, 48, 64):
+        rows = 777
+        a = rng.integers(0, 2 ** 32, size=(rows, eb // 4), dtype=np.uint64).astype(np.uint32)
+        a[5, 0] = 0x7FC0_0001  # a NaN payload as float32
+        for idx in (rng.integers(0, rows, 1000), np.arange(rows)[::-1], np.zeros(3, np.int64)):
+            got = orc.gather(a, idx)
+            assert np.array_equal(got, a[idx]), eb
+    assert orc.gather(np.zeros((4, 8), np.float32), np.zeros(0, np.uint32)).shape == (0, 8)

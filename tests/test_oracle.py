@@ -172,6 +172,10 @@ MUTATIONS = {
                                 "for (int64_t z = k[2]; z <= k[2] + 1; ++z) {"),
     "neighbor_x_window_short": ("for (int64_t x = k[0] - 1; x <= k[0] + 1; ++x) {",
                                 "for (int64_t x = k[0] - 1; x <= k[0]; ++x) {"),
+    "gather_short_copy": ("memcpy(d + (size_t)k * elem_bytes, s + (size_t)idx[k] * elem_bytes, elem_bytes);",
+                          "memcpy(d + (size_t)k * elem_bytes, s + (size_t)idx[k] * elem_bytes, elem_bytes - 4);"),
+    "gather_scatter_direction": ("memcpy(d + (size_t)k * elem_bytes, s + (size_t)idx[k] * elem_bytes, elem_bytes);",
+                                 "memcpy(d + (size_t)idx[k] * elem_bytes, s + (size_t)k * elem_bytes, elem_bytes);"),
     "morton_drops_top_level": ("for (uint32_t b = 0; b < bits; ++b) {\n        key",
                                "for (uint32_t b = 0; b + 1 < bits; ++b) {\n        key"),
 }
@@ -202,6 +206,10 @@ def test_morton_relabels_linear(orc, which):
     else:  # the contention recipe on a 32^3 grid (hot cell, clusters, clamped outsiders)
         wl = W.make_contention(20_000, 32, seed=4, hot=1000, per_cluster=3000, outside=1000)
     pins.pin_morton_relabels_linear(orc, wl)
+
+
+def test_gather_bytes(orc):
+    pins.pin_gather_bytes(orc)
 
 
 def test_neighbors_lattice(orc):
@@ -249,6 +257,7 @@ def _all_pins(orc_m):
         lambda: pins.pin_morton_relabels_linear(orc_m, tiny),
         lambda: pins.pin_morton_relabels_linear(orc_m, noncubic),
         lambda: pins.pin_neighbors_lattice(orc_m),
+        lambda: pins.pin_gather_bytes(orc_m),
         lambda: pins.pin_neighbors_brute_force(orc_m, tiny, float(tiny.cell_size)),
     ]
     failed = 0
