@@ -298,6 +298,74 @@ def neighbor_bench(ugp, torch, dev, evict, stream, reps: int = 5) -> dict:
     return res
 
 
+def reorder_policy_bench(ugp, torch, dev, evict, stream, reps: int = 5) -> dict:
+    """Reorder policies of the reorder page on MI355X: (a) hot kinematics and
+    cold appearance (32 bytes each) gathered with one index in one kernel vs
+    two single-array gathers; (b) on the SPH-like workload, the per-frame
+    cost of reordering every frame vs building only the index and querying
+    neighbours through ordenado on an array reordered some frames ago."""
+    import workloads
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        t = []
+        for _ in range(reps):
+            evict()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t.append(1e3 * e0.elapsed_time(e1))
+        return statistics.median(t)
+
+    res = {}
+    wl = workloads.make_config("baseline")
+    n = wl.n
+    hot = torch.from_numpy(wl.particles).to(dev)
+    cold = torch.rand((n, 8), device=dev)
+    idx = ugp.grid_build(hot, wl.origin.tolist(), float(wl.cell_size), wl.dims.tolist(), index_only=True).ordenado
+    outs = [torch.empty_like(hot), torch.empty_like(cold)]
+    one = timed(lambda: ugp.reorder_arrays(idx, [hot, cold], outs=outs))
+    two = timed(lambda: (ugp.reorder(hot, idx, out=outs[0]), ugp.reorder(cold, idx, out=outs[1])))
+    alg = 4 * n + 2 * 64 * n  # index once; each array 32 B read (gathered) + 32 B written
+    res["hot_cold_split"] = {"n": n, "one_kernel_us": round(one, 2), "two_kernels_us": round(two, 2),
+                             "one_kernel_GBps": round(alg / (one * 1e3), 1),
+                             "note": "1M particles, two 32-byte arrays, the build's ordenado as the index"}
+
+    wl = workloads.make_sph_like()
+    n, dims = wl.n, [int(v) for v in wl.dims]
+    origin, h = [float(v) for v in wl.origin], float(wl.cell_size)
+    radius = workloads.SPH_RADIUS_FRACTION * h
+    parts = torch.from_numpy(wl.particles).to(dev)
+    full = ugp.grid_build(parts, origin, h, dims)
+    state = full.reordered.clone()
+    gen = torch.Generator(device=dev).manual_seed(7)
+    frames = {}
+    counts = torch.empty(n, dtype=torch.int32, device=dev)
+    idx_out, idx_ws = ugp.alloc_outputs(n, dims, dev, ugp.FLAG_INDEX_ONLY)
+    for age in range(1, 9):  # frames since the last reorder; particles move 0.05 cell (rms, per axis) a frame
+        state[:, :3] += torch.randn((n, 3), device=dev, generator=gen) * (0.05 * h)
+        if age in (1, 4, 8):
+            b_us = timed(lambda: ugp.grid_build(state, origin, h, dims, index_only=True, out=idx_out, workspace=idx_ws))
+            q_us = timed(lambda: ugp.neighbor_count(state, origin, h, dims, idx_out.inicios, idx_out.ordenado, radius,
+                                                    out=counts))
+            frames[f"age_{age}"] = {"index_only_build_us": round(b_us, 2), "query_through_ordenado_us": round(q_us, 2)}
+    full_out, full_ws = ugp.alloc_outputs(n, dims, dev, 0)
+    fb_us = timed(lambda: ugp.grid_build(state, origin, h, dims, out=full_out, workspace=full_ws))
+    fq_us = timed(lambda: ugp.neighbor_count(full_out.reordered, origin, h, dims, full_out.inicios, None, radius,
+                                             out=counts))
+    res["every_n_frames"] = {
+        "workload": "SPH-like, 1M particles on 32^3, radius 0.87 cell; 0.05 cell of motion per frame",
+        "reorder_every_frame": {"build_us": round(fb_us, 2), "query_reordered_us": round(fq_us, 2),
+                                "frame_us": round(fb_us + fq_us, 2)},
+        "index_only_frames": frames,
+    }
+    return res
+
+
 def main(argv=None) -> int:
     if argv is None and len(sys.argv) > 1 and sys.argv[1] == "summarize":
         return summarize_main(sys.argv[2:])
@@ -375,7 +443,10 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     step_ms = [starts[k].elapsed_time(ends[k]) for k in range(K)]
-    ms_per_step = sum(step_ms) / K
+    # the median step (with p10/p90): a single step delayed by the host (the
+    # GPU idles until the launch arrives) must not stand for the kernels
+    ms_per_step = statistics.median(step_ms)
+    ms_mean = sum(step_ms) / K
 
     # ---- achievable bandwidth on this device: cold device-to-device copies,
     # one of 1 GiB moved (512 MiB read + 512 MiB written) and one moving the
@@ -528,7 +599,8 @@ def main(argv=None) -> int:
             "cell_size": h,
             "seed": wl.seed,
             "mode": args.mode,
-            "timing": "cold: 1 GiB read-only cache eviction before each step, outside the per-step HIP events",
+            "timing": "cold: 1 GiB read-only cache eviction before each step, outside the per-step HIP events; "
+                      "ms_per_step is the median of the K steps (mean, p10/p90 and worst step also reported)",
         },
         "hbm_frac_e2e": (b_total / t_s) / (HBM_PEAK_GBS * 1e9),
         "achievable_copy_GBps": {"1GiB": round(copy_big, 1), "same_bytes": round(copy_same, 1),
@@ -537,6 +609,8 @@ def main(argv=None) -> int:
                              "same_bytes": (b_total / t_s) / (copy_same * 1e9)},
         "alg_bytes_per_step": b_total,
         "step_ms_median": statistics.median(step_ms),
+        "step_ms_mean": ms_mean,
+        "step_ms_worst": [max(step_ms), int(np.argmax(step_ms))],
         "step_ms_p10_p90": [float(np.percentile(step_ms, 10)), float(np.percentile(step_ms, 90))],
         "warm_ms_per_step": warm_ms,
         "morton_variant": {"ms_per_step": morton_ms, "keys": ugp.key_count(dims, mflags),
@@ -567,6 +641,7 @@ def main(argv=None) -> int:
     }
     if not args.no_neighbors:
         result["neighbor_query"] = neighbor_bench(ugp, torch, dev, evict, stream)
+        result["reorder_policy"] = reorder_policy_bench(ugp, torch, dev, evict, stream)
     if args.cpu_budget > 0 and int(os.environ.get("RANK", "0")) == 0:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
     else:

@@ -97,6 +97,13 @@ typedef struct ugp_particle {
  * reordered are then in keys: conteos has K entries and inicios K+1
  * (ugp_grid_key_count()). */
 #define UGP_FLAG_MORTON 0x4u
+/* Build the index only: celdaDe, conteos, inicios and ordenado as usual,
+ * `reordered` neither written nor required (may be NULL). For reordering
+ * every few frames (page "Reordenar por celda...", section "Reordenar o
+ * no"): between reorders the caller keeps its array, rebuilds the index of
+ * the slightly moved particles, and reaches them through ordenado, which
+ * then points to nearby positions. */
+#define UGP_FLAG_INDEX_ONLY 0x8u
 
 /* Pipeline stage slots, for ugp_grid_build_stage() / ugp_grid_build_timed().
  * The library picks one of three execution paths from n and the key count K
@@ -148,7 +155,8 @@ int ugp_grid_workspace_bytes(uint32_t n, const uint32_t dims[3], uint32_t flags,
  *   ordenado    device, out: n u32, particle indices grouped by cell:
  *               cell c occupies [inicios[c], inicios[c+1])
  *   reordered   device, out: n records, reordered[k] = particles[ordenado[k]]
- *               bit for bit; must not overlap particles (double buffer,
+ *               bit for bit (unused, may be NULL, with UGP_FLAG_INDEX_ONLY);
+ *               must not overlap particles (double buffer,
  *               page "Reordenar por celda...", section "El kernel de
  *               reordenación")
  *   workspace   device scratch of at least ugp_grid_workspace_bytes(); its
@@ -279,6 +287,33 @@ int ugp_exclusive_scan_u32(const uint32_t *in, uint32_t count, uint32_t *out, vo
  *   dst  device, out: n records, must not overlap src or idx. */
 int ugp_reorder(const ugp_particle *src, uint32_t n_src, const uint32_t *idx, uint32_t n,
                 ugp_particle *dst, void *stream);
+
+/* One array of a split particle state for ugp_reorder_arrays(). */
+typedef struct ugp_array_desc {
+  const void *src;      /* device, in: n_src elements of elem_bytes */
+  void *dst;            /* device, out: n elements of elem_bytes */
+  uint32_t elem_bytes;  /* a multiple of 4 */
+} ugp_array_desc;
+
+/* Gather several arrays with one index in one kernel: for every array q and
+ * k < n, dst_q[k] = src_q[idx[k]], elem_bytes_q bytes, bit for bit. Page
+ * "Reordenar por celda...", section "El kernel de reordenación": a state
+ * split over buffers (page "El estado de las partículas en storage
+ * buffers", section "Array de estructuras o estructura de arrays": hot
+ * kinematics and cold appearance) is reordered with the same ordenado,
+ * read once for all arrays.
+ *   idx     device, in: n u32; entries >= n_src are skipped (that dst
+ *           element is left unwritten; the call still returns UGP_OK)
+ *   arrays  host, in: `count` descriptors, 1 <= count <= 8; pointers 4-byte
+ *           aligned; 16-byte element chunks are used when every size is a
+ *           multiple of 16 and every pointer 16-byte aligned, 4-byte chunks
+ *           otherwise; one element of all arrays together must fit 256
+ *           chunks (up to 4096 bytes with 16-byte chunks, 1024 otherwise).
+ *           No dst may overlap idx, any src, or another dst.
+ * Returns UGP_OK once enqueued, UGP_ERR_ARG / UGP_ERR_NULL / UGP_ERR_ALIGN /
+ * UGP_ERR_ALIAS with nothing enqueued, or UGP_ERR_HIP. */
+int ugp_reorder_arrays(const uint32_t *idx, uint32_t n, uint32_t n_src,
+                       const ugp_array_desc *arrays, uint32_t count, void *stream);
 
 /* Human-readable text for a status code (static storage, never NULL). */
 const char *ugp_status_string(int status);

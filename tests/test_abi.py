@@ -235,3 +235,26 @@ def test_neighbor_validation_on_host(lib):
     assert call(counts=b + (2 << 30) + 8) == ugp.UGP_ERR_ALIAS  # inside ordenado
     assert lib.ugp_neighbor_count(None, 0, o, ctypes.c_float(1.0), d, None, None, ctypes.c_float(1.0), None, 0,
                                   None) == ugp.UGP_OK  # n = 0: nothing to do
+
+
+def test_reorder_arrays_validation_on_host(lib):
+    b = 1 << 40
+
+    def call(descs, n=100, n_src=100, idx=b):
+        arr = (ugp.ArrayDesc * max(1, len(descs)))(*descs)
+        return lib.ugp_reorder_arrays(idx, n, n_src, arr, len(descs), None)
+
+    ok = ugp.ArrayDesc(b + (1 << 30), b + (2 << 30), 32)
+    assert call([]) == ugp.UGP_ERR_ARG
+    assert call([ok] * 9) == ugp.UGP_ERR_ARG
+    assert call([ugp.ArrayDesc(b + (1 << 30), b + (2 << 30), 6)]) == ugp.UGP_ERR_ARG
+    assert call([ugp.ArrayDesc(b + (1 << 30), b + (2 << 30), 0)]) == ugp.UGP_ERR_ARG
+    assert call([ugp.ArrayDesc(b + (1 << 30), b + (2 << 30), 4100)]) == ugp.UGP_ERR_ARG  # > 4096 bytes
+    assert call([ugp.ArrayDesc(b + (1 << 30) + 4, b + (2 << 30), 1028)]) == ugp.UGP_ERR_ARG  # > 256 4-byte chunks
+    assert call([ugp.ArrayDesc(None, b + (2 << 30), 32)]) == ugp.UGP_ERR_NULL
+    assert call([ugp.ArrayDesc(b + (1 << 30) + 2, b + (2 << 30), 32)]) == ugp.UGP_ERR_ALIGN
+    assert call([ok], idx=None) == ugp.UGP_ERR_NULL
+    assert call([ugp.ArrayDesc(b + (1 << 30), b + (1 << 30) + 64, 32)]) == ugp.UGP_ERR_ALIAS  # dst inside src
+    assert call([ok, ugp.ArrayDesc(b + (3 << 30), b + (2 << 30) + 32, 32)]) == ugp.UGP_ERR_ALIAS  # dsts overlap
+    assert call([ugp.ArrayDesc(b + (1 << 30), b + 16, 32)]) == ugp.UGP_ERR_ALIAS  # dst over idx
+    assert call([ok], n=0, idx=None) == ugp.UGP_OK

@@ -33,6 +33,7 @@ UGP_ERR_HIP = -7
 FLAG_STABLE = 0x1
 FLAG_GATHER = 0x2
 FLAG_MORTON = 0x4
+FLAG_INDEX_ONLY = 0x8
 
 NUM_STAGES = 6  # stage slots; names depend on the path, see stage_names()
 
@@ -42,6 +43,12 @@ _u32_3 = _u32 * 3
 _f32_3 = ctypes.c_float * 3
 
 _lib = None
+
+
+class ArrayDesc(ctypes.Structure):
+    """ugp_array_desc: one array of a split state."""
+
+    _fields_ = [("src", ctypes.c_void_p), ("dst", ctypes.c_void_p), ("elem_bytes", ctypes.c_uint32)]
 
 
 class UGPError(RuntimeError):
@@ -86,6 +93,8 @@ def load_library():
     lib.ugp_neighbor_count.restype = ctypes.c_int
     lib.ugp_neighbor_count.argtypes = [_vp, _u32, ctypes.POINTER(ctypes.c_float), ctypes.c_float,
                                        ctypes.POINTER(_u32), _vp, _vp, ctypes.c_float, _vp, _u32, _vp]
+    lib.ugp_reorder_arrays.restype = ctypes.c_int
+    lib.ugp_reorder_arrays.argtypes = [_vp, _u32, _u32, ctypes.POINTER(ArrayDesc), _u32, _vp]
     lib.ugp_cell_diag.restype = ctypes.c_int
     lib.ugp_cell_diag.argtypes = [_vp, _u32, _u32, _vp, _vp]
     lib.ugp_grid_stage_name.restype = ctypes.c_char_p
@@ -190,7 +199,7 @@ def alloc_outputs(n: int, dims: Sequence[int], device, flags: int = 0):
         conteos=torch.empty(cells, dtype=torch.int32, device=dev),
         inicios=torch.empty(cells + 1, dtype=torch.int32, device=dev),
         ordenado=torch.empty(n, dtype=torch.int32, device=dev),
-        reordered=torch.empty((n, 8), dtype=torch.float32, device=dev),
+        reordered=torch.empty((0 if flags & FLAG_INDEX_ONLY else n, 8), dtype=torch.float32, device=dev),
     )
     ws = torch.empty(max(workspace_bytes(n, d, flags), 256), dtype=torch.uint8, device=dev)
     return out, ws
@@ -204,10 +213,12 @@ def _build_args(particles, origin, cell_size, dims, out: GridIndex, workspace, f
     d = _dims3(dims)
     for name in ("celdaDe", "conteos", "inicios", "ordenado"):
         _require_gpu(getattr(out, name), name, torch.int32)
-    _require_gpu(out.reordered, "reordered", torch.float32)
+    index_only = bool(flags & FLAG_INDEX_ONLY)
+    if not index_only:
+        _require_gpu(out.reordered, "reordered", torch.float32)
     _require_gpu(workspace, "workspace", torch.uint8)
     cells = key_count(d, flags)
-    if out.celdaDe.numel() < n or out.ordenado.numel() < n or out.reordered.numel() < 8 * n:
+    if out.celdaDe.numel() < n or out.ordenado.numel() < n or (not index_only and out.reordered.numel() < 8 * n):
         raise ValueError("per-particle outputs are smaller than N")
     if out.conteos.numel() < cells or out.inicios.numel() < cells + 1:
         raise ValueError("per-cell outputs are smaller than the cell count")
@@ -215,7 +226,7 @@ def _build_args(particles, origin, cell_size, dims, out: GridIndex, workspace, f
     return [
         _ptr(particles), n, o, ctypes.c_float(float(cell_size)), _u32_3(*d),
         _ptr(out.celdaDe), _ptr(out.conteos), _ptr(out.inicios), _ptr(out.ordenado),
-        _ptr(out.reordered), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
+        None if index_only else _ptr(out.reordered), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
         int(flags), _stream_handle(particles.device, stream),
     ]
 
@@ -229,13 +240,15 @@ def grid_build(
     stable: bool = False,
     gather: bool = False,
     morton: bool = False,
+    index_only: bool = False,
     out: Optional[GridIndex] = None,
     workspace: Optional[torch.Tensor] = None,
     stream=None,
 ) -> GridIndex:
-    """ugp_grid_build on torch tensors; enqueued on the current stream."""
+    """ugp_grid_build on torch tensors; enqueued on the current stream.
+    index_only: build the index without writing `reordered`."""
     lib = load_library()
-    flags = _flags(stable, gather, morton)
+    flags = _flags(stable, gather, morton) | (FLAG_INDEX_ONLY if index_only else 0)
     n = int(particles.shape[0])
     if out is None or workspace is None:
         o2, w2 = alloc_outputs(n, dims, particles.device, flags)
@@ -386,6 +399,37 @@ def reorder(src: torch.Tensor, idx: torch.Tensor, out: Optional[torch.Tensor] = 
     return out
 
 
+def reorder_arrays(idx: torch.Tensor, srcs: Sequence[torch.Tensor], outs: Optional[Sequence[torch.Tensor]] = None,
+                   stream=None) -> list:
+    """ugp_reorder_arrays: out_q[k] = src_q[idx[k]] for every array in one
+    kernel. Each src is a contiguous GPU tensor whose first dimension indexes
+    particles (an element is one row, any dtype, a multiple of 4 bytes)."""
+    lib = load_library()
+    _require_gpu(idx, "idx", torch.int32)
+    n = int(idx.numel())
+    if not srcs:
+        raise ValueError("at least one array")
+    n_src = int(srcs[0].shape[0])
+    if outs is None:
+        outs = [torch.empty((n,) + tuple(s.shape[1:]), dtype=s.dtype, device=s.device) for s in srcs]
+    if len(outs) != len(srcs):
+        raise ValueError("one output per array")
+    descs = (ArrayDesc * len(srcs))()
+    for q, (s, o) in enumerate(zip(srcs, outs)):
+        for t, name in ((s, "src"), (o, "out")):
+            if not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{name} {q} must be a contiguous GPU tensor")
+        if int(s.shape[0]) != n_src:
+            raise ValueError("every source needs the same number of rows")
+        eb = s.element_size() * (s.numel() // max(1, s.shape[0]))
+        if o.dtype != s.dtype or tuple(o.shape[1:]) != tuple(s.shape[1:]) or int(o.shape[0]) < n:
+            raise ValueError(f"out {q} must match src {q} row shape and hold N rows")
+        descs[q] = ArrayDesc(s.data_ptr(), o.data_ptr(), eb)
+    st = lib.ugp_reorder_arrays(_ptr(idx), n, n_src, descs, len(srcs), _stream_handle(idx.device, stream))
+    _check(st, "ugp_reorder_arrays")
+    return list(outs)
+
+
 def as_u32_numpy(t: torch.Tensor):
     """Copy a u32-in-int32 GPU tensor to a NumPy uint32 array."""
     return t.detach().cpu().numpy().view("uint32")
@@ -393,7 +437,7 @@ def as_u32_numpy(t: torch.Tensor):
 
 __all__ = [
     "GridIndex", "UGPError", "alloc_outputs", "as_u32_numpy", "cell_diag", "exclusive_scan_u32", "grid_build",
-    "grid_build_diag", "neighbor_count",
+    "grid_build_diag", "neighbor_count", "reorder_arrays", "ArrayDesc", "FLAG_INDEX_ONLY",
     "grid_build_stage", "grid_build_timed", "library_path", "load_library", "reorder", "stage_names",
     "status_string", "workspace_bytes", "key_count", "FLAG_STABLE", "FLAG_GATHER", "FLAG_MORTON", "NUM_STAGES",
 ]

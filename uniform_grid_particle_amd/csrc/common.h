@@ -88,6 +88,50 @@ __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x) {
   return x;
 }
 
+// Inclusive maximum across the 64 lanes of a wave (same DPP moves as
+// wave_inclusive_sum; lanes without a source take 0, the identity for the
+// unsigned values it is used on).
+__device__ __forceinline__ uint32_t wave_inclusive_max(uint32_t x) {
+  constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+  constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+  uint32_t y;
+  y = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), kRowShr1, 0xf, 0xf, false));
+  x = (y > x) ? y : x;
+  y = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), kRowShr2, 0xf, 0xf, false));
+  x = (y > x) ? y : x;
+  y = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), kRowShr4, 0xf, 0xf, false));
+  x = (y > x) ? y : x;
+  y = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), kRowShr8, 0xf, 0xf, false));
+  x = (y > x) ? y : x;
+  y = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), kRowBcast15, 0xa, 0xf, false));
+  x = (y > x) ? y : x;
+  y = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), kRowBcast31, 0xc, 0xf, false));
+  x = (y > x) ? y : x;
+  return x;
+}
+
+// Exclusive maximum of one value per thread across a workgroup of NT
+// threads (0 for thread 0). s_wave: NT/64 words of LDS; two barriers.
+template <int NT>
+__device__ __forceinline__ uint32_t block_exclusive_max(uint32_t x, uint32_t* s_wave) {
+  constexpr int kWaves = NT / 64;
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const uint32_t incl = wave_inclusive_max(x);
+  if (lane == 63) s_wave[wid] = incl;
+  const uint32_t up = static_cast<uint32_t>(__shfl_up(static_cast<int>(incl), 1, 64));
+  __syncthreads();
+  uint32_t before = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const uint32_t v = s_wave[w];
+    before = (w < wid && v > before) ? v : before;
+  }
+  __syncthreads();
+  const uint32_t in_wave = (lane > 0) ? up : 0u;
+  return (in_wave > before) ? in_wave : before;
+}
+
 // Exclusive scan of one value per thread across a workgroup of NT threads.
 // Returns the exclusive prefix; *total receives the workgroup sum.
 // s_wave: NT/64 words of LDS. Contains two barriers; every thread of the

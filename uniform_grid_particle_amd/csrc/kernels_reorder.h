@@ -35,6 +35,71 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(const uint32_t* __restri
     if (ok[j]) dst[static_cast<size_t>(r[j]) * 2u + half] = v[j];
 }
 
+// Gather of several arrays with one index (page "Reordenar por celda y la
+// coalescencia de memoria", section "El kernel de reordenación": a state
+// split over several buffers is reordered in one kernel that reads each
+// ordenado[k] once for all of them). Every element of every array is cut
+// into chunks of sizeof(T) bytes (16 when every size and pointer allows,
+// else 4); the W chunks of one destination element k, all arrays in turn,
+// go to W consecutive threads, so a store instruction covers contiguous
+// spans and ordenado[k] is read by those W threads together (one line).
+// A workgroup handles kArrayItems groups of E = kBlock / W elements, the
+// loads of all groups in flight before the first store. Indices >= n_src
+// are skipped.
+constexpr uint32_t kMaxArrays = 8;
+constexpr int kArrayItems = 8;
+
+struct ArraySet {
+  const void* src[kMaxArrays];
+  void* dst[kMaxArrays];
+  uint32_t chunks[kMaxArrays];     // chunks per element of array q
+  uint32_t first[kMaxArrays + 1];  // first[q]: chunk of array q within an element's W chunks
+  uint32_t count;                  // arrays
+};
+
+template <typename T>
+__global__ __launch_bounds__(kBlock) void gather_arrays_kernel(const uint32_t* __restrict__ idx,
+                                                               uint32_t n, uint32_t n_src,
+                                                               ArraySet a) {
+  const uint32_t w_all = a.first[a.count];  // chunks per element, 1..kBlock
+  const uint32_t per = kBlock / w_all;       // elements per group
+  const uint32_t e = threadIdx.x / w_all, c = threadIdx.x - e * w_all;
+  if (e >= per) return;  // no barrier below: idle lanes may leave
+  uint32_t q = 0;
+  while (q + 1 < a.count && a.first[q + 1] <= c) ++q;
+  const uint32_t local = c - a.first[q], chunks = a.chunks[q];
+  const T* src = static_cast<const T*>(a.src[q]);
+  T* dst = static_cast<T*>(a.dst[q]);
+  // register arrays as scalars (an array of 16-byte vectors is placed in
+  // scratch memory by the compiler)
+  uint32_t v0[kArrayItems], v1[kArrayItems], v2[kArrayItems], v3[kArrayItems];
+  uint32_t k[kArrayItems];
+  bool ok[kArrayItems];
+#pragma unroll
+  for (int j = 0; j < kArrayItems; ++j) {
+    const uint64_t kk = (static_cast<uint64_t>(blockIdx.x) * kArrayItems + j) * per + e;
+    k[j] = (kk < n) ? static_cast<uint32_t>(kk) : n - 1u;
+    const uint32_t s = idx[k[j]];
+    ok[j] = (kk < n) && (s < n_src);
+    const T x = src[static_cast<size_t>(s < n_src ? s : n_src - 1u) * chunks + local];  // clamped, unconditional
+    if constexpr (sizeof(T) == 16) {
+      v0[j] = x.x; v1[j] = x.y; v2[j] = x.z; v3[j] = x.w;
+    } else {
+      v0[j] = x;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kArrayItems; ++j) {
+    if (!ok[j]) continue;
+    T* d = dst + static_cast<size_t>(k[j]) * chunks + local;
+    if constexpr (sizeof(T) == 16) {
+      *d = make_uint4(v0[j], v1[j], v2[j], v3[j]);
+    } else {
+      *d = v0[j];
+    }
+  }
+}
+
 // Stable mode, short cells: one thread per cell. Cells of at most 16
 // entries are sorted in registers with a bitonic network (static indices,
 // padding with 0xFFFFFFFF which no particle index reaches); longer cells

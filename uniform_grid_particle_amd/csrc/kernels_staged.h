@@ -47,6 +47,7 @@ constexpr int kChunkItems = 8;                      // particles per chunk_sort 
 constexpr uint32_t kStagedMaxTiles = 512;
 constexpr uint32_t kStagedMaxChunks = 1024;
 constexpr int kStagedRegs = 8;                      // particles per tile_sort thread in registers
+constexpr uint32_t kShortRun = 64;                  // longest chunk run a thread expands by itself
 
 // Geometry the host uses (chosen by measurement on MI355X, 1M particles on
 // 128^3 cells: runs of 8+ records per chunk and tile keep tile_sort's loads
@@ -109,13 +110,11 @@ __global__ __launch_bounds__(CT) void staged_keys_kernel(
 #pragma unroll
   for (int j = 0; j < kChunkItems; ++j) {
     const uint32_t i = base + j * kChunkThreads + threadIdx.x;
-    cellv[j] = 0xFFFFFFFFu;
-    rank[j] = 0u;
-    if (i < n) {
-      cellv[j] = cell_of(__uint_as_float(w[0][j]), __uint_as_float(w[1][j]),
-                         __uint_as_float(w[2][j]), g);
-      rank[j] = atomicAdd(&s_hist[cellv[j] >> tile_shift], 1u);
-    }
+    const bool act = i < n;
+    const uint32_t c = cell_of(__uint_as_float(w[0][j]), __uint_as_float(w[1][j]),
+                               __uint_as_float(w[2][j]), g);
+    cellv[j] = act ? c : 0xFFFFFFFFu;
+    rank[j] = act ? atomicAdd(&s_hist[c >> tile_shift], 1u) : 0u;
   }
   __syncthreads();
   // exclusive scan of the tile histogram: kTilesPerThread consecutive bins per thread
@@ -194,6 +193,7 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
   __shared__ uint4 s_rec[2 * kStagedWin];
   __shared__ uint32_t s_idx[kStagedWin];
   __shared__ uint32_t s_wave[NT / 64];
+  __shared__ uint32_t s_runmax[NT / 64];
   __shared__ uint32_t s_dm[DIAG ? NT / 64 : 1], s_do[DIAG ? NT / 64 : 1];
 
   const uint32_t t = tile_of_block(blockIdx.x, ntiles);
@@ -212,8 +212,18 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
     pre_sum += r[q].y;
   }
   uint32_t count;
+  // the longest chunk run of the tile (it picks how the source map is built)
+  uint32_t my_run = 0;
+#pragma unroll
+  for (uint32_t q = 0; q < kChunksPerThread; ++q) my_run = (r[q].x > my_run) ? r[q].x : my_run;
+  my_run = wave_inclusive_max(my_run);
+  if ((threadIdx.x & 63) == 63) s_runmax[threadIdx.x >> 6] = my_run;  // visible after the next barrier
   uint32_t run_dst = block_exclusive_sum<NT>(len_sum, s_wave, &count);
   const uint32_t bs = block_sum<NT>(pre_sum, s_wave);
+  uint32_t longest_run = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) longest_run = (s_runmax[w] > longest_run) ? s_runmax[w] : longest_run;
+  const bool short_runs = longest_run <= kShortRun;
 #pragma unroll
   for (uint32_t q = 0; q < kChunksPerThread; ++q) {
     const uint32_t c = threadIdx.x * kChunksPerThread + q;
@@ -227,13 +237,22 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
   __syncthreads();
 
   // source map of a window of the tile: s_map[q] = chunk-array position of
-  // tile-local particle base + q, for q < len (s_map aliases the staging
-  // buffer, which holds kStagedCap words). Callers put barriers around it.
+  // tile-local particle base + q, for q < len <= kStagedCap (s_map aliases the
+  // staging buffer). Runs are laid out in chunk order, so the chunk of a
+  // position is the last chunk whose run starts at or before it: every run
+  // start (or, for the run covering `base`, position 0) is marked with its
+  // chunk number plus one, and an inclusive maximum scan over the window
+  // spreads it, whatever the run lengths (a few long runs, as from nearly
+  // sorted input). When every run is short (shuffled input) each thread
+  // simply expands its own chunk's run instead. The scan contains barriers
+  // (the tile-uniform choice keeps them uniform); callers put one before
+  // build_map (the previous reads of s_map are done) and one after.
   uint32_t* s_map = reinterpret_cast<uint32_t*>(s_rec);
+  constexpr uint32_t kMapPer = kStagedCap / NT;  // window entries per thread
   auto build_map = [&](uint32_t base, uint32_t len) {
     const uint32_t end = base + len;
-    if (nchunks >= NT / 16) {
-      // many chunks, short runs: each thread expands the runs of its chunks
+    if (short_runs) {
+      // every run short: each thread expands the runs of its own chunks
 #pragma unroll
       for (uint32_t q = 0; q < kChunksPerThread; ++q) {
         const uint32_t c = threadIdx.x * kChunksPerThread + q;
@@ -243,14 +262,34 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
           for (uint32_t k = lo; k < hi; ++k) s_map[k - base] = s_src[c] + (k - d0);
         }
       }
-    } else {
-      // few chunks, long runs: one wave per run, its lanes striding the run
-      const uint32_t lane = threadIdx.x & 63u;
-      for (uint32_t c = threadIdx.x >> 6; c < nchunks; c += NT / 64) {
-        const uint32_t d0 = s_dst[c], d1 = (c + 1 < nchunks) ? s_dst[c + 1] : count;
-        const uint32_t lo = (d0 > base) ? d0 : base, hi = (d1 < end) ? d1 : end;
-        for (uint32_t k = lo + lane; k < hi; k += 64) s_map[k - base] = s_src[c] + (k - d0);
+      return;
+    }
+    const uint32_t m0 = threadIdx.x * kMapPer;
+#pragma unroll
+    for (uint32_t q = 0; q < kMapPer; ++q) s_map[m0 + q] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (uint32_t q = 0; q < kChunksPerThread; ++q) {
+      const uint32_t c = threadIdx.x * kChunksPerThread + q;
+      if (c < nchunks && r[q].x > 0u) {
+        const uint32_t d0 = s_dst[c], d1 = d0 + r[q].x;
+        if (d0 < end && d1 > base) s_map[(d0 > base) ? d0 - base : 0u] = c + 1u;
       }
+    }
+    __syncthreads();
+    uint32_t mark[kMapPer];
+    uint32_t run = 0;
+#pragma unroll
+    for (uint32_t q = 0; q < kMapPer; ++q) {
+      mark[q] = s_map[m0 + q];
+      run = (mark[q] > run) ? mark[q] : run;
+    }
+    uint32_t cur = block_exclusive_max<NT>(run, s_wave);
+#pragma unroll
+    for (uint32_t q = 0; q < kMapPer; ++q) {
+      cur = (mark[q] > cur) ? mark[q] : cur;
+      const uint32_t pos = base + m0 + q;
+      if (m0 + q < len && cur > 0u) s_map[m0 + q] = s_src[cur - 1u] + (pos - s_dst[cur - 1u]);
     }
   };
 
@@ -333,7 +372,7 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
     uint32_t w[8][kStagedRegs], idx[kStagedRegs], lr[kStagedRegs];
 #pragma unroll
     for (int k = 0; k < kStagedRegs; ++k) lr[k] = 0xFFFFFFFFu;
-    build_map(0u, count);
+    build_map(0u, count);  // s_dst, s_src: visible since the barrier above
     __syncthreads();
     if (count > 0) {  // count == 0: no valid source to clamp the idle lanes to
       uint32_t src[kStagedRegs];
@@ -355,11 +394,9 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
 #pragma unroll
       for (int k = 0; k < kStagedRegs; ++k) {
         const uint32_t p = threadIdx.x + k * NT;
-        if (p < count) {
-          const uint32_t loc = cell_of(__uint_as_float(w[0][k]), __uint_as_float(w[1][k]),
-                                       __uint_as_float(w[2][k]), g) - cell0;
-          if (loc < tc) lr[k] = (loc << 16) | atomicAdd(&s_cnt[loc], 1u);
-        }
+        const uint32_t loc = cell_of(__uint_as_float(w[0][k]), __uint_as_float(w[1][k]),
+                                     __uint_as_float(w[2][k]), g) - cell0;
+        if (p < count && loc < tc) lr[k] = (loc << 16) | atomicAdd(&s_cnt[loc], 1u);
       }
     }
     __syncthreads();
@@ -421,10 +458,8 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
 #pragma unroll
       for (int k = 0; k < kStagedRegs; ++k) {
         const uint32_t p = base + threadIdx.x + k * NT;
-        if (p < count) {
-          const uint32_t loc = cell_of(px[k], py[k], pz[k], g) - cell0;
-          if (loc < tc) atomicAdd(&s_cnt[loc], 1u);
-        }
+        const uint32_t loc = cell_of(px[k], py[k], pz[k], g) - cell0;
+        if (p < count && loc < tc) atomicAdd(&s_cnt[loc], 1u);
       }
     }
     __syncthreads();
@@ -457,18 +492,15 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
 #pragma unroll
       for (int k = 0; k < kOver; ++k) {
         const uint32_t p = base + threadIdx.x + k * NT;
-        if (p < count) {
-          const uint32_t loc = cell_of(__uint_as_float(v[0][k]), __uint_as_float(v[1][k]),
-                                       __uint_as_float(v[2][k]), g) - cell0;
-          if (loc < tc) {
-            const size_t out = static_cast<size_t>(bs) + atomicAdd(&s_cnt[loc], 1u);
-            if (out < n) {
-              ordenado[out] = id[k];
-              if (MOVE) {
-                dst[out * 2u] = make_uint4(v[0][k], v[1][k], v[2][k], v[3][k]);
-                dst[out * 2u + 1u] = make_uint4(v[4][k], v[5][k], v[6][k], v[7][k]);
-              }
-            }
+        const uint32_t loc = cell_of(__uint_as_float(v[0][k]), __uint_as_float(v[1][k]),
+                                     __uint_as_float(v[2][k]), g) - cell0;
+        if (!(p < count && loc < tc)) continue;
+        const size_t out = static_cast<size_t>(bs) + atomicAdd(&s_cnt[loc], 1u);
+        if (out < n) {
+          ordenado[out] = id[k];
+          if (MOVE) {
+            dst[out * 2u] = make_uint4(v[0][k], v[1][k], v[2][k], v[3][k]);
+            dst[out * 2u + 1u] = make_uint4(v[4][k], v[5][k], v[6][k], v[7][k]);
           }
         }
       }

@@ -66,6 +66,7 @@ struct Plan {
   uint64_t cells = 0;
   bool stable = false;
   bool gather = false;  // a separate gather kernel moves the records
+  bool move = true;     // the scatter kernel itself moves the records
   // tiled
   uint32_t tile_shift = kTileShiftMin, ntiles = 1, items = kBatch, nblk = 0;
   size_t off_hist = 0, off_tile_total = 0, off_bucket = 0;
@@ -83,7 +84,8 @@ struct Plan {
 
 int make_plan(uint32_t n, const uint32_t dims[3], uint32_t flags, Plan* p) {
   if (!dims) return UGP_ERR_NULL;
-  if (flags & ~(UGP_FLAG_STABLE | UGP_FLAG_GATHER | UGP_FLAG_MORTON)) return UGP_ERR_ARG;
+  if (flags & ~(UGP_FLAG_STABLE | UGP_FLAG_GATHER | UGP_FLAG_MORTON | UGP_FLAG_INDEX_ONLY))
+    return UGP_ERR_ARG;
   for (int a = 0; a < 3; ++a)
     if (dims[a] < 1u || dims[a] > kMaxDim) return UGP_ERR_RANGE;
   uint64_t cells = static_cast<uint64_t>(dims[0]) * dims[1] * dims[2];
@@ -99,7 +101,9 @@ int make_plan(uint32_t n, const uint32_t dims[3], uint32_t flags, Plan* p) {
   *p = Plan{};
   p->cells = cells;
   p->stable = (flags & UGP_FLAG_STABLE) != 0;
-  p->gather = p->stable || (flags & UGP_FLAG_GATHER) != 0;
+  const bool index_only = (flags & UGP_FLAG_INDEX_ONLY) != 0;
+  p->gather = !index_only && (p->stable || (flags & UGP_FLAG_GATHER) != 0);
+  p->move = !index_only && !p->gather;
   const uint32_t lg = ceil_log2_u64(cells);
   size_t off = 0;
   if (n == 0) {
@@ -226,10 +230,12 @@ int validate(const BuildArgs& a, Plan* plan) {
   for (int k = 0; k < 3; ++k)
     if (!std::isfinite(a.origin[k])) return UGP_ERR_ARG;
   if (!a.conteos || !a.inicios || !a.workspace) return UGP_ERR_NULL;
-  if (a.n > 0 && (!a.particles || !a.celdaDe || !a.ordenado || !a.reordered)) return UGP_ERR_NULL;
+  const bool writes_records = (a.flags & UGP_FLAG_INDEX_ONLY) == 0;
+  if (a.n > 0 && (!a.particles || !a.celdaDe || !a.ordenado || (writes_records && !a.reordered)))
+    return UGP_ERR_NULL;
   if (!aligned(a.conteos, 16) || !aligned(a.inicios, 16) || !aligned(a.workspace, 256))
     return UGP_ERR_ALIGN;
-  if (a.n > 0 && (!aligned(a.particles, 16) || !aligned(a.reordered, 16) ||
+  if (a.n > 0 && (!aligned(a.particles, 16) || (writes_records && !aligned(a.reordered, 16)) ||
                   !aligned(a.celdaDe, 16) || !aligned(a.ordenado, 16)))
     return UGP_ERR_ALIGN;
   if (a.diag && !aligned(a.diag, 4)) return UGP_ERR_ALIGN;
@@ -238,7 +244,8 @@ int validate(const BuildArgs& a, Plan* plan) {
   const size_t c = plan->cells;
   const Span spans[8] = {
       span_of(a.particles, 32 * n),    span_of(a.celdaDe, 4 * n),   span_of(a.conteos, 4 * c),
-      span_of(a.inicios, 4 * (c + 1)), span_of(a.ordenado, 4 * n), span_of(a.reordered, 32 * n),
+      span_of(a.inicios, 4 * (c + 1)), span_of(a.ordenado, 4 * n),
+      span_of(a.reordered, writes_records ? 32 * n : 0),
       span_of(a.workspace, plan->total), span_of(a.diag, a.diag ? 8 : 0),
   };
   for (int i = 0; i < 8; ++i)
@@ -381,13 +388,13 @@ void enqueue_staged(uint32_t stage, const BuildArgs& a, const Plan& p) {
                          a.celdaDe, rows, p.tile_shift, p.ntiles, chunk_rec, chunk_idx, a.diag);
       break;
     case 3: {
-      uint4* dst = p.gather ? nullptr : reinterpret_cast<uint4*>(a.reordered);
+      uint4* dst = p.move ? reinterpret_cast<uint4*>(a.reordered) : nullptr;
       const dim3 grid(p.ntiles);
-      if (p.gather && a.diag)
+      if (!p.move && a.diag)
         launch_staged_cells<false, true>(p.tile_shift, grid, s, rows, p.nchunks, p.ntiles,
                                          grid_params(a), cells, a.n, chunk_rec, chunk_idx,
                                          a.conteos, a.inicios, a.ordenado, dst, a.capacity, a.diag);
-      else if (p.gather)
+      else if (!p.move)
         launch_staged_cells<false, false>(p.tile_shift, grid, s, rows, p.nchunks, p.ntiles,
                                           grid_params(a), cells, a.n, chunk_rec, chunk_idx,
                                           a.conteos, a.inicios, a.ordenado, dst, 0u, nullptr);
@@ -434,7 +441,7 @@ void enqueue_tiled(uint32_t stage, const BuildArgs& a, const Plan& p) {
                          hist, tile_total, p.tile_shift, p.ntiles, p.items, bucket);
       break;
     case 3:
-      if (p.gather)
+      if (!p.move)
         launch_tiled_cells<false>(p.tile_shift, dim3(p.ntiles), s, bucket, tile_total, p.ntiles,
                                   cells, a.n, a.conteos, a.inicios, a.ordenado, nullptr, nullptr);
       else
@@ -476,7 +483,7 @@ void enqueue_direct(uint32_t stage, const BuildArgs& a, const Plan& p) {
                          tilesum, p.bin_shift, a.inicios, cursor);
       break;
     case 3:
-      if (p.gather)
+      if (!p.move)
         hipLaunchKernelGGL(scatter_kernel<false>, pgrid, dim3(kBlock), 0, s, a.celdaDe, a.n, cells,
                            cursor, a.ordenado, nullptr, nullptr);
       else
@@ -742,6 +749,57 @@ int ugp_exclusive_scan_u32(const uint32_t* in, uint32_t count, uint32_t* out, vo
                      static_cast<uint64_t>(count), shift, tilesum);
   hipLaunchKernelGGL(scan_kernel, dim3(nbins), dim3(kBlock), 0, s, in, static_cast<uint64_t>(count),
                      tilesum, shift, out, nullptr);
+  return hipGetLastError() == hipSuccess ? UGP_OK : UGP_ERR_HIP;
+}
+
+int ugp_reorder_arrays(const uint32_t* idx, uint32_t n, uint32_t n_src, const ugp_array_desc* arrays,
+                       uint32_t count, void* stream) {
+  if (count == 0 || count > kMaxArrays) return UGP_ERR_ARG;
+  if (!arrays) return UGP_ERR_NULL;
+  uint32_t bytes = 0;
+  bool vec16 = true;
+  for (uint32_t q = 0; q < count; ++q) {
+    const ugp_array_desc& d = arrays[q];
+    if (d.elem_bytes == 0 || d.elem_bytes % 4 != 0) return UGP_ERR_ARG;
+    bytes += d.elem_bytes;
+    if (n > 0 && (!d.src || !d.dst)) return UGP_ERR_NULL;
+    if (!aligned(d.src, 4) || !aligned(d.dst, 4)) return UGP_ERR_ALIGN;
+    vec16 = vec16 && d.elem_bytes % 16 == 0 && aligned(d.src, 16) && aligned(d.dst, 16);
+  }
+  const uint32_t chunk = vec16 ? 16u : 4u;
+  if (bytes / chunk > static_cast<uint32_t>(kBlock)) return UGP_ERR_ARG;  // one element's chunks fit a workgroup
+  if (n == 0) return UGP_OK;
+  if (!idx) return UGP_ERR_NULL;
+  if (!aligned(idx, 4)) return UGP_ERR_ALIGN;
+  // no destination may overlap the index, a source, or another destination
+  const Span si = span_of(idx, 4ull * n);
+  for (uint32_t q = 0; q < count; ++q) {
+    const Span dq = span_of(arrays[q].dst, static_cast<size_t>(arrays[q].elem_bytes) * n);
+    if (overlap(dq, si)) return UGP_ERR_ALIAS;
+    for (uint32_t r = 0; r < count; ++r) {
+      if (overlap(dq, span_of(arrays[r].src, static_cast<size_t>(arrays[r].elem_bytes) * n_src)))
+        return UGP_ERR_ALIAS;
+      if (r != q && overlap(dq, span_of(arrays[r].dst, static_cast<size_t>(arrays[r].elem_bytes) * n)))
+        return UGP_ERR_ALIAS;
+    }
+  }
+  if (n_src == 0) return UGP_OK;  // every index is out of range: nothing to write
+  ArraySet set{};
+  set.count = count;
+  set.first[0] = 0;
+  for (uint32_t q = 0; q < count; ++q) {
+    set.src[q] = arrays[q].src;
+    set.dst[q] = arrays[q].dst;
+    set.chunks[q] = arrays[q].elem_bytes / chunk;
+    set.first[q + 1] = set.first[q] + set.chunks[q];
+  }
+  const uint32_t per = kBlock / set.first[count];
+  const dim3 grid(blocks_for(n, static_cast<uint64_t>(per) * kArrayItems));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (vec16)
+    hipLaunchKernelGGL(gather_arrays_kernel<uint4>, grid, dim3(kBlock), 0, s, idx, n, n_src, set);
+  else
+    hipLaunchKernelGGL(gather_arrays_kernel<uint32_t>, grid, dim3(kBlock), 0, s, idx, n, n_src, set);
   return hipGetLastError() == hipSuccess ? UGP_OK : UGP_ERR_HIP;
 }
 
