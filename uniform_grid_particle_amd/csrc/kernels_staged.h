@@ -398,9 +398,14 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
                                      __uint_as_float(w[2][k]), g) - cell0;
         if (p < count && loc < tc) lr[k] = (loc << 16) | atomicAdd(&s_cnt[loc], 1u);
       }
+      // every record load of this thread has landed: the compiler then needs
+      // no wait before using those registers after the stores below (one
+      // counter tracks loads and stores alike)
+      __builtin_amdgcn_s_waitcnt(kWaitLoadsAndStores);
     }
     __syncthreads();
     const uint32_t tot = scan_tile();
+    write_counts_starts(tot);  // overlaps the placement below
     uint32_t slot[kStagedRegs];
 #pragma unroll
     for (int k = 0; k < kStagedRegs; ++k)
@@ -428,9 +433,6 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
       }
       __syncthreads();
     }
-    // last: a later wait for a register loaded before a store would also
-    // wait for that store (one counter tracks loads and stores)
-    write_counts_starts(tot);
   } else {
     // a tile past the staged capacity (count > kStagedCap > 0): rounds of
     // kStagedCap particles (kStagedRegs per thread), each with the source
