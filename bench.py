@@ -52,9 +52,9 @@ WORKLOAD_NAMES = {
 
 def alg_bytes(n: int, c: int, mode: str) -> dict:
     """Bytes each kernel must move by design, each logical array counted once
-    per kernel that touches it (32 B per record, 4 B per u32, 8 B per
-    (cell, index) pair). The small per-block tile matrix of the tiled path
-    is left out; tile_scan moves only that matrix and gets no figure.
+    per kernel that touches it (32 B per record, 4 B per u32). The small
+    block x tile matrix of the bucketed path is left out; tile_scan moves
+    only that matrix and gets no figure.
 
     The end-to-end figure uses the fixed model of the four page steps
     instead: 116 N + 16 C + 4 (see hbm_frac_e2e)."""
@@ -63,11 +63,10 @@ def alg_bytes(n: int, c: int, mode: str) -> dict:
         # staged path (cells <= 2^22, n <= 2^21)
         "chunk_sort": 72 * n,  # record read, celdaDe, chunk records + indices written
         "tile_sort": (36 * n + 4 * c + 4 * (c + 1) + 4 * n + (32 * n if move else 0)),
-        # tiled path (cells <= 2^24)
+        # bucketed path (more particles or keys; tile_sort as above)
         "keys": 36 * n,  # record read + celdaDe write
         "tile_scan": None,
-        "bucket": 12 * n,  # celdaDe read + pair write
-        "cells": (8 * n + 4 * c + 4 * (c + 1) + 4 * n + (64 * n if move else 0)),
+        "bucket": 72 * n,  # record + celdaDe read, record + index written in tile order
         # direct path (larger grids)
         "clear": 4 * c,
         "count": 36 * n,
@@ -209,8 +208,8 @@ def summarize_counters(fetch_csv: str, write_csv: str, copy_bytes: int = 256 << 
 # kernel symbol -> stage name, for the traffic file
 KERNEL_STAGE = {
     "staged_keys_kernel": "chunk_sort", "staged_cells_kernel": "tile_sort",
-    "tiled_keys_kernel": "keys", "tiled_colscan_kernel": "tile_scan", "tiled_bucket_kernel": "bucket",
-    "tiled_cells_kernel": "cells", "clear_kernel": "clear", "count_kernel": "count", "scan_kernel": "scan",
+    "bucket_keys_kernel": "keys", "bucket_colscan_kernel": "tile_scan", "bucket_records_kernel": "bucket",
+    "clear_kernel": "clear", "count_kernel": "count", "scan_kernel": "scan",
     "scatter_kernel": "scatter", "gather_kernel": "gather",
 }
 

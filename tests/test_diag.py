@@ -66,7 +66,7 @@ def test_diag_configs(ugp, orc, name):
 
 
 def test_diag_large_tiled_path(ugp, orc):
-    """16,777,216 particles on 256^3: the tiled path reduces conteos afterwards."""
+    """16,777,216 particles on 256^3: the bucketed path (diagnostics folded into its tile kernel)."""
     print("[diag] large", flush=True)
     wl = W.make_config("large")
     assert ugp.stage_names(wl.n, wl.dims.tolist())[0] == "keys"
@@ -77,13 +77,13 @@ def test_diag_large_tiled_path(ugp, orc):
 
 
 def test_diag_direct_path(ugp, orc):
-    """More than 2^24 cells (global-atomic path) with one dense cell."""
-    dims = (4096, 4097, 1)
+    """More than 2^26 cells (global-atomic path) with one dense cell."""
+    dims = (8192, 8193, 1)
     n = 100_003
     rng = np.random.Generator(np.random.PCG64(77))
     parts = rng.standard_normal((n, 8)).astype(np.float32)
-    parts[:, 0] = (rng.random(n) * 4096).astype(np.float32)
-    parts[:, 1] = (rng.random(n) * 4097).astype(np.float32)
+    parts[:, 0] = (rng.random(n) * 8192).astype(np.float32)
+    parts[:, 1] = (rng.random(n) * 8193).astype(np.float32)
     parts[:, 2] = 0.5
     parts[: n // 7, :3] = parts[0, :3]
     wl = W.Workload("direct", parts, np.zeros(3, np.float32), np.float32(1.0), np.asarray(dims, np.uint32))

@@ -157,14 +157,47 @@ def test_dense_grids(ugp, orc, d):
         assert_parity(wl, run_gpu(ugp, wl, mode), ref, mode)
 
 
-def test_direct_path_beyond_tiled_limit(ugp, orc):
-    """More than 2^24 cells: the global-atomic path."""
-    dims = (4096, 4097, 1)
+@pytest.mark.parametrize("n,dims", [
+    ((1 << 21) + 1, (128, 128, 128)),   # just past the staged path's particle limit
+    (3_000_003, (64, 64, 64)),          # dense: ~11 per cell, tiles shrink
+    (2_500_000, (160, 150, 140)),       # non-cubic, ragged last tile
+    (5_000, (512, 512, 64)),            # sparse: 2^24 cells, 1024 tiles of 16384 cells
+    (1_000, (1024, 1024, 64)),          # 2^26 keys, the largest the path takes
+])
+def test_bucketed_path_shapes(ugp, orc, n, dims):
+    """More particles than the staged path takes, or more cells: keys,
+    tile_scan, bucket, tile_sort."""
+    print(f"[parity] bucketed n={n} dims={dims}", flush=True)
+    assert ugp.stage_names(n, dims)[:4] == ["keys", "tile_scan", "bucket", "tile_sort"]
+    rng = np.random.Generator(np.random.PCG64(n))
+    parts = rng.standard_normal((n, 8)).astype(np.float32)
+    ext = np.asarray(dims, np.float64) * 0.5
+    parts[:, :3] = (rng.random((n, 3)) * ext * 1.02 - 0.01 * ext).astype(np.float32)
+    wl = W.Workload("bucketed", parts, np.zeros(3, np.float32), np.float32(0.5), np.asarray(dims, np.uint32))
+    ref = orc.grid_build(wl.particles, wl.origin, wl.cell_size, wl.dims)
+    for mode in (MODES if n < 3_000_000 else ("atomic", "stable")):
+        assert_parity(wl, run_gpu(ugp, wl, mode), ref, mode)
+
+
+def test_bucketed_one_cell_holds_everything(ugp, orc):
+    """2.5M particles in one cell: one tile far past the staged capacity,
+    taken in rounds by one workgroup."""
+    n = 2_500_000
+    parts = np.random.Generator(np.random.PCG64(77)).standard_normal((n, 8)).astype(np.float32)
+    wl = W.Workload("one_cell", parts, np.zeros(3, np.float32), np.float32(1.0), np.array([1, 1, 1], np.uint32))
+    assert ugp.stage_names(n, [1, 1, 1])[0] == "keys"
+    ref = orc.grid_build(wl.particles, wl.origin, wl.cell_size, wl.dims)
+    assert_parity(wl, run_gpu(ugp, wl, "atomic"), ref, "atomic")
+
+
+def test_direct_path_beyond_bucketed_limit(ugp, orc):
+    """More than 2^26 cells: the global-atomic path."""
+    dims = (8192, 8193, 1)
     assert ugp.stage_names(n := 200_003, dims)[:4] == ["clear", "count", "scan", "scatter"]
     rng = np.random.Generator(np.random.PCG64(99))
     parts = rng.standard_normal((n, 8)).astype(np.float32)
-    parts[:, 0] = (rng.random(n) * 4096 * 1.01 - 10).astype(np.float32)
-    parts[:, 1] = (rng.random(n) * 4097 * 1.01 - 10).astype(np.float32)
+    parts[:, 0] = (rng.random(n) * 8192 * 1.01 - 10).astype(np.float32)
+    parts[:, 1] = (rng.random(n) * 8193 * 1.01 - 10).astype(np.float32)
     parts[:, 2] = (rng.random(n) * 2 - 0.5).astype(np.float32)
     parts[: n // 10, :3] = parts[0, :3]  # one dense cell
     wl = W.Workload("direct", parts, np.zeros(3, np.float32), np.float32(1.0), np.asarray(dims, np.uint32))

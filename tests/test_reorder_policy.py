@@ -134,11 +134,11 @@ def test_index_only_build(ugp, orc, name, flags):
 
 
 def test_index_only_other_paths(ugp, orc):
-    """Tiled path (3M particles on 256^3) and global-atomic path (> 2^24 cells)."""
+    """Bucketed path (3M particles on 256^3) and global-atomic path (> 2^26 cells)."""
     dev = torch.device(DEV)
     for wl in (W.make_uniform(3_000_000, 256, seed=61),
                W.Workload("direct", np.random.Generator(np.random.PCG64(3)).random((50_000, 8)).astype(np.float32) * 4000,
-                          np.zeros(3, np.float32), np.float32(1.0), np.array([4096, 4097, 1], np.uint32))):
+                          np.zeros(3, np.float32), np.float32(1.0), np.array([8192, 8193, 1], np.uint32))):
         r = ugp.grid_build(torch.from_numpy(wl.particles).to(dev), wl.origin.tolist(), float(wl.cell_size),
                            wl.dims.tolist(), index_only=True)
         torch.cuda.synchronize()

@@ -168,7 +168,7 @@ __global__ __launch_bounds__(CT) void staged_keys_kernel(
 // MOVE: also write the records (otherwise a separate gather follows).
 // DIAG: also fold the tile's histogram into the overflow diagnostics
 // (diag[0] max occupancy, diag[1] overflowing insertions over capacity cap;
-// both zeroed by chunk_sort).
+// both zeroed by the kernel before this one).
 template <bool MOVE, bool DIAG, uint32_t SHIFT, int NT, uint32_t WIN>
 __global__ __launch_bounds__(NT) void staged_cells_kernel(
     const uint2* __restrict__ rows, uint32_t nchunks, uint32_t chunk, uint32_t ntiles, GridParams g,
@@ -251,6 +251,11 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
   constexpr uint32_t kMapPer = kStagedCap / NT;  // window entries per thread
   auto build_map = [&](uint32_t base, uint32_t len) {
     const uint32_t end = base + len;
+    if (nchunks == 1u) {
+      // one run (a tile stored contiguously): the source is its start plus p
+      for (uint32_t q = threadIdx.x; q < len; q += NT) s_map[q] = s_src[0] + (base + q);
+      return;
+    }
     if (short_runs) {
       // every run short: each thread expands the runs of its own chunks
 #pragma unroll

@@ -14,8 +14,9 @@
 //   empty   n == 0: conteos and inicios are zeroed.
 //   staged  cells <= 2^22 and n <= 2^21: the two-kernel, atomic-free
 //           counting sort of kernels_staged.h (keys, cells).
-//   tiled   other grids up to 2^24 cells: the four-kernel atomic-free
-//           counting sort of kernels_tiled.h (keys, tile_scan, bucket, cells).
+//   bucketed  other grids up to 2^26 keys: the four-kernel atomic-free
+//           counting sort of kernels_bucket.h (keys, tile_scan, bucket) ending
+//           in the staged tile kernel (tile_sort).
 //   direct  larger grids: the global-atomic chain of kernels_direct.h
 //           (clear, count, scan, scatter).
 // Stable mode (ascending particle index inside every cell) and gather
@@ -36,18 +37,17 @@
 #include "kernels_direct.h"
 #include "kernels_reorder.h"
 #include "kernels_staged.h"
-#include "kernels_tiled.h"
+#include "kernels_bucket.h"
 #include "ugp.h"
 
 namespace {
 
 using namespace ugp;
 
-constexpr uint32_t kMaxKeyBlocks = 1024;  // rows of the tiled block x tile matrix
 constexpr uint32_t kCounterWords = 64;    // small counter block (direct path)
 constexpr uint32_t kMortonMaxBits = 10;   // Morton keys: 10 bits per axis, 2^30 keys
 
-enum class Path { kEmpty, kStaged, kTiled, kDirect };
+enum class Path { kEmpty, kStaged, kBucketed, kDirect };
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -68,8 +68,8 @@ struct Plan {
   bool gather = false;  // a separate gather kernel moves the records
   bool move = true;     // the scatter kernel itself moves the records
   // tiled
-  uint32_t tile_shift = kTileShiftMin, ntiles = 1, items = kBatch, nblk = 0;
-  size_t off_hist = 0, off_tile_total = 0, off_bucket = 0;
+  uint32_t tile_shift = kStagedMinShift, ntiles = 1, nblk = 0, per_block = 0;
+  size_t off_hist = 0, off_tile_total = 0;
   // staged
   uint32_t nchunks = 0;
   size_t off_rows = 0, off_chunk_rec = 0, off_chunk_idx = 0;
@@ -81,6 +81,20 @@ struct Plan {
   size_t off_long_count = 0, off_long = 0;
   size_t total = 256;
 };
+
+// Bucketed path tile shift: as large as 256 tiles allow but no larger than
+// keeps the mean tile at kStagedTarget particles, and at least large enough
+// for kBucketMaxTiles tiles (then tiles may exceed the staged capacity; the
+// tile kernel takes them in rounds).
+uint32_t bucket_shift(uint64_t n, uint64_t cells, uint32_t lg) {
+  uint32_t s = (lg > kStagedMinShift + 8) ? lg - 8 : kStagedMinShift;
+  uint32_t dense = 0;  // largest d with n * 2^d <= kStagedTarget * cells
+  while (dense < 40 && (n << (dense + 1)) <= kStagedTarget * cells) ++dense;
+  if (dense < s) s = dense;
+  if (s > kStagedMaxShift) s = kStagedMaxShift;  // sparse grids: more, smaller tiles
+  const uint32_t fewest = (lg > kStagedMinShift + 12) ? lg - 12 : kStagedMinShift;  // 4096 tiles
+  return (s < fewest) ? fewest : s;
+}
 
 int make_plan(uint32_t n, const uint32_t dims[3], uint32_t flags, Plan* p) {
   if (!dims) return UGP_ERR_NULL;
@@ -111,7 +125,6 @@ int make_plan(uint32_t n, const uint32_t dims[3], uint32_t flags, Plan* p) {
     p->total = 256;
     return UGP_OK;
   }
-  const uint32_t tile_shift = (lg > kTileShiftMin + 9) ? lg - 9 : kTileShiftMin;
   // staged path: tiles of 2^shift consecutive keys. As large as 256 tiles
   // allow (one round of tile_sort workgroups), but no larger than keeps the
   // mean tile at kStagedTarget particles (dense grids: more, smaller tiles),
@@ -135,21 +148,27 @@ int make_plan(uint32_t n, const uint32_t dims[3], uint32_t flags, Plan* p) {
     off = align_up(off + static_cast<size_t>(n) * 32u, 256);
     p->off_chunk_idx = off;
     off = align_up(off + static_cast<size_t>(n) * 4u, 256);
-  } else if (cells <= (static_cast<uint64_t>(kMaxTiles) << kTileShiftMax)) {
-    p->path = Path::kTiled;
-    p->tile_shift = tile_shift;
+  } else if (bucket_shift(n, cells, lg) <= kStagedMaxShift) {
+    // bucketed path: the same tile rule with up to kBucketMaxTiles tiles
+    p->path = Path::kBucketed;
+    p->tile_shift = bucket_shift(n, cells, lg);
     p->ntiles = static_cast<uint32_t>((cells + (1ull << p->tile_shift) - 1) >> p->tile_shift);
-    const uint64_t per_pass = static_cast<uint64_t>(kBlock) * kMaxKeyBlocks;
-    uint64_t items = (n + per_pass - 1) / per_pass;
-    items = (items + kBatch - 1) / kBatch * kBatch;
-    p->items = static_cast<uint32_t>(items < kBatch ? kBatch : items);
-    p->nblk = blocks_for(n, static_cast<uint64_t>(kBlock) * p->items);
+    const uint64_t step = static_cast<uint64_t>(kBucketThreads) * kBucketBatch;
+    uint64_t per = (n + kBucketBlocks - 1) / kBucketBlocks;
+    per = (per + step - 1) / step * step;
+    p->per_block = static_cast<uint32_t>(per);
+    p->nblk = blocks_for(n, per);
+    p->nchunks = 1;  // the tile kernel sees each tile as one contiguous run
     p->off_hist = off;
     off = align_up(off + static_cast<size_t>(p->nblk) * p->ntiles * 4u, 256);
     p->off_tile_total = off;
     off = align_up(off + static_cast<size_t>(p->ntiles) * 4u, 256);
-    p->off_bucket = off;
-    off = align_up(off + static_cast<size_t>(n) * 8u, 256);
+    p->off_rows = off;
+    off = align_up(off + static_cast<size_t>(p->ntiles) * 8u, 256);
+    p->off_chunk_rec = off;
+    off = align_up(off + static_cast<size_t>(n) * 32u, 256);
+    p->off_chunk_idx = off;
+    off = align_up(off + static_cast<size_t>(n) * 4u, 256);
   } else {
     p->path = Path::kDirect;
     p->bin_shift = (lg > kMinBinShift + 9) ? lg - 9 : kMinBinShift;
@@ -172,7 +191,7 @@ int make_plan(uint32_t n, const uint32_t dims[3], uint32_t flags, Plan* p) {
 }
 
 const char* stage_name(const Plan& p, uint32_t stage) {
-  static const char* const kTiled[UGP_NUM_STAGES] = {"keys", "tile_scan", "bucket", "cells",
+  static const char* const kBucket[UGP_NUM_STAGES] = {"keys", "tile_scan", "bucket", "tile_sort",
                                                      "stable_sort", "gather"};
   static const char* const kDirect[UGP_NUM_STAGES] = {"clear", "count", "scan", "scatter",
                                                       "stable_sort", "gather"};
@@ -183,7 +202,7 @@ const char* stage_name(const Plan& p, uint32_t stage) {
   if (p.path == Path::kStaged && stage < 4) return kStaged[stage];
   if (stage == 4 && !p.stable) return nullptr;
   if (stage == 5 && !p.gather) return nullptr;
-  return p.path == Path::kTiled ? kTiled[stage] : kDirect[stage];
+  return p.path == Path::kBucketed ? kBucket[stage] : kDirect[stage];
 }
 
 struct Span {
@@ -277,32 +296,6 @@ void launch_clear(uint32_t* ptr, uint64_t words, uint32_t* extra, uint32_t extra
   hipLaunchKernelGGL(clear_kernel, dim3(blocks), dim3(kBlock), 0, s, ptr, words, extra, extra_words);
 }
 
-template <bool MOVE>
-void launch_tiled_cells(uint32_t shift, dim3 grid, hipStream_t s, const uint2* bucket,
-                        const uint32_t* tile_total, uint32_t ntiles, uint32_t cells, uint32_t n,
-                        uint32_t* conteos, uint32_t* inicios, uint32_t* ordenado, const uint4* src,
-                        uint4* dst) {
-  const dim3 block(kCellsBlock);
-  switch (shift) {
-    case 12:
-      hipLaunchKernelGGL((tiled_cells_kernel<MOVE, 12>), grid, block, 0, s, bucket, tile_total,
-                         ntiles, cells, n, conteos, inicios, ordenado, src, dst);
-      break;
-    case 13:
-      hipLaunchKernelGGL((tiled_cells_kernel<MOVE, 13>), grid, block, 0, s, bucket, tile_total,
-                         ntiles, cells, n, conteos, inicios, ordenado, src, dst);
-      break;
-    case 14:
-      hipLaunchKernelGGL((tiled_cells_kernel<MOVE, 14>), grid, block, 0, s, bucket, tile_total,
-                         ntiles, cells, n, conteos, inicios, ordenado, src, dst);
-      break;
-    default:
-      hipLaunchKernelGGL((tiled_cells_kernel<MOVE, 15>), grid, block, 0, s, bucket, tile_total,
-                         ntiles, cells, n, conteos, inicios, ordenado, src, dst);
-      break;
-  }
-}
-
 template <bool MOVE, bool DIAG, uint32_t SHIFT>
 void launch_staged_cells_at(dim3 grid, hipStream_t s, const uint2* rows, uint32_t nchunks,
                             uint32_t ntiles, GridParams g, uint32_t cells, uint32_t n,
@@ -374,12 +367,38 @@ void enqueue_gather(const BuildArgs& a) {
                      reinterpret_cast<uint4*>(a.reordered));
 }
 
+// the staged tile kernel over tiles given by rows (staged: chunk rows;
+// bucketed: one contiguous run per tile), with or without records and the
+// diagnostic variant
+void launch_tile_sort(const BuildArgs& a, const Plan& p, const uint2* rows, const uint4* rec,
+                      const uint32_t* idx) {
+  const uint32_t cells = static_cast<uint32_t>(p.cells);
+  uint4* dst = p.move ? reinterpret_cast<uint4*>(a.reordered) : nullptr;
+  const dim3 grid(p.ntiles);
+  hipStream_t s = a.stream;
+  if (!p.move && a.diag)
+    launch_staged_cells<false, true>(p.tile_shift, grid, s, rows, p.nchunks, p.ntiles, grid_params(a),
+                                     cells, a.n, rec, idx, a.conteos, a.inicios, a.ordenado, dst,
+                                     a.capacity, a.diag);
+  else if (!p.move)
+    launch_staged_cells<false, false>(p.tile_shift, grid, s, rows, p.nchunks, p.ntiles, grid_params(a),
+                                      cells, a.n, rec, idx, a.conteos, a.inicios, a.ordenado, dst, 0u,
+                                      nullptr);
+  else if (a.diag)
+    launch_staged_cells<true, true>(p.tile_shift, grid, s, rows, p.nchunks, p.ntiles, grid_params(a),
+                                    cells, a.n, rec, idx, a.conteos, a.inicios, a.ordenado, dst,
+                                    a.capacity, a.diag);
+  else
+    launch_staged_cells<true, false>(p.tile_shift, grid, s, rows, p.nchunks, p.ntiles, grid_params(a),
+                                     cells, a.n, rec, idx, a.conteos, a.inicios, a.ordenado, dst, 0u,
+                                     nullptr);
+}
+
 void enqueue_staged(uint32_t stage, const BuildArgs& a, const Plan& p) {
   char* ws = static_cast<char*>(a.workspace);
   uint2* rows = reinterpret_cast<uint2*>(ws + p.off_rows);
   uint4* chunk_rec = reinterpret_cast<uint4*>(ws + p.off_chunk_rec);
   uint32_t* chunk_idx = reinterpret_cast<uint32_t*>(ws + p.off_chunk_idx);
-  const uint32_t cells = static_cast<uint32_t>(p.cells);
   hipStream_t s = a.stream;
   switch (stage) {
     case 0:
@@ -387,27 +406,9 @@ void enqueue_staged(uint32_t stage, const BuildArgs& a, const Plan& p) {
                          reinterpret_cast<const uint4*>(a.particles), a.n, grid_params(a),
                          a.celdaDe, rows, p.tile_shift, p.ntiles, chunk_rec, chunk_idx, a.diag);
       break;
-    case 3: {
-      uint4* dst = p.move ? reinterpret_cast<uint4*>(a.reordered) : nullptr;
-      const dim3 grid(p.ntiles);
-      if (!p.move && a.diag)
-        launch_staged_cells<false, true>(p.tile_shift, grid, s, rows, p.nchunks, p.ntiles,
-                                         grid_params(a), cells, a.n, chunk_rec, chunk_idx,
-                                         a.conteos, a.inicios, a.ordenado, dst, a.capacity, a.diag);
-      else if (!p.move)
-        launch_staged_cells<false, false>(p.tile_shift, grid, s, rows, p.nchunks, p.ntiles,
-                                          grid_params(a), cells, a.n, chunk_rec, chunk_idx,
-                                          a.conteos, a.inicios, a.ordenado, dst, 0u, nullptr);
-      else if (a.diag)
-        launch_staged_cells<true, true>(p.tile_shift, grid, s, rows, p.nchunks, p.ntiles,
-                                        grid_params(a), cells, a.n, chunk_rec, chunk_idx,
-                                        a.conteos, a.inicios, a.ordenado, dst, a.capacity, a.diag);
-      else
-        launch_staged_cells<true, false>(p.tile_shift, grid, s, rows, p.nchunks, p.ntiles,
-                                         grid_params(a), cells, a.n, chunk_rec, chunk_idx,
-                                         a.conteos, a.inicios, a.ordenado, dst, 0u, nullptr);
+    case 3:
+      launch_tile_sort(a, p, rows, chunk_rec, chunk_idx);
       break;
-    }
     case 4:
       if (p.stable) enqueue_stable_sort(a, p, ws);
       break;
@@ -419,37 +420,31 @@ void enqueue_staged(uint32_t stage, const BuildArgs& a, const Plan& p) {
   }
 }
 
-void enqueue_tiled(uint32_t stage, const BuildArgs& a, const Plan& p) {
+void enqueue_bucketed(uint32_t stage, const BuildArgs& a, const Plan& p) {
   char* ws = static_cast<char*>(a.workspace);
   uint32_t* hist = reinterpret_cast<uint32_t*>(ws + p.off_hist);
   uint32_t* tile_total = reinterpret_cast<uint32_t*>(ws + p.off_tile_total);
-  uint2* bucket = reinterpret_cast<uint2*>(ws + p.off_bucket);
-  const uint32_t cells = static_cast<uint32_t>(p.cells);
+  uint2* rows = reinterpret_cast<uint2*>(ws + p.off_rows);
+  uint4* tile_rec = reinterpret_cast<uint4*>(ws + p.off_chunk_rec);
+  uint32_t* tile_idx = reinterpret_cast<uint32_t*>(ws + p.off_chunk_idx);
   hipStream_t s = a.stream;
   switch (stage) {
     case 0:
-      hipLaunchKernelGGL(tiled_keys_kernel, dim3(p.nblk), dim3(kBlock), 0, s,
-                         reinterpret_cast<const float4*>(a.particles), a.n, grid_params(a),
-                         a.celdaDe, hist, p.tile_shift, p.ntiles, p.items);
+      hipLaunchKernelGGL(bucket_keys_kernel, dim3(p.nblk), dim3(kBucketThreads), 0, s,
+                         reinterpret_cast<const uint4*>(a.particles), a.n, p.per_block, grid_params(a),
+                         a.celdaDe, hist, p.tile_shift, p.ntiles, a.diag);
       break;
     case 1:
-      hipLaunchKernelGGL(tiled_colscan_kernel, dim3(p.ntiles), dim3(kBlock), 0, s, hist, p.nblk,
+      hipLaunchKernelGGL(bucket_colscan_kernel, dim3(p.ntiles), dim3(kBlock), 0, s, hist, p.nblk,
                          p.ntiles, tile_total);
       break;
     case 2:
-      hipLaunchKernelGGL(tiled_bucket_kernel, dim3(p.nblk), dim3(kBlock), 0, s, a.celdaDe, a.n,
-                         hist, tile_total, p.tile_shift, p.ntiles, p.items, bucket);
+      hipLaunchKernelGGL(bucket_records_kernel, dim3(p.nblk), dim3(kBucketThreads), 0, s,
+                         reinterpret_cast<const uint4*>(a.particles), a.celdaDe, a.n, p.per_block, hist,
+                         tile_total, p.tile_shift, p.ntiles, tile_rec, tile_idx, rows);
       break;
     case 3:
-      if (!p.move)
-        launch_tiled_cells<false>(p.tile_shift, dim3(p.ntiles), s, bucket, tile_total, p.ntiles,
-                                  cells, a.n, a.conteos, a.inicios, a.ordenado, nullptr, nullptr);
-      else
-        launch_tiled_cells<true>(p.tile_shift, dim3(p.ntiles), s, bucket, tile_total, p.ntiles,
-                                 cells, a.n, a.conteos, a.inicios, a.ordenado,
-                                 reinterpret_cast<const uint4*>(a.particles),
-                                 reinterpret_cast<uint4*>(a.reordered));
-      if (a.diag) enqueue_cell_diag(a.conteos, p.cells, a.capacity, a.diag, s);
+      launch_tile_sort(a, p, rows, tile_rec, tile_idx);
       break;
     case 4:
       if (p.stable) enqueue_stable_sort(a, p, ws);
@@ -515,8 +510,8 @@ int enqueue_stage(uint32_t stage, const BuildArgs& a, const Plan& p) {
     case Path::kStaged:
       enqueue_staged(stage, a, p);
       break;
-    case Path::kTiled:
-      enqueue_tiled(stage, a, p);
+    case Path::kBucketed:
+      enqueue_bucketed(stage, a, p);
       break;
     case Path::kDirect:
       enqueue_direct(stage, a, p);
