@@ -58,7 +58,7 @@ def alg_bytes(n: int, c: int, mode: str) -> dict:
 
     The end-to-end figure uses the fixed model of the four page steps
     instead: 116 N + 16 C + 4 (see hbm_frac_e2e)."""
-    move = mode == "atomic"
+    move = mode in ("atomic", "stable")  # stable: the tile kernel moves records into a workspace copy
     return {
         # staged path (cells <= 2^22, n <= 2^21)
         "chunk_sort": 72 * n,  # record read, celdaDe, chunk records + indices written
@@ -73,7 +73,7 @@ def alg_bytes(n: int, c: int, mode: str) -> dict:
         "scan": 12 * c + 4,
         "scatter": 80 * n if move else 12 * n,
         # optional passes
-        "stable_sort": 4 * (c + 1) + 8 * n,
+        "stable_sort": 4 * (c + 1) + 8 * n + 64 * n,  # starts, ordenado r/w, records copy -> reordered
         "gather": 68 * n,
     }
 

@@ -119,8 +119,9 @@ typedef struct ugp_particle {
  *                     counting sort with LDS histograms and no global atomics
  *   K >  2^24         "clear", "count", "scan", "scatter"     -- one global
  *                     atomic per particle in count and in scatter
- *   slot 4 "stable_sort" (UGP_FLAG_STABLE only), slot 5 "gather"
- *   (UGP_FLAG_GATHER or UGP_FLAG_STABLE only). */
+ *   slot 4 "stable_sort" (UGP_FLAG_STABLE only: sorts every cell's slice
+ *   by particle index and writes the records in that order), slot 5
+ *   "gather" (UGP_FLAG_GATHER only). */
 #define UGP_NUM_STAGES 6u
 
 /* Number of cell keys K for a grid and flags: C = dims[0]*dims[1]*dims[2]

@@ -92,7 +92,8 @@ def _call_build(lib, *, n=4, origin=(0.0, 0.0, 0.0), h=1.0, dims=(4, 4, 4), ptrs
 def test_stage_names(lib):
     assert ugp.stage_names(1000, (128, 128, 128)) == ["chunk_sort", None, None, "tile_sort", None, None]
     assert ugp.stage_names(3_000_000, (128, 128, 128)) == ["keys", "tile_scan", "bucket", "tile_sort", None, None]
-    assert ugp.stage_names(1000, (128, 128, 128), ugp.FLAG_STABLE)[4:] == ["stable_sort", "gather"]
+    assert ugp.stage_names(1000, (128, 128, 128), ugp.FLAG_STABLE)[4:] == ["stable_sort", None]
+    assert ugp.stage_names(1000, (128, 128, 128), ugp.FLAG_STABLE | ugp.FLAG_GATHER)[4:] == ["stable_sort", None]
     assert ugp.stage_names(1000, (128, 128, 128), ugp.FLAG_GATHER)[4:] == [None, "gather"]
     assert ugp.stage_names(0, (128, 128, 128)) == ["clear", None, None, None, None, None]
     assert ugp.stage_names(1000, (8192, 8193, 1))[:4] == ["clear", "count", "scan", "scatter"]

@@ -273,6 +273,32 @@ def test_one_cell_holds_everything(ugp, orc, n):
         assert_parity(wl, run_gpu(ugp, wl, mode), ref, mode)
 
 
+@pytest.mark.parametrize("seed", [3, 4])
+def test_stable_cell_lengths(ugp, orc, seed):
+    """Stable order across the cell lengths the tile kernel treats apart:
+    single particles, short cells sorted in LDS (up to 32), longer ones and
+    cells crossing a staging window (fixed up afterwards: registers up to 16,
+    LDS beyond), on a shuffled and on an already ordered input, with and
+    without the overflow diagnostics."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lengths = np.array([0, 1, 2, 3, 15, 16, 17, 31, 32, 33, 64, 700])
+    conteos = rng.choice(lengths, size=2500, p=[.2, .2, .15, .1, .05, .05, .05, .05, .05, .05, .04, .01])
+    wl = W.make_worked_example(conteos, seed=seed)
+    ref = orc.grid_build(wl.particles, wl.origin, wl.cell_size, wl.dims)
+    assert_parity(wl, run_gpu(ugp, wl, "stable"), ref, "stable")
+    ordered = W.Workload("ordered", np.ascontiguousarray(ref.reordered), wl.origin, wl.cell_size, wl.dims)
+    ref2 = orc.grid_build(ordered.particles, ordered.origin, ordered.cell_size, ordered.dims)
+    assert_parity(ordered, run_gpu(ugp, ordered, "stable"), ref2, "stable")
+    dev = torch.device("cuda:0")
+    r, diag = ugp.grid_build_diag(torch.from_numpy(wl.particles).to(dev), wl.origin.tolist(), float(wl.cell_size),
+                                  wl.dims.tolist(), 24, stable=True)
+    torch.cuda.synchronize()
+    got = oracle.GridIndex(_u32(r.celdaDe), _u32(r.conteos), _u32(r.inicios), _u32(r.ordenado),
+                           r.reordered.cpu().numpy())
+    assert_parity(wl, got, ref, "stable")
+    assert _u32(diag).tolist() == list(orc.diag(ref.conteos, 24))
+
+
 def test_run_to_run(ugp):
     wl = W.make_config("contention")
     a1, a2 = run_gpu(ugp, wl, "atomic"), run_gpu(ugp, wl, "atomic")

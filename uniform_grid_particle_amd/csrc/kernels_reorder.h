@@ -101,27 +101,50 @@ __global__ __launch_bounds__(kBlock) void gather_arrays_kernel(const uint32_t* _
 }
 
 // Stable mode, short cells: one thread per cell. Cells of at most 16
-// entries are sorted in registers with a bitonic network (static indices,
-// padding with 0xFFFFFFFF which no particle index reaches); longer cells
-// are appended to a list for the LDS kernel.
+// entries are sorted in registers with a bitonic network on (particle
+// index, position in the slice) pairs (static indices, padding with all
+// ones, which no pair reaches); longer cells are appended to a list for the
+// LDS kernel. RECS: the scatter kernel left the records in `unstable` in the
+// slice's original order, and each short cell writes its records to
+// `reordered` in the sorted order (reads stay inside the cell's slice);
+// the long-cell kernel writes the records of long cells.
+//
+// LISTED: only the cells of `listed` (its first min(*listed_count,
+// listed_cap) entries; the tile kernel appended the cells it could not sort
+// itself), and their
+// records come from the input particles by index (`unstable` then points to
+// the particles) instead of from a copy by position.
+template <bool RECS, bool LISTED>
 __global__ __launch_bounds__(kBlock) void sort_short_cells_kernel(
     const uint32_t* __restrict__ inicios, uint32_t cells, uint32_t n,
     uint32_t* __restrict__ ordenado, uint32_t* __restrict__ long_list, uint32_t long_cap,
-    uint32_t* __restrict__ long_count) {
-  const uint32_t c = blockIdx.x * kBlock + threadIdx.x;
+    uint32_t* __restrict__ long_count, const uint4* __restrict__ unstable, uint4* __restrict__ reordered,
+    const uint32_t* __restrict__ listed, const uint32_t* __restrict__ listed_count,
+    uint32_t listed_cap) {
+  const uint32_t tid = blockIdx.x * kBlock + threadIdx.x;
+  if (LISTED && (tid >= *listed_count || tid >= listed_cap)) return;
+  const uint32_t c = LISTED ? listed[tid] : tid;
   if (c >= cells) return;
   const uint32_t s = inicios[c];
   const uint32_t e = inicios[c + 1];
-  if (e > n || e <= s || e - s < 2) return;
+  if (e > n || e <= s) return;
   const uint32_t len = e - s;
   if (len > kSmallSort) {
     const uint32_t k = atomicAdd(long_count, 1u);
     if (k < long_cap) long_list[k] = c;
     return;
   }
-  uint32_t v[kSmallSort];
+  if (len == 1) {
+    if (RECS && !LISTED) {
+      reordered[2ull * s] = unstable[2ull * s];
+      reordered[2ull * s + 1u] = unstable[2ull * s + 1u];
+    }
+    return;
+  }
+  uint64_t v[kSmallSort];
 #pragma unroll
-  for (uint32_t k = 0; k < kSmallSort; ++k) v[k] = (k < len) ? ordenado[s + k] : 0xFFFFFFFFu;
+  for (uint32_t k = 0; k < kSmallSort; ++k)
+    v[k] = (k < len) ? (static_cast<uint64_t>(ordenado[s + k]) << 32) | k : ~0ull;
 #pragma unroll
   for (uint32_t kk = 2; kk <= kSmallSort; kk <<= 1) {
 #pragma unroll
@@ -131,7 +154,7 @@ __global__ __launch_bounds__(kBlock) void sort_short_cells_kernel(
         const uint32_t l = i ^ j;
         if (l > i) {
           const bool up = (i & kk) == 0;
-          const uint32_t a = v[i], b = v[l];
+          const uint64_t a = v[i], b = v[l];
           if ((a > b) == up) {
             v[i] = b;
             v[l] = a;
@@ -141,18 +164,31 @@ __global__ __launch_bounds__(kBlock) void sort_short_cells_kernel(
     }
   }
 #pragma unroll
-  for (uint32_t k = 0; k < kSmallSort; ++k)
-    if (k < len) ordenado[s + k] = v[k];
+  for (uint32_t k = 0; k < kSmallSort; ++k) {
+    if (k < len) {
+      ordenado[s + k] = static_cast<uint32_t>(v[k] >> 32);
+      if (RECS) {
+        const size_t from = LISTED ? 2ull * static_cast<uint32_t>(v[k] >> 32)
+                                   : 2ull * (s + static_cast<uint32_t>(v[k] & 0xFFFFFFFFu));
+        const uint4 a = unstable[from], b = unstable[from + 1u];
+        reordered[2ull * (s + k)] = a;
+        reordered[2ull * (s + k) + 1u] = b;
+      }
+    }
+  }
 }
 
 // Stable mode, long cells: one workgroup per listed cell (grid-stride over
 // the list). Up to 16384 entries: bitonic sort in LDS. Longer: ordered
 // compaction, i.e. walk all particles in index order and append those of
 // this cell (the cell's membership is exact already; only order changes).
+// RECS: each sorted entry's record is copied from the input particles.
+template <bool RECS>
 __global__ __launch_bounds__(kSortBlock) void sort_long_cells_kernel(
     const uint32_t* __restrict__ inicios, const uint32_t* __restrict__ celdaDe, uint32_t n,
     const uint32_t* __restrict__ long_list, uint32_t long_cap,
-    const uint32_t* __restrict__ long_count, uint32_t* __restrict__ ordenado) {
+    const uint32_t* __restrict__ long_count, uint32_t* __restrict__ ordenado,
+    const uint4* __restrict__ particles, uint4* __restrict__ reordered) {
   __shared__ uint32_t s_keys[kLdsSort];
   __shared__ uint32_t s_wave[kSortBlock / 64];
   uint32_t count = *long_count;
@@ -184,7 +220,14 @@ __global__ __launch_bounds__(kSortBlock) void sort_long_cells_kernel(
           __syncthreads();
         }
       }
-      for (uint32_t t = threadIdx.x; t < len; t += kSortBlock) ordenado[s + t] = s_keys[t];
+      for (uint32_t t = threadIdx.x; t < len; t += kSortBlock) {
+        const uint32_t idx = s_keys[t];
+        ordenado[s + t] = idx;
+        if (RECS && idx < n) {
+          reordered[2ull * (s + t)] = particles[2ull * idx];
+          reordered[2ull * (s + t) + 1u] = particles[2ull * idx + 1u];
+        }
+      }
       __syncthreads();
     } else {
       uint32_t run = 0;
@@ -194,7 +237,13 @@ __global__ __launch_bounds__(kSortBlock) void sort_long_cells_kernel(
         uint32_t total;
         const uint32_t excl = block_exclusive_sum<kSortBlock>(flag, s_wave, &total);
         const uint32_t dst = s + run + excl;
-        if (flag && dst < e) ordenado[dst] = static_cast<uint32_t>(i);
+        if (flag && dst < e) {
+          ordenado[dst] = static_cast<uint32_t>(i);
+          if (RECS) {
+            reordered[2ull * dst] = particles[2u * i];
+            reordered[2ull * dst + 1u] = particles[2u * i + 1u];
+          }
+        }
         run += total;
       }
     }

@@ -48,6 +48,7 @@ constexpr uint32_t kStagedMaxTiles = 512;
 constexpr uint32_t kStagedMaxChunks = 1024;
 constexpr int kStagedRegs = 8;                      // particles per tile_sort thread in registers
 constexpr uint32_t kShortRun = 64;                  // longest chunk run a thread expands by itself
+constexpr uint32_t kCellSortMax = 32;               // longest cell a tile sorts itself in stable mode
 
 // Geometry the host uses (chosen by measurement on MI355X, 1M particles on
 // 128^3 cells: runs of 8+ records per chunk and tile keep tile_sort's loads
@@ -69,6 +70,25 @@ __device__ __forceinline__ uint32_t tile_of_block(uint32_t b, uint32_t ntiles) {
   return (b % 8) * (ntiles / 8) + b / 8;
 }
 
+// Sorts one cell's staged slice by particle index, carrying each entry's
+// staging slot: keys[0..len) and perm[0..len) in LDS (perm holds the
+// identity on entry), 2 <= len <= kCellSortMax. Insertion sort in LDS: a few
+// steps for the usual cell of two or three, no registers held. Particle
+// indices are distinct, so the order is the stable one.
+__device__ __forceinline__ void sort_cell_in_lds(uint32_t* keys, uint32_t* perm, uint32_t len) {
+  for (uint32_t i = 1; i < len; ++i) {
+    const uint32_t key = keys[i], pv = perm[i];
+    uint32_t j = i;
+    while (j > 0 && keys[j - 1] > key) {
+      keys[j] = keys[j - 1];
+      perm[j] = perm[j - 1];
+      --j;
+    }
+    keys[j] = key;
+    perm[j] = pv;
+  }
+}
+
 // chunk_sort: CT threads, chunk b holds particles [b*chunk, (b+1)*chunk)
 // with chunk = CT * kChunkItems.
 // rows[b*ntiles + t] = {particles of chunk b in tile t, those in tiles < t}.
@@ -76,7 +96,7 @@ template <int CT>
 __global__ __launch_bounds__(CT) void staged_keys_kernel(
     const uint4* __restrict__ parts, uint32_t n, GridParams g, uint32_t* __restrict__ celdaDe,
     uint2* __restrict__ rows, uint32_t tile_shift, uint32_t ntiles, uint4* __restrict__ chunk_rec,
-    uint32_t* __restrict__ chunk_idx, uint32_t* __restrict__ diag) {
+    uint32_t* __restrict__ chunk_idx, uint32_t* __restrict__ diag, uint32_t* __restrict__ fix_count) {
   constexpr int kChunkThreads = CT;
   constexpr uint32_t kChunk = CT * kChunkItems;
   constexpr uint32_t kTilesPerThread = kStagedMaxTiles / CT;  // tile bins per thread
@@ -89,6 +109,7 @@ __global__ __launch_bounds__(CT) void staged_keys_kernel(
   for (uint32_t t = threadIdx.x; t < kStagedMaxTiles; t += kChunkThreads) s_hist[t] = 0u;
   // the overflow diagnostics (when asked for) accumulate in tile_sort
   if (diag != nullptr && blockIdx.x == 0 && threadIdx.x < 2) diag[threadIdx.x] = 0u;
+  if (fix_count != nullptr && blockIdx.x == 0 && threadIdx.x == 0) *fix_count = 0u;  // stable fix-up list
   const uint32_t base = blockIdx.x * kChunk;
   // the records stay in registers (scalar arrays, static indices) until
   // they are placed in LDS in tile order
@@ -169,13 +190,22 @@ __global__ __launch_bounds__(CT) void staged_keys_kernel(
 // DIAG: also fold the tile's histogram into the overflow diagnostics
 // (diag[0] max occupancy, diag[1] overflowing insertions over capacity cap;
 // both zeroed by the kernel before this one).
-template <bool MOVE, bool DIAG, uint32_t SHIFT, int NT, uint32_t WIN>
+// STABLE: every cell lists its particles in ascending index order (page
+// "Construir el índice...", section "El orden dentro de la celda"). Cells
+// that lie wholly inside a staging window are sorted in LDS before the
+// window is written (windows end on cell boundaries); a cell longer than
+// kCellSortMax or than a window, and every multi-particle cell of a tile
+// past the staged capacity, is written in arrival order and appended to
+// fix_list (fix_count zeroed by the kernel before this one) for the fix-up
+// pass.
+template <bool MOVE, bool DIAG, bool STABLE, uint32_t SHIFT, int NT, uint32_t WIN>
 __global__ __launch_bounds__(NT) void staged_cells_kernel(
     const uint2* __restrict__ rows, uint32_t nchunks, uint32_t chunk, uint32_t ntiles, GridParams g,
     uint32_t cells, uint32_t n, const uint4* __restrict__ chunk_rec,
     const uint32_t* __restrict__ chunk_idx, uint32_t* __restrict__ conteos,
     uint32_t* __restrict__ inicios, uint32_t* __restrict__ ordenado, uint4* __restrict__ dst,
-    uint32_t cap, uint32_t* __restrict__ diag) {
+    uint32_t cap, uint32_t* __restrict__ diag, uint32_t* __restrict__ fix_list, uint32_t fix_cap,
+    uint32_t* __restrict__ fix_count) {
   constexpr uint32_t kTileCells = 1u << SHIFT;
   // cells per thread in the scan (tiles smaller than the workgroup: one
   // cell for each of the first kTileCells threads)
@@ -195,6 +225,7 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
   __shared__ uint32_t s_wave[NT / 64];
   __shared__ uint32_t s_runmax[NT / 64];
   __shared__ uint32_t s_dm[DIAG ? NT / 64 : 1], s_do[DIAG ? NT / 64 : 1];
+  __shared__ uint32_t s_perm[STABLE ? WIN : 1];  // stable: window slot -> staged slot
 
   const uint32_t t = tile_of_block(blockIdx.x, ntiles);
   const uint32_t cell0 = t << SHIFT;
@@ -415,8 +446,20 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
 #pragma unroll
     for (int k = 0; k < kStagedRegs; ++k)
       slot[k] = (lr[k] != 0xFFFFFFFFu) ? s_cnt[lr[k] >> 16] + (lr[k] & 0xFFFFu) : 0xFFFFFFFFu;
-    for (uint32_t w0 = 0; w0 < count; w0 += kStagedWin) {
-      const uint32_t wn = (count - w0 < kStagedWin) ? count - w0 : kStagedWin;
+    uint32_t w0 = 0;
+    while (w0 < count) {  // tile-uniform
+      uint32_t w1 = (count - w0 <= kStagedWin) ? count : w0 + kStagedWin;
+      if (STABLE && w1 < count) {
+        // end the window at the last cell start within reach (the starts in
+        // s_cnt never decrease); if that is w0, one cell spans the window
+        uint32_t lo = 0, hi = kTileCells - 1u;
+        while (lo < hi) {
+          const uint32_t mid = (lo + hi + 1u) >> 1;
+          if (s_cnt[mid] <= w1) lo = mid; else hi = mid - 1u;
+        }
+        if (s_cnt[lo] > w0) w1 = s_cnt[lo];
+      }
+      const uint32_t wn = w1 - w0;
 #pragma unroll
       for (int k = 0; k < kStagedRegs; ++k) {
         const uint32_t o = slot[k] - w0;
@@ -428,15 +471,34 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
           s_idx[o] = idx[k];
         }
       }
+      if (STABLE) {
+        for (uint32_t q = threadIdx.x; q < wn; q += NT) s_perm[q] = q;
+        __syncthreads();
+        // each cell starting in this window: sorted here if it fits, listed otherwise
+        for (uint32_t j = threadIdx.x; j < tc; j += NT) {
+          const uint32_t a = s_cnt[j];
+          const uint32_t e = (j + 1u < kTileCells) ? s_cnt[j + 1u] : tot;
+          if (a < w0 || a >= w1 || e - a < 2u) continue;
+          if (e > w1 || e - a > kCellSortMax) {
+            const uint32_t f = atomicAdd(fix_count, 1u);
+            if (f < fix_cap) fix_list[f] = cell0 + j;
+            continue;
+          }
+          sort_cell_in_lds(s_idx + (a - w0), s_perm + (a - w0), e - a);
+        }
+      }
       __syncthreads();
       const size_t out0 = static_cast<size_t>(bs) + w0;
       for (uint32_t q = threadIdx.x; q < wn; q += NT)
         if (out0 + q < n) ordenado[out0 + q] = s_idx[q];
       if (MOVE) {
-        for (uint32_t q = threadIdx.x; q < 2 * wn; q += NT)
-          if (out0 * 2u + q < 2ull * n) dst[out0 * 2u + q] = s_rec[q];
+        for (uint32_t q = threadIdx.x; q < 2 * wn; q += NT) {
+          const uint32_t from = STABLE ? 2u * s_perm[q >> 1] + (q & 1u) : q;
+          if (out0 * 2u + q < 2ull * n) dst[out0 * 2u + q] = s_rec[from];
+        }
       }
       __syncthreads();
+      w0 = w1;
     }
   } else {
     // a tile past the staged capacity (count > kStagedCap > 0): rounds of
@@ -509,6 +571,18 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
             dst[out * 2u] = make_uint4(v[0][k], v[1][k], v[2][k], v[3][k]);
             dst[out * 2u + 1u] = make_uint4(v[4][k], v[5][k], v[6][k], v[7][k]);
           }
+        }
+      }
+    }
+    if (STABLE) {
+      // slots were taken in arrival order: every cell of two or more is
+      // fixed up afterwards. Once every cursor is final it holds its cell's
+      // end, so a cell's count is its end minus the previous cell's.
+      __syncthreads();
+      for (uint32_t j = threadIdx.x; j < tc; j += NT) {
+        if (s_cnt[j] - (j ? s_cnt[j - 1u] : 0u) >= 2u) {
+          const uint32_t f = atomicAdd(fix_count, 1u);
+          if (f < fix_cap) fix_list[f] = cell0 + j;
         }
       }
     }

@@ -78,7 +78,10 @@ struct Plan {
   size_t off_cursor = 0, off_small = 0;
   // stable
   uint32_t long_cap = 0;
-  size_t off_long_count = 0, off_long = 0;
+  size_t off_long_count = 0, off_long = 0, off_unstable = 0;
+  // stable mode on the tile paths: cells the tile kernel could not sort
+  uint32_t fix_cap = 0;
+  size_t off_fix_count = 0, off_fix = 0;
   size_t total = 256;
 };
 
@@ -116,7 +119,9 @@ int make_plan(uint32_t n, const uint32_t dims[3], uint32_t flags, Plan* p) {
   p->cells = cells;
   p->stable = (flags & UGP_FLAG_STABLE) != 0;
   const bool index_only = (flags & UGP_FLAG_INDEX_ONLY) != 0;
-  p->gather = !index_only && (p->stable || (flags & UGP_FLAG_GATHER) != 0);
+  // stable mode moves the records in the tile kernel, into a workspace copy
+  // that the per-cell sort then permutes into `reordered`
+  p->gather = !index_only && !p->stable && (flags & UGP_FLAG_GATHER) != 0;
   p->move = !index_only && !p->gather;
   const uint32_t lg = ceil_log2_u64(cells);
   size_t off = 0;
@@ -185,6 +190,19 @@ int make_plan(uint32_t n, const uint32_t dims[3], uint32_t flags, Plan* p) {
     off = align_up(off + 4u, 256);
     p->off_long = off;
     off = align_up(off + static_cast<size_t>(p->long_cap) * 4u, 256);
+    if (p->path == Path::kDirect) {
+      if (p->move) {  // the scatter kernel's records, in arrival order
+        p->off_unstable = off;
+        off = align_up(off + static_cast<size_t>(n) * 32u, 256);
+      }
+    } else {  // at most one entry per cell of two or more particles
+      const uint64_t fcap = static_cast<uint64_t>(n) / 2 + 1;
+      p->fix_cap = static_cast<uint32_t>(fcap < cells ? fcap : cells);
+      p->off_fix_count = off;
+      off = align_up(off + 4u, 256);
+      p->off_fix = off;
+      off = align_up(off + static_cast<size_t>(p->fix_cap) * 4u, 256);
+    }
   }
   p->total = off ? off : 256;
   return UGP_OK;
@@ -296,27 +314,29 @@ void launch_clear(uint32_t* ptr, uint64_t words, uint32_t* extra, uint32_t extra
   hipLaunchKernelGGL(clear_kernel, dim3(blocks), dim3(kBlock), 0, s, ptr, words, extra, extra_words);
 }
 
-template <bool MOVE, bool DIAG, uint32_t SHIFT>
+template <bool MOVE, bool DIAG, bool STABLE, uint32_t SHIFT>
 void launch_staged_cells_at(dim3 grid, hipStream_t s, const uint2* rows, uint32_t nchunks,
                             uint32_t ntiles, GridParams g, uint32_t cells, uint32_t n,
                             const uint4* chunk_rec, const uint32_t* chunk_idx, uint32_t* conteos,
                             uint32_t* inicios, uint32_t* ordenado, uint4* dst, uint32_t cap,
-                            uint32_t* diag) {
-  hipLaunchKernelGGL((staged_cells_kernel<MOVE, DIAG, SHIFT, kCellsThreads, kCellsWin>), grid,
+                            uint32_t* diag, uint32_t* fix, uint32_t fix_cap, uint32_t* fix_count) {
+  hipLaunchKernelGGL((staged_cells_kernel<MOVE, DIAG, STABLE, SHIFT, kCellsThreads, kCellsWin>), grid,
                      dim3(kCellsThreads), 0, s, rows, nchunks, kChunk, ntiles, g, cells, n, chunk_rec,
-                     chunk_idx, conteos, inicios, ordenado, dst, cap, diag);
+                     chunk_idx, conteos, inicios, ordenado, dst, cap, diag, fix, fix_cap, fix_count);
 }
 
-template <bool MOVE, bool DIAG>
+template <bool MOVE, bool DIAG, bool STABLE>
 void launch_staged_cells(uint32_t shift, dim3 grid, hipStream_t s, const uint2* rows,
                          uint32_t nchunks, uint32_t ntiles, GridParams g, uint32_t cells,
                          uint32_t n, const uint4* chunk_rec, const uint32_t* chunk_idx,
                          uint32_t* conteos, uint32_t* inicios, uint32_t* ordenado, uint4* dst,
-                         uint32_t cap, uint32_t* diag) {
-#define UGP_STAGED_CASE(S)                                                                    \
-  case S:                                                                                     \
-    launch_staged_cells_at<MOVE, DIAG, S>(grid, s, rows, nchunks, ntiles, g, cells, n, chunk_rec, \
-                                          chunk_idx, conteos, inicios, ordenado, dst, cap, diag); \
+                         uint32_t cap, uint32_t* diag, uint32_t* fix, uint32_t fix_cap,
+                         uint32_t* fix_count) {
+#define UGP_STAGED_CASE(S)                                                                            \
+  case S:                                                                                             \
+    launch_staged_cells_at<MOVE, DIAG, STABLE, S>(grid, s, rows, nchunks, ntiles, g, cells, n,         \
+                                                  chunk_rec, chunk_idx, conteos, inicios, ordenado,   \
+                                                  dst, cap, diag, fix, fix_cap, fix_count);           \
     break;
   switch (shift) {
     UGP_STAGED_CASE(4)
@@ -330,8 +350,9 @@ void launch_staged_cells(uint32_t shift, dim3 grid, hipStream_t s, const uint2* 
     UGP_STAGED_CASE(12)
     UGP_STAGED_CASE(13)
     default:
-      launch_staged_cells_at<MOVE, DIAG, 14>(grid, s, rows, nchunks, ntiles, g, cells, n, chunk_rec,
-                                             chunk_idx, conteos, inicios, ordenado, dst, cap, diag);
+      launch_staged_cells_at<MOVE, DIAG, STABLE, 14>(grid, s, rows, nchunks, ntiles, g, cells, n,
+                                                     chunk_rec, chunk_idx, conteos, inicios, ordenado,
+                                                     dst, cap, diag, fix, fix_cap, fix_count);
       break;
   }
 #undef UGP_STAGED_CASE
@@ -349,16 +370,62 @@ void enqueue_cell_diag(const uint32_t* conteos, uint64_t cells, uint32_t cap, ui
                      static_cast<uint32_t>(cells), cap, diag);
 }
 
+// Where the scatter kernels write the records: nowhere (a gather follows, or
+// index only), a workspace copy (stable mode: the per-cell sort then writes
+// `reordered`), or `reordered` itself.
+uint4* record_dst(const BuildArgs& a, const Plan& p) {
+  if (!p.move) return nullptr;
+  if (p.stable && p.path == Path::kDirect)
+    return reinterpret_cast<uint4*>(static_cast<char*>(a.workspace) + p.off_unstable);
+  return reinterpret_cast<uint4*>(a.reordered);
+}
+
+// the stable fix-up list of the tile paths (nullptr otherwise)
+uint32_t* fix_count_of(const BuildArgs& a, const Plan& p) {
+  if (!p.stable || p.path == Path::kDirect) return nullptr;
+  return reinterpret_cast<uint32_t*>(static_cast<char*>(a.workspace) + p.off_fix_count);
+}
+
 // Stable-order and gather passes, shared by every path.
 void enqueue_stable_sort(const BuildArgs& a, const Plan& p, char* ws) {
   uint32_t* long_count = reinterpret_cast<uint32_t*>(ws + p.off_long_count);
   uint32_t* long_list = reinterpret_cast<uint32_t*>(ws + p.off_long);
   const uint32_t cells = static_cast<uint32_t>(p.cells);
   launch_clear(long_count, 1, nullptr, 0, a.stream);
-  hipLaunchKernelGGL(sort_short_cells_kernel, dim3(blocks_for(cells, kBlock)), dim3(kBlock), 0,
-                     a.stream, a.inicios, cells, a.n, a.ordenado, long_list, p.long_cap, long_count);
-  hipLaunchKernelGGL(sort_long_cells_kernel, dim3(kSortGrid), dim3(kSortBlock), 0, a.stream,
-                     a.inicios, a.celdaDe, a.n, long_list, p.long_cap, long_count, a.ordenado);
+  const uint4* parts = reinterpret_cast<const uint4*>(a.particles);
+  uint4* out = p.move ? reinterpret_cast<uint4*>(a.reordered) : nullptr;
+  if (p.path != Path::kDirect) {
+    // the tile kernel sorted every cell it could; fix up the listed ones,
+    // taking their records from the input by particle index
+    const uint32_t* fix = reinterpret_cast<const uint32_t*>(ws + p.off_fix);
+    const uint32_t* fix_count = reinterpret_cast<const uint32_t*>(ws + p.off_fix_count);
+    const dim3 grid(blocks_for(p.fix_cap, kBlock));
+    if (p.move)
+      hipLaunchKernelGGL((sort_short_cells_kernel<true, true>), grid, dim3(kBlock), 0, a.stream, a.inicios,
+                         cells, a.n, a.ordenado, long_list, p.long_cap, long_count, parts, out, fix,
+                         fix_count, p.fix_cap);
+    else
+      hipLaunchKernelGGL((sort_short_cells_kernel<false, true>), grid, dim3(kBlock), 0, a.stream, a.inicios,
+                         cells, a.n, a.ordenado, long_list, p.long_cap, long_count, nullptr, nullptr, fix,
+                         fix_count, p.fix_cap);
+  } else {
+    const dim3 grid(blocks_for(cells, kBlock));
+    if (p.move)
+      hipLaunchKernelGGL((sort_short_cells_kernel<true, false>), grid, dim3(kBlock), 0, a.stream, a.inicios,
+                         cells, a.n, a.ordenado, long_list, p.long_cap, long_count,
+                         reinterpret_cast<const uint4*>(ws + p.off_unstable), out, nullptr, nullptr, 0u);
+    else
+      hipLaunchKernelGGL((sort_short_cells_kernel<false, false>), grid, dim3(kBlock), 0, a.stream, a.inicios,
+                         cells, a.n, a.ordenado, long_list, p.long_cap, long_count, nullptr, nullptr, nullptr,
+                         nullptr, 0u);
+  }
+  if (p.move)
+    hipLaunchKernelGGL(sort_long_cells_kernel<true>, dim3(kSortGrid), dim3(kSortBlock), 0, a.stream,
+                       a.inicios, a.celdaDe, a.n, long_list, p.long_cap, long_count, a.ordenado, parts, out);
+  else
+    hipLaunchKernelGGL(sort_long_cells_kernel<false>, dim3(kSortGrid), dim3(kSortBlock), 0, a.stream,
+                       a.inicios, a.celdaDe, a.n, long_list, p.long_cap, long_count, a.ordenado, nullptr,
+                       nullptr);
 }
 
 void enqueue_gather(const BuildArgs& a) {
@@ -373,25 +440,27 @@ void enqueue_gather(const BuildArgs& a) {
 void launch_tile_sort(const BuildArgs& a, const Plan& p, const uint2* rows, const uint4* rec,
                       const uint32_t* idx) {
   const uint32_t cells = static_cast<uint32_t>(p.cells);
-  uint4* dst = p.move ? reinterpret_cast<uint4*>(a.reordered) : nullptr;
+  uint4* dst = record_dst(a, p);
   const dim3 grid(p.ntiles);
   hipStream_t s = a.stream;
-  if (!p.move && a.diag)
-    launch_staged_cells<false, true>(p.tile_shift, grid, s, rows, p.nchunks, p.ntiles, grid_params(a),
-                                     cells, a.n, rec, idx, a.conteos, a.inicios, a.ordenado, dst,
-                                     a.capacity, a.diag);
-  else if (!p.move)
-    launch_staged_cells<false, false>(p.tile_shift, grid, s, rows, p.nchunks, p.ntiles, grid_params(a),
-                                      cells, a.n, rec, idx, a.conteos, a.inicios, a.ordenado, dst, 0u,
-                                      nullptr);
-  else if (a.diag)
-    launch_staged_cells<true, true>(p.tile_shift, grid, s, rows, p.nchunks, p.ntiles, grid_params(a),
-                                    cells, a.n, rec, idx, a.conteos, a.inicios, a.ordenado, dst,
-                                    a.capacity, a.diag);
-  else
-    launch_staged_cells<true, false>(p.tile_shift, grid, s, rows, p.nchunks, p.ntiles, grid_params(a),
-                                     cells, a.n, rec, idx, a.conteos, a.inicios, a.ordenado, dst, 0u,
-                                     nullptr);
+  uint32_t* fix_count = fix_count_of(a, p);
+  uint32_t* fix = fix_count ? reinterpret_cast<uint32_t*>(static_cast<char*>(a.workspace) + p.off_fix) : nullptr;
+  const GridParams g = grid_params(a);
+  // one instantiation per (moves records, diagnostics, stable order)
+#define UGP_TILE_SORT(M, D, S)                                                                       \
+  launch_staged_cells<M, D, S>(p.tile_shift, grid, s, rows, p.nchunks, p.ntiles, g, cells, a.n, rec, \
+                               idx, a.conteos, a.inicios, a.ordenado, dst, D ? a.capacity : 0u,     \
+                               D ? a.diag : nullptr, fix, p.fix_cap, fix_count)
+  const bool m = p.move, d = a.diag != nullptr, st = p.stable;
+  if (m && d && st) UGP_TILE_SORT(true, true, true);
+  else if (m && d) UGP_TILE_SORT(true, true, false);
+  else if (m && st) UGP_TILE_SORT(true, false, true);
+  else if (m) UGP_TILE_SORT(true, false, false);
+  else if (d && st) UGP_TILE_SORT(false, true, true);
+  else if (d) UGP_TILE_SORT(false, true, false);
+  else if (st) UGP_TILE_SORT(false, false, true);
+  else UGP_TILE_SORT(false, false, false);
+#undef UGP_TILE_SORT
 }
 
 void enqueue_staged(uint32_t stage, const BuildArgs& a, const Plan& p) {
@@ -404,7 +473,8 @@ void enqueue_staged(uint32_t stage, const BuildArgs& a, const Plan& p) {
     case 0:
       hipLaunchKernelGGL(staged_keys_kernel<kChunkThreads>, dim3(p.nchunks), dim3(kChunkThreads), 0, s,
                          reinterpret_cast<const uint4*>(a.particles), a.n, grid_params(a),
-                         a.celdaDe, rows, p.tile_shift, p.ntiles, chunk_rec, chunk_idx, a.diag);
+                         a.celdaDe, rows, p.tile_shift, p.ntiles, chunk_rec, chunk_idx, a.diag,
+                         fix_count_of(a, p));
       break;
     case 3:
       launch_tile_sort(a, p, rows, chunk_rec, chunk_idx);
@@ -432,7 +502,7 @@ void enqueue_bucketed(uint32_t stage, const BuildArgs& a, const Plan& p) {
     case 0:
       hipLaunchKernelGGL(bucket_keys_kernel, dim3(p.nblk), dim3(kBucketThreads), 0, s,
                          reinterpret_cast<const uint4*>(a.particles), a.n, p.per_block, grid_params(a),
-                         a.celdaDe, hist, p.tile_shift, p.ntiles, a.diag);
+                         a.celdaDe, hist, p.tile_shift, p.ntiles, a.diag, fix_count_of(a, p));
       break;
     case 1:
       hipLaunchKernelGGL(bucket_colscan_kernel, dim3(p.ntiles), dim3(kBlock), 0, s, hist, p.nblk,
@@ -484,7 +554,7 @@ void enqueue_direct(uint32_t stage, const BuildArgs& a, const Plan& p) {
       else
         hipLaunchKernelGGL(scatter_kernel<true>, pgrid, dim3(kBlock), 0, s, a.celdaDe, a.n, cells,
                            cursor, a.ordenado, reinterpret_cast<const uint4*>(a.particles),
-                           reinterpret_cast<uint4*>(a.reordered));
+                           record_dst(a, p));
       if (a.diag) enqueue_cell_diag(a.conteos, p.cells, a.capacity, a.diag, s);
       break;
     case 4:
