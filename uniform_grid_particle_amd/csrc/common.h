@@ -14,6 +14,49 @@ constexpr uint32_t kMaxDim = 1u << 24;
 // encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
 constexpr int kWaitLoadsAndStores = 0x0F70;
 
+// Stable mode on the tile paths: the cells a tile kernel leaves in arrival
+// order. Cells of 2..kRankSortMax particles go on the short list (put in
+// order afterwards by one wave each), longer ones on the long list (one
+// workgroup each). One block of words holds both: the two list lengths
+// (zeroed by the first kernel of the build) at base[0] and base[1], the
+// short list from base[kFixHeader], the long list after it. A list never
+// holds more than its capacity.
+constexpr uint32_t kRankSortMax = 256;
+constexpr uint32_t kFixHeader = 64;  // words before the short list (256 bytes)
+struct FixLists {
+  uint32_t* base;
+  uint32_t fix_cap;   // short-list capacity
+  uint32_t long_cap;  // long-list capacity
+  __device__ __forceinline__ uint32_t* counts() const { return base; }
+  __device__ __forceinline__ uint32_t* fix() const { return base + kFixHeader; }
+  __device__ __forceinline__ uint32_t* lng() const { return base + kFixHeader + fix_cap; }
+};
+
+// Puts the cells of the calling wave's lanes with `listed` set on the list
+// their length picks, one global atomic per list and wave. Every lane of
+// the wave must call it (uniform control flow).
+__device__ __forceinline__ void list_cells_wave(const FixLists& fl, uint32_t cell, uint32_t len, bool listed) {
+  const bool sh = listed && len <= kRankSortMax, lo = listed && len > kRankSortMax;
+  const uint64_t ms = __ballot(sh), ml = __ballot(lo);
+  const uint32_t lane = __lane_id();
+  const uint64_t below = (1ull << lane) - 1ull;
+  uint32_t bs = 0, bl = 0;
+  if (lane == 0) {
+    if (ms) bs = atomicAdd(&fl.base[0], static_cast<uint32_t>(__popcll(ms)));
+    if (ml) bl = atomicAdd(&fl.base[1], static_cast<uint32_t>(__popcll(ml)));
+  }
+  bs = __shfl(bs, 0);
+  bl = __shfl(bl, 0);
+  if (sh) {
+    const uint32_t f = bs + static_cast<uint32_t>(__popcll(ms & below));
+    if (f < fl.fix_cap) fl.fix()[f] = cell;
+  }
+  if (lo) {
+    const uint32_t f = bl + static_cast<uint32_t>(__popcll(ml & below));
+    if (f < fl.long_cap) fl.lng()[f] = cell;
+  }
+}
+
 struct GridParams {
   float ox, oy, oz;  // origin
   float h;           // cell size
@@ -158,6 +201,21 @@ __device__ __forceinline__ uint32_t block_exclusive_sum(uint32_t x, uint32_t* s_
   __syncthreads();
   *total = all;
   return before + incl - x;
+}
+
+// Maximum of one value per thread across a workgroup (all threads get it).
+// s_wave: NT/64 words of LDS; two barriers, every thread must call it.
+template <int NT>
+__device__ __forceinline__ uint32_t block_max(uint32_t x, uint32_t* s_wave) {
+  constexpr int kWaves = NT / 64;
+  const uint32_t incl = wave_inclusive_max(x);
+  if ((threadIdx.x & 63) == 63) s_wave[threadIdx.x >> 6] = incl;
+  __syncthreads();
+  uint32_t m = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) m = (s_wave[w] > m) ? s_wave[w] : m;
+  __syncthreads();
+  return m;
 }
 
 // Sum of one value per thread across a workgroup (all threads get it).

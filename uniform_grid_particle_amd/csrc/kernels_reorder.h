@@ -10,6 +10,9 @@ constexpr uint32_t kSmallSort = 16;  // cells up to this length are sorted in re
 constexpr int kSortBlock = 1024;     // threads of the long-cell sort
 constexpr uint32_t kLdsSort = 16384; // longest cell sorted in LDS (64 KiB)
 constexpr int kSortGrid = 512;       // workgroups of the long-cell sort
+constexpr uint32_t kBitmapPasses = 4;     // bitmap windows a long cell may take (2^21 index values)
+constexpr uint32_t kFixLongBlocks = 128;   // fix-up workgroups on long cells
+constexpr uint32_t kFixShortBlocks = 256;  // fix-up workgroups on short cells, a wave per cell
 
 // Gather: two lanes per record, each moving one 16-byte half, so every
 // store instruction writes a contiguous span. Indices >= n_src are skipped.
@@ -108,22 +111,12 @@ __global__ __launch_bounds__(kBlock) void gather_arrays_kernel(const uint32_t* _
 // slice's original order, and each short cell writes its records to
 // `reordered` in the sorted order (reads stay inside the cell's slice);
 // the long-cell kernel writes the records of long cells.
-//
-// LISTED: only the cells of `listed` (its first min(*listed_count,
-// listed_cap) entries; the tile kernel appended the cells it could not sort
-// itself), and their
-// records come from the input particles by index (`unstable` then points to
-// the particles) instead of from a copy by position.
-template <bool RECS, bool LISTED>
+template <bool RECS>
 __global__ __launch_bounds__(kBlock) void sort_short_cells_kernel(
     const uint32_t* __restrict__ inicios, uint32_t cells, uint32_t n,
     uint32_t* __restrict__ ordenado, uint32_t* __restrict__ long_list, uint32_t long_cap,
-    uint32_t* __restrict__ long_count, const uint4* __restrict__ unstable, uint4* __restrict__ reordered,
-    const uint32_t* __restrict__ listed, const uint32_t* __restrict__ listed_count,
-    uint32_t listed_cap) {
-  const uint32_t tid = blockIdx.x * kBlock + threadIdx.x;
-  if (LISTED && (tid >= *listed_count || tid >= listed_cap)) return;
-  const uint32_t c = LISTED ? listed[tid] : tid;
+    uint32_t* __restrict__ long_count, const uint4* __restrict__ unstable, uint4* __restrict__ reordered) {
+  const uint32_t c = blockIdx.x * kBlock + threadIdx.x;
   if (c >= cells) return;
   const uint32_t s = inicios[c];
   const uint32_t e = inicios[c + 1];
@@ -135,7 +128,7 @@ __global__ __launch_bounds__(kBlock) void sort_short_cells_kernel(
     return;
   }
   if (len == 1) {
-    if (RECS && !LISTED) {
+    if (RECS) {
       reordered[2ull * s] = unstable[2ull * s];
       reordered[2ull * s + 1u] = unstable[2ull * s + 1u];
     }
@@ -168,8 +161,7 @@ __global__ __launch_bounds__(kBlock) void sort_short_cells_kernel(
     if (k < len) {
       ordenado[s + k] = static_cast<uint32_t>(v[k] >> 32);
       if (RECS) {
-        const size_t from = LISTED ? 2ull * static_cast<uint32_t>(v[k] >> 32)
-                                   : 2ull * (s + static_cast<uint32_t>(v[k] & 0xFFFFFFFFu));
+        const size_t from = 2ull * (s + static_cast<uint32_t>(v[k] & 0xFFFFFFFFu));
         const uint4 a = unstable[from], b = unstable[from + 1u];
         reordered[2ull * (s + k)] = a;
         reordered[2ull * (s + k) + 1u] = b;
@@ -178,28 +170,84 @@ __global__ __launch_bounds__(kBlock) void sort_short_cells_kernel(
   }
 }
 
-// Stable mode, long cells: one workgroup per listed cell (grid-stride over
-// the list). Up to 16384 entries: bitonic sort in LDS. Longer: ordered
-// compaction, i.e. walk all particles in index order and append those of
-// this cell (the cell's membership is exact already; only order changes).
-// RECS: each sorted entry's record is copied from the input particles.
+// Stable mode, long cells: the workgroups first, first + stride, ... take
+// entries first, first + stride, ... of the list of long cells. Up to 16384
+// entries, held in registers: when the cell's indices span at most
+// kBitmapPasses * 2^19 values, a bitmap of one such window at a time in LDS
+// (s_keys): each index sets its bit, each thread counts the set bits of its
+// 16 words, a block scan of those counts gives every set bit its place, and
+// the bits are written out in order. Otherwise a bitonic sort in LDS.
+// Longer: ordered compaction, i.e. walk all particles in index order and
+// append those of this cell (the cell's membership is exact already; only
+// order changes). RECS: each sorted entry's record is copied from the input
+// particles.
 template <bool RECS>
-__global__ __launch_bounds__(kSortBlock) void sort_long_cells_kernel(
+__device__ __forceinline__ void sort_long_cells(
     const uint32_t* __restrict__ inicios, const uint32_t* __restrict__ celdaDe, uint32_t n,
-    const uint32_t* __restrict__ long_list, uint32_t long_cap,
-    const uint32_t* __restrict__ long_count, uint32_t* __restrict__ ordenado,
-    const uint4* __restrict__ particles, uint4* __restrict__ reordered) {
-  __shared__ uint32_t s_keys[kLdsSort];
-  __shared__ uint32_t s_wave[kSortBlock / 64];
-  uint32_t count = *long_count;
-  if (count > long_cap) count = long_cap;
-  for (uint32_t k = blockIdx.x; k < count; k += gridDim.x) {
+    const uint32_t* __restrict__ long_list, uint32_t count, uint32_t first, uint32_t stride,
+    uint32_t* __restrict__ ordenado, const uint4* __restrict__ particles, uint4* __restrict__ reordered,
+    uint32_t* s_keys, uint32_t* s_wave) {
+  for (uint32_t k = first; k < count; k += stride) {
     const uint32_t c = long_list[k];
     const uint32_t s = inicios[c];
     const uint32_t e = inicios[c + 1];
     if (e <= s || e > n) continue;  // uniform across the workgroup
     const uint32_t len = e - s;
     if (len <= kLdsSort) {
+      constexpr uint32_t kPer = kLdsSort / kSortBlock;  // entries (and bitmap words) per thread
+      constexpr uint32_t kWindow = kLdsSort * 32u;      // indices per bitmap window
+      uint32_t v[kPer];
+      uint32_t lo = 0xFFFFFFFFu, hi = 0;
+#pragma unroll
+      for (uint32_t q = 0; q < kPer; ++q) {
+        const uint32_t t = threadIdx.x + q * kSortBlock;
+        v[q] = (t < len) ? ordenado[s + t] : 0u;
+        if (t < len) {
+          lo = (v[q] < lo) ? v[q] : lo;
+          hi = (v[q] > hi) ? v[q] : hi;
+        }
+      }
+      lo = ~block_max<kSortBlock>(~lo, s_wave);
+      hi = block_max<kSortBlock>(hi, s_wave);
+      if (hi - lo < kBitmapPasses * kWindow) {  // len >= 1, so lo <= hi; uniform
+        uint32_t placed = 0;
+        for (uint64_t base = lo; base <= hi; base += kWindow) {
+#pragma unroll
+          for (uint32_t q = 0; q < kPer; ++q) s_keys[threadIdx.x * kPer + q] = 0u;
+          __syncthreads();
+#pragma unroll
+          for (uint32_t q = 0; q < kPer; ++q) {
+            const uint64_t off = static_cast<uint64_t>(v[q]) - base;
+            if (threadIdx.x + q * kSortBlock < len && v[q] >= base && off < kWindow)
+              atomicOr(&s_keys[off >> 5], 1u << (off & 31u));
+          }
+          __syncthreads();
+          uint32_t bits = 0;
+#pragma unroll
+          for (uint32_t q = 0; q < kPer; ++q) bits += __popc(s_keys[threadIdx.x * kPer + q]);
+          uint32_t total;
+          uint32_t pos = placed + block_exclusive_sum<kSortBlock>(bits, s_wave, &total);
+#pragma unroll 1
+          for (uint32_t q = 0; q < kPer; ++q) {
+            uint32_t w = s_keys[threadIdx.x * kPer + q];
+            while (w != 0u) {
+              const uint32_t idx = static_cast<uint32_t>(base) + (threadIdx.x * kPer + q) * 32u + __builtin_ctz(w);
+              w &= w - 1u;
+              if (pos < len) {
+                ordenado[s + pos] = idx;
+                if (RECS && idx < n) {
+                  reordered[2ull * (s + pos)] = particles[2ull * idx];
+                  reordered[2ull * (s + pos) + 1u] = particles[2ull * idx + 1u];
+                }
+              }
+              ++pos;
+            }
+          }
+          placed += total;
+          __syncthreads();  // this window's reads end before the next one is cleared
+        }
+        continue;
+      }
       uint32_t L = 1;
       while (L < len) L <<= 1;
       for (uint32_t t = threadIdx.x; t < L; t += kSortBlock)
@@ -208,7 +256,7 @@ __global__ __launch_bounds__(kSortBlock) void sort_long_cells_kernel(
       for (uint32_t kk = 2; kk <= L; kk <<= 1) {
         for (uint32_t j = kk >> 1; j > 0; j >>= 1) {
           for (uint32_t t = threadIdx.x; t < (L >> 1); t += kSortBlock) {
-            const uint32_t i = (t / j) * (2 * j) + (t % j);
+            const uint32_t i = ((t & ~(j - 1u)) << 1) | (t & (j - 1u));  // j is a power of two
             const uint32_t l = i + j;
             const bool up = (i & kk) == 0;
             const uint32_t a = s_keys[i], b = s_keys[l];
@@ -247,6 +295,85 @@ __global__ __launch_bounds__(kSortBlock) void sort_long_cells_kernel(
         run += total;
       }
     }
+  }
+}
+
+// The long-cell pass of the direct path: one workgroup per listed cell.
+template <bool RECS>
+__global__ __launch_bounds__(kSortBlock) void sort_long_cells_kernel(
+    const uint32_t* __restrict__ inicios, const uint32_t* __restrict__ celdaDe, uint32_t n,
+    const uint32_t* __restrict__ long_list, uint32_t long_cap,
+    const uint32_t* __restrict__ long_count, uint32_t* __restrict__ ordenado,
+    const uint4* __restrict__ particles, uint4* __restrict__ reordered) {
+  __shared__ uint32_t s_keys[kLdsSort];
+  __shared__ uint32_t s_wave[kSortBlock / 64];
+  uint32_t count = *long_count;
+  if (count > long_cap) count = long_cap;
+  sort_long_cells<RECS>(inicios, celdaDe, n, long_list, count, blockIdx.x, gridDim.x, ordenado, particles,
+                        reordered, s_keys, s_wave);
+}
+
+// Stable mode on the tile paths: the one pass over the cells the tile
+// kernel left in arrival order (FixLists). Workgroups below long_blocks
+// sort the long cells as above; every wave of the others takes whole cells
+// of the short list (at most kRankSortMax entries): the cell's indices go
+// to the wave's LDS slice, each lane counts the indices below its own
+// (distinct, so that count is its place) and writes it there, with its
+// record read from the input. LDS is shared by the two roles.
+template <bool RECS>
+__global__ __launch_bounds__(kSortBlock) void fix_cells_kernel(
+    const uint32_t* __restrict__ inicios, const uint32_t* __restrict__ celdaDe, uint32_t n, FixLists fl,
+    uint32_t long_blocks, uint32_t* __restrict__ ordenado, const uint4* __restrict__ particles,
+    uint4* __restrict__ reordered) {
+  constexpr uint32_t kWaves = kSortBlock / 64;
+  static_assert(kWaves * kRankSortMax <= kLdsSort, "one slice per wave fits the long-cell buffer");
+  static_assert(kRankSortMax % 4 == 0, "slices are read four entries at a time");
+  __shared__ __align__(16) uint32_t s_keys[kLdsSort];  // slices read as uint4
+  __shared__ uint32_t s_wave[kWaves];
+  if (blockIdx.x < long_blocks) {
+    uint32_t count = fl.counts()[1];
+    if (count > fl.long_cap) count = fl.long_cap;
+    sort_long_cells<RECS>(inicios, celdaDe, n, fl.lng(), count, blockIdx.x, long_blocks, ordenado, particles,
+                          reordered, s_keys, s_wave);
+    return;
+  }
+  const uint32_t lane = threadIdx.x & 63u;
+  uint32_t* slice = s_keys + (threadIdx.x >> 6) * kRankSortMax;
+  uint32_t count = fl.counts()[0];
+  if (count > fl.fix_cap) count = fl.fix_cap;
+  const uint32_t stride = (gridDim.x - long_blocks) * kWaves;
+  for (uint32_t k = (blockIdx.x - long_blocks) * kWaves + (threadIdx.x >> 6); k < count; k += stride) {
+    const uint32_t c = fl.fix()[k];
+    const uint32_t s = inicios[c];
+    const uint32_t e = inicios[c + 1];
+    if (e <= s || e > n || e - s > kRankSortMax) continue;  // uniform across the wave
+    const uint32_t len = e - s, len4 = (len + 3u) & ~3u;
+    // all ones pads the slice: no index reaches it
+    for (uint32_t q = lane; q < len4; q += 64u) slice[q] = (q < len) ? ordenado[s + q] : 0xFFFFFFFFu;
+    // a wave's LDS accesses complete in order: the slice is whole for
+    // every lane after this point
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (uint32_t g = 0; g < len; g += 64u) {
+      const uint32_t q = g + lane;
+      const uint32_t mine = (q < len) ? slice[q] : 0xFFFFFFFFu;
+      uint32_t rank = 0;
+      for (uint32_t j = 0; j < len4; j += 4u) {
+        const uint4 v = *reinterpret_cast<const uint4*>(slice + j);
+        rank += (v.x < mine ? 1u : 0u) + (v.y < mine ? 1u : 0u) + (v.z < mine ? 1u : 0u) + (v.w < mine ? 1u : 0u);
+      }
+      if (q < len) {
+        ordenado[s + rank] = mine;
+        if (RECS && mine < n) {
+          reordered[2ull * (s + rank)] = particles[2ull * mine];
+          reordered[2ull * (s + rank) + 1u] = particles[2ull * mine + 1u];
+        }
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();  // every read of the slice before the next cell's writes
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 }
 

@@ -48,7 +48,6 @@ constexpr uint32_t kStagedMaxTiles = 512;
 constexpr uint32_t kStagedMaxChunks = 1024;
 constexpr int kStagedRegs = 8;                      // particles per tile_sort thread in registers
 constexpr uint32_t kShortRun = 64;                  // longest chunk run a thread expands by itself
-constexpr uint32_t kCellSortMax = 32;               // longest cell a tile sorts itself in stable mode
 
 // Geometry the host uses (chosen by measurement on MI355X, 1M particles on
 // 128^3 cells: runs of 8+ records per chunk and tile keep tile_sort's loads
@@ -70,25 +69,6 @@ __device__ __forceinline__ uint32_t tile_of_block(uint32_t b, uint32_t ntiles) {
   return (b % 8) * (ntiles / 8) + b / 8;
 }
 
-// Sorts one cell's staged slice by particle index, carrying each entry's
-// staging slot: keys[0..len) and perm[0..len) in LDS (perm holds the
-// identity on entry), 2 <= len <= kCellSortMax. Insertion sort in LDS: a few
-// steps for the usual cell of two or three, no registers held. Particle
-// indices are distinct, so the order is the stable one.
-__device__ __forceinline__ void sort_cell_in_lds(uint32_t* keys, uint32_t* perm, uint32_t len) {
-  for (uint32_t i = 1; i < len; ++i) {
-    const uint32_t key = keys[i], pv = perm[i];
-    uint32_t j = i;
-    while (j > 0 && keys[j - 1] > key) {
-      keys[j] = keys[j - 1];
-      perm[j] = perm[j - 1];
-      --j;
-    }
-    keys[j] = key;
-    perm[j] = pv;
-  }
-}
-
 // chunk_sort: CT threads, chunk b holds particles [b*chunk, (b+1)*chunk)
 // with chunk = CT * kChunkItems.
 // rows[b*ntiles + t] = {particles of chunk b in tile t, those in tiles < t}.
@@ -96,7 +76,7 @@ template <int CT>
 __global__ __launch_bounds__(CT) void staged_keys_kernel(
     const uint4* __restrict__ parts, uint32_t n, GridParams g, uint32_t* __restrict__ celdaDe,
     uint2* __restrict__ rows, uint32_t tile_shift, uint32_t ntiles, uint4* __restrict__ chunk_rec,
-    uint32_t* __restrict__ chunk_idx, uint32_t* __restrict__ diag, uint32_t* __restrict__ fix_count) {
+    uint32_t* __restrict__ chunk_idx, uint32_t* __restrict__ diag, uint32_t* __restrict__ fix_counts) {
   constexpr int kChunkThreads = CT;
   constexpr uint32_t kChunk = CT * kChunkItems;
   constexpr uint32_t kTilesPerThread = kStagedMaxTiles / CT;  // tile bins per thread
@@ -109,7 +89,7 @@ __global__ __launch_bounds__(CT) void staged_keys_kernel(
   for (uint32_t t = threadIdx.x; t < kStagedMaxTiles; t += kChunkThreads) s_hist[t] = 0u;
   // the overflow diagnostics (when asked for) accumulate in tile_sort
   if (diag != nullptr && blockIdx.x == 0 && threadIdx.x < 2) diag[threadIdx.x] = 0u;
-  if (fix_count != nullptr && blockIdx.x == 0 && threadIdx.x == 0) *fix_count = 0u;  // stable fix-up list
+  if (fix_counts != nullptr && blockIdx.x == 0 && threadIdx.x < 2) fix_counts[threadIdx.x] = 0u;  // stable fix-up lists
   const uint32_t base = blockIdx.x * kChunk;
   // the records stay in registers (scalar arrays, static indices) until
   // they are placed in LDS in tile order
@@ -191,21 +171,18 @@ __global__ __launch_bounds__(CT) void staged_keys_kernel(
 // (diag[0] max occupancy, diag[1] overflowing insertions over capacity cap;
 // both zeroed by the kernel before this one).
 // STABLE: every cell lists its particles in ascending index order (page
-// "Construir el índice...", section "El orden dentro de la celda"). Cells
-// that lie wholly inside a staging window are sorted in LDS before the
-// window is written (windows end on cell boundaries); a cell longer than
-// kCellSortMax or than a window, and every multi-particle cell of a tile
-// past the staged capacity, is written in arrival order and appended to
-// fix_list (fix_count zeroed by the kernel before this one) for the fix-up
-// pass.
+// "Construir el índice...", section "El orden dentro de la celda"). Each
+// particle of a cell of up to kRankSortMax counts the cell's smaller
+// particle indices, which is its place in that order, and is staged there.
+// A longer cell, and every multi-particle cell of a tile past the staged
+// capacity, is written in arrival order and put on one of the fix-up lists.
 template <bool MOVE, bool DIAG, bool STABLE, uint32_t SHIFT, int NT, uint32_t WIN>
 __global__ __launch_bounds__(NT) void staged_cells_kernel(
     const uint2* __restrict__ rows, uint32_t nchunks, uint32_t chunk, uint32_t ntiles, GridParams g,
     uint32_t cells, uint32_t n, const uint4* __restrict__ chunk_rec,
     const uint32_t* __restrict__ chunk_idx, uint32_t* __restrict__ conteos,
     uint32_t* __restrict__ inicios, uint32_t* __restrict__ ordenado, uint4* __restrict__ dst,
-    uint32_t cap, uint32_t* __restrict__ diag, uint32_t* __restrict__ fix_list, uint32_t fix_cap,
-    uint32_t* __restrict__ fix_count) {
+    uint32_t cap, uint32_t* __restrict__ diag, FixLists fl) {
   constexpr uint32_t kTileCells = 1u << SHIFT;
   // cells per thread in the scan (tiles smaller than the workgroup: one
   // cell for each of the first kTileCells threads)
@@ -216,7 +193,7 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
   static_assert(kTileCells < NT || kTileCells % NT == 0, "whole cells per thread");
   static_assert(SHIFT >= 2, "tiles start on 16-byte boundaries of conteos and inicios");
   static_assert(kStagedMaxChunks % NT == 0, "whole chunk rows per thread");
-  static_assert(2 * WIN * 4 >= kStagedCap, "the source map fits in the staging buffer");
+  static_assert(2 * WIN * 4 >= kStagedCap, "the source map (and, stable, every index) fits in the staging buffer");
   __shared__ uint32_t s_cnt[kTileCells];
   __shared__ uint32_t s_dst[kStagedMaxChunks];  // tile-local start of each chunk's run
   __shared__ uint32_t s_src[kStagedMaxChunks];  // where that run starts in the chunk array
@@ -225,7 +202,7 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
   __shared__ uint32_t s_wave[NT / 64];
   __shared__ uint32_t s_runmax[NT / 64];
   __shared__ uint32_t s_dm[DIAG ? NT / 64 : 1], s_do[DIAG ? NT / 64 : 1];
-  __shared__ uint32_t s_perm[STABLE ? WIN : 1];  // stable: window slot -> staged slot
+  __shared__ uint32_t s_any_long;  // stable: some cell of the tile is longer than kRankSortMax
 
   const uint32_t t = tile_of_block(blockIdx.x, ntiles);
   const uint32_t cell0 = t << SHIFT;
@@ -337,13 +314,13 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
     const bool scans = j0 < kTileCells;
     uint32_t sum = 0;
     if (scans) {
-#pragma unroll
+#pragma unroll 4
       for (uint32_t q = 0; q < kPer; ++q) sum += s_cnt[j0 + q];
     }
     uint32_t tot;
     uint32_t run = block_exclusive_sum<NT>(sum, s_wave, &tot);
     if (scans) {
-#pragma unroll
+#pragma unroll 4
       for (uint32_t q = 0; q < kPer; ++q) {
         const uint32_t v = s_cnt[j0 + q];
         s_cnt[j0 + q] = run;
@@ -446,20 +423,44 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
 #pragma unroll
     for (int k = 0; k < kStagedRegs; ++k)
       slot[k] = (lr[k] != 0xFFFFFFFFu) ? s_cnt[lr[k] >> 16] + (lr[k] & 0xFFFFu) : 0xFFFFFFFFu;
-    uint32_t w0 = 0;
-    while (w0 < count) {  // tile-uniform
-      uint32_t w1 = (count - w0 <= kStagedWin) ? count : w0 + kStagedWin;
-      if (STABLE && w1 < count) {
-        // end the window at the last cell start within reach (the starts in
-        // s_cnt never decrease); if that is w0, one cell spans the window
-        uint32_t lo = 0, hi = kTileCells - 1u;
-        while (lo < hi) {
-          const uint32_t mid = (lo + hi + 1u) >> 1;
-          if (s_cnt[mid] <= w1) lo = mid; else hi = mid - 1u;
+    if (STABLE) {
+      // every index at its arrival slot (the source map is dead: s_rec is
+      // free); then each particle of a cell of up to kRankSortMax counts
+      // the cell's smaller indices (distinct), which is its place in index
+      // order. A longer cell keeps the arrival order and is listed.
+      uint32_t* s_all = reinterpret_cast<uint32_t*>(s_rec);
+#pragma unroll
+      for (int k = 0; k < kStagedRegs; ++k)
+        if (slot[k] != 0xFFFFFFFFu) s_all[slot[k]] = idx[k];
+      if (threadIdx.x == 0) s_any_long = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < kStagedRegs; ++k) {
+        if (slot[k] != 0xFFFFFFFFu) {
+          const uint32_t loc = lr[k] >> 16;
+          const uint32_t a = s_cnt[loc];
+          const uint32_t e = (loc + 1u < kTileCells) ? s_cnt[loc + 1u] : tot;
+          if (e - a <= kRankSortMax) {
+            uint32_t pos = a;
+            for (uint32_t j = a; j < e; ++j) pos += (s_all[j] < idx[k]) ? 1u : 0u;
+            slot[k] = pos;
+          } else {
+            s_any_long = 1u;
+          }
         }
-        if (s_cnt[lo] > w0) w1 = s_cnt[lo];
       }
-      const uint32_t wn = w1 - w0;
+      __syncthreads();  // every rank counted before the window loop reuses s_rec
+      if (s_any_long != 0u) {
+        for (uint32_t j0 = 0; j0 < tc; j0 += NT) {  // whole waves: the listing is per wave
+          const uint32_t j = j0 + threadIdx.x;
+          const uint32_t a = (j < tc) ? s_cnt[j] : 0u;
+          const uint32_t e = (j < tc) ? ((j + 1u < kTileCells) ? s_cnt[j + 1u] : tot) : 0u;
+          list_cells_wave(fl, cell0 + j, e - a, e - a > kRankSortMax);
+        }
+      }
+    }
+    for (uint32_t w0 = 0; w0 < count; w0 += kStagedWin) {  // tile-uniform
+      const uint32_t wn = (count - w0 < kStagedWin) ? count - w0 : kStagedWin;
 #pragma unroll
       for (int k = 0; k < kStagedRegs; ++k) {
         const uint32_t o = slot[k] - w0;
@@ -471,34 +472,15 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
           s_idx[o] = idx[k];
         }
       }
-      if (STABLE) {
-        for (uint32_t q = threadIdx.x; q < wn; q += NT) s_perm[q] = q;
-        __syncthreads();
-        // each cell starting in this window: sorted here if it fits, listed otherwise
-        for (uint32_t j = threadIdx.x; j < tc; j += NT) {
-          const uint32_t a = s_cnt[j];
-          const uint32_t e = (j + 1u < kTileCells) ? s_cnt[j + 1u] : tot;
-          if (a < w0 || a >= w1 || e - a < 2u) continue;
-          if (e > w1 || e - a > kCellSortMax) {
-            const uint32_t f = atomicAdd(fix_count, 1u);
-            if (f < fix_cap) fix_list[f] = cell0 + j;
-            continue;
-          }
-          sort_cell_in_lds(s_idx + (a - w0), s_perm + (a - w0), e - a);
-        }
-      }
       __syncthreads();
       const size_t out0 = static_cast<size_t>(bs) + w0;
       for (uint32_t q = threadIdx.x; q < wn; q += NT)
         if (out0 + q < n) ordenado[out0 + q] = s_idx[q];
       if (MOVE) {
-        for (uint32_t q = threadIdx.x; q < 2 * wn; q += NT) {
-          const uint32_t from = STABLE ? 2u * s_perm[q >> 1] + (q & 1u) : q;
-          if (out0 * 2u + q < 2ull * n) dst[out0 * 2u + q] = s_rec[from];
-        }
+        for (uint32_t q = threadIdx.x; q < 2 * wn; q += NT)
+          if (out0 * 2u + q < 2ull * n) dst[out0 * 2u + q] = s_rec[q];
       }
       __syncthreads();
-      w0 = w1;
     }
   } else {
     // a tile past the staged capacity (count > kStagedCap > 0): rounds of
@@ -576,14 +558,13 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
     }
     if (STABLE) {
       // slots were taken in arrival order: every cell of two or more is
-      // fixed up afterwards. Once every cursor is final it holds its cell's
-      // end, so a cell's count is its end minus the previous cell's.
+      // listed. Once every cursor is final it holds its cell's end, so a
+      // cell's count is its end minus the previous cell's.
       __syncthreads();
-      for (uint32_t j = threadIdx.x; j < tc; j += NT) {
-        if (s_cnt[j] - (j ? s_cnt[j - 1u] : 0u) >= 2u) {
-          const uint32_t f = atomicAdd(fix_count, 1u);
-          if (f < fix_cap) fix_list[f] = cell0 + j;
-        }
+      for (uint32_t j0 = 0; j0 < tc; j0 += NT) {  // whole waves: the listing is per wave
+        const uint32_t j = j0 + threadIdx.x;
+        const uint32_t len = (j < tc) ? s_cnt[j] - (j ? s_cnt[j - 1u] : 0u) : 0u;
+        list_cells_wave(fl, cell0 + j, len, len >= 2u);
       }
     }
   }

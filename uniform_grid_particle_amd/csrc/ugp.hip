@@ -81,7 +81,7 @@ struct Plan {
   size_t off_long_count = 0, off_long = 0, off_unstable = 0;
   // stable mode on the tile paths: cells the tile kernel could not sort
   uint32_t fix_cap = 0;
-  size_t off_fix_count = 0, off_fix = 0;
+  size_t off_fix = 0;
   size_t total = 256;
 };
 
@@ -184,24 +184,23 @@ int make_plan(uint32_t n, const uint32_t dims[3], uint32_t flags, Plan* p) {
     off = align_up(off + (static_cast<size_t>(p->nbins) + kCounterWords) * 4u, 256);
   }
   if (p->stable) {
+    // cells longer than kSmallSort (direct path) or kRankSortMax (tile paths)
     const uint64_t cap = static_cast<uint64_t>(n) / (kSmallSort + 1) + 1;
     p->long_cap = static_cast<uint32_t>(cap < cells ? cap : cells);
-    p->off_long_count = off;
-    off = align_up(off + 4u, 256);
-    p->off_long = off;
-    off = align_up(off + static_cast<size_t>(p->long_cap) * 4u, 256);
     if (p->path == Path::kDirect) {
+      p->off_long_count = off;
+      off = align_up(off + 4u, 256);
+      p->off_long = off;
+      off = align_up(off + static_cast<size_t>(p->long_cap) * 4u, 256);
       if (p->move) {  // the scatter kernel's records, in arrival order
         p->off_unstable = off;
         off = align_up(off + static_cast<size_t>(n) * 32u, 256);
       }
-    } else {  // at most one entry per cell of two or more particles
+    } else {  // FixLists: header, short list (one entry per cell of two or more), long list
       const uint64_t fcap = static_cast<uint64_t>(n) / 2 + 1;
       p->fix_cap = static_cast<uint32_t>(fcap < cells ? fcap : cells);
-      p->off_fix_count = off;
-      off = align_up(off + 4u, 256);
       p->off_fix = off;
-      off = align_up(off + static_cast<size_t>(p->fix_cap) * 4u, 256);
+      off = align_up(off + (static_cast<size_t>(kFixHeader) + p->fix_cap + p->long_cap) * 4u, 256);
     }
   }
   p->total = off ? off : 256;
@@ -319,10 +318,10 @@ void launch_staged_cells_at(dim3 grid, hipStream_t s, const uint2* rows, uint32_
                             uint32_t ntiles, GridParams g, uint32_t cells, uint32_t n,
                             const uint4* chunk_rec, const uint32_t* chunk_idx, uint32_t* conteos,
                             uint32_t* inicios, uint32_t* ordenado, uint4* dst, uint32_t cap,
-                            uint32_t* diag, uint32_t* fix, uint32_t fix_cap, uint32_t* fix_count) {
+                            uint32_t* diag, FixLists fl) {
   hipLaunchKernelGGL((staged_cells_kernel<MOVE, DIAG, STABLE, SHIFT, kCellsThreads, kCellsWin>), grid,
                      dim3(kCellsThreads), 0, s, rows, nchunks, kChunk, ntiles, g, cells, n, chunk_rec,
-                     chunk_idx, conteos, inicios, ordenado, dst, cap, diag, fix, fix_cap, fix_count);
+                     chunk_idx, conteos, inicios, ordenado, dst, cap, diag, fl);
 }
 
 template <bool MOVE, bool DIAG, bool STABLE>
@@ -330,13 +329,12 @@ void launch_staged_cells(uint32_t shift, dim3 grid, hipStream_t s, const uint2* 
                          uint32_t nchunks, uint32_t ntiles, GridParams g, uint32_t cells,
                          uint32_t n, const uint4* chunk_rec, const uint32_t* chunk_idx,
                          uint32_t* conteos, uint32_t* inicios, uint32_t* ordenado, uint4* dst,
-                         uint32_t cap, uint32_t* diag, uint32_t* fix, uint32_t fix_cap,
-                         uint32_t* fix_count) {
+                         uint32_t cap, uint32_t* diag, FixLists fl) {
 #define UGP_STAGED_CASE(S)                                                                            \
   case S:                                                                                             \
     launch_staged_cells_at<MOVE, DIAG, STABLE, S>(grid, s, rows, nchunks, ntiles, g, cells, n,         \
                                                   chunk_rec, chunk_idx, conteos, inicios, ordenado,   \
-                                                  dst, cap, diag, fix, fix_cap, fix_count);           \
+                                                  dst, cap, diag, fl);                            \
     break;
   switch (shift) {
     UGP_STAGED_CASE(4)
@@ -352,7 +350,7 @@ void launch_staged_cells(uint32_t shift, dim3 grid, hipStream_t s, const uint2* 
     default:
       launch_staged_cells_at<MOVE, DIAG, STABLE, 14>(grid, s, rows, nchunks, ntiles, g, cells, n,
                                                      chunk_rec, chunk_idx, conteos, inicios, ordenado,
-                                                     dst, cap, diag, fix, fix_cap, fix_count);
+                                                     dst, cap, diag, fl);
       break;
   }
 #undef UGP_STAGED_CASE
@@ -380,52 +378,54 @@ uint4* record_dst(const BuildArgs& a, const Plan& p) {
   return reinterpret_cast<uint4*>(a.reordered);
 }
 
-// the stable fix-up list of the tile paths (nullptr otherwise)
-uint32_t* fix_count_of(const BuildArgs& a, const Plan& p) {
-  if (!p.stable || p.path == Path::kDirect) return nullptr;
-  return reinterpret_cast<uint32_t*>(static_cast<char*>(a.workspace) + p.off_fix_count);
+// the stable fix-up lists of the tile paths (null otherwise)
+FixLists fix_lists_of(const BuildArgs& a, const Plan& p) {
+  FixLists fl{};
+  if (!p.stable || p.path == Path::kDirect) return fl;
+  fl.base = reinterpret_cast<uint32_t*>(static_cast<char*>(a.workspace) + p.off_fix);
+  fl.fix_cap = p.fix_cap;
+  fl.long_cap = p.long_cap;
+  return fl;
 }
 
 // Stable-order and gather passes, shared by every path.
 void enqueue_stable_sort(const BuildArgs& a, const Plan& p, char* ws) {
+  const uint4* parts = reinterpret_cast<const uint4*>(a.particles);
+  uint4* out = p.move ? reinterpret_cast<uint4*>(a.reordered) : nullptr;
+  if (p.path != Path::kDirect) {
+    // the tile kernel put every cell it could in order and listed the rest
+    // (list lengths zeroed by the build's first kernel): one pass over them,
+    // records read from the input by particle index
+    const FixLists fl = fix_lists_of(a, p);
+    const uint32_t long_blocks = (p.long_cap < kFixLongBlocks) ? p.long_cap : kFixLongBlocks;
+    const uint32_t short_blocks = blocks_for(p.fix_cap, kSortBlock / 64);
+    const dim3 grid(long_blocks + ((short_blocks < kFixShortBlocks) ? short_blocks : kFixShortBlocks));
+    if (p.move)
+      hipLaunchKernelGGL(fix_cells_kernel<true>, grid, dim3(kSortBlock), 0, a.stream, a.inicios, a.celdaDe,
+                         a.n, fl, long_blocks, a.ordenado, parts, out);
+    else
+      hipLaunchKernelGGL(fix_cells_kernel<false>, grid, dim3(kSortBlock), 0, a.stream, a.inicios, a.celdaDe,
+                         a.n, fl, long_blocks, a.ordenado, nullptr, nullptr);
+    return;
+  }
   uint32_t* long_count = reinterpret_cast<uint32_t*>(ws + p.off_long_count);
   uint32_t* long_list = reinterpret_cast<uint32_t*>(ws + p.off_long);
   const uint32_t cells = static_cast<uint32_t>(p.cells);
   launch_clear(long_count, 1, nullptr, 0, a.stream);
-  const uint4* parts = reinterpret_cast<const uint4*>(a.particles);
-  uint4* out = p.move ? reinterpret_cast<uint4*>(a.reordered) : nullptr;
-  if (p.path != Path::kDirect) {
-    // the tile kernel sorted every cell it could; fix up the listed ones,
-    // taking their records from the input by particle index
-    const uint32_t* fix = reinterpret_cast<const uint32_t*>(ws + p.off_fix);
-    const uint32_t* fix_count = reinterpret_cast<const uint32_t*>(ws + p.off_fix_count);
-    const dim3 grid(blocks_for(p.fix_cap, kBlock));
-    if (p.move)
-      hipLaunchKernelGGL((sort_short_cells_kernel<true, true>), grid, dim3(kBlock), 0, a.stream, a.inicios,
-                         cells, a.n, a.ordenado, long_list, p.long_cap, long_count, parts, out, fix,
-                         fix_count, p.fix_cap);
-    else
-      hipLaunchKernelGGL((sort_short_cells_kernel<false, true>), grid, dim3(kBlock), 0, a.stream, a.inicios,
-                         cells, a.n, a.ordenado, long_list, p.long_cap, long_count, nullptr, nullptr, fix,
-                         fix_count, p.fix_cap);
-  } else {
-    const dim3 grid(blocks_for(cells, kBlock));
-    if (p.move)
-      hipLaunchKernelGGL((sort_short_cells_kernel<true, false>), grid, dim3(kBlock), 0, a.stream, a.inicios,
-                         cells, a.n, a.ordenado, long_list, p.long_cap, long_count,
-                         reinterpret_cast<const uint4*>(ws + p.off_unstable), out, nullptr, nullptr, 0u);
-    else
-      hipLaunchKernelGGL((sort_short_cells_kernel<false, false>), grid, dim3(kBlock), 0, a.stream, a.inicios,
-                         cells, a.n, a.ordenado, long_list, p.long_cap, long_count, nullptr, nullptr, nullptr,
-                         nullptr, 0u);
-  }
-  if (p.move)
+  const dim3 grid(blocks_for(cells, kBlock));
+  if (p.move) {
+    hipLaunchKernelGGL(sort_short_cells_kernel<true>, grid, dim3(kBlock), 0, a.stream, a.inicios, cells, a.n,
+                       a.ordenado, long_list, p.long_cap, long_count,
+                       reinterpret_cast<const uint4*>(ws + p.off_unstable), out);
     hipLaunchKernelGGL(sort_long_cells_kernel<true>, dim3(kSortGrid), dim3(kSortBlock), 0, a.stream,
                        a.inicios, a.celdaDe, a.n, long_list, p.long_cap, long_count, a.ordenado, parts, out);
-  else
+  } else {
+    hipLaunchKernelGGL(sort_short_cells_kernel<false>, grid, dim3(kBlock), 0, a.stream, a.inicios, cells, a.n,
+                       a.ordenado, long_list, p.long_cap, long_count, nullptr, nullptr);
     hipLaunchKernelGGL(sort_long_cells_kernel<false>, dim3(kSortGrid), dim3(kSortBlock), 0, a.stream,
                        a.inicios, a.celdaDe, a.n, long_list, p.long_cap, long_count, a.ordenado, nullptr,
                        nullptr);
+  }
 }
 
 void enqueue_gather(const BuildArgs& a) {
@@ -443,14 +443,13 @@ void launch_tile_sort(const BuildArgs& a, const Plan& p, const uint2* rows, cons
   uint4* dst = record_dst(a, p);
   const dim3 grid(p.ntiles);
   hipStream_t s = a.stream;
-  uint32_t* fix_count = fix_count_of(a, p);
-  uint32_t* fix = fix_count ? reinterpret_cast<uint32_t*>(static_cast<char*>(a.workspace) + p.off_fix) : nullptr;
+  const FixLists fl = fix_lists_of(a, p);
   const GridParams g = grid_params(a);
   // one instantiation per (moves records, diagnostics, stable order)
 #define UGP_TILE_SORT(M, D, S)                                                                       \
   launch_staged_cells<M, D, S>(p.tile_shift, grid, s, rows, p.nchunks, p.ntiles, g, cells, a.n, rec, \
                                idx, a.conteos, a.inicios, a.ordenado, dst, D ? a.capacity : 0u,     \
-                               D ? a.diag : nullptr, fix, p.fix_cap, fix_count)
+                               D ? a.diag : nullptr, fl)
   const bool m = p.move, d = a.diag != nullptr, st = p.stable;
   if (m && d && st) UGP_TILE_SORT(true, true, true);
   else if (m && d) UGP_TILE_SORT(true, true, false);
@@ -474,7 +473,7 @@ void enqueue_staged(uint32_t stage, const BuildArgs& a, const Plan& p) {
       hipLaunchKernelGGL(staged_keys_kernel<kChunkThreads>, dim3(p.nchunks), dim3(kChunkThreads), 0, s,
                          reinterpret_cast<const uint4*>(a.particles), a.n, grid_params(a),
                          a.celdaDe, rows, p.tile_shift, p.ntiles, chunk_rec, chunk_idx, a.diag,
-                         fix_count_of(a, p));
+                         fix_lists_of(a, p).base);
       break;
     case 3:
       launch_tile_sort(a, p, rows, chunk_rec, chunk_idx);
@@ -502,7 +501,7 @@ void enqueue_bucketed(uint32_t stage, const BuildArgs& a, const Plan& p) {
     case 0:
       hipLaunchKernelGGL(bucket_keys_kernel, dim3(p.nblk), dim3(kBucketThreads), 0, s,
                          reinterpret_cast<const uint4*>(a.particles), a.n, p.per_block, grid_params(a),
-                         a.celdaDe, hist, p.tile_shift, p.ntiles, a.diag, fix_count_of(a, p));
+                         a.celdaDe, hist, p.tile_shift, p.ntiles, a.diag, fix_lists_of(a, p).base);
       break;
     case 1:
       hipLaunchKernelGGL(bucket_colscan_kernel, dim3(p.ntiles), dim3(kBlock), 0, s, hist, p.nblk,
