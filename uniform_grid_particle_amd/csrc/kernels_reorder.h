@@ -10,9 +10,10 @@ constexpr uint32_t kSmallSort = 16;  // cells up to this length are sorted in re
 constexpr int kSortBlock = 1024;     // threads of the long-cell sort
 constexpr uint32_t kLdsSort = 16384; // longest cell sorted in LDS (64 KiB)
 constexpr int kSortGrid = 512;       // workgroups of the long-cell sort
+constexpr uint32_t kRecBatch = 8;         // records gathered together by one thread (long cells)
 constexpr uint32_t kBitmapPasses = 4;     // bitmap windows a long cell may take (2^21 index values)
 constexpr uint32_t kFixLongBlocks = 128;   // fix-up workgroups on long cells
-constexpr uint32_t kFixShortBlocks = 256;  // fix-up workgroups on short cells, a wave per cell
+constexpr uint32_t kFixShortBlocks = 256;  // fix-up workgroups on short cells, 64 cells per wave at a time
 
 // Gather: two lanes per record, each moving one 16-byte half, so every
 // store instruction writes a contiguous span. Indices >= n_src are skipped.
@@ -103,11 +104,73 @@ __global__ __launch_bounds__(kBlock) void gather_arrays_kernel(const uint32_t* _
   }
 }
 
-// Stable mode, short cells: one thread per cell. Cells of at most 16
-// entries are sorted in registers with a bitonic network on (particle
+// One thread puts a cell of 2..kSmallSort entries (slice [s, s + len) of
+// ordenado) in index order: a bitonic network in registers on (particle
 // index, position in the slice) pairs (static indices, padding with all
-// ones, which no pair reaches); longer cells are appended to a list for the
-// LDS kernel. RECS: the scatter kernel left the records in `unstable` in the
+// ones, which no pair reaches). RECS: the records follow, read from `src`
+// by position in the slice (BY_INDEX false: src holds the slice's records
+// in its original order) or by particle index (BY_INDEX true: src is the
+// input), BATCH records at a time.
+template <bool RECS, bool BY_INDEX, uint32_t BATCH>
+__device__ __forceinline__ void sort_cell_in_registers(uint32_t s, uint32_t len, uint32_t n,
+                                                       uint32_t* __restrict__ ordenado,
+                                                       const uint4* __restrict__ src,
+                                                       uint4* __restrict__ reordered) {
+  uint64_t v[kSmallSort];
+#pragma unroll
+  for (uint32_t k = 0; k < kSmallSort; ++k)
+    v[k] = (k < len) ? (static_cast<uint64_t>(ordenado[s + k]) << 32) | k : ~0ull;
+#pragma unroll
+  for (uint32_t kk = 2; kk <= kSmallSort; kk <<= 1) {
+#pragma unroll
+    for (uint32_t j = kk >> 1; j > 0; j >>= 1) {
+#pragma unroll
+      for (uint32_t i = 0; i < kSmallSort; ++i) {
+        const uint32_t l = i ^ j;
+        if (l > i) {
+          const bool up = (i & kk) == 0;
+          const uint64_t a = v[i], b = v[l];
+          if ((a > b) == up) {
+            v[i] = b;
+            v[l] = a;
+          }
+        }
+      }
+    }
+  }
+  // records BATCH at a time: a batch's loads are all in flight before
+  // its stores (one wait per batch, not per record)
+#pragma unroll
+  for (uint32_t k0 = 0; k0 < kSmallSort; k0 += BATCH) {
+    uint4 ra[BATCH], rb[BATCH];
+#pragma unroll
+    for (uint32_t j = 0; j < BATCH; ++j) ra[j] = rb[j] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (uint32_t j = 0; j < BATCH; ++j) {
+      const uint32_t k = k0 + j, idx = static_cast<uint32_t>(v[k] >> 32);
+      if (RECS && k < len && (!BY_INDEX || idx < n)) {
+        const size_t from = BY_INDEX ? 2ull * idx : 2ull * (s + static_cast<uint32_t>(v[k] & 0xFFFFFFFFu));
+        ra[j] = src[from];
+        rb[j] = src[from + 1u];
+      }
+    }
+#pragma unroll
+    for (uint32_t j = 0; j < BATCH; ++j) {
+      const uint32_t k = k0 + j, idx = static_cast<uint32_t>(v[k] >> 32);
+      if (k < len) {
+        ordenado[s + k] = idx;
+        if (RECS && (!BY_INDEX || idx < n)) {
+          reordered[2ull * (s + k)] = ra[j];
+          reordered[2ull * (s + k) + 1u] = rb[j];
+        }
+      }
+    }
+  }
+}
+
+// Stable mode, short cells: one thread per cell. Cells of at most 16
+// entries are sorted in registers (sort_cell_in_registers); longer cells
+// are appended to a list for the LDS kernel. RECS: the scatter kernel left the records in `unstable` in the
 // slice's original order, and each short cell writes its records to
 // `reordered` in the sorted order (reads stay inside the cell's slice);
 // the long-cell kernel writes the records of long cells.
@@ -134,40 +197,41 @@ __global__ __launch_bounds__(kBlock) void sort_short_cells_kernel(
     }
     return;
   }
-  uint64_t v[kSmallSort];
+  sort_cell_in_registers<RECS, false, 4>(s, len, n, ordenado, unstable, reordered);
+}
+
+// The records of a long cell once its indices are in order: the workgroup
+// reads ordenado[s, s + len) back (its own writes, visible after the
+// barrier) and gathers kRecBatch records per thread at a time. Ends with a
+// barrier.
+__device__ __forceinline__ void copy_cell_records(uint32_t s, uint32_t len, uint32_t n,
+                                                  const uint32_t* __restrict__ ordenado,
+                                                  const uint4* __restrict__ particles,
+                                                  uint4* __restrict__ reordered) {
+  __syncthreads();
+  for (uint32_t t0 = threadIdx.x; t0 < len; t0 += kRecBatch * kSortBlock) {
+    uint32_t id[kRecBatch];
+    uint4 ra[kRecBatch], rb[kRecBatch];
 #pragma unroll
-  for (uint32_t k = 0; k < kSmallSort; ++k)
-    v[k] = (k < len) ? (static_cast<uint64_t>(ordenado[s + k]) << 32) | k : ~0ull;
+    for (uint32_t j = 0; j < kRecBatch; ++j) {
+      const uint32_t t = t0 + j * kSortBlock;
+      id[j] = (t < len) ? ordenado[s + t] : 0xFFFFFFFFu;
+      ra[j] = rb[j] = make_uint4(0u, 0u, 0u, 0u);
+      if (id[j] < n) {
+        ra[j] = particles[2ull * id[j]];
+        rb[j] = particles[2ull * id[j] + 1u];
+      }
+    }
 #pragma unroll
-  for (uint32_t kk = 2; kk <= kSmallSort; kk <<= 1) {
-#pragma unroll
-    for (uint32_t j = kk >> 1; j > 0; j >>= 1) {
-#pragma unroll
-      for (uint32_t i = 0; i < kSmallSort; ++i) {
-        const uint32_t l = i ^ j;
-        if (l > i) {
-          const bool up = (i & kk) == 0;
-          const uint64_t a = v[i], b = v[l];
-          if ((a > b) == up) {
-            v[i] = b;
-            v[l] = a;
-          }
-        }
+    for (uint32_t j = 0; j < kRecBatch; ++j) {
+      const uint32_t t = t0 + j * kSortBlock;
+      if (t < len && id[j] < n) {
+        reordered[2ull * (s + t)] = ra[j];
+        reordered[2ull * (s + t) + 1u] = rb[j];
       }
     }
   }
-#pragma unroll
-  for (uint32_t k = 0; k < kSmallSort; ++k) {
-    if (k < len) {
-      ordenado[s + k] = static_cast<uint32_t>(v[k] >> 32);
-      if (RECS) {
-        const size_t from = 2ull * (s + static_cast<uint32_t>(v[k] & 0xFFFFFFFFu));
-        const uint4 a = unstable[from], b = unstable[from + 1u];
-        reordered[2ull * (s + k)] = a;
-        reordered[2ull * (s + k) + 1u] = b;
-      }
-    }
-  }
+  __syncthreads();
 }
 
 // Stable mode, long cells: the workgroups first, first + stride, ... take
@@ -179,8 +243,8 @@ __global__ __launch_bounds__(kBlock) void sort_short_cells_kernel(
 // the bits are written out in order. Otherwise a bitonic sort in LDS.
 // Longer: ordered compaction, i.e. walk all particles in index order and
 // append those of this cell (the cell's membership is exact already; only
-// order changes). RECS: each sorted entry's record is copied from the input
-// particles.
+// order changes). Each way writes indices only; RECS: the records follow in
+// one pass over the ordered slice (copy_cell_records).
 template <bool RECS>
 __device__ __forceinline__ void sort_long_cells(
     const uint32_t* __restrict__ inicios, const uint32_t* __restrict__ celdaDe, uint32_t n,
@@ -222,6 +286,8 @@ __device__ __forceinline__ void sort_long_cells(
               atomicOr(&s_keys[off >> 5], 1u << (off & 31u));
           }
           __syncthreads();
+          // thread t owns bitmap words [t * kPer, (t + 1) * kPer) and writes
+          // their set bits, in order, from the place the block scan gives it
           uint32_t bits = 0;
 #pragma unroll
           for (uint32_t q = 0; q < kPer; ++q) bits += __popc(s_keys[threadIdx.x * kPer + q]);
@@ -230,22 +296,17 @@ __device__ __forceinline__ void sort_long_cells(
 #pragma unroll 1
           for (uint32_t q = 0; q < kPer; ++q) {
             uint32_t w = s_keys[threadIdx.x * kPer + q];
-            while (w != 0u) {
+            while (w != 0u) {  // stores only: nothing to wait for between bits
               const uint32_t idx = static_cast<uint32_t>(base) + (threadIdx.x * kPer + q) * 32u + __builtin_ctz(w);
               w &= w - 1u;
-              if (pos < len) {
-                ordenado[s + pos] = idx;
-                if (RECS && idx < n) {
-                  reordered[2ull * (s + pos)] = particles[2ull * idx];
-                  reordered[2ull * (s + pos) + 1u] = particles[2ull * idx + 1u];
-                }
-              }
+              if (pos < len) ordenado[s + pos] = idx;
               ++pos;
             }
           }
           placed += total;
           __syncthreads();  // this window's reads end before the next one is cleared
         }
+        if (RECS) copy_cell_records(s, len, n, ordenado, particles, reordered);
         continue;
       }
       uint32_t L = 1;
@@ -268,14 +329,8 @@ __device__ __forceinline__ void sort_long_cells(
           __syncthreads();
         }
       }
-      for (uint32_t t = threadIdx.x; t < len; t += kSortBlock) {
-        const uint32_t idx = s_keys[t];
-        ordenado[s + t] = idx;
-        if (RECS && idx < n) {
-          reordered[2ull * (s + t)] = particles[2ull * idx];
-          reordered[2ull * (s + t) + 1u] = particles[2ull * idx + 1u];
-        }
-      }
+      for (uint32_t t = threadIdx.x; t < len; t += kSortBlock) ordenado[s + t] = s_keys[t];
+      if (RECS) copy_cell_records(s, len, n, ordenado, particles, reordered);
       __syncthreads();
     } else {
       uint32_t run = 0;
@@ -285,15 +340,10 @@ __device__ __forceinline__ void sort_long_cells(
         uint32_t total;
         const uint32_t excl = block_exclusive_sum<kSortBlock>(flag, s_wave, &total);
         const uint32_t dst = s + run + excl;
-        if (flag && dst < e) {
-          ordenado[dst] = static_cast<uint32_t>(i);
-          if (RECS) {
-            reordered[2ull * dst] = particles[2u * i];
-            reordered[2ull * dst + 1u] = particles[2u * i + 1u];
-          }
-        }
+        if (flag && dst < e) ordenado[dst] = static_cast<uint32_t>(i);
         run += total;
       }
+      if (RECS) copy_cell_records(s, len, n, ordenado, particles, reordered);
     }
   }
 }
@@ -315,15 +365,17 @@ __global__ __launch_bounds__(kSortBlock) void sort_long_cells_kernel(
 
 // Stable mode on the tile paths: the one pass over the cells the tile
 // kernel left in arrival order (FixLists). Workgroups below long_blocks
-// sort the long cells as above; every wave of the others takes whole cells
-// of the short list (at most kRankSortMax entries): the cell's indices go
-// to the wave's LDS slice, each lane counts the indices below its own
-// (distinct, so that count is its place) and writes it there, with its
-// record read from the input. LDS is shared by the two roles.
+// sort the long cells as above; every wave of the others takes 64 entries
+// of the short list at a time (cells of at most kRankSortMax): a lane sorts
+// a cell of up to kSmallSort in registers; a longer one is taken by the
+// whole wave: its indices go to the wave's LDS slice, each lane counts the
+// indices below its own (distinct, so that count is its place) and writes
+// it there. Records are read from the input by index. LDS is shared by the
+// two roles.
 template <bool RECS>
 __global__ __launch_bounds__(kSortBlock) void fix_cells_kernel(
-    const uint32_t* __restrict__ inicios, const uint32_t* __restrict__ celdaDe, uint32_t n, FixLists fl,
-    uint32_t long_blocks, uint32_t* __restrict__ ordenado, const uint4* __restrict__ particles,
+    const uint32_t* __restrict__ inicios, const uint32_t* __restrict__ celdaDe, uint32_t cells, uint32_t n,
+    FixLists fl, uint32_t long_blocks, uint32_t* __restrict__ ordenado, const uint4* __restrict__ particles,
     uint4* __restrict__ reordered) {
   constexpr uint32_t kWaves = kSortBlock / 64;
   static_assert(kWaves * kRankSortMax <= kLdsSort, "one slice per wave fits the long-cell buffer");
@@ -341,33 +393,45 @@ __global__ __launch_bounds__(kSortBlock) void fix_cells_kernel(
   uint32_t* slice = s_keys + (threadIdx.x >> 6) * kRankSortMax;
   uint32_t count = fl.counts()[0];
   if (count > fl.fix_cap) count = fl.fix_cap;
-  const uint32_t stride = (gridDim.x - long_blocks) * kWaves;
-  for (uint32_t k = (blockIdx.x - long_blocks) * kWaves + (threadIdx.x >> 6); k < count; k += stride) {
+  // cell of list entry k: {start, length} when it is one this role takes
+  auto listed = [&](uint32_t k) -> uint2 {
     const uint32_t c = fl.fix()[k];
-    const uint32_t s = inicios[c];
-    const uint32_t e = inicios[c + 1];
-    if (e <= s || e > n || e - s > kRankSortMax) continue;  // uniform across the wave
-    const uint32_t len = e - s, len4 = (len + 3u) & ~3u;
+    if (c >= cells) return make_uint2(0u, 0u);
+    const uint32_t a = inicios[c], e = inicios[c + 1];
+    return (e > a && e <= n && e - a <= kRankSortMax) ? make_uint2(a, e - a) : make_uint2(0u, 0u);
+  };
+  const uint32_t first_thread = (blockIdx.x - long_blocks) * kSortBlock + threadIdx.x;
+  const uint32_t threads = (gridDim.x - long_blocks) * kSortBlock;
+  // a thread per entry: cells of up to kSmallSort, sorted in registers
+  for (uint32_t k = first_thread; k < count; k += threads) {
+    const uint2 sl = listed(k);
+    if (sl.y >= 2u && sl.y <= kSmallSort) sort_cell_in_registers<RECS, true, 2>(sl.x, sl.y, n, ordenado, particles, reordered);
+  }
+  // a wave per entry: the longer cells
+  for (uint32_t k = first_thread >> 6; k < count; k += threads >> 6) {  // uniform across the wave
+    const uint2 sl = listed(k);
+    if (sl.y <= kSmallSort) continue;
+    const uint32_t cs = sl.x, cl = sl.y, cl4 = (cl + 3u) & ~3u;
     // all ones pads the slice: no index reaches it
-    for (uint32_t q = lane; q < len4; q += 64u) slice[q] = (q < len) ? ordenado[s + q] : 0xFFFFFFFFu;
+    for (uint32_t q = lane; q < cl4; q += 64u) slice[q] = (q < cl) ? ordenado[cs + q] : 0xFFFFFFFFu;
     // a wave's LDS accesses complete in order: the slice is whole for
     // every lane after this point
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    for (uint32_t g = 0; g < len; g += 64u) {
+    for (uint32_t g = 0; g < cl; g += 64u) {
       const uint32_t q = g + lane;
-      const uint32_t mine = (q < len) ? slice[q] : 0xFFFFFFFFu;
+      const uint32_t mine = (q < cl) ? slice[q] : 0xFFFFFFFFu;
       uint32_t rank = 0;
-      for (uint32_t j = 0; j < len4; j += 4u) {
+      for (uint32_t j = 0; j < cl4; j += 4u) {  // the same address for every lane
         const uint4 v = *reinterpret_cast<const uint4*>(slice + j);
         rank += (v.x < mine ? 1u : 0u) + (v.y < mine ? 1u : 0u) + (v.z < mine ? 1u : 0u) + (v.w < mine ? 1u : 0u);
       }
-      if (q < len) {
-        ordenado[s + rank] = mine;
+      if (q < cl) {
+        ordenado[cs + rank] = mine;
         if (RECS && mine < n) {
-          reordered[2ull * (s + rank)] = particles[2ull * mine];
-          reordered[2ull * (s + rank) + 1u] = particles[2ull * mine + 1u];
+          reordered[2ull * (cs + rank)] = particles[2ull * mine];
+          reordered[2ull * (cs + rank) + 1u] = particles[2ull * mine + 1u];
         }
       }
     }

@@ -398,14 +398,14 @@ void enqueue_stable_sort(const BuildArgs& a, const Plan& p, char* ws) {
     // records read from the input by particle index
     const FixLists fl = fix_lists_of(a, p);
     const uint32_t long_blocks = (p.long_cap < kFixLongBlocks) ? p.long_cap : kFixLongBlocks;
-    const uint32_t short_blocks = blocks_for(p.fix_cap, kSortBlock / 64);
+    const uint32_t short_blocks = blocks_for(p.fix_cap, kSortBlock);  // 64 entries per wave
     const dim3 grid(long_blocks + ((short_blocks < kFixShortBlocks) ? short_blocks : kFixShortBlocks));
     if (p.move)
       hipLaunchKernelGGL(fix_cells_kernel<true>, grid, dim3(kSortBlock), 0, a.stream, a.inicios, a.celdaDe,
-                         a.n, fl, long_blocks, a.ordenado, parts, out);
+                         static_cast<uint32_t>(p.cells), a.n, fl, long_blocks, a.ordenado, parts, out);
     else
       hipLaunchKernelGGL(fix_cells_kernel<false>, grid, dim3(kSortBlock), 0, a.stream, a.inicios, a.celdaDe,
-                         a.n, fl, long_blocks, a.ordenado, nullptr, nullptr);
+                         static_cast<uint32_t>(p.cells), a.n, fl, long_blocks, a.ordenado, nullptr, nullptr);
     return;
   }
   uint32_t* long_count = reinterpret_cast<uint32_t*>(ws + p.off_long_count);
