@@ -54,11 +54,12 @@ def alg_bytes(n: int, c: int, mode: str) -> dict:
     """Bytes each kernel must move by design, each logical array counted once
     per kernel that touches it (32 B per record, 4 B per u32). The small
     block x tile matrix of the bucketed path is left out; tile_scan moves
-    only that matrix and gets no figure.
+    only that matrix and gets no figure, nor does the stable fix-up, whose
+    work depends on the input.
 
     The end-to-end figure uses the fixed model of the four page steps
     instead: 116 N + 16 C + 4 (see hbm_frac_e2e)."""
-    move = mode in ("atomic", "stable")  # stable: the tile kernel moves records into a workspace copy
+    move = mode in ("atomic", "stable")  # stable: the tile kernel still moves every record
     return {
         # staged path (cells <= 2^22, n <= 2^21)
         "chunk_sort": 72 * n,  # record read, celdaDe, chunk records + indices written
@@ -73,7 +74,9 @@ def alg_bytes(n: int, c: int, mode: str) -> dict:
         "scan": 12 * c + 4,
         "scatter": 80 * n if move else 12 * n,
         # optional passes
-        "stable_sort": 4 * (c + 1) + 8 * n + 64 * n,  # starts, ordenado r/w, records copy -> reordered
+        # data-dependent: on the tile paths only the cells the tile kernel
+        # listed are touched (none on uniform inputs)
+        "stable_sort": None,
         "gather": 68 * n,
     }
 
@@ -210,7 +213,7 @@ KERNEL_STAGE = {
     "staged_keys_kernel": "chunk_sort", "staged_cells_kernel": "tile_sort",
     "bucket_keys_kernel": "keys", "bucket_colscan_kernel": "tile_scan", "bucket_records_kernel": "bucket",
     "clear_kernel": "clear", "count_kernel": "count", "scan_kernel": "scan",
-    "scatter_kernel": "scatter", "gather_kernel": "gather",
+    "scatter_kernel": "scatter", "gather_kernel": "gather", "fix_cells_kernel": "stable_sort",
 }
 
 

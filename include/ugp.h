@@ -111,17 +111,21 @@ typedef struct ugp_particle {
  * each path fills the six slots with its own kernels, named by
  * ugp_grid_stage_name():
  *   n == 0            slot 0 "clear" (zero conteos and inicios); others empty
- *   K <= 2^22 and n <= 2^21
+ *   K <= 2^22 and n <= 2^21 (K up to 2^23 on dense grids)
  *                     "chunk_sort", -, -, "tile_sort" -- two kernels, no
  *                     global atomics, records moved through LDS
- *   other K <= 2^24
- *                     "keys", "tile_scan", "bucket", "cells"  -- a two-level
- *                     counting sort with LDS histograms and no global atomics
- *   K >  2^24         "clear", "count", "scan", "scatter"     -- one global
+ *   other K <= 2^26   "keys", "tile_scan", "bucket", "tile_sort" -- a
+ *                     two-level counting sort with LDS histograms and no
+ *                     global atomics, ending in the same tile kernel
+ *   larger K          "clear", "count", "scan", "scatter"     -- one global
  *                     atomic per particle in count and in scatter
- *   slot 4 "stable_sort" (UGP_FLAG_STABLE only: sorts every cell's slice
- *   by particle index and writes the records in that order), slot 5
- *   "gather" (UGP_FLAG_GATHER only). */
+ *   slot 4 "stable_sort" (UGP_FLAG_STABLE only; page "Construir el índice
+ *   de la rejilla con un prefix sum", section "El orden dentro de la
+ *   celda"). On the two tile paths the tile kernel already puts every cell
+ *   of up to 256 particles in ascending particle index and lists the rest;
+ *   this slot orders the listed cells and copies their records from the
+ *   input. On the direct path it orders every cell's slice and writes the
+ *   records in that order. Slot 5 "gather" (UGP_FLAG_GATHER only). */
 #define UGP_NUM_STAGES 6u
 
 /* Number of cell keys K for a grid and flags: C = dims[0]*dims[1]*dims[2]

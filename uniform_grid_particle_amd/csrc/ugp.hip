@@ -12,15 +12,18 @@
 //
 // Four execution paths, chosen on the host from n and the grid size:
 //   empty   n == 0: conteos and inicios are zeroed.
-//   staged  cells <= 2^22 and n <= 2^21: the two-kernel, atomic-free
-//           counting sort of kernels_staged.h (keys, cells).
+//   staged  keys <= 2^22 (2^23 on dense grids) and n <= 2^21: the
+//           two-kernel, atomic-free counting sort of kernels_staged.h
+//           (chunk_sort, tile_sort).
 //   bucketed  other grids up to 2^26 keys: the four-kernel atomic-free
 //           counting sort of kernels_bucket.h (keys, tile_scan, bucket) ending
 //           in the staged tile kernel (tile_sort).
 //   direct  larger grids: the global-atomic chain of kernels_direct.h
 //           (clear, count, scan, scatter).
-// Stable mode (ascending particle index inside every cell) and gather
-// mode add kernels_reorder.h passes after the scatter. The overflow
+// Stable mode (ascending particle index inside every cell): the tile
+// kernel orders the cells it can and lists the rest for one fix-up kernel
+// (kernels_reorder.h); the direct path orders every cell after its
+// scatter. Gather mode adds a gather pass. The overflow
 // diagnostics are folded into the staged tile kernel (a compile-time
 // variant); the other paths reduce conteos once it is final.
 
@@ -119,8 +122,9 @@ int make_plan(uint32_t n, const uint32_t dims[3], uint32_t flags, Plan* p) {
   p->cells = cells;
   p->stable = (flags & UGP_FLAG_STABLE) != 0;
   const bool index_only = (flags & UGP_FLAG_INDEX_ONLY) != 0;
-  // stable mode moves the records in the tile kernel, into a workspace copy
-  // that the per-cell sort then permutes into `reordered`
+  // gather mode writes the records in a pass of their own; stable mode keeps
+  // them in the tile kernel (direct path: in a workspace copy that the
+  // per-cell sort then permutes into `reordered`)
   p->gather = !index_only && !p->stable && (flags & UGP_FLAG_GATHER) != 0;
   p->move = !index_only && !p->gather;
   const uint32_t lg = ceil_log2_u64(cells);
@@ -369,8 +373,8 @@ void enqueue_cell_diag(const uint32_t* conteos, uint64_t cells, uint32_t cap, ui
 }
 
 // Where the scatter kernels write the records: nowhere (a gather follows, or
-// index only), a workspace copy (stable mode: the per-cell sort then writes
-// `reordered`), or `reordered` itself.
+// index only), a workspace copy (stable mode on the direct path: the
+// per-cell sort then writes `reordered`), or `reordered` itself.
 uint4* record_dst(const BuildArgs& a, const Plan& p) {
   if (!p.move) return nullptr;
   if (p.stable && p.path == Path::kDirect)
@@ -388,7 +392,7 @@ FixLists fix_lists_of(const BuildArgs& a, const Plan& p) {
   return fl;
 }
 
-// Stable-order and gather passes, shared by every path.
+// The stable-order pass of every path, and the gather pass.
 void enqueue_stable_sort(const BuildArgs& a, const Plan& p, char* ws) {
   const uint4* parts = reinterpret_cast<const uint4*>(a.particles);
   uint4* out = p.move ? reinterpret_cast<uint4*>(a.reordered) : nullptr;
