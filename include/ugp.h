@@ -106,11 +106,14 @@ typedef struct ugp_particle {
 #define UGP_FLAG_INDEX_ONLY 0x8u
 
 /* Pipeline stage slots, for ugp_grid_build_stage() / ugp_grid_build_timed().
- * The library picks one of three execution paths from n and the key count K
+ * The library picks one of five execution paths from n and the key count K
  * (ugp_grid_key_count(); the cell count C unless UGP_FLAG_MORTON);
  * each path fills the six slots with its own kernels, named by
  * ugp_grid_stage_name():
  *   n == 0            slot 0 "clear" (zero conteos and inicios); others empty
+ *   n <= 8192 and K <= 2^14
+ *                     -, -, -, "tile_sort" -- one launch: a single workgroup
+ *                     reads the input, writes celdaDe and the whole index
  *   K <= 2^22 and n <= 2^21 (K up to 2^23 on dense grids)
  *                     "chunk_sort", -, -, "tile_sort" -- two kernels, no
  *                     global atomics, records moved through LDS

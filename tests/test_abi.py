@@ -91,6 +91,12 @@ def _call_build(lib, *, n=4, origin=(0.0, 0.0, 0.0), h=1.0, dims=(4, 4, 4), ptrs
 
 def test_stage_names(lib):
     assert ugp.stage_names(1000, (128, 128, 128)) == ["chunk_sort", None, None, "tile_sort", None, None]
+    # one tile over the whole input: at most 8192 particles and 2^14 keys
+    assert ugp.stage_names(4096, (16, 16, 16)) == [None, None, None, "tile_sort", None, None]
+    assert ugp.stage_names(8192, (128, 1, 128)) == [None, None, None, "tile_sort", None, None]
+    assert ugp.stage_names(8193, (16, 16, 16))[0] == "chunk_sort"
+    assert ugp.stage_names(8192, (129, 1, 128))[0] == "chunk_sort"
+    assert ugp.stage_names(1, (1, 1, 1), ugp.FLAG_STABLE)[3:5] == ["tile_sort", "stable_sort"]
     assert ugp.stage_names(3_000_000, (128, 128, 128)) == ["keys", "tile_scan", "bucket", "tile_sort", None, None]
     assert ugp.stage_names(1000, (128, 128, 128), ugp.FLAG_STABLE)[4:] == ["stable_sort", None]
     assert ugp.stage_names(1000, (128, 128, 128), ugp.FLAG_STABLE | ugp.FLAG_GATHER)[4:] == ["stable_sort", None]
@@ -207,10 +213,10 @@ def test_key_count_on_host(lib):
     with pytest.raises(ugp.UGPError) as e:
         ugp.key_count((1025, 1, 1), ugp.FLAG_MORTON)
     assert e.value.status == ugp.UGP_ERR_RANGE
-    # the path follows the key count: 7x5x3 Morton has 512 keys (staged),
-    # 257x2x2 has 2^27 (global-atomic path)
+    # the path follows the key count: 7x5x3 Morton has 512 keys (a tile
+    # path), 257x2x2 has 2^27 (global-atomic path)
     assert ugp.stage_names(100, (257, 2, 2), ugp.FLAG_MORTON)[0] == "clear"
-    assert ugp.stage_names(100, (257, 2, 2))[0] == "chunk_sort"
+    assert ugp.stage_names(100, (257, 2, 2))[3] == "tile_sort"
     assert ugp.workspace_bytes(1000, (7, 5, 3), ugp.FLAG_MORTON) > 0
 
 

@@ -112,6 +112,41 @@ def test_cell_faces(ugp, orc, h, o, d):
     assert_parity(wl, run_gpu(ugp, wl, "atomic"), ref, "atomic")
 
 
+@pytest.mark.parametrize("n,dims", [(8192, (128, 1, 128)), (8192, (7, 5, 3)), (5000, (16, 16, 16)),
+                                    (3, (1, 1, 1)), (777, (33, 1, 17))])
+def test_single_tile_path(ugp, orc, n, dims):
+    """Inputs that fit one tile kernel workgroup (at most 8192 particles and
+    2^14 keys): one launch reads the input directly and writes celdaDe; with
+    the overflow diagnostics and Morton keys too."""
+    assert ugp.stage_names(n, dims)[:4] == [None, None, None, "tile_sort"]
+    rng = np.random.Generator(np.random.PCG64(n + sum(dims)))
+    parts = rng.standard_normal((n, 8)).astype(np.float32)
+    ext = np.asarray(dims, np.float64) * 0.25
+    parts[:, :3] = (rng.random((n, 3)) * ext * 1.1 - 0.05 * ext).astype(np.float32)
+    parts[: n // 4, :3] = parts[0, :3]  # one crowded cell
+    wl = W.Workload("single", parts, np.zeros(3, np.float32), np.float32(0.25), np.asarray(dims, np.uint32))
+    ref = orc.grid_build(wl.particles, wl.origin, wl.cell_size, wl.dims)
+    for mode in MODES:
+        assert_parity(wl, run_gpu(ugp, wl, mode), ref, mode)
+    dev = torch.device("cuda:0")
+    r, diag = ugp.grid_build_diag(torch.from_numpy(parts).to(dev), [0.0, 0.0, 0.0], 0.25, list(dims), 5, stable=True)
+    torch.cuda.synchronize()
+    got = oracle.GridIndex(_u32(r.celdaDe), _u32(r.conteos), _u32(r.inicios), _u32(r.ordenado),
+                           r.reordered.cpu().numpy())
+    assert_parity(wl, got, ref, "stable")
+    assert _u32(diag).tolist() == list(orc.diag(ref.conteos, 5))
+    # Morton keys: the same path while the key count stays within one tile
+    if ugp.key_count(dims, ugp.FLAG_MORTON) <= (1 << 14):
+        assert ugp.stage_names(n, dims, ugp.FLAG_MORTON)[0] is None
+    refm = orc.grid_build(wl.particles, wl.origin, wl.cell_size, wl.dims, morton=True)
+    rm = ugp.grid_build(torch.from_numpy(parts).to(dev), [0.0, 0.0, 0.0], 0.25, list(dims), morton=True, stable=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(_u32(rm.celdaDe), refm.celdaDe)
+    assert np.array_equal(_u32(rm.inicios), refm.inicios)
+    assert np.array_equal(_u32(rm.ordenado), refm.ordenado)
+    assert np.array_equal(rm.reordered.cpu().numpy().view(np.uint32), refm.reordered.view(np.uint32))
+
+
 def test_noncubic_ragged(ugp, orc):
     """Non-cubic grid (x/y/z strides differ), cells and particles off every tile size."""
     rng = np.random.Generator(np.random.PCG64(21))

@@ -59,6 +59,7 @@ constexpr uint32_t kStagedMinShift = 4;            // at least 16 cells per tile
 constexpr uint32_t kStagedMaxShift = 14;            // up to 16384 cells per tile
 constexpr uint64_t kStagedTarget = 4096;            // mean particles per tile sought (half the capacity)
 constexpr int kCellsThreads = 1024;                 // tile_sort workgroup
+constexpr uint32_t kSingleMax = kCellsThreads * kStagedRegs;  // particles one tile kernel workgroup stages
 constexpr uint32_t kCellsWin = 2048;                // tile_sort LDS staging window
 
 // Tile t's workgroup index, spreading consecutive tiles over workgroups of
@@ -166,6 +167,10 @@ __global__ __launch_bounds__(CT) void staged_keys_kernel(
 
 // tile_sort: NT threads; the tile of block b (tile_of_block) owns cells
 // [t << SHIFT, (t+1) << SHIFT); WIN records are staged in LDS at a time.
+// SINGLE: one workgroup, one tile over every cell; rows and chunk_idx are
+// not read (the one run is the input itself, chunk_rec = the particles, in
+// index order), and the kernel also writes each particle's key to keys_out
+// (celdaDe), which is not read otherwise.
 // MOVE: also write the records (otherwise a separate gather follows).
 // DIAG: also fold the tile's histogram into the overflow diagnostics
 // (diag[0] max occupancy, diag[1] overflowing insertions over capacity cap;
@@ -176,13 +181,13 @@ __global__ __launch_bounds__(CT) void staged_keys_kernel(
 // particle indices, which is its place in that order, and is staged there.
 // A longer cell, and every multi-particle cell of a tile past the staged
 // capacity, is written in arrival order and put on one of the fix-up lists.
-template <bool MOVE, bool DIAG, bool STABLE, uint32_t SHIFT, int NT, uint32_t WIN>
+template <bool MOVE, bool DIAG, bool STABLE, bool SINGLE, uint32_t SHIFT, int NT, uint32_t WIN>
 __global__ __launch_bounds__(NT) void staged_cells_kernel(
-    const uint2* __restrict__ rows, uint32_t nchunks, uint32_t chunk, uint32_t ntiles, GridParams g,
+    const uint2* __restrict__ rows, uint32_t nchunks, uint32_t ntiles, GridParams g,
     uint32_t cells, uint32_t n, const uint4* __restrict__ chunk_rec,
     const uint32_t* __restrict__ chunk_idx, uint32_t* __restrict__ conteos,
     uint32_t* __restrict__ inicios, uint32_t* __restrict__ ordenado, uint4* __restrict__ dst,
-    uint32_t cap, uint32_t* __restrict__ diag, FixLists fl) {
+    uint32_t cap, uint32_t* __restrict__ diag, FixLists fl, uint32_t* __restrict__ keys_out) {
   constexpr uint32_t kTileCells = 1u << SHIFT;
   // cells per thread in the scan (tiles smaller than the workgroup: one
   // cell for each of the first kTileCells threads)
@@ -204,6 +209,13 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
   __shared__ uint32_t s_dm[DIAG ? NT / 64 : 1], s_do[DIAG ? NT / 64 : 1];
   __shared__ uint32_t s_any_long;  // stable: some cell of the tile is longer than kRankSortMax
 
+  // one tile holding the whole input: no kernel runs before this one, so the
+  // words it would zero are zeroed here, before the first barrier below
+  if (SINGLE && threadIdx.x < 2) {
+    if (diag != nullptr) diag[threadIdx.x] = 0u;
+    if (fl.base != nullptr) fl.base[threadIdx.x] = 0u;
+  }
+
   const uint32_t t = tile_of_block(blockIdx.x, ntiles);
   const uint32_t cell0 = t << SHIFT;
   const uint32_t tc = (cells - cell0 < kTileCells) ? cells - cell0 : kTileCells;
@@ -215,7 +227,8 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
 #pragma unroll
   for (uint32_t q = 0; q < kChunksPerThread; ++q) {
     const uint32_t c = threadIdx.x * kChunksPerThread + q;
-    r[q] = (c < nchunks) ? rows[static_cast<size_t>(c) * ntiles + t] : make_uint2(0u, 0u);
+    // SINGLE: one run of all n particles
+    r[q] = (c < nchunks) ? (SINGLE ? make_uint2(n, 0u) : rows[static_cast<size_t>(c) * ntiles + t]) : make_uint2(0u, 0u);
     len_sum += r[q].x;
     pre_sum += r[q].y;
   }
@@ -237,7 +250,7 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
     const uint32_t c = threadIdx.x * kChunksPerThread + q;
     if (c < nchunks) {
       s_dst[c] = run_dst;
-      s_src[c] = c * chunk + r[q].y;
+      s_src[c] = c * kChunk + r[q].y;  // chunks of kChunk particles (bucketed: one chunk)
     }
     run_dst += r[q].x;
   }
@@ -398,7 +411,7 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
       for (int k = 0; k < kStagedRegs; ++k) {
         const uint4 a = chunk_rec[static_cast<size_t>(src[k]) * 2u];
         const uint4 b = MOVE ? chunk_rec[static_cast<size_t>(src[k]) * 2u + 1u] : make_uint4(0u, 0u, 0u, 0u);
-        idx[k] = chunk_idx[src[k]];
+        idx[k] = SINGLE ? src[k] : chunk_idx[src[k]];  // SINGLE: the input itself, in order
         w[0][k] = a.x; w[1][k] = a.y; w[2][k] = a.z; w[3][k] = a.w;
         w[4][k] = b.x; w[5][k] = b.y; w[6][k] = b.z; w[7][k] = b.w;
       }
@@ -415,6 +428,11 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
       // no wait before using those registers after the stores below (one
       // counter tracks loads and stores alike)
       __builtin_amdgcn_s_waitcnt(kWaitLoadsAndStores);
+      if (SINGLE) {
+#pragma unroll
+        for (int k = 0; k < kStagedRegs; ++k)
+          if (lr[k] != 0xFFFFFFFFu) keys_out[idx[k]] = cell0 + (lr[k] >> 16);
+      }
     }
     __syncthreads();
     const uint32_t tot = scan_tile();
@@ -536,7 +554,7 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
       for (int k = 0; k < kOver; ++k) {
         const uint4 a = chunk_rec[static_cast<size_t>(src[k]) * 2u];
         const uint4 b = MOVE ? chunk_rec[static_cast<size_t>(src[k]) * 2u + 1u] : make_uint4(0u, 0u, 0u, 0u);
-        id[k] = chunk_idx[src[k]];
+        id[k] = SINGLE ? src[k] : chunk_idx[src[k]];
         v[0][k] = a.x; v[1][k] = a.y; v[2][k] = a.z; v[3][k] = a.w;
         v[4][k] = b.x; v[5][k] = b.y; v[6][k] = b.z; v[7][k] = b.w;
       }
@@ -546,6 +564,7 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
         const uint32_t loc = cell_of(__uint_as_float(v[0][k]), __uint_as_float(v[1][k]),
                                      __uint_as_float(v[2][k]), g) - cell0;
         if (!(p < count && loc < tc)) continue;
+        if (SINGLE) keys_out[id[k]] = cell0 + loc;
         const size_t out = static_cast<size_t>(bs) + atomicAdd(&s_cnt[loc], 1u);
         if (out < n) {
           ordenado[out] = id[k];

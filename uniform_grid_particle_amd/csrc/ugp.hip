@@ -10,8 +10,10 @@
 // (page "Reordenar por celda y la coalescencia de memoria", section "El
 // kernel de reordenación").
 //
-// Four execution paths, chosen on the host from n and the grid size:
+// Five execution paths, chosen on the host from n and the grid size:
 //   empty   n == 0: conteos and inicios are zeroed.
+//   single  n <= 8192 and keys <= 2^14: the tile kernel alone, one
+//           workgroup reading the input directly (one launch).
 //   staged  keys <= 2^22 (2^23 on dense grids) and n <= 2^21: the
 //           two-kernel, atomic-free counting sort of kernels_staged.h
 //           (chunk_sort, tile_sort).
@@ -50,7 +52,7 @@ using namespace ugp;
 constexpr uint32_t kCounterWords = 64;    // small counter block (direct path)
 constexpr uint32_t kMortonMaxBits = 10;   // Morton keys: 10 bits per axis, 2^30 keys
 
-enum class Path { kEmpty, kStaged, kBucketed, kDirect };
+enum class Path { kEmpty, kSingle, kStaged, kBucketed, kDirect };
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -134,6 +136,13 @@ int make_plan(uint32_t n, const uint32_t dims[3], uint32_t flags, Plan* p) {
     p->total = 256;
     return UGP_OK;
   }
+  // single tile: everything fits one staged tile kernel workgroup
+  if (n <= kSingleMax && lg <= kStagedMaxShift) {
+    p->path = Path::kSingle;
+    p->tile_shift = (lg > kStagedMinShift) ? lg : kStagedMinShift;
+    p->ntiles = 1;
+    p->nchunks = 1;
+  }
   // staged path: tiles of 2^shift consecutive keys. As large as 256 tiles
   // allow (one round of tile_sort workgroups), but no larger than keeps the
   // mean tile at kStagedTarget particles (dense grids: more, smaller tiles),
@@ -146,7 +155,9 @@ int make_plan(uint32_t n, const uint32_t dims[3], uint32_t flags, Plan* p) {
   const uint32_t fewest_shift = (lg > kStagedMinShift + 9) ? lg - 9 : kStagedMinShift;  // 512 tiles
   if (staged_shift < fewest_shift) staged_shift = fewest_shift;
   const uint64_t nchunks = (static_cast<uint64_t>(n) + kChunk - 1) / kChunk;
-  if (staged_shift <= kStagedMaxShift && nchunks <= kStagedMaxChunks) {
+  if (p->path == Path::kSingle) {
+    // no workspace beyond the stable-mode lists below
+  } else if (staged_shift <= kStagedMaxShift && nchunks <= kStagedMaxChunks) {
     p->path = Path::kStaged;
     p->tile_shift = staged_shift;
     p->ntiles = static_cast<uint32_t>((cells + (1ull << staged_shift) - 1) >> staged_shift);
@@ -218,9 +229,12 @@ const char* stage_name(const Plan& p, uint32_t stage) {
                                                       "stable_sort", "gather"};
   static const char* const kStaged[UGP_NUM_STAGES] = {"chunk_sort", nullptr, nullptr, "tile_sort",
                                                       "stable_sort", "gather"};
+  static const char* const kSingleNames[UGP_NUM_STAGES] = {nullptr, nullptr, nullptr, "tile_sort",
+                                                           "stable_sort", "gather"};
   if (stage >= UGP_NUM_STAGES) return nullptr;
   if (p.path == Path::kEmpty) return stage == 0 ? "clear" : nullptr;
   if (p.path == Path::kStaged && stage < 4) return kStaged[stage];
+  if (p.path == Path::kSingle && stage < 4) return kSingleNames[stage];
   if (stage == 4 && !p.stable) return nullptr;
   if (stage == 5 && !p.gather) return nullptr;
   return p.path == Path::kBucketed ? kBucket[stage] : kDirect[stage];
@@ -317,28 +331,28 @@ void launch_clear(uint32_t* ptr, uint64_t words, uint32_t* extra, uint32_t extra
   hipLaunchKernelGGL(clear_kernel, dim3(blocks), dim3(kBlock), 0, s, ptr, words, extra, extra_words);
 }
 
-template <bool MOVE, bool DIAG, bool STABLE, uint32_t SHIFT>
+template <bool MOVE, bool DIAG, bool STABLE, bool SINGLE, uint32_t SHIFT>
 void launch_staged_cells_at(dim3 grid, hipStream_t s, const uint2* rows, uint32_t nchunks,
                             uint32_t ntiles, GridParams g, uint32_t cells, uint32_t n,
                             const uint4* chunk_rec, const uint32_t* chunk_idx, uint32_t* conteos,
                             uint32_t* inicios, uint32_t* ordenado, uint4* dst, uint32_t cap,
-                            uint32_t* diag, FixLists fl) {
-  hipLaunchKernelGGL((staged_cells_kernel<MOVE, DIAG, STABLE, SHIFT, kCellsThreads, kCellsWin>), grid,
-                     dim3(kCellsThreads), 0, s, rows, nchunks, kChunk, ntiles, g, cells, n, chunk_rec,
-                     chunk_idx, conteos, inicios, ordenado, dst, cap, diag, fl);
+                            uint32_t* diag, FixLists fl, uint32_t* keys_out) {
+  hipLaunchKernelGGL((staged_cells_kernel<MOVE, DIAG, STABLE, SINGLE, SHIFT, kCellsThreads, kCellsWin>), grid,
+                     dim3(kCellsThreads), 0, s, rows, nchunks, ntiles, g, cells, n, chunk_rec,
+                     chunk_idx, conteos, inicios, ordenado, dst, cap, diag, fl, keys_out);
 }
 
-template <bool MOVE, bool DIAG, bool STABLE>
+template <bool MOVE, bool DIAG, bool STABLE, bool SINGLE>
 void launch_staged_cells(uint32_t shift, dim3 grid, hipStream_t s, const uint2* rows,
                          uint32_t nchunks, uint32_t ntiles, GridParams g, uint32_t cells,
                          uint32_t n, const uint4* chunk_rec, const uint32_t* chunk_idx,
                          uint32_t* conteos, uint32_t* inicios, uint32_t* ordenado, uint4* dst,
-                         uint32_t cap, uint32_t* diag, FixLists fl) {
-#define UGP_STAGED_CASE(S)                                                                            \
-  case S:                                                                                             \
-    launch_staged_cells_at<MOVE, DIAG, STABLE, S>(grid, s, rows, nchunks, ntiles, g, cells, n,         \
-                                                  chunk_rec, chunk_idx, conteos, inicios, ordenado,   \
-                                                  dst, cap, diag, fl);                            \
+                         uint32_t cap, uint32_t* diag, FixLists fl, uint32_t* keys_out) {
+#define UGP_STAGED_CASE(S)                                                                           \
+  case S:                                                                                            \
+    launch_staged_cells_at<MOVE, DIAG, STABLE, SINGLE, S>(grid, s, rows, nchunks, ntiles, g, cells, n,       \
+                                                  chunk_rec, chunk_idx, conteos, inicios, ordenado,  \
+                                                  dst, cap, diag, fl, keys_out);                     \
     break;
   switch (shift) {
     UGP_STAGED_CASE(4)
@@ -352,9 +366,9 @@ void launch_staged_cells(uint32_t shift, dim3 grid, hipStream_t s, const uint2* 
     UGP_STAGED_CASE(12)
     UGP_STAGED_CASE(13)
     default:
-      launch_staged_cells_at<MOVE, DIAG, STABLE, 14>(grid, s, rows, nchunks, ntiles, g, cells, n,
+      launch_staged_cells_at<MOVE, DIAG, STABLE, SINGLE, 14>(grid, s, rows, nchunks, ntiles, g, cells, n,
                                                      chunk_rec, chunk_idx, conteos, inicios, ordenado,
-                                                     dst, cap, diag, fl);
+                                                     dst, cap, diag, fl, keys_out);
       break;
   }
 #undef UGP_STAGED_CASE
@@ -439,8 +453,9 @@ void enqueue_gather(const BuildArgs& a) {
 }
 
 // the staged tile kernel over tiles given by rows (staged: chunk rows;
-// bucketed: one contiguous run per tile), with or without records and the
-// diagnostic variant
+// bucketed: one contiguous run per tile; SINGLE: the one tile over the
+// input, no rows), with or without records, diagnostics and stable order
+template <bool SINGLE>
 void launch_tile_sort(const BuildArgs& a, const Plan& p, const uint2* rows, const uint4* rec,
                       const uint32_t* idx) {
   const uint32_t cells = static_cast<uint32_t>(p.cells);
@@ -449,11 +464,12 @@ void launch_tile_sort(const BuildArgs& a, const Plan& p, const uint2* rows, cons
   hipStream_t s = a.stream;
   const FixLists fl = fix_lists_of(a, p);
   const GridParams g = grid_params(a);
+  uint32_t* keys_out = SINGLE ? a.celdaDe : nullptr;
   // one instantiation per (moves records, diagnostics, stable order)
-#define UGP_TILE_SORT(M, D, S)                                                                       \
-  launch_staged_cells<M, D, S>(p.tile_shift, grid, s, rows, p.nchunks, p.ntiles, g, cells, a.n, rec, \
-                               idx, a.conteos, a.inicios, a.ordenado, dst, D ? a.capacity : 0u,     \
-                               D ? a.diag : nullptr, fl)
+#define UGP_TILE_SORT(M, D, S)                                                                        \
+  launch_staged_cells<M, D, S, SINGLE>(p.tile_shift, grid, s, rows, p.nchunks, p.ntiles, g, cells,   \
+                                       a.n, rec, idx, a.conteos, a.inicios, a.ordenado, dst,         \
+                                       D ? a.capacity : 0u, D ? a.diag : nullptr, fl, keys_out)
   const bool m = p.move, d = a.diag != nullptr, st = p.stable;
   if (m && d && st) UGP_TILE_SORT(true, true, true);
   else if (m && d) UGP_TILE_SORT(true, true, false);
@@ -464,6 +480,24 @@ void launch_tile_sort(const BuildArgs& a, const Plan& p, const uint2* rows, cons
   else if (st) UGP_TILE_SORT(false, false, true);
   else UGP_TILE_SORT(false, false, false);
 #undef UGP_TILE_SORT
+}
+
+// single tile: the tile kernel reads the input directly (one run, identity
+// indices) and writes celdaDe itself
+void enqueue_single(uint32_t stage, const BuildArgs& a, const Plan& p) {
+  switch (stage) {
+    case 3:
+      launch_tile_sort<true>(a, p, nullptr, reinterpret_cast<const uint4*>(a.particles), nullptr);
+      break;
+    case 4:
+      if (p.stable) enqueue_stable_sort(a, p, static_cast<char*>(a.workspace));
+      break;
+    case 5:
+      if (p.gather) enqueue_gather(a);
+      break;
+    default:
+      break;
+  }
 }
 
 void enqueue_staged(uint32_t stage, const BuildArgs& a, const Plan& p) {
@@ -480,7 +514,7 @@ void enqueue_staged(uint32_t stage, const BuildArgs& a, const Plan& p) {
                          fix_lists_of(a, p).base);
       break;
     case 3:
-      launch_tile_sort(a, p, rows, chunk_rec, chunk_idx);
+      launch_tile_sort<false>(a, p, rows, chunk_rec, chunk_idx);
       break;
     case 4:
       if (p.stable) enqueue_stable_sort(a, p, ws);
@@ -517,7 +551,7 @@ void enqueue_bucketed(uint32_t stage, const BuildArgs& a, const Plan& p) {
                          tile_total, p.tile_shift, p.ntiles, tile_rec, tile_idx, rows);
       break;
     case 3:
-      launch_tile_sort(a, p, rows, tile_rec, tile_idx);
+      launch_tile_sort<false>(a, p, rows, tile_rec, tile_idx);
       break;
     case 4:
       if (p.stable) enqueue_stable_sort(a, p, ws);
@@ -579,6 +613,9 @@ int enqueue_stage(uint32_t stage, const BuildArgs& a, const Plan& p) {
         launch_clear(a.conteos, p.cells, a.diag, a.diag ? 2u : 0u, a.stream);
         launch_clear(a.inicios, p.cells + 1, nullptr, 0, a.stream);
       }
+      break;
+    case Path::kSingle:
+      enqueue_single(stage, a, p);
       break;
     case Path::kStaged:
       enqueue_staged(stage, a, p);
