@@ -28,7 +28,20 @@
 namespace ugp {
 
 constexpr int kNeighborBlock = 256;
+constexpr uint32_t kNeighborUnroll = 8;  // candidates per step of the contiguous loop
 
+// 1 when candidate q lies within the radius of pi, decided as described above
+__device__ __forceinline__ uint32_t within(float4 q, float4 pi, float r2) {
+  const float dx = q.x - pi.x;
+  const float dy = q.y - pi.y;
+  const float dz = q.z - pi.z;
+  const float d2 = dx * dx + dy * dy + dz * dz;
+  return (d2 <= r2) ? 1u : 0u;
+}
+
+// Candidates of slice [s, e): INDIRECT through ordenado, skipping the query
+// itself; otherwise the contiguous records s..e-1, the query included when
+// it lies in the slice (the caller takes its own term off once).
 template <bool INDIRECT>
 __device__ __forceinline__ uint32_t count_range(const float4* __restrict__ parts,
                                                 const uint32_t* __restrict__ ordenado, uint32_t n,
@@ -36,16 +49,25 @@ __device__ __forceinline__ uint32_t count_range(const float4* __restrict__ parts
                                                 uint32_t e) {
   e = (e < n) ? e : n;  // a slice never runs past the particle count
   uint32_t cnt = 0;
-  for (uint32_t t = s; t < e; ++t) {
-    const uint32_t j = INDIRECT ? ordenado[t] : t;
-    if (j >= n || j == self) continue;
-    const float4 q = parts[2u * static_cast<size_t>(j)];
-    const float dx = q.x - pi.x;
-    const float dy = q.y - pi.y;
-    const float dz = q.z - pi.z;
-    const float d2 = dx * dx + dy * dy + dz * dz;
-    cnt += (d2 <= r2) ? 1u : 0u;
+  if (INDIRECT) {
+    for (uint32_t t = s; t < e; ++t) {
+      const uint32_t j = ordenado[t];
+      if (j >= n || j == self) continue;
+      cnt += within(parts[2u * static_cast<size_t>(j)], pi, r2);
+    }
+    return cnt;
   }
+  const float4* q = parts + 2u * static_cast<size_t>(s);
+  const uint32_t len = (e > s) ? e - s : 0u;
+  uint32_t t = 0;
+  for (; t + kNeighborUnroll <= len; t += kNeighborUnroll) {  // these candidates' loads in flight together
+    float4 c[kNeighborUnroll];
+#pragma unroll
+    for (uint32_t u = 0; u < kNeighborUnroll; ++u) c[u] = q[2u * (t + u)];
+#pragma unroll
+    for (uint32_t u = 0; u < kNeighborUnroll; ++u) cnt += within(c[u], pi, r2);
+  }
+  for (; t < len; ++t) cnt += within(q[2u * t], pi, r2);
   return cnt;
 }
 
@@ -67,21 +89,28 @@ __global__ __launch_bounds__(kNeighborBlock) void neighbor_count_kernel(
   const uint32_t y0 = ky ? ky - 1u : 0u, y1 = (ky + 1u < ny) ? ky + 1u : ky;
   const uint32_t z0 = kz ? kz - 1u : 0u, z1 = (kz + 1u < nz) ? kz + 1u : kz;
   uint32_t cnt = 0;
+  bool self_seen = false;  // reordered: the query's own record was among the candidates
   for (uint32_t z = z0; z <= z1; ++z) {
     for (uint32_t y = y0; y <= y1; ++y) {
       if (MORTON) {
         const uint32_t yz = (spread_bits3(y) << 1) | (spread_bits3(z) << 2);
         for (uint32_t x = x0; x <= x1; ++x) {
           const uint32_t key = spread_bits3(x) | yz;
-          cnt += count_range<INDIRECT>(parts, ordenado, n, k, pi, r2, inicios[key], inicios[key + 1u]);
+          const uint32_t s = inicios[key], e = inicios[key + 1u];
+          cnt += count_range<INDIRECT>(parts, ordenado, n, k, pi, r2, s, e);
+          self_seen = self_seen || (s <= k && k < e);
         }
       } else {
         const uint32_t row = y * g.nx + z * g.nxy;
-        cnt += count_range<INDIRECT>(parts, ordenado, n, k, pi, r2, inicios[row + x0],
-                                     inicios[row + x1 + 1u]);
+        const uint32_t s = inicios[row + x0], e = inicios[row + x1 + 1u];
+        cnt += count_range<INDIRECT>(parts, ordenado, n, k, pi, r2, s, e);
+        self_seen = self_seen || (s <= k && k < e);
       }
     }
   }
+  // reordered: the query met itself once, with the same arithmetic as any
+  // other candidate; take that term off
+  if (!INDIRECT && self_seen) cnt -= within(pi, pi, r2);
   counts[k] = cnt;
 }
 
