@@ -405,7 +405,7 @@ def next_rows_summary(result: dict, wl, with_oracle: bool) -> dict:
         "gpu": {"fused_step_us": round(dv["ms_per_step"] * 1e3, 2),
                 "fused_overhead_us": round(dv["ms_per_step"] * 1e3 - step_us, 2),
                 "standalone_us": dv["cell_diag_us"]},
-        "roofline": {"kernel": "diag_kernel (standalone, over conteos)", "bound": "hbm", "achieved": round(diag_gbs, 1),
+        "roofline": {"kernel": "diag_kernel<256> (standalone, over conteos)", "bound": "hbm", "achieved": round(diag_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": diag_gbs / HBM_PEAK_GBS},
     }
     mv = result["morton_variant"]

@@ -29,21 +29,52 @@ FLAGS = [
 ]
 
 
+def sources() -> list:
+    """Every translation unit: the host code and C ABI (ugp.hip) and the tile
+    kernel variants (tile_sort_*.hip), compiled in parallel."""
+    d = os.path.dirname(SRC)
+    return [SRC] + sorted(os.path.join(d, f) for f in os.listdir(d) if f.startswith("tile_sort_") and f.endswith(".hip"))
+
+
 def build(verbose: bool = False) -> str:
+    objs, procs = [], []
+    for src in sources():
+        obj = os.path.join(os.path.dirname(LIB), "_obj_" + os.path.basename(src) + ".o")
+        cmd = [HIPCC, *[f for f in FLAGS if f != "-shared"], "-I", INCLUDE, "-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((subprocess.Popen(cmd), cmd))
+        objs.append(obj)
+    failed = [cmd for p, cmd in procs if p.wait() != 0]
+    if failed:
+        raise subprocess.CalledProcessError(1, failed[0])
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", INCLUDE, SRC, "-o", tmp]
+    cmd = [HIPCC, "--offload-arch=gfx950", "-fPIC", "-shared", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    for obj in objs:
+        os.remove(obj)
     return LIB
 
 
 def assembly(out: str) -> str:
-    """Device assembly of the library, for inspection (gfx950 only)."""
-    cmd = [HIPCC, *[f for f in FLAGS if f not in ("-shared", "-fPIC")], "-I", INCLUDE,
-           "--cuda-device-only", "-S", SRC, "-o", out]
-    subprocess.run(cmd, check=True)
+    """Device assembly of every translation unit, concatenated (gfx950 only),
+    for inspection."""
+    parts = []
+    for src in sources():
+        part = out + "." + os.path.basename(src) + ".s"
+        cmd = [HIPCC, *[f for f in FLAGS if f not in ("-shared", "-fPIC")], "-I", INCLUDE,
+               "--cuda-device-only", "-S", src, "-o", part]
+        parts.append((subprocess.Popen(cmd), part))
+    with open(out, "w") as f:
+        for p, part in parts:
+            if p.wait() != 0:
+                raise subprocess.CalledProcessError(1, part)
+            with open(part) as g:
+                f.write(g.read())
+            os.remove(part)
     return out
 
 

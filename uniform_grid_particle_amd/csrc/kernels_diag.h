@@ -60,20 +60,22 @@ __device__ __forceinline__ void publish_diag(const uint32_t* s_m, const uint32_t
 // over c < cells. diag must be zeroed before. conteos 16-byte aligned. Each
 // thread issues kDiagItems 16-byte loads per round before using any of them.
 constexpr int kDiagItems = 4;
-__global__ __launch_bounds__(kDiagBlock) void diag_kernel(const uint32_t* __restrict__ conteos,
-                                                          uint32_t cells, uint32_t cap,
-                                                          uint32_t* __restrict__ diag) {
-  __shared__ uint32_t s_m[kDiagBlock / 64], s_o[kDiagBlock / 64];
+// NT threads per workgroup (a template, so that every translation unit that
+// sees this header may define it).
+template <int NT>
+__global__ __launch_bounds__(NT) void diag_kernel(const uint32_t* __restrict__ conteos, uint32_t cells,
+                                                  uint32_t cap, uint32_t* __restrict__ diag) {
+  __shared__ uint32_t s_m[NT / 64], s_o[NT / 64];
   uint32_t m = 0, o = 0;
   const uint64_t nvec = cells / 4u;
-  const uint64_t round = static_cast<uint64_t>(gridDim.x) * kDiagBlock * kDiagItems;
+  const uint64_t round = static_cast<uint64_t>(gridDim.x) * NT * kDiagItems;
   const uint4* c4 = reinterpret_cast<const uint4*>(conteos);
-  for (uint64_t q0 = static_cast<uint64_t>(blockIdx.x) * kDiagBlock * kDiagItems + threadIdx.x; q0 < nvec;
+  for (uint64_t q0 = static_cast<uint64_t>(blockIdx.x) * NT * kDiagItems + threadIdx.x; q0 < nvec;
        q0 += round) {
     uint4 v[kDiagItems];
 #pragma unroll
     for (int k = 0; k < kDiagItems; ++k) {
-      const uint64_t q = q0 + static_cast<uint64_t>(k) * kDiagBlock;
+      const uint64_t q = q0 + static_cast<uint64_t>(k) * NT;
       v[k] = (q < nvec) ? load_stream(c4 + q) : make_uint4(0u, 0u, 0u, 0u);  // 0 adds nothing
     }
 #pragma unroll
@@ -86,8 +88,8 @@ __global__ __launch_bounds__(kDiagBlock) void diag_kernel(const uint32_t* __rest
            overflow_of(v[k].w, cap);
     }
   }
-  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kDiagBlock;
-  for (uint64_t j = 4u * nvec + static_cast<uint64_t>(blockIdx.x) * kDiagBlock + threadIdx.x; j < cells;
+  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * NT;
+  for (uint64_t j = 4u * nvec + static_cast<uint64_t>(blockIdx.x) * NT + threadIdx.x; j < cells;
        j += stride) {
     const uint32_t v = conteos[j];
     m = (v > m) ? v : m;
@@ -100,7 +102,7 @@ __global__ __launch_bounds__(kDiagBlock) void diag_kernel(const uint32_t* __rest
     s_o[threadIdx.x >> 6] = o;
   }
   __syncthreads();
-  publish_diag<kDiagBlock>(s_m, s_o, diag);
+  publish_diag<NT>(s_m, s_o, diag);
 }
 
 }  // namespace ugp

@@ -43,6 +43,7 @@
 #include "kernels_reorder.h"
 #include "kernels_staged.h"
 #include "kernels_bucket.h"
+#include "tile_launch.h"
 #include "ugp.h"
 
 namespace {
@@ -331,49 +332,6 @@ void launch_clear(uint32_t* ptr, uint64_t words, uint32_t* extra, uint32_t extra
   hipLaunchKernelGGL(clear_kernel, dim3(blocks), dim3(kBlock), 0, s, ptr, words, extra, extra_words);
 }
 
-template <bool MOVE, bool DIAG, bool STABLE, bool SINGLE, uint32_t SHIFT>
-void launch_staged_cells_at(dim3 grid, hipStream_t s, const uint2* rows, uint32_t nchunks,
-                            uint32_t ntiles, GridParams g, uint32_t cells, uint32_t n,
-                            const uint4* chunk_rec, const uint32_t* chunk_idx, uint32_t* conteos,
-                            uint32_t* inicios, uint32_t* ordenado, uint4* dst, uint32_t cap,
-                            uint32_t* diag, FixLists fl, uint32_t* keys_out) {
-  hipLaunchKernelGGL((staged_cells_kernel<MOVE, DIAG, STABLE, SINGLE, SHIFT, kCellsThreads, kCellsWin>), grid,
-                     dim3(kCellsThreads), 0, s, rows, nchunks, ntiles, g, cells, n, chunk_rec,
-                     chunk_idx, conteos, inicios, ordenado, dst, cap, diag, fl, keys_out);
-}
-
-template <bool MOVE, bool DIAG, bool STABLE, bool SINGLE>
-void launch_staged_cells(uint32_t shift, dim3 grid, hipStream_t s, const uint2* rows,
-                         uint32_t nchunks, uint32_t ntiles, GridParams g, uint32_t cells,
-                         uint32_t n, const uint4* chunk_rec, const uint32_t* chunk_idx,
-                         uint32_t* conteos, uint32_t* inicios, uint32_t* ordenado, uint4* dst,
-                         uint32_t cap, uint32_t* diag, FixLists fl, uint32_t* keys_out) {
-#define UGP_STAGED_CASE(S)                                                                           \
-  case S:                                                                                            \
-    launch_staged_cells_at<MOVE, DIAG, STABLE, SINGLE, S>(grid, s, rows, nchunks, ntiles, g, cells, n,       \
-                                                  chunk_rec, chunk_idx, conteos, inicios, ordenado,  \
-                                                  dst, cap, diag, fl, keys_out);                     \
-    break;
-  switch (shift) {
-    UGP_STAGED_CASE(4)
-    UGP_STAGED_CASE(5)
-    UGP_STAGED_CASE(6)
-    UGP_STAGED_CASE(7)
-    UGP_STAGED_CASE(8)
-    UGP_STAGED_CASE(9)
-    UGP_STAGED_CASE(10)
-    UGP_STAGED_CASE(11)
-    UGP_STAGED_CASE(12)
-    UGP_STAGED_CASE(13)
-    default:
-      launch_staged_cells_at<MOVE, DIAG, STABLE, SINGLE, 14>(grid, s, rows, nchunks, ntiles, g, cells, n,
-                                                     chunk_rec, chunk_idx, conteos, inicios, ordenado,
-                                                     dst, cap, diag, fl, keys_out);
-      break;
-  }
-#undef UGP_STAGED_CASE
-}
-
 // Overflow diagnostics of a final conteos array: zero the two words, then
 // reduce (paths other than staged, and the standalone entry point).
 void enqueue_cell_diag(const uint32_t* conteos, uint64_t cells, uint32_t cap, uint32_t* diag,
@@ -382,7 +340,7 @@ void enqueue_cell_diag(const uint32_t* conteos, uint64_t cells, uint32_t cap, ui
   if (cells == 0) return;
   uint32_t blocks = blocks_for((cells + 3) / 4, static_cast<uint64_t>(kDiagBlock) * kDiagItems);
   if (blocks > kDiagMaxGrid) blocks = kDiagMaxGrid;
-  hipLaunchKernelGGL(diag_kernel, dim3(blocks), dim3(kDiagBlock), 0, s, conteos,
+  hipLaunchKernelGGL(diag_kernel<kDiagBlock>, dim3(blocks), dim3(kDiagBlock), 0, s, conteos,
                      static_cast<uint32_t>(cells), cap, diag);
 }
 
