@@ -8,7 +8,6 @@
 namespace ugp {
 
 constexpr int kBlock = 256;     // threads of the streaming kernels (4 waves of 64)
-constexpr int kBatch = 8;       // items per thread loaded together (memory-level parallelism)
 constexpr uint32_t kMaxDim = 1u << 24;
 // s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left free (CDNA
 // encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)

@@ -1,19 +1,22 @@
-// kernels_reorder.h -- the gather reorder and the stable-order pass.
+// kernels_reorder.h -- the gather reorder (gather mode, ugp_reorder and
+// ugp_reorder_arrays) and the stable-order passes: the fix-up of the cells
+// the tile kernel could not order itself (tile paths), and the per-cell
+// sort after the atomic scatter (direct path).
 #pragma once
 
 #include "common.h"
 
 namespace ugp {
 
-constexpr int kGatherItems = 8;      // half-records per thread in the gather
-constexpr uint32_t kSmallSort = 16;  // cells up to this length are sorted in registers
-constexpr int kSortBlock = 1024;     // threads of the long-cell sort
-constexpr uint32_t kLdsSort = 16384; // longest cell sorted in LDS (64 KiB)
-constexpr int kSortGrid = 512;       // workgroups of the long-cell sort
-constexpr uint32_t kRecBatch = 8;         // records gathered together by one thread (long cells)
-constexpr uint32_t kBitmapPasses = 4;     // bitmap windows a long cell may take (2^21 index values)
+constexpr int kGatherItems = 8;            // half-records per thread in the gather
+constexpr uint32_t kSmallSort = 16;        // cells up to this length are sorted in registers
+constexpr int kSortBlock = 1024;           // threads of the long-cell sort
+constexpr uint32_t kLdsSort = 16384;       // longest cell sorted in LDS (64 KiB)
+constexpr int kSortGrid = 512;             // workgroups of the long-cell sort (direct path)
+constexpr uint32_t kRecBatch = 8;          // records gathered together by one thread (long cells)
+constexpr uint32_t kBitmapPasses = 4;      // bitmap windows a long cell may take (2^21 index values)
 constexpr uint32_t kFixLongBlocks = 128;   // fix-up workgroups on long cells
-constexpr uint32_t kFixShortBlocks = 256;  // fix-up workgroups on short cells, 64 cells per wave at a time
+constexpr uint32_t kFixShortBlocks = 256;  // fix-up workgroups on short cells
 
 // Gather: two lanes per record, each moving one 16-byte half, so every
 // store instruction writes a contiguous span. Indices >= n_src are skipped.

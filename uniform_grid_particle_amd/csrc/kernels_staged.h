@@ -1,5 +1,6 @@
-// kernels_staged.h -- the two-kernel index build (grids of up to 2^22 cells
-// and up to 2^21 particles; larger problems use kernels_tiled.h).
+// kernels_staged.h -- the two-kernel index build (up to 2^21 particles on
+// grids of up to 2^22 keys; the tile kernel also ends the bucketed path of
+// kernels_bucket.h and, alone, builds inputs that fit one tile).
 //
 // Measured on MI355X: a dependent kernel boundary costs about 2.6 us, a
 // device-scope global atomic is a memory-side operation (about 23 G/s for
@@ -28,14 +29,15 @@
 //               pass, then a pass that takes slots from LDS cursors and
 //               writes them directly.
 //
-// The workgroup sizes, the chunk size and the staging window are template
-// parameters; the host picks them per problem size.
+// The tile kernel is compiled per tile shift (4..14) and per variant:
+// records moved or not, overflow diagnostics, stable order, single tile.
 //
 // The result is the counting sort of the pages: exact histogram, exclusive
 // scan with the total in the extra slot, every particle inside its cell's
 // range; only the order inside a cell depends on LDS atomic arrival order,
 // as with the pages' atomic cursor (page "Construir el índice de la rejilla
-// con un prefix sum", section "El orden dentro de la celda").
+// con un prefix sum", section "El orden dentro de la celda"), unless the
+// stable variant puts it in particle-index order.
 #pragma once
 
 #include "common.h"
@@ -44,8 +46,8 @@
 namespace ugp {
 
 constexpr int kChunkItems = 8;                      // particles per chunk_sort thread
-constexpr uint32_t kStagedMaxTiles = 512;
-constexpr uint32_t kStagedMaxChunks = 1024;
+constexpr uint32_t kStagedMaxTiles = 512;            // tiles at most on the staged path (chunk_sort LDS bins)
+constexpr uint32_t kStagedMaxChunks = 1024;          // chunks at most (one row per chunk in tile_sort)
 constexpr int kStagedRegs = 8;                      // particles per tile_sort thread in registers
 constexpr uint32_t kShortRun = 64;                  // longest chunk run a thread expands by itself
 
@@ -54,7 +56,6 @@ constexpr uint32_t kShortRun = 64;                  // longest chunk run a threa
 // efficient, 2048-particle chunks let two chunk_sort workgroups share a CU).
 constexpr int kChunkThreads = 256;                  // chunk_sort workgroup
 constexpr uint32_t kChunk = kChunkThreads * kChunkItems;  // 2048 particles per chunk
-constexpr uint32_t kStagedTiles = 256;              // tiles at most (one tile_sort round)
 constexpr uint32_t kStagedMinShift = 4;            // at least 16 cells per tile
 constexpr uint32_t kStagedMaxShift = 14;            // up to 16384 cells per tile
 constexpr uint64_t kStagedTarget = 4096;            // mean particles per tile sought (half the capacity)
