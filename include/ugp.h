@@ -112,8 +112,9 @@ typedef struct ugp_particle {
  * ugp_grid_stage_name():
  *   n == 0            slot 0 "clear" (zero conteos and inicios); others empty
  *   n <= 8192 and K <= 2^14
- *                     -, -, -, "tile_sort" -- one launch: a single workgroup
- *                     reads the input, writes celdaDe and the whole index
+ *                     -, -, -, "tile_sort" -- one launch: up to 16 workgroups
+ *                     each read the whole input and build the index of their
+ *                     own cells, celdaDe included
  *   K <= 2^22 and n <= 2^21 (K up to 2^23 on dense grids)
  *                     "chunk_sort", -, -, "tile_sort" -- two kernels, no
  *                     global atomics, records moved through LDS

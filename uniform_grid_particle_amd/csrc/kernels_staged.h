@@ -61,6 +61,7 @@ constexpr uint32_t kStagedMaxShift = 14;            // up to 16384 cells per til
 constexpr uint64_t kStagedTarget = 4096;            // mean particles per tile sought (half the capacity)
 constexpr int kCellsThreads = 1024;                 // tile_sort workgroup
 constexpr uint32_t kSingleMax = kCellsThreads * kStagedRegs;  // particles one tile kernel workgroup stages
+constexpr uint32_t kSingleSplitLog = 4;             // single path: up to 2^4 tiles (no diagnostics, no stable order)
 constexpr uint32_t kCellsWin = 2048;                // tile_sort LDS staging window
 
 // Tile t's workgroup index, spreading consecutive tiles over workgroups of
@@ -168,10 +169,13 @@ __global__ __launch_bounds__(CT) void staged_keys_kernel(
 
 // tile_sort: NT threads; the tile of block b (tile_of_block) owns cells
 // [t << SHIFT, (t+1) << SHIFT); WIN records are staged in LDS at a time.
-// SINGLE: one workgroup, one tile over every cell; rows and chunk_idx are
-// not read (the one run is the input itself, chunk_rec = the particles, in
-// index order), and the kernel also writes each particle's key to keys_out
-// (celdaDe), which is not read otherwise.
+// SINGLE: inputs of at most kSingleMax particles; rows and chunk_idx are
+// not read: every workgroup loads the whole input as its one run
+// (chunk_rec = the particles, in index order), keeps the particles of its
+// own tile, counts those of earlier tiles for its first slot, and writes
+// its particles' keys to keys_out (celdaDe), which is not read otherwise.
+// With DIAG or STABLE the host launches a single tile: the words those
+// variants accumulate into are zeroed here by the workgroup itself.
 // MOVE: also write the records (otherwise a separate gather follows).
 // DIAG: also fold the tile's histogram into the overflow diagnostics
 // (diag[0] max occupancy, diag[1] overflowing insertions over capacity cap;
@@ -209,6 +213,7 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
   __shared__ uint32_t s_runmax[NT / 64];
   __shared__ uint32_t s_dm[DIAG ? NT / 64 : 1], s_do[DIAG ? NT / 64 : 1];
   __shared__ uint32_t s_any_long;  // stable: some cell of the tile is longer than kRankSortMax
+  __shared__ uint32_t s_below;  // SINGLE: particles in earlier tiles
 
   // one tile holding the whole input: no kernel runs before this one, so the
   // words it would zero are zeroed here, before the first barrier below
@@ -241,7 +246,8 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
   my_run = wave_inclusive_max(my_run);
   if ((threadIdx.x & 63) == 63) s_runmax[threadIdx.x >> 6] = my_run;  // visible after the next barrier
   uint32_t run_dst = block_exclusive_sum<NT>(len_sum, s_wave, &count);
-  const uint32_t bs = block_sum<NT>(pre_sum, s_wave);
+  // the tile's first slot (SINGLE: recomputed below from the particles' keys)
+  uint32_t bs = block_sum<NT>(pre_sum, s_wave);
   uint32_t longest_run = 0;
 #pragma unroll
   for (int w = 0; w < NT / 64; ++w) longest_run = (s_runmax[w] > longest_run) ? s_runmax[w] : longest_run;
@@ -256,6 +262,7 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
     run_dst += r[q].x;
   }
   for (uint32_t j = threadIdx.x; j < kTileCells; j += NT) s_cnt[j] = 0u;
+  if (SINGLE && threadIdx.x == 0) s_below = 0u;
   __syncthreads();
 
   // source map of a window of the tile: s_map[q] = chunk-array position of
@@ -377,7 +384,7 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
         dover += overflow_of(c, cap);
       }
     }
-    if (t == ntiles - 1 && threadIdx.x == 0) inicios[cells] = bs + count;
+    if (t == ntiles - 1 && threadIdx.x == 0) inicios[cells] = bs + tot;
     if (DIAG) {
       dmax = wave_max_u32(dmax);
       dover = wave_add_u32(dover);
@@ -421,9 +428,14 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
 #pragma unroll
       for (int k = 0; k < kStagedRegs; ++k) {
         const uint32_t p = threadIdx.x + k * NT;
-        const uint32_t loc = cell_of(__uint_as_float(w[0][k]), __uint_as_float(w[1][k]),
-                                     __uint_as_float(w[2][k]), g) - cell0;
+        const uint32_t key = cell_of(__uint_as_float(w[0][k]), __uint_as_float(w[1][k]),
+                                     __uint_as_float(w[2][k]), g);
+        const uint32_t loc = key - cell0;
         if (p < count && loc < tc) lr[k] = (loc << 16) | atomicAdd(&s_cnt[loc], 1u);
+        if (SINGLE) {  // particles of earlier tiles, one LDS atomic per wave
+          const uint64_t m = __ballot(p < count && key < cell0);
+          if ((threadIdx.x & 63) == 0 && m != 0ull) atomicAdd(&s_below, static_cast<uint32_t>(__popcll(m)));
+        }
       }
       // every record load of this thread has landed: the compiler then needs
       // no wait before using those registers after the stores below (one
@@ -436,6 +448,9 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
       }
     }
     __syncthreads();
+    // SINGLE: every workgroup read the whole input; its tile starts after the
+    // particles of the tiles before it
+    if (SINGLE) bs = s_below;
     const uint32_t tot = scan_tile();
     write_counts_starts(tot);  // overlaps the placement below
     uint32_t slot[kStagedRegs];
@@ -478,8 +493,8 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
         }
       }
     }
-    for (uint32_t w0 = 0; w0 < count; w0 += kStagedWin) {  // tile-uniform
-      const uint32_t wn = (count - w0 < kStagedWin) ? count - w0 : kStagedWin;
+    for (uint32_t w0 = 0; w0 < tot; w0 += kStagedWin) {  // tile-uniform
+      const uint32_t wn = (tot - w0 < kStagedWin) ? tot - w0 : kStagedWin;
 #pragma unroll
       for (int k = 0; k < kStagedRegs; ++k) {
         const uint32_t o = slot[k] - w0;

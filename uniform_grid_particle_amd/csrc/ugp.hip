@@ -444,9 +444,19 @@ void launch_tile_sort(const BuildArgs& a, const Plan& p, const uint2* rows, cons
 // indices) and writes celdaDe itself
 void enqueue_single(uint32_t stage, const BuildArgs& a, const Plan& p) {
   switch (stage) {
-    case 3:
-      launch_tile_sort<true>(a, p, nullptr, reinterpret_cast<const uint4*>(a.particles), nullptr);
+    case 3: {
+      // without diagnostics or stable order (whose words one workgroup zeroes
+      // for itself) the cells are split into up to 16 tiles, each workgroup
+      // reading the whole input: more than one CU on a latency-bound build
+      Plan q = p;
+      if (!p.stable && a.diag == nullptr) {
+        const uint32_t lg = p.tile_shift;  // the one tile covers 2^lg >= K keys
+        q.tile_shift = (lg > kStagedMinShift + kSingleSplitLog) ? lg - kSingleSplitLog : kStagedMinShift;
+        q.ntiles = static_cast<uint32_t>((p.cells + (1ull << q.tile_shift) - 1) >> q.tile_shift);
+      }
+      launch_tile_sort<true>(a, q, nullptr, reinterpret_cast<const uint4*>(a.particles), nullptr);
       break;
+    }
     case 4:
       if (p.stable) enqueue_stable_sort(a, p, static_cast<char*>(a.workspace));
       break;
