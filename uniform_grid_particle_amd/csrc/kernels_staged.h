@@ -56,6 +56,11 @@ constexpr uint32_t kShortRun = 64;                  // longest chunk run a threa
 // efficient, 2048-particle chunks let two chunk_sort workgroups share a CU).
 constexpr int kChunkThreads = 256;                  // chunk_sort workgroup
 constexpr uint32_t kChunk = kChunkThreads * kChunkItems;  // 2048 particles per chunk
+// inputs of up to kSmallChunkMaxN particles: 512-particle chunks, so that
+// more than a few dozen chunk_sort workgroups share the latency-bound work
+constexpr int kSmallChunkThreads = 64;
+constexpr uint32_t kSmallChunk = kSmallChunkThreads * kChunkItems;
+constexpr uint32_t kSmallChunkMaxN = 1u << 18;
 constexpr uint32_t kStagedMinShift = 4;            // at least 16 cells per tile
 constexpr uint32_t kStagedMaxShift = 14;            // up to 16384 cells per tile
 constexpr uint64_t kStagedTarget = 4096;            // mean particles per tile sought (half the capacity)
@@ -188,7 +193,7 @@ __global__ __launch_bounds__(CT) void staged_keys_kernel(
 // capacity, is written in arrival order and put on one of the fix-up lists.
 template <bool MOVE, bool DIAG, bool STABLE, bool SINGLE, uint32_t SHIFT, int NT, uint32_t WIN>
 __global__ __launch_bounds__(NT) void staged_cells_kernel(
-    const uint2* __restrict__ rows, uint32_t nchunks, uint32_t ntiles, GridParams g,
+    const uint2* __restrict__ rows, uint32_t nchunks, uint32_t chunk, uint32_t ntiles, GridParams g,
     uint32_t cells, uint32_t n, const uint4* __restrict__ chunk_rec,
     const uint32_t* __restrict__ chunk_idx, uint32_t* __restrict__ conteos,
     uint32_t* __restrict__ inicios, uint32_t* __restrict__ ordenado, uint4* __restrict__ dst,
@@ -257,7 +262,7 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
     const uint32_t c = threadIdx.x * kChunksPerThread + q;
     if (c < nchunks) {
       s_dst[c] = run_dst;
-      s_src[c] = c * kChunk + r[q].y;  // chunks of kChunk particles (bucketed: one chunk)
+      s_src[c] = c * chunk + r[q].y;  // chunks of `chunk` particles (bucketed, single: one chunk)
     }
     run_dst += r[q].x;
   }

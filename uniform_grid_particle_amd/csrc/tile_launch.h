@@ -12,10 +12,10 @@
 namespace ugp {
 
 #define UGP_TILE_LAUNCH_PARAMS                                                                     \
-  uint32_t shift, dim3 grid, hipStream_t s, const uint2 *rows, uint32_t nchunks, uint32_t ntiles, \
-      GridParams g, uint32_t cells, uint32_t n, const uint4 *chunk_rec, const uint32_t *chunk_idx, \
-      uint32_t *conteos, uint32_t *inicios, uint32_t *ordenado, uint4 *dst, uint32_t cap,          \
-      uint32_t *diag, FixLists fl, uint32_t *keys_out
+  uint32_t shift, dim3 grid, hipStream_t s, const uint2 *rows, uint32_t nchunks, uint32_t chunk,    \
+      uint32_t ntiles, GridParams g, uint32_t cells, uint32_t n, const uint4 *chunk_rec,           \
+      const uint32_t *chunk_idx, uint32_t *conteos, uint32_t *inicios, uint32_t *ordenado,         \
+      uint4 *dst, uint32_t cap, uint32_t *diag, FixLists fl, uint32_t *keys_out
 
 template <bool MOVE, bool DIAG, bool STABLE, bool SINGLE>
 void launch_staged_cells(UGP_TILE_LAUNCH_PARAMS);
@@ -23,12 +23,12 @@ void launch_staged_cells(UGP_TILE_LAUNCH_PARAMS);
 #ifdef UGP_TILE_LAUNCH_DEFINE
 template <bool MOVE, bool DIAG, bool STABLE, bool SINGLE, uint32_t SHIFT>
 void launch_staged_cells_at(dim3 grid, hipStream_t s, const uint2* rows, uint32_t nchunks,
-                            uint32_t ntiles, GridParams g, uint32_t cells, uint32_t n,
+                            uint32_t chunk, uint32_t ntiles, GridParams g, uint32_t cells, uint32_t n,
                             const uint4* chunk_rec, const uint32_t* chunk_idx, uint32_t* conteos,
                             uint32_t* inicios, uint32_t* ordenado, uint4* dst, uint32_t cap,
                             uint32_t* diag, FixLists fl, uint32_t* keys_out) {
   hipLaunchKernelGGL((staged_cells_kernel<MOVE, DIAG, STABLE, SINGLE, SHIFT, kCellsThreads, kCellsWin>), grid,
-                     dim3(kCellsThreads), 0, s, rows, nchunks, ntiles, g, cells, n, chunk_rec,
+                     dim3(kCellsThreads), 0, s, rows, nchunks, chunk, ntiles, g, cells, n, chunk_rec,
                      chunk_idx, conteos, inicios, ordenado, dst, cap, diag, fl, keys_out);
 }
 
@@ -36,8 +36,8 @@ template <bool MOVE, bool DIAG, bool STABLE, bool SINGLE>
 void launch_staged_cells(UGP_TILE_LAUNCH_PARAMS) {
 #define UGP_STAGED_CASE(S)                                                                       \
   case S:                                                                                        \
-    launch_staged_cells_at<MOVE, DIAG, STABLE, SINGLE, S>(grid, s, rows, nchunks, ntiles, g,     \
-                                                          cells, n, chunk_rec, chunk_idx,        \
+    launch_staged_cells_at<MOVE, DIAG, STABLE, SINGLE, S>(grid, s, rows, nchunks, chunk, ntiles, \
+                                                          g, cells, n, chunk_rec, chunk_idx,     \
                                                           conteos, inicios, ordenado, dst, cap,  \
                                                           diag, fl, keys_out);                   \
     break;

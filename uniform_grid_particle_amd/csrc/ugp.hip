@@ -75,6 +75,7 @@ struct Plan {
   bool move = true;     // the scatter kernel itself moves the records
   // tiled
   uint32_t tile_shift = kStagedMinShift, ntiles = 1, nblk = 0, per_block = 0;
+  uint32_t chunk = kChunk;  // particles per chunk_sort workgroup (staged path)
   size_t off_hist = 0, off_tile_total = 0;
   // staged
   uint32_t nchunks = 0;
@@ -155,7 +156,8 @@ int make_plan(uint32_t n, const uint32_t dims[3], uint32_t flags, Plan* p) {
   if (dense_shift < staged_shift) staged_shift = dense_shift;
   const uint32_t fewest_shift = (lg > kStagedMinShift + 9) ? lg - 9 : kStagedMinShift;  // 512 tiles
   if (staged_shift < fewest_shift) staged_shift = fewest_shift;
-  const uint64_t nchunks = (static_cast<uint64_t>(n) + kChunk - 1) / kChunk;
+  const uint32_t chunk = (n <= kSmallChunkMaxN) ? kSmallChunk : kChunk;
+  const uint64_t nchunks = (static_cast<uint64_t>(n) + chunk - 1) / chunk;
   if (p->path == Path::kSingle) {
     // no workspace beyond the stable-mode lists below
   } else if (staged_shift <= kStagedMaxShift && nchunks <= kStagedMaxChunks) {
@@ -163,6 +165,7 @@ int make_plan(uint32_t n, const uint32_t dims[3], uint32_t flags, Plan* p) {
     p->tile_shift = staged_shift;
     p->ntiles = static_cast<uint32_t>((cells + (1ull << staged_shift) - 1) >> staged_shift);
     p->nchunks = static_cast<uint32_t>(nchunks);
+    p->chunk = chunk;
     p->off_rows = off;
     off = align_up(off + static_cast<size_t>(p->nchunks) * p->ntiles * 8u, 256);
     p->off_chunk_rec = off;
@@ -425,8 +428,8 @@ void launch_tile_sort(const BuildArgs& a, const Plan& p, const uint2* rows, cons
   uint32_t* keys_out = SINGLE ? a.celdaDe : nullptr;
   // one instantiation per (moves records, diagnostics, stable order)
 #define UGP_TILE_SORT(M, D, S)                                                                        \
-  launch_staged_cells<M, D, S, SINGLE>(p.tile_shift, grid, s, rows, p.nchunks, p.ntiles, g, cells,   \
-                                       a.n, rec, idx, a.conteos, a.inicios, a.ordenado, dst,         \
+  launch_staged_cells<M, D, S, SINGLE>(p.tile_shift, grid, s, rows, p.nchunks, p.chunk, p.ntiles, g, \
+                                       cells, a.n, rec, idx, a.conteos, a.inicios, a.ordenado, dst,  \
                                        D ? a.capacity : 0u, D ? a.diag : nullptr, fl, keys_out)
   const bool m = p.move, d = a.diag != nullptr, st = p.stable;
   if (m && d && st) UGP_TILE_SORT(true, true, true);
@@ -476,10 +479,14 @@ void enqueue_staged(uint32_t stage, const BuildArgs& a, const Plan& p) {
   hipStream_t s = a.stream;
   switch (stage) {
     case 0:
-      hipLaunchKernelGGL(staged_keys_kernel<kChunkThreads>, dim3(p.nchunks), dim3(kChunkThreads), 0, s,
-                         reinterpret_cast<const uint4*>(a.particles), a.n, grid_params(a),
-                         a.celdaDe, rows, p.tile_shift, p.ntiles, chunk_rec, chunk_idx, a.diag,
-                         fix_lists_of(a, p).base);
+      if (p.chunk == kSmallChunk)
+        hipLaunchKernelGGL(staged_keys_kernel<kSmallChunkThreads>, dim3(p.nchunks), dim3(kSmallChunkThreads), 0,
+                           s, reinterpret_cast<const uint4*>(a.particles), a.n, grid_params(a), a.celdaDe, rows,
+                           p.tile_shift, p.ntiles, chunk_rec, chunk_idx, a.diag, fix_lists_of(a, p).base);
+      else
+        hipLaunchKernelGGL(staged_keys_kernel<kChunkThreads>, dim3(p.nchunks), dim3(kChunkThreads), 0, s,
+                           reinterpret_cast<const uint4*>(a.particles), a.n, grid_params(a), a.celdaDe, rows,
+                           p.tile_shift, p.ntiles, chunk_rec, chunk_idx, a.diag, fix_lists_of(a, p).base);
       break;
     case 3:
       launch_tile_sort<false>(a, p, rows, chunk_rec, chunk_idx);
