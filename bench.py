@@ -475,6 +475,9 @@ def main(argv=None) -> int:
     ap.add_argument("--mode", default="atomic", choices=["atomic", "gather", "stable"])
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle timing (0 = skip)")
     ap.add_argument("--no-neighbors", action="store_true", help="skip the neighbour-query section")
+    ap.add_argument("--presorted", action="store_true",
+                    help="time the workload's records already in cell order (the build's own reordered "
+                         "output of one untimed build), the secondary variant of the contention config")
     ap.add_argument("--copy-reference", action="store_true",
                     help="also run a 256 MiB device copy (counter calibration for rocprofv3 --pmc)")
     args = ap.parse_args(argv)
@@ -500,6 +503,15 @@ def main(argv=None) -> int:
     origin, h = [float(v) for v in wl.origin], float(wl.cell_size)
     flags = {"atomic": 0, "gather": ugp.FLAG_GATHER, "stable": ugp.FLAG_STABLE}[args.mode]
     parts = torch.from_numpy(wl.particles).to(dev)
+    if args.presorted:
+        # records in cell order: one untimed build's own reordered output (the
+        # order inside a cell is that build's); the oracle timing below then
+        # runs on the same records
+        first = ugp.grid_build(parts, origin, h, dims)
+        torch.cuda.synchronize()
+        parts = first.reordered.clone()
+        wl = workloads.Workload(wl.name + "_presorted", parts.cpu().numpy(), wl.origin, wl.cell_size, wl.dims)
+        del first
     out, ws = ugp.alloc_outputs(n, dims, dev, flags)
     flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB, read to evict caches
 
@@ -693,7 +705,7 @@ def main(argv=None) -> int:
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": WORKLOAD_NAMES[args.workload],
+            "workload": WORKLOAD_NAMES[args.workload] + (" (records pre-sorted by cell)" if args.presorted else ""),
             "n_particles": n,
             "dims": dims,
             "cells": cells,
