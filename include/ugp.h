@@ -205,10 +205,10 @@ int ugp_grid_build_stage(uint32_t stage, const ugp_particle *particles, uint32_t
  *             diag[1] = insertions that found their cell already holding
  *                       `capacity` or more particles
  *                     = sum_c max(0, conteos[c] - capacity).
- * Both are independent of the order of insertion. On grids of up to 2^22
- * cells with n <= 2^21 the reduction runs inside the tile kernel over its
- * LDS histogram (no extra memory traffic); otherwise a reduction over
- * conteos follows the scatter. Other arguments and errors as
+ * Both are independent of the order of insertion. On the tile paths (up to
+ * 2^26 keys) the reduction runs inside the tile kernel over its LDS
+ * histogram (no extra memory traffic); on the global-atomic path a
+ * reduction over conteos follows the scatter. Other arguments and errors as
  * ugp_grid_build(); UGP_ERR_NULL for a NULL diag. */
 int ugp_grid_build_diag(const ugp_particle *particles, uint32_t n, const float origin[3],
                         float cell_size, const uint32_t dims[3], uint32_t *celdaDe,
