@@ -443,13 +443,15 @@ def test_gpu_validation_errors(ugp):
         ugp.grid_build(torch.from_numpy(wl.particles), *args)  # CPU tensor: no CPU path
 
 
+@pytest.mark.parametrize("n,d", [(250_000, 128), (4_096, 16), (2_200_000, 128)])
 @pytest.mark.parametrize("mode", ["atomic", "stable"])
-def test_graph_capture_replays(ugp, orc, mode):
+def test_graph_capture_replays(ugp, orc, mode, n, d):
     """A build captured in a HIP graph replays correctly, several times, with
-    eager work (new particle data, an eager build) between the replays."""
+    eager work (new particle data, an eager build) between the replays, on
+    the staged, single-tile and bucketed paths."""
     dev = torch.device("cuda:0")
     flags = ugp.FLAG_STABLE if mode == "stable" else 0
-    wl0 = W.make_uniform(250_000, 128, seed=40)
+    wl0 = W.make_uniform(n, d, seed=40)
     parts = torch.from_numpy(wl0.particles).to(dev)
     args = (wl0.origin.tolist(), float(wl0.cell_size), wl0.dims.tolist())
     out, ws = ugp.alloc_outputs(wl0.n, wl0.dims.tolist(), dev, flags)
@@ -459,7 +461,7 @@ def test_graph_capture_replays(ugp, orc, mode):
     with torch.cuda.graph(graph):
         ugp.grid_build(parts, *args, stable=(mode == "stable"), out=out, workspace=ws)
     for rep in range(3):
-        wl = W.make_uniform(250_000, 128, seed=41 + rep)
+        wl = W.make_uniform(n, d, seed=41 + rep)
         parts.copy_(torch.from_numpy(wl.particles).to(dev))  # eager work between replays
         eager = ugp.grid_build(parts, *args, stable=(mode == "stable"))
         torch.cuda.synchronize()
