@@ -299,13 +299,53 @@ def test_empty_and_tiny_inputs(ugp, orc):
 @pytest.mark.parametrize("n", [16, 17, 5000, 16384, 16385, 40000])
 def test_one_cell_holds_everything(ugp, orc, n):
     """C = 1: every particle in one cell; long-cell sort paths in stable mode
-    (registers, LDS bitonic, and the ordered compaction beyond 16384)."""
+    (registers, the LDS bitmap of the index range, and the ordered compaction
+    beyond 16384)."""
     rng = np.random.Generator(np.random.PCG64(n))
     parts = rng.standard_normal((n, 8)).astype(np.float32)
     wl = W.Workload("one_cell", parts, np.zeros(3, np.float32), np.float32(1.0), np.array([1, 1, 1], np.uint32))
     ref = orc.grid_build(wl.particles, wl.origin, wl.cell_size, wl.dims)
     for mode in MODES:
         assert_parity(wl, run_gpu(ugp, wl, mode), ref, mode)
+
+
+@pytest.mark.parametrize("dims", [(128, 128, 128), (8192, 8193, 1)])
+def test_stable_long_cells_wide_index_range(ugp, orc, dims):
+    """Long cells whose indices span more than 2^21 values, too many for the
+    LDS bitmap: the stable fix-up's bitonic sort in LDS (about 300 and
+    16380 particles) and the ordered compaction beyond 16384, on the bucketed
+    path (2.3M particles) and on the direct path (more than 2^26 cells)."""
+    n = 2_300_000
+    print(f"[parity] wide long cells n={n} dims={dims}", flush=True)
+    assert ugp.stage_names(n, list(dims))[0] == ("keys" if dims[0] == 128 else "clear")
+    rng = np.random.Generator(np.random.PCG64(2300))
+    parts = rng.standard_normal((n, 8)).astype(np.float32)
+    h = 0.5
+    parts[:, :3] = (rng.random((n, 3)) * np.asarray(dims, np.float64) * h).astype(np.float32)
+    hot = [300, 16376, 16385]  # the uniform background adds a few to each
+    cells = set()
+    start = 0
+    for size in hot:
+        while True:
+            k = tuple(int(rng.integers(0, d)) for d in dims)
+            if k not in cells:
+                break
+        cells.add(k)
+        pos = (np.asarray(k, np.float64) + 0.25 + 0.5 * rng.random((size, 3))) * h
+        parts[start:start + size, :3] = pos.astype(np.float32)
+        start += size
+    parts = np.ascontiguousarray(parts[rng.permutation(n)])
+    wl = W.Workload("wide", parts, np.zeros(3, np.float32), np.float32(h), np.asarray(dims, np.uint32))
+    ref = orc.grid_build(wl.particles, wl.origin, wl.cell_size, wl.dims)
+    lens = []
+    for k in cells:
+        c = k[0] + k[1] * dims[0] + k[2] * dims[0] * dims[1]
+        s, e = int(ref.inicios[c]), int(ref.inicios[c + 1])
+        lens.append(e - s)
+        assert int(ref.ordenado[e - 1]) - int(ref.ordenado[s]) >= 1 << 21  # past four bitmap windows of 2^19
+    lens.sort()
+    assert 256 < lens[0] and lens[1] <= 16384 < lens[2], lens  # bitonic, bitonic, compaction
+    assert_parity(wl, run_gpu(ugp, wl, "stable"), ref, "stable")
 
 
 @pytest.mark.parametrize("seed", [3, 4])
