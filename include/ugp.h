@@ -127,9 +127,11 @@ typedef struct ugp_particle {
  *   de la rejilla con un prefix sum", section "El orden dentro de la
  *   celda"). On the two tile paths the tile kernel already puts every cell
  *   of up to 256 particles in ascending particle index and lists the rest;
- *   this slot orders the listed cells and copies their records from the
- *   input. On the direct path it orders every cell's slice and writes the
- *   records in that order. Slot 5 "gather" (UGP_FLAG_GATHER only). */
+ *   this slot orders the listed cells: those of up to 256 in place (indices
+ *   and records permuted inside the cell's slice), longer ones from a
+ *   workspace copy of their arrival order, records gathered from the input.
+ *   On the direct path it orders every cell's slice and writes the records
+ *   in that order. Slot 5 "gather" (UGP_FLAG_GATHER only). */
 #define UGP_NUM_STAGES 6u
 
 /* Number of cell keys K for a grid and flags: C = dims[0]*dims[1]*dims[2]

@@ -29,6 +29,11 @@ struct FixLists {
   __device__ __forceinline__ uint32_t* counts() const { return base; }
   __device__ __forceinline__ uint32_t* fix() const { return base + kFixHeader; }
   __device__ __forceinline__ uint32_t* lng() const { return base + kFixHeader + fix_cap; }
+  // one word per output place: the arrival-order index, written by the tile
+  // kernel for every tile that holds a long cell or overflows its staging,
+  // so the long-cell fix-up reads the cell's indices from a copy it does not
+  // itself rewrite
+  __device__ __forceinline__ uint32_t* idx() const { return base + kFixHeader + fix_cap + long_cap; }
 };
 
 // Puts the cells of the calling wave's lanes with `listed` set on the list

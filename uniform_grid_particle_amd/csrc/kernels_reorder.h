@@ -15,6 +15,7 @@ constexpr uint32_t kLdsSort = 16384;       // longest cell sorted in LDS (64 KiB
 constexpr int kSortGrid = 512;             // workgroups of the long-cell sort (direct path)
 constexpr uint32_t kRecBatch = 8;          // records gathered together by one thread (long cells)
 constexpr uint32_t kBitmapPasses = 4;      // bitmap windows a long cell may take (2^21 index values)
+constexpr uint32_t kMinPart = 1024;        // fewest places of a shared long cell one workgroup takes
 constexpr uint32_t kFixLongBlocks = 128;   // fix-up workgroups on long cells
 constexpr uint32_t kFixShortBlocks = 256;  // fix-up workgroups on short cells
 
@@ -248,18 +249,43 @@ __device__ __forceinline__ void copy_cell_records(uint32_t s, uint32_t len, uint
 // append those of this cell (the cell's membership is exact already; only
 // order changes). Each way writes indices only; RECS: the records follow in
 // one pass over the ordered slice (copy_cell_records).
-template <bool RECS>
+//
+// SHARE: the cell's arrival-order indices are read from `arrival` (at the
+// same places), which nothing writes meanwhile, so with fewer cells than
+// workgroups stride / count workgroups can share a cell of up to kLdsSort:
+// each finds every place as above, which costs little next to the stores
+// and the record gathers, and writes and gathers only its own share
+// [p0, p1) of the places (at least kMinPart of them). No workgroup waits
+// for another. Without SHARE the indices are read from ordenado itself and
+// a cell has one workgroup.
+template <bool RECS, bool SHARE>
 __device__ __forceinline__ void sort_long_cells(
     const uint32_t* __restrict__ inicios, const uint32_t* __restrict__ celdaDe, uint32_t n,
     const uint32_t* __restrict__ long_list, uint32_t count, uint32_t first, uint32_t stride,
-    uint32_t* __restrict__ ordenado, const uint4* __restrict__ particles, uint4* __restrict__ reordered,
-    uint32_t* s_keys, uint32_t* s_wave) {
+    const uint32_t* arrival, uint32_t* __restrict__ ordenado, const uint4* __restrict__ particles,
+    uint4* __restrict__ reordered, uint32_t* s_keys, uint32_t* s_wave) {
+  const uint32_t* src = SHARE ? arrival : ordenado;
+  uint32_t share = 1, part = 0;
+  if (SHARE && count != 0u && count < stride) {
+    share = stride / count;
+    part = first % share;
+    first /= share;
+    stride = count;  // one cell per workgroup
+  }
   for (uint32_t k = first; k < count; k += stride) {
     const uint32_t c = long_list[k];
     const uint32_t s = inicios[c];
     const uint32_t e = inicios[c + 1];
     if (e <= s || e > n) continue;  // uniform across the workgroup
     const uint32_t len = e - s;
+    uint32_t parts = 1;
+    if (len <= kLdsSort) {
+      parts = (len + kMinPart - 1u) / kMinPart;
+      parts = (parts < share) ? parts : share;
+    }
+    if (part >= parts) continue;
+    const uint32_t p0 = static_cast<uint32_t>(static_cast<uint64_t>(len) * part / parts);
+    const uint32_t p1 = static_cast<uint32_t>(static_cast<uint64_t>(len) * (part + 1u) / parts);
     if (len <= kLdsSort) {
       constexpr uint32_t kPer = kLdsSort / kSortBlock;  // entries (and bitmap words) per thread
       constexpr uint32_t kWindow = kLdsSort * 32u;      // indices per bitmap window
@@ -268,7 +294,7 @@ __device__ __forceinline__ void sort_long_cells(
 #pragma unroll
       for (uint32_t q = 0; q < kPer; ++q) {
         const uint32_t t = threadIdx.x + q * kSortBlock;
-        v[q] = (t < len) ? ordenado[s + t] : 0u;
+        v[q] = (t < len) ? src[s + t] : 0u;
         if (t < len) {
           lo = (v[q] < lo) ? v[q] : lo;
           hi = (v[q] > hi) ? v[q] : hi;
@@ -297,25 +323,30 @@ __device__ __forceinline__ void sort_long_cells(
           uint32_t total;
           uint32_t pos = placed + block_exclusive_sum<kSortBlock>(bits, s_wave, &total);
 #pragma unroll 1
-          for (uint32_t q = 0; q < kPer; ++q) {
+          for (uint32_t q = 0; q < kPer && pos < p1; ++q) {
             uint32_t w = s_keys[threadIdx.x * kPer + q];
+            const uint32_t past = pos + __popc(w);
+            if (past <= p0) {  // every bit of this word has its place before the share
+              pos = past;
+              continue;
+            }
             while (w != 0u) {  // stores only: nothing to wait for between bits
               const uint32_t idx = static_cast<uint32_t>(base) + (threadIdx.x * kPer + q) * 32u + __builtin_ctz(w);
               w &= w - 1u;
-              if (pos < len) ordenado[s + pos] = idx;
+              if (pos >= p0 && pos < p1) ordenado[s + pos] = idx;
               ++pos;
             }
           }
           placed += total;
           __syncthreads();  // this window's reads end before the next one is cleared
         }
-        if (RECS) copy_cell_records(s, len, n, ordenado, particles, reordered);
+        if (RECS) copy_cell_records(s + p0, p1 - p0, n, ordenado, particles, reordered);
         continue;
       }
       uint32_t L = 1;
       while (L < len) L <<= 1;
       for (uint32_t t = threadIdx.x; t < L; t += kSortBlock)
-        s_keys[t] = (t < len) ? ordenado[s + t] : 0xFFFFFFFFu;
+        s_keys[t] = (t < len) ? src[s + t] : 0xFFFFFFFFu;
       __syncthreads();
       for (uint32_t kk = 2; kk <= L; kk <<= 1) {
         for (uint32_t j = kk >> 1; j > 0; j >>= 1) {
@@ -332,8 +363,8 @@ __device__ __forceinline__ void sort_long_cells(
           __syncthreads();
         }
       }
-      for (uint32_t t = threadIdx.x; t < len; t += kSortBlock) ordenado[s + t] = s_keys[t];
-      if (RECS) copy_cell_records(s, len, n, ordenado, particles, reordered);
+      for (uint32_t t = p0 + threadIdx.x; t < p1; t += kSortBlock) ordenado[s + t] = s_keys[t];
+      if (RECS) copy_cell_records(s + p0, p1 - p0, n, ordenado, particles, reordered);
       __syncthreads();
     } else {
       uint32_t run = 0;
@@ -362,19 +393,23 @@ __global__ __launch_bounds__(kSortBlock) void sort_long_cells_kernel(
   __shared__ uint32_t s_wave[kSortBlock / 64];
   uint32_t count = *long_count;
   if (count > long_cap) count = long_cap;
-  sort_long_cells<RECS>(inicios, celdaDe, n, long_list, count, blockIdx.x, gridDim.x, ordenado, particles,
-                        reordered, s_keys, s_wave);
+  sort_long_cells<RECS, false>(inicios, celdaDe, n, long_list, count, blockIdx.x, gridDim.x, nullptr, ordenado,
+                               particles, reordered, s_keys, s_wave);
 }
 
 // Stable mode on the tile paths: the one pass over the cells the tile
 // kernel left in arrival order (FixLists). Workgroups below long_blocks
-// sort the long cells as above; every wave of the others takes 64 entries
-// of the short list at a time (cells of at most kRankSortMax): a lane sorts
-// a cell of up to kSmallSort in registers; a longer one is taken by the
-// whole wave: its indices go to the wave's LDS slice, each lane counts the
-// indices below its own (distinct, so that count is its place) and writes
-// it there. Records are read from the input by index. LDS is shared by the
-// two roles.
+// take the long cells (sort_long_cells, reading the arrival order from
+// fl.idx(), so that several of them can share one cell). In the others the
+// listed short cells are permuted in place inside their slices, where the
+// tile kernel put their indices and (RECS) records: groups of 16 lanes take
+// the cells of up to kSmallSort (lane j holds entry j; its place is the
+// number of smaller indices among the group's, counted with lane shuffles),
+// then whole waves take the cells of up to kRankSortMax (each lane holds up
+// to kRankSortMax / 64 entries; the cell's indices go to the wave's LDS
+// slice and each lane counts the ones below its own). Every entry is read
+// before any is written back, so the permutation in place is safe. LDS is
+// shared by the two roles.
 template <bool RECS>
 __global__ __launch_bounds__(kSortBlock) void fix_cells_kernel(
     const uint32_t* __restrict__ inicios, const uint32_t* __restrict__ celdaDe, uint32_t cells, uint32_t n,
@@ -382,14 +417,16 @@ __global__ __launch_bounds__(kSortBlock) void fix_cells_kernel(
     uint4* __restrict__ reordered) {
   constexpr uint32_t kWaves = kSortBlock / 64;
   static_assert(kWaves * kRankSortMax <= kLdsSort, "one slice per wave fits the long-cell buffer");
-  static_assert(kRankSortMax % 4 == 0, "slices are read four entries at a time");
+  constexpr uint32_t kWaveEntries = kRankSortMax / 64;  // entries per lane in the wave pass
+  static_assert(kRankSortMax % 64 == 0, "whole entries per lane");
+  static_assert(kSmallSort == 16, "one group of 16 lanes per short cell");
   __shared__ __align__(16) uint32_t s_keys[kLdsSort];  // slices read as uint4
   __shared__ uint32_t s_wave[kWaves];
   if (blockIdx.x < long_blocks) {
     uint32_t count = fl.counts()[1];
     if (count > fl.long_cap) count = fl.long_cap;
-    sort_long_cells<RECS>(inicios, celdaDe, n, fl.lng(), count, blockIdx.x, long_blocks, ordenado, particles,
-                          reordered, s_keys, s_wave);
+    sort_long_cells<RECS, true>(inicios, celdaDe, n, fl.lng(), count, blockIdx.x, long_blocks, fl.idx(),
+                                ordenado, particles, reordered, s_keys, s_wave);
     return;
   }
   const uint32_t lane = threadIdx.x & 63u;
@@ -403,38 +440,74 @@ __global__ __launch_bounds__(kSortBlock) void fix_cells_kernel(
     const uint32_t a = inicios[c], e = inicios[c + 1];
     return (e > a && e <= n && e - a <= kRankSortMax) ? make_uint2(a, e - a) : make_uint2(0u, 0u);
   };
-  const uint32_t first_thread = (blockIdx.x - long_blocks) * kSortBlock + threadIdx.x;
-  const uint32_t threads = (gridDim.x - long_blocks) * kSortBlock;
-  // a thread per entry: cells of up to kSmallSort, sorted in registers
-  for (uint32_t k = first_thread; k < count; k += threads) {
+  const uint32_t role_thread = (blockIdx.x - long_blocks) * kSortBlock + threadIdx.x;
+  const uint32_t role_threads = (gridDim.x - long_blocks) * kSortBlock;
+  // groups of 16 lanes: cells of up to kSmallSort
+  const uint32_t gl = threadIdx.x & 15u;
+  for (uint32_t k = role_thread >> 4; k < count; k += role_threads >> 4) {  // uniform across the group
     const uint2 sl = listed(k);
-    if (sl.y >= 2u && sl.y <= kSmallSort) sort_cell_in_registers<RECS, true, 2>(sl.x, sl.y, n, ordenado, particles, reordered);
+    if (sl.y < 2u || sl.y > kSmallSort) continue;
+    const bool has = gl < sl.y;
+    const uint32_t mine = has ? ordenado[sl.x + gl] : 0xFFFFFFFFu;  // all ones: no index reaches it
+    uint4 ra = make_uint4(0u, 0u, 0u, 0u), rb = ra;
+    if (RECS && has) {
+      ra = reordered[2ull * (sl.x + gl)];
+      rb = reordered[2ull * (sl.x + gl) + 1u];
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitLoadsAndStores);  // every entry read before any is written back
+    uint32_t rank = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) rank += (static_cast<uint32_t>(__shfl(static_cast<int>(mine), i, 16)) < mine) ? 1u : 0u;
+    if (has) {
+      ordenado[sl.x + rank] = mine;
+      if (RECS) {
+        reordered[2ull * (sl.x + rank)] = ra;
+        reordered[2ull * (sl.x + rank) + 1u] = rb;
+      }
+    }
   }
-  // a wave per entry: the longer cells
-  for (uint32_t k = first_thread >> 6; k < count; k += threads >> 6) {  // uniform across the wave
+  // whole waves: cells of kSmallSort + 1 .. kRankSortMax
+  for (uint32_t k = role_thread >> 6; k < count; k += role_threads >> 6) {  // uniform across the wave
     const uint2 sl = listed(k);
     if (sl.y <= kSmallSort) continue;
     const uint32_t cs = sl.x, cl = sl.y, cl4 = (cl + 3u) & ~3u;
-    // all ones pads the slice: no index reaches it
-    for (uint32_t q = lane; q < cl4; q += 64u) slice[q] = (q < cl) ? ordenado[cs + q] : 0xFFFFFFFFu;
+    uint32_t mine[kWaveEntries];
+    uint4 ra[kWaveEntries], rb[kWaveEntries];
+#pragma unroll
+    for (uint32_t g = 0; g < kWaveEntries; ++g) {
+      const uint32_t q = g * 64u + lane;
+      mine[g] = (q < cl) ? ordenado[cs + q] : 0xFFFFFFFFu;  // all ones pads the slice: no index reaches it
+      ra[g] = rb[g] = make_uint4(0u, 0u, 0u, 0u);
+      if (RECS && q < cl) {
+        ra[g] = reordered[2ull * (cs + q)];
+        rb[g] = reordered[2ull * (cs + q) + 1u];
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitLoadsAndStores);  // every entry read before any is written back
+#pragma unroll
+    for (uint32_t g = 0; g < kWaveEntries; ++g)
+      if (g * 64u + lane < cl4) slice[g * 64u + lane] = mine[g];
     // a wave's LDS accesses complete in order: the slice is whole for
     // every lane after this point
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    for (uint32_t g = 0; g < cl; g += 64u) {
-      const uint32_t q = g + lane;
-      const uint32_t mine = (q < cl) ? slice[q] : 0xFFFFFFFFu;
-      uint32_t rank = 0;
-      for (uint32_t j = 0; j < cl4; j += 4u) {  // the same address for every lane
-        const uint4 v = *reinterpret_cast<const uint4*>(slice + j);
-        rank += (v.x < mine ? 1u : 0u) + (v.y < mine ? 1u : 0u) + (v.z < mine ? 1u : 0u) + (v.w < mine ? 1u : 0u);
-      }
-      if (q < cl) {
-        ordenado[cs + rank] = mine;
-        if (RECS && mine < n) {
-          reordered[2ull * (cs + rank)] = particles[2ull * mine];
-          reordered[2ull * (cs + rank) + 1u] = particles[2ull * mine + 1u];
+#pragma unroll
+    for (uint32_t g = 0; g < kWaveEntries; ++g) {
+      const uint32_t q = g * 64u + lane;
+      if (g * 64u < cl) {  // uniform across the wave
+        uint32_t rank = 0;
+        for (uint32_t j = 0; j < cl4; j += 4u) {  // the same address for every lane
+          const uint4 w4 = *reinterpret_cast<const uint4*>(slice + j);
+          rank += (w4.x < mine[g] ? 1u : 0u) + (w4.y < mine[g] ? 1u : 0u) + (w4.z < mine[g] ? 1u : 0u) +
+                  (w4.w < mine[g] ? 1u : 0u);
+        }
+        if (q < cl) {
+          ordenado[cs + rank] = mine[g];
+          if (RECS) {
+            reordered[2ull * (cs + rank)] = ra[g];
+            reordered[2ull * (cs + rank) + 1u] = rb[g];
+          }
         }
       }
     }

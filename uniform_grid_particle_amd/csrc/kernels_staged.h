@@ -462,6 +462,7 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
 #pragma unroll
     for (int k = 0; k < kStagedRegs; ++k)
       slot[k] = (lr[k] != 0xFFFFFFFFu) ? s_cnt[lr[k] >> 16] + (lr[k] & 0xFFFFu) : 0xFFFFFFFFu;
+    bool any_long = false;  // stable: the tile's indices also go to fl.idx()
     if (STABLE) {
       // every index at its arrival slot (the source map is dead: s_rec is
       // free); then each particle of a cell of up to kRankSortMax counts
@@ -489,7 +490,8 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
         }
       }
       __syncthreads();  // every rank counted before the window loop reuses s_rec
-      if (s_any_long != 0u) {
+      any_long = s_any_long != 0u;
+      if (any_long) {
         for (uint32_t j0 = 0; j0 < tc; j0 += NT) {  // whole waves: the listing is per wave
           const uint32_t j = j0 + threadIdx.x;
           const uint32_t a = (j < tc) ? s_cnt[j] : 0u;
@@ -513,8 +515,12 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
       }
       __syncthreads();
       const size_t out0 = static_cast<size_t>(bs) + w0;
-      for (uint32_t q = threadIdx.x; q < wn; q += NT)
-        if (out0 + q < n) ordenado[out0 + q] = s_idx[q];
+      for (uint32_t q = threadIdx.x; q < wn; q += NT) {
+        if (out0 + q < n) {
+          ordenado[out0 + q] = s_idx[q];
+          if (STABLE && any_long) fl.idx()[out0 + q] = s_idx[q];
+        }
+      }
       if (MOVE) {
         for (uint32_t q = threadIdx.x; q < 2 * wn; q += NT)
           if (out0 * 2u + q < 2ull * n) dst[out0 * 2u + q] = s_rec[q];
@@ -599,12 +605,47 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
     if (STABLE) {
       // slots were taken in arrival order: every cell of two or more is
       // listed. Once every cursor is final it holds its cell's end, so a
-      // cell's count is its end minus the previous cell's.
+      // cell's count is its end minus the previous cell's. The long cells
+      // (tile-local numbers in s_idx, free now) then have their indices
+      // copied to fl.idx() for the fix-up; a tile with more of them than
+      // s_idx holds copies its whole range.
+      if (threadIdx.x == 0) s_any_long = 0u;
       __syncthreads();
       for (uint32_t j0 = 0; j0 < tc; j0 += NT) {  // whole waves: the listing is per wave
         const uint32_t j = j0 + threadIdx.x;
         const uint32_t len = (j < tc) ? s_cnt[j] - (j ? s_cnt[j - 1u] : 0u) : 0u;
         list_cells_wave(fl, cell0 + j, len, len >= 2u);
+        if (len > kRankSortMax) {
+          const uint32_t at = atomicAdd(&s_any_long, 1u);
+          if (at < kStagedWin) s_idx[at] = j;
+        }
+      }
+      __syncthreads();  // the list is whole, and this workgroup's ordenado stores are visible to it
+      const uint32_t nl = s_any_long;
+      const uint32_t places = n - bs;  // this tile's places that exist
+      const uint32_t* from = ordenado + bs;
+      uint32_t* to = fl.idx() + bs;
+      for (uint32_t l = 0; l < ((nl <= kStagedWin) ? nl : 1u); ++l) {  // tile-uniform
+        uint32_t a = 0u, e = count;
+        if (nl <= kStagedWin) {
+          const uint32_t j = s_idx[l];
+          a = j ? s_cnt[j - 1u] : 0u;
+          e = s_cnt[j];
+        }
+        e = (e < places) ? e : places;
+        for (uint32_t q0 = a; q0 < e; q0 += NT * kStagedRegs) {
+          uint32_t v[kStagedRegs];
+#pragma unroll
+          for (int k = 0; k < kStagedRegs; ++k) {
+            const uint32_t loc = q0 + threadIdx.x + static_cast<uint32_t>(k) * NT;
+            v[k] = (loc < e && loc >= q0) ? from[loc] : 0u;  // loc >= q0: no wrap past 2^32
+          }
+#pragma unroll
+          for (int k = 0; k < kStagedRegs; ++k) {
+            const uint32_t loc = q0 + threadIdx.x + static_cast<uint32_t>(k) * NT;
+            if (loc < e && loc >= q0) to[loc] = v[k];
+          }
+        }
       }
     }
   }

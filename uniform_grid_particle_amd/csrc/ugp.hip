@@ -215,11 +215,12 @@ int make_plan(uint32_t n, const uint32_t dims[3], uint32_t flags, Plan* p) {
         p->off_unstable = off;
         off = align_up(off + static_cast<size_t>(n) * 32u, 256);
       }
-    } else {  // FixLists: header, short list (one entry per cell of two or more), long list
+    } else {  // FixLists: header, short list (one entry per cell of two or more), long list,
+              // arrival-order indices of the tiles with a long cell (n words)
       const uint64_t fcap = static_cast<uint64_t>(n) / 2 + 1;
       p->fix_cap = static_cast<uint32_t>(fcap < cells ? fcap : cells);
       p->off_fix = off;
-      off = align_up(off + (static_cast<size_t>(kFixHeader) + p->fix_cap + p->long_cap) * 4u, 256);
+      off = align_up(off + (static_cast<size_t>(kFixHeader) + p->fix_cap + p->long_cap + n) * 4u, 256);
     }
   }
   p->total = off ? off : 256;
