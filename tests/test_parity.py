@@ -180,6 +180,29 @@ def test_tile_sizes(ugp, orc, dims):
         assert_parity(wl, run_gpu(ugp, wl, mode), ref, mode)
 
 
+@pytest.mark.parametrize("n,dims", [
+    (1 << 21, (128, 128, 128)),  # the staged path's largest input: 1024 chunks, one row per tile-kernel thread
+    (1 << 21, (161, 161, 161)),  # and with 2^22 keys (tiles of 16384 cells)
+    (1 << 18, (64, 64, 64)),     # the last input of 512-particle chunks
+    ((1 << 18) + 1, (64, 64, 64)),  # the first of 2048-particle chunks
+    (8193, (16, 16, 16)),        # one past the single-launch path
+])
+def test_staged_path_limits(ugp, orc, n, dims):
+    """The staged path at the sizes where its layout changes."""
+    print(f"[parity] staged limits n={n} dims={dims}", flush=True)
+    assert ugp.stage_names(n, list(dims))[:4] == ["chunk_sort", None, None, "tile_sort"]
+    rng = np.random.Generator(np.random.PCG64(n + dims[0]))
+    parts = rng.standard_normal((n, 8)).astype(np.float32)
+    ext = np.asarray(dims, np.float64) * 0.25
+    parts[:, :3] = (rng.random((n, 3)) * ext * 1.04 - 0.02 * ext).astype(np.float32)
+    m = rng.random(n) < 0.05  # a dense clump
+    parts[m, :3] = (ext * 0.4 + rng.standard_normal((int(m.sum()), 3)) * 0.3).astype(np.float32)
+    wl = W.Workload("limits", parts, np.zeros(3, np.float32), np.float32(0.25), np.asarray(dims, np.uint32))
+    ref = orc.grid_build(wl.particles, wl.origin, wl.cell_size, wl.dims)
+    for mode in MODES:
+        assert_parity(wl, run_gpu(ugp, wl, mode), ref, mode)
+
+
 @pytest.mark.parametrize("d", [16, 24, 32, 40, 64])
 def test_dense_grids(ugp, orc, d):
     """1M particles on coarse grids (about 244, 72, 30, 16 and 4 per cell):
