@@ -504,6 +504,16 @@ def test_gpu_validation_errors(ugp):
     assert e.value.status == ugp.UGP_ERR_ARG
     with pytest.raises(ValueError):
         ugp.grid_build(torch.from_numpy(wl.particles), *args)  # CPU tensor: no CPU path
+    idx = torch.arange(wl.n, dtype=torch.int32, device=dev)
+    with pytest.raises(ValueError):  # one record short: refused before anything is enqueued
+        ugp.reorder(parts, idx, out=torch.empty((wl.n - 1, 8), dtype=torch.float32, device=dev))
+    with pytest.raises(ValueError):  # an output on the host
+        ugp.grid_build(parts, *args, out=ugp.GridIndex(out.celdaDe.cpu(), out.conteos, out.inicios, out.ordenado,
+                                                       out.reordered), workspace=ws)
+    r, _ = ugp.alloc_outputs(wl.n, wl.dims.tolist(), dev)  # outputs given, workspace allocated
+    ugp.grid_build(parts, *args, out=r)
+    torch.cuda.synchronize()
+    assert int(r.inicios[-1].item()) == wl.n
 
 
 @pytest.mark.parametrize("n,d", [(250_000, 128), (4_096, 16), (2_200_000, 128)])

@@ -130,13 +130,21 @@ def _stream_handle(device: torch.device, stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _require_gpu(t: torch.Tensor, name: str, dtype: torch.dtype):
+def _require_gpu(t: torch.Tensor, name: str, dtype: Optional[torch.dtype], device: Optional[torch.device] = None):
+    """A contiguous GPU tensor of `dtype` (None: any), on `device` if given."""
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor (no CPU path exists)")
-    if t.dtype != dtype:
+    if dtype is not None and t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the other arrays on {device}")
+
+
+def _on(device: torch.device):
+    """The library launches on the current device: make it the arrays' one."""
+    return torch.cuda.device(device)
 
 
 def _dims3(dims) -> tuple[int, int, int]:
@@ -191,32 +199,40 @@ class GridIndex:
 
 def alloc_outputs(n: int, dims: Sequence[int], device, flags: int = 0):
     """Output tensors and the workspace for one build (torch allocations)."""
+    return _fill_in(n, dims, device, flags, None, None)
+
+
+def _fill_in(n: int, dims, device, flags: int, out: Optional[GridIndex], workspace: Optional[torch.Tensor]):
+    """Allocate the outputs and/or the workspace the caller did not pass."""
     d = _dims3(dims)
-    cells = key_count(d, flags)
     dev = torch.device(device)
-    out = GridIndex(
-        celdaDe=torch.empty(n, dtype=torch.int32, device=dev),
-        conteos=torch.empty(cells, dtype=torch.int32, device=dev),
-        inicios=torch.empty(cells + 1, dtype=torch.int32, device=dev),
-        ordenado=torch.empty(n, dtype=torch.int32, device=dev),
-        reordered=torch.empty((0 if flags & FLAG_INDEX_ONLY else n, 8), dtype=torch.float32, device=dev),
-    )
-    ws = torch.empty(max(workspace_bytes(n, d, flags), 256), dtype=torch.uint8, device=dev)
-    return out, ws
+    if out is None:
+        cells = key_count(d, flags)
+        out = GridIndex(
+            celdaDe=torch.empty(n, dtype=torch.int32, device=dev),
+            conteos=torch.empty(cells, dtype=torch.int32, device=dev),
+            inicios=torch.empty(cells + 1, dtype=torch.int32, device=dev),
+            ordenado=torch.empty(n, dtype=torch.int32, device=dev),
+            reordered=torch.empty((0 if flags & FLAG_INDEX_ONLY else n, 8), dtype=torch.float32, device=dev),
+        )
+    if workspace is None:
+        workspace = torch.empty(max(workspace_bytes(n, d, flags), 256), dtype=torch.uint8, device=dev)
+    return out, workspace
 
 
 def _build_args(particles, origin, cell_size, dims, out: GridIndex, workspace, flags, stream):
     _require_gpu(particles, "particles", torch.float32)
     if particles.dim() != 2 or particles.shape[1] != 8:
         raise ValueError("particles must have shape (N, 8) (32-byte records)")
+    dev = particles.device
     n = int(particles.shape[0])
     d = _dims3(dims)
     for name in ("celdaDe", "conteos", "inicios", "ordenado"):
-        _require_gpu(getattr(out, name), name, torch.int32)
+        _require_gpu(getattr(out, name), name, torch.int32, dev)
     index_only = bool(flags & FLAG_INDEX_ONLY)
     if not index_only:
-        _require_gpu(out.reordered, "reordered", torch.float32)
-    _require_gpu(workspace, "workspace", torch.uint8)
+        _require_gpu(out.reordered, "reordered", torch.float32, dev)
+    _require_gpu(workspace, "workspace", torch.uint8, dev)
     cells = key_count(d, flags)
     if out.celdaDe.numel() < n or out.ordenado.numel() < n or (not index_only and out.reordered.numel() < 8 * n):
         raise ValueError("per-particle outputs are smaller than N")
@@ -250,12 +266,10 @@ def grid_build(
     lib = load_library()
     flags = _flags(stable, gather, morton) | (FLAG_INDEX_ONLY if index_only else 0)
     n = int(particles.shape[0])
-    if out is None or workspace is None:
-        o2, w2 = alloc_outputs(n, dims, particles.device, flags)
-        out = out or o2
-        workspace = workspace if workspace is not None else w2
+    out, workspace = _fill_in(n, dims, particles.device, flags, out, workspace)
     args = _build_args(particles, origin, cell_size, dims, out, workspace, flags, stream)
-    _check(lib.ugp_grid_build(*args), "ugp_grid_build")
+    with _on(particles.device):
+        _check(lib.ugp_grid_build(*args), "ugp_grid_build")
     return out
 
 
@@ -279,17 +293,15 @@ def grid_build_diag(
     lib = load_library()
     flags = _flags(stable, gather, morton)
     n = int(particles.shape[0])
-    if out is None or workspace is None:
-        o2, w2 = alloc_outputs(n, dims, particles.device, flags)
-        out = out or o2
-        workspace = workspace if workspace is not None else w2
+    out, workspace = _fill_in(n, dims, particles.device, flags, out, workspace)
     if diag is None:
         diag = torch.empty(2, dtype=torch.int32, device=particles.device)
-    _require_gpu(diag, "diag", torch.int32)
+    _require_gpu(diag, "diag", torch.int32, particles.device)
     if diag.numel() < 2:
         raise ValueError("diag needs 2 entries")
     args = _build_args(particles, origin, cell_size, dims, out, workspace, flags, stream)
-    _check(lib.ugp_grid_build_diag(*args[:-2], int(capacity), _ptr(diag), *args[-2:]), "ugp_grid_build_diag")
+    with _on(particles.device):
+        _check(lib.ugp_grid_build_diag(*args[:-2], int(capacity), _ptr(diag), *args[-2:]), "ugp_grid_build_diag")
     return out, diag
 
 
@@ -300,11 +312,12 @@ def cell_diag(conteos: torch.Tensor, capacity: int, out: Optional[torch.Tensor] 
     _require_gpu(conteos, "conteos", torch.int32)
     if out is None:
         out = torch.empty(2, dtype=torch.int32, device=conteos.device)
-    _require_gpu(out, "out", torch.int32)
+    _require_gpu(out, "out", torch.int32, conteos.device)
     if out.numel() < 2:
         raise ValueError("out needs 2 entries")
-    st = lib.ugp_cell_diag(_ptr(conteos), int(conteos.numel()), int(capacity), _ptr(out),
-                           _stream_handle(conteos.device, stream))
+    with _on(conteos.device):
+        st = lib.ugp_cell_diag(_ptr(conteos), int(conteos.numel()), int(capacity), _ptr(out),
+                               _stream_handle(conteos.device, stream))
     _check(st, "ugp_cell_diag")
     return out
 
@@ -322,22 +335,24 @@ def neighbor_count(particles: torch.Tensor, origin: Sequence[float], cell_size: 
     n = int(particles.shape[0])
     d = _dims3(dims)
     flags = FLAG_MORTON if morton else 0
-    _require_gpu(inicios, "inicios", torch.int32)
+    dev = particles.device
+    _require_gpu(inicios, "inicios", torch.int32, dev)
     if inicios.numel() < key_count(d, flags) + 1:
         raise ValueError("inicios is smaller than the key count + 1")
     if ordenado is not None:
-        _require_gpu(ordenado, "ordenado", torch.int32)
+        _require_gpu(ordenado, "ordenado", torch.int32, dev)
         if ordenado.numel() < n:
             raise ValueError("ordenado is smaller than N")
     if out is None:
         out = torch.empty(n, dtype=torch.int32, device=particles.device)
-    _require_gpu(out, "out", torch.int32)
+    _require_gpu(out, "out", torch.int32, dev)
     if out.numel() < n:
         raise ValueError("out is smaller than N")
     o = _f32_3(*[float(v) for v in origin])
-    st = lib.ugp_neighbor_count(_ptr(particles), n, o, ctypes.c_float(float(cell_size)), _u32_3(*d), _ptr(inicios),
-                                _ptr(ordenado), ctypes.c_float(float(radius)), _ptr(out), flags,
-                                _stream_handle(particles.device, stream))
+    with _on(dev):
+        st = lib.ugp_neighbor_count(_ptr(particles), n, o, ctypes.c_float(float(cell_size)), _u32_3(*d),
+                                    _ptr(inicios), _ptr(ordenado), ctypes.c_float(float(radius)), _ptr(out), flags,
+                                    _stream_handle(dev, stream))
     _check(st, "ugp_neighbor_count")
     return out
 
@@ -347,7 +362,8 @@ def grid_build_stage(stage: int, particles, origin, cell_size, dims, out: GridIn
     """ugp_grid_build_stage: enqueue one stage with the same arguments."""
     lib = load_library()
     args = _build_args(particles, origin, cell_size, dims, out, workspace, flags, stream)
-    _check(lib.ugp_grid_build_stage(int(stage), *args), f"ugp_grid_build_stage({stage})")
+    with _on(particles.device):
+        _check(lib.ugp_grid_build_stage(int(stage), *args), f"ugp_grid_build_stage({stage})")
 
 
 def grid_build_timed(stage: int, event_before, event_after, particles, origin, cell_size, dims,
@@ -359,8 +375,9 @@ def grid_build_timed(stage: int, event_before, event_after, particles, origin, c
         if not getattr(ev, "cuda_event", 0):
             ev.record()  # torch creates the underlying event lazily
     args = _build_args(particles, origin, cell_size, dims, out, workspace, flags, stream)
-    st = lib.ugp_grid_build_timed(*args, int(stage), ctypes.c_void_p(event_before.cuda_event),
-                                  ctypes.c_void_p(event_after.cuda_event))
+    with _on(particles.device):
+        st = lib.ugp_grid_build_timed(*args, int(stage), ctypes.c_void_p(event_before.cuda_event),
+                                      ctypes.c_void_p(event_after.cuda_event))
     _check(st, "ugp_grid_build_timed")
 
 
@@ -371,14 +388,15 @@ def exclusive_scan_u32(x: torch.Tensor, out: Optional[torch.Tensor] = None, stre
     n = int(x.numel())
     if out is None:
         out = torch.empty(n + 1, dtype=torch.int32, device=x.device)
-    _require_gpu(out, "out", torch.int32)
+    _require_gpu(out, "out", torch.int32, x.device)
     if out.numel() < n + 1:
         raise ValueError("out needs n+1 entries")
     need = ctypes.c_size_t(0)
     _check(lib.ugp_scan_workspace_bytes(n, ctypes.byref(need)), "ugp_scan_workspace_bytes")
     ws = torch.empty(max(int(need.value), 256), dtype=torch.uint8, device=x.device)
-    st = lib.ugp_exclusive_scan_u32(_ptr(x), n, _ptr(out), _ptr(ws), ctypes.c_size_t(ws.numel()),
-                                    _stream_handle(x.device, stream))
+    with _on(x.device):
+        st = lib.ugp_exclusive_scan_u32(_ptr(x), n, _ptr(out), _ptr(ws), ctypes.c_size_t(ws.numel()),
+                                        _stream_handle(x.device, stream))
     _check(st, "ugp_exclusive_scan_u32")
     return out
 
@@ -387,14 +405,18 @@ def reorder(src: torch.Tensor, idx: torch.Tensor, out: Optional[torch.Tensor] = 
     """ugp_reorder: out[k] = src[idx[k]] (32-byte records, bit for bit)."""
     lib = load_library()
     _require_gpu(src, "src", torch.float32)
-    _require_gpu(idx, "idx", torch.int32)
+    _require_gpu(idx, "idx", torch.int32, src.device)
     if src.dim() != 2 or src.shape[1] != 8:
         raise ValueError("src must have shape (N, 8)")
     n = int(idx.numel())
     if out is None:
         out = torch.empty((n, 8), dtype=torch.float32, device=src.device)
-    _require_gpu(out, "out", torch.float32)
-    st = lib.ugp_reorder(_ptr(src), int(src.shape[0]), _ptr(idx), n, _ptr(out), _stream_handle(src.device, stream))
+    _require_gpu(out, "out", torch.float32, src.device)
+    if out.numel() < 8 * n:
+        raise ValueError("out must hold one 32-byte record per index")
+    with _on(src.device):
+        st = lib.ugp_reorder(_ptr(src), int(src.shape[0]), _ptr(idx), n, _ptr(out),
+                             _stream_handle(src.device, stream))
     _check(st, "ugp_reorder")
     return out
 
@@ -417,15 +439,15 @@ def reorder_arrays(idx: torch.Tensor, srcs: Sequence[torch.Tensor], outs: Option
     descs = (ArrayDesc * len(srcs))()
     for q, (s, o) in enumerate(zip(srcs, outs)):
         for t, name in ((s, "src"), (o, "out")):
-            if not t.is_cuda or not t.is_contiguous():
-                raise ValueError(f"{name} {q} must be a contiguous GPU tensor")
+            _require_gpu(t, f"{name} {q}", None, idx.device)
         if int(s.shape[0]) != n_src:
             raise ValueError("every source needs the same number of rows")
         eb = s.element_size() * (s.numel() // max(1, s.shape[0]))
         if o.dtype != s.dtype or tuple(o.shape[1:]) != tuple(s.shape[1:]) or int(o.shape[0]) < n:
             raise ValueError(f"out {q} must match src {q} row shape and hold N rows")
         descs[q] = ArrayDesc(s.data_ptr(), o.data_ptr(), eb)
-    st = lib.ugp_reorder_arrays(_ptr(idx), n, n_src, descs, len(srcs), _stream_handle(idx.device, stream))
+    with _on(idx.device):
+        st = lib.ugp_reorder_arrays(_ptr(idx), n, n_src, descs, len(srcs), _stream_handle(idx.device, stream))
     _check(st, "ugp_reorder_arrays")
     return list(outs)
 
