@@ -260,6 +260,8 @@ def test_reorder_arrays_validation_on_host(lib):
     assert call([ugp.ArrayDesc(b + (1 << 30), b + (2 << 30), 0)]) == ugp.UGP_ERR_ARG
     assert call([ugp.ArrayDesc(b + (1 << 30), b + (2 << 30), 4100)]) == ugp.UGP_ERR_ARG  # > 4096 bytes
     assert call([ugp.ArrayDesc(b + (1 << 30) + 4, b + (2 << 30), 1028)]) == ugp.UGP_ERR_ARG  # > 256 4-byte chunks
+    huge = [ugp.ArrayDesc(b + (1 << 30), b + (2 << 30), 1 << 31), ugp.ArrayDesc(b + (3 << 30), b + (4 << 30), (1 << 31) + 4)]
+    assert call(huge) == ugp.UGP_ERR_ARG  # sizes whose 32-bit sum would wrap to 4 bytes
     assert call([ugp.ArrayDesc(None, b + (2 << 30), 32)]) == ugp.UGP_ERR_NULL
     assert call([ugp.ArrayDesc(b + (1 << 30) + 2, b + (2 << 30), 32)]) == ugp.UGP_ERR_ALIGN
     assert call([ok], idx=None) == ugp.UGP_ERR_NULL

@@ -841,7 +841,10 @@ int ugp_reorder_arrays(const uint32_t* idx, uint32_t n, uint32_t n_src, const ug
   bool vec16 = true;
   for (uint32_t q = 0; q < count; ++q) {
     const ugp_array_desc& d = arrays[q];
-    if (d.elem_bytes == 0 || d.elem_bytes % 4 != 0) return UGP_ERR_ARG;
+    // an element's 4-byte chunks must fit one workgroup; checked per array
+    // first so that the sum below cannot wrap
+    if (d.elem_bytes == 0 || d.elem_bytes % 4 != 0 || d.elem_bytes / 4u > static_cast<uint32_t>(kBlock))
+      return UGP_ERR_ARG;
     bytes += d.elem_bytes;
     if (n > 0 && (!d.src || !d.dst)) return UGP_ERR_NULL;
     if (!aligned(d.src, 4) || !aligned(d.dst, 4)) return UGP_ERR_ALIGN;
