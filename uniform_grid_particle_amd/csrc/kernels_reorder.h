@@ -242,9 +242,12 @@ __device__ __forceinline__ void copy_cell_records(uint32_t s, uint32_t len, uint
 // entries first, first + stride, ... of the list of long cells. Up to 16384
 // entries, held in registers: when the cell's indices span at most
 // kBitmapPasses * 2^19 values, a bitmap of one such window at a time in LDS
-// (s_keys): each index sets its bit, each thread counts the set bits of its
-// 16 words, a block scan of those counts gives every set bit its place, and
-// the bits are written out in order. Otherwise a bitonic sort in LDS.
+// (s_keys): each index sets its bit, wave scans of the words' set bits and
+// a scan of the wave totals (s_tab) give each word the number of set bits
+// before it (s_pre, 16 bits per word), and each index's place is that
+// number plus the set bits below it in its own word, so every thread places
+// its own indices with no serial walk over the bits (a dense cell would put
+// hundreds of bits in one thread's words). Otherwise a bitonic sort in LDS.
 // Longer: ordered compaction, i.e. walk all particles in index order and
 // append those of this cell (the cell's membership is exact already; only
 // order changes). Each way writes indices only; RECS: the records follow in
@@ -263,7 +266,7 @@ __device__ __forceinline__ void sort_long_cells(
     const uint32_t* __restrict__ inicios, const uint32_t* __restrict__ celdaDe, uint32_t n,
     const uint32_t* __restrict__ long_list, uint32_t count, uint32_t first, uint32_t stride,
     const uint32_t* arrival, uint32_t* __restrict__ ordenado, const uint4* __restrict__ particles,
-    uint4* __restrict__ reordered, uint32_t* s_keys, uint32_t* s_wave) {
+    uint4* __restrict__ reordered, uint32_t* s_keys, uint16_t* s_pre, uint32_t* s_tab, uint32_t* s_wave) {
   const uint32_t* src = SHARE ? arrival : ordenado;
   uint32_t share = 1, part = 0;
   if (SHARE && count != 0u && count < stride) {
@@ -289,6 +292,8 @@ __device__ __forceinline__ void sort_long_cells(
     if (len <= kLdsSort) {
       constexpr uint32_t kPer = kLdsSort / kSortBlock;  // entries (and bitmap words) per thread
       constexpr uint32_t kWindow = kLdsSort * 32u;      // indices per bitmap window
+      constexpr uint32_t kWaves = kSortBlock / 64;
+      const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
       uint32_t v[kPer];
       uint32_t lo = 0xFFFFFFFFu, hi = 0;
 #pragma unroll
@@ -304,37 +309,60 @@ __device__ __forceinline__ void sort_long_cells(
       hi = block_max<kSortBlock>(hi, s_wave);
       if (hi - lo < kBitmapPasses * kWindow) {  // len >= 1, so lo <= hi; uniform
         uint32_t placed = 0;
-        for (uint64_t base = lo; base <= hi; base += kWindow) {
-#pragma unroll
-          for (uint32_t q = 0; q < kPer; ++q) s_keys[threadIdx.x * kPer + q] = 0u;
+        for (uint64_t base64 = lo; base64 <= hi; base64 += kWindow) {
+          const uint32_t base = static_cast<uint32_t>(base64);  // <= hi: fits
+          // the bitmap words this window's part of the cell can touch; thread
+          // t owns words t, t + kSortBlock, ... (a wave's lanes touch
+          // consecutive words: no LDS bank conflicts)
+          const uint32_t top = (hi - base < kWindow - 1u) ? hi - base : kWindow - 1u;
+          const uint32_t used = (top >> 5) + 1u;
+#pragma unroll 4
+          for (uint32_t q = 0; q < kPer; ++q)
+            if (q * kSortBlock + threadIdx.x < used) s_keys[q * kSortBlock + threadIdx.x] = 0u;
           __syncthreads();
-#pragma unroll
+#pragma unroll 4
           for (uint32_t q = 0; q < kPer; ++q) {
-            const uint64_t off = static_cast<uint64_t>(v[q]) - base;
+            const uint32_t off = v[q] - base;  // wraps (and fails the test) below the window
             if (threadIdx.x + q * kSortBlock < len && v[q] >= base && off < kWindow)
               atomicOr(&s_keys[off >> 5], 1u << (off & 31u));
           }
           __syncthreads();
-          // thread t owns bitmap words [t * kPer, (t + 1) * kPer) and writes
-          // their set bits, in order, from the place the block scan gives it
-          uint32_t bits = 0;
-#pragma unroll
-          for (uint32_t q = 0; q < kPer; ++q) bits += __popc(s_keys[threadIdx.x * kPer + q]);
+          // s_pre[word] = set bits in the words before it. Words in order
+          // are groups q of kSortBlock, each the 64-word runs of the waves:
+          // a wave scan places a word inside its run, and an exclusive scan
+          // of the run totals in (q, wave) order (s_tab) places the runs.
+#pragma unroll 4
+          for (uint32_t q = 0; q < kPer; ++q) {
+            const uint32_t wd = q * kSortBlock + threadIdx.x;
+            const uint32_t incl = wave_inclusive_sum((wd < used) ? __popc(s_keys[wd]) : 0u);
+            if (lane == 63u) s_tab[q * kWaves + wave] = incl;
+          }
+          __syncthreads();
           uint32_t total;
-          uint32_t pos = placed + block_exclusive_sum<kSortBlock>(bits, s_wave, &total);
-#pragma unroll 1
-          for (uint32_t q = 0; q < kPer && pos < p1; ++q) {
-            uint32_t w = s_keys[threadIdx.x * kPer + q];
-            const uint32_t past = pos + __popc(w);
-            if (past <= p0) {  // every bit of this word has its place before the share
-              pos = past;
-              continue;
-            }
-            while (w != 0u) {  // stores only: nothing to wait for between bits
-              const uint32_t idx = static_cast<uint32_t>(base) + (threadIdx.x * kPer + q) * 32u + __builtin_ctz(w);
-              w &= w - 1u;
-              if (pos >= p0 && pos < p1) ordenado[s + pos] = idx;
-              ++pos;
+          {
+            const uint32_t x = (threadIdx.x < kPer * kWaves) ? s_tab[threadIdx.x] : 0u;
+            const uint32_t ex = block_exclusive_sum<kSortBlock>(x, s_wave, &total);
+            if (threadIdx.x < kPer * kWaves) s_tab[threadIdx.x] = ex;  // its own entry only
+          }
+          __syncthreads();
+#pragma unroll 4
+          for (uint32_t q = 0; q < kPer; ++q) {
+            const uint32_t wd = q * kSortBlock + threadIdx.x;
+            const uint32_t c = (wd < used) ? __popc(s_keys[wd]) : 0u;
+            const uint32_t incl = wave_inclusive_sum(c);
+            if (wd < used) s_pre[wd] = static_cast<uint16_t>(s_tab[q * kWaves + wave] + incl - c);  // < kLdsSort
+          }
+          __syncthreads();
+          // every index's place: the indices below its word plus the set
+          // bits below it in its word
+#pragma unroll 4
+          for (uint32_t q = 0; q < kPer; ++q) {
+            const uint32_t off = v[q] - base;
+            if (threadIdx.x + q * kSortBlock < len && v[q] >= base && off < kWindow) {
+              const uint32_t wd = off >> 5;
+              const uint32_t place =
+                  placed + s_pre[wd] + __popc(s_keys[wd] & ((1u << (off & 31u)) - 1u));
+              if (place >= p0 && place < p1) ordenado[s + place] = v[q];
             }
           }
           placed += total;
@@ -390,11 +418,13 @@ __global__ __launch_bounds__(kSortBlock) void sort_long_cells_kernel(
     const uint32_t* __restrict__ long_count, uint32_t* __restrict__ ordenado,
     const uint4* __restrict__ particles, uint4* __restrict__ reordered) {
   __shared__ uint32_t s_keys[kLdsSort];
+  __shared__ uint16_t s_pre[kLdsSort];
+  __shared__ uint32_t s_tab[kLdsSort / 64];
   __shared__ uint32_t s_wave[kSortBlock / 64];
   uint32_t count = *long_count;
   if (count > long_cap) count = long_cap;
   sort_long_cells<RECS, false>(inicios, celdaDe, n, long_list, count, blockIdx.x, gridDim.x, nullptr, ordenado,
-                               particles, reordered, s_keys, s_wave);
+                               particles, reordered, s_keys, s_pre, s_tab, s_wave);
 }
 
 // Stable mode on the tile paths: the one pass over the cells the tile
@@ -421,12 +451,14 @@ __global__ __launch_bounds__(kSortBlock) void fix_cells_kernel(
   static_assert(kRankSortMax % 64 == 0, "whole entries per lane");
   static_assert(kSmallSort == 16, "one group of 16 lanes per short cell");
   __shared__ __align__(16) uint32_t s_keys[kLdsSort];  // slices read as uint4
+  __shared__ uint16_t s_pre[kLdsSort];
+  __shared__ uint32_t s_tab[kLdsSort / 64];
   __shared__ uint32_t s_wave[kWaves];
   if (blockIdx.x < long_blocks) {
     uint32_t count = fl.counts()[1];
     if (count > fl.long_cap) count = fl.long_cap;
     sort_long_cells<RECS, true>(inicios, celdaDe, n, fl.lng(), count, blockIdx.x, long_blocks, fl.idx(),
-                                ordenado, particles, reordered, s_keys, s_wave);
+                                ordenado, particles, reordered, s_keys, s_pre, s_tab, s_wave);
     return;
   }
   const uint32_t lane = threadIdx.x & 63u;
