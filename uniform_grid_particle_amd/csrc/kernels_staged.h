@@ -190,7 +190,10 @@ __global__ __launch_bounds__(CT) void staged_keys_kernel(
 // particle of a cell of up to kRankSortMax counts the cell's smaller
 // particle indices, which is its place in that order, and is staged there.
 // A longer cell, and every multi-particle cell of a tile past the staged
-// capacity, is written in arrival order and put on one of the fix-up lists.
+// capacity, is written in arrival order and put on one of the fix-up lists;
+// a tile holding such a longer cell also copies those arrival-order indices
+// to fl.idx() (the whole tile when it is staged, the long cells' ranges when
+// it is scattered), which the fix-up's long-cell pass reads.
 template <bool MOVE, bool DIAG, bool STABLE, bool SINGLE, uint32_t SHIFT, int NT, uint32_t WIN>
 __global__ __launch_bounds__(NT) void staged_cells_kernel(
     const uint2* __restrict__ rows, uint32_t nchunks, uint32_t chunk, uint32_t ntiles, GridParams g,
@@ -217,7 +220,9 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
   __shared__ uint32_t s_wave[NT / 64];
   __shared__ uint32_t s_runmax[NT / 64];
   __shared__ uint32_t s_dm[DIAG ? NT / 64 : 1], s_do[DIAG ? NT / 64 : 1];
-  __shared__ uint32_t s_any_long;  // stable: some cell of the tile is longer than kRankSortMax
+  // stable: a staged tile has a cell longer than kRankSortMax (0/1); a tile
+  // past the capacity counts such cells
+  __shared__ uint32_t s_any_long;
   __shared__ uint32_t s_below;  // SINGLE: particles in earlier tiles
 
   // one tile holding the whole input: no kernel runs before this one, so the
