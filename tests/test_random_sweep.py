@@ -1,4 +1,4 @@
-"""GPU parity over a seeded sweep of small random problems.
+"""GPU parity over seeded sweeps of random problems.
 
 Each case draws a grid (1 to 80 cells per axis, some axes of one cell), a
 particle count (0 to 120,000), a position mix (uniform, a few dense clumps,
@@ -9,6 +9,10 @@ Every case is checked against the oracle by the rules of test_parity.py:
 celdaDe, conteos, inicios and the diagnostics bit-exact; ordenado element
 for element in stable mode, otherwise per cell; reordered bit-exact against
 the GPU's own ordenado (or the oracle's, in stable mode).
+
+A second, shorter sweep draws larger problems (120,000 to 3,000,000
+particles on grids of up to 300 cells per axis), which reach the staged
+path's limits, the bucketed path and large tiles past the staged capacity.
 """
 
 from __future__ import annotations
@@ -82,9 +86,50 @@ def draw_case(seed: int):
     return wl, flags, cap
 
 
+LARGE_CASES = 12
+
+
+def draw_large_case(seed: int):
+    rng = np.random.Generator(np.random.PCG64(50_000 + seed))
+    dims = [int(v) for v in rng.integers(1, 301, 3)]
+    for a in range(3):
+        if rng.random() < 0.1:
+            dims[a] = 1
+    n = int(rng.integers(120_000, 3_000_001))
+    h = np.float32(rng.choice([0.25, 0.5, 1.0 / 3.0]))
+    origin = (rng.random(3) * 4 - 2).astype(np.float32)
+    ext = np.asarray(dims, np.float64) * float(h)
+    parts = rng.standard_normal((n, 8)).astype(np.float32)
+    parts[:, :3] = (origin + rng.random((n, 3)) * ext).astype(np.float32)
+    kind = rng.integers(0, 3)
+    if kind == 1:  # dense clumps of varying width
+        for _ in range(int(rng.integers(1, 4))):
+            m = rng.random(n) < rng.uniform(0.02, 0.3)
+            centre = origin + rng.random(3) * ext
+            width = float(h) * rng.uniform(0.1, 3.0)
+            parts[m, :3] = (centre + rng.standard_normal((int(m.sum()), 3)) * width).astype(np.float32)
+    elif kind == 2:  # points outside the domain on every side
+        m = rng.random(n) < 0.2
+        parts[m, :3] = (origin + (rng.random((int(m.sum()), 3)) * 1.6 - 0.3) * ext).astype(np.float32)
+    flags = dict(stable=bool(rng.random() < 0.45), gather=bool(rng.random() < 0.2),
+                 index_only=bool(rng.random() < 0.1),
+                 morton=bool(rng.random() < 0.25 and max(dims) <= 256))
+    cap = int(rng.integers(0, 60)) if rng.random() < 0.25 else None
+    wl = W.Workload(f"large_sweep{seed}", parts, origin, h, np.asarray(dims, np.uint32))
+    return wl, flags, cap
+
+
 @pytest.mark.parametrize("seed", range(CASES))
 def test_random_case(ugp, orc, seed):
-    wl, flags, cap = draw_case(seed)
+    check_case(ugp, orc, *draw_case(seed), seed)
+
+
+@pytest.mark.parametrize("seed", range(LARGE_CASES))
+def test_random_large_case(ugp, orc, seed):
+    check_case(ugp, orc, *draw_large_case(seed), seed)
+
+
+def check_case(ugp, orc, wl, flags, cap, seed):
     print(f"[sweep] seed={seed} n={wl.n} dims={wl.dims.tolist()} flags={flags} cap={cap}", flush=True)
     ref = orc.grid_build(wl.particles, wl.origin, wl.cell_size, wl.dims, morton=flags["morton"])
     dev = torch.device("cuda:0")
