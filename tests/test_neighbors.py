@@ -120,3 +120,28 @@ def test_neighbors_empty_and_errors(ugp):
     with pytest.raises(ugp.UGPError) as e:  # counts written over the particles
         ugp.neighbor_count(p, *args, idx.inicios, idx.ordenado, 0.5, out=p.view(torch.int32).reshape(-1))
     assert e.value.status == ugp.UGP_ERR_ALIAS
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_neighbors_random_sweep(ugp, orc, seed):
+    """Seeded random problems: grids of 1-40 cells per axis, up to 40,000
+    particles (some outside the domain, some on exact lattice points so that
+    distances fall exactly on the radius), radius 0 to one cell, linear or
+    Morton keys, atomic or stable index; both data orders against the oracle."""
+    rng = np.random.Generator(np.random.PCG64(90_000 + seed))
+    dims = [int(v) for v in rng.integers(1, 41, 3)]
+    n = int(rng.integers(0, 40_001))
+    h = float(np.float32(rng.choice([0.25, 0.1, 1.0 / 3.0, 0.7])))
+    origin = (rng.random(3) * 4 - 2).astype(np.float32)
+    ext = np.asarray(dims, np.float64) * h
+    parts = rng.standard_normal((n, 8)).astype(np.float32)
+    parts[:, :3] = (origin + rng.random((n, 3)) * ext * 1.1 - 0.05 * ext).astype(np.float32)
+    if n and rng.random() < 0.3:
+        k = rng.integers(0, np.asarray(dims) + 1, (n, 3))
+        parts[:, :3] = (origin + k * np.float32(h)).astype(np.float32)
+    radius = float(np.float32(h * rng.choice([0.0, 0.3, 0.5, 0.87, 1.0])))
+    morton = bool(rng.random() < 0.4 and max(dims) <= 32)
+    stable = bool(rng.random() < 0.5)
+    print(f"[neighbors] seed={seed} n={n} dims={dims} h={h} r={radius} morton={morton}", flush=True)
+    wl = W.Workload(f"nb{seed}", parts, origin, np.float32(h), np.asarray(dims, np.uint32))
+    check_neighbors(ugp, orc, wl, radius, morton, stable=stable)
