@@ -463,6 +463,17 @@ def test_scan_sizes(ugp, orc, count):
     assert np.array_equal(got, orc.exclusive_scan(x))
 
 
+def test_scan_wraps_mod_2_32(ugp):
+    """The stand-alone scan's prefixes are taken mod 2^32 (ugp.h): values near
+    2^32 make them wrap many times; the closed form is the 64-bit prefix sum
+    reduced mod 2^32."""
+    rng = np.random.Generator(np.random.PCG64(32))
+    x = rng.integers(2**32 - 2**20, 2**32, 300_007, dtype=np.uint64).astype(np.uint32)
+    got = _u32(ugp.exclusive_scan_u32(torch.from_numpy(x.view(np.int32)).to("cuda:0")))
+    want = np.concatenate([[0], np.cumsum(x, dtype=np.uint64)]) % (1 << 32)
+    assert np.array_equal(got, want.astype(np.uint32))
+
+
 def test_reorder_entry_point(ugp, orc):
     rng = np.random.Generator(np.random.PCG64(77))
     n = 123_457
