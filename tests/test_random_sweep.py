@@ -12,7 +12,8 @@ the GPU's own ordenado (or the oracle's, in stable mode).
 
 A second, shorter sweep draws larger problems (120,000 to 3,000,000
 particles on grids of up to 300 cells per axis), which reach the staged
-path's limits, the bucketed path and large tiles past the staged capacity.
+path's limits, the bucketed path and large tiles past the staged capacity;
+a third draws problems past 2^26 keys, for the global-atomic path.
 """
 
 from __future__ import annotations
@@ -119,6 +120,35 @@ def draw_large_case(seed: int):
     return wl, flags, cap
 
 
+DIRECT_CASES = 4
+
+
+def draw_direct_case(seed: int):
+    """Past 2^26 keys (the global-atomic path): a wide flat linear grid, or
+    Morton keys on a grid wider than 256 cells (padded to 2^27 keys)."""
+    rng = np.random.Generator(np.random.PCG64(80_000 + seed))
+    if seed % 2 == 0:
+        dims = [int(rng.integers(8200, 9000)), int(rng.integers(8193, 9000)), 1]
+        morton = False
+    else:
+        dims = [int(v) for v in rng.integers(257, 513, 3)]
+        dims[int(rng.integers(0, 3))] = int(rng.integers(1, 40))
+        morton = True
+    n = int(rng.integers(1, 400_001))
+    ext = np.asarray(dims, np.float64)
+    parts = rng.standard_normal((n, 8)).astype(np.float32)
+    parts[:, :3] = (rng.random((n, 3)) * ext * 1.02 - 0.01 * ext).astype(np.float32)
+    if rng.random() < 0.5:
+        m = rng.random(n) < rng.uniform(0.01, 0.2)
+        parts[m, :3] = parts[0, :3]  # one dense cell
+    flags = dict(stable=bool(rng.random() < 0.5), gather=bool(rng.random() < 0.3),
+                 index_only=bool(rng.random() < 0.1), morton=morton)
+    cap = int(rng.integers(0, 40)) if rng.random() < 0.3 else None
+    wl = W.Workload(f"direct_sweep{seed}", parts, np.zeros(3, np.float32), np.float32(1.0),
+                    np.asarray(dims, np.uint32))
+    return wl, flags, cap
+
+
 @pytest.mark.parametrize("seed", range(CASES))
 def test_random_case(ugp, orc, seed):
     check_case(ugp, orc, *draw_case(seed), seed)
@@ -127,6 +157,14 @@ def test_random_case(ugp, orc, seed):
 @pytest.mark.parametrize("seed", range(LARGE_CASES))
 def test_random_large_case(ugp, orc, seed):
     check_case(ugp, orc, *draw_large_case(seed), seed)
+
+
+@pytest.mark.parametrize("seed", range(DIRECT_CASES))
+def test_random_direct_case(ugp, orc, seed):
+    wl, flags, cap = draw_direct_case(seed)
+    fl = ugp.FLAG_MORTON if flags["morton"] else 0
+    assert ugp.stage_names(wl.n, wl.dims.tolist(), fl)[:4] == ["clear", "count", "scan", "scatter"]
+    check_case(ugp, orc, wl, flags, cap, seed)
 
 
 def check_case(ugp, orc, wl, flags, cap, seed):
