@@ -112,7 +112,7 @@ typedef struct ugp_particle {
  * ugp_grid_stage_name():
  *   n == 0            slot 0 "clear" (zero conteos and inicios); others empty
  *   n <= 8192 and K <= 2^14
- *                     -, -, -, "tile_sort" -- one launch: up to 16 workgroups
+ *                     -, -, -, "tile_sort" -- one launch: up to 64 workgroups
  *                     each read the whole input and build the index of their
  *                     own cells, celdaDe included
  *   K <= 2^22 and n <= 2^21 (K up to 2^23 on dense grids)

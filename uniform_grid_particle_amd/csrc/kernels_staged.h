@@ -66,7 +66,7 @@ constexpr uint32_t kStagedMaxShift = 14;            // up to 16384 cells per til
 constexpr uint64_t kStagedTarget = 4096;            // mean particles per tile sought (half the capacity)
 constexpr int kCellsThreads = 1024;                 // tile_sort workgroup
 constexpr uint32_t kSingleMax = kCellsThreads * kStagedRegs;  // particles one tile kernel workgroup stages
-constexpr uint32_t kSingleSplitLog = 4;             // single path: up to 2^4 tiles (no diagnostics, no stable order)
+constexpr uint32_t kSingleSplitLog = 6;             // single path: up to 2^6 tiles (no diagnostics, no stable order)
 constexpr uint32_t kCellsWin = 2048;                // tile_sort LDS staging window
 
 // Tile t's workgroup index, spreading consecutive tiles over workgroups of

@@ -450,8 +450,9 @@ void enqueue_single(uint32_t stage, const BuildArgs& a, const Plan& p) {
   switch (stage) {
     case 3: {
       // without diagnostics or stable order (whose words one workgroup zeroes
-      // for itself) the cells are split into up to 16 tiles, each workgroup
-      // reading the whole input: more than one CU on a latency-bound build
+      // for itself) the cells are split into up to 64 tiles (of at least 16
+      // cells), each workgroup reading the whole input: many CUs on a
+      // latency-bound build
       Plan q = p;
       if (!p.stable && a.diag == nullptr) {
         const uint32_t lg = p.tile_shift;  // the one tile covers 2^lg >= K keys
