@@ -48,3 +48,11 @@ def test_bench_json_line():
     for key in ("value", "unit", "cores", "kind", "sample"):
         assert key in cb, key
     assert cb["kind"] == "oracle" and cb["cores"] == 1 and cb["value"] > 0
+
+
+@pytest.mark.gpu
+def test_smoke_entry_point():
+    sys.path.insert(0, ROOT)
+    import __graft_entry__
+
+    __graft_entry__.smoke()
