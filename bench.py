@@ -109,32 +109,63 @@ def read_traffic(kernel: str):
 
 
 def cpu_baseline(wl, budget_s: float):
-    """The oracle as it stands, single-threaded, on the same workload."""
+    """The oracle as it stands, single-threaded and pinned to one core, on the
+    same workload: each step (count = cell keys + histogram, scan, scatter,
+    reorder) timed on its own into output arrays allocated once, repeated
+    until the budget is spent (at least 3 builds); medians per step."""
     import oracle
 
     orc = oracle.load()
-    times = []
-    t_end = time.perf_counter() + budget_s
-    while True:
-        t0 = time.perf_counter()
-        orc.grid_build(wl.particles, wl.origin, wl.cell_size, wl.dims)
-        times.append(time.perf_counter() - t0)
-        if time.perf_counter() >= t_end and len(times) >= 3:
-            break
-    med = statistics.median(times)
+    bufs = orc.alloc_build(wl.n, wl.cells)
+    pinned = None
+    old_aff = None
+    if hasattr(os, "sched_setaffinity"):
+        old_aff = os.sched_getaffinity(0)
+        pinned = min(old_aff)
+        os.sched_setaffinity(0, {pinned})
+    try:
+        runs = []
+        t_end = time.perf_counter() + budget_s
+        while True:
+            runs.append(orc.timed_stages(wl.particles, wl.origin, wl.cell_size, wl.dims, bufs))
+            if time.perf_counter() >= t_end and len(runs) >= 3:
+                break
+    finally:
+        if old_aff is not None:
+            os.sched_setaffinity(0, old_aff)
+    stage_s = {k: statistics.median(r[k] for r in runs) for k in runs[0]}
+    total = statistics.median(sum(r.values()) for r in runs)
     return {
-        "value": wl.n / med,
+        "value": wl.n / total,
         "unit": "particles/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"full {wl.name} build ({wl.n} particles, {wl.cells} cells) repeated {len(times)}x, "
-                  f"median {med * 1e3:.1f} ms; single-threaded C oracle",
+        "sample": f"full {wl.name} build ({wl.n} particles, {wl.cells} cells) repeated {len(runs)}x into "
+                  f"preallocated outputs, median {total * 1e3:.1f} ms; single-threaded C oracle pinned to core "
+                  f"{pinned}",
+        "stages_ms": {k: round(v * 1e3, 3) for k, v in stage_s.items()},
+        "stages_particles_per_s": {k: wl.n / v for k, v in stage_s.items() if v > 0},
         "host_cpu": _cpu_model(),
         "host_threads": os.cpu_count(),
     }
 
 
+def _p10_p90(xs) -> list:
+    """10th and 90th percentiles of a list of timings, rounded."""
+    return [round(float(np.percentile(xs, 10)), 3), round(float(np.percentile(xs, 90)), 3)]
+
+
 def _cpu_model() -> str:
+    """lscpu's "Model name" (else /proc/cpuinfo's), as printed."""
+    import subprocess
+
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
     try:
         with open("/proc/cpuinfo", encoding="utf-8") as f:
             for line in f:
@@ -405,7 +436,7 @@ def next_rows_summary(result: dict, wl, with_oracle: bool) -> dict:
         "gpu": {"fused_step_us": round(dv["ms_per_step"] * 1e3, 2),
                 "fused_overhead_us": round(dv["ms_per_step"] * 1e3 - step_us, 2),
                 "standalone_us": dv["cell_diag_us"]},
-        "roofline": {"kernel": "diag_kernel<256> (standalone, over conteos)", "bound": "hbm", "achieved": round(diag_gbs, 1),
+        "roofline": {"kernel": "cell_diag_kernel<512> (standalone, over conteos)", "bound": "hbm", "achieved": round(diag_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": diag_gbs / HBM_PEAK_GBS},
     }
     mv = result["morton_variant"]
@@ -598,7 +629,8 @@ def main(argv=None) -> int:
                             gather=args.mode == "gather", out=out, workspace=ws)
         dends[k].record(stream)
     torch.cuda.synchronize()
-    diag_ms = sum(dstarts[k].elapsed_time(dends[k]) for k in range(K)) / K
+    diag_steps = [dstarts[k].elapsed_time(dends[k]) for k in range(K)]
+    diag_ms = statistics.median(diag_steps)
     diag_val = [int(v) for v in ugp.as_u32_numpy(diag)]
     cd = []
     for _ in range(K):
@@ -609,8 +641,8 @@ def main(argv=None) -> int:
         ugp.cell_diag(out.conteos, 64, out=diag)
         c1.record(stream)
         torch.cuda.synchronize()
-        cd.append(c0.elapsed_time(c1))
-    cell_diag_us = 1e3 * statistics.median(cd)
+        cd.append(1e3 * c0.elapsed_time(c1))
+    cell_diag_us = statistics.median(cd)
 
     # ---- Morton-keyed variant: K cold builds numbering cells along the Z curve ----
     mflags = flags | ugp.FLAG_MORTON
@@ -624,7 +656,8 @@ def main(argv=None) -> int:
                        morton=True, out=mout, workspace=mws)
         mends[k].record(stream)
     torch.cuda.synchronize()
-    morton_ms = sum(mstarts[k].elapsed_time(mends[k]) for k in range(K)) / K
+    morton_steps = [mstarts[k].elapsed_time(mends[k]) for k in range(K)]
+    morton_ms = statistics.median(morton_steps)
     del mout, mws
 
     # ---- warm: K back-to-back builds between one event pair ----
@@ -652,10 +685,11 @@ def main(argv=None) -> int:
             evict()
             ugp.grid_build_timed(st, evs[k][0], evs[k][1], parts, origin, h, dims, out, ws, flags=flags)
         torch.cuda.synchronize()
-        us = 1e3 * sum(e0.elapsed_time(e1) for e0, e1 in evs) / K
+        per = [1e3 * e0.elapsed_time(e1) for e0, e1 in evs]
+        us = statistics.median(per)
         b = bytes_k.get(name)
         gbs = (b / (us * 1e3)) if (b and us > 0) else None
-        stages[name] = {"slot": st, "us": round(us, 3), "alg_bytes": b,
+        stages[name] = {"slot": st, "us": round(us, 3), "us_p10_p90": _p10_p90(per), "alg_bytes": b,
                         "GBps": None if gbs is None else round(gbs, 1),
                         "frac_hbm": None if gbs is None else round(gbs / HBM_PEAK_GBS, 4)}
 
@@ -727,17 +761,19 @@ def main(argv=None) -> int:
         "step_ms_worst": [max(step_ms), int(np.argmax(step_ms))],
         "step_ms_p10_p90": [float(np.percentile(step_ms, 10)), float(np.percentile(step_ms, 90))],
         "warm_ms_per_step": warm_ms,
-        "morton_variant": {"ms_per_step": morton_ms, "keys": ugp.key_count(dims, mflags),
-                           "note": "same cold protocol, cells numbered along the Z curve"},
-        "diag_variant": {"capacity": 64, "ms_per_step": diag_ms, "max_per_cell_and_overflows": diag_val,
-                         "note": "same cold protocol, overflow diagnostics folded into the build",
-                         "cell_diag_us": round(cell_diag_us, 3),
+        "morton_variant": {"ms_per_step": morton_ms, "ms_p10_p90": _p10_p90(morton_steps),
+                           "keys": ugp.key_count(dims, mflags),
+                           "note": "same cold protocol (median of K steps), cells numbered along the Z curve"},
+        "diag_variant": {"capacity": 64, "ms_per_step": diag_ms, "ms_p10_p90": _p10_p90(diag_steps),
+                         "max_per_cell_and_overflows": diag_val,
+                         "note": "same cold protocol (median of K steps), overflow diagnostics folded into the build",
+                         "cell_diag_us": round(cell_diag_us, 3), "cell_diag_us_p10_p90": _p10_p90(cd),
                          "cell_diag_GBps": round(4 * cells / (cell_diag_us * 1e3), 1)},
         "warm_note": "back-to-back builds; the working set can stay in the 256 MiB Infinity Cache",
         "stages": stages,
         "stage_sum_us": round(sum(s["us"] for s in stages.values()), 3),
         "stage_note": "each stage timed inside a full cold build, events recorded around it in the same C call "
-                      "(includes the event marker's own cost)",
+                      "(includes the event marker's own cost); median of K builds per stage, p10/p90 beside it",
         "wall_s_timed_loop": wall,
         "roofline": {
             "kernel": dominant,

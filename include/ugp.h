@@ -33,8 +33,10 @@
  *  - Device pointers are HIP device memory on the current device; host
  *    pointers are read before the call returns.
  *  - The caller allocates and owns every buffer. The library never
- *    allocates or frees memory, never synchronises the host with the
- *    device, and keeps no state between calls.
+ *    allocates or frees memory and never synchronises the host with the
+ *    device. It keeps no state between calls except one fixed device array
+ *    of its own per GPU (zero at load): the per-workgroup partials of
+ *    ugp_cell_diag() (left ready for the next launch by every launch).
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    The call returns once the work is enqueued; outputs are valid when the
  *    stream reaches that point, and inputs must not change before then.
@@ -224,6 +226,11 @@ int ugp_grid_build_diag(const ugp_particle *particles, uint32_t n, const float o
  *             cells == 0)
  *   diag      device, out: 2 u32 as in ugp_grid_build_diag(), 4-byte
  *             aligned, must not overlap conteos.
+ * One kernel launch: each workgroup reduces its part into a partial held in
+ * a slot of a library-owned device array, and the last workgroup to finish
+ * folds the partials into diag (no clear beforehand). Slots are dealt round
+ * robin over 64, so up to 64 calls (also those inside ugp_grid_build_diag()
+ * on the global-atomic path) may be in flight at once on one GPU.
  * Returns UGP_OK once enqueued, UGP_ERR_NULL / UGP_ERR_ALIGN /
  * UGP_ERR_ALIAS with nothing enqueued, or UGP_ERR_HIP. */
 int ugp_cell_diag(const uint32_t *conteos, uint32_t cells, uint32_t capacity, uint32_t *diag,

@@ -206,6 +206,40 @@ class Oracle:
         self._check(st, "grid_build")
         return GridIndex(celdaDe, conteos, inicios, ordenado, reordered)
 
+    def alloc_build(self, n: int, cells: int) -> dict:
+        """Output arrays (and the scatter's cursor) for timed_stages, allocated once."""
+        return {"celdaDe": np.empty(n, dtype=np.uint32), "conteos": np.empty(cells, dtype=np.uint32),
+                "inicios": np.empty(cells + 1, dtype=np.uint32), "ordenado": np.empty(n, dtype=np.uint32),
+                "reordered": np.empty((n, 8), dtype=np.float32), "cursor": np.empty(max(cells, 1), dtype=np.uint32)}
+
+    def timed_stages(self, particles, origin, cell_size, dims, bufs: dict) -> dict:
+        """One linear-keyed build into preallocated `bufs` (alloc_build), each
+        step timed on its own with a monotonic clock: count (cell keys, then
+        the histogram), scan, scatter, reorder. Returns seconds per step."""
+        import time
+
+        p = np.ascontiguousarray(particles, dtype=np.float32).reshape(-1, 8)
+        o, h, d = self._grid(origin, cell_size, dims)
+        n = p.shape[0]
+        cells = bufs["conteos"].size
+        lib = self._lib
+        pp, po, pd = self._p(p, _f32p), self._p(o, _f32p), self._p(d, _u32p)
+        k, c, s = (self._p(bufs[x], _u32p) for x in ("celdaDe", "conteos", "inicios"))
+        r, cur, out = self._p(bufs["ordenado"], _u32p), self._p(bufs["cursor"], _u32p), self._p(bufs["reordered"], _f32p)
+        clock = time.perf_counter
+        t0 = clock()
+        st = lib.ugp_oracle_cell_index(pp, n, po, h, pd, k)
+        st = st or lib.ugp_oracle_histogram(k, n, cells, c)
+        t1 = clock()
+        st = st or lib.ugp_oracle_exclusive_scan(c, cells, s)
+        t2 = clock()
+        st = st or lib.ugp_oracle_scatter(k, n, s, cells, cur, r)
+        t3 = clock()
+        st = st or lib.ugp_oracle_reorder(pp, r, n, out)
+        t4 = clock()
+        self._check(st, "timed_stages")
+        return {"count": t1 - t0, "scan": t2 - t1, "scatter": t3 - t2, "reorder": t4 - t3}
+
     def neighbor_count(self, particles, origin, cell_size, dims, radius: float, morton: bool = False,
                        index: "GridIndex | None" = None) -> np.ndarray:
         """Per particle (original order): other particles in the 27 cells around

@@ -443,6 +443,34 @@ def test_reuse_buffers_and_workspace(ugp, orc):
         assert_parity(wl, got, ref, "stable")
 
 
+@pytest.mark.parametrize("mode", ["atomic", "stable"])
+def test_side_stream_build(ugp, orc, mode):
+    """A build enqueued on a stream other than the current one, with outputs
+    and workspace allocated by the binding, while the current stream keeps
+    allocating and writing memory: the binding's allocations belong to the
+    build's stream, so none of them is handed to the current stream's work
+    before the build has finished."""
+    dev = torch.device("cuda:0")
+    wl = W.make_config("baseline")
+    parts = torch.from_numpy(wl.particles).to(dev)
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    results = []
+    for _ in range(3):
+        r = ugp.grid_build(parts, wl.origin.tolist(), float(wl.cell_size), wl.dims.tolist(),
+                           stable=(mode == "stable"), stream=side)
+        results.append(r)
+        # current-stream work that would reuse freed blocks of the same sizes
+        junk = [torch.full((wl.n * 9,), 7, dtype=torch.int32, device=dev) for _ in range(4)]
+        del junk
+    torch.cuda.synchronize(dev)
+    ref = orc.grid_build(wl.particles, wl.origin, wl.cell_size, wl.dims)
+    for r in results:
+        got = oracle.GridIndex(_u32(r.celdaDe), _u32(r.conteos), _u32(r.inicios), _u32(r.ordenado),
+                               r.reordered.cpu().numpy())
+        assert_parity(wl, got, ref, mode)
+
+
 # ---------------------------------------------------------------------------
 # Stand-alone scan and reorder entry points
 # ---------------------------------------------------------------------------

@@ -147,6 +147,18 @@ def _on(device: torch.device):
     return torch.cuda.device(device)
 
 
+def _alloc_on(device: torch.device, stream):
+    """Context for allocating what a call on `stream` reads or writes: the
+    caching allocator then ties those blocks to that stream, so memory freed
+    when the call returns is not handed to work on another stream while the
+    call may still be running. No stream: the current one, as the call uses."""
+    import contextlib
+
+    if stream is None:
+        return contextlib.nullcontext()
+    return torch.cuda.stream(stream)
+
+
 def _dims3(dims) -> tuple[int, int, int]:
     d = tuple(int(v) for v in dims)
     if len(d) != 3:
@@ -197,15 +209,23 @@ class GridIndex:
     reordered: torch.Tensor  # (N, 8) float32 records in cell order
 
 
-def alloc_outputs(n: int, dims: Sequence[int], device, flags: int = 0):
-    """Output tensors and the workspace for one build (torch allocations)."""
-    return _fill_in(n, dims, device, flags, None, None)
+def alloc_outputs(n: int, dims: Sequence[int], device, flags: int = 0, stream=None):
+    """Output tensors and the workspace for one build (torch allocations),
+    tied to `stream` (default: the current stream)."""
+    return _fill_in(n, dims, device, flags, None, None, stream)
 
 
-def _fill_in(n: int, dims, device, flags: int, out: Optional[GridIndex], workspace: Optional[torch.Tensor]):
-    """Allocate the outputs and/or the workspace the caller did not pass."""
+def _fill_in(n: int, dims, device, flags: int, out: Optional[GridIndex], workspace: Optional[torch.Tensor],
+             stream=None):
+    """Allocate the outputs and/or the workspace the caller did not pass, on
+    the stream the build is enqueued on."""
     d = _dims3(dims)
     dev = torch.device(device)
+    with _alloc_on(dev, stream):
+        return _fill_in_now(n, d, dev, flags, out, workspace)
+
+
+def _fill_in_now(n: int, d, dev, flags: int, out: Optional[GridIndex], workspace: Optional[torch.Tensor]):
     if out is None:
         cells = key_count(d, flags)
         out = GridIndex(
@@ -232,7 +252,8 @@ def _build_args(particles, origin, cell_size, dims, out: GridIndex, workspace, f
     index_only = bool(flags & FLAG_INDEX_ONLY)
     if not index_only:
         _require_gpu(out.reordered, "reordered", torch.float32, dev)
-    _require_gpu(workspace, "workspace", torch.uint8, dev)
+    if workspace is not None:  # None: the no-allocation entry point, which takes none
+        _require_gpu(workspace, "workspace", torch.uint8, dev)
     cells = key_count(d, flags)
     if out.celdaDe.numel() < n or out.ordenado.numel() < n or (not index_only and out.reordered.numel() < 8 * n):
         raise ValueError("per-particle outputs are smaller than N")
@@ -242,7 +263,8 @@ def _build_args(particles, origin, cell_size, dims, out: GridIndex, workspace, f
     return [
         _ptr(particles), n, o, ctypes.c_float(float(cell_size)), _u32_3(*d),
         _ptr(out.celdaDe), _ptr(out.conteos), _ptr(out.inicios), _ptr(out.ordenado),
-        None if index_only else _ptr(out.reordered), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
+        None if index_only else _ptr(out.reordered), _ptr(workspace),
+        ctypes.c_size_t(0 if workspace is None else workspace.numel()),
         int(flags), _stream_handle(particles.device, stream),
     ]
 
@@ -266,7 +288,7 @@ def grid_build(
     lib = load_library()
     flags = _flags(stable, gather, morton) | (FLAG_INDEX_ONLY if index_only else 0)
     n = int(particles.shape[0])
-    out, workspace = _fill_in(n, dims, particles.device, flags, out, workspace)
+    out, workspace = _fill_in(n, dims, particles.device, flags, out, workspace, stream)
     args = _build_args(particles, origin, cell_size, dims, out, workspace, flags, stream)
     with _on(particles.device):
         _check(lib.ugp_grid_build(*args), "ugp_grid_build")
@@ -293,9 +315,10 @@ def grid_build_diag(
     lib = load_library()
     flags = _flags(stable, gather, morton)
     n = int(particles.shape[0])
-    out, workspace = _fill_in(n, dims, particles.device, flags, out, workspace)
+    out, workspace = _fill_in(n, dims, particles.device, flags, out, workspace, stream)
     if diag is None:
-        diag = torch.empty(2, dtype=torch.int32, device=particles.device)
+        with _alloc_on(particles.device, stream):
+            diag = torch.empty(2, dtype=torch.int32, device=particles.device)
     _require_gpu(diag, "diag", torch.int32, particles.device)
     if diag.numel() < 2:
         raise ValueError("diag needs 2 entries")
@@ -311,7 +334,8 @@ def cell_diag(conteos: torch.Tensor, capacity: int, out: Optional[torch.Tensor] 
     lib = load_library()
     _require_gpu(conteos, "conteos", torch.int32)
     if out is None:
-        out = torch.empty(2, dtype=torch.int32, device=conteos.device)
+        with _alloc_on(conteos.device, stream):
+            out = torch.empty(2, dtype=torch.int32, device=conteos.device)
     _require_gpu(out, "out", torch.int32, conteos.device)
     if out.numel() < 2:
         raise ValueError("out needs 2 entries")
@@ -344,7 +368,8 @@ def neighbor_count(particles: torch.Tensor, origin: Sequence[float], cell_size: 
         if ordenado.numel() < n:
             raise ValueError("ordenado is smaller than N")
     if out is None:
-        out = torch.empty(n, dtype=torch.int32, device=particles.device)
+        with _alloc_on(dev, stream):
+            out = torch.empty(n, dtype=torch.int32, device=particles.device)
     _require_gpu(out, "out", torch.int32, dev)
     if out.numel() < n:
         raise ValueError("out is smaller than N")
@@ -387,13 +412,15 @@ def exclusive_scan_u32(x: torch.Tensor, out: Optional[torch.Tensor] = None, stre
     _require_gpu(x, "x", torch.int32)
     n = int(x.numel())
     if out is None:
-        out = torch.empty(n + 1, dtype=torch.int32, device=x.device)
+        with _alloc_on(x.device, stream):
+            out = torch.empty(n + 1, dtype=torch.int32, device=x.device)
     _require_gpu(out, "out", torch.int32, x.device)
     if out.numel() < n + 1:
         raise ValueError("out needs n+1 entries")
     need = ctypes.c_size_t(0)
     _check(lib.ugp_scan_workspace_bytes(n, ctypes.byref(need)), "ugp_scan_workspace_bytes")
-    ws = torch.empty(max(int(need.value), 256), dtype=torch.uint8, device=x.device)
+    with _alloc_on(x.device, stream):  # freed on return, while the scan may still run on `stream`
+        ws = torch.empty(max(int(need.value), 256), dtype=torch.uint8, device=x.device)
     with _on(x.device):
         st = lib.ugp_exclusive_scan_u32(_ptr(x), n, _ptr(out), _ptr(ws), ctypes.c_size_t(ws.numel()),
                                         _stream_handle(x.device, stream))
@@ -410,7 +437,8 @@ def reorder(src: torch.Tensor, idx: torch.Tensor, out: Optional[torch.Tensor] = 
         raise ValueError("src must have shape (N, 8)")
     n = int(idx.numel())
     if out is None:
-        out = torch.empty((n, 8), dtype=torch.float32, device=src.device)
+        with _alloc_on(src.device, stream):
+            out = torch.empty((n, 8), dtype=torch.float32, device=src.device)
     _require_gpu(out, "out", torch.float32, src.device)
     if out.numel() < 8 * n:
         raise ValueError("out must hold one 32-byte record per index")
@@ -433,7 +461,8 @@ def reorder_arrays(idx: torch.Tensor, srcs: Sequence[torch.Tensor], outs: Option
         raise ValueError("at least one array")
     n_src = int(srcs[0].shape[0])
     if outs is None:
-        outs = [torch.empty((n,) + tuple(s.shape[1:]), dtype=s.dtype, device=s.device) for s in srcs]
+        with _alloc_on(idx.device, stream):
+            outs = [torch.empty((n,) + tuple(s.shape[1:]), dtype=s.dtype, device=s.device) for s in srcs]
     if len(outs) != len(srcs):
         raise ValueError("one output per array")
     descs = (ArrayDesc * len(srcs))()

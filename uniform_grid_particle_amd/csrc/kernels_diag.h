@@ -18,9 +18,6 @@
 
 namespace ugp {
 
-constexpr int kDiagBlock = 256;
-constexpr uint32_t kDiagMaxGrid = 1024;
-
 __device__ __forceinline__ uint32_t overflow_of(uint32_t count, uint32_t cap) {
   return count > cap ? count - cap : 0u;
 }
@@ -56,16 +53,31 @@ __device__ __forceinline__ void publish_diag(const uint32_t* s_m, const uint32_t
   if (o != 0u) atomicAdd(&diag[1], o);
 }
 
-// Standalone: diag[0] = max conteos[c], diag[1] += sum max(0, conteos[c] - cap)
-// over c < cells. diag must be zeroed before. conteos 16-byte aligned. Each
-// thread issues kDiagItems 16-byte loads per round before using any of them.
+// Standalone reduction over a conteos array in one launch, with no clear
+// beforehand: every workgroup folds its part and stores the pair in its
+// entry of `part`, then takes a ticket; the workgroup that takes the last
+// ticket folds the gridDim.x pairs, writes diag[0] (largest count) and
+// diag[1] (sum of max(0, count - cap)) and puts the ticket back to zero for
+// the next launch. ticket/part: one slot of a library-owned device array
+// (zero at load, zero again after every launch); at most kDiagGrid
+// workgroups. conteos 16-byte aligned. Each thread issues kDiagItems
+// 16-byte loads per round before using any of them.
 constexpr int kDiagItems = 4;
-// NT threads per workgroup (a template, so that every translation unit that
-// sees this header may define it).
+constexpr int kDiagThreads = 512;
+constexpr uint32_t kDiagGrid = 256;  // workgroups at most (one partial each)
+constexpr uint32_t kDiagSlots = 64;  // launches that may be in flight at once on one GPU
+struct DiagScratch {
+  uint32_t ticket[kDiagSlots];
+  uint2 part[kDiagSlots][kDiagGrid];
+};
+
 template <int NT>
-__global__ __launch_bounds__(NT) void diag_kernel(const uint32_t* __restrict__ conteos, uint32_t cells,
-                                                  uint32_t cap, uint32_t* __restrict__ diag) {
+__global__ __launch_bounds__(NT) void cell_diag_kernel(const uint32_t* __restrict__ conteos, uint32_t cells,
+                                                       uint32_t cap, uint32_t* __restrict__ diag,
+                                                       uint32_t* ticket, uint2* part) {
+  static_assert(kDiagGrid <= static_cast<uint32_t>(NT), "the last workgroup folds one partial per thread");
   __shared__ uint32_t s_m[NT / 64], s_o[NT / 64];
+  __shared__ uint32_t s_last;
   uint32_t m = 0, o = 0;
   const uint64_t nvec = cells / 4u;
   const uint64_t round = static_cast<uint64_t>(gridDim.x) * NT * kDiagItems;
@@ -102,7 +114,47 @@ __global__ __launch_bounds__(NT) void diag_kernel(const uint32_t* __restrict__ c
     s_o[threadIdx.x >> 6] = o;
   }
   __syncthreads();
-  publish_diag<NT>(s_m, s_o, diag);
+  if (threadIdx.x == 0) {
+    uint32_t bm = 0, bo = 0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+      bm = (s_m[w] > bm) ? s_m[w] : bm;
+      bo += s_o[w];
+    }
+    part[blockIdx.x] = make_uint2(bm, bo);
+    // release: the pair is visible device-wide before the ticket is taken;
+    // acquire: the last workgroup then sees every earlier pair
+    const uint32_t t = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = (t == gridDim.x - 1u) ? 1u : 0u;
+  }
+  __syncthreads();
+  if (s_last == 0u) return;  // workgroup-uniform
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  uint2 pr = make_uint2(0u, 0u);
+  if (threadIdx.x < gridDim.x) {
+    const uint64_t v = __hip_atomic_load(reinterpret_cast<uint64_t*>(part) + threadIdx.x, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    pr = make_uint2(static_cast<uint32_t>(v), static_cast<uint32_t>(v >> 32));
+  }
+  m = wave_max_u32(pr.x);
+  o = wave_add_u32(pr.y);
+  __syncthreads();  // s_m/s_o reads of the fold above are done
+  if ((threadIdx.x & 63) == 0) {
+    s_m[threadIdx.x >> 6] = m;
+    s_o[threadIdx.x >> 6] = o;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t bm = 0, bo = 0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+      bm = (s_m[w] > bm) ? s_m[w] : bm;
+      bo += s_o[w];
+    }
+    diag[0] = bm;
+    diag[1] = bo;
+    __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next launch
+  }
 }
 
 }  // namespace ugp

@@ -1,5 +1,6 @@
-// kernels_direct.h -- the direct (global-atomic) index build, used for grids
-// above 2^24 cells, plus the stand-alone scan.
+// kernels_direct.h -- the direct (global-atomic) index build, used when the
+// tile paths do not apply (more than 2^26 cell keys, or a bucketed tile
+// would exceed 2^14 cells), plus the stand-alone scan.
 //
 // These follow the pages' chain closely: a clear, a count kernel with one
 // device-scope atomicAdd per particle on conteos, a prefix scan, and a

@@ -31,6 +31,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cfloat>
 #include <cmath>
 #include <cstddef>
@@ -49,6 +50,34 @@
 namespace {
 
 using namespace ugp;
+
+// Library-owned device memory, one copy on every GPU the library runs on,
+// zero when the code object loads and held until the process ends. Host
+// code never passes these names to a kernel (in host code they stand for a
+// host-side shadow, not a device address): it asks for each array's address
+// on the current device once (symbol_address) and passes that.
+//   diag_scratch  per-workgroup partials and tickets of the one-launch
+//                 overflow diagnostics (cell_diag_kernel)
+static __device__ __align__(256) DiagScratch diag_scratch;
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_diag_scratch_ptr[kMaxDevices];
+std::atomic<uint32_t> g_diag_slot{0};
+
+// Device address of a library-owned __device__ array on the current device:
+// hipGetSymbolAddress on the first call per device, the kept address after.
+template <typename T>
+int symbol_address(const T& symbol, std::atomic<void*>* cache, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return UGP_ERR_HIP;
+  void* p = cache[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, symbol) != hipSuccess || p == nullptr) return UGP_ERR_HIP;
+    cache[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return UGP_OK;
+}
 
 constexpr uint32_t kCounterWords = 64;    // small counter block (direct path)
 constexpr uint32_t kMortonMaxBits = 10;   // Morton keys: 10 bits per axis, 2^30 keys
@@ -336,16 +365,24 @@ void launch_clear(uint32_t* ptr, uint64_t words, uint32_t* extra, uint32_t extra
   hipLaunchKernelGGL(clear_kernel, dim3(blocks), dim3(kBlock), 0, s, ptr, words, extra, extra_words);
 }
 
-// Overflow diagnostics of a final conteos array: zero the two words, then
-// reduce (paths other than staged, and the standalone entry point).
-void enqueue_cell_diag(const uint32_t* conteos, uint64_t cells, uint32_t cap, uint32_t* diag,
-                       hipStream_t s) {
-  launch_clear(diag, 2, nullptr, 0, s);
-  if (cells == 0) return;
-  uint32_t blocks = blocks_for((cells + 3) / 4, static_cast<uint64_t>(kDiagBlock) * kDiagItems);
-  if (blocks > kDiagMaxGrid) blocks = kDiagMaxGrid;
-  hipLaunchKernelGGL(diag_kernel<kDiagBlock>, dim3(blocks), dim3(kDiagBlock), 0, s, conteos,
-                     static_cast<uint32_t>(cells), cap, diag);
+// Overflow diagnostics of a final conteos array (the direct path, and the
+// standalone entry point): one launch whose last workgroup writes both
+// words, with per-workgroup partials in one slot of diag_scratch. Slots are
+// dealt round robin, so up to kDiagSlots launches may be in flight at once
+// on one GPU (more race on a slot).
+int enqueue_cell_diag(const uint32_t* conteos, uint64_t cells, uint32_t cap, uint32_t* diag,
+                      hipStream_t s) {
+  void* base = nullptr;
+  const int st = symbol_address(HIP_SYMBOL(diag_scratch), g_diag_scratch_ptr, &base);
+  if (st != UGP_OK) return st;
+  DiagScratch* sc = static_cast<DiagScratch*>(base);
+  const uint32_t slot = g_diag_slot.fetch_add(1u, std::memory_order_relaxed) % kDiagSlots;
+  uint32_t blocks = blocks_for((cells + 3) / 4, static_cast<uint64_t>(kDiagThreads) * kDiagItems);
+  if (blocks > kDiagGrid) blocks = kDiagGrid;
+  if (blocks == 0) blocks = 1;  // no cells: one workgroup writes the two zeros
+  hipLaunchKernelGGL(cell_diag_kernel<kDiagThreads>, dim3(blocks), dim3(kDiagThreads), 0, s, conteos,
+                     static_cast<uint32_t>(cells), cap, diag, &sc->ticket[slot], &sc->part[slot][0]);
+  return UGP_OK;
 }
 
 // Where the scatter kernels write the records: nowhere (a gather follows, or
@@ -541,7 +578,7 @@ void enqueue_bucketed(uint32_t stage, const BuildArgs& a, const Plan& p) {
   }
 }
 
-void enqueue_direct(uint32_t stage, const BuildArgs& a, const Plan& p) {
+int enqueue_direct(uint32_t stage, const BuildArgs& a, const Plan& p) {
   char* ws = static_cast<char*>(a.workspace);
   uint32_t* cursor = reinterpret_cast<uint32_t*>(ws + p.off_cursor);
   uint32_t* tilesum = reinterpret_cast<uint32_t*>(ws + p.off_small);
@@ -569,7 +606,10 @@ void enqueue_direct(uint32_t stage, const BuildArgs& a, const Plan& p) {
         hipLaunchKernelGGL(scatter_kernel<true>, pgrid, dim3(kBlock), 0, s, a.celdaDe, a.n, cells,
                            cursor, a.ordenado, reinterpret_cast<const uint4*>(a.particles),
                            record_dst(a, p));
-      if (a.diag) enqueue_cell_diag(a.conteos, p.cells, a.capacity, a.diag, s);
+      if (a.diag) {
+        const int st = enqueue_cell_diag(a.conteos, p.cells, a.capacity, a.diag, s);
+        if (st != UGP_OK) return st;
+      }
       break;
     case 4:
       if (p.stable) enqueue_stable_sort(a, p, ws);
@@ -580,6 +620,7 @@ void enqueue_direct(uint32_t stage, const BuildArgs& a, const Plan& p) {
     default:
       break;
   }
+  return UGP_OK;
 }
 
 int enqueue_stage(uint32_t stage, const BuildArgs& a, const Plan& p) {
@@ -600,9 +641,11 @@ int enqueue_stage(uint32_t stage, const BuildArgs& a, const Plan& p) {
     case Path::kBucketed:
       enqueue_bucketed(stage, a, p);
       break;
-    case Path::kDirect:
-      enqueue_direct(stage, a, p);
+    case Path::kDirect: {
+      const int st = enqueue_direct(stage, a, p);
+      if (st != UGP_OK) return st;
       break;
+    }
   }
   return hipGetLastError() == hipSuccess ? UGP_OK : UGP_ERR_HIP;
 }
@@ -721,7 +764,8 @@ int ugp_cell_diag(const uint32_t* conteos, uint32_t cells, uint32_t capacity, ui
   if (!diag || (cells > 0 && !conteos)) return UGP_ERR_NULL;
   if (!aligned(diag, 4) || (cells > 0 && !aligned(conteos, 16))) return UGP_ERR_ALIGN;
   if (overlap(span_of(conteos, 4ull * cells), span_of(diag, 8))) return UGP_ERR_ALIAS;
-  enqueue_cell_diag(conteos, cells, capacity, diag, static_cast<hipStream_t>(stream));
+  const int st = enqueue_cell_diag(conteos, cells, capacity, diag, static_cast<hipStream_t>(stream));
+  if (st != UGP_OK) return st;
   return hipGetLastError() == hipSuccess ? UGP_OK : UGP_ERR_HIP;
 }
 
