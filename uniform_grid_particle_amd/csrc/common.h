@@ -61,6 +61,45 @@ __device__ __forceinline__ void list_cells_wave(const FixLists& fl, uint32_t cel
   }
 }
 
+// Work shared among the workgroups of one tile kernel launch: the scatter
+// of tiles past the staged capacity. The workgroup that owns such a tile
+// claims one of kMaxSlots slots as soon as it knows its count; while it
+// counts the tile it writes the chunk-array position of every particle of
+// the tile, in the tile's own order, into the tile's places of a source
+// list (n words); after the scan it leaves one cursor per cell in the slot
+// (its next free tile-local place) and marks the slot ready. The tile's
+// particles are then scattered in rounds of kRound, each taken from the
+// slot's ticket by the owner or by any other tile's workgroup that saw a
+// claimed slot before its own stores. A workgroup waits only for a slot that
+// was claimed, i.e. for an owner that is running and that waits for no one.
+//   header (kQueueHeader words, zeroed by the first kernel of the build):
+//     [0] slots claimed; for slot s: [kReadyWord + s] ready (0/1),
+//     [kTicketWord + s] next round to hand out, [kRoundsWord + s] rounds,
+//     [kStartWord + s] the tile's first place, [kCountWord + s] its count,
+//     [kTileWord + s] the tile
+//   slot s: one cursor per cell of a tile
+constexpr uint32_t kRound = 4096;
+constexpr uint32_t kMaxSlots = 64;
+constexpr uint32_t kReadyWord = 64;
+constexpr uint32_t kTicketWord = kReadyWord + kMaxSlots;
+constexpr uint32_t kRoundsWord = kTicketWord + kMaxSlots;
+constexpr uint32_t kStartWord = kRoundsWord + kMaxSlots;
+constexpr uint32_t kCountWord = kStartWord + kMaxSlots;
+constexpr uint32_t kTileWord = kCountWord + kMaxSlots;
+constexpr uint32_t kQueueHeader = kTileWord + kMaxSlots;
+// chunk_sort's index words on the staged path: (tile-local cell << kIdxBits)
+// | index inside the chunk (chunks of at most 2^kIdxBits particles)
+constexpr uint32_t kIdxBits = 11;
+struct TileQueue {
+  uint32_t* base;      // nullptr: no sharing (single-tile path)
+  uint32_t* sources;   // n words: chunk-array positions of shared tiles' particles
+  uint32_t slot_words; // cursors per slot (the tile size)
+  __device__ __forceinline__ uint32_t* hdr() const { return base; }
+  __device__ __forceinline__ uint32_t* cursors(uint32_t s) const {
+    return base + kQueueHeader + static_cast<size_t>(s) * slot_words;
+  }
+};
+
 struct GridParams {
   float ox, oy, oz;  // origin
   float h;           // cell size

@@ -35,17 +35,21 @@ constexpr uint32_t kBucketBlocks = 256;     // blocks at most: the matrix stays 
 constexpr int kBucketThreads = 1024;        // threads per block
 constexpr int kBucketBatch = 4;             // particles per thread in flight
 
-// keys: particles [blockIdx.x * per_block, ...) of n. diag, fix_counts (or
-// nullptr): the two overflow-diagnostic words and the two stable fix-up
-// list lengths, zeroed here for the tile kernel.
+// keys: particles [blockIdx.x * per_block, ...) of n. diag, fix_counts,
+// queue_hdr (or nullptr): the two overflow-diagnostic words, the two stable
+// fix-up list lengths and the shared-round counters, zeroed here for the
+// tile kernel.
 __global__ __launch_bounds__(kBucketThreads) void bucket_keys_kernel(
     const uint4* __restrict__ parts, uint32_t n, uint32_t per_block, GridParams g,
     uint32_t* __restrict__ celdaDe, uint32_t* __restrict__ hist, uint32_t tile_shift,
-    uint32_t ntiles, uint32_t* __restrict__ diag, uint32_t* __restrict__ fix_counts) {
+    uint32_t ntiles, uint32_t* __restrict__ diag, uint32_t* __restrict__ fix_counts,
+    uint32_t* __restrict__ queue_hdr) {
   __shared__ uint32_t s_hist[kBucketMaxTiles];
   for (uint32_t t = threadIdx.x; t < ntiles; t += kBucketThreads) s_hist[t] = 0u;
   if (diag != nullptr && blockIdx.x == 0 && threadIdx.x < 2) diag[threadIdx.x] = 0u;
   if (fix_counts != nullptr && blockIdx.x == 0 && threadIdx.x < 2) fix_counts[threadIdx.x] = 0u;
+  if (queue_hdr != nullptr && blockIdx.x == 0)  // shared rounds: claimed slots and ready flags
+    for (uint32_t j = threadIdx.x; j < kQueueHeader; j += kBucketThreads) queue_hdr[j] = 0u;
   __syncthreads();
   const uint64_t base = static_cast<uint64_t>(blockIdx.x) * per_block;
   const uint64_t end = (base + per_block < n) ? base + per_block : n;

@@ -69,6 +69,18 @@ constexpr uint32_t kSingleMax = kCellsThreads * kStagedRegs;  // particles one t
 constexpr uint32_t kSingleSplitLog = 6;             // single path: up to 2^6 tiles (no diagnostics, no stable order)
 constexpr uint32_t kCellsWin = 2048;                // tile_sort LDS staging window
 
+// Words shared through the tile kernel's queue are written and read with
+// device-scope atomic operations, which are coherent across the XCDs'
+// separate L2 caches without writing back or invalidating those caches
+// (a release or acquire fence at device scope would do both, for every
+// line, while other workgroups stream their tiles).
+__device__ __forceinline__ uint32_t shared_load(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void shared_store(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Tile t's workgroup index, spreading consecutive tiles over workgroups of
 // the same XCD (workgroups are dealt to the 8 XCDs round robin), so tiles
 // that read neighbouring runs of each chunk share that XCD's L2 lines.
@@ -80,11 +92,15 @@ __device__ __forceinline__ uint32_t tile_of_block(uint32_t b, uint32_t ntiles) {
 // chunk_sort: CT threads, chunk b holds particles [b*chunk, (b+1)*chunk)
 // with chunk = CT * kChunkItems.
 // rows[b*ntiles + t] = {particles of chunk b in tile t, those in tiles < t}.
+// chunk_idx[q] = (tile-local cell << kIdxBits) | index inside the chunk.
+// diag, fix_counts, queue_hdr (or nullptr): words the tile kernel
+// accumulates into, zeroed here.
 template <int CT>
 __global__ __launch_bounds__(CT) void staged_keys_kernel(
     const uint4* __restrict__ parts, uint32_t n, GridParams g, uint32_t* __restrict__ celdaDe,
     uint2* __restrict__ rows, uint32_t tile_shift, uint32_t ntiles, uint4* __restrict__ chunk_rec,
-    uint32_t* __restrict__ chunk_idx, uint32_t* __restrict__ diag, uint32_t* __restrict__ fix_counts) {
+    uint32_t* __restrict__ chunk_idx, uint32_t* __restrict__ diag, uint32_t* __restrict__ fix_counts,
+    uint32_t* __restrict__ queue_hdr) {
   constexpr int kChunkThreads = CT;
   constexpr uint32_t kChunk = CT * kChunkItems;
   constexpr uint32_t kTilesPerThread = kStagedMaxTiles / CT;  // tile bins per thread
@@ -95,9 +111,13 @@ __global__ __launch_bounds__(CT) void staged_keys_kernel(
   __shared__ uint32_t s_wave[kChunkThreads / 64];
 
   for (uint32_t t = threadIdx.x; t < kStagedMaxTiles; t += kChunkThreads) s_hist[t] = 0u;
+  const uint32_t tile_mask = (1u << tile_shift) - 1u;
   // the overflow diagnostics (when asked for) accumulate in tile_sort
   if (diag != nullptr && blockIdx.x == 0 && threadIdx.x < 2) diag[threadIdx.x] = 0u;
   if (fix_counts != nullptr && blockIdx.x == 0 && threadIdx.x < 2) fix_counts[threadIdx.x] = 0u;  // stable fix-up lists
+  if (queue_hdr != nullptr && blockIdx.x == 0)  // shared rounds: claimed slots and ready flags
+    for (uint32_t j = threadIdx.x; j < kQueueHeader; j += CT) queue_hdr[j] = 0u;
+  static_assert(kChunk <= (1u << kIdxBits), "chunk-local indices fit their field");
   const uint32_t base = blockIdx.x * kChunk;
   // the records stay in registers (scalar arrays, static indices) until
   // they are placed in LDS in tile order
@@ -112,9 +132,10 @@ __global__ __launch_bounds__(CT) void staged_keys_kernel(
     w[4][j] = b.x; w[5][j] = b.y; w[6][j] = b.z; w[7][j] = b.w;
   }
   __syncthreads();  // s_hist zeroed
-  // cell keys and tile ranks; every global store of this kernel is issued
-  // at its end: the wait for a record register loaded earlier would also
-  // wait for every store issued since (one counter tracks both)
+  // cell keys and tile ranks; the keys go out at once (celdaDe), so those
+  // stores drain while the chunk is sorted in LDS (memory operations
+  // complete in issue order, so waiting for a record register loaded
+  // before them does not wait for them)
   uint32_t cellv[kChunkItems], rank[kChunkItems];
 #pragma unroll
   for (int j = 0; j < kChunkItems; ++j) {
@@ -125,6 +146,9 @@ __global__ __launch_bounds__(CT) void staged_keys_kernel(
     cellv[j] = act ? c : 0xFFFFFFFFu;
     rank[j] = act ? atomicAdd(&s_hist[c >> tile_shift], 1u) : 0u;
   }
+#pragma unroll
+  for (int j = 0; j < kChunkItems; ++j)
+    if (cellv[j] != 0xFFFFFFFFu) celdaDe[base + j * kChunkThreads + threadIdx.x] = cellv[j];
   __syncthreads();
   // exclusive scan of the tile histogram: kTilesPerThread consecutive bins per thread
   uint32_t cnt[kTilesPerThread], exq[kTilesPerThread];
@@ -151,7 +175,7 @@ __global__ __launch_bounds__(CT) void staged_keys_kernel(
       const uint32_t local = s_hist[cellv[j] >> tile_shift] + rank[j];
       s_rec[2 * local] = make_uint4(w[0][j], w[1][j], w[2][j], w[3][j]);
       s_rec[2 * local + 1] = make_uint4(w[4][j], w[5][j], w[6][j], w[7][j]);
-      s_idx[local] = base + j * kChunkThreads + threadIdx.x;
+      s_idx[local] = ((cellv[j] & tile_mask) << kIdxBits) | (j * kChunkThreads + threadIdx.x);
     }
   }
   __syncthreads();
@@ -167,9 +191,6 @@ __global__ __launch_bounds__(CT) void staged_keys_kernel(
     const uint32_t t = threadIdx.x * kTilesPerThread + q;
     if (t < ntiles) rows[static_cast<size_t>(blockIdx.x) * ntiles + t] = make_uint2(cnt[q], exq[q]);
   }
-#pragma unroll
-  for (int j = 0; j < kChunkItems; ++j)
-    if (cellv[j] != 0xFFFFFFFFu) celdaDe[base + j * kChunkThreads + threadIdx.x] = cellv[j];
 }
 
 // tile_sort: NT threads; the tile of block b (tile_of_block) owns cells
@@ -194,13 +215,23 @@ __global__ __launch_bounds__(CT) void staged_keys_kernel(
 // a tile holding such a longer cell also copies those arrival-order indices
 // to fl.idx() (the whole tile when it is staged, the long cells' ranges when
 // it is scattered), which the fix-up's long-cell pass reads.
+// packed (staged path): chunk_idx words hold the tile-local cell and the
+// index inside the chunk (chunk_sort), so no cell key is computed here and
+// a particle's index is its chunk's first index plus that field; otherwise
+// (bucketed path, single path) a word is the particle index and the cell
+// comes from the record's position.
+// q (not SINGLE): the shared scatter rounds of tiles past the staged
+// capacity (TileQueue), taken by the tile's owner and by every workgroup
+// that saw a claimed slot before its own stores. In stable mode such a tile
+// scatters alone.
 template <bool MOVE, bool DIAG, bool STABLE, bool SINGLE, uint32_t SHIFT, int NT, uint32_t WIN>
 __global__ __launch_bounds__(NT) void staged_cells_kernel(
     const uint2* __restrict__ rows, uint32_t nchunks, uint32_t chunk, uint32_t ntiles, GridParams g,
     uint32_t cells, uint32_t n, const uint4* __restrict__ chunk_rec,
     const uint32_t* __restrict__ chunk_idx, uint32_t* __restrict__ conteos,
     uint32_t* __restrict__ inicios, uint32_t* __restrict__ ordenado, uint4* __restrict__ dst,
-    uint32_t cap, uint32_t* __restrict__ diag, FixLists fl, uint32_t* __restrict__ keys_out) {
+    uint32_t cap, uint32_t* __restrict__ diag, FixLists fl, uint32_t* __restrict__ keys_out,
+    TileQueue q, uint32_t packed) {
   constexpr uint32_t kTileCells = 1u << SHIFT;
   // cells per thread in the scan (tiles smaller than the workgroup: one
   // cell for each of the first kTileCells threads)
@@ -208,10 +239,15 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
   constexpr uint32_t kChunksPerThread = kStagedMaxChunks / NT;
   constexpr uint32_t kStagedCap = NT * kStagedRegs;  // staged tile capacity
   constexpr uint32_t kStagedWin = WIN;
+  constexpr uint32_t kRoundPer = kRound / NT;  // particles per thread in a shared round
+  constexpr uint32_t kSpinLimit = 1u << 20;  // bound on every wait (each ends in microseconds)
+  constexpr uint32_t kIdxMask = (1u << kIdxBits) - 1u;
   static_assert(kTileCells < NT || kTileCells % NT == 0, "whole cells per thread");
   static_assert(SHIFT >= 2, "tiles start on 16-byte boundaries of conteos and inicios");
   static_assert(kStagedMaxChunks % NT == 0, "whole chunk rows per thread");
   static_assert(2 * WIN * 4 >= kStagedCap, "the source map (and, stable, every index) fits in the staging buffer");
+  static_assert(kRound % NT == 0 && kRound <= kStagedCap, "a shared round is whole particles per thread");
+  static_assert(SHIFT <= 16, "tile-local cells and round ranks share a word");
   __shared__ uint32_t s_cnt[kTileCells];
   __shared__ uint32_t s_dst[kStagedMaxChunks];  // tile-local start of each chunk's run
   __shared__ uint32_t s_src[kStagedMaxChunks];  // where that run starts in the chunk array
@@ -224,6 +260,7 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
   // past the capacity counts such cells
   __shared__ uint32_t s_any_long;
   __shared__ uint32_t s_below;  // SINGLE: particles in earlier tiles
+  __shared__ uint32_t s_item;   // shared rounds: the item or slot this workgroup took
 
   // one tile holding the whole input: no kernel runs before this one, so the
   // words it would zero are zeroed here, before the first barrier below
@@ -231,7 +268,8 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
     if (diag != nullptr) diag[threadIdx.x] = 0u;
     if (fl.base != nullptr) fl.base[threadIdx.x] = 0u;
   }
-
+  const bool share = !SINGLE && q.base != nullptr;
+  const bool pk = !SINGLE && packed != 0u;
   const uint32_t t = tile_of_block(blockIdx.x, ntiles);
   const uint32_t cell0 = t << SHIFT;
   const uint32_t tc = (cells - cell0 < kTileCells) ? cells - cell0 : kTileCells;
@@ -241,18 +279,18 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
   uint2 r[kChunksPerThread];
   uint32_t len_sum = 0, pre_sum = 0;
 #pragma unroll
-  for (uint32_t q = 0; q < kChunksPerThread; ++q) {
-    const uint32_t c = threadIdx.x * kChunksPerThread + q;
+  for (uint32_t k = 0; k < kChunksPerThread; ++k) {
+    const uint32_t c = threadIdx.x * kChunksPerThread + k;
     // SINGLE: one run of all n particles
-    r[q] = (c < nchunks) ? (SINGLE ? make_uint2(n, 0u) : rows[static_cast<size_t>(c) * ntiles + t]) : make_uint2(0u, 0u);
-    len_sum += r[q].x;
-    pre_sum += r[q].y;
+    r[k] = (c < nchunks) ? (SINGLE ? make_uint2(n, 0u) : rows[static_cast<size_t>(c) * ntiles + t]) : make_uint2(0u, 0u);
+    len_sum += r[k].x;
+    pre_sum += r[k].y;
   }
   uint32_t count;
   // the longest chunk run of the tile (it picks how the source map is built)
   uint32_t my_run = 0;
 #pragma unroll
-  for (uint32_t q = 0; q < kChunksPerThread; ++q) my_run = (r[q].x > my_run) ? r[q].x : my_run;
+  for (uint32_t k = 0; k < kChunksPerThread; ++k) my_run = (r[k].x > my_run) ? r[k].x : my_run;
   my_run = wave_inclusive_max(my_run);
   if ((threadIdx.x & 63) == 63) s_runmax[threadIdx.x >> 6] = my_run;  // visible after the next barrier
   uint32_t run_dst = block_exclusive_sum<NT>(len_sum, s_wave, &count);
@@ -261,22 +299,22 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
   uint32_t longest_run = 0;
 #pragma unroll
   for (int w = 0; w < NT / 64; ++w) longest_run = (s_runmax[w] > longest_run) ? s_runmax[w] : longest_run;
-  const bool short_runs = longest_run <= kShortRun;
+  bool short_runs = longest_run <= kShortRun;
 #pragma unroll
-  for (uint32_t q = 0; q < kChunksPerThread; ++q) {
-    const uint32_t c = threadIdx.x * kChunksPerThread + q;
+  for (uint32_t k = 0; k < kChunksPerThread; ++k) {
+    const uint32_t c = threadIdx.x * kChunksPerThread + k;
     if (c < nchunks) {
       s_dst[c] = run_dst;
-      s_src[c] = c * chunk + r[q].y;  // chunks of `chunk` particles (bucketed, single: one chunk)
+      s_src[c] = c * chunk + r[k].y;  // chunks of `chunk` particles (bucketed, single: one chunk)
     }
-    run_dst += r[q].x;
+    run_dst += r[k].x;
   }
   for (uint32_t j = threadIdx.x; j < kTileCells; j += NT) s_cnt[j] = 0u;
   if (SINGLE && threadIdx.x == 0) s_below = 0u;
   __syncthreads();
 
-  // source map of a window of the tile: s_map[q] = chunk-array position of
-  // tile-local particle base + q, for q < len <= kStagedCap (s_map aliases the
+  // source map of a window of the tile: s_map[k] = chunk-array position of
+  // tile-local particle base + k, for k < len <= kStagedCap (s_map aliases the
   // staging buffer). Runs are laid out in chunk order, so the chunk of a
   // position is the last chunk whose run starts at or before it: every run
   // start (or, for the run covering `base`, position 0) is marked with its
@@ -286,37 +324,39 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
   // simply expands its own chunk's run instead. The scan contains barriers
   // (the tile-uniform choice keeps them uniform); callers put one before
   // build_map (the previous reads of s_map are done) and one after.
+  // r[].x, short_runs, s_dst and s_src describe the tile being mapped (a
+  // shared round replaces them with its slot's run table).
   uint32_t* s_map = reinterpret_cast<uint32_t*>(s_rec);
   constexpr uint32_t kMapPer = kStagedCap / NT;  // window entries per thread
-  auto build_map = [&](uint32_t base, uint32_t len) {
+  auto build_map = [&](uint32_t base, uint32_t len) __attribute__((always_inline)) {
     const uint32_t end = base + len;
     if (nchunks == 1u) {
       // one run (a tile stored contiguously): the source is its start plus p
-      for (uint32_t q = threadIdx.x; q < len; q += NT) s_map[q] = s_src[0] + (base + q);
+      for (uint32_t k = threadIdx.x; k < len; k += NT) s_map[k] = s_src[0] + (base + k);
       return;
     }
     if (short_runs) {
       // every run short: each thread expands the runs of its own chunks
 #pragma unroll
-      for (uint32_t q = 0; q < kChunksPerThread; ++q) {
-        const uint32_t c = threadIdx.x * kChunksPerThread + q;
+      for (uint32_t k = 0; k < kChunksPerThread; ++k) {
+        const uint32_t c = threadIdx.x * kChunksPerThread + k;
         if (c < nchunks) {
-          const uint32_t d0 = s_dst[c], d1 = d0 + r[q].x;
+          const uint32_t d0 = s_dst[c], d1 = d0 + r[k].x;
           const uint32_t lo = (d0 > base) ? d0 : base, hi = (d1 < end) ? d1 : end;
-          for (uint32_t k = lo; k < hi; ++k) s_map[k - base] = s_src[c] + (k - d0);
+          for (uint32_t j = lo; j < hi; ++j) s_map[j - base] = s_src[c] + (j - d0);
         }
       }
       return;
     }
     const uint32_t m0 = threadIdx.x * kMapPer;
 #pragma unroll
-    for (uint32_t q = 0; q < kMapPer; ++q) s_map[m0 + q] = 0u;
+    for (uint32_t k = 0; k < kMapPer; ++k) s_map[m0 + k] = 0u;
     __syncthreads();
 #pragma unroll
-    for (uint32_t q = 0; q < kChunksPerThread; ++q) {
-      const uint32_t c = threadIdx.x * kChunksPerThread + q;
-      if (c < nchunks && r[q].x > 0u) {
-        const uint32_t d0 = s_dst[c], d1 = d0 + r[q].x;
+    for (uint32_t k = 0; k < kChunksPerThread; ++k) {
+      const uint32_t c = threadIdx.x * kChunksPerThread + k;
+      if (c < nchunks && r[k].x > 0u) {
+        const uint32_t d0 = s_dst[c], d1 = d0 + r[k].x;
         if (d0 < end && d1 > base) s_map[(d0 > base) ? d0 - base : 0u] = c + 1u;
       }
     }
@@ -324,37 +364,42 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
     uint32_t mark[kMapPer];
     uint32_t run = 0;
 #pragma unroll
-    for (uint32_t q = 0; q < kMapPer; ++q) {
-      mark[q] = s_map[m0 + q];
-      run = (mark[q] > run) ? mark[q] : run;
+    for (uint32_t k = 0; k < kMapPer; ++k) {
+      mark[k] = s_map[m0 + k];
+      run = (mark[k] > run) ? mark[k] : run;
     }
     uint32_t cur = block_exclusive_max<NT>(run, s_wave);
 #pragma unroll
-    for (uint32_t q = 0; q < kMapPer; ++q) {
-      cur = (mark[q] > cur) ? mark[q] : cur;
-      const uint32_t pos = base + m0 + q;
-      if (m0 + q < len && cur > 0u) s_map[m0 + q] = s_src[cur - 1u] + (pos - s_dst[cur - 1u]);
+    for (uint32_t k = 0; k < kMapPer; ++k) {
+      cur = (mark[k] > cur) ? mark[k] : cur;
+      const uint32_t pos = base + m0 + k;
+      if (m0 + k < len && cur > 0u) s_map[m0 + k] = s_src[cur - 1u] + (pos - s_dst[cur - 1u]);
     }
+  };
+
+  // a particle's index from its chunk-array position and index word
+  auto index_of = [&](uint32_t src, uint32_t word) __attribute__((always_inline)) -> uint32_t {
+    return pk ? (src & ~(chunk - 1u)) + (word & kIdxMask) : word;
   };
 
   // exclusive scan in LDS: kPer consecutive cells per thread, then the
   // block scan of the per-thread sums; s_cnt becomes the tile-local starts
   // (cells past tc count 0, so their start is the tile total)
-  auto scan_tile = [&]() -> uint32_t {
+  auto scan_tile = [&]() __attribute__((always_inline)) -> uint32_t {
     const uint32_t j0 = threadIdx.x * kPer;
     const bool scans = j0 < kTileCells;
     uint32_t sum = 0;
     if (scans) {
 #pragma unroll 4
-      for (uint32_t q = 0; q < kPer; ++q) sum += s_cnt[j0 + q];
+      for (uint32_t k = 0; k < kPer; ++k) sum += s_cnt[j0 + k];
     }
     uint32_t tot;
     uint32_t run = block_exclusive_sum<NT>(sum, s_wave, &tot);
     if (scans) {
 #pragma unroll 4
-      for (uint32_t q = 0; q < kPer; ++q) {
-        const uint32_t v = s_cnt[j0 + q];
-        s_cnt[j0 + q] = run;
+      for (uint32_t k = 0; k < kPer; ++k) {
+        const uint32_t v = s_cnt[j0 + k];
+        s_cnt[j0 + k] = run;
         run += v;
       }
     }
@@ -366,16 +411,16 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
   // start minus its own. Lane-contiguous 16-byte stores (tiles start at
   // multiples of 16 cells). DIAG: the same counts feed the overflow
   // diagnostics (one more barrier, after which thread 0 publishes).
-  auto write_counts_starts = [&](uint32_t tot) {
+  auto write_counts_starts = [&](uint32_t tot) __attribute__((always_inline)) {
     const uint4* s_cnt4 = reinterpret_cast<const uint4*>(s_cnt);
     const uint32_t tc4 = tc / 4;
     uint32_t dmax = 0, dover = 0;
-    for (uint32_t q = threadIdx.x; q < tc4; q += NT) {
-      const uint4 v = s_cnt4[q];
-      const uint32_t next = (4 * q + 4 < kTileCells) ? s_cnt[4 * q + 4] : tot;
+    for (uint32_t k = threadIdx.x; k < tc4; k += NT) {
+      const uint4 v = s_cnt4[k];
+      const uint32_t next = (4 * k + 4 < kTileCells) ? s_cnt[4 * k + 4] : tot;
       const uint4 c = make_uint4(v.y - v.x, v.z - v.y, v.w - v.z, next - v.w);
-      reinterpret_cast<uint4*>(conteos + cell0)[q] = c;
-      reinterpret_cast<uint4*>(inicios + cell0)[q] = make_uint4(bs + v.x, bs + v.y, bs + v.z, bs + v.w);
+      reinterpret_cast<uint4*>(conteos + cell0)[k] = c;
+      reinterpret_cast<uint4*>(inicios + cell0)[k] = make_uint4(bs + v.x, bs + v.y, bs + v.z, bs + v.w);
       if (DIAG) {
         const uint32_t a = (c.x > c.y) ? c.x : c.y;
         const uint32_t b = (c.z > c.w) ? c.z : c.w;
@@ -407,6 +452,149 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
     }
   };
 
+  // One shared scatter round: positions [base, base + len) of a shared
+  // tile's own order (its sources from the source list), counted per cell
+  // in LDS (rank = the value the LDS atomic returns); every cell the round
+  // touches takes a block of places from the slot's cursor with one atomic,
+  // and every particle goes to its cell's block plus its rank.
+  auto scatter_round = [&](uint32_t slot, uint32_t round, uint32_t wbs, uint32_t wcount,
+                           uint32_t wtile) __attribute__((always_inline)) {
+    const uint32_t base = round * kRound;
+    if (base >= wcount) return;  // uniform
+    const uint32_t len = (wcount - base < kRound) ? wcount - base : kRound;
+    const uint32_t rcell0 = wtile << SHIFT;
+    const uint32_t rtc = (cells - rcell0 < kTileCells) ? cells - rcell0 : kTileCells;
+    uint32_t* cur = q.cursors(slot);
+    __syncthreads();  // the previous use of s_cnt is over
+    for (uint32_t j = threadIdx.x; j < kTileCells; j += NT) s_cnt[j] = 0u;
+    uint32_t src[kRoundPer], word[kRoundPer], lr[kRoundPer], v[8][kRoundPer];
+#pragma unroll
+    for (uint32_t k = 0; k < kRoundPer; ++k) {
+      const uint32_t j = threadIdx.x + k * NT;
+      const size_t pos = static_cast<size_t>(wbs) + base + j;
+      const uint32_t m = (j < len && pos < n) ? shared_load(q.sources + pos) : 0u;
+      src[k] = (m < n) ? m : n - 1u;  // n >= 1: a tile holds particles
+    }
+#pragma unroll
+    for (uint32_t k = 0; k < kRoundPer; ++k) word[k] = chunk_idx[src[k]];
+#pragma unroll
+    for (uint32_t k = 0; k < kRoundPer; ++k) {
+      const uint4 a = (MOVE || !pk) ? chunk_rec[static_cast<size_t>(src[k]) * 2u] : make_uint4(0u, 0u, 0u, 0u);
+      const uint4 b = MOVE ? chunk_rec[static_cast<size_t>(src[k]) * 2u + 1u] : make_uint4(0u, 0u, 0u, 0u);
+      v[0][k] = a.x; v[1][k] = a.y; v[2][k] = a.z; v[3][k] = a.w;
+      v[4][k] = b.x; v[5][k] = b.y; v[6][k] = b.z; v[7][k] = b.w;
+    }
+    __syncthreads();  // s_cnt is zero
+#pragma unroll
+    for (uint32_t k = 0; k < kRoundPer; ++k) {
+      const uint32_t j = threadIdx.x + k * NT;
+      const uint32_t loc = pk ? word[k] >> kIdxBits
+                              : cell_of(__uint_as_float(v[0][k]), __uint_as_float(v[1][k]),
+                                        __uint_as_float(v[2][k]), g) - rcell0;
+      lr[k] = (j < len && loc < rtc) ? (loc << 16) | atomicAdd(&s_cnt[loc], 1u) : 0xFFFFFFFFu;
+    }
+    __syncthreads();
+    {
+      // the block of places this round takes in each cell it touches: the
+      // atomics of a batch of 4 cells per thread in flight together
+      constexpr uint32_t kCellIter = (kTileCells + NT - 1) / NT;
+      constexpr uint32_t kBatch = (kCellIter < 4u) ? kCellIter : 4u;
+#pragma unroll 1
+      for (uint32_t k0 = 0; k0 < kCellIter; k0 += kBatch) {
+        uint32_t cnt[kBatch], at[kBatch];
+#pragma unroll
+        for (uint32_t k = 0; k < kBatch; ++k) {
+          const uint32_t j = threadIdx.x + (k0 + k) * NT;
+          cnt[k] = (j < rtc) ? s_cnt[j] : 0u;
+          at[k] = (cnt[k] != 0u) ? atomicAdd(&cur[j], cnt[k]) : 0u;
+        }
+#pragma unroll
+        for (uint32_t k = 0; k < kBatch; ++k)
+          if (cnt[k] != 0u) s_cnt[threadIdx.x + (k0 + k) * NT] = at[k];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (uint32_t k = 0; k < kRoundPer; ++k) {
+      if (lr[k] == 0xFFFFFFFFu) continue;
+      const size_t out = static_cast<size_t>(wbs) + s_cnt[lr[k] >> 16] + (lr[k] & 0xFFFFu);
+      if (out < n) {
+        ordenado[out] = index_of(src[k], word[k]);
+        if (MOVE) {
+          dst[out * 2u] = make_uint4(v[0][k], v[1][k], v[2][k], v[3][k]);
+          dst[out * 2u + 1u] = make_uint4(v[4][k], v[5][k], v[6][k], v[7][k]);
+        }
+      }
+    }
+  };
+
+  // Takes rounds of the claimed slots until every slot is ready and its
+  // ticket has run past its rounds. Wave 0 reads every slot's ready flag,
+  // ticket and round count at once (one lane per slot), picks the first
+  // slot with rounds left at or after `first` (so that workgroups spread
+  // over the slots) and takes a round from its ticket; a slot not ready yet
+  // counts as having rounds and is waited for: its owner claimed it, so it
+  // is running, and it marks it ready without waiting.
+  auto help = [&](uint32_t first) __attribute__((always_inline)) {
+    for (;;) {
+      __syncthreads();  // every thread has read the previous pick
+      if (threadIdx.x < 64) {
+        const uint32_t lane = threadIdx.x;
+        uint32_t got = 0xFFFFFFFFu, slot = 0, wbs = 0, wcount = 0, wtile = 0;
+        for (uint32_t spin = 0; spin < kSpinLimit; ++spin) {
+          const uint32_t claimed = shared_load(q.hdr());
+          const uint32_t nslots = (claimed < kMaxSlots) ? claimed : kMaxSlots;
+          bool ready = false, left = false;
+          if (lane < nslots) {
+            ready = shared_load(q.hdr() + kReadyWord + lane) != 0u;
+            left = !ready || shared_load(q.hdr() + kTicketWord + lane) < shared_load(q.hdr() + kRoundsWord + lane);
+          }
+          const uint64_t mleft = __ballot(left);
+          if (mleft == 0ull) break;  // every slot ready and exhausted
+          const uint64_t mready = __ballot(left && ready);
+          if (mready == 0ull) {  // rounds remain only in slots not ready yet
+            __builtin_amdgcn_s_sleep(2);
+            continue;
+          }
+          // the first ready slot with rounds left at or after `first` (cyclically)
+          const uint32_t sh = first % 64u;
+          const uint64_t rot = (mready >> sh) | (sh ? (mready << (64u - sh)) : 0ull);
+          const uint32_t pick = (static_cast<uint32_t>(__builtin_ctzll(rot)) + sh) % 64u;
+          uint32_t r = 0xFFFFFFFFu, nr = 0u, b0 = 0u, c0 = 0u, t0 = 0u;
+          if (lane == pick) {
+            r = atomicAdd(q.hdr() + kTicketWord + pick, 1u);
+            nr = shared_load(q.hdr() + kRoundsWord + pick);
+            b0 = shared_load(q.hdr() + kStartWord + pick);
+            c0 = shared_load(q.hdr() + kCountWord + pick);
+            t0 = shared_load(q.hdr() + kTileWord + pick);
+          }
+          r = static_cast<uint32_t>(__shfl(static_cast<int>(r), static_cast<int>(pick)));
+          nr = static_cast<uint32_t>(__shfl(static_cast<int>(nr), static_cast<int>(pick)));
+          if (r < nr) {
+            got = r;
+            slot = pick;
+            wbs = static_cast<uint32_t>(__shfl(static_cast<int>(b0), static_cast<int>(pick)));
+            wcount = static_cast<uint32_t>(__shfl(static_cast<int>(c0), static_cast<int>(pick)));
+            wtile = static_cast<uint32_t>(__shfl(static_cast<int>(t0), static_cast<int>(pick)));
+            break;
+          }
+        }
+        if (lane == 0) {  // s_dst and s_src are free once the workgroup's own tile is done
+          s_item = got;
+          s_dst[0] = wbs;
+          s_src[0] = wcount;
+          s_dst[1] = slot;
+          s_src[1] = wtile;
+        }
+      }
+      __syncthreads();
+      const uint32_t round = s_item, wbs = s_dst[0], wcount = s_src[0], slot = s_dst[1], wtile = s_src[1];
+      if (round == 0xFFFFFFFFu) return;  // uniform
+      if (wtile < ntiles && wcount <= n && wbs <= n - wcount)  // uniform checks keep it in bounds
+        scatter_round(slot, round, wbs, wcount, wtile);
+    }
+  };
+
   if (count <= kStagedCap) {
     // records held in registers as scalar arrays (static indices); lr packs
     // a particle's tile-local cell (high half) and its rank in that cell
@@ -425,11 +613,15 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
         const uint32_t p = threadIdx.x + k * NT;
         src[k] = s_map[p < count ? p : 0u];  // clamped: loads below are unconditional
       }
+      // index words first, then the records: with packed words the count
+      // below needs only the words (loads complete in issue order), so it
+      // runs while the records are still on their way
+#pragma unroll
+      for (int k = 0; k < kStagedRegs; ++k) idx[k] = SINGLE ? src[k] : chunk_idx[src[k]];  // SINGLE: the input itself
 #pragma unroll
       for (int k = 0; k < kStagedRegs; ++k) {
-        const uint4 a = chunk_rec[static_cast<size_t>(src[k]) * 2u];
+        const uint4 a = (MOVE || !pk) ? chunk_rec[static_cast<size_t>(src[k]) * 2u] : make_uint4(0u, 0u, 0u, 0u);
         const uint4 b = MOVE ? chunk_rec[static_cast<size_t>(src[k]) * 2u + 1u] : make_uint4(0u, 0u, 0u, 0u);
-        idx[k] = SINGLE ? src[k] : chunk_idx[src[k]];  // SINGLE: the input itself, in order
         w[0][k] = a.x; w[1][k] = a.y; w[2][k] = a.z; w[3][k] = a.w;
         w[4][k] = b.x; w[5][k] = b.y; w[6][k] = b.z; w[7][k] = b.w;
       }
@@ -438,9 +630,14 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
 #pragma unroll
       for (int k = 0; k < kStagedRegs; ++k) {
         const uint32_t p = threadIdx.x + k * NT;
-        const uint32_t key = cell_of(__uint_as_float(w[0][k]), __uint_as_float(w[1][k]),
-                                     __uint_as_float(w[2][k]), g);
-        const uint32_t loc = key - cell0;
+        uint32_t loc, key = 0;
+        if (pk) {
+          loc = idx[k] >> kIdxBits;
+          idx[k] = index_of(src[k], idx[k]);
+        } else {
+          key = cell_of(__uint_as_float(w[0][k]), __uint_as_float(w[1][k]), __uint_as_float(w[2][k]), g);
+          loc = key - cell0;
+        }
         if (p < count && loc < tc) lr[k] = (loc << 16) | atomicAdd(&s_cnt[loc], 1u);
         if (SINGLE) {  // particles of earlier tiles, one LDS atomic per wave
           const uint64_t m = __ballot(p < count && key < cell0);
@@ -461,6 +658,11 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
     // SINGLE: every workgroup read the whole input; its tile starts after the
     // particles of the tiles before it
     if (SINGLE) bs = s_below;
+    // slots claimed so far (owners claim theirs right after reading their
+    // rows), read before this tile's stores and kept in s_item, which is
+    // unused until the tail: after the stores the workgroup helps only when
+    // some slot was claimed (a load used after the stores waits for them)
+    if (share && threadIdx.x == 0) s_item = shared_load(q.hdr());
     const uint32_t tot = scan_tile();
     write_counts_starts(tot);  // overlaps the placement below
     uint32_t slot[kStagedRegs];
@@ -520,89 +722,138 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
       }
       __syncthreads();
       const size_t out0 = static_cast<size_t>(bs) + w0;
-      for (uint32_t q = threadIdx.x; q < wn; q += NT) {
-        if (out0 + q < n) {
-          ordenado[out0 + q] = s_idx[q];
-          if (STABLE && any_long) fl.idx()[out0 + q] = s_idx[q];
+      for (uint32_t k = threadIdx.x; k < wn; k += NT) {
+        if (out0 + k < n) {
+          ordenado[out0 + k] = s_idx[k];
+          if (STABLE && any_long) fl.idx()[out0 + k] = s_idx[k];
         }
       }
       if (MOVE) {
-        for (uint32_t q = threadIdx.x; q < 2 * wn; q += NT)
-          if (out0 * 2u + q < 2ull * n) dst[out0 * 2u + q] = s_rec[q];
+        for (uint32_t k = threadIdx.x; k < 2 * wn; k += NT)
+          if (out0 * 2u + k < 2ull * n) dst[out0 * 2u + k] = s_rec[k];
       }
       __syncthreads();
     }
+    if (share && !STABLE && s_item != 0u) help(blockIdx.x);  // uniform: written before the barriers above
   } else {
-    // a tile past the staged capacity (count > kStagedCap > 0): rounds of
-    // kStagedCap particles (kStagedRegs per thread), each with the source
-    // map of its window and its loads in flight together; the records are
-    // read again for the scatter below
+    // a tile past the staged capacity (count > kStagedCap > 0). Not in
+    // stable mode: claim a slot now, so that tiles still loading see it
+    uint32_t sidx = kMaxSlots;
+    if (share && !STABLE) {
+      if (threadIdx.x == 0) s_item = atomicAdd(q.hdr(), 1u);
+      __syncthreads();
+      sidx = s_item;
+    }
+    const bool shared = sidx < kMaxSlots;  // uniform
+    // the count goes in rounds of kStagedCap particles (kStagedRegs per thread), each
+    // with the source map of its window and its loads in flight together;
+    // packed index words give the cells directly, else the positions are
+    // read. Shared: the sources go to the source list as well.
     for (uint32_t base = 0; base < count; base += kStagedCap) {
       const uint32_t len = (count - base < kStagedCap) ? count - base : kStagedCap;
       __syncthreads();  // the previous round's map reads are done
       build_map(base, len);
       __syncthreads();
-      uint32_t src[kStagedRegs];
-      float px[kStagedRegs], py[kStagedRegs], pz[kStagedRegs];
+      uint32_t src[kStagedRegs], loc[kStagedRegs];
 #pragma unroll
       for (int k = 0; k < kStagedRegs; ++k) {
-        const uint32_t q = threadIdx.x + k * NT;
-        src[k] = s_map[q < len ? q : 0u];  // clamped: loads below are unconditional
+        const uint32_t p = threadIdx.x + k * NT;
+        src[k] = s_map[p < len ? p : 0u];  // clamped: loads below are unconditional
       }
+      if (pk) {
 #pragma unroll
-      for (int k = 0; k < kStagedRegs; ++k) {
-        const uint4 a = chunk_rec[static_cast<size_t>(src[k]) * 2u];
-        px[k] = __uint_as_float(a.x);
-        py[k] = __uint_as_float(a.y);
-        pz[k] = __uint_as_float(a.z);
+        for (int k = 0; k < kStagedRegs; ++k) loc[k] = chunk_idx[src[k]] >> kIdxBits;
+      } else {
+        float px[kStagedRegs], py[kStagedRegs], pz[kStagedRegs];
+#pragma unroll
+        for (int k = 0; k < kStagedRegs; ++k) {
+          const uint4 a = chunk_rec[static_cast<size_t>(src[k]) * 2u];
+          px[k] = __uint_as_float(a.x);
+          py[k] = __uint_as_float(a.y);
+          pz[k] = __uint_as_float(a.z);
+        }
+#pragma unroll
+        for (int k = 0; k < kStagedRegs; ++k) loc[k] = cell_of(px[k], py[k], pz[k], g) - cell0;
       }
 #pragma unroll
       for (int k = 0; k < kStagedRegs; ++k) {
         const uint32_t p = base + threadIdx.x + k * NT;
-        const uint32_t loc = cell_of(px[k], py[k], pz[k], g) - cell0;
-        if (p < count && loc < tc) atomicAdd(&s_cnt[loc], 1u);
+        if (p < count && loc[k] < tc) atomicAdd(&s_cnt[loc[k]], 1u);
+      }
+      if (shared) {  // after the loads: they complete in issue order, so these stores do not delay them
+#pragma unroll
+        for (int k = 0; k < kStagedRegs; ++k) {
+          const uint32_t p = threadIdx.x + k * NT;
+          const uint32_t pos = bs + base + p;  // < n when p < len
+          if (p < len) shared_store(q.sources + pos, src[k]);
+        }
       }
     }
     __syncthreads();
     const uint32_t tot = scan_tile();
+    if (shared) {
+      // the cursors (tile-local starts) and the header words go out with
+      // device-coherent stores, all complete before the slot is marked
+      // ready (each wave waits for its own, then the barrier); conteos and
+      // inicios follow
+      uint32_t* curs = q.cursors(sidx);
+      for (uint32_t j = threadIdx.x; j < tc; j += NT) shared_store(curs + j, s_cnt[j]);
+      if (threadIdx.x == 0) {
+        shared_store(q.hdr() + kRoundsWord + sidx, (count + kRound - 1u) / kRound);
+        shared_store(q.hdr() + kStartWord + sidx, bs);
+        shared_store(q.hdr() + kCountWord + sidx, count);
+        shared_store(q.hdr() + kTileWord + sidx, t);
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitLoadsAndStores);
+      __syncthreads();
+      if (threadIdx.x == 0) shared_store(q.hdr() + kReadyWord + sidx, 1u);
+    }
     write_counts_starts(tot);
     __syncthreads();  // every start read before the cursors advance
-    // the same rounds: each particle takes its slot from its cell's cursor
-    // and is written there directly (the tile's output range is small
-    // enough that partial lines merge in L2)
-    constexpr int kOver = kStagedRegs;
-    for (uint32_t base = 0; base < count; base += NT * kOver) {
-      const uint32_t len = (count - base < NT * kOver) ? count - base : NT * kOver;
-      __syncthreads();  // the previous round's map reads are done
-      build_map(base, len);
-      __syncthreads();
-      uint32_t src[kOver], id[kOver], v[8][kOver];
+    if (shared) help(sidx);
+    if (!shared) {
+      // alone: the same rounds again, each particle taking its slot from its
+      // cell's cursor and written there directly (the tile's output range is
+      // small enough that partial lines merge in L2)
+      constexpr int kOver = kStagedRegs;
+      for (uint32_t base = 0; base < count; base += NT * kOver) {
+        const uint32_t len = (count - base < NT * kOver) ? count - base : NT * kOver;
+        __syncthreads();  // the previous round's map reads are done
+        build_map(base, len);
+        __syncthreads();
+        uint32_t src[kOver], id[kOver], v[8][kOver];
 #pragma unroll
-      for (int k = 0; k < kOver; ++k) {
-        const uint32_t q = threadIdx.x + k * NT;
-        src[k] = s_map[q < len ? q : 0u];
-      }
+        for (int k = 0; k < kOver; ++k) {
+          const uint32_t p = threadIdx.x + k * NT;
+          src[k] = s_map[p < len ? p : 0u];
+        }
 #pragma unroll
-      for (int k = 0; k < kOver; ++k) {
-        const uint4 a = chunk_rec[static_cast<size_t>(src[k]) * 2u];
-        const uint4 b = MOVE ? chunk_rec[static_cast<size_t>(src[k]) * 2u + 1u] : make_uint4(0u, 0u, 0u, 0u);
-        id[k] = SINGLE ? src[k] : chunk_idx[src[k]];
-        v[0][k] = a.x; v[1][k] = a.y; v[2][k] = a.z; v[3][k] = a.w;
-        v[4][k] = b.x; v[5][k] = b.y; v[6][k] = b.z; v[7][k] = b.w;
-      }
+        for (int k = 0; k < kOver; ++k) {
+          const uint4 a = (MOVE || !pk) ? chunk_rec[static_cast<size_t>(src[k]) * 2u] : make_uint4(0u, 0u, 0u, 0u);
+          const uint4 b = MOVE ? chunk_rec[static_cast<size_t>(src[k]) * 2u + 1u] : make_uint4(0u, 0u, 0u, 0u);
+          id[k] = SINGLE ? src[k] : chunk_idx[src[k]];
+          v[0][k] = a.x; v[1][k] = a.y; v[2][k] = a.z; v[3][k] = a.w;
+          v[4][k] = b.x; v[5][k] = b.y; v[6][k] = b.z; v[7][k] = b.w;
+        }
 #pragma unroll
-      for (int k = 0; k < kOver; ++k) {
-        const uint32_t p = base + threadIdx.x + k * NT;
-        const uint32_t loc = cell_of(__uint_as_float(v[0][k]), __uint_as_float(v[1][k]),
-                                     __uint_as_float(v[2][k]), g) - cell0;
-        if (!(p < count && loc < tc)) continue;
-        if (SINGLE) keys_out[id[k]] = cell0 + loc;
-        const size_t out = static_cast<size_t>(bs) + atomicAdd(&s_cnt[loc], 1u);
-        if (out < n) {
-          ordenado[out] = id[k];
-          if (MOVE) {
-            dst[out * 2u] = make_uint4(v[0][k], v[1][k], v[2][k], v[3][k]);
-            dst[out * 2u + 1u] = make_uint4(v[4][k], v[5][k], v[6][k], v[7][k]);
+        for (int k = 0; k < kOver; ++k) {
+          const uint32_t p = base + threadIdx.x + k * NT;
+          uint32_t loc;
+          if (pk) {
+            loc = id[k] >> kIdxBits;
+            id[k] = index_of(src[k], id[k]);
+          } else {
+            loc = cell_of(__uint_as_float(v[0][k]), __uint_as_float(v[1][k]), __uint_as_float(v[2][k]), g) - cell0;
+          }
+          if (!(p < count && loc < tc)) continue;
+          if (SINGLE) keys_out[id[k]] = cell0 + loc;
+          const size_t out = static_cast<size_t>(bs) + atomicAdd(&s_cnt[loc], 1u);
+          if (out < n) {
+            ordenado[out] = id[k];
+            if (MOVE) {
+              dst[out * 2u] = make_uint4(v[0][k], v[1][k], v[2][k], v[3][k]);
+              dst[out * 2u + 1u] = make_uint4(v[4][k], v[5][k], v[6][k], v[7][k]);
+            }
           }
         }
       }

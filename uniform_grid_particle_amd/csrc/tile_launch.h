@@ -15,7 +15,8 @@ namespace ugp {
   uint32_t shift, dim3 grid, hipStream_t s, const uint2 *rows, uint32_t nchunks, uint32_t chunk,    \
       uint32_t ntiles, GridParams g, uint32_t cells, uint32_t n, const uint4 *chunk_rec,           \
       const uint32_t *chunk_idx, uint32_t *conteos, uint32_t *inicios, uint32_t *ordenado,         \
-      uint4 *dst, uint32_t cap, uint32_t *diag, FixLists fl, uint32_t *keys_out
+      uint4 *dst, uint32_t cap, uint32_t *diag, FixLists fl, uint32_t *keys_out, TileQueue q,              \
+      uint32_t packed
 
 template <bool MOVE, bool DIAG, bool STABLE, bool SINGLE>
 void launch_staged_cells(UGP_TILE_LAUNCH_PARAMS);
@@ -26,10 +27,10 @@ void launch_staged_cells_at(dim3 grid, hipStream_t s, const uint2* rows, uint32_
                             uint32_t chunk, uint32_t ntiles, GridParams g, uint32_t cells, uint32_t n,
                             const uint4* chunk_rec, const uint32_t* chunk_idx, uint32_t* conteos,
                             uint32_t* inicios, uint32_t* ordenado, uint4* dst, uint32_t cap,
-                            uint32_t* diag, FixLists fl, uint32_t* keys_out) {
+                            uint32_t* diag, FixLists fl, uint32_t* keys_out, TileQueue q, uint32_t packed) {
   hipLaunchKernelGGL((staged_cells_kernel<MOVE, DIAG, STABLE, SINGLE, SHIFT, kCellsThreads, kCellsWin>), grid,
                      dim3(kCellsThreads), 0, s, rows, nchunks, chunk, ntiles, g, cells, n, chunk_rec,
-                     chunk_idx, conteos, inicios, ordenado, dst, cap, diag, fl, keys_out);
+                     chunk_idx, conteos, inicios, ordenado, dst, cap, diag, fl, keys_out, q, packed);
 }
 
 template <bool MOVE, bool DIAG, bool STABLE, bool SINGLE>
@@ -39,7 +40,7 @@ void launch_staged_cells(UGP_TILE_LAUNCH_PARAMS) {
     launch_staged_cells_at<MOVE, DIAG, STABLE, SINGLE, S>(grid, s, rows, nchunks, chunk, ntiles, \
                                                           g, cells, n, chunk_rec, chunk_idx,     \
                                                           conteos, inicios, ordenado, dst, cap,  \
-                                                          diag, fl, keys_out);                   \
+                                                          diag, fl, keys_out, q, packed);        \
     break;
   switch (shift) {
     UGP_STAGED_CASE(4)

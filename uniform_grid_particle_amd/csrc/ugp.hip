@@ -118,6 +118,9 @@ struct Plan {
   // stable mode on the tile paths: cells the tile kernel could not sort
   uint32_t fix_cap = 0;
   size_t off_fix = 0;
+  // tile paths (staged, bucketed): the shared scatter rounds (TileQueue)
+  bool queue = false;
+  size_t off_queue = 0, off_sources = 0;
   size_t total = 256;
 };
 
@@ -133,6 +136,17 @@ uint32_t bucket_shift(uint64_t n, uint64_t cells, uint32_t lg) {
   if (s > kStagedMaxShift) s = kStagedMaxShift;  // sparse grids: more, smaller tiles
   const uint32_t fewest = (lg > kStagedMinShift + 12) ? lg - 12 : kStagedMinShift;  // 4096 tiles
   return (s < fewest) ? fewest : s;
+}
+
+// The shared scatter of a tile path: the queue header, kMaxSlots cursor
+// arrays of one tile each, and the source list (n words).
+size_t plan_queue(Plan* p, uint32_t n, size_t off) {
+  p->queue = true;
+  p->off_queue = off;
+  off = align_up(off + (static_cast<size_t>(kQueueHeader) + static_cast<size_t>(kMaxSlots) * (1u << p->tile_shift)) * 4u,
+                 256);
+  p->off_sources = off;
+  return align_up(off + static_cast<size_t>(n) * 4u, 256);
 }
 
 int make_plan(uint32_t n, const uint32_t dims[3], uint32_t flags, Plan* p) {
@@ -201,6 +215,7 @@ int make_plan(uint32_t n, const uint32_t dims[3], uint32_t flags, Plan* p) {
     off = align_up(off + static_cast<size_t>(n) * 32u, 256);
     p->off_chunk_idx = off;
     off = align_up(off + static_cast<size_t>(n) * 4u, 256);
+    off = plan_queue(p, n, off);
   } else if (bucket_shift(n, cells, lg) <= kStagedMaxShift) {
     // bucketed path: the same tile rule with up to kBucketMaxTiles tiles
     p->path = Path::kBucketed;
@@ -222,6 +237,7 @@ int make_plan(uint32_t n, const uint32_t dims[3], uint32_t flags, Plan* p) {
     off = align_up(off + static_cast<size_t>(n) * 32u, 256);
     p->off_chunk_idx = off;
     off = align_up(off + static_cast<size_t>(n) * 4u, 256);
+    off = plan_queue(p, n, off);
   } else {
     p->path = Path::kDirect;
     p->bin_shift = (lg > kMinBinShift + 9) ? lg - 9 : kMinBinShift;
@@ -395,6 +411,16 @@ uint4* record_dst(const BuildArgs& a, const Plan& p) {
   return reinterpret_cast<uint4*>(a.reordered);
 }
 
+// the shared scatter of the tile paths (no queue otherwise)
+TileQueue tile_queue_of(const BuildArgs& a, const Plan& p) {
+  TileQueue q{};
+  if (!p.queue) return q;
+  q.base = reinterpret_cast<uint32_t*>(static_cast<char*>(a.workspace) + p.off_queue);
+  q.sources = reinterpret_cast<uint32_t*>(static_cast<char*>(a.workspace) + p.off_sources);
+  q.slot_words = 1u << p.tile_shift;
+  return q;
+}
+
 // the stable fix-up lists of the tile paths (null otherwise)
 FixLists fix_lists_of(const BuildArgs& a, const Plan& p) {
   FixLists fl{};
@@ -464,11 +490,14 @@ void launch_tile_sort(const BuildArgs& a, const Plan& p, const uint2* rows, cons
   const FixLists fl = fix_lists_of(a, p);
   const GridParams g = grid_params(a);
   uint32_t* keys_out = SINGLE ? a.celdaDe : nullptr;
+  const TileQueue q = SINGLE ? TileQueue{} : tile_queue_of(a, p);
+  const uint32_t packed = (p.path == Path::kStaged) ? 1u : 0u;  // chunk_sort's index words
   // one instantiation per (moves records, diagnostics, stable order)
 #define UGP_TILE_SORT(M, D, S)                                                                        \
   launch_staged_cells<M, D, S, SINGLE>(p.tile_shift, grid, s, rows, p.nchunks, p.chunk, p.ntiles, g, \
                                        cells, a.n, rec, idx, a.conteos, a.inicios, a.ordenado, dst,  \
-                                       D ? a.capacity : 0u, D ? a.diag : nullptr, fl, keys_out)
+                                       D ? a.capacity : 0u, D ? a.diag : nullptr, fl, keys_out, q,   \
+                                       packed)
   const bool m = p.move, d = a.diag != nullptr, st = p.stable;
   if (m && d && st) UGP_TILE_SORT(true, true, true);
   else if (m && d) UGP_TILE_SORT(true, true, false);
@@ -521,11 +550,13 @@ void enqueue_staged(uint32_t stage, const BuildArgs& a, const Plan& p) {
       if (p.chunk == kSmallChunk)
         hipLaunchKernelGGL(staged_keys_kernel<kSmallChunkThreads>, dim3(p.nchunks), dim3(kSmallChunkThreads), 0,
                            s, reinterpret_cast<const uint4*>(a.particles), a.n, grid_params(a), a.celdaDe, rows,
-                           p.tile_shift, p.ntiles, chunk_rec, chunk_idx, a.diag, fix_lists_of(a, p).base);
+                           p.tile_shift, p.ntiles, chunk_rec, chunk_idx, a.diag, fix_lists_of(a, p).base,
+                           tile_queue_of(a, p).base);
       else
         hipLaunchKernelGGL(staged_keys_kernel<kChunkThreads>, dim3(p.nchunks), dim3(kChunkThreads), 0, s,
                            reinterpret_cast<const uint4*>(a.particles), a.n, grid_params(a), a.celdaDe, rows,
-                           p.tile_shift, p.ntiles, chunk_rec, chunk_idx, a.diag, fix_lists_of(a, p).base);
+                           p.tile_shift, p.ntiles, chunk_rec, chunk_idx, a.diag, fix_lists_of(a, p).base,
+                           tile_queue_of(a, p).base);
       break;
     case 3:
       launch_tile_sort<false>(a, p, rows, chunk_rec, chunk_idx);
@@ -553,7 +584,8 @@ void enqueue_bucketed(uint32_t stage, const BuildArgs& a, const Plan& p) {
     case 0:
       hipLaunchKernelGGL(bucket_keys_kernel, dim3(p.nblk), dim3(kBucketThreads), 0, s,
                          reinterpret_cast<const uint4*>(a.particles), a.n, p.per_block, grid_params(a),
-                         a.celdaDe, hist, p.tile_shift, p.ntiles, a.diag, fix_lists_of(a, p).base);
+                         a.celdaDe, hist, p.tile_shift, p.ntiles, a.diag, fix_lists_of(a, p).base,
+                         tile_queue_of(a, p).base);
       break;
     case 1:
       hipLaunchKernelGGL(bucket_colscan_kernel, dim3(p.ntiles), dim3(kBlock), 0, s, hist, p.nblk,
