@@ -34,9 +34,10 @@
  *    pointers are read before the call returns.
  *  - The caller allocates and owns every buffer. The library never
  *    allocates or frees memory and never synchronises the host with the
- *    device. It keeps no state between calls except one fixed device array
+ *    device. It keeps no state between calls except two fixed device arrays
  *    of its own per GPU (zero at load): the per-workgroup partials of
- *    ugp_cell_diag() (left ready for the next launch by every launch).
+ *    ugp_cell_diag() (left ready for the next launch by every launch), and
+ *    the workspace of ugp_grid_build_noalloc().
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    The call returns once the work is enqueued; outputs are valid when the
  *    stream reaches that point, and inputs must not change before then.
@@ -184,6 +185,23 @@ int ugp_grid_build(const ugp_particle *particles, uint32_t n, const float origin
                    float cell_size, const uint32_t dims[3], uint32_t *celdaDe, uint32_t *conteos,
                    uint32_t *inicios, uint32_t *ordenado, ugp_particle *reordered, void *workspace,
                    size_t workspace_bytes, uint32_t flags, void *stream);
+
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc: the same
+ * build as ugp_grid_build() without a workspace argument. Its workspace is a
+ * library-owned device array of UGP_NOALLOC_SCRATCH_BYTES on each GPU (held
+ * from the library's load until the process ends); the call allocates and
+ * frees nothing. Every call on one GPU shares that array, so calls that
+ * overlap on one GPU (other streams, other host threads) race: order them
+ * on one stream. Arguments, outputs and errors as ugp_grid_build();
+ * UGP_ERR_WORKSPACE, with nothing enqueued, when ugp_grid_workspace_bytes()
+ * for (n, dims, flags) exceeds UGP_NOALLOC_SCRATCH_BYTES (it covers, for
+ * example, 1,000,000 particles on a 128^3 grid with any flags). */
+#define UGP_NOALLOC_SCRATCH_BYTES (48u << 20)
+int ugp_grid_build_noalloc(const ugp_particle *particles, uint32_t n, const float origin[3],
+                           float cell_size, const uint32_t dims[3], uint32_t *celdaDe, uint32_t *conteos,
+                           uint32_t *inicios, uint32_t *ordenado, ugp_particle *reordered, uint32_t flags,
+                           void *stream);
 
 /* Enqueue one stage slot (0..UGP_NUM_STAGES-1) of ugp_grid_build() with the
  * same arguments. Running the slots 0..UGP_NUM_STAGES-1 in order on one stream

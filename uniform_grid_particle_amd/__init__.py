@@ -90,6 +90,8 @@ def load_library():
     lib.ugp_grid_build_timed.argtypes = [*build_args, _u32, _vp, _vp]
     lib.ugp_grid_build_diag.restype = ctypes.c_int
     lib.ugp_grid_build_diag.argtypes = [*build_args[:-2], _u32, _vp, _u32, _vp]
+    lib.ugp_grid_build_noalloc.restype = ctypes.c_int
+    lib.ugp_grid_build_noalloc.argtypes = [*build_args[:10], _u32, _vp]
     lib.ugp_neighbor_count.restype = ctypes.c_int
     lib.ugp_neighbor_count.argtypes = [_vp, _u32, ctypes.POINTER(ctypes.c_float), ctypes.c_float,
                                        ctypes.POINTER(_u32), _vp, _vp, ctypes.c_float, _vp, _u32, _vp]
@@ -295,6 +297,33 @@ def grid_build(
     return out
 
 
+NOALLOC_SCRATCH_BYTES = 48 << 20  # UGP_NOALLOC_SCRATCH_BYTES
+
+
+def grid_build_noalloc(
+    particles: torch.Tensor,
+    origin: Sequence[float],
+    cell_size: float,
+    dims: Sequence[int],
+    out: GridIndex,
+    *,
+    stable: bool = False,
+    gather: bool = False,
+    morton: bool = False,
+    index_only: bool = False,
+    stream=None,
+) -> GridIndex:
+    """ugp_grid_build_noalloc: the build into caller-given outputs with the
+    library's own fixed device workspace (nothing is allocated). Calls that
+    overlap on one GPU race on that workspace."""
+    lib = load_library()
+    flags = _flags(stable, gather, morton) | (FLAG_INDEX_ONLY if index_only else 0)
+    args = _build_args(particles, origin, cell_size, dims, out, None, flags, stream)
+    with _on(particles.device):
+        _check(lib.ugp_grid_build_noalloc(*args[:10], args[12], args[13]), "ugp_grid_build_noalloc")
+    return out
+
+
 def grid_build_diag(
     particles: torch.Tensor,
     origin: Sequence[float],
@@ -488,7 +517,7 @@ def as_u32_numpy(t: torch.Tensor):
 
 __all__ = [
     "GridIndex", "UGPError", "alloc_outputs", "as_u32_numpy", "cell_diag", "exclusive_scan_u32", "grid_build",
-    "grid_build_diag", "neighbor_count", "reorder_arrays", "ArrayDesc", "FLAG_INDEX_ONLY",
+    "grid_build_diag", "grid_build_noalloc", "neighbor_count", "reorder_arrays", "ArrayDesc", "FLAG_INDEX_ONLY",
     "grid_build_stage", "grid_build_timed", "library_path", "load_library", "reorder", "stage_names",
     "status_string", "workspace_bytes", "key_count", "FLAG_STABLE", "FLAG_GATHER", "FLAG_MORTON", "NUM_STAGES",
 ]

@@ -58,10 +58,13 @@ using namespace ugp;
 // on the current device once (symbol_address) and passes that.
 //   diag_scratch  per-workgroup partials and tickets of the one-launch
 //                 overflow diagnostics (cell_diag_kernel)
+//   scratch       the workspace of ugp_grid_build_noalloc
 static __device__ __align__(256) DiagScratch diag_scratch;
+static __device__ __align__(256) unsigned char scratch[UGP_NOALLOC_SCRATCH_BYTES];
 
 constexpr int kMaxDevices = 64;
 std::atomic<void*> g_diag_scratch_ptr[kMaxDevices];
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
 std::atomic<uint32_t> g_diag_slot{0};
 
 // Device address of a library-owned __device__ array on the current device:
@@ -763,6 +766,29 @@ int ugp_grid_build(const ugp_particle* particles, uint32_t n, const float origin
                                 ordenado, reordered, workspace, workspace_bytes, flags, stream);
   Plan p;
   int st = validate(a, &p);
+  if (st != UGP_OK) return st;
+  for (uint32_t stage = 0; stage < UGP_NUM_STAGES; ++stage) {
+    st = enqueue_stage(stage, a, p);
+    if (st != UGP_OK) return st;
+  }
+  return UGP_OK;
+}
+
+int ugp_grid_build_noalloc(const ugp_particle* particles, uint32_t n, const float origin[3],
+                           float cell_size, const uint32_t dims[3], uint32_t* celdaDe, uint32_t* conteos,
+                           uint32_t* inicios, uint32_t* ordenado, ugp_particle* reordered, uint32_t flags,
+                           void* stream) {
+  Plan p;
+  if (!dims) return UGP_ERR_NULL;
+  int st = make_plan(n, dims, flags, &p);
+  if (st != UGP_OK) return st;
+  if (p.total > UGP_NOALLOC_SCRATCH_BYTES) return UGP_ERR_WORKSPACE;
+  void* ws = nullptr;
+  st = symbol_address(HIP_SYMBOL(scratch), g_scratch_ptr, &ws);
+  if (st != UGP_OK) return st;
+  const BuildArgs a = make_args(particles, n, origin, cell_size, dims, celdaDe, conteos, inicios, ordenado,
+                                reordered, ws, UGP_NOALLOC_SCRATCH_BYTES, flags, stream);
+  st = validate(a, &p);
   if (st != UGP_OK) return st;
   for (uint32_t stage = 0; stage < UGP_NUM_STAGES; ++stage) {
     st = enqueue_stage(stage, a, p);
