@@ -12,11 +12,11 @@ event times (mean, p10/p90 and the worst step are reported beside it). A warm fi
 reported separately; at this size the whole working set fits in the
 Infinity Cache, so warm numbers can exceed what HBM alone allows.
 
-Per-stage durations come from HIP events (torch events on the stream the
-kernels are launched on) that the library records around one stage slot
-inside a full cold build (one C call, so no host work separates stages),
-K builds per slot; the stage with the longest mean duration is the
-dominant kernel whose algorithmic bytes / duration is the roofline figure.
+Per-stage durations come from HIP events that the library records at the
+stage kernel's own start and end (hipExtLaunchKernel) inside a full cold
+build (one C call, so no host work separates stages), K builds per slot,
+median; the stage with the longest median is the dominant kernel, whose
+kernel-I/O bytes / median duration is the roofline figure.
 
 Prints ONE JSON line on stdout.
 """
@@ -632,17 +632,22 @@ def main(argv=None) -> int:
     diag_steps = [dstarts[k].elapsed_time(dends[k]) for k in range(K)]
     diag_ms = statistics.median(diag_steps)
     diag_val = [int(v) for v in ugp.as_u32_numpy(diag)]
-    cd = []
-    for _ in range(K):
-        evict()
-        c0 = torch.cuda.Event(enable_timing=True)
-        c1 = torch.cuda.Event(enable_timing=True)
-        c0.record(stream)
-        ugp.cell_diag(out.conteos, 64, out=diag)
-        c1.record(stream)
-        torch.cuda.synchronize()
-        cd.append(1e3 * c0.elapsed_time(c1))
+    # standalone reduction, cold, timed by its kernel's own start and end;
+    # then the same entry point over an empty histogram (one workgroup, no
+    # loads), the fixed cost of any launch on this clock
+    def diag_kernel_us(conteos):
+        t = []
+        for _ in range(K):
+            evict()
+            c0 = torch.cuda.Event(enable_timing=True)
+            c1 = torch.cuda.Event(enable_timing=True)
+            ugp.cell_diag_timed(conteos, 64, c0, c1, out=diag)
+            torch.cuda.synchronize()
+            t.append(1e3 * c0.elapsed_time(c1))
+        return t
+    cd = diag_kernel_us(out.conteos)
     cell_diag_us = statistics.median(cd)
+    cd0 = diag_kernel_us(out.conteos[:0])
 
     # ---- Morton-keyed variant: K cold builds numbering cells along the Z curve ----
     mflags = flags | ugp.FLAG_MORTON
@@ -695,32 +700,7 @@ def main(argv=None) -> int:
 
     b_total = 116 * n + 16 * cells + 4
     dominant = max((st for st in stages if stages[st]["GBps"] is not None), key=lambda st: stages[st]["us"])
-
-    # ---- dominant kernel alone: after one full build (so its inputs are in
-    # place, as inside the pipeline), REP back-to-back launches of its stage
-    # captured in a HIP graph; events around one replay give the per-launch
-    # time without an event marker per launch ----
-    REP = 20
-    build()
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    slot = stages[dominant]["slot"]
-    with torch.cuda.graph(graph):
-        for _ in range(REP):
-            ugp.grid_build_stage(slot, parts, origin, h, dims, out, ws, flags=flags)
-    graph.replay()
-    torch.cuda.synchronize()
-    g0 = torch.cuda.Event(enable_timing=True)
-    g1 = torch.cuda.Event(enable_timing=True)
-    reps_us = []
-    for _ in range(5):
-        g0.record(stream)
-        graph.replay()
-        g1.record(stream)
-        torch.cuda.synchronize()
-        reps_us.append(1e3 * g0.elapsed_time(g1) / REP)
-    dom_us = statistics.median(reps_us)
-    del graph
+    dom_us = stages[dominant]["us"]
     achieved = bytes_k[dominant] / (dom_us * 1e3)
     traffic = read_traffic(dominant)
 
@@ -768,25 +748,35 @@ def main(argv=None) -> int:
                          "max_per_cell_and_overflows": diag_val,
                          "note": "same cold protocol (median of K steps), overflow diagnostics folded into the build",
                          "cell_diag_us": round(cell_diag_us, 3), "cell_diag_us_p10_p90": _p10_p90(cd),
+                         "cell_diag_empty_us": round(statistics.median(cd0), 3),
+                         "cell_diag_timing": "kernel's own start and end events, cold; "
+                                             "_empty_us: the same call over zero cells (launch and ticket only)",
                          "cell_diag_GBps": round(4 * cells / (cell_diag_us * 1e3), 1)},
         "warm_note": "back-to-back builds; the working set can stay in the 256 MiB Infinity Cache",
         "stages": stages,
         "stage_sum_us": round(sum(s["us"] for s in stages.values()), 3),
-        "stage_note": "each stage timed inside a full cold build, events recorded around it in the same C call "
-                      "(includes the event marker's own cost); median of K builds per stage, p10/p90 beside it",
+        "stage_note": "each stage timed inside a full cold build (one C call): a one-kernel stage by events at its "
+                      "kernel's own start and end (hipExtLaunchKernel), other stages by events around the stage; "
+                      "median of K builds per stage, p10/p90 beside it; GBps and frac_hbm use the kernel-I/O bytes "
+                      "(alg_bytes: every array a kernel reads or writes, counted once for that kernel)",
         "wall_s_timed_loop": wall,
         "roofline": {
             "kernel": dominant,
             "kernel_us": round(dom_us, 3),
             "alg_bytes": bytes_k[dominant],
-            "timing": f"{REP} back-to-back launches replayed from a HIP graph after one full build; "
-                      "events around the replay",
+            "bytes_model": "kernel I/O: every array the kernel reads or writes, counted once (the build's own "
+                           "intermediate arrays included); the method-level figure is hbm_frac_e2e",
+            "timing": "cold: median over K cold builds of the kernel's own start-to-end time (events recorded by "
+                      "the launch itself, hipExtLaunchKernel)",
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": None if achieved is None else achieved / HBM_PEAK_GBS,
             "traffic": traffic,
+            "traffic_note": "fabric traffic per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE between L2 and the "
+                            "Infinity Fabric, each scaled by its reading for a plain device copy; Infinity Cache "
+                            "hits included), or null when the kernel sources changed since it was counted",
         },
     }
     if not args.no_neighbors:

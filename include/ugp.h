@@ -254,6 +254,14 @@ int ugp_grid_build_diag(const ugp_particle *particles, uint32_t n, const float o
 int ugp_cell_diag(const uint32_t *conteos, uint32_t cells, uint32_t capacity, uint32_t *diag,
                   void *stream);
 
+/* ugp_cell_diag() with two caller-owned HIP events (hipEvent_t passed as
+ * void*) recorded at its kernel's own start and end (hipExtLaunchKernel), so
+ * their interval is the kernel's execution time. Returns UGP_ERR_ARG for a
+ * NULL event (nothing enqueued); otherwise as ugp_cell_diag(), and on an
+ * error the events are not recorded. Intended for per-kernel timing. */
+int ugp_cell_diag_timed(const uint32_t *conteos, uint32_t cells, uint32_t capacity, uint32_t *diag,
+                        void *stream, void *event_before, void *event_after);
+
 /* A neighbour query that consumes a finished index: for each particle, the
  * number of other particles among the 27 cells around its cell whose
  * squared distance (dx*dx + dy*dy) + dz*dz (binary32, dx = xj - xi, no fused
@@ -285,10 +293,14 @@ int ugp_neighbor_count(const ugp_particle *particles, uint32_t n, const float or
                        void *stream);
 
 /* ugp_grid_build() with two caller-owned HIP events (hipEvent_t passed as
- * void*) recorded on `stream` immediately before and after stage slot
- * `timed_stage`, in the same call, so no host work separates the stages.
- * Returns UGP_ERR_ARG for a bad slot or a NULL event; otherwise as
- * ugp_grid_build(). Intended for per-kernel timing. */
+ * void*) that time stage slot `timed_stage`, in the same call, so no host
+ * work separates the stages. When the slot is one kernel launch, the events
+ * are recorded at that kernel's own start and end (hipExtLaunchKernel), so
+ * their interval is the kernel's execution time, as a profiler's kernel
+ * trace reports it; otherwise they are recorded on `stream` immediately
+ * before and after the slot (a slot that enqueues nothing gives an empty
+ * interval). Returns UGP_ERR_ARG for a bad slot or a NULL event; otherwise
+ * as ugp_grid_build(). Intended for per-kernel timing. */
 int ugp_grid_build_timed(const ugp_particle *particles, uint32_t n, const float origin[3],
                          float cell_size, const uint32_t dims[3], uint32_t *celdaDe,
                          uint32_t *conteos, uint32_t *inicios, uint32_t *ordenado,

@@ -200,6 +200,12 @@ def test_diag_validation_on_host(lib):
     assert lib.ugp_cell_diag(b + 4, 100, 8, b + (1 << 20), None) == ugp.UGP_ERR_ALIGN
     assert lib.ugp_cell_diag(b, 100, 8, b + (1 << 20) + 1, None) == ugp.UGP_ERR_ALIGN
     assert lib.ugp_cell_diag(b, 100, 8, b + 396, None) == ugp.UGP_ERR_ALIAS  # last word of conteos
+    ev = 1 << 44  # never dereferenced: every case below fails before its launch
+    assert lib.ugp_cell_diag_timed(b, 100, 8, b + (1 << 20), None, None, ev) == ugp.UGP_ERR_ARG
+    assert lib.ugp_cell_diag_timed(b, 100, 8, b + (1 << 20), None, ev, None) == ugp.UGP_ERR_ARG
+    assert lib.ugp_cell_diag_timed(b, 100, 8, None, None, ev, ev) == ugp.UGP_ERR_NULL
+    assert lib.ugp_cell_diag_timed(b + 4, 100, 8, b + (1 << 20), None, ev, ev) == ugp.UGP_ERR_ALIGN
+    assert lib.ugp_cell_diag_timed(b, 100, 8, b + 396, None, ev, ev) == ugp.UGP_ERR_ALIAS
 
 
 def test_key_count_on_host(lib):

@@ -123,3 +123,10 @@ def test_cell_diag_entry_point(ugp, orc, cells):
         ugp.cell_diag(t, cap, out=out)
         torch.cuda.synchronize()
         assert tuple(int(v) for v in _u32(out)) == orc.diag(counts, cap), f"cells={cells} cap={cap}"
+    # the timed entry point runs the same kernel and records its own events
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    out.fill_(-1)
+    ugp.cell_diag_timed(t, 64, e0, e1, out=out)
+    torch.cuda.synchronize()
+    assert tuple(int(v) for v in _u32(out)) == orc.diag(counts, 64), f"timed cells={cells}"
+    assert e0.elapsed_time(e1) >= 0.0

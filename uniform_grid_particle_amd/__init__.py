@@ -99,6 +99,8 @@ def load_library():
     lib.ugp_reorder_arrays.argtypes = [_vp, _u32, _u32, ctypes.POINTER(ArrayDesc), _u32, _vp]
     lib.ugp_cell_diag.restype = ctypes.c_int
     lib.ugp_cell_diag.argtypes = [_vp, _u32, _u32, _vp, _vp]
+    lib.ugp_cell_diag_timed.restype = ctypes.c_int
+    lib.ugp_cell_diag_timed.argtypes = [_vp, _u32, _u32, _vp, _vp, _vp, _vp]
     lib.ugp_grid_stage_name.restype = ctypes.c_char_p
     lib.ugp_grid_stage_name.argtypes = [_u32, ctypes.POINTER(_u32), _u32, _u32]
     lib.ugp_scan_workspace_bytes.restype = ctypes.c_int
@@ -372,6 +374,30 @@ def cell_diag(conteos: torch.Tensor, capacity: int, out: Optional[torch.Tensor] 
         st = lib.ugp_cell_diag(_ptr(conteos), int(conteos.numel()), int(capacity), _ptr(out),
                                _stream_handle(conteos.device, stream))
     _check(st, "ugp_cell_diag")
+    return out
+
+
+def cell_diag_timed(conteos: torch.Tensor, capacity: int, event_before, event_after,
+                    out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """ugp_cell_diag_timed: cell_diag with two torch.cuda.Event objects
+    recorded at its kernel's own start and end."""
+    lib = load_library()
+    _require_gpu(conteos, "conteos", torch.int32)
+    for ev in (event_before, event_after):
+        if not getattr(ev, "cuda_event", 0):
+            ev.record()  # torch creates the underlying event lazily
+    if out is None:
+        with _alloc_on(conteos.device, stream):
+            out = torch.empty(2, dtype=torch.int32, device=conteos.device)
+    _require_gpu(out, "out", torch.int32, conteos.device)
+    if out.numel() < 2:
+        raise ValueError("out needs 2 entries")
+    with _on(conteos.device):
+        st = lib.ugp_cell_diag_timed(_ptr(conteos), int(conteos.numel()), int(capacity), _ptr(out),
+                                     _stream_handle(conteos.device, stream),
+                                     ctypes.c_void_p(event_before.cuda_event),
+                                     ctypes.c_void_p(event_after.cuda_event))
+    _check(st, "ugp_cell_diag_timed")
     return out
 
 

@@ -1,11 +1,33 @@
 // common.h -- constants and device helpers shared by the index-build kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
 
 namespace ugp {
+
+// Kernel launches of the library. When a timed build has armed a pair of
+// events (ugp_grid_build_timed), the next launch records them at that
+// kernel's own start and end (so the interval is the kernel alone, as a
+// profiler's kernel trace measures it) and disarms them; otherwise a plain
+// launch. Host-side, per calling thread.
+struct TimedLaunch {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+extern thread_local TimedLaunch g_timed_launch;
+
+template <typename F, typename... Args>
+inline void launch(F kernel, const dim3& grid, const dim3& block, uint32_t shmem, hipStream_t s, Args... args) {
+  if (g_timed_launch.start != nullptr) {
+    const TimedLaunch t = g_timed_launch;
+    g_timed_launch = TimedLaunch{};
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, t.start, t.stop, 0u, args...);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, shmem, s, args...);
+  }
+}
 
 constexpr int kBlock = 256;     // threads of the streaming kernels (4 waves of 64)
 constexpr uint32_t kMaxDim = 1u << 24;

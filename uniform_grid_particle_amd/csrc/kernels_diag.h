@@ -65,6 +65,7 @@ __device__ __forceinline__ void publish_diag(const uint32_t* s_m, const uint32_t
 constexpr int kDiagItems = 4;
 constexpr int kDiagThreads = 512;
 constexpr uint32_t kDiagGrid = 256;  // workgroups at most (one partial each)
+constexpr uint32_t kDiagRounds = 2;  // load rounds per workgroup below that cap
 constexpr uint32_t kDiagSlots = 64;  // launches that may be in flight at once on one GPU
 struct DiagScratch {
   uint32_t ticket[kDiagSlots];
@@ -121,15 +122,20 @@ __global__ __launch_bounds__(NT) void cell_diag_kernel(const uint32_t* __restric
       bm = (s_m[w] > bm) ? s_m[w] : bm;
       bo += s_o[w];
     }
-    part[blockIdx.x] = make_uint2(bm, bo);
-    // release: the pair is visible device-wide before the ticket is taken;
-    // acquire: the last workgroup then sees every earlier pair
-    const uint32_t t = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    // the pair goes out with a device-coherent store and has completed
+    // before the ticket is taken, so the workgroup that takes the last
+    // ticket reads every pair with device-coherent loads (no cache
+    // writeback or invalidation, which a release or acquire at device scope
+    // would do for every line of the XCD's L2)
+    __hip_atomic_store(reinterpret_cast<uint64_t*>(part) + blockIdx.x,
+                       static_cast<uint64_t>(bm) | (static_cast<uint64_t>(bo) << 32), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(kWaitLoadsAndStores);
+    const uint32_t t = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = (t == gridDim.x - 1u) ? 1u : 0u;
   }
   __syncthreads();
   if (s_last == 0u) return;  // workgroup-uniform
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   uint2 pr = make_uint2(0u, 0u);
   if (threadIdx.x < gridDim.x) {
     const uint64_t v = __hip_atomic_load(reinterpret_cast<uint64_t*>(part) + threadIdx.x, __ATOMIC_RELAXED,

@@ -16,8 +16,10 @@ constexpr int kSortGrid = 512;             // workgroups of the long-cell sort (
 constexpr uint32_t kRecBatch = 8;          // records gathered together by one thread (long cells)
 constexpr uint32_t kBitmapPasses = 4;      // bitmap windows a long cell may take (2^21 index values)
 constexpr uint32_t kMinPart = 1024;        // fewest places of a shared long cell one workgroup takes
-constexpr uint32_t kFixLongBlocks = 128;   // fix-up workgroups on long cells
-constexpr uint32_t kFixShortBlocks = 256;  // fix-up workgroups on short cells
+// fix-up workgroups: 256 in all, one per CU (each takes ~97 KB of LDS), so
+// that a fix-up with nothing listed is one round of workgroups that exit
+constexpr uint32_t kFixLongBlocks = 32;    // on long cells (a cell of 10,000 takes 10)
+constexpr uint32_t kFixShortBlocks = 224;  // on short cells
 
 // Gather: two lanes per record, each moving one 16-byte half, so every
 // store instruction writes a contiguous span. Indices >= n_src are skipped.

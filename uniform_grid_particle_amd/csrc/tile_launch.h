@@ -28,7 +28,7 @@ void launch_staged_cells_at(dim3 grid, hipStream_t s, const uint2* rows, uint32_
                             const uint4* chunk_rec, const uint32_t* chunk_idx, uint32_t* conteos,
                             uint32_t* inicios, uint32_t* ordenado, uint4* dst, uint32_t cap,
                             uint32_t* diag, FixLists fl, uint32_t* keys_out, TileQueue q, uint32_t packed) {
-  hipLaunchKernelGGL((staged_cells_kernel<MOVE, DIAG, STABLE, SINGLE, SHIFT, kCellsThreads, kCellsWin>), grid,
+  launch((staged_cells_kernel<MOVE, DIAG, STABLE, SINGLE, SHIFT, kCellsThreads, kCellsWin>), grid,
                      dim3(kCellsThreads), 0, s, rows, nchunks, chunk, ntiles, g, cells, n, chunk_rec,
                      chunk_idx, conteos, inicios, ordenado, dst, cap, diag, fl, keys_out, q, packed);
 }

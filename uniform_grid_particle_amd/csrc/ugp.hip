@@ -47,6 +47,10 @@
 #include "tile_launch.h"
 #include "ugp.h"
 
+namespace ugp {
+thread_local TimedLaunch g_timed_launch;
+}  // namespace ugp
+
 namespace {
 
 using namespace ugp;
@@ -381,7 +385,7 @@ void launch_clear(uint32_t* ptr, uint64_t words, uint32_t* extra, uint32_t extra
   const uint64_t vec = words / 4;
   uint32_t blocks = blocks_for(vec ? vec : 1, kBlock);
   if (blocks > 2048) blocks = 2048;
-  hipLaunchKernelGGL(clear_kernel, dim3(blocks), dim3(kBlock), 0, s, ptr, words, extra, extra_words);
+  launch(clear_kernel, dim3(blocks), dim3(kBlock), 0, s, ptr, words, extra, extra_words);
 }
 
 // Overflow diagnostics of a final conteos array (the direct path, and the
@@ -396,10 +400,12 @@ int enqueue_cell_diag(const uint32_t* conteos, uint64_t cells, uint32_t cap, uin
   if (st != UGP_OK) return st;
   DiagScratch* sc = static_cast<DiagScratch*>(base);
   const uint32_t slot = g_diag_slot.fetch_add(1u, std::memory_order_relaxed) % kDiagSlots;
-  uint32_t blocks = blocks_for((cells + 3) / 4, static_cast<uint64_t>(kDiagThreads) * kDiagItems);
+  // two load rounds per workgroup: half as many workgroups take the ticket
+  // one after another at the end, for the same bytes in flight
+  uint32_t blocks = blocks_for((cells + 3) / 4, static_cast<uint64_t>(kDiagThreads) * kDiagItems * kDiagRounds);
   if (blocks > kDiagGrid) blocks = kDiagGrid;
   if (blocks == 0) blocks = 1;  // no cells: one workgroup writes the two zeros
-  hipLaunchKernelGGL(cell_diag_kernel<kDiagThreads>, dim3(blocks), dim3(kDiagThreads), 0, s, conteos,
+  launch(cell_diag_kernel<kDiagThreads>, dim3(blocks), dim3(kDiagThreads), 0, s, conteos,
                      static_cast<uint32_t>(cells), cap, diag, &sc->ticket[slot], &sc->part[slot][0]);
   return UGP_OK;
 }
@@ -447,10 +453,10 @@ void enqueue_stable_sort(const BuildArgs& a, const Plan& p, char* ws) {
     const uint32_t short_blocks = blocks_for(p.fix_cap, kSortBlock);  // 64 entries per wave
     const dim3 grid(long_blocks + ((short_blocks < kFixShortBlocks) ? short_blocks : kFixShortBlocks));
     if (p.move)
-      hipLaunchKernelGGL(fix_cells_kernel<true>, grid, dim3(kSortBlock), 0, a.stream, a.inicios, a.celdaDe,
+      launch(fix_cells_kernel<true>, grid, dim3(kSortBlock), 0, a.stream, a.inicios, a.celdaDe,
                          static_cast<uint32_t>(p.cells), a.n, fl, long_blocks, a.ordenado, parts, out);
     else
-      hipLaunchKernelGGL(fix_cells_kernel<false>, grid, dim3(kSortBlock), 0, a.stream, a.inicios, a.celdaDe,
+      launch(fix_cells_kernel<false>, grid, dim3(kSortBlock), 0, a.stream, a.inicios, a.celdaDe,
                          static_cast<uint32_t>(p.cells), a.n, fl, long_blocks, a.ordenado, nullptr, nullptr);
     return;
   }
@@ -460,22 +466,22 @@ void enqueue_stable_sort(const BuildArgs& a, const Plan& p, char* ws) {
   launch_clear(long_count, 1, nullptr, 0, a.stream);
   const dim3 grid(blocks_for(cells, kBlock));
   if (p.move) {
-    hipLaunchKernelGGL(sort_short_cells_kernel<true>, grid, dim3(kBlock), 0, a.stream, a.inicios, cells, a.n,
+    launch(sort_short_cells_kernel<true>, grid, dim3(kBlock), 0, a.stream, a.inicios, cells, a.n,
                        a.ordenado, long_list, p.long_cap, long_count,
                        reinterpret_cast<const uint4*>(ws + p.off_unstable), out);
-    hipLaunchKernelGGL(sort_long_cells_kernel<true>, dim3(kSortGrid), dim3(kSortBlock), 0, a.stream,
+    launch(sort_long_cells_kernel<true>, dim3(kSortGrid), dim3(kSortBlock), 0, a.stream,
                        a.inicios, a.celdaDe, a.n, long_list, p.long_cap, long_count, a.ordenado, parts, out);
   } else {
-    hipLaunchKernelGGL(sort_short_cells_kernel<false>, grid, dim3(kBlock), 0, a.stream, a.inicios, cells, a.n,
+    launch(sort_short_cells_kernel<false>, grid, dim3(kBlock), 0, a.stream, a.inicios, cells, a.n,
                        a.ordenado, long_list, p.long_cap, long_count, nullptr, nullptr);
-    hipLaunchKernelGGL(sort_long_cells_kernel<false>, dim3(kSortGrid), dim3(kSortBlock), 0, a.stream,
+    launch(sort_long_cells_kernel<false>, dim3(kSortGrid), dim3(kSortBlock), 0, a.stream,
                        a.inicios, a.celdaDe, a.n, long_list, p.long_cap, long_count, a.ordenado, nullptr,
                        nullptr);
   }
 }
 
 void enqueue_gather(const BuildArgs& a) {
-  hipLaunchKernelGGL(gather_kernel, dim3(blocks_for(a.n, kBlock * kGatherItems / 2)), dim3(kBlock),
+  launch(gather_kernel, dim3(blocks_for(a.n, kBlock * kGatherItems / 2)), dim3(kBlock),
                      0, a.stream, a.ordenado, a.n, a.n, reinterpret_cast<const uint4*>(a.particles),
                      reinterpret_cast<uint4*>(a.reordered));
 }
@@ -551,12 +557,12 @@ void enqueue_staged(uint32_t stage, const BuildArgs& a, const Plan& p) {
   switch (stage) {
     case 0:
       if (p.chunk == kSmallChunk)
-        hipLaunchKernelGGL(staged_keys_kernel<kSmallChunkThreads>, dim3(p.nchunks), dim3(kSmallChunkThreads), 0,
+        launch(staged_keys_kernel<kSmallChunkThreads>, dim3(p.nchunks), dim3(kSmallChunkThreads), 0,
                            s, reinterpret_cast<const uint4*>(a.particles), a.n, grid_params(a), a.celdaDe, rows,
                            p.tile_shift, p.ntiles, chunk_rec, chunk_idx, a.diag, fix_lists_of(a, p).base,
                            tile_queue_of(a, p).base);
       else
-        hipLaunchKernelGGL(staged_keys_kernel<kChunkThreads>, dim3(p.nchunks), dim3(kChunkThreads), 0, s,
+        launch(staged_keys_kernel<kChunkThreads>, dim3(p.nchunks), dim3(kChunkThreads), 0, s,
                            reinterpret_cast<const uint4*>(a.particles), a.n, grid_params(a), a.celdaDe, rows,
                            p.tile_shift, p.ntiles, chunk_rec, chunk_idx, a.diag, fix_lists_of(a, p).base,
                            tile_queue_of(a, p).base);
@@ -585,17 +591,17 @@ void enqueue_bucketed(uint32_t stage, const BuildArgs& a, const Plan& p) {
   hipStream_t s = a.stream;
   switch (stage) {
     case 0:
-      hipLaunchKernelGGL(bucket_keys_kernel, dim3(p.nblk), dim3(kBucketThreads), 0, s,
+      launch(bucket_keys_kernel, dim3(p.nblk), dim3(kBucketThreads), 0, s,
                          reinterpret_cast<const uint4*>(a.particles), a.n, p.per_block, grid_params(a),
                          a.celdaDe, hist, p.tile_shift, p.ntiles, a.diag, fix_lists_of(a, p).base,
                          tile_queue_of(a, p).base);
       break;
     case 1:
-      hipLaunchKernelGGL(bucket_colscan_kernel, dim3(p.ntiles), dim3(kBlock), 0, s, hist, p.nblk,
+      launch(bucket_colscan_kernel, dim3(p.ntiles), dim3(kBlock), 0, s, hist, p.nblk,
                          p.ntiles, tile_total);
       break;
     case 2:
-      hipLaunchKernelGGL(bucket_records_kernel, dim3(p.nblk), dim3(kBucketThreads), 0, s,
+      launch(bucket_records_kernel, dim3(p.nblk), dim3(kBucketThreads), 0, s,
                          reinterpret_cast<const uint4*>(a.particles), a.celdaDe, a.n, p.per_block, hist,
                          tile_total, p.tile_shift, p.ntiles, tile_rec, tile_idx, rows);
       break;
@@ -625,20 +631,20 @@ int enqueue_direct(uint32_t stage, const BuildArgs& a, const Plan& p) {
       launch_clear(a.conteos, p.cells, tilesum, p.nbins + kCounterWords, s);
       break;
     case 1:
-      hipLaunchKernelGGL(count_kernel, pgrid, dim3(kBlock), 0, s,
+      launch(count_kernel, pgrid, dim3(kBlock), 0, s,
                          reinterpret_cast<const float4*>(a.particles), a.n, grid_params(a),
                          a.celdaDe, a.conteos, tilesum, p.bin_shift, p.nbins);
       break;
     case 2:
-      hipLaunchKernelGGL(scan_kernel, dim3(p.nbins), dim3(kBlock), 0, s, a.conteos, p.cells,
+      launch(scan_kernel, dim3(p.nbins), dim3(kBlock), 0, s, a.conteos, p.cells,
                          tilesum, p.bin_shift, a.inicios, cursor);
       break;
     case 3:
       if (!p.move)
-        hipLaunchKernelGGL(scatter_kernel<false>, pgrid, dim3(kBlock), 0, s, a.celdaDe, a.n, cells,
+        launch(scatter_kernel<false>, pgrid, dim3(kBlock), 0, s, a.celdaDe, a.n, cells,
                            cursor, a.ordenado, nullptr, nullptr);
       else
-        hipLaunchKernelGGL(scatter_kernel<true>, pgrid, dim3(kBlock), 0, s, a.celdaDe, a.n, cells,
+        launch(scatter_kernel<true>, pgrid, dim3(kBlock), 0, s, a.celdaDe, a.n, cells,
                            cursor, a.ordenado, reinterpret_cast<const uint4*>(a.particles),
                            record_dst(a, p));
       if (a.diag) {
@@ -683,6 +689,24 @@ int enqueue_stage(uint32_t stage, const BuildArgs& a, const Plan& p) {
     }
   }
   return hipGetLastError() == hipSuccess ? UGP_OK : UGP_ERR_HIP;
+}
+
+// Whether a stage slot of this plan is exactly one kernel launch (its
+// timing can then be the kernel's own start and end).
+bool single_kernel_stage(const Plan& p, uint32_t stage, bool diag) {
+  switch (p.path) {
+    case Path::kEmpty:
+      return false;
+    case Path::kSingle:
+      return stage == 3 || (stage == 4 && p.stable) || (stage == 5 && p.gather);
+    case Path::kStaged:
+      return stage == 0 || stage == 3 || (stage == 4 && p.stable) || (stage == 5 && p.gather);
+    case Path::kBucketed:
+      return stage <= 3 || (stage == 4 && p.stable) || (stage == 5 && p.gather);
+    case Path::kDirect:
+      return stage <= 2 || (stage == 3 && !diag) || (stage == 5 && p.gather);
+  }
+  return false;
 }
 
 BuildArgs make_args(const ugp_particle* particles, uint32_t n, const float origin[3],
@@ -827,6 +851,15 @@ int ugp_cell_diag(const uint32_t* conteos, uint32_t cells, uint32_t capacity, ui
   return hipGetLastError() == hipSuccess ? UGP_OK : UGP_ERR_HIP;
 }
 
+int ugp_cell_diag_timed(const uint32_t* conteos, uint32_t cells, uint32_t capacity, uint32_t* diag,
+                        void* stream, void* event_before, void* event_after) {
+  if (!event_before || !event_after) return UGP_ERR_ARG;
+  g_timed_launch = TimedLaunch{static_cast<hipEvent_t>(event_before), static_cast<hipEvent_t>(event_after)};
+  const int st = ugp_cell_diag(conteos, cells, capacity, diag, stream);
+  g_timed_launch = TimedLaunch{};  // disarmed also when the call failed before its launch
+  return st;
+}
+
 int ugp_neighbor_count(const ugp_particle* particles, uint32_t n, const float origin[3],
                        float cell_size, const uint32_t dims[3], const uint32_t* inicios,
                        const uint32_t* ordenado, float radius, uint32_t* counts, uint32_t flags,
@@ -858,16 +891,16 @@ int ugp_neighbor_count(const ugp_particle* particles, uint32_t n, const float or
   hipStream_t s = a.stream;
   const bool morton = (flags & UGP_FLAG_MORTON) != 0;
   if (ordenado && morton)
-    hipLaunchKernelGGL((neighbor_count_kernel<true, true>), grid, block, 0, s, pf, n, g, dims[1], dims[2],
+    launch((neighbor_count_kernel<true, true>), grid, block, 0, s, pf, n, g, dims[1], dims[2],
                        inicios, ordenado, r2, counts);
   else if (ordenado)
-    hipLaunchKernelGGL((neighbor_count_kernel<true, false>), grid, block, 0, s, pf, n, g, dims[1], dims[2],
+    launch((neighbor_count_kernel<true, false>), grid, block, 0, s, pf, n, g, dims[1], dims[2],
                        inicios, ordenado, r2, counts);
   else if (morton)
-    hipLaunchKernelGGL((neighbor_count_kernel<false, true>), grid, block, 0, s, pf, n, g, dims[1], dims[2],
+    launch((neighbor_count_kernel<false, true>), grid, block, 0, s, pf, n, g, dims[1], dims[2],
                        inicios, nullptr, r2, counts);
   else
-    hipLaunchKernelGGL((neighbor_count_kernel<false, false>), grid, block, 0, s, pf, n, g, dims[1], dims[2],
+    launch((neighbor_count_kernel<false, false>), grid, block, 0, s, pf, n, g, dims[1], dims[2],
                        inicios, nullptr, r2, counts);
   return hipGetLastError() == hipSuccess ? UGP_OK : UGP_ERR_HIP;
 }
@@ -884,15 +917,26 @@ int ugp_grid_build_timed(const ugp_particle* particles, uint32_t n, const float 
   Plan p;
   int st = validate(a, &p);
   if (st != UGP_OK) return st;
+  hipEvent_t ev0 = static_cast<hipEvent_t>(event_before), ev1 = static_cast<hipEvent_t>(event_after);
+  const bool one_kernel = single_kernel_stage(p, timed_stage, false);
   for (uint32_t stage = 0; stage < UGP_NUM_STAGES; ++stage) {
-    if (stage == timed_stage &&
-        hipEventRecord(static_cast<hipEvent_t>(event_before), a.stream) != hipSuccess)
-      return UGP_ERR_HIP;
+    const bool timed = stage == timed_stage;
+    if (timed) {
+      if (one_kernel) {
+        g_timed_launch = TimedLaunch{ev0, ev1};  // the stage's kernel records them itself
+      } else if (hipEventRecord(ev0, a.stream) != hipSuccess) {
+        return UGP_ERR_HIP;
+      }
+    }
     st = enqueue_stage(stage, a, p);
+    if (timed && one_kernel && g_timed_launch.start != nullptr) {
+      // no kernel took the events (a stage that enqueued nothing): record an empty interval
+      g_timed_launch = TimedLaunch{};
+      if (st == UGP_OK && (hipEventRecord(ev0, a.stream) != hipSuccess || hipEventRecord(ev1, a.stream) != hipSuccess))
+        return UGP_ERR_HIP;
+    }
     if (st != UGP_OK) return st;
-    if (stage == timed_stage &&
-        hipEventRecord(static_cast<hipEvent_t>(event_after), a.stream) != hipSuccess)
-      return UGP_ERR_HIP;
+    if (timed && !one_kernel && hipEventRecord(ev1, a.stream) != hipSuccess) return UGP_ERR_HIP;
   }
   return UGP_OK;
 }
@@ -929,9 +973,9 @@ int ugp_exclusive_scan_u32(const uint32_t* in, uint32_t count, uint32_t* out, vo
   const uint32_t shift = (lg > kMinBinShift + 9) ? lg - 9 : kMinBinShift;
   const uint32_t nbins =
       static_cast<uint32_t>((static_cast<uint64_t>(count) + (1ull << shift) - 1) >> shift);
-  hipLaunchKernelGGL(tile_reduce_kernel, dim3(nbins), dim3(kBlock), 0, s, in,
+  launch(tile_reduce_kernel, dim3(nbins), dim3(kBlock), 0, s, in,
                      static_cast<uint64_t>(count), shift, tilesum);
-  hipLaunchKernelGGL(scan_kernel, dim3(nbins), dim3(kBlock), 0, s, in, static_cast<uint64_t>(count),
+  launch(scan_kernel, dim3(nbins), dim3(kBlock), 0, s, in, static_cast<uint64_t>(count),
                      tilesum, shift, out, nullptr);
   return hipGetLastError() == hipSuccess ? UGP_OK : UGP_ERR_HIP;
 }
@@ -984,9 +1028,9 @@ int ugp_reorder_arrays(const uint32_t* idx, uint32_t n, uint32_t n_src, const ug
   const dim3 grid(blocks_for(n, static_cast<uint64_t>(per) * kArrayItems));
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (vec16)
-    hipLaunchKernelGGL(gather_arrays_kernel<uint4>, grid, dim3(kBlock), 0, s, idx, n, n_src, set);
+    launch(gather_arrays_kernel<uint4>, grid, dim3(kBlock), 0, s, idx, n, n_src, set);
   else
-    hipLaunchKernelGGL(gather_arrays_kernel<uint32_t>, grid, dim3(kBlock), 0, s, idx, n, n_src, set);
+    launch(gather_arrays_kernel<uint32_t>, grid, dim3(kBlock), 0, s, idx, n, n_src, set);
   return hipGetLastError() == hipSuccess ? UGP_OK : UGP_ERR_HIP;
 }
 
@@ -1000,7 +1044,7 @@ int ugp_reorder(const ugp_particle* src, uint32_t n_src, const uint32_t* idx, ui
   const Span sd = span_of(dst, 32ull * n);
   if (overlap(ss, sd) || overlap(si, sd)) return UGP_ERR_ALIAS;
   if (n_src == 0) return UGP_OK;  // every index is out of range: nothing to write
-  hipLaunchKernelGGL(gather_kernel, dim3(blocks_for(n, kBlock * kGatherItems / 2)), dim3(kBlock), 0,
+  launch(gather_kernel, dim3(blocks_for(n, kBlock * kGatherItems / 2)), dim3(kBlock), 0,
                      static_cast<hipStream_t>(stream), idx, n, n_src,
                      reinterpret_cast<const uint4*>(src), reinterpret_cast<uint4*>(dst));
   return hipGetLastError() == hipSuccess ? UGP_OK : UGP_ERR_HIP;
