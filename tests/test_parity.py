@@ -221,6 +221,7 @@ def test_dense_grids(ugp, orc, d):
     (2_500_000, (160, 150, 140)),       # non-cubic, ragged last tile
     (5_000, (512, 512, 64)),            # sparse: 2^24 cells, 1024 tiles of 16384 cells
     (1_000, (1024, 1024, 64)),          # 2^26 keys, the largest the path takes
+    ((1 << 24) + 4097, (256, 256, 256)),  # 65536 particles per block at most: 257 blocks, a short last one
 ])
 def test_bucketed_path_shapes(ugp, orc, n, dims):
     """More particles than the staged path takes, or more cells: keys,

@@ -231,6 +231,9 @@ int make_plan(uint32_t n, const uint32_t dims[3], uint32_t flags, Plan* p) {
     const uint64_t step = static_cast<uint64_t>(kBucketThreads) * kBucketBatch;
     uint64_t per = (n + kBucketBlocks - 1) / kBucketBlocks;
     per = (per + step - 1) / step * step;
+    if (per > kBucketMaxPerBlock) per = kBucketMaxPerBlock;  // more blocks instead
+    static_assert(kBucketMaxPerBlock % (static_cast<uint64_t>(kBucketThreads) * kBucketBatch) == 0,
+                  "a whole number of batches per block");
     p->per_block = static_cast<uint32_t>(per);
     p->nblk = blocks_for(n, per);
     p->nchunks = 1;  // the tile kernel sees each tile as one contiguous run
@@ -597,7 +600,7 @@ void enqueue_bucketed(uint32_t stage, const BuildArgs& a, const Plan& p) {
                          tile_queue_of(a, p).base);
       break;
     case 1:
-      launch(bucket_colscan_kernel, dim3(p.ntiles), dim3(kBlock), 0, s, hist, p.nblk,
+      launch(bucket_colscan_kernel, dim3(blocks_for(p.ntiles, 64)), dim3(kScanWaves * 64), 0, s, hist, p.nblk,
                          p.ntiles, tile_total);
       break;
     case 2:
