@@ -53,9 +53,8 @@ WORKLOAD_NAMES = {
 def alg_bytes(n: int, c: int, mode: str) -> dict:
     """Bytes each kernel must move by design, each logical array counted once
     per kernel that touches it (32 B per record, 4 B per u32). The small
-    block x tile matrix of the bucketed path is left out; tile_scan moves
-    only that matrix and gets no figure, nor does the stable fix-up, whose
-    work depends on the input.
+    row-block x tile matrices of the bucketed path are left out, and so is
+    the stable fix-up, whose work depends on the input.
 
     The end-to-end figure uses the fixed model of the four page steps
     instead: 116 N + 16 C + 4 (see hbm_frac_e2e)."""
@@ -65,9 +64,9 @@ def alg_bytes(n: int, c: int, mode: str) -> dict:
         "chunk_sort": 72 * n,  # record read, celdaDe, chunk records + indices written
         "tile_sort": (36 * n + 4 * c + 4 * (c + 1) + 4 * n + (32 * n if move else 0)),
         # bucketed path (more particles or keys; tile_sort as above)
-        "keys": 36 * n,  # record read + celdaDe write
-        "tile_scan": None,
-        "bucket": 72 * n,  # record + celdaDe read, record + index written in tile order
+        "coarse_sort": 72 * n,  # as chunk_sort, by bucket
+        "tile_scan": 4 * n,  # the packed index words read (count per tile)
+        "rebucket": 72 * n,  # chunk records + indices read, written in tile order
         # direct path (larger grids)
         "clear": 4 * c,
         "count": 36 * n,
@@ -242,7 +241,7 @@ def summarize_counters(fetch_csv: str, write_csv: str, copy_bytes: int = 256 << 
 # kernel symbol -> stage name, for the traffic file
 KERNEL_STAGE = {
     "staged_keys_kernel": "chunk_sort", "staged_cells_kernel": "tile_sort",
-    "bucket_keys_kernel": "keys", "bucket_colscan_kernel": "tile_scan", "bucket_records_kernel": "bucket",
+    "bucket_fine_count_kernel": "tile_scan", "bucket_colscan_kernel": "tile_scan", "bucket_rebucket_kernel": "rebucket",
     "clear_kernel": "clear", "count_kernel": "count", "scan_kernel": "scan",
     "scatter_kernel": "scatter", "gather_kernel": "gather", "fix_cells_kernel": "stable_sort",
 }
@@ -256,12 +255,24 @@ def write_traffic_file(traffic: dict, path: str, command: str) -> None:
         f.write(f"source_sha256_16: {source_digest()}\n")
         # per stage, the most-dispatched variant (the headline's; the
         # diagnostic and Morton variants run a few times beside it)
+        # variant of each kernel; a stage of two kernels sums them. The
+        # chunk kernel is the bucketed path's coarse_sort when bucket
+        # kernels ran beside it
+        bucketed = any(k.startswith("bucket_") for k in traffic)
         best = {}
         for k, (b, dispatches) in traffic.items():
-            stage = KERNEL_STAGE.get(k.split("<")[0])
-            if stage is not None and (stage not in best or dispatches > best[stage][1]):
-                best[stage] = (b, dispatches)
-        for stage, (b, _) in best.items():
+            base = k.split("<")[0]
+            if base not in KERNEL_STAGE:
+                continue
+            if base not in best or dispatches > best[base][1]:
+                best[base] = (b, dispatches)
+        per_stage = {}
+        for base, (b, _) in best.items():
+            stage = KERNEL_STAGE[base]
+            if stage == "chunk_sort" and bucketed:
+                stage = "coarse_sort"
+            per_stage[stage] = per_stage.get(stage, 0.0) + b
+        for stage, b in per_stage.items():
             f.write(f"{stage}_bytes_per_dispatch: {b:.0f}\n")
 
 

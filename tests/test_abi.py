@@ -97,14 +97,14 @@ def test_stage_names(lib):
     assert ugp.stage_names(8193, (16, 16, 16))[0] == "chunk_sort"
     assert ugp.stage_names(8192, (129, 1, 128))[0] == "chunk_sort"
     assert ugp.stage_names(1, (1, 1, 1), ugp.FLAG_STABLE)[3:5] == ["tile_sort", "stable_sort"]
-    assert ugp.stage_names(3_000_000, (128, 128, 128)) == ["keys", "tile_scan", "bucket", "tile_sort", None, None]
+    assert ugp.stage_names(3_000_000, (128, 128, 128)) == ["coarse_sort", "tile_scan", "rebucket", "tile_sort", None, None]
     assert ugp.stage_names(1000, (128, 128, 128), ugp.FLAG_STABLE)[4:] == ["stable_sort", None]
     assert ugp.stage_names(1000, (128, 128, 128), ugp.FLAG_STABLE | ugp.FLAG_GATHER)[4:] == ["stable_sort", None]
     assert ugp.stage_names(1000, (128, 128, 128), ugp.FLAG_GATHER)[4:] == [None, "gather"]
     assert ugp.stage_names(0, (128, 128, 128)) == ["clear", None, None, None, None, None]
     assert ugp.stage_names(1000, (8192, 8193, 1))[:4] == ["clear", "count", "scan", "scatter"]
-    assert ugp.stage_names(1000, (256, 256, 256))[:4] == ["keys", "tile_scan", "bucket", "tile_sort"]
-    assert ugp.stage_names(1000, (1024, 1024, 64))[:4] == ["keys", "tile_scan", "bucket", "tile_sort"]  # 2^26 keys
+    assert ugp.stage_names(1000, (256, 256, 256))[:4] == ["coarse_sort", "tile_scan", "rebucket", "tile_sort"]
+    assert ugp.stage_names(1000, (1024, 1024, 64))[:4] == ["coarse_sort", "tile_scan", "rebucket", "tile_sort"]  # 2^26 keys
     assert ugp.stage_names(1000, (1024, 1024, 65))[:4] == ["clear", "count", "scan", "scatter"]
 
 

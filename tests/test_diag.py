@@ -69,7 +69,7 @@ def test_diag_large_tiled_path(ugp, orc):
     """16,777,216 particles on 256^3: the bucketed path (diagnostics folded into its tile kernel)."""
     print("[diag] large", flush=True)
     wl = W.make_config("large")
-    assert ugp.stage_names(wl.n, wl.dims.tolist())[0] == "keys"
+    assert ugp.stage_names(wl.n, wl.dims.tolist())[0] == "coarse_sort"
     ref = orc.grid_build(wl.particles, wl.origin, wl.cell_size, wl.dims)
     got, d = run_diag(ugp, wl, 3)
     assert_parity(wl, got, ref, "atomic")

@@ -75,7 +75,7 @@ def test_morton_configs(ugp, orc, name, mode):
 def test_morton_large_tiled_path(ugp, orc):
     print("[morton] large", flush=True)
     wl = W.make_config("large")
-    assert ugp.stage_names(wl.n, wl.dims.tolist(), ugp.FLAG_MORTON)[0] == "keys"
+    assert ugp.stage_names(wl.n, wl.dims.tolist(), ugp.FLAG_MORTON)[0] == "coarse_sort"
     assert_morton_parity(orc, ugp, wl, "atomic")
 
 

@@ -225,9 +225,9 @@ def test_dense_grids(ugp, orc, d):
 ])
 def test_bucketed_path_shapes(ugp, orc, n, dims):
     """More particles than the staged path takes, or more cells: keys,
-    tile_scan, bucket, tile_sort."""
+    tile_scan, rebucket, tile_sort."""
     print(f"[parity] bucketed n={n} dims={dims}", flush=True)
-    assert ugp.stage_names(n, dims)[:4] == ["keys", "tile_scan", "bucket", "tile_sort"]
+    assert ugp.stage_names(n, dims)[:4] == ["coarse_sort", "tile_scan", "rebucket", "tile_sort"]
     rng = np.random.Generator(np.random.PCG64(n))
     parts = rng.standard_normal((n, 8)).astype(np.float32)
     ext = np.asarray(dims, np.float64) * 0.5
@@ -244,7 +244,7 @@ def test_bucketed_one_cell_holds_everything(ugp, orc):
     n = 2_500_000
     parts = np.random.Generator(np.random.PCG64(77)).standard_normal((n, 8)).astype(np.float32)
     wl = W.Workload("one_cell", parts, np.zeros(3, np.float32), np.float32(1.0), np.array([1, 1, 1], np.uint32))
-    assert ugp.stage_names(n, [1, 1, 1])[0] == "keys"
+    assert ugp.stage_names(n, [1, 1, 1])[0] == "coarse_sort"
     ref = orc.grid_build(wl.particles, wl.origin, wl.cell_size, wl.dims)
     assert_parity(wl, run_gpu(ugp, wl, "atomic"), ref, "atomic")
 
@@ -341,7 +341,7 @@ def test_stable_long_cells_wide_index_range(ugp, orc, dims):
     path (2.3M particles) and on the direct path (more than 2^26 cells)."""
     n = 2_300_000
     print(f"[parity] wide long cells n={n} dims={dims}", flush=True)
-    assert ugp.stage_names(n, list(dims))[0] == ("keys" if dims[0] == 128 else "clear")
+    assert ugp.stage_names(n, list(dims))[0] == ("coarse_sort" if dims[0] == 128 else "clear")
     rng = np.random.Generator(np.random.PCG64(2300))
     parts = rng.standard_normal((n, 8)).astype(np.float32)
     h = 0.5

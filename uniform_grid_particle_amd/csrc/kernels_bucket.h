@@ -1,212 +1,238 @@
 // kernels_bucket.h -- the index build for more particles than the staged
-// path takes (n > 2^21) or more cells (keys up to 2^26): four kernels, no
-// global atomics, every record moved with coalesced-by-tile stores.
+// path takes (n > 2^21) or more cells (keys up to 2^26). Every record moves
+// in runs: writing a 32-byte record at a time to scattered places costs
+// about three times what whole 128-byte lines cost on MI355X (measured:
+// 2^24 records, 790 us scattered one by one, 276 us as randomly placed
+// whole lines, 261 us copied), so no pass here scatters single records.
 //
-// A tile is 2^shift consecutive cell keys (16 to 16384 cells, up to 4096
-// tiles, sized so a tile holds about 4096 particles on average).
+// A tile is 2^shift consecutive cell keys (fine tiles, up to 4096, sized so
+// a tile holds about 4096 particles on average, as on the staged path); a
+// bucket is up to 64 consecutive tiles (2^cshift keys, at most 64 buckets).
 //
-//   keys       one workgroup per block of particles (at most 256 blocks):
-//              cell key per particle (celdaDe) and an LDS histogram over
-//              the tiles, stored as one row of a [blocks x tiles] matrix.
-//   tile_scan  one workgroup per 64 tiles: exclusive scan of each column
-//              over the blocks, in place, and the tile totals.
-//   bucket     the same blocks again: tile starts (scan of the totals) plus
-//              the block's column give an LDS cursor per tile; each
-//              particle takes a slot with an LDS atomic and its record is
-//              written there, so every tile's particles end up contiguous;
-//              the indices follow at the end, run by run, from an inverse
-//              map in LDS. Block 0 also writes one row {count, start} per
-//              tile.
-//   tile_sort  the staged tile kernel (kernels_staged.h) with one "chunk"
-//              per tile: the tile's particles are one contiguous run at its
-//              start, so no chunk rows and no source map are needed.
+//   coarse_sort  the staged path's chunk kernel (kernels_staged.h) with
+//                buckets for tiles: cell key per particle (celdaDe), each
+//                2048-particle chunk counting-sorted by bucket in LDS and
+//                written back contiguously, one row {count, prefix} per
+//                (chunk, bucket). A chunk's run of one bucket averages
+//                2048 / 64 = 32 records.
+//   tile_scan    fine_count: one workgroup per (row block of kRbChunks
+//                chunks, bucket) counts the block's runs of that bucket per
+//                tile, from the packed index words alone; then the column
+//                scan of that [row block x tile] matrix (exclusive, in
+//                place), the tile totals and per-64-tile group totals.
+//   rebucket     the same workgroups again: each moves its runs in rounds
+//                of up to kRbRound particles, sorts a round by tile in LDS
+//                and writes every tile's group contiguously at the tile's
+//                start plus the row block's offset in it, so the tiles end
+//                up contiguous (about 32 records per group). Row block 0
+//                also writes one row {count, start} per tile.
+//   tile_sort    the staged tile kernel with one contiguous run per tile
+//                (kernels_staged.h), as on the staged path's last step.
 //
-// Against the pages' chain this reads the records twice (keys, bucket) and
-// the bucketed copy once; every access is coalesced or a run per (block,
-// tile), where the pages' scatter and gather touch a random record per
-// particle.
+// Against the pages' chain this moves the records three times (into
+// buckets, into tiles, into cells) where the pages scatter and gather one
+// record per particle; every one of these moves is a run.
 #pragma once
 
 #include "common.h"
+#include "kernels_staged.h"
 
 namespace ugp {
 
-constexpr uint32_t kBucketMaxTiles = 4096;  // LDS bins (16 KiB) in keys and bucket
-constexpr uint32_t kBucketBlocks = 256;     // blocks sought: the matrix stays small
-constexpr uint32_t kBucketMaxPerBlock = 1u << 16;  // particles per block at most (16-bit offsets in LDS)
-constexpr int kBucketThreads = 1024;        // threads per block
-constexpr int kBucketBatch = 4;             // particles per thread in flight
+constexpr uint32_t kBucketMaxTiles = 4096;  // tiles at most
+constexpr uint32_t kMaxBuckets = 64;        // buckets at most (coarse_sort LDS bins: <= kStagedMaxTiles)
+constexpr uint32_t kMaxFine = 64;           // tiles per bucket at most
+constexpr uint32_t kRbChunks = 64;          // chunks per row block
+constexpr int kRbThreads = 256;             // fine_count and rebucket workgroups
+constexpr uint32_t kRbRound = 2048;         // particles a rebucket round stages in LDS
+constexpr uint32_t kRbPer = kRbRound / kRbThreads;  // particles per thread in a round
+static_assert(kRbChunks <= 64, "a row block's run table is one wave wide");
+static_assert(kMaxFine <= 64, "a bucket's tiles are one wave wide");
 
-// keys: particles [blockIdx.x * per_block, ...) of n. diag, fix_counts,
-// queue_hdr (or nullptr): the two overflow-diagnostic words, the two stable
-// fix-up list lengths and the shared-round counters, zeroed here for the
-// tile kernel.
-__global__ __launch_bounds__(kBucketThreads) void bucket_keys_kernel(
-    const uint4* __restrict__ parts, uint32_t n, uint32_t per_block, GridParams g,
-    uint32_t* __restrict__ celdaDe, uint32_t* __restrict__ hist, uint32_t tile_shift,
-    uint32_t ntiles, uint32_t* __restrict__ diag, uint32_t* __restrict__ fix_counts,
-    uint32_t* __restrict__ queue_hdr) {
-  __shared__ uint32_t s_hist[kBucketMaxTiles];
-  for (uint32_t t = threadIdx.x; t < ntiles; t += kBucketThreads) s_hist[t] = 0u;
-  if (diag != nullptr && blockIdx.x == 0 && threadIdx.x < 2) diag[threadIdx.x] = 0u;
-  if (fix_counts != nullptr && blockIdx.x == 0 && threadIdx.x < 2) fix_counts[threadIdx.x] = 0u;
-  if (queue_hdr != nullptr && blockIdx.x == 0)  // shared rounds: claimed slots and ready flags
-    for (uint32_t j = threadIdx.x; j < kQueueHeader; j += kBucketThreads) queue_hdr[j] = 0u;
-  __syncthreads();
-  const uint64_t base = static_cast<uint64_t>(blockIdx.x) * per_block;
-  const uint64_t end = (base + per_block < n) ? base + per_block : n;
-  for (uint64_t i0 = base; i0 < end; i0 += static_cast<uint64_t>(kBucketThreads) * kBucketBatch) {
-    float x[kBucketBatch], y[kBucketBatch], z[kBucketBatch];
-#pragma unroll
-    for (int j = 0; j < kBucketBatch; ++j) {  // unconditional loads, clamped index
-      const uint64_t i = i0 + static_cast<uint64_t>(j) * kBucketThreads + threadIdx.x;
-      const uint4 a = load_stream(parts + (i < end ? i : end - 1u) * 2u);
-      x[j] = __uint_as_float(a.x);
-      y[j] = __uint_as_float(a.y);
-      z[j] = __uint_as_float(a.z);
-    }
-#pragma unroll
-    for (int j = 0; j < kBucketBatch; ++j) {
-      const uint64_t i = i0 + static_cast<uint64_t>(j) * kBucketThreads + threadIdx.x;
-      if (i < end) {
-        const uint32_t c = cell_of(x[j], y[j], z[j], g);
-        celdaDe[i] = c;
-        atomicAdd(&s_hist[c >> tile_shift], 1u);
-      }
-    }
+// The run table of row block rb for bucket B: chunks [rb*kRbChunks, ...)
+// of the coarse chunk array, s_pre[k] = particles of the runs before chunk
+// k of the block, s_src[k] = where chunk k's run starts; returns the block's
+// total for the bucket. rows1 holds the coarse rows [chunk x nbuckets].
+// Wave 0 does it (one lane per chunk); the caller's barrier follows.
+__device__ __forceinline__ void bucket_run_table(const uint2* __restrict__ rows1, uint32_t nchunks,
+                                                 uint32_t nbuckets, uint32_t rb, uint32_t B,
+                                                 uint32_t* s_pre, uint32_t* s_src, uint32_t* s_total) {
+  if (threadIdx.x >= 64) return;
+  const uint32_t lane = threadIdx.x;
+  const uint32_t c = rb * kRbChunks + lane;
+  uint2 r = make_uint2(0u, 0u);
+  if (lane < kRbChunks && c < nchunks) r = rows1[static_cast<size_t>(c) * nbuckets + B];
+  const uint32_t incl = wave_inclusive_sum(r.x);
+  if (lane < kRbChunks) {
+    s_pre[lane] = incl - r.x;
+    s_src[lane] = c * kChunk + r.y;
   }
-  __syncthreads();
-  uint32_t* row = hist + static_cast<size_t>(blockIdx.x) * ntiles;
-  for (uint32_t t = threadIdx.x; t < ntiles; t += kBucketThreads) row[t] = s_hist[t];
+  if (lane == 63) *s_total = incl;
 }
 
-// bucket: the same blocks as keys; hist holds the column-scanned matrix and
-// tile_total the tile totals. Writes tile_rec/tile_idx in tile order and
-// (block 0) rows[t] = {tile_total[t], start of tile t}.
-//
-// Records go out as they are placed (32 bytes each, whole 32-byte sectors).
-// Indices would go out 4 bytes at a time into the ~16-word run of each
-// (block, tile), the run's line filled over the whole pass and written back
-// piecemeal; so the block keeps an inverse map in LDS instead (local
-// position in tile order -> particle offset in the block, 16 bits) and
-// writes every run of indices at the end, consecutive lanes to consecutive
-// words. Local positions: the block's own counts (the difference of its row
-// and the next in the scanned matrix) scanned over the tiles; tile t's
-// local range [lbase_t, lbase_t + count) maps onto its slots
-// [start_t + col_t, ...) by the offset s_d[t].
-//
-// Every lane of a wave reaches the lane exchange below (no early exit), as
-// the shuffles need. per_block <= kBucketMaxPerBlock.
-__global__ __launch_bounds__(kBucketThreads) void bucket_records_kernel(
-    const uint4* __restrict__ parts, const uint32_t* __restrict__ celdaDe, uint32_t n,
-    uint32_t per_block, const uint32_t* __restrict__ hist, const uint32_t* __restrict__ tile_total,
-    uint32_t tile_shift, uint32_t ntiles, uint4* __restrict__ tile_rec,
-    uint32_t* __restrict__ tile_idx, uint2* __restrict__ rows) {
-  constexpr uint32_t kPer = kBucketMaxTiles / kBucketThreads;  // tiles per thread in the scans
-  // 160 KiB: per tile a local cursor and a slot offset, then the inverse map
-  // (whose first words also serve the scans before the map is written)
-  __shared__ uint32_t s_lds[2 * kBucketMaxTiles + kBucketMaxPerBlock / 2];
-  uint32_t* s_loc = s_lds;
-  uint32_t* s_d = s_lds + kBucketMaxTiles;
-  uint16_t* s_inv = reinterpret_cast<uint16_t*>(s_lds + 2 * kBucketMaxTiles);
-  uint32_t* s_wave = s_lds + 2 * kBucketMaxTiles;
+// The chunk of the block holding the block's p-th particle of the bucket
+// (the last chunk whose runs start at or before p; runs in chunk order).
+__device__ __forceinline__ uint32_t bucket_run_of(const uint32_t* s_pre, uint32_t p) {
+  uint32_t k = 0;
+#pragma unroll
+  for (uint32_t step = kRbChunks / 2; step != 0u; step >>= 1)
+    if (s_pre[k + step] <= p) k += step;
+  return k;
+}
 
-  const uint32_t* col = hist + static_cast<size_t>(blockIdx.x) * ntiles;
-  const uint32_t* next = (blockIdx.x + 1u == gridDim.x) ? tile_total : col + ntiles;
-  uint32_t tot[kPer], cnt[kPer], c0[kPer];
-  uint32_t sum = 0, lsum = 0;
-#pragma unroll
-  for (uint32_t q = 0; q < kPer; ++q) {
-    const uint32_t t = threadIdx.x * kPer + q;
-    tot[q] = (t < ntiles) ? tile_total[t] : 0u;
-    c0[q] = (t < ntiles) ? col[t] : 0u;
-    cnt[q] = (t < ntiles) ? next[t] - c0[q] : 0u;
-    sum += tot[q];
-    lsum += cnt[q];
-  }
-  uint32_t all;
-  uint32_t start = block_exclusive_sum<kBucketThreads>(sum, s_wave, &all);
-  uint32_t lbase = block_exclusive_sum<kBucketThreads>(lsum, s_wave, &all);
-#pragma unroll
-  for (uint32_t q = 0; q < kPer; ++q) {
-    const uint32_t t = threadIdx.x * kPer + q;
-    if (t < ntiles) {
-      s_loc[t] = lbase;
-      s_d[t] = start + c0[q] - lbase;  // modulo 2^32: slot = local + s_d
-      if (blockIdx.x == 0) rows[t] = make_uint2(tot[q], start);
-    }
-    start += tot[q];
-    lbase += cnt[q];
-  }
+// fine_count: workgroup (rb, B) = (blockIdx.x, blockIdx.y) counts its runs
+// per tile into hist[rb * ntiles + B * fpb + f] (f < fpb tiles in the
+// bucket), from the packed index words (bucket-local cell << kIdxBits).
+__global__ __launch_bounds__(kRbThreads) void bucket_fine_count_kernel(
+    const uint2* __restrict__ rows1, uint32_t nchunks, uint32_t nbuckets,
+    const uint32_t* __restrict__ chunk_idx, uint32_t tile_shift, uint32_t fpb, uint32_t ntiles,
+    uint32_t* __restrict__ hist) {
+  __shared__ uint32_t s_pre[kRbChunks], s_src[kRbChunks], s_total;
+  __shared__ uint32_t s_h[kMaxFine];
+  const uint32_t rb = blockIdx.x, B = blockIdx.y;
+  if (threadIdx.x < kMaxFine) s_h[threadIdx.x] = 0u;
+  bucket_run_table(rows1, nchunks, nbuckets, rb, B, s_pre, s_src, &s_total);
   __syncthreads();
-  const uint64_t base = static_cast<uint64_t>(blockIdx.x) * per_block;
-  const uint64_t end = (base + per_block < n) ? base + per_block : n;
-  for (uint64_t i0 = base; i0 < end; i0 += static_cast<uint64_t>(kBucketThreads) * kBucketBatch) {
-    uint32_t w[8][kBucketBatch], c[kBucketBatch];
+  const uint32_t total = s_total;
+  constexpr uint32_t kBatch = 8;  // index words per thread in flight
+  for (uint32_t p0 = 0; p0 < total; p0 += kRbThreads * kBatch) {
+    uint32_t word[kBatch];
 #pragma unroll
-    for (int j = 0; j < kBucketBatch; ++j) {
-      const uint64_t i = i0 + static_cast<uint64_t>(j) * kBucketThreads + threadIdx.x;
-      const uint64_t ic = (i < end) ? i : end - 1u;
-      const uint4 a = load_stream(parts + ic * 2u);
-      const uint4 b = load_stream(parts + ic * 2u + 1u);
-      c[j] = celdaDe[ic];
-      w[0][j] = a.x; w[1][j] = a.y; w[2][j] = a.z; w[3][j] = a.w;
-      w[4][j] = b.x; w[5][j] = b.y; w[6][j] = b.z; w[7][j] = b.w;
+    for (uint32_t k = 0; k < kBatch; ++k) {
+      const uint32_t p = p0 + k * kRbThreads + threadIdx.x;
+      word[k] = 0xFFFFFFFFu;
+      if (p < total) {
+        const uint32_t j = bucket_run_of(s_pre, p);
+        word[k] = chunk_idx[s_src[j] + (p - s_pre[j])];
+      }
     }
-    const uint32_t lane = threadIdx.x & 63u, half = lane & 1u;
 #pragma unroll
-    for (int j = 0; j < kBucketBatch; ++j) {
-      const uint64_t i = i0 + static_cast<uint64_t>(j) * kBucketThreads + threadIdx.x;
-      const uint32_t tile = c[j] >> tile_shift;
-      uint32_t slot = 0xFFFFFFFFu;  // none
-      if (i < end && tile < ntiles) {
-        const uint32_t local = atomicAdd(&s_loc[tile], 1u);
-        if (local < kBucketMaxPerBlock) s_inv[local] = static_cast<uint16_t>(i - base);
-        slot = local + s_d[tile];
-        if (slot >= n) slot = 0xFFFFFFFFu;
-      }
-      // the records go out with lanes 2m and 2m + 1 storing the two halves
-      // of one record (that of lane m, then of lane 32 + m): each store
-      // instruction touches 32 records instead of 64
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int src = h * 32 + static_cast<int>(lane >> 1);
-        const uint32_t to = static_cast<uint32_t>(__shfl(static_cast<int>(slot), src));
-        uint32_t v[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) v[q] = static_cast<uint32_t>(__shfl(static_cast<int>(w[q][j]), src));
-        const uint4 part = half ? make_uint4(v[4], v[5], v[6], v[7]) : make_uint4(v[0], v[1], v[2], v[3]);
-        if (to != 0xFFFFFFFFu) tile_rec[static_cast<size_t>(to) * 2u + half] = part;
-      }
+    for (uint32_t k = 0; k < kBatch; ++k) {
+      if (word[k] == 0xFFFFFFFFu) continue;
+      const uint32_t f = (word[k] >> kIdxBits) >> tile_shift;
+      if (f < fpb) atomicAdd(&s_h[f], 1u);
     }
   }
   __syncthreads();
-  // the index runs: s_loc[t] now ends tile t's local range, so the tile of
-  // local position q is the number of tiles whose range ends at or before q
-  const uint32_t count = static_cast<uint32_t>(end > base ? end - base : 0u);
-  for (uint32_t q = threadIdx.x; q < count; q += kBucketThreads) {
-    uint32_t t = 0;
+  if (threadIdx.x < fpb) {
+    const uint32_t t = B * fpb + threadIdx.x;
+    if (t < ntiles) hist[static_cast<size_t>(rb) * ntiles + t] = s_h[threadIdx.x];
+  }
+}
+
+// rebucket: workgroup (rb, B) moves the runs fine_count counted. hist holds
+// the column-scanned matrix, tile_total the tile totals, group_total the
+// sums of 64 consecutive tiles. Each tile's group of a round goes to
+// tile_rec/tile_idx at the tile's start plus this row block's offset in the
+// tile plus what earlier rounds put there; row block 0 writes
+// rows[t] = {tile_total[t], start of tile t}.
+__global__ __launch_bounds__(kRbThreads) void bucket_rebucket_kernel(
+    const uint2* __restrict__ rows1, uint32_t nchunks, uint32_t nbuckets,
+    const uint4* __restrict__ chunk_rec, const uint32_t* __restrict__ chunk_idx, uint32_t tile_shift,
+    uint32_t fpb, uint32_t ntiles, const uint32_t* __restrict__ hist,
+    const uint32_t* __restrict__ tile_total, const uint32_t* __restrict__ group_total, uint32_t n,
+    uint4* __restrict__ tile_rec, uint32_t* __restrict__ tile_idx, uint2* __restrict__ rows) {
+  __shared__ uint4 s_rec[2 * kRbRound];
+  __shared__ uint32_t s_id[kRbRound];
+  __shared__ uint8_t s_f[kRbRound];
+  __shared__ uint32_t s_pre[kRbChunks], s_src[kRbChunks], s_total;
+  __shared__ uint32_t s_cnt[kMaxFine], s_off[kMaxFine], s_cur[kMaxFine];
+  const uint32_t rb = blockIdx.x, B = blockIdx.y;
+  bucket_run_table(rows1, nchunks, nbuckets, rb, B, s_pre, s_src, &s_total);
+  if (threadIdx.x >= 64 && threadIdx.x < 128) {
+    // wave 1: the cursors. Start of the bucket's first tile t0 = the groups
+    // of 64 tiles before it plus the tiles of its own group before it; then
+    // each tile's start within the bucket
+    const uint32_t lane = threadIdx.x - 64;
+    const uint32_t t0 = B * fpb;
+    const uint32_t g0 = t0 / 64u;
+    uint32_t v = (lane < g0) ? group_total[lane] : 0u;
+    if (64u * g0 + lane < t0) v += tile_total[64u * g0 + lane];
+    const uint32_t bstart = wave_inclusive_sum(v);  // lane 63 holds the sum
+    const uint32_t base_all = static_cast<uint32_t>(__shfl(static_cast<int>(bstart), 63));
+    const uint32_t t = t0 + lane;
+    const uint32_t tot = (lane < fpb && t < ntiles) ? tile_total[t] : 0u;
+    const uint32_t start = base_all + wave_inclusive_sum(tot) - tot;
+    if (lane < fpb) {
+      s_cur[lane] = (t < ntiles) ? start + hist[static_cast<size_t>(rb) * ntiles + t] : 0u;
+      if (rb == 0 && t < ntiles) rows[t] = make_uint2(tot, start);
+    }
+  }
+  __syncthreads();
+  const uint32_t total = s_total;
+  for (uint32_t base = 0; base < total; base += kRbRound) {  // workgroup-uniform
+    const uint32_t len = (total - base < kRbRound) ? total - base : kRbRound;
+    if (threadIdx.x < kMaxFine) s_cnt[threadIdx.x] = 0u;
+    uint32_t w[8][kRbPer], id[kRbPer], fr[kRbPer], ft[kRbPer];
 #pragma unroll
-    for (uint32_t step = kBucketMaxTiles; step != 0u; step >>= 1) {
-      if (t + step <= ntiles && s_loc[t + step - 1u] <= q) t += step;
+    for (uint32_t k = 0; k < kRbPer; ++k) {
+      const uint32_t p = base + k * kRbThreads + threadIdx.x;
+      const uint32_t q = (p < base + len) ? p : base;  // clamped: loads below are unconditional
+      const uint32_t j = bucket_run_of(s_pre, q);
+      const uint32_t src = s_src[j] + (q - s_pre[j]);
+      const uint32_t word = chunk_idx[src];
+      const uint4 a = chunk_rec[static_cast<size_t>(src) * 2u];
+      const uint4 b = chunk_rec[static_cast<size_t>(src) * 2u + 1u];
+      w[0][k] = a.x; w[1][k] = a.y; w[2][k] = a.z; w[3][k] = a.w;
+      w[4][k] = b.x; w[5][k] = b.y; w[6][k] = b.z; w[7][k] = b.w;
+      // the particle: its chunk's first index plus the index inside the
+      // chunk; its tile in the bucket: the bucket-local cell's high bits
+      id[k] = (src & ~(kChunk - 1u)) + (word & ((1u << kIdxBits) - 1u));
+      ft[k] = (word >> kIdxBits) >> tile_shift;
     }
-    if (t < ntiles) {
-      const uint32_t slot = q + s_d[t];
-      if (slot < n) tile_idx[slot] = static_cast<uint32_t>(base) + s_inv[q];
+    __syncthreads();  // s_cnt zeroed; the previous round's LDS reads are done
+#pragma unroll
+    for (uint32_t k = 0; k < kRbPer; ++k) {
+      const uint32_t p = k * kRbThreads + threadIdx.x;
+      const uint32_t f = ft[k];
+      fr[k] = (p < len && f < fpb) ? (f << 16) | atomicAdd(&s_cnt[f], 1u) : 0xFFFFFFFFu;
     }
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      const uint32_t c = (threadIdx.x < kMaxFine) ? s_cnt[threadIdx.x] : 0u;
+      const uint32_t ex = wave_inclusive_sum(c) - c;
+      if (threadIdx.x < kMaxFine) s_off[threadIdx.x] = ex;
+    }
+    __syncthreads();
+#pragma unroll
+    for (uint32_t k = 0; k < kRbPer; ++k) {
+      if (fr[k] == 0xFFFFFFFFu) continue;
+      const uint32_t f = fr[k] >> 16;
+      const uint32_t o = s_off[f] + (fr[k] & 0xFFFFu);
+      s_rec[2 * o] = make_uint4(w[0][k], w[1][k], w[2][k], w[3][k]);
+      s_rec[2 * o + 1] = make_uint4(w[4][k], w[5][k], w[6][k], w[7][k]);
+      s_id[o] = id[k];
+      s_f[o] = static_cast<uint8_t>(f);
+    }
+    __syncthreads();
+    // every tile's group out contiguously: 16-byte halves, consecutive
+    // lanes on consecutive halves
+    for (uint32_t h = threadIdx.x; h < 2 * len; h += kRbThreads) {
+      const uint32_t o = h >> 1, f = s_f[o];
+      const uint32_t d = s_cur[f] + (o - s_off[f]);
+      if (d < n) tile_rec[static_cast<size_t>(d) * 2u + (h & 1u)] = s_rec[h];
+    }
+    for (uint32_t o = threadIdx.x; o < len; o += kRbThreads) {
+      const uint32_t f = s_f[o];
+      const uint32_t d = s_cur[f] + (o - s_off[f]);
+      if (d < n) tile_idx[d] = s_id[o];
+    }
+    __syncthreads();
+    if (threadIdx.x < kMaxFine) s_cur[threadIdx.x] += s_cnt[threadIdx.x];
   }
 }
 
 // tile_scan: workgroup g scans columns [64g, 64g + 64) of hist over the nblk
-// rows, in place (exclusive), and writes the column totals to tile_total.
-// Wave r of kScanWaves takes the rows [r*R, (r+1)*R), lane l column
+// rows, in place (exclusive), and writes the column totals to tile_total
+// and their sum to group_total[g]. Wave r of kScanWaves takes the rows [r*R, (r+1)*R), lane l column
 // 64g + l, so every load and store of a wave is 64 consecutive words of one
 // row; each lane keeps kScanUnroll loads in flight.
 constexpr int kScanWaves = 16;
 constexpr uint32_t kScanUnroll = 8;
 __global__ __launch_bounds__(kScanWaves * 64) void bucket_colscan_kernel(uint32_t* __restrict__ hist,
                                                                          uint32_t nblk, uint32_t ntiles,
-                                                                         uint32_t* __restrict__ tile_total) {
+                                                                         uint32_t* __restrict__ tile_total,
+                                                                         uint32_t* __restrict__ group_total) {
   __shared__ uint32_t s_part[kScanWaves][64];
   const uint32_t lane = threadIdx.x & 63u, r = threadIdx.x >> 6;
   const uint32_t t = blockIdx.x * 64u + lane;
@@ -246,6 +272,11 @@ __global__ __launch_bounds__(kScanWaves * 64) void bucket_colscan_kernel(uint32_
       }
     }
     if (r == 0) tile_total[t] = total;
+  }
+  // the group's sum (its 64 tiles) for the rebucket cursors
+  if (r == 0) {
+    const uint32_t g = wave_inclusive_sum(live ? total : 0u);
+    if (lane == 63) group_total[blockIdx.x] = g;
   }
 }
 

@@ -110,9 +110,13 @@ struct Plan {
   bool gather = false;  // a separate gather kernel moves the records
   bool move = true;     // the scatter kernel itself moves the records
   // tiled
-  uint32_t tile_shift = kStagedMinShift, ntiles = 1, nblk = 0, per_block = 0;
+  uint32_t tile_shift = kStagedMinShift, ntiles = 1;
   uint32_t chunk = kChunk;  // particles per chunk_sort workgroup (staged path)
-  size_t off_hist = 0, off_tile_total = 0;
+  // bucketed: coarse chunks and buckets (2^cshift keys), row blocks of
+  // kRbChunks coarse chunks, [row block x tile] counts, tile and group totals
+  uint32_t cshift = 0, nbuckets = 0, ncoarse = 0, nrb = 0;
+  size_t off_rows1 = 0, off_coarse_rec = 0, off_coarse_idx = 0;
+  size_t off_hist = 0, off_tile_total = 0, off_group_total = 0;
   // staged
   uint32_t nchunks = 0;
   size_t off_rows = 0, off_chunk_rec = 0, off_chunk_idx = 0;
@@ -228,19 +232,28 @@ int make_plan(uint32_t n, const uint32_t dims[3], uint32_t flags, Plan* p) {
     p->path = Path::kBucketed;
     p->tile_shift = bucket_shift(n, cells, lg);
     p->ntiles = static_cast<uint32_t>((cells + (1ull << p->tile_shift) - 1) >> p->tile_shift);
-    const uint64_t step = static_cast<uint64_t>(kBucketThreads) * kBucketBatch;
-    uint64_t per = (n + kBucketBlocks - 1) / kBucketBlocks;
-    per = (per + step - 1) / step * step;
-    if (per > kBucketMaxPerBlock) per = kBucketMaxPerBlock;  // more blocks instead
-    static_assert(kBucketMaxPerBlock % (static_cast<uint64_t>(kBucketThreads) * kBucketBatch) == 0,
-                  "a whole number of batches per block");
-    p->per_block = static_cast<uint32_t>(per);
-    p->nblk = blocks_for(n, per);
+    // buckets of 64 tiles: at most kMaxBuckets, and the bucket-local cell
+    // fits the packed index word beside the 11-bit index inside a chunk
+    p->cshift = p->tile_shift + 6u;
+    static_assert(kStagedMaxShift + 6u + kIdxBits <= 32u, "bucket-local cells fit the packed word");
+    static_assert(kBucketMaxTiles <= kMaxBuckets * 64u, "64 tiles per bucket cover every tile");
+    static_assert(kMaxBuckets <= kStagedMaxTiles, "buckets fit the chunk kernel's bins");
+    p->nbuckets = static_cast<uint32_t>((cells + (1ull << p->cshift) - 1) >> p->cshift);
+    p->ncoarse = blocks_for(n, kChunk);
+    p->nrb = blocks_for(p->ncoarse, kRbChunks);
     p->nchunks = 1;  // the tile kernel sees each tile as one contiguous run
+    p->off_rows1 = off;
+    off = align_up(off + static_cast<size_t>(p->ncoarse) * p->nbuckets * 8u, 256);
+    p->off_coarse_rec = off;
+    off = align_up(off + static_cast<size_t>(n) * 32u, 256);
+    p->off_coarse_idx = off;
+    off = align_up(off + static_cast<size_t>(n) * 4u, 256);
     p->off_hist = off;
-    off = align_up(off + static_cast<size_t>(p->nblk) * p->ntiles * 4u, 256);
+    off = align_up(off + static_cast<size_t>(p->nrb) * p->ntiles * 4u, 256);
     p->off_tile_total = off;
     off = align_up(off + static_cast<size_t>(p->ntiles) * 4u, 256);
+    p->off_group_total = off;
+    off = align_up(off + static_cast<size_t>(blocks_for(p->ntiles, 64)) * 4u, 256);
     p->off_rows = off;
     off = align_up(off + static_cast<size_t>(p->ntiles) * 8u, 256);
     p->off_chunk_rec = off;
@@ -283,7 +296,7 @@ int make_plan(uint32_t n, const uint32_t dims[3], uint32_t flags, Plan* p) {
 }
 
 const char* stage_name(const Plan& p, uint32_t stage) {
-  static const char* const kBucket[UGP_NUM_STAGES] = {"keys", "tile_scan", "bucket", "tile_sort",
+  static const char* const kBucket[UGP_NUM_STAGES] = {"coarse_sort", "tile_scan", "rebucket", "tile_sort",
                                                      "stable_sort", "gather"};
   static const char* const kDirect[UGP_NUM_STAGES] = {"clear", "count", "scan", "scatter",
                                                       "stable_sort", "gather"};
@@ -586,27 +599,34 @@ void enqueue_staged(uint32_t stage, const BuildArgs& a, const Plan& p) {
 
 void enqueue_bucketed(uint32_t stage, const BuildArgs& a, const Plan& p) {
   char* ws = static_cast<char*>(a.workspace);
+  uint2* rows1 = reinterpret_cast<uint2*>(ws + p.off_rows1);
+  uint4* coarse_rec = reinterpret_cast<uint4*>(ws + p.off_coarse_rec);
+  uint32_t* coarse_idx = reinterpret_cast<uint32_t*>(ws + p.off_coarse_idx);
   uint32_t* hist = reinterpret_cast<uint32_t*>(ws + p.off_hist);
   uint32_t* tile_total = reinterpret_cast<uint32_t*>(ws + p.off_tile_total);
+  uint32_t* group_total = reinterpret_cast<uint32_t*>(ws + p.off_group_total);
   uint2* rows = reinterpret_cast<uint2*>(ws + p.off_rows);
   uint4* tile_rec = reinterpret_cast<uint4*>(ws + p.off_chunk_rec);
   uint32_t* tile_idx = reinterpret_cast<uint32_t*>(ws + p.off_chunk_idx);
+  const uint32_t fpb = 1u << (p.cshift - p.tile_shift);
+  const dim3 rb_grid(p.nrb, p.nbuckets);
   hipStream_t s = a.stream;
   switch (stage) {
-    case 0:
-      launch(bucket_keys_kernel, dim3(p.nblk), dim3(kBucketThreads), 0, s,
-                         reinterpret_cast<const uint4*>(a.particles), a.n, p.per_block, grid_params(a),
-                         a.celdaDe, hist, p.tile_shift, p.ntiles, a.diag, fix_lists_of(a, p).base,
-                         tile_queue_of(a, p).base);
+    case 0:  // chunks sorted by bucket: the chunk kernel with buckets for tiles
+      launch(staged_keys_kernel<kChunkThreads>, dim3(p.ncoarse), dim3(kChunkThreads), 0, s,
+             reinterpret_cast<const uint4*>(a.particles), a.n, grid_params(a), a.celdaDe, rows1, p.cshift,
+             p.nbuckets, coarse_rec, coarse_idx, a.diag, fix_lists_of(a, p).base, tile_queue_of(a, p).base);
       break;
     case 1:
-      launch(bucket_colscan_kernel, dim3(blocks_for(p.ntiles, 64)), dim3(kScanWaves * 64), 0, s, hist, p.nblk,
-                         p.ntiles, tile_total);
+      launch(bucket_fine_count_kernel, rb_grid, dim3(kRbThreads), 0, s, rows1, p.ncoarse, p.nbuckets,
+             coarse_idx, p.tile_shift, fpb, p.ntiles, hist);
+      launch(bucket_colscan_kernel, dim3(blocks_for(p.ntiles, 64)), dim3(kScanWaves * 64), 0, s, hist, p.nrb,
+             p.ntiles, tile_total, group_total);
       break;
     case 2:
-      launch(bucket_records_kernel, dim3(p.nblk), dim3(kBucketThreads), 0, s,
-                         reinterpret_cast<const uint4*>(a.particles), a.celdaDe, a.n, p.per_block, hist,
-                         tile_total, p.tile_shift, p.ntiles, tile_rec, tile_idx, rows);
+      launch(bucket_rebucket_kernel, rb_grid, dim3(kRbThreads), 0, s, rows1, p.ncoarse, p.nbuckets, coarse_rec,
+             coarse_idx, p.tile_shift, fpb, p.ntiles, hist, tile_total, group_total, a.n, tile_rec, tile_idx,
+             rows);
       break;
     case 3:
       launch_tile_sort<false>(a, p, rows, tile_rec, tile_idx);
@@ -704,8 +724,8 @@ bool single_kernel_stage(const Plan& p, uint32_t stage, bool diag) {
       return stage == 3 || (stage == 4 && p.stable) || (stage == 5 && p.gather);
     case Path::kStaged:
       return stage == 0 || stage == 3 || (stage == 4 && p.stable) || (stage == 5 && p.gather);
-    case Path::kBucketed:
-      return stage <= 3 || (stage == 4 && p.stable) || (stage == 5 && p.gather);
+    case Path::kBucketed:  // slot 1 holds two kernels (count, column scan)
+      return stage == 0 || stage == 2 || stage == 3 || (stage == 4 && p.stable) || (stage == 5 && p.gather);
     case Path::kDirect:
       return stage <= 2 || (stage == 3 && !diag) || (stage == 5 && p.gather);
   }
