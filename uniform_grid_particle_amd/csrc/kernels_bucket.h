@@ -15,11 +15,11 @@
 //                written back contiguously, one row {count, prefix} per
 //                (chunk, bucket). A chunk's run of one bucket averages
 //                2048 / 64 = 32 records.
-//   tile_scan    fine_count: one workgroup per (row block of kRbChunks
-//                chunks, bucket) counts the block's runs of that bucket per
-//                tile, from the packed index words alone; then the column
-//                scan of that [row block x tile] matrix (exclusive, in
-//                place), the tile totals and per-64-tile group totals.
+//   tile_scan    fine_count: the cell keys (celdaDe) of every quarter row
+//                block (kRbChunks / 4 chunks of particles) counted per tile;
+//                then the column scan of that [quarter x tile] matrix
+//                (exclusive, in place), the tile totals and the sums of 64
+//                tiles (one bucket each).
 //   rebucket     the same workgroups again: each moves its runs in rounds
 //                of up to kRbRound particles, sorts a round by tile in LDS
 //                and writes every tile's group contiguously at the tile's
@@ -47,6 +47,7 @@ constexpr int kRbThreads = 256;             // fine_count and rebucket workgroup
 constexpr uint32_t kRbRound = 2048;         // particles a rebucket round stages in LDS
 constexpr uint32_t kRbPer = kRbRound / kRbThreads;  // particles per thread in a round
 static_assert(kRbChunks <= 64, "a row block's run table is one wave wide");
+constexpr uint32_t kRunTable = 64;  // run table entries (lanes past kRbChunks hold empty runs)
 static_assert(kMaxFine <= 64, "a bucket's tiles are one wave wide");
 
 // The run table of row block rb for bucket B: chunks [rb*kRbChunks, ...)
@@ -63,10 +64,8 @@ __device__ __forceinline__ void bucket_run_table(const uint2* __restrict__ rows1
   uint2 r = make_uint2(0u, 0u);
   if (lane < kRbChunks && c < nchunks) r = rows1[static_cast<size_t>(c) * nbuckets + B];
   const uint32_t incl = wave_inclusive_sum(r.x);
-  if (lane < kRbChunks) {
-    s_pre[lane] = incl - r.x;
-    s_src[lane] = c * kChunk + r.y;
-  }
+  s_pre[lane] = incl - r.x;
+  s_src[lane] = c * kChunk + r.y;
   if (lane == 63) *s_total = incl;
 }
 
@@ -75,69 +74,84 @@ __device__ __forceinline__ void bucket_run_table(const uint2* __restrict__ rows1
 __device__ __forceinline__ uint32_t bucket_run_of(const uint32_t* s_pre, uint32_t p) {
   uint32_t k = 0;
 #pragma unroll
-  for (uint32_t step = kRbChunks / 2; step != 0u; step >>= 1)
+  for (uint32_t step = kRunTable / 2; step != 0u; step >>= 1)
     if (s_pre[k + step] <= p) k += step;
   return k;
 }
 
-// fine_count: workgroup (rb, B) = (blockIdx.x, blockIdx.y) counts its runs
-// per tile into hist[rb * ntiles + B * fpb + f] (f < fpb tiles in the
-// bucket), from the packed index words (bucket-local cell << kIdxBits).
-__global__ __launch_bounds__(kRbThreads) void bucket_fine_count_kernel(
-    const uint2* __restrict__ rows1, uint32_t nchunks, uint32_t nbuckets,
-    const uint32_t* __restrict__ chunk_idx, uint32_t tile_shift, uint32_t fpb, uint32_t ntiles,
+// fine_count: workgroup w counts the cell keys of particles
+// [w * kCountPer, (w+1) * kCountPer) per tile into hist[w * ntiles + t]
+// (celdaDe read with 16-byte loads, counted in LDS). kCountSub count rows
+// make one row block, so the column scan's exclusive prefix at row
+// rb * kCountSub is what the row blocks before rb put in each tile.
+constexpr int kCountThreads = 1024;
+constexpr uint32_t kCountSub = 4;
+constexpr uint32_t kCountPer = kRbChunks * kChunk / kCountSub;  // particles per count row
+static_assert(kCountPer % (4u * kCountThreads) == 0, "whole 16-byte loads per thread");
+__global__ __launch_bounds__(kCountThreads) void bucket_fine_count_kernel(
+    const uint32_t* __restrict__ celdaDe, uint32_t n, uint32_t tile_shift, uint32_t ntiles,
     uint32_t* __restrict__ hist) {
-  __shared__ uint32_t s_pre[kRbChunks], s_src[kRbChunks], s_total;
-  __shared__ uint32_t s_h[kMaxFine];
-  const uint32_t rb = blockIdx.x, B = blockIdx.y;
-  if (threadIdx.x < kMaxFine) s_h[threadIdx.x] = 0u;
-  bucket_run_table(rows1, nchunks, nbuckets, rb, B, s_pre, s_src, &s_total);
+  constexpr uint32_t kLoads = kCountPer / (4u * kCountThreads);  // 16-byte loads per thread
+  __shared__ uint32_t s_h[kBucketMaxTiles];
+  for (uint32_t t = threadIdx.x; t < ntiles; t += kCountThreads) s_h[t] = 0u;
   __syncthreads();
-  const uint32_t total = s_total;
-  constexpr uint32_t kBatch = 8;  // index words per thread in flight
-  for (uint32_t p0 = 0; p0 < total; p0 += kRbThreads * kBatch) {
-    uint32_t word[kBatch];
+  const uint64_t base = static_cast<uint64_t>(blockIdx.x) * kCountPer;
+  const uint64_t end = (base + kCountPer < n) ? base + kCountPer : n;
+  const uint4* c4 = reinterpret_cast<const uint4*>(celdaDe + base);  // base: a multiple of 4
+  const uint32_t quads = static_cast<uint32_t>((end - base) / 4u);
+  uint4 v[kLoads];
 #pragma unroll
-    for (uint32_t k = 0; k < kBatch; ++k) {
-      const uint32_t p = p0 + k * kRbThreads + threadIdx.x;
-      word[k] = 0xFFFFFFFFu;
-      if (p < total) {
-        const uint32_t j = bucket_run_of(s_pre, p);
-        word[k] = chunk_idx[s_src[j] + (p - s_pre[j])];
-      }
-    }
+  for (uint32_t k = 0; k < kLoads; ++k) {
+    const uint32_t q = k * kCountThreads + threadIdx.x;
+    v[k] = (q < quads) ? c4[q] : make_uint4(0u, 0u, 0u, 0u);
+  }
 #pragma unroll
-    for (uint32_t k = 0; k < kBatch; ++k) {
-      if (word[k] == 0xFFFFFFFFu) continue;
-      const uint32_t f = (word[k] >> kIdxBits) >> tile_shift;
-      if (f < fpb) atomicAdd(&s_h[f], 1u);
+  for (uint32_t k = 0; k < kLoads; ++k) {
+    if (k * kCountThreads + threadIdx.x < quads) {
+      atomicAdd(&s_h[v[k].x >> tile_shift], 1u);
+      atomicAdd(&s_h[v[k].y >> tile_shift], 1u);
+      atomicAdd(&s_h[v[k].z >> tile_shift], 1u);
+      atomicAdd(&s_h[v[k].w >> tile_shift], 1u);
     }
   }
+  for (uint64_t j = base + 4ull * quads + threadIdx.x; j < end; j += kCountThreads)
+    atomicAdd(&s_h[celdaDe[j] >> tile_shift], 1u);
   __syncthreads();
-  if (threadIdx.x < fpb) {
-    const uint32_t t = B * fpb + threadIdx.x;
-    if (t < ntiles) hist[static_cast<size_t>(rb) * ntiles + t] = s_h[threadIdx.x];
-  }
+  for (uint32_t t = threadIdx.x; t < ntiles; t += kCountThreads)
+    hist[static_cast<size_t>(blockIdx.x) * ntiles + t] = s_h[t];
 }
 
-// rebucket: workgroup (rb, B) moves the runs fine_count counted. hist holds
-// the column-scanned matrix, tile_total the tile totals, group_total the
-// sums of 64 consecutive tiles. Each tile's group of a round goes to
+// Row block and bucket of rebucket workgroup w. Workgroups are dealt to the
+// 8 XCDs round robin; when the buckets split evenly over the XCDs, XCD x
+// takes the buckets x, x + 8, ... and walks the row blocks of one bucket in
+// order, so the workgroups it runs at one time write neighbouring segments
+// of every tile and share the lines at their boundaries in its L2.
+__device__ __forceinline__ uint2 rebucket_item(uint32_t w, uint32_t nrb, uint32_t nbuckets) {
+  if (nbuckets % 8u != 0u) return make_uint2(w % nrb, w / nrb);
+  const uint32_t x = w % 8u, i = w / 8u;
+  return make_uint2(i % nrb, x + 8u * (i / nrb));
+}
+
+// rebucket: workgroup (rb, B) moves the runs of bucket B in row block rb.
+// hist holds the column-scanned count matrix (row rb * kCountSub: what the
+// row blocks before rb put in each tile), tile_total the tile totals,
+// group_total the sums of 64 consecutive tiles (one bucket each). Each tile's group of a round goes to
 // tile_rec/tile_idx at the tile's start plus this row block's offset in the
 // tile plus what earlier rounds put there; row block 0 writes
 // rows[t] = {tile_total[t], start of tile t}.
 __global__ __launch_bounds__(kRbThreads) void bucket_rebucket_kernel(
     const uint2* __restrict__ rows1, uint32_t nchunks, uint32_t nbuckets,
-    const uint4* __restrict__ chunk_rec, const uint32_t* __restrict__ chunk_idx, uint32_t tile_shift,
-    uint32_t fpb, uint32_t ntiles, const uint32_t* __restrict__ hist,
+    const uint4* __restrict__ chunk_rec, const uint32_t* __restrict__ chunk_idx, uint32_t nrb,
+    uint32_t tile_shift, uint32_t fpb, uint32_t ntiles, const uint32_t* __restrict__ hist,
     const uint32_t* __restrict__ tile_total, const uint32_t* __restrict__ group_total, uint32_t n,
     uint4* __restrict__ tile_rec, uint32_t* __restrict__ tile_idx, uint2* __restrict__ rows) {
   __shared__ uint4 s_rec[2 * kRbRound];
   __shared__ uint32_t s_id[kRbRound];
   __shared__ uint8_t s_f[kRbRound];
-  __shared__ uint32_t s_pre[kRbChunks], s_src[kRbChunks], s_total;
+  __shared__ uint32_t s_pre[kRunTable], s_src[kRunTable], s_total;
   __shared__ uint32_t s_cnt[kMaxFine], s_off[kMaxFine], s_cur[kMaxFine];
-  const uint32_t rb = blockIdx.x, B = blockIdx.y;
+  const uint2 item = rebucket_item(blockIdx.x, nrb, nbuckets);
+  const uint32_t rb = item.x, B = item.y;
   bucket_run_table(rows1, nchunks, nbuckets, rb, B, s_pre, s_src, &s_total);
   if (threadIdx.x >= 64 && threadIdx.x < 128) {
     // wave 1: the cursors. Start of the bucket's first tile t0 = the groups
@@ -154,7 +168,7 @@ __global__ __launch_bounds__(kRbThreads) void bucket_rebucket_kernel(
     const uint32_t tot = (lane < fpb && t < ntiles) ? tile_total[t] : 0u;
     const uint32_t start = base_all + wave_inclusive_sum(tot) - tot;
     if (lane < fpb) {
-      s_cur[lane] = (t < ntiles) ? start + hist[static_cast<size_t>(rb) * ntiles + t] : 0u;
+      s_cur[lane] = (t < ntiles) ? start + hist[static_cast<size_t>(rb) * kCountSub * ntiles + t] : 0u;
       if (rb == 0 && t < ntiles) rows[t] = make_uint2(tot, start);
     }
   }

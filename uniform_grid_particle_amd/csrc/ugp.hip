@@ -114,7 +114,7 @@ struct Plan {
   uint32_t chunk = kChunk;  // particles per chunk_sort workgroup (staged path)
   // bucketed: coarse chunks and buckets (2^cshift keys), row blocks of
   // kRbChunks coarse chunks, [row block x tile] counts, tile and group totals
-  uint32_t cshift = 0, nbuckets = 0, ncoarse = 0, nrb = 0;
+  uint32_t cshift = 0, nbuckets = 0, ncoarse = 0, nrb = 0, ncount = 0;
   size_t off_rows1 = 0, off_coarse_rec = 0, off_coarse_idx = 0;
   size_t off_hist = 0, off_tile_total = 0, off_group_total = 0;
   // staged
@@ -241,6 +241,7 @@ int make_plan(uint32_t n, const uint32_t dims[3], uint32_t flags, Plan* p) {
     p->nbuckets = static_cast<uint32_t>((cells + (1ull << p->cshift) - 1) >> p->cshift);
     p->ncoarse = blocks_for(n, kChunk);
     p->nrb = blocks_for(p->ncoarse, kRbChunks);
+    p->ncount = blocks_for(n, kCountPer);
     p->nchunks = 1;  // the tile kernel sees each tile as one contiguous run
     p->off_rows1 = off;
     off = align_up(off + static_cast<size_t>(p->ncoarse) * p->nbuckets * 8u, 256);
@@ -249,7 +250,7 @@ int make_plan(uint32_t n, const uint32_t dims[3], uint32_t flags, Plan* p) {
     p->off_coarse_idx = off;
     off = align_up(off + static_cast<size_t>(n) * 4u, 256);
     p->off_hist = off;
-    off = align_up(off + static_cast<size_t>(p->nrb) * p->ntiles * 4u, 256);
+    off = align_up(off + static_cast<size_t>(p->ncount) * p->ntiles * 4u, 256);
     p->off_tile_total = off;
     off = align_up(off + static_cast<size_t>(p->ntiles) * 4u, 256);
     p->off_group_total = off;
@@ -609,7 +610,6 @@ void enqueue_bucketed(uint32_t stage, const BuildArgs& a, const Plan& p) {
   uint4* tile_rec = reinterpret_cast<uint4*>(ws + p.off_chunk_rec);
   uint32_t* tile_idx = reinterpret_cast<uint32_t*>(ws + p.off_chunk_idx);
   const uint32_t fpb = 1u << (p.cshift - p.tile_shift);
-  const dim3 rb_grid(p.nrb, p.nbuckets);
   hipStream_t s = a.stream;
   switch (stage) {
     case 0:  // chunks sorted by bucket: the chunk kernel with buckets for tiles
@@ -618,15 +618,15 @@ void enqueue_bucketed(uint32_t stage, const BuildArgs& a, const Plan& p) {
              p.nbuckets, coarse_rec, coarse_idx, a.diag, fix_lists_of(a, p).base, tile_queue_of(a, p).base);
       break;
     case 1:
-      launch(bucket_fine_count_kernel, rb_grid, dim3(kRbThreads), 0, s, rows1, p.ncoarse, p.nbuckets,
-             coarse_idx, p.tile_shift, fpb, p.ntiles, hist);
-      launch(bucket_colscan_kernel, dim3(blocks_for(p.ntiles, 64)), dim3(kScanWaves * 64), 0, s, hist, p.nrb,
+      launch(bucket_fine_count_kernel, dim3(p.ncount), dim3(kCountThreads), 0, s, a.celdaDe, a.n, p.tile_shift,
+             p.ntiles, hist);
+      launch(bucket_colscan_kernel, dim3(blocks_for(p.ntiles, 64)), dim3(kScanWaves * 64), 0, s, hist, p.ncount,
              p.ntiles, tile_total, group_total);
       break;
     case 2:
-      launch(bucket_rebucket_kernel, rb_grid, dim3(kRbThreads), 0, s, rows1, p.ncoarse, p.nbuckets, coarse_rec,
-             coarse_idx, p.tile_shift, fpb, p.ntiles, hist, tile_total, group_total, a.n, tile_rec, tile_idx,
-             rows);
+      launch(bucket_rebucket_kernel, dim3(p.nrb * p.nbuckets), dim3(kRbThreads), 0, s, rows1, p.ncoarse,
+             p.nbuckets, coarse_rec, coarse_idx, p.nrb, p.tile_shift, fpb, p.ntiles, hist, tile_total, group_total,
+             a.n, tile_rec, tile_idx, rows);
       break;
     case 3:
       launch_tile_sort<false>(a, p, rows, tile_rec, tile_idx);
