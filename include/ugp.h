@@ -155,8 +155,9 @@ int ugp_grid_workspace_bytes(uint32_t n, const uint32_t dims[3], uint32_t flags,
  *   n           number of particles (0 is valid: conteos and inicios are
  *               zeroed and nothing else is written)
  *   origin      host, in:    3 floats, lower corner of cell (0,0,0)
- *   cell_size   edge length of a cubic cell: finite, positive and normal
- *               (>= FLT_MIN)
+ *   cell_size   edge length of a cubic cell: finite and positive (a
+ *               subnormal size is valid: every position more than a
+ *               few thousand subnormal steps from the origin clamps)
  *   dims        host, in:    cells per axis, each in [1, 2^24]; the cell
  *               count C = dims[0]*dims[1]*dims[2] must be <= 2^32-2
  *   celdaDe     device, out: n u32, cell index of each particle (its key

@@ -92,8 +92,9 @@
 int ugp_oracle_check_grid(const float origin[3], float cell_size, const uint32_t dims[3],
                           uint64_t *cells_out) {
     if (!origin || !dims) return UGPO_ERR_NULL;
-    /* a usable cell size is a finite, normal, positive float */
-    if (!isfinite(cell_size) || !(cell_size >= FLT_MIN)) return UGPO_ERR_ARG;
+    /* a usable cell size is any finite positive float, subnormal ones
+       included: the division and the clamp are defined for all of them */
+    if (!isfinite(cell_size) || !(cell_size > 0.0f)) return UGPO_ERR_ARG;
     for (int a = 0; a < 3; ++a) {
         if (!isfinite(origin[a])) return UGPO_ERR_ARG;
         if (dims[a] < 1u || dims[a] > UGPO_MAX_DIM) return UGPO_ERR_RANGE;

@@ -302,7 +302,9 @@ def pin_grid_validation(orc):
     assert orc.check_grid(ok[0], np.float32(-1.0), ok[2]) != 0
     assert orc.check_grid(ok[0], np.float32(np.nan), ok[2]) != 0
     assert orc.check_grid(ok[0], np.float32(np.inf), ok[2]) != 0
-    assert orc.check_grid(ok[0], np.float32(1e-40), ok[2]) != 0  # subnormal cell size
+    assert orc.check_grid(ok[0], np.float32(-0.0), ok[2]) != 0
+    assert orc.check_grid(ok[0], np.float32(1e-40), ok[2]) == 0  # subnormal cell size
+    assert orc.check_grid(ok[0], np.float32(1.4e-45), ok[2]) == 0  # the smallest subnormal
     assert orc.check_grid(ok[0], np.float32(1.1754944e-38), ok[2]) == 0  # smallest normal
     assert orc.check_grid(np.array([0, np.nan, 0], np.float32), ok[1], ok[2]) != 0
     assert orc.check_grid(ok[0], ok[1], np.array([0, 4, 4], np.uint32)) != 0

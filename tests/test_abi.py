@@ -114,7 +114,7 @@ def test_validation_errors_on_host(lib):
     assert _call_build(lib, h=-1.0) == ugp.UGP_ERR_ARG
     assert _call_build(lib, h=nan) == ugp.UGP_ERR_ARG
     assert _call_build(lib, h=inf) == ugp.UGP_ERR_ARG
-    assert _call_build(lib, h=1e-40) == ugp.UGP_ERR_ARG  # subnormal cell size
+    assert _call_build(lib, h=-0.0) == ugp.UGP_ERR_ARG
     assert _call_build(lib, origin=(0.0, nan, 0.0)) == ugp.UGP_ERR_ARG
     assert _call_build(lib, origin=(inf, 0.0, 0.0)) == ugp.UGP_ERR_ARG
     assert _call_build(lib, dims=(0, 4, 4)) == ugp.UGP_ERR_RANGE

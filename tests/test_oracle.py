@@ -66,6 +66,19 @@ def test_binary32_model_nondyadic_faces(orc, h, o, d):
     pins.pin_binary32_model(orc, wl)
 
 
+# Subnormal cell sizes (dyadic 2^-140, non-dyadic 1e-40 and 3e-40): faces
+# at subnormal multiples of h, origins at zero and below it.
+SUBNORMAL_GRIDS = [(2.0 ** -140, 0.0, 16), (1e-40, 0.0, 16), (3e-40, -2e-39, 12)]
+
+
+@pytest.mark.parametrize("h,o,d", SUBNORMAL_GRIDS)
+def test_binary32_model_subnormal_cell_size(orc, h, o, d):
+    wl = W.make_boundary_probe((d, d, d), (o, o, o), np.float32(h), per_axis_random=256)
+    assert 0.0 < float(wl.cell_size) < 1.1754944e-38
+    pins.pin_binary32_model(orc, wl)
+    pins.pin_brute_force_slices(orc, wl)
+
+
 def test_binary32_model_tiny(orc):
     wl = W.make_config("tiny")
     pins.pin_binary32_model(orc, wl)

@@ -112,6 +112,19 @@ def test_cell_faces(ugp, orc, h, o, d):
     assert_parity(wl, run_gpu(ugp, wl, "atomic"), ref, "atomic")
 
 
+@pytest.mark.parametrize("h,o,d", [(2.0 ** -140, 0.0, 16), (1e-40, 0.0, 16), (3e-40, -2e-39, 12),
+                                   (1e-40, 0.0, 128)])
+def test_cell_faces_subnormal_cell_size(ugp, orc, h, o, d):
+    """Subnormal cell sizes (kept, not flushed, by the kernels): faces at
+    subnormal multiples of h, on the single and the staged paths."""
+    print(f"[parity] subnormal faces h={h} d={d}", flush=True)
+    wl = W.make_boundary_probe((d, d, d), (o, o, o), np.float32(h), per_axis_random=2048)
+    assert 0.0 < float(wl.cell_size) < 1.1754944e-38
+    ref = orc.grid_build(wl.particles, wl.origin, wl.cell_size, wl.dims)
+    for mode in ("atomic", "stable"):
+        assert_parity(wl, run_gpu(ugp, wl, mode), ref, mode)
+
+
 @pytest.mark.parametrize("n,dims", [(8192, (128, 1, 128)), (8192, (7, 5, 3)), (5000, (16, 16, 16)),
                                     (3, (1, 1, 1)), (777, (33, 1, 17))])
 def test_single_tile_path(ugp, orc, n, dims):

@@ -353,8 +353,9 @@ int validate(const BuildArgs& a, Plan* plan) {
   if (!a.origin || !a.dims) return UGP_ERR_NULL;
   int st = make_plan(a.n, a.dims, a.flags, plan);
   if (st != UGP_OK) return st;
-  // a usable cell size is a finite, normal, positive float
-  if (!std::isfinite(a.cell_size) || !(a.cell_size >= FLT_MIN)) return UGP_ERR_ARG;
+  // a usable cell size is any finite positive float (subnormal ones too:
+  // the kernels keep fp32 subnormals and divide correctly rounded)
+  if (!std::isfinite(a.cell_size) || !(a.cell_size > 0.0f)) return UGP_ERR_ARG;
   for (int k = 0; k < 3; ++k)
     if (!std::isfinite(a.origin[k])) return UGP_ERR_ARG;
   if (!a.conteos || !a.inicios || !a.workspace) return UGP_ERR_NULL;
@@ -892,7 +893,7 @@ int ugp_neighbor_count(const ugp_particle* particles, uint32_t n, const float or
   Plan p;
   int st = make_plan(n, dims, flags, &p);
   if (st != UGP_OK) return st;
-  if (!std::isfinite(cell_size) || !(cell_size >= FLT_MIN)) return UGP_ERR_ARG;
+  if (!std::isfinite(cell_size) || !(cell_size > 0.0f)) return UGP_ERR_ARG;
   for (int k = 0; k < 3; ++k)
     if (!std::isfinite(origin[k])) return UGP_ERR_ARG;
   if (!std::isfinite(radius) || !(radius >= 0.0f)) return UGP_ERR_ARG;
