@@ -214,7 +214,8 @@ __global__ __launch_bounds__(CT) void staged_keys_kernel(
 // capacity, is written in arrival order and put on one of the fix-up lists;
 // a tile holding such a longer cell also copies those arrival-order indices
 // to fl.idx() (the whole tile when it is staged, the long cells' ranges when
-// it is scattered), which the fix-up's long-cell pass reads.
+// it scatters alone, every index when its rounds are shared), which the
+// fix-up's long-cell pass reads.
 // packed (staged path): chunk_idx words hold the tile-local cell and the
 // index inside the chunk (chunk_sort), so no cell key is computed here and
 // a particle's index is its chunk's first index plus that field; otherwise
@@ -222,8 +223,9 @@ __global__ __launch_bounds__(CT) void staged_keys_kernel(
 // comes from the record's position.
 // q (not SINGLE): the shared scatter rounds of tiles past the staged
 // capacity (TileQueue), taken by the tile's owner and by every workgroup
-// that saw a claimed slot before its own stores. In stable mode such a tile
-// scatters alone.
+// that saw a claimed slot before its own stores. In stable mode the owner
+// lists every multi-particle cell of such a tile from its starts, and the
+// rounds copy each index to fl.idx() as well.
 template <bool MOVE, bool DIAG, bool STABLE, bool SINGLE, uint32_t SHIFT, int NT, uint32_t WIN>
 __global__ __launch_bounds__(NT) void staged_cells_kernel(
     const uint2* __restrict__ rows, uint32_t nchunks, uint32_t chunk, uint32_t ntiles, GridParams g,
@@ -519,7 +521,11 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
       if (lr[k] == 0xFFFFFFFFu) continue;
       const size_t out = static_cast<size_t>(wbs) + s_cnt[lr[k] >> 16] + (lr[k] & 0xFFFFu);
       if (out < n) {
-        ordenado[out] = index_of(src[k], word[k]);
+        const uint32_t id = index_of(src[k], word[k]);
+        ordenado[out] = id;
+        // stable: every cell of a shared tile is listed for the fix-up, and
+        // its long cells read their arrival order from this copy
+        if (STABLE) fl.idx()[out] = id;
         if (MOVE) {
           dst[out * 2u] = make_uint4(v[0][k], v[1][k], v[2][k], v[3][k]);
           dst[out * 2u + 1u] = make_uint4(v[4][k], v[5][k], v[6][k], v[7][k]);
@@ -734,12 +740,12 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
       }
       __syncthreads();
     }
-    if (share && !STABLE && s_item != 0u) help(blockIdx.x);  // uniform: written before the barriers above
+    if (share && s_item != 0u) help(blockIdx.x);  // uniform: written before the barriers above
   } else {
-    // a tile past the staged capacity (count > kStagedCap > 0). Not in
-    // stable mode: claim a slot now, so that tiles still loading see it
+    // a tile past the staged capacity (count > kStagedCap > 0): claim a
+    // slot now, so that tiles still loading see it
     uint32_t sidx = kMaxSlots;
-    if (share && !STABLE) {
+    if (share) {
       if (threadIdx.x == 0) s_item = atomicAdd(q.hdr(), 1u);
       __syncthreads();
       sidx = s_item;
@@ -809,6 +815,18 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
       if (threadIdx.x == 0) shared_store(q.hdr() + kReadyWord + sidx, 1u);
     }
     write_counts_starts(tot);
+    if (STABLE && shared) {
+      // the rounds take slots in arrival order: every cell of two or more
+      // is listed now, from the starts (the rounds reuse s_cnt), and the
+      // rounds themselves copy every index to fl.idx()
+      __syncthreads();  // s_cnt holds the starts (write_counts_starts read them too)
+      for (uint32_t j0 = 0; j0 < tc; j0 += NT) {  // whole waves: the listing is per wave
+        const uint32_t j = j0 + threadIdx.x;
+        const uint32_t a = (j < tc) ? s_cnt[j] : 0u;
+        const uint32_t e = (j < tc) ? ((j + 1u < kTileCells) ? s_cnt[j + 1u] : tot) : 0u;
+        list_cells_wave(fl, cell0 + j, e - a, e - a >= 2u);
+      }
+    }
     __syncthreads();  // every start read before the cursors advance
     if (shared) help(sidx);
     if (!shared) {
@@ -858,7 +876,7 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
         }
       }
     }
-    if (STABLE) {
+    if (STABLE && !shared) {
       // slots were taken in arrival order: every cell of two or more is
       // listed. Once every cursor is final it holds its cell's end, so a
       // cell's count is its end minus the previous cell's. The long cells
