@@ -212,7 +212,7 @@ def _counter_means(csv_path: str, counter: str) -> dict:
 
 
 def summarize_counters(fetch_csv: str, write_csv: str, copy_bytes: int = 256 << 20) -> tuple[str, dict]:
-    """HBM bytes per dispatch from FETCH_SIZE / WRITE_SIZE (KiB), each scaled by
+    """Fabric bytes per dispatch from FETCH_SIZE / WRITE_SIZE (KiB), each scaled by
     what the same counter reads for the largest device copy (copy_bytes read
     and written) in the same run -- the reference copy of bench.py
     --copy-reference, which then skips its other copies."""
@@ -249,7 +249,8 @@ KERNEL_STAGE = {
 
 def write_traffic_file(traffic: dict, path: str, command: str) -> None:
     with open(path, "w", encoding="utf-8") as f:
-        f.write("# Measured HBM traffic per dispatch (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE),\n")
+        f.write("# Measured fabric traffic per dispatch (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE: bytes between\n")
+        f.write("# the L2 caches and the Infinity Fabric, Infinity Cache hits included),\n")
         f.write("# each counter scaled by its reading for a 256 MiB device copy in the same run.\n")
         f.write(f"# command: {command}\n")
         f.write(f"source_sha256_16: {source_digest()}\n")
