@@ -155,24 +155,37 @@ def _p10_p90(xs) -> list:
 
 
 def _cpu_model() -> str:
-    """lscpu's "Model name" (else /proc/cpuinfo's), as printed."""
+    """lscpu's "Model name" (else /proc/cpuinfo's), as printed, with the x86
+    family, model and stepping numbers (a virtualised host may print only
+    the brand)."""
     import subprocess
 
+    name = "unknown"
     try:
         out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
         for line in out.splitlines():
             if line.startswith("Model name:"):
-                return line.split(":", 1)[1].strip()
+                name = line.split(":", 1)[1].strip()
+                break
     except (OSError, subprocess.SubprocessError):
         pass
+    ids = {}
     try:
         with open("/proc/cpuinfo", encoding="utf-8") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                key, _, val = line.partition(":")
+                key = key.strip()
+                if key in ("model name", "cpu family", "model", "stepping") and key not in ids:
+                    ids[key] = val.strip()
+                if not line.strip() and ids:
+                    break  # first processor only
     except OSError:
         pass
-    return "unknown"
+    if name == "unknown":
+        name = ids.get("model name", "unknown")
+    if "cpu family" in ids:
+        name += f" (family {ids['cpu family']}, model {ids.get('model', '?')}, stepping {ids.get('stepping', '?')})"
+    return name
 
 
 # ---------------------------------------------------------------------------
