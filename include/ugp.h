@@ -121,9 +121,11 @@ typedef struct ugp_particle {
  *   K <= 2^22 and n <= 2^21 (K up to 2^23 on dense grids)
  *                     "chunk_sort", -, -, "tile_sort" -- two kernels, no
  *                     global atomics, records moved through LDS
- *   other K <= 2^26   "keys", "tile_scan", "bucket", "tile_sort" -- a
- *                     two-level counting sort with LDS histograms and no
- *                     global atomics, ending in the same tile kernel
+ *   other K <= 2^26   "coarse_sort", "tile_scan", "rebucket", "tile_sort"
+ *                     -- chunks sorted by bucket of 64 tiles, a per-tile
+ *                     count and its column scan (two kernels), the
+ *                     buckets' runs regrouped by tile, then the same tile
+ *                     kernel; no global atomics, every record moved in runs
  *   larger K          "clear", "count", "scan", "scatter"     -- one global
  *                     atomic per particle in count and in scatter
  *   slot 4 "stable_sort" (UGP_FLAG_STABLE only; page "Construir el índice
@@ -309,8 +311,8 @@ int ugp_grid_build_timed(const ugp_particle *particles, uint32_t n, const float 
                          uint32_t flags, void *stream, uint32_t timed_stage, void *event_before,
                          void *event_after);
 
-/* Name of stage slot `stage` for this problem shape and flags ("keys",
- * "count", ...), or NULL when the slot runs nothing or the shape is
+/* Name of stage slot `stage` for this problem shape and flags
+ * ("chunk_sort", "count", ...), or NULL when the slot runs nothing or the shape is
  * invalid. Static storage. Pure host function. */
 const char *ugp_grid_stage_name(uint32_t n, const uint32_t dims[3], uint32_t flags, uint32_t stage);
 

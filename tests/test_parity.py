@@ -262,6 +262,25 @@ def test_bucketed_one_cell_holds_everything(ugp, orc):
     assert_parity(wl, run_gpu(ugp, wl, "atomic"), ref, "atomic")
 
 
+@pytest.mark.parametrize("mode", ["atomic", "stable"])
+def test_bucketed_one_bucket_holds_everything(ugp, orc, mode):
+    """3,000,000 particles in a z-slab of 8 planes of 128^3: every particle
+    in one of 16 buckets, so each rebucket workgroup of that bucket moves its
+    runs in 64 rounds, and the bucket's 64 tiles (about 47,000 particles
+    each) all overflow the staged capacity and fill every queue slot."""
+    n, dims = 3_000_000, (128, 128, 128)
+    print(f"[parity] bucketed one bucket {mode}", flush=True)
+    assert ugp.stage_names(n, dims)[:4] == ["coarse_sort", "tile_scan", "rebucket", "tile_sort"]
+    rng = np.random.Generator(np.random.PCG64(4242))
+    parts = rng.standard_normal((n, 8)).astype(np.float32)
+    parts[:, 0:2] = (rng.random((n, 2)) * 128.0).astype(np.float32)
+    parts[:, 2] = (40.0 + rng.random(n) * 7.99).astype(np.float32)  # planes 40..47: one bucket of 8 planes
+    wl = W.Workload("one_bucket", parts, np.zeros(3, np.float32), np.float32(1.0), np.asarray(dims, np.uint32))
+    ref = orc.grid_build(wl.particles, wl.origin, wl.cell_size, wl.dims)
+    assert int(np.count_nonzero(ref.conteos)) <= 8 * 128 * 128
+    assert_parity(wl, run_gpu(ugp, wl, mode), ref, mode)
+
+
 def test_direct_path_beyond_bucketed_limit(ugp, orc):
     """More than 2^26 cells: the global-atomic path."""
     dims = (8192, 8193, 1)

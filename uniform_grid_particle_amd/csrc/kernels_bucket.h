@@ -236,23 +236,24 @@ __global__ __launch_bounds__(kRbThreads) void bucket_rebucket_kernel(
   }
 }
 
-// tile_scan: workgroup g scans columns [64g, 64g + 64) of hist over the nblk
-// rows, in place (exclusive), and writes the column totals to tile_total
-// and their sum to group_total[g]. Wave r of kScanWaves takes the rows [r*R, (r+1)*R), lane l column
-// 64g + l, so every load and store of a wave is 64 consecutive words of one
-// row; each lane keeps kScanUnroll loads in flight.
+// tile_scan: workgroup g scans columns [64g, 64g + 64) of hist over the
+// nrows rows, in place (exclusive), and writes the column totals to
+// tile_total and their sum to group_total[g]. Wave r of kScanWaves takes the
+// rows [r*R, (r+1)*R), lane l column 64g + l, so every load and store of a
+// wave is 64 consecutive words of one row; each lane keeps kScanUnroll loads
+// in flight.
 constexpr int kScanWaves = 16;
 constexpr uint32_t kScanUnroll = 8;
 __global__ __launch_bounds__(kScanWaves * 64) void bucket_colscan_kernel(uint32_t* __restrict__ hist,
-                                                                         uint32_t nblk, uint32_t ntiles,
+                                                                         uint32_t nrows, uint32_t ntiles,
                                                                          uint32_t* __restrict__ tile_total,
                                                                          uint32_t* __restrict__ group_total) {
   __shared__ uint32_t s_part[kScanWaves][64];
   const uint32_t lane = threadIdx.x & 63u, r = threadIdx.x >> 6;
   const uint32_t t = blockIdx.x * 64u + lane;
-  const uint32_t per = (nblk + kScanWaves - 1u) / kScanWaves;
+  const uint32_t per = (nrows + kScanWaves - 1u) / kScanWaves;
   const uint32_t w0 = r * per;
-  const uint32_t w1 = (w0 + per < nblk) ? w0 + per : nblk;
+  const uint32_t w1 = (w0 + per < nrows) ? w0 + per : nrows;
   const bool live = t < ntiles;
   uint32_t part = 0;
   if (live) {
