@@ -356,9 +356,9 @@ def neighbor_bench(ugp, torch, dev, evict, stream, reps: int = 5) -> dict:
     res["mean_neighbors"] = float(ugp.as_u32_numpy(out).mean())
     res["speedup_reordered_vs_indirect"] = res["indirect_linear"]["us"] / res["reordered_linear"]["us"]
     res["speedup_morton_vs_linear_reordered"] = res["reordered_linear"]["us"] / res["reordered_morton"]["us"]
-    res["note"] = ("one thread per query; pairs = distance evaluations (27-cell candidates, self excluded); "
-                   "the reordered runs read the build's cell-ordered records, the indirect ones read the "
-                   "original array through ordenado")
+    res["note"] = ("one thread per query, queries taken in cell order; pairs = distance evaluations "
+                   "(27-cell candidates, self excluded); the reordered runs read the build's cell-ordered "
+                   "records, the indirect ones read the original array through ordenado")
     return res
 
 

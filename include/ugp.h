@@ -284,7 +284,11 @@ int ugp_cell_diag_timed(const uint32_t *conteos, uint32_t cells, uint32_t capaci
  *   radius     finite, >= 0
  *   counts     device, out: n u32, counts[k] for particle k of `particles`
  *              (original index with ordenado; cell-order slot without);
- *              must not overlap the inputs
+ *              must not overlap the inputs. Queries are taken in cell
+ *              order (with ordenado, the one at place k is particle
+ *              ordenado[k]), so with ordenado every entry is written when
+ *              ordenado is a permutation of 0..n-1, as the build leaves
+ *              it; an entry >= n is skipped
  *   flags      0 or UGP_FLAG_MORTON, as in the build
  * Returns UGP_OK once enqueued; UGP_ERR_NULL / UGP_ERR_ARG / UGP_ERR_RANGE /
  * UGP_ERR_ALIGN / UGP_ERR_ALIAS with nothing enqueued; UGP_ERR_HIP. The
