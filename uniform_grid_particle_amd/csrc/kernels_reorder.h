@@ -257,12 +257,14 @@ __device__ __forceinline__ void copy_cell_records(uint32_t s, uint32_t len, uint
 //
 // SHARE: the cell's arrival-order indices are read from `arrival` (at the
 // same places), which nothing writes meanwhile, so with fewer cells than
-// workgroups stride / count workgroups can share a cell of up to kLdsSort:
-// each finds every place as above, which costs little next to the stores
-// and the record gathers, and writes and gathers only its own share
-// [p0, p1) of the places (at least kMinPart of them). No workgroup waits
-// for another. Without SHARE the indices are read from ordenado itself and
-// a cell has one workgroup.
+// workgroups stride / count workgroups can share a cell of up to kLdsSort
+// (at least kMinPart entries each): with the bitmap, each takes an equal
+// part of the cell's index range, counts the cell's indices below it (its
+// first place) and in it, and orders only those; with the bitonic sort,
+// each sorts the whole cell and keeps an equal share of the places. Each
+// writes and gathers only its own places. No workgroup waits for another.
+// Without SHARE the indices are read from ordenado itself and a cell has
+// one workgroup.
 template <bool RECS, bool SHARE>
 __device__ __forceinline__ void sort_long_cells(
     const uint32_t* __restrict__ inicios, const uint32_t* __restrict__ celdaDe, uint32_t n,
@@ -310,13 +312,30 @@ __device__ __forceinline__ void sort_long_cells(
       lo = ~block_max<kSortBlock>(~lo, s_wave);
       hi = block_max<kSortBlock>(hi, s_wave);
       if (hi - lo < kBitmapPasses * kWindow) {  // len >= 1, so lo <= hi; uniform
-        uint32_t placed = 0;
-        for (uint64_t base64 = lo; base64 <= hi; base64 += kWindow) {
-          const uint32_t base = static_cast<uint32_t>(base64);  // <= hi: fits
-          // the bitmap words this window's part of the cell can touch; thread
-          // t owns words t, t + kSortBlock, ... (a wave's lanes touch
+        // this workgroup's part [w_lo, w_end) of the index range (the whole
+        // range unshared; empty only if the cell repeats an index) and its
+        // places [q0, q1): the cell's indices below w_lo come first
+        const uint64_t span = static_cast<uint64_t>(hi - lo) + 1u;
+        const uint64_t w_lo = lo + span * part / parts;
+        const uint64_t w_end = lo + span * (part + 1u) / parts;  // <= hi + 1 <= 2^32
+        uint32_t below = 0, inside = 0;
+#pragma unroll
+        for (uint32_t q = 0; q < kPer; ++q) {
+          if (threadIdx.x + q * kSortBlock < len) {
+            below += (v[q] < w_lo) ? 1u : 0u;
+            inside += (v[q] >= w_lo && v[q] < w_end) ? 1u : 0u;
+          }
+        }
+        const uint32_t packed = block_sum<kSortBlock>(below | (inside << 16), s_wave);  // each <= kLdsSort < 2^16
+        const uint32_t q0 = packed & 0xFFFFu, q1 = q0 + (packed >> 16);
+        uint32_t placed = q0;
+        for (uint64_t base64 = w_lo; base64 < w_end; base64 += kWindow) {
+          const uint32_t base = static_cast<uint32_t>(base64);  // < w_end <= 2^32: fits
+          // the bitmap words this window's part of the range can touch;
+          // thread t owns words t, t + kSortBlock, ... (a wave's lanes touch
           // consecutive words: no LDS bank conflicts)
-          const uint32_t top = (hi - base < kWindow - 1u) ? hi - base : kWindow - 1u;
+          const uint64_t last = w_end - 1u - base64;
+          const uint32_t top = (last < kWindow - 1u) ? static_cast<uint32_t>(last) : kWindow - 1u;
           const uint32_t used = (top >> 5) + 1u;
 #pragma unroll 4
           for (uint32_t q = 0; q < kPer; ++q)
@@ -325,7 +344,7 @@ __device__ __forceinline__ void sort_long_cells(
 #pragma unroll 4
           for (uint32_t q = 0; q < kPer; ++q) {
             const uint32_t off = v[q] - base;  // wraps (and fails the test) below the window
-            if (threadIdx.x + q * kSortBlock < len && v[q] >= base && off < kWindow)
+            if (threadIdx.x + q * kSortBlock < len && v[q] >= base && off <= top)
               atomicOr(&s_keys[off >> 5], 1u << (off & 31u));
           }
           __syncthreads();
@@ -360,17 +379,17 @@ __device__ __forceinline__ void sort_long_cells(
 #pragma unroll 4
           for (uint32_t q = 0; q < kPer; ++q) {
             const uint32_t off = v[q] - base;
-            if (threadIdx.x + q * kSortBlock < len && v[q] >= base && off < kWindow) {
+            if (threadIdx.x + q * kSortBlock < len && v[q] >= base && off <= top) {
               const uint32_t wd = off >> 5;
               const uint32_t place =
                   placed + s_pre[wd] + __popc(s_keys[wd] & ((1u << (off & 31u)) - 1u));
-              if (place >= p0 && place < p1) ordenado[s + place] = v[q];
+              if (place < q1) ordenado[s + place] = v[q];  // < len: distinct indices
             }
           }
           placed += total;
           __syncthreads();  // this window's reads end before the next one is cleared
         }
-        if (RECS) copy_cell_records(s + p0, p1 - p0, n, ordenado, particles, reordered);
+        if (RECS) copy_cell_records(s + q0, q1 - q0, n, ordenado, particles, reordered);
         continue;
       }
       uint32_t L = 1;
