@@ -263,6 +263,7 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
   __shared__ uint32_t s_any_long;
   __shared__ uint32_t s_below;  // SINGLE: particles in earlier tiles
   __shared__ uint32_t s_item;   // shared rounds: the item or slot this workgroup took
+  __shared__ uint32_t s_list[2];  // stable: the tile's first places on the two fix-up lists
 
   // one tile holding the whole input: no kernel runs before this one, so the
   // words it would zero are zeroed here, before the first barrier below
@@ -452,6 +453,45 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
       __syncthreads();
       publish_diag<NT>(s_dm, s_do, diag);
     }
+  };
+
+  // Stable mode: puts the tile's cells of min_len or more particles
+  // (len_of(j) for tile-local cell j) on the short or long fix-up list, with
+  // one block scan of the per-thread counts and one global atomic per list
+  // for the whole tile (each thread takes kPer consecutive cells, so the
+  // list holds them in cell order). Contains barriers: call it uniformly.
+  auto list_cells_tile = [&](uint32_t min_len, auto len_of) __attribute__((always_inline)) {
+    static_assert(kTileCells < (1u << 16), "a tile's list counts fit a half-word");
+    const uint32_t j0 = threadIdx.x * kPer;
+    uint32_t len[kPer];
+    uint32_t ns = 0, nl = 0;
+#pragma unroll
+    for (uint32_t k = 0; k < kPer; ++k) {
+      len[k] = (j0 + k < tc) ? len_of(j0 + k) : 0u;
+      const bool listed = len[k] >= min_len;
+      ns += (listed && len[k] <= kRankSortMax) ? 1u : 0u;
+      nl += (listed && len[k] > kRankSortMax) ? 1u : 0u;
+    }
+    uint32_t total;
+    const uint32_t ex = block_exclusive_sum<NT>(ns | (nl << 16), s_wave, &total);
+    if (threadIdx.x == 0) {
+      s_list[0] = (total & 0xFFFFu) ? atomicAdd(&fl.base[0], total & 0xFFFFu) : 0u;
+      s_list[1] = (total >> 16) ? atomicAdd(&fl.base[1], total >> 16) : 0u;
+    }
+    __syncthreads();
+    uint32_t fs = s_list[0] + (ex & 0xFFFFu), fo = s_list[1] + (ex >> 16);
+#pragma unroll
+    for (uint32_t k = 0; k < kPer; ++k) {
+      if (len[k] < min_len) continue;
+      if (len[k] <= kRankSortMax) {
+        if (fs < fl.fix_cap) fl.fix()[fs] = cell0 + j0 + k;
+        ++fs;
+      } else {
+        if (fo < fl.long_cap) fl.lng()[fo] = cell0 + j0 + k;
+        ++fo;
+      }
+    }
+    __syncthreads();  // s_list is read before it is used again
   };
 
   // One shared scatter round: positions [base, base + len) of a shared
@@ -820,12 +860,7 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
       // is listed now, from the starts (the rounds reuse s_cnt), and the
       // rounds themselves copy every index to fl.idx()
       __syncthreads();  // s_cnt holds the starts (write_counts_starts read them too)
-      for (uint32_t j0 = 0; j0 < tc; j0 += NT) {  // whole waves: the listing is per wave
-        const uint32_t j = j0 + threadIdx.x;
-        const uint32_t a = (j < tc) ? s_cnt[j] : 0u;
-        const uint32_t e = (j < tc) ? ((j + 1u < kTileCells) ? s_cnt[j + 1u] : tot) : 0u;
-        list_cells_wave(fl, cell0 + j, e - a, e - a >= 2u);
-      }
+      list_cells_tile(2u, [&](uint32_t j) { return ((j + 1u < kTileCells) ? s_cnt[j + 1u] : tot) - s_cnt[j]; });
     }
     __syncthreads();  // every start read before the cursors advance
     if (shared) help(sidx);
@@ -885,10 +920,9 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
       // s_idx holds copies its whole range.
       if (threadIdx.x == 0) s_any_long = 0u;
       __syncthreads();
-      for (uint32_t j0 = 0; j0 < tc; j0 += NT) {  // whole waves: the listing is per wave
-        const uint32_t j = j0 + threadIdx.x;
-        const uint32_t len = (j < tc) ? s_cnt[j] - (j ? s_cnt[j - 1u] : 0u) : 0u;
-        list_cells_wave(fl, cell0 + j, len, len >= 2u);
+      list_cells_tile(2u, [&](uint32_t j) { return s_cnt[j] - (j ? s_cnt[j - 1u] : 0u); });
+      for (uint32_t j = threadIdx.x; j < tc; j += NT) {
+        const uint32_t len = s_cnt[j] - (j ? s_cnt[j - 1u] : 0u);
         if (len > kRankSortMax) {
           const uint32_t at = atomicAdd(&s_any_long, 1u);
           if (at < kStagedWin) s_idx[at] = j;
