@@ -404,6 +404,28 @@ def test_stable_long_cells_wide_index_range(ugp, orc, dims):
     assert_parity(wl, run_gpu(ugp, wl, "stable"), ref, "stable")
 
 
+def test_stable_long_cell_split_by_index_range(ugp, orc):
+    """One long cell (9,000 particles) whose fix-up is shared by 9 workgroups,
+    each ordering one ninth of the cell's index range: the cell's indices sit
+    at both ends of the input (the first 4,000 and the last 5,000), so the
+    middle parts hold none and the end parts hold more than their share."""
+    n, d, h = 200_000, 64, 0.5
+    print(f"[parity] long cell split by index range n={n}", flush=True)
+    rng = np.random.Generator(np.random.PCG64(9000))
+    parts = rng.standard_normal((n, 8)).astype(np.float32)
+    parts[:, :3] = (rng.random((n, 3)) * d * h).astype(np.float32)
+    hot = np.r_[0:4000, n - 5000:n]
+    k = np.array([17, 40, 9], np.float64)
+    parts[hot, :3] = ((k + 0.25 + 0.5 * rng.random((hot.size, 3))) * h).astype(np.float32)
+    wl = W.Workload("split", np.ascontiguousarray(parts), np.zeros(3, np.float32), np.float32(h),
+                    np.array([d, d, d], np.uint32))
+    ref = orc.grid_build(wl.particles, wl.origin, wl.cell_size, wl.dims)
+    c = 17 + 40 * d + 9 * d * d
+    s, e = int(ref.inicios[c]), int(ref.inicios[c + 1])
+    assert 9000 <= e - s <= 9100 and int(ref.ordenado[s]) == 0 and int(ref.ordenado[e - 1]) == n - 1
+    assert_parity(wl, run_gpu(ugp, wl, "stable"), ref, "stable")
+
+
 @pytest.mark.parametrize("seed", [3, 4])
 def test_stable_cell_lengths(ugp, orc, seed):
     """Stable order across the cell lengths the tile kernel treats apart:
