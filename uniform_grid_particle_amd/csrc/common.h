@@ -58,31 +58,6 @@ struct FixLists {
   __device__ __forceinline__ uint32_t* idx() const { return base + kFixHeader + fix_cap + long_cap; }
 };
 
-// Puts the cells of the calling wave's lanes with `listed` set on the list
-// their length picks, one global atomic per list and wave. Every lane of
-// the wave must call it (uniform control flow).
-__device__ __forceinline__ void list_cells_wave(const FixLists& fl, uint32_t cell, uint32_t len, bool listed) {
-  const bool sh = listed && len <= kRankSortMax, lo = listed && len > kRankSortMax;
-  const uint64_t ms = __ballot(sh), ml = __ballot(lo);
-  const uint32_t lane = __lane_id();
-  const uint64_t below = (1ull << lane) - 1ull;
-  uint32_t bs = 0, bl = 0;
-  if (lane == 0) {
-    if (ms) bs = atomicAdd(&fl.base[0], static_cast<uint32_t>(__popcll(ms)));
-    if (ml) bl = atomicAdd(&fl.base[1], static_cast<uint32_t>(__popcll(ml)));
-  }
-  bs = __shfl(bs, 0);
-  bl = __shfl(bl, 0);
-  if (sh) {
-    const uint32_t f = bs + static_cast<uint32_t>(__popcll(ms & below));
-    if (f < fl.fix_cap) fl.fix()[f] = cell;
-  }
-  if (lo) {
-    const uint32_t f = bl + static_cast<uint32_t>(__popcll(ml & below));
-    if (f < fl.long_cap) fl.lng()[f] = cell;
-  }
-}
-
 // Work shared among the workgroups of one tile kernel launch: the scatter
 // of tiles past the staged capacity. The workgroup that owns such a tile
 // claims one of kMaxSlots slots as soon as it knows its count; while it

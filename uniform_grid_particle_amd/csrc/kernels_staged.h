@@ -744,14 +744,9 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
       }
       __syncthreads();  // every rank counted before the window loop reuses s_rec
       any_long = s_any_long != 0u;
-      if (any_long) {
-        for (uint32_t j0 = 0; j0 < tc; j0 += NT) {  // whole waves: the listing is per wave
-          const uint32_t j = j0 + threadIdx.x;
-          const uint32_t a = (j < tc) ? s_cnt[j] : 0u;
-          const uint32_t e = (j < tc) ? ((j + 1u < kTileCells) ? s_cnt[j + 1u] : tot) : 0u;
-          list_cells_wave(fl, cell0 + j, e - a, e - a > kRankSortMax);
-        }
-      }
+      if (any_long)  // tile-uniform; s_cnt holds the starts
+        list_cells_tile(kRankSortMax + 1u,
+                        [&](uint32_t j) { return ((j + 1u < kTileCells) ? s_cnt[j + 1u] : tot) - s_cnt[j]; });
     }
     for (uint32_t w0 = 0; w0 < tot; w0 += kStagedWin) {  // tile-uniform
       const uint32_t wn = (tot - w0 < kStagedWin) ? tot - w0 : kStagedWin;
