@@ -16,6 +16,7 @@ constexpr int kSortGrid = 512;             // workgroups of the long-cell sort (
 constexpr uint32_t kRecBatch = 8;          // records gathered together by one thread (long cells)
 constexpr uint32_t kBitmapPasses = 4;      // bitmap windows a long cell may take (2^21 index values)
 constexpr uint32_t kMinPart = 1024;        // fewest places of a shared long cell one workgroup takes
+constexpr uint32_t kOutStage = 8192;       // places of a long cell the fix-up orders in LDS before writing
 // fix-up workgroups: 256 in all, one per CU (each takes ~97 KB of LDS), so
 // that a fix-up with nothing listed is one round of workgroups that exit
 constexpr uint32_t kFixLongBlocks = 32;    // on long cells (a cell of 10,000 takes 10)
@@ -240,6 +241,42 @@ __device__ __forceinline__ void copy_cell_records(uint32_t s, uint32_t len, uint
   __syncthreads();
 }
 
+// The places [s, s + len) of a long cell whose indices, in order, are in
+// LDS (ids): ordenado and the records gathered from the input by index are
+// written contiguously, kRecBatch records per thread at a time. Ends with
+// a barrier.
+__device__ __forceinline__ void write_cell_from_lds(uint32_t s, uint32_t len, uint32_t n, const uint32_t* ids,
+                                                    uint32_t* __restrict__ ordenado,
+                                                    const uint4* __restrict__ particles,
+                                                    uint4* __restrict__ reordered, bool recs) {
+  for (uint32_t t0 = threadIdx.x; t0 < len; t0 += kRecBatch * kSortBlock) {
+    uint32_t id[kRecBatch];
+    uint4 ra[kRecBatch], rb[kRecBatch];
+#pragma unroll
+    for (uint32_t j = 0; j < kRecBatch; ++j) {
+      const uint32_t t = t0 + j * kSortBlock;
+      id[j] = (t < len) ? ids[t] : 0xFFFFFFFFu;
+      if (t < len) ordenado[s + t] = id[j];
+      ra[j] = rb[j] = make_uint4(0u, 0u, 0u, 0u);
+      if (recs && id[j] < n) {
+        ra[j] = particles[2ull * id[j]];
+        rb[j] = particles[2ull * id[j] + 1u];
+      }
+    }
+    if (recs) {
+#pragma unroll
+      for (uint32_t j = 0; j < kRecBatch; ++j) {
+        const uint32_t t = t0 + j * kSortBlock;
+        if (t < len && id[j] < n) {
+          reordered[2ull * (s + t)] = ra[j];
+          reordered[2ull * (s + t) + 1u] = rb[j];
+        }
+      }
+    }
+  }
+  __syncthreads();
+}
+
 // Stable mode, long cells: the workgroups first, first + stride, ... take
 // entries first, first + stride, ... of the list of long cells. Up to 16384
 // entries, held in registers: when the cell's indices span at most
@@ -253,7 +290,10 @@ __device__ __forceinline__ void copy_cell_records(uint32_t s, uint32_t len, uint
 // Longer: ordered compaction, i.e. walk all particles in index order and
 // append those of this cell (the cell's membership is exact already; only
 // order changes). Each way writes indices only; RECS: the records follow in
-// one pass over the ordered slice (copy_cell_records).
+// one pass over the ordered slice (copy_cell_records). With the bitmap and
+// s_out (kOutStage words of LDS, or nullptr), a part of up to kOutStage
+// places is ordered in LDS first and written out contiguously, records
+// gathered by the indices held there (write_cell_from_lds).
 //
 // SHARE: the cell's arrival-order indices are read from `arrival` (at the
 // same places), which nothing writes meanwhile, so with fewer cells than
@@ -270,7 +310,8 @@ __device__ __forceinline__ void sort_long_cells(
     const uint32_t* __restrict__ inicios, const uint32_t* __restrict__ celdaDe, uint32_t n,
     const uint32_t* __restrict__ long_list, uint32_t count, uint32_t first, uint32_t stride,
     const uint32_t* arrival, uint32_t* __restrict__ ordenado, const uint4* __restrict__ particles,
-    uint4* __restrict__ reordered, uint32_t* s_keys, uint16_t* s_pre, uint32_t* s_tab, uint32_t* s_wave) {
+    uint4* __restrict__ reordered, uint32_t* s_keys, uint16_t* s_pre, uint32_t* s_tab, uint32_t* s_wave,
+    uint32_t* s_out) {
   const uint32_t* src = SHARE ? arrival : ordenado;
   uint32_t share = 1, part = 0;
   if (SHARE && count != 0u && count < stride) {
@@ -328,6 +369,7 @@ __device__ __forceinline__ void sort_long_cells(
         }
         const uint32_t packed = block_sum<kSortBlock>(below | (inside << 16), s_wave);  // each <= kLdsSort < 2^16
         const uint32_t q0 = packed & 0xFFFFu, q1 = q0 + (packed >> 16);
+        const bool staged = s_out != nullptr && q1 - q0 <= kOutStage;  // uniform
         uint32_t placed = q0;
         for (uint64_t base64 = w_lo; base64 < w_end; base64 += kWindow) {
           const uint32_t base = static_cast<uint32_t>(base64);  // < w_end <= 2^32: fits
@@ -337,8 +379,8 @@ __device__ __forceinline__ void sort_long_cells(
           const uint64_t last = w_end - 1u - base64;
           const uint32_t top = (last < kWindow - 1u) ? static_cast<uint32_t>(last) : kWindow - 1u;
           const uint32_t used = (top >> 5) + 1u;
-#pragma unroll 4
-          for (uint32_t q = 0; q < kPer; ++q)
+          const uint32_t nq = (used + kSortBlock - 1u) / kSortBlock;  // word groups in use (<= kPer)
+          for (uint32_t q = 0; q < nq; ++q)
             if (q * kSortBlock + threadIdx.x < used) s_keys[q * kSortBlock + threadIdx.x] = 0u;
           __syncthreads();
 #pragma unroll 4
@@ -352,8 +394,7 @@ __device__ __forceinline__ void sort_long_cells(
           // are groups q of kSortBlock, each the 64-word runs of the waves:
           // a wave scan places a word inside its run, and an exclusive scan
           // of the run totals in (q, wave) order (s_tab) places the runs.
-#pragma unroll 4
-          for (uint32_t q = 0; q < kPer; ++q) {
+          for (uint32_t q = 0; q < nq; ++q) {
             const uint32_t wd = q * kSortBlock + threadIdx.x;
             const uint32_t incl = wave_inclusive_sum((wd < used) ? __popc(s_keys[wd]) : 0u);
             if (lane == 63u) s_tab[q * kWaves + wave] = incl;
@@ -361,13 +402,12 @@ __device__ __forceinline__ void sort_long_cells(
           __syncthreads();
           uint32_t total;
           {
-            const uint32_t x = (threadIdx.x < kPer * kWaves) ? s_tab[threadIdx.x] : 0u;
+            const uint32_t x = (threadIdx.x < nq * kWaves) ? s_tab[threadIdx.x] : 0u;
             const uint32_t ex = block_exclusive_sum<kSortBlock>(x, s_wave, &total);
-            if (threadIdx.x < kPer * kWaves) s_tab[threadIdx.x] = ex;  // its own entry only
+            if (threadIdx.x < nq * kWaves) s_tab[threadIdx.x] = ex;  // its own entry only
           }
           __syncthreads();
-#pragma unroll 4
-          for (uint32_t q = 0; q < kPer; ++q) {
+          for (uint32_t q = 0; q < nq; ++q) {
             const uint32_t wd = q * kSortBlock + threadIdx.x;
             const uint32_t c = (wd < used) ? __popc(s_keys[wd]) : 0u;
             const uint32_t incl = wave_inclusive_sum(c);
@@ -383,13 +423,21 @@ __device__ __forceinline__ void sort_long_cells(
               const uint32_t wd = off >> 5;
               const uint32_t place =
                   placed + s_pre[wd] + __popc(s_keys[wd] & ((1u << (off & 31u)) - 1u));
-              if (place < q1) ordenado[s + place] = v[q];  // < len: distinct indices
+              if (place < q1) {  // < len: distinct indices
+                if (staged)
+                  s_out[place - q0] = v[q];
+                else
+                  ordenado[s + place] = v[q];
+              }
             }
           }
           placed += total;
           __syncthreads();  // this window's reads end before the next one is cleared
         }
-        if (RECS) copy_cell_records(s + q0, q1 - q0, n, ordenado, particles, reordered);
+        if (staged)
+          write_cell_from_lds(s + q0, q1 - q0, n, s_out, ordenado, particles, reordered, RECS);
+        else if (RECS)
+          copy_cell_records(s + q0, q1 - q0, n, ordenado, particles, reordered);
         continue;
       }
       uint32_t L = 1;
@@ -445,7 +493,7 @@ __global__ __launch_bounds__(kSortBlock) void sort_long_cells_kernel(
   uint32_t count = *long_count;
   if (count > long_cap) count = long_cap;
   sort_long_cells<RECS, false>(inicios, celdaDe, n, long_list, count, blockIdx.x, gridDim.x, nullptr, ordenado,
-                               particles, reordered, s_keys, s_pre, s_tab, s_wave);
+                               particles, reordered, s_keys, s_pre, s_tab, s_wave, nullptr);
 }
 
 // Stable mode on the tile paths: the one pass over the cells the tile
@@ -475,11 +523,12 @@ __global__ __launch_bounds__(kSortBlock) void fix_cells_kernel(
   __shared__ uint16_t s_pre[kLdsSort];
   __shared__ uint32_t s_tab[kLdsSort / 64];
   __shared__ uint32_t s_wave[kWaves];
+  __shared__ uint32_t s_out[kOutStage];  // a long cell's ordered places before they are written
   if (blockIdx.x < long_blocks) {
     uint32_t count = fl.counts()[1];
     if (count > fl.long_cap) count = fl.long_cap;
     sort_long_cells<RECS, true>(inicios, celdaDe, n, fl.lng(), count, blockIdx.x, long_blocks, fl.idx(),
-                                ordenado, particles, reordered, s_keys, s_pre, s_tab, s_wave);
+                                ordenado, particles, reordered, s_keys, s_pre, s_tab, s_wave, s_out);
     return;
   }
   const uint32_t lane = threadIdx.x & 63u;
@@ -493,80 +542,106 @@ __global__ __launch_bounds__(kSortBlock) void fix_cells_kernel(
     const uint32_t a = inicios[c], e = inicios[c + 1];
     return (e > a && e <= n && e - a <= kRankSortMax) ? make_uint2(a, e - a) : make_uint2(0u, 0u);
   };
-  const uint32_t role_thread = (blockIdx.x - long_blocks) * kSortBlock + threadIdx.x;
-  const uint32_t role_threads = (gridDim.x - long_blocks) * kSortBlock;
-  // groups of 16 lanes: cells of up to kSmallSort
+  // The role's workgroups take the list entries in turn (entry k to
+  // workgroup k mod role_wgs), a batch of kSortBlock of them at a time: every
+  // thread reads one entry's slice into an LDS table (one round of loads for
+  // the whole batch), the longer cells are gathered into a second table, and
+  // then the groups take the short cells and the waves, one at a time from
+  // an LDS counter, the longer ones, so that a wave's work follows the cells'
+  // sizes rather than the order of the list.
+  const uint32_t role_wg = blockIdx.x - long_blocks, role_wgs = gridDim.x - long_blocks;
+  uint2* s_cells = reinterpret_cast<uint2*>(s_keys + kWaves * kRankSortMax);  // kSortBlock slices
+  uint32_t* s_med = s_keys + kWaves * kRankSortMax + 2u * kSortBlock;         // the batch's longer cells
+  static_assert(kWaves * kRankSortMax + 3u * kSortBlock <= kLdsSort, "the batch tables fit beside the slices");
   const uint32_t gl = threadIdx.x & 15u;
-  for (uint32_t k = role_thread >> 4; k < count; k += role_threads >> 4) {  // uniform across the group
-    const uint2 sl = listed(k);
-    if (sl.y < 2u || sl.y > kSmallSort) continue;
-    const bool has = gl < sl.y;
-    const uint32_t mine = has ? ordenado[sl.x + gl] : 0xFFFFFFFFu;  // all ones: no index reaches it
-    uint4 ra = make_uint4(0u, 0u, 0u, 0u), rb = ra;
-    if (RECS && has) {
-      ra = reordered[2ull * (sl.x + gl)];
-      rb = reordered[2ull * (sl.x + gl) + 1u];
+  for (uint64_t b0 = 0; role_wg + b0 * role_wgs < count; b0 += kSortBlock) {  // uniform
+    __syncthreads();  // the previous batch's tables are read
+    if (threadIdx.x == 0) {
+      s_tab[0] = 0u;  // longer cells in the batch
+      s_tab[1] = 0u;  // the next of them to take
     }
-    __builtin_amdgcn_s_waitcnt(kWaitLoadsAndStores);  // every entry read before any is written back
-    uint32_t rank = 0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) rank += (static_cast<uint32_t>(__shfl(static_cast<int>(mine), i, 16)) < mine) ? 1u : 0u;
-    if (has) {
-      ordenado[sl.x + rank] = mine;
-      if (RECS) {
-        reordered[2ull * (sl.x + rank)] = ra;
-        reordered[2ull * (sl.x + rank) + 1u] = rb;
+    __syncthreads();
+    const uint64_t kk = role_wg + (b0 + threadIdx.x) * role_wgs;
+    const uint2 mine_cell = (kk < count) ? listed(static_cast<uint32_t>(kk)) : make_uint2(0u, 0u);
+    s_cells[threadIdx.x] = mine_cell;
+    if (mine_cell.y > kSmallSort) s_med[atomicAdd(&s_tab[0], 1u)] = threadIdx.x;
+    __syncthreads();
+    // groups of 16 lanes: the batch's cells of up to kSmallSort
+    for (uint32_t ci = threadIdx.x >> 4; ci < kSortBlock; ci += kSortBlock / 16u) {  // uniform across the group
+      const uint2 sl = s_cells[ci];
+      if (sl.y < 2u || sl.y > kSmallSort) continue;
+      const bool has = gl < sl.y;
+      const uint32_t mine = has ? ordenado[sl.x + gl] : 0xFFFFFFFFu;  // all ones: no index reaches it
+      uint4 ra = make_uint4(0u, 0u, 0u, 0u), rb = ra;
+      if (RECS && has) {
+        ra = reordered[2ull * (sl.x + gl)];
+        rb = reordered[2ull * (sl.x + gl) + 1u];
       }
-    }
-  }
-  // whole waves: cells of kSmallSort + 1 .. kRankSortMax
-  for (uint32_t k = role_thread >> 6; k < count; k += role_threads >> 6) {  // uniform across the wave
-    const uint2 sl = listed(k);
-    if (sl.y <= kSmallSort) continue;
-    const uint32_t cs = sl.x, cl = sl.y, cl4 = (cl + 3u) & ~3u;
-    uint32_t mine[kWaveEntries];
-    uint4 ra[kWaveEntries], rb[kWaveEntries];
+      __builtin_amdgcn_s_waitcnt(kWaitLoadsAndStores);  // every entry read before any is written back
+      uint32_t rank = 0;
 #pragma unroll
-    for (uint32_t g = 0; g < kWaveEntries; ++g) {
-      const uint32_t q = g * 64u + lane;
-      mine[g] = (q < cl) ? ordenado[cs + q] : 0xFFFFFFFFu;  // all ones pads the slice: no index reaches it
-      ra[g] = rb[g] = make_uint4(0u, 0u, 0u, 0u);
-      if (RECS && q < cl) {
-        ra[g] = reordered[2ull * (cs + q)];
-        rb[g] = reordered[2ull * (cs + q) + 1u];
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(kWaitLoadsAndStores);  // every entry read before any is written back
-#pragma unroll
-    for (uint32_t g = 0; g < kWaveEntries; ++g)
-      if (g * 64u + lane < cl4) slice[g * 64u + lane] = mine[g];
-    // a wave's LDS accesses complete in order: the slice is whole for
-    // every lane after this point
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-    for (uint32_t g = 0; g < kWaveEntries; ++g) {
-      const uint32_t q = g * 64u + lane;
-      if (g * 64u < cl) {  // uniform across the wave
-        uint32_t rank = 0;
-        for (uint32_t j = 0; j < cl4; j += 4u) {  // the same address for every lane
-          const uint4 w4 = *reinterpret_cast<const uint4*>(slice + j);
-          rank += (w4.x < mine[g] ? 1u : 0u) + (w4.y < mine[g] ? 1u : 0u) + (w4.z < mine[g] ? 1u : 0u) +
-                  (w4.w < mine[g] ? 1u : 0u);
+      for (int i = 0; i < 16; ++i) rank += (static_cast<uint32_t>(__shfl(static_cast<int>(mine), i, 16)) < mine) ? 1u : 0u;
+      if (has) {
+        ordenado[sl.x + rank] = mine;
+        if (RECS) {
+          reordered[2ull * (sl.x + rank)] = ra;
+          reordered[2ull * (sl.x + rank) + 1u] = rb;
         }
-        if (q < cl) {
-          ordenado[cs + rank] = mine[g];
-          if (RECS) {
-            reordered[2ull * (cs + rank)] = ra[g];
-            reordered[2ull * (cs + rank) + 1u] = rb[g];
+      }
+    }
+    // whole waves: the batch's cells of kSmallSort + 1 .. kRankSortMax
+    const uint32_t nmed = s_tab[0];
+    for (;;) {  // uniform across the wave
+      uint32_t j = 0;
+      if (lane == 0u) j = atomicAdd(&s_tab[1], 1u);
+      j = static_cast<uint32_t>(__shfl(static_cast<int>(j), 0));
+      if (j >= nmed) break;
+      const uint2 sl = s_cells[s_med[j]];
+      const uint32_t cs = sl.x, cl = sl.y, cl4 = (cl + 3u) & ~3u;
+      uint32_t mine[kWaveEntries];
+      uint4 ra[kWaveEntries], rb[kWaveEntries];
+#pragma unroll
+      for (uint32_t g = 0; g < kWaveEntries; ++g) {
+        const uint32_t q = g * 64u + lane;
+        mine[g] = (q < cl) ? ordenado[cs + q] : 0xFFFFFFFFu;  // all ones pads the slice: no index reaches it
+        ra[g] = rb[g] = make_uint4(0u, 0u, 0u, 0u);
+        if (RECS && q < cl) {
+          ra[g] = reordered[2ull * (cs + q)];
+          rb[g] = reordered[2ull * (cs + q) + 1u];
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitLoadsAndStores);  // every entry read before any is written back
+#pragma unroll
+      for (uint32_t g = 0; g < kWaveEntries; ++g)
+        if (g * 64u + lane < cl4) slice[g * 64u + lane] = mine[g];
+      // a wave's LDS accesses complete in order: the slice is whole for
+      // every lane after this point
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (uint32_t g = 0; g < kWaveEntries; ++g) {
+        const uint32_t q = g * 64u + lane;
+        if (g * 64u < cl) {  // uniform across the wave
+          uint32_t rank = 0;
+          for (uint32_t j = 0; j < cl4; j += 4u) {  // the same address for every lane
+            const uint4 w4 = *reinterpret_cast<const uint4*>(slice + j);
+            rank += (w4.x < mine[g] ? 1u : 0u) + (w4.y < mine[g] ? 1u : 0u) + (w4.z < mine[g] ? 1u : 0u) +
+                    (w4.w < mine[g] ? 1u : 0u);
+          }
+          if (q < cl) {
+            ordenado[cs + rank] = mine[g];
+            if (RECS) {
+              reordered[2ull * (cs + rank)] = ra[g];
+              reordered[2ull * (cs + rank) + 1u] = rb[g];
+            }
           }
         }
       }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();  // every read of the slice before the next cell's writes
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();  // every read of the slice before the next cell's writes
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 }
 
