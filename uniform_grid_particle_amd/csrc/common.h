@@ -63,8 +63,10 @@ struct FixLists {
 // claims one of kMaxSlots slots as soon as it knows its count; while it
 // counts the tile it writes the chunk-array position of every particle of
 // the tile, in the tile's own order, into the tile's places of a source
-// list (n words); after the scan it leaves one cursor per cell in the slot
-// (its next free tile-local place) and marks the slot ready. The tile's
+// list (n words) -- or, when every chunk run of the tile is short, it
+// leaves the tile's run table in the slot instead, from which a round
+// rebuilds those positions; after the scan it leaves one cursor per cell in
+// the slot (its next free tile-local place) and marks the slot ready. The tile's
 // particles are then scattered in rounds of kRound, each taken from the
 // slot's ticket by the owner or by any other tile's workgroup that saw a
 // claimed slot before its own stores. A workgroup waits only for a slot that
@@ -73,8 +75,8 @@ struct FixLists {
 //     [0] slots claimed; for slot s: [kReadyWord + s] ready (0/1),
 //     [kTicketWord + s] next round to hand out, [kRoundsWord + s] rounds,
 //     [kStartWord + s] the tile's first place, [kCountWord + s] its count,
-//     [kTileWord + s] the tile
-//   slot s: one cursor per cell of a tile
+//     [kTileWord + s] the tile (| kRunTableBit: the run table holds the sources)
+//   slot s: one cursor per cell of a tile, then the run table (kQueueRunWords)
 constexpr uint32_t kRound = 4096;
 constexpr uint32_t kMaxSlots = 64;
 constexpr uint32_t kReadyWord = 64;
@@ -87,14 +89,22 @@ constexpr uint32_t kQueueHeader = kTileWord + kMaxSlots;
 // chunk_sort's index words on the staged path: (tile-local cell << kIdxBits)
 // | index inside the chunk (chunks of at most 2^kIdxBits particles)
 constexpr uint32_t kIdxBits = 11;
+// A slot also holds a run table (kQueueRunWords words after its cursors):
+// the tile-local start of each chunk's run, then where each run starts in
+// the chunk arrays, written instead of the source list when every run of
+// the tile is short (the rounds rebuild their sources from it).
+constexpr uint32_t kQueueRunWords = 2048;
+constexpr uint32_t kRunTableBit = 0x80000000u;  // in a slot's tile word: its rounds use the run table
 struct TileQueue {
   uint32_t* base;      // nullptr: no sharing (single-tile path)
   uint32_t* sources;   // n words: chunk-array positions of shared tiles' particles
-  uint32_t slot_words; // cursors per slot (the tile size)
+  uint32_t slot_words; // words per slot: one cursor per cell of a tile, then the run table
+  uint32_t run_off;    // where the run table starts in a slot (the tile size)
   __device__ __forceinline__ uint32_t* hdr() const { return base; }
   __device__ __forceinline__ uint32_t* cursors(uint32_t s) const {
     return base + kQueueHeader + static_cast<size_t>(s) * slot_words;
   }
+  __device__ __forceinline__ uint32_t* runs(uint32_t s) const { return cursors(s) + run_off; }
 };
 
 struct GridParams {

@@ -250,6 +250,7 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
   static_assert(2 * WIN * 4 >= kStagedCap, "the source map (and, stable, every index) fits in the staging buffer");
   static_assert(kRound % NT == 0 && kRound <= kStagedCap, "a shared round is whole particles per thread");
   static_assert(SHIFT <= 16, "tile-local cells and round ranks share a word");
+  static_assert(2 * kStagedMaxChunks <= kQueueRunWords, "a slot's run table holds every chunk's run");
   __shared__ uint32_t s_cnt[kTileCells];
   __shared__ uint32_t s_dst[kStagedMaxChunks];  // tile-local start of each chunk's run
   __shared__ uint32_t s_src[kStagedMaxChunks];  // where that run starts in the chunk array
@@ -500,22 +501,54 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
   // touches takes a block of places from the slot's cursor with one atomic,
   // and every particle goes to its cell's block plus its rank.
   auto scatter_round = [&](uint32_t slot, uint32_t round, uint32_t wbs, uint32_t wcount,
-                           uint32_t wtile) __attribute__((always_inline)) {
+                           uint32_t wtile, bool by_runs) __attribute__((always_inline)) {
     const uint32_t base = round * kRound;
     if (base >= wcount) return;  // uniform
     const uint32_t len = (wcount - base < kRound) ? wcount - base : kRound;
     const uint32_t rcell0 = wtile << SHIFT;
     const uint32_t rtc = (cells - rcell0 < kTileCells) ? cells - rcell0 : kTileCells;
     uint32_t* cur = q.cursors(slot);
-    __syncthreads();  // the previous use of s_cnt is over
+    __syncthreads();  // the previous use of s_cnt (and of s_dst, s_src, s_map) is over
     for (uint32_t j = threadIdx.x; j < kTileCells; j += NT) s_cnt[j] = 0u;
     uint32_t src[kRoundPer], word[kRoundPer], lr[kRoundPer], v[8][kRoundPer];
+    if (by_runs) {  // uniform
+      // the slot's run table replaces this workgroup's own (its tile is
+      // done): every run is short, so each thread expands its own chunk's
+      // run over the round's window
+      const uint32_t* rt = q.runs(slot);
 #pragma unroll
-    for (uint32_t k = 0; k < kRoundPer; ++k) {
-      const uint32_t j = threadIdx.x + k * NT;
-      const size_t pos = static_cast<size_t>(wbs) + base + j;
-      const uint32_t m = (j < len && pos < n) ? shared_load(q.sources + pos) : 0u;
-      src[k] = (m < n) ? m : n - 1u;  // n >= 1: a tile holds particles
+      for (uint32_t k = 0; k < kChunksPerThread; ++k) {
+        const uint32_t c = threadIdx.x * kChunksPerThread + k;
+        if (c < nchunks) {
+          s_dst[c] = shared_load(rt + c);
+          s_src[c] = shared_load(rt + kStagedMaxChunks + c);
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (uint32_t k = 0; k < kChunksPerThread; ++k) {
+        const uint32_t c = threadIdx.x * kChunksPerThread + k;
+        const uint32_t d0 = (c < nchunks) ? s_dst[c] : wcount;
+        const uint32_t d1 = (c + 1u < nchunks) ? s_dst[c + 1u] : wcount;
+        r[k].x = (d1 > d0) ? d1 - d0 : 0u;
+      }
+      short_runs = true;
+      build_map(base, len);
+      __syncthreads();
+#pragma unroll
+      for (uint32_t k = 0; k < kRoundPer; ++k) {
+        const uint32_t j = threadIdx.x + k * NT;
+        const uint32_t m = (j < len) ? s_map[j] : 0u;
+        src[k] = (m < n) ? m : n - 1u;  // n >= 1: a tile holds particles
+      }
+    } else {
+#pragma unroll
+      for (uint32_t k = 0; k < kRoundPer; ++k) {
+        const uint32_t j = threadIdx.x + k * NT;
+        const size_t pos = static_cast<size_t>(wbs) + base + j;
+        const uint32_t m = (j < len && pos < n) ? shared_load(q.sources + pos) : 0u;
+        src[k] = (m < n) ? m : n - 1u;  // n >= 1: a tile holds particles
+      }
     }
 #pragma unroll
     for (uint32_t k = 0; k < kRoundPer; ++k) word[k] = chunk_idx[src[k]];
@@ -634,10 +667,12 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
         }
       }
       __syncthreads();
-      const uint32_t round = s_item, wbs = s_dst[0], wcount = s_src[0], slot = s_dst[1], wtile = s_src[1];
+      const uint32_t round = s_item, wbs = s_dst[0], wcount = s_src[0], slot = s_dst[1];
+      const uint32_t wtile = s_src[1] & ~kRunTableBit;
+      const bool by_runs = (s_src[1] & kRunTableBit) != 0u;
       if (round == 0xFFFFFFFFu) return;  // uniform
       if (wtile < ntiles && wcount <= n && wbs <= n - wcount)  // uniform checks keep it in bounds
-        scatter_round(slot, round, wbs, wcount, wtile);
+        scatter_round(slot, round, wbs, wcount, wtile, by_runs);
     }
   };
 
@@ -786,6 +821,34 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
       sidx = s_item;
     }
     const bool shared = sidx < kMaxSlots;  // uniform
+    // every run short (shuffled input): one pass, each thread counting its
+    // own chunk's run (one 16-byte load per four words, all in flight
+    // together), and the rounds rebuild their sources from the run table
+    const bool by_runs = shared && pk && short_runs && nchunks > 1u;  // uniform
+    if (by_runs) {
+      constexpr uint32_t kRunLoads = (kShortRun + 6u) / 4u;  // 16-byte loads covering a run of kShortRun
+      static_assert(kChunksPerThread == 1, "one chunk run per thread");
+      const uint32_t c = threadIdx.x;
+      const uint32_t rl = (c < nchunks) ? r[0].x : 0u;  // <= kShortRun
+      const uint32_t a = c * chunk + r[0].y;            // the run's first word
+      const uint32_t a4 = a & ~3u;
+      uint4 wv[kRunLoads];
+#pragma unroll
+      for (uint32_t m = 0; m < kRunLoads; ++m)
+        wv[m] = (rl != 0u && a4 + 4u * m < a + rl) ? reinterpret_cast<const uint4*>(chunk_idx)[a4 / 4u + m]
+                                                  : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+      for (uint32_t m = 0; m < kRunLoads; ++m) {
+        const uint32_t w0 = a4 + 4u * m;
+        const uint32_t e[4] = {wv[m].x, wv[m].y, wv[m].z, wv[m].w};
+#pragma unroll
+        for (uint32_t i = 0; i < 4; ++i) {
+          const uint32_t w = w0 + i;
+          const uint32_t loc = e[i] >> kIdxBits;
+          if (w >= a && w < a + rl && loc < tc) atomicAdd(&s_cnt[loc], 1u);
+        }
+      }
+    } else {
     // the count goes in rounds of kStagedCap particles (kStagedRegs per thread), each
     // with the source map of its window and its loads in flight together;
     // packed index words give the cells directly, else the positions are
@@ -830,6 +893,7 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
         }
       }
     }
+    }
     __syncthreads();
     const uint32_t tot = scan_tile();
     if (shared) {
@@ -839,11 +903,18 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
       // inicios follow
       uint32_t* curs = q.cursors(sidx);
       for (uint32_t j = threadIdx.x; j < tc; j += NT) shared_store(curs + j, s_cnt[j]);
+      if (by_runs) {  // the run table: tile-local starts, then chunk-array starts
+        uint32_t* rt = q.runs(sidx);
+        for (uint32_t c = threadIdx.x; c < nchunks; c += NT) {
+          shared_store(rt + c, s_dst[c]);
+          shared_store(rt + kStagedMaxChunks + c, s_src[c]);
+        }
+      }
       if (threadIdx.x == 0) {
         shared_store(q.hdr() + kRoundsWord + sidx, (count + kRound - 1u) / kRound);
         shared_store(q.hdr() + kStartWord + sidx, bs);
         shared_store(q.hdr() + kCountWord + sidx, count);
-        shared_store(q.hdr() + kTileWord + sidx, t);
+        shared_store(q.hdr() + kTileWord + sidx, t | (by_runs ? kRunTableBit : 0u));
       }
       __builtin_amdgcn_s_waitcnt(kWaitLoadsAndStores);
       __syncthreads();

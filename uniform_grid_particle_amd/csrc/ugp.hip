@@ -149,12 +149,14 @@ uint32_t bucket_shift(uint64_t n, uint64_t cells, uint32_t lg) {
   return (s < fewest) ? fewest : s;
 }
 
-// The shared scatter of a tile path: the queue header, kMaxSlots cursor
-// arrays of one tile each, and the source list (n words).
+// The shared scatter of a tile path: the queue header, kMaxSlots slots of
+// one cursor per cell of a tile plus a run table, and the source list (n
+// words).
 size_t plan_queue(Plan* p, uint32_t n, size_t off) {
   p->queue = true;
   p->off_queue = off;
-  off = align_up(off + (static_cast<size_t>(kQueueHeader) + static_cast<size_t>(kMaxSlots) * (1u << p->tile_shift)) * 4u,
+  off = align_up(off + (static_cast<size_t>(kQueueHeader) +
+                        static_cast<size_t>(kMaxSlots) * ((1u << p->tile_shift) + kQueueRunWords)) * 4u,
                  256);
   p->off_sources = off;
   return align_up(off + static_cast<size_t>(n) * 4u, 256);
@@ -444,7 +446,8 @@ TileQueue tile_queue_of(const BuildArgs& a, const Plan& p) {
   if (!p.queue) return q;
   q.base = reinterpret_cast<uint32_t*>(static_cast<char*>(a.workspace) + p.off_queue);
   q.sources = reinterpret_cast<uint32_t*>(static_cast<char*>(a.workspace) + p.off_sources);
-  q.slot_words = 1u << p.tile_shift;
+  q.slot_words = (1u << p.tile_shift) + kQueueRunWords;
+  q.run_off = 1u << p.tile_shift;
   return q;
 }
 
