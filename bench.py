@@ -26,6 +26,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import re
 import os
 import statistics
 import sys
@@ -80,13 +81,22 @@ def alg_bytes(n: int, c: int, mode: str) -> dict:
     }
 
 
+def _code_only(text: str) -> str:
+    """A source file without its comments and blank lines (the sources hold no
+    string literal with a comment marker in it)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*", "", line).rstrip() for line in text.splitlines())
+    return "\n".join(line for line in lines if line.strip())
+
+
 def source_digest() -> str:
-    """Digest of every kernel source file (traffic figures go stale with it)."""
+    """Digest of the code of every kernel source file, comments left out
+    (traffic figures go stale with the code, not with its comments)."""
     h = hashlib.sha256()
     for name in sorted(os.listdir(KERNEL_DIR)):
         if name.endswith((".hip", ".h")):
-            with open(os.path.join(KERNEL_DIR, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+            with open(os.path.join(KERNEL_DIR, name), encoding="utf-8") as f:
+                h.update(name.encode() + b"\0" + _code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

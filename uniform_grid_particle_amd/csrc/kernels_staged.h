@@ -25,9 +25,12 @@
 //               the histogram (inicios), and writes ordenado and reordered
 //               at start + rank through an LDS staging window so the stores
 //               are contiguous. A tile with more particles than the
-//               registers hold (8192) goes in rounds of 8192: one counting
-//               pass, then a pass that takes slots from LDS cursors and
-//               writes them directly.
+//               registers hold (8192) is counted by its workgroup (the
+//               owner) and scattered in rounds of 4096 shared with every
+//               other workgroup through a queue of 64 slots (TileQueue),
+//               each round taking places from the slot's per-cell cursors
+//               with device atomics; past 64 such tiles, a tile scatters
+//               alone in rounds of 8192 from LDS cursors.
 //
 // The tile kernel is compiled per tile shift (4..14) and per variant:
 // records moved or not, overflow diagnostics, stable order, single tile.
@@ -496,10 +499,11 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
   };
 
   // One shared scatter round: positions [base, base + len) of a shared
-  // tile's own order (its sources from the source list), counted per cell
-  // in LDS (rank = the value the LDS atomic returns); every cell the round
-  // touches takes a block of places from the slot's cursor with one atomic,
-  // and every particle goes to its cell's block plus its rank.
+  // tile's own order (its sources from the source list, or rebuilt from the
+  // slot's run table), counted per cell in LDS (rank = the value the LDS
+  // atomic returns); every cell the round touches takes a block of places
+  // from the slot's cursor with one atomic, and every particle goes to its
+  // cell's block plus its rank.
   auto scatter_round = [&](uint32_t slot, uint32_t round, uint32_t wbs, uint32_t wcount,
                            uint32_t wtile, bool by_runs) __attribute__((always_inline)) {
     const uint32_t base = round * kRound;
