@@ -102,6 +102,38 @@ def test_contention_presorted_input(ugp, orc):
         assert_parity(wl2, run_gpu(ugp, wl2, mode), ref, mode)
 
 
+def test_contention_mixed_run_lengths(ugp, orc):
+    """Tiles past the staging capacity of both kinds in one build: two dense
+    clusters whose records come first, sorted by cell (every chunk holds long
+    runs of their tiles: those tiles publish a source list), then a shuffled
+    contention workload (its cluster tiles get at most 64 particles from each
+    chunk: they publish a run table instead)."""
+    print("[parity] contention with mixed run lengths", flush=True)
+    b = W.make_contention(n=600_000, d=128, seed=21, hot=5_000, clusters=3, per_cluster=100_000, outside=10_000,
+                          name="mixed_b")
+    rng = np.random.Generator(np.random.PCG64(2121))
+    centres = np.array([[3.0, -3.0, 2.5], [-3.5, 3.0, -2.0]])
+    pos = (centres[:, None, :] + 0.25 * rng.standard_normal((2, 60_000, 3))).reshape(-1, 3)
+    a = np.empty((pos.shape[0], 8), np.float32)
+    a[:, :3] = pos.astype(np.float32)
+    a[:, 3] = 1.0 + 3.0 * rng.random(pos.shape[0])
+    a[:, 4:7] = rng.standard_normal((pos.shape[0], 3)).astype(np.float32)
+    a[:, 7] = 0.5 + rng.random(pos.shape[0])
+    c = np.clip(np.floor((pos - b.origin.astype(np.float64)) / float(b.cell_size)).astype(np.int64), 0, 127)
+    a = a[np.argsort(c[:, 0] + 128 * (c[:, 1] + 128 * c[:, 2]), kind="stable")]
+    wl = W.Workload("mixed_runs", np.ascontiguousarray(np.concatenate([a, b.particles], axis=0)), b.origin,
+                    b.cell_size, b.dims)
+    ref = orc.grid_build(wl.particles, wl.origin, wl.cell_size, wl.dims)
+    # both kinds are there: tiles of 2^13 cells, chunks of 2048 particles
+    tile = np.asarray(ref.celdaDe, np.int64) >> 13
+    nchunks = (wl.n + 2047) // 2048
+    runs = np.bincount((np.arange(wl.n) // 2048) * 256 + tile, minlength=nchunks * 256).reshape(-1, 256).max(axis=0)
+    over = np.nonzero(np.bincount(tile, minlength=256) > 8192)[0]
+    assert (runs[over] <= 64).sum() >= 4 and (runs[over] > 64).sum() >= 4, runs[over]
+    for mode in ("atomic", "stable"):
+        assert_parity(wl, run_gpu(ugp, wl, mode), ref, mode)
+
+
 @pytest.mark.parametrize("h,o,d", [(0.625, -5.0, 16), (0.078125, -5.0, 128), (0.0390625, -5.0, 256),
                                    (0.1, -3.0, 64), (0.013, -0.5, 200), (1.0 / 3.0, -2.0, 30)])
 def test_cell_faces(ugp, orc, h, o, d):
