@@ -372,6 +372,54 @@ def neighbor_bench(ugp, torch, dev, evict, stream, reps: int = 5) -> dict:
     return res
 
 
+def other_workloads_bench(ugp, torch, dev, evict, stream, steps: int = 20, warmup: int = 3) -> dict:
+    """The other workloads of the build, each timed like the headline: warm-up
+    builds, then `steps` cold builds (the same 1 GiB eviction before each,
+    outside the per-build events), median with p10/p90. The method-level byte
+    model (116 N + 16 C + 4) gives each its fraction of the 8 TB/s peak."""
+    import workloads
+
+    res = {}
+    for name, mode in (("tiny", "atomic"), ("sparse", "atomic"), ("contention", "atomic"),
+                       ("contention", "stable"), ("large", "atomic")):
+        wl = workloads.make_config(name)
+        dims = [int(v) for v in wl.dims]
+        origin, h = [float(v) for v in wl.origin], float(wl.cell_size)
+        stable = mode == "stable"
+        parts = torch.from_numpy(wl.particles).to(dev)
+        out, ws = ugp.alloc_outputs(wl.n, dims, dev, ugp.FLAG_STABLE if stable else 0)
+
+        def build():
+            ugp.grid_build(parts, origin, h, dims, stable=stable, out=out, workspace=ws)
+
+        for _ in range(warmup):
+            build()
+        torch.cuda.synchronize()
+        ini = ugp.as_u32_numpy(out.inicios)
+        if int(ini[-1]) != wl.n:
+            raise RuntimeError(f"{name}: inicios[C] != N after the warm-up builds")
+        t = []
+        for _ in range(steps):
+            evict()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            build()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t.append(1e3 * e0.elapsed_time(e1))
+        med = statistics.median(t)
+        model = 116 * wl.n + 16 * wl.cells + 4
+        res[f"{name}_{mode}"] = {
+            "workload": WORKLOAD_NAMES[name], "mode": mode, "us": round(med, 2), "us_p10_p90": _p10_p90(t),
+            "particles_per_s": wl.n / (med * 1e-6), "hbm_frac_e2e": model / (med * 1e-6) / (HBM_PEAK_GBS * 1e9)}
+        del parts, out, ws
+        torch.cuda.empty_cache()
+    res["note"] = ("cold builds (1 GiB read-only eviction before each, outside the per-build events), median of "
+                   f"{steps} after {warmup} warm-up builds; hbm_frac_e2e from the byte model 116 N + 16 C + 4")
+    return res
+
+
 def reorder_policy_bench(ugp, torch, dev, evict, stream, reps: int = 5) -> dict:
     """Reorder policies of the reorder page on MI355X: (a) hot kinematics and
     cold appearance (32 bytes each) gathered with one index in one kernel vs
@@ -540,7 +588,8 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default="baseline", choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--mode", default="atomic", choices=["atomic", "gather", "stable"])
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle timing (0 = skip)")
-    ap.add_argument("--no-neighbors", action="store_true", help="skip the neighbour-query section")
+    ap.add_argument("--no-neighbors", action="store_true",
+                    help="skip the neighbour-query, reorder-policy and other-workload sections")
     ap.add_argument("--presorted", action="store_true",
                     help="time the workload's records already in cell order (the build's own reordered "
                          "output of one untimed build), the secondary variant of the contention config")
@@ -817,6 +866,8 @@ def main(argv=None) -> int:
     if not args.no_neighbors:
         result["neighbor_query"] = neighbor_bench(ugp, torch, dev, evict, stream)
         result["reorder_policy"] = reorder_policy_bench(ugp, torch, dev, evict, stream)
+        if args.workload == "baseline" and args.mode == "atomic" and not args.presorted:
+            result["other_workloads"] = other_workloads_bench(ugp, torch, dev, evict, stream)
     result["next_rows"] = next_rows_summary(result, wl, with_oracle=args.cpu_budget > 0)
     if args.cpu_budget > 0 and int(os.environ.get("RANK", "0")) == 0:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
