@@ -51,6 +51,29 @@ def test_bench_json_line():
 
 
 @pytest.mark.gpu
+def test_other_workloads_section():
+    """The default run's timings of the other workloads: one entry per
+    workload and mode, each a positive median with its spread."""
+    print("[bench] other workloads, 2 cold builds each", flush=True)
+    sys.path.insert(0, ROOT)
+    import torch
+
+    import bench
+    import uniform_grid_particle_amd as ugp
+
+    ugp.load_library()
+    dev = torch.device("cuda:0")
+    flush = torch.ones(1 << 26, dtype=torch.float32, device=dev)
+    res = bench.other_workloads_bench(ugp, torch, dev, lambda: torch.sum(flush), torch.cuda.current_stream(dev),
+                                      steps=2, warmup=1)
+    keys = {"tiny_atomic", "sparse_atomic", "contention_atomic", "contention_stable", "large_atomic"}
+    assert keys <= set(res), sorted(res)
+    for k in keys:
+        v = res[k]
+        assert v["us"] > 0 and 0 < v["hbm_frac_e2e"] < 1 and len(v["us_p10_p90"]) == 2, (k, v)
+
+
+@pytest.mark.gpu
 def test_smoke_entry_point():
     sys.path.insert(0, ROOT)
     import __graft_entry__
