@@ -134,6 +134,67 @@ def test_contention_mixed_run_lengths(ugp, orc):
         assert_parity(wl, run_gpu(ugp, wl, mode), ref, mode)
 
 
+def _row_workload(conteos, seed, name):
+    """Particles at the centres of a 1-D row of cells (cell c gets conteos[c]),
+    shuffled; vida holds the cell and masa the place before the shuffle."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    c = np.repeat(np.arange(conteos.size, dtype=np.int64), conteos)
+    parts = np.zeros((c.size, 8), np.float32)
+    parts[:, 0] = (c + 0.5).astype(np.float32)
+    parts[:, 1:3] = 0.5
+    parts[:, 3] = c.astype(np.float32)
+    parts[:, 7] = np.arange(c.size, dtype=np.float32)
+    parts = np.ascontiguousarray(parts[rng.permutation(c.size)])
+    return W.Workload(name, parts, np.zeros(3, np.float32), np.float32(1.0),
+                      np.array([conteos.size, 1, 1], np.uint32))
+
+
+def test_hot_tiles_cell_lengths(ugp, orc):
+    """Tiles past the staging capacity (scattered in shared rounds), every
+    chunk run short, with their longest cells at lengths of interest: 4096
+    and 4097 particles, several cells longer than the in-LDS stable ranking
+    (257 to 1000, one of them the tile's last cell), a tile of exactly
+    16,100 particles whose last cell holds 150, and one of 16,402 particles
+    in cells of exactly 10 (one of 12)."""
+    print("[parity] hot tiles with long cells", flush=True)
+    cells, tile = 1 << 21, 8192  # 256 tiles of 2^13 cells
+    rng = np.random.Generator(np.random.PCG64(4242))
+    conteos = np.bincount(rng.integers(0, cells, 900_000), minlength=cells).astype(np.int64)
+
+    def spread(t, m):
+        conteos[t * tile:(t + 1) * tile] += np.bincount(rng.integers(0, tile, m), minlength=tile)
+
+    spread(10, 6000)
+    conteos[10 * tile + 5000] += 4096 - conteos[10 * tile + 5000]
+    spread(20, 6000)
+    conteos[20 * tile + 77] += 4097 - conteos[20 * tile + 77]
+    spread(30, 8000)
+    for j, m in ((100, 1000), (2000, 300), (4000, 257), (6000, 256), (8191, 700)):
+        conteos[30 * tile + j] = m
+    t4 = conteos[40 * tile:41 * tile]
+    t4[:] = np.bincount(rng.integers(0, tile - 2, 16100 - 342), minlength=tile)
+    t4[3000] = 192
+    t4[tile - 1] = 150
+    t4[1] += 16100 - t4.sum()
+    t5 = conteos[50 * tile:51 * tile]
+    t5[:] = 0
+    t5[:1640] = 10
+    t5[1639] = 12
+    wl = _row_workload(conteos, 4243, "hot_tiles")
+    ref = orc.grid_build(wl.particles, wl.origin, wl.cell_size, wl.dims)
+    # the tiles are what they are meant to be: past the capacity, every
+    # chunk run short (chunks of 2048), longest cells as built
+    tiles = np.asarray(ref.celdaDe, np.int64) >> 13
+    nchunks = (wl.n + 2047) // 2048
+    runs = np.bincount((np.arange(wl.n) // 2048) * 256 + tiles, minlength=nchunks * 256).reshape(-1, 256).max(axis=0)
+    per_tile = conteos.reshape(256, tile)
+    for t, longest in ((10, 4096), (20, 4097), (30, 1000), (40, 192), (50, 12)):
+        assert per_tile[t].sum() > 8192 and runs[t] <= 64 and per_tile[t].max() == longest, (t, runs[t])
+    assert per_tile[40].sum() == 16100 and per_tile[50].sum() == 16402
+    for mode in ("atomic", "stable"):
+        assert_parity(wl, run_gpu(ugp, wl, mode), ref, mode)
+
+
 @pytest.mark.parametrize("h,o,d", [(0.625, -5.0, 16), (0.078125, -5.0, 128), (0.0390625, -5.0, 256),
                                    (0.1, -3.0, 64), (0.013, -0.5, 200), (1.0 / 3.0, -2.0, 30)])
 def test_cell_faces(ugp, orc, h, o, d):
