@@ -165,6 +165,24 @@ __device__ __forceinline__ void store_stream(uint4* p, uint4 v) {
   __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(p));
 }
 __device__ __forceinline__ uint32_t load_stream(const uint32_t* p) { return __builtin_nontemporal_load(p); }
+
+// Stores written through the L2 to memory (cache policy sc1: device scope),
+// 16 bytes at a time through a buffer resource over an output array of
+// `bytes` bytes (the hardware drops a store past them). Used for outputs the
+// build never reads again (conteos, inicios): they leave the L2 while the
+// kernel runs rather than in the write-back of dirty lines at its end, which
+// follows its last store. Measured on MI355X: Sparse 21.9 -> 20.7 us, Large
+// 860 -> 843 us, Baseline unchanged; the records, written last, lose more
+// than they gain this way.
+constexpr int kStoreThrough = 16;  // the sc1 bit of a buffer store's cache policy
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t output_rsrc(void* p, uint32_t bytes) {
+  // dword 3: 32-bit data format, no swizzle, no thread-id offset
+  return __builtin_amdgcn_make_buffer_rsrc(p, static_cast<short>(0), static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ void store_through(__amdgpu_buffer_rsrc_t r, uint32_t offset, uint4 v) {
+  const u32x4_t w = {v.x, v.y, v.z, v.w};
+  __builtin_amdgcn_raw_buffer_store_b128(w, r, static_cast<int>(offset), 0, kStoreThrough);
+}
 __device__ __forceinline__ void store_stream(uint32_t* p, uint32_t v) { __builtin_nontemporal_store(v, p); }
 
 // Inclusive prefix sum across the 64 lanes of a wave, with DPP lane moves

@@ -416,18 +416,22 @@ __global__ __launch_bounds__(NT) void staged_cells_kernel(
 
   // conteos and inicios out, from the starts: a cell's count is the next
   // start minus its own. Lane-contiguous 16-byte stores (tiles start at
-  // multiples of 16 cells). DIAG: the same counts feed the overflow
-  // diagnostics (one more barrier, after which thread 0 publishes).
+  // multiples of 16 cells), written through to memory (store_through; the
+  // paths using this kernel have at most 2^26 keys, so byte offsets fit 32
+  // bits). DIAG: the same counts feed the overflow diagnostics (one more
+  // barrier, after which thread 0 publishes).
   auto write_counts_starts = [&](uint32_t tot) __attribute__((always_inline)) {
     const uint4* s_cnt4 = reinterpret_cast<const uint4*>(s_cnt);
     const uint32_t tc4 = tc / 4;
+    const __amdgpu_buffer_rsrc_t r_conteos = output_rsrc(conteos, 4u * cells);
+    const __amdgpu_buffer_rsrc_t r_inicios = output_rsrc(inicios, 4u * cells + 4u);
     uint32_t dmax = 0, dover = 0;
     for (uint32_t k = threadIdx.x; k < tc4; k += NT) {
       const uint4 v = s_cnt4[k];
       const uint32_t next = (4 * k + 4 < kTileCells) ? s_cnt[4 * k + 4] : tot;
       const uint4 c = make_uint4(v.y - v.x, v.z - v.y, v.w - v.z, next - v.w);
-      reinterpret_cast<uint4*>(conteos + cell0)[k] = c;
-      reinterpret_cast<uint4*>(inicios + cell0)[k] = make_uint4(bs + v.x, bs + v.y, bs + v.z, bs + v.w);
+      store_through(r_conteos, 4u * (cell0 + 4u * k), c);
+      store_through(r_inicios, 4u * (cell0 + 4u * k), make_uint4(bs + v.x, bs + v.y, bs + v.z, bs + v.w));
       if (DIAG) {
         const uint32_t a = (c.x > c.y) ? c.x : c.y;
         const uint32_t b = (c.z > c.w) ? c.z : c.w;
