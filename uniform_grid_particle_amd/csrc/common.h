@@ -167,13 +167,18 @@ __device__ __forceinline__ void store_stream(uint4* p, uint4 v) {
 __device__ __forceinline__ uint32_t load_stream(const uint32_t* p) { return __builtin_nontemporal_load(p); }
 
 // Stores written through the L2 to memory (cache policy sc1: device scope),
-// 16 bytes at a time through a buffer resource over an output array of
-// `bytes` bytes (the hardware drops a store past them). Used for outputs the
-// build never reads again (conteos, inicios): they leave the L2 while the
-// kernel runs rather than in the write-back of dirty lines at its end, which
-// follows its last store. Measured on MI355X: Sparse 21.9 -> 20.7 us, Large
-// 860 -> 843 us, Baseline unchanged; the records, written last, lose more
-// than they gain this way.
+// through a buffer resource over one workgroup's own output range of `bytes`
+// bytes (the hardware drops a store past them; offsets are from the range's
+// start). A workgroup's dirty L2 lines are otherwise written back when the
+// kernel ends, after its last store: sent out while it runs, they leave that
+// write-back short. Used for the chunk kernel's chunk array when it is larger
+// than the L2 caches hold (read by the next kernel from memory in either
+// case) and the tile kernel's conteos and inicios (never read again by the
+// build). Measured on MI355X, each change
+// against the one before: the counts and starts, Sparse 21.9 -> 20.7 us and
+// Large 860 -> 843 us (Baseline unchanged); the chunk array, Baseline 37.4 ->
+// 36.5 us, Sparse 20.6 -> 20.1 us, Large 842 -> 835 us. The tile kernel's
+// records (written last) and celdaDe lose or gain nothing this way.
 constexpr int kStoreThrough = 16;  // the sc1 bit of a buffer store's cache policy
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t output_rsrc(void* p, uint32_t bytes) {
   // dword 3: 32-bit data format, no swizzle, no thread-id offset
@@ -182,6 +187,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t output_rsrc(void* p, uint32_t 
 __device__ __forceinline__ void store_through(__amdgpu_buffer_rsrc_t r, uint32_t offset, uint4 v) {
   const u32x4_t w = {v.x, v.y, v.z, v.w};
   __builtin_amdgcn_raw_buffer_store_b128(w, r, static_cast<int>(offset), 0, kStoreThrough);
+}
+__device__ __forceinline__ void store_through(__amdgpu_buffer_rsrc_t r, uint32_t offset, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, static_cast<int>(offset), 0, kStoreThrough);
 }
 __device__ __forceinline__ void store_stream(uint32_t* p, uint32_t v) { __builtin_nontemporal_store(v, p); }
 

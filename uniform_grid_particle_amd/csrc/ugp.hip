@@ -240,8 +240,6 @@ int make_plan(uint32_t n, const uint32_t dims[3], uint32_t flags, Plan* p) {
     static_assert(kStagedMaxShift + 6u + kIdxBits <= 32u, "bucket-local cells fit the packed word");
     static_assert(kBucketMaxTiles <= kMaxBuckets * 64u, "64 tiles per bucket cover every tile");
     static_assert(kMaxBuckets <= kStagedMaxTiles, "buckets fit the chunk kernel's bins");
-    static_assert((static_cast<uint64_t>(kBucketMaxTiles) << kStagedMaxShift) * 4u + 4u <= 0xFFFFFFFFull,
-                  "the tile kernel's conteos and inicios byte offsets fit 32 bits");
     p->nbuckets = static_cast<uint32_t>((cells + (1ull << p->cshift) - 1) >> p->cshift);
     p->ncoarse = blocks_for(n, kChunk);
     p->nrb = blocks_for(p->ncoarse, kRbChunks);
