@@ -23,7 +23,9 @@ constexpr uint32_t kFixLongBlocks = 32;    // on long cells (a cell of 10,000 ta
 constexpr uint32_t kFixShortBlocks = 224;  // on short cells
 
 // Gather: two lanes per record, each moving one 16-byte half, so every
-// store instruction writes a contiguous span. Indices >= n_src are skipped.
+// store instruction writes a contiguous span, with the non-temporal hint
+// (measured on MI355X: the gather of 1M records 24.9 -> 23.8 us). Indices
+// >= n_src are skipped.
 __global__ __launch_bounds__(kBlock) void gather_kernel(const uint32_t* __restrict__ idx, uint32_t n,
                                                         uint32_t n_src,
                                                         const uint4* __restrict__ src,
@@ -43,7 +45,7 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(const uint32_t* __restri
   }
 #pragma unroll
   for (int j = 0; j < kGatherItems; ++j)
-    if (ok[j]) dst[static_cast<size_t>(r[j]) * 2u + half] = v[j];
+    if (ok[j]) store_stream(dst + static_cast<size_t>(r[j]) * 2u + half, v[j]);
 }
 
 // Gather of several arrays with one index (page "Reordenar por celda y la
@@ -99,14 +101,16 @@ __global__ __launch_bounds__(kBlock) void gather_arrays_kernel(const uint32_t* _
       v0[j] = x;
     }
   }
+  // stores with the non-temporal hint (measured on MI355X: two 32-byte
+  // arrays of 1M records 50.4 -> 49.4 us)
 #pragma unroll
   for (int j = 0; j < kArrayItems; ++j) {
     if (!ok[j]) continue;
     T* d = dst + static_cast<size_t>(k[j]) * chunks + local;
     if constexpr (sizeof(T) == 16) {
-      *d = make_uint4(v0[j], v1[j], v2[j], v3[j]);
+      store_stream(d, make_uint4(v0[j], v1[j], v2[j], v3[j]));
     } else {
-      *d = v0[j];
+      store_stream(d, v0[j]);
     }
   }
 }
