@@ -97,13 +97,14 @@ __device__ __forceinline__ uint32_t tile_of_block(uint32_t b, uint32_t ntiles) {
 // rows[b*ntiles + t] = {particles of chunk b in tile t, those in tiles < t}.
 // chunk_idx[q] = (tile-local cell << kIdxBits) | index inside the chunk.
 // diag, fix_counts, queue_hdr (or nullptr): words the tile kernel
-// accumulates into, zeroed here.
+// accumulates into, zeroed here. nt_out: the chunk array's write-through
+// stores also carry the non-temporal bit (1 on the bucketed path).
 template <int CT>
 __global__ __launch_bounds__(CT) void staged_keys_kernel(
     const uint4* __restrict__ parts, uint32_t n, GridParams g, uint32_t* __restrict__ celdaDe,
     uint2* __restrict__ rows, uint32_t tile_shift, uint32_t ntiles, uint4* __restrict__ chunk_rec,
     uint32_t* __restrict__ chunk_idx, uint32_t* __restrict__ diag, uint32_t* __restrict__ fix_counts,
-    uint32_t* __restrict__ queue_hdr) {
+    uint32_t* __restrict__ queue_hdr, uint32_t nt_out) {
   constexpr int kChunkThreads = CT;
   constexpr uint32_t kChunk = CT * kChunkItems;
   constexpr uint32_t kTilesPerThread = kStagedMaxTiles / CT;  // tile bins per thread
@@ -194,9 +195,14 @@ __global__ __launch_bounds__(CT) void staged_keys_kernel(
   uint32_t* dsti = chunk_idx + base;
   if (kThrough) {
     const __amdgpu_buffer_rsrc_t r_rec = output_rsrc(dst, 32u * in_chunk);
-    for (uint32_t q = threadIdx.x; q < 2 * in_chunk; q += kChunkThreads) store_through(r_rec, 16u * q, s_rec[q]);
     const __amdgpu_buffer_rsrc_t r_idx = output_rsrc(dsti, 4u * in_chunk);
-    for (uint32_t q = threadIdx.x; q < in_chunk; q += kChunkThreads) store_through(r_idx, 4u * q, s_idx[q]);
+    if (nt_out != 0u) {  // uniform
+      for (uint32_t q = threadIdx.x; q < 2 * in_chunk; q += kChunkThreads) store_through_nt(r_rec, 16u * q, s_rec[q]);
+      for (uint32_t q = threadIdx.x; q < in_chunk; q += kChunkThreads) store_through_nt(r_idx, 4u * q, s_idx[q]);
+    } else {
+      for (uint32_t q = threadIdx.x; q < 2 * in_chunk; q += kChunkThreads) store_through(r_rec, 16u * q, s_rec[q]);
+      for (uint32_t q = threadIdx.x; q < in_chunk; q += kChunkThreads) store_through(r_idx, 4u * q, s_idx[q]);
+    }
   } else {
     for (uint32_t q = threadIdx.x; q < 2 * in_chunk; q += kChunkThreads) dst[q] = s_rec[q];
     for (uint32_t q = threadIdx.x; q < in_chunk; q += kChunkThreads) dsti[q] = s_idx[q];

@@ -581,12 +581,12 @@ void enqueue_staged(uint32_t stage, const BuildArgs& a, const Plan& p) {
         launch(staged_keys_kernel<kSmallChunkThreads>, dim3(p.nchunks), dim3(kSmallChunkThreads), 0,
                            s, reinterpret_cast<const uint4*>(a.particles), a.n, grid_params(a), a.celdaDe, rows,
                            p.tile_shift, p.ntiles, chunk_rec, chunk_idx, a.diag, fix_lists_of(a, p).base,
-                           tile_queue_of(a, p).base);
+                           tile_queue_of(a, p).base, 0u);
       else
         launch(staged_keys_kernel<kChunkThreads>, dim3(p.nchunks), dim3(kChunkThreads), 0, s,
                            reinterpret_cast<const uint4*>(a.particles), a.n, grid_params(a), a.celdaDe, rows,
                            p.tile_shift, p.ntiles, chunk_rec, chunk_idx, a.diag, fix_lists_of(a, p).base,
-                           tile_queue_of(a, p).base);
+                           tile_queue_of(a, p).base, 0u);
       break;
     case 3:
       launch_tile_sort<false>(a, p, rows, chunk_rec, chunk_idx);
@@ -619,7 +619,7 @@ void enqueue_bucketed(uint32_t stage, const BuildArgs& a, const Plan& p) {
     case 0:  // chunks sorted by bucket: the chunk kernel with buckets for tiles
       launch(staged_keys_kernel<kChunkThreads>, dim3(p.ncoarse), dim3(kChunkThreads), 0, s,
              reinterpret_cast<const uint4*>(a.particles), a.n, grid_params(a), a.celdaDe, rows1, p.cshift,
-             p.nbuckets, coarse_rec, coarse_idx, a.diag, fix_lists_of(a, p).base, tile_queue_of(a, p).base);
+             p.nbuckets, coarse_rec, coarse_idx, a.diag, fix_lists_of(a, p).base, tile_queue_of(a, p).base, 1u);
       break;
     case 1:
       launch(bucket_fine_count_kernel, dim3(p.ncount), dim3(kCountThreads), 0, s, a.celdaDe, a.n, p.tile_shift,
