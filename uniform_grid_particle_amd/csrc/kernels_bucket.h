@@ -97,13 +97,14 @@ __global__ __launch_bounds__(kCountThreads) void bucket_fine_count_kernel(
   __syncthreads();
   const uint64_t base = static_cast<uint64_t>(blockIdx.x) * kCountPer;
   const uint64_t end = (base + kCountPer < n) ? base + kCountPer : n;
+  // read once here: non-temporal loads (measured on MI355X: Large 811 -> 805 us)
   const uint4* c4 = reinterpret_cast<const uint4*>(celdaDe + base);  // base: a multiple of 4
   const uint32_t quads = static_cast<uint32_t>((end - base) / 4u);
   uint4 v[kLoads];
 #pragma unroll
   for (uint32_t k = 0; k < kLoads; ++k) {
     const uint32_t q = k * kCountThreads + threadIdx.x;
-    v[k] = (q < quads) ? c4[q] : make_uint4(0u, 0u, 0u, 0u);
+    v[k] = (q < quads) ? load_stream(c4 + q) : make_uint4(0u, 0u, 0u, 0u);
   }
 #pragma unroll
   for (uint32_t k = 0; k < kLoads; ++k) {
