@@ -165,6 +165,7 @@ __device__ __forceinline__ void store_stream(uint4* p, uint4 v) {
   __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(p));
 }
 __device__ __forceinline__ uint32_t load_stream(const uint32_t* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ void store_stream(uint32_t* p, uint32_t v) { __builtin_nontemporal_store(v, p); }
 
 // Stores written through the L2 to memory (cache policy sc1: device scope),
 // through a buffer resource over one workgroup's own output range of `bytes`
@@ -172,13 +173,15 @@ __device__ __forceinline__ uint32_t load_stream(const uint32_t* p) { return __bu
 // start). A workgroup's dirty L2 lines are otherwise written back when the
 // kernel ends, after its last store: sent out while it runs, they leave that
 // write-back short. Used for the chunk kernel's chunk array when it is larger
-// than the L2 caches hold (read by the next kernel from memory in either
-// case) and the tile kernel's conteos and inicios (never read again by the
-// build). Measured on MI355X, each change
-// against the one before: the counts and starts, Sparse 21.9 -> 20.7 us and
-// Large 860 -> 843 us (Baseline unchanged); the chunk array, Baseline 37.4 ->
-// 36.5 us, Sparse 20.6 -> 20.1 us, Large 842 -> 835 us. The tile kernel's
-// records (written last) and celdaDe lose or gain nothing this way.
+// than the L2 caches hold (the next kernel reads it from memory either way)
+// and for the tile kernel's conteos and inicios (never read again by the
+// build). Measured on MI355X, each change against the one before:
+//   conteos and inicios  Sparse 21.9 -> 20.7 us, Large 860 -> 843 us,
+//                        Baseline unchanged;
+//   the chunk array      Baseline 37.4 -> 36.5 us, Sparse 20.6 -> 20.1 us,
+//                        Large 842 -> 835 us.
+// Written through, the tile kernel's records (its last stores) cost 4 us at
+// Baseline and celdaDe gained nothing.
 constexpr int kStoreThrough = 16;  // the sc1 bit of a buffer store's cache policy
 constexpr int kStoreThroughNT = 16 | 2;  // sc1 and the non-temporal bit
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t output_rsrc(void* p, uint32_t bytes) {
@@ -201,7 +204,6 @@ __device__ __forceinline__ void store_through_nt(__amdgpu_buffer_rsrc_t r, uint3
 __device__ __forceinline__ void store_through_nt(__amdgpu_buffer_rsrc_t r, uint32_t offset, uint32_t v) {
   __builtin_amdgcn_raw_buffer_store_b32(v, r, static_cast<int>(offset), 0, kStoreThroughNT);
 }
-__device__ __forceinline__ void store_stream(uint32_t* p, uint32_t v) { __builtin_nontemporal_store(v, p); }
 
 // Inclusive prefix sum across the 64 lanes of a wave, with DPP lane moves
 // (no LDS traffic): shifts of 1, 2, 4 and 8 lanes inside each row of 16
